@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunk-wise forward of the generalized linear-attention recurrence.
+
+One step = one full chunk-wise forward (chunk operators, then the ordered scan
+that produces the outputs and the final state) over one batch of seeded
+synthetic input already resident in HBM.  The decay operands A, B are built
+by the device parameter kernel before the timed region (they are inputs of
+the forward call).  Prints ONE JSON line (rank 0):
+
+  value       whole-job forward tokens/s (tokens = batch x sequence positions)
+  roofline    the dominant kernel, measured with HIP events on its stream
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "fwd tokens/sec + % bf16 MFMA peak, rank-2 HDLA B8 H16 T4096 d128"
+PEAK = {  # MI355X published peaks
+    "hbm_GBs": 8000.0,
+    "bf16_mfma_TFs": 2500.0,
+    "fp32_mfma_TFs": 157.3,
+    # fp32 vector without packed-fp32 issue: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+    "fp32_valu_TFs": 78.6,
+}
+KERNEL_SOURCES = {
+    "general_fp32": ["structured_decay_sequence_amd/csrc/general.hip"],
+    "mfma_bf16": ["structured_decay_sequence_amd/csrc/fast.hip"],
+}
+
+
+def canonical_work(spec):
+    """Algorithmic flops and bytes of one forward (per-chunk-head MAC formulas of the
+    three stages: chunk summary, inter-chunk scan, output; inputs + outputs once)."""
+    C, dk, dv = spec.chunk, spec.dk, spec.dv
+    na, nk = C * spec.r_ab, C * spec.r_kv
+    mac_a = (2 * na * na * dk + na * nk * dk + na ** 3 / 6 + na * nk * dv + na * na * dv + na * dk * dk
+             + nk * dk * dv + na * dk * dv)
+    mac_b = dk * dk * dv
+    mac_c = 2 * C * na * dk + C * nk * dk + C * dk * dv + C * nk * dv + C * na * dv
+    BH = spec.B * spec.H
+    N = -(-spec.T // C)
+    flops = 2.0 * (mac_a + mac_b + mac_c) * BH * N
+    e = 2 if spec.dtype == "bf16" else 4
+    dec = 4 if spec.scalar_decay else 4 * dk
+    per_tok = e * (dk + spec.r_kv * dk + spec.r_kv * dv + 2 * spec.r_ab * dk + dv) + dec
+    nbytes = per_tok * BH * spec.T + BH * dk * dv * 4
+    return flops, nbytes
+
+
+def kernel_work(spec, kernels):
+    """Per-launch work of each kernel of the two-stage decomposition.
+
+    prepare: reads q, K, A, B, log-decay once; writes the chunk operator
+             M_j ((dk + C) x (dk + C r_kv)) once per chunk.
+    scan:    reads M_j and V once, writes out and the final state once.
+    flops: the multiply-adds each kernel's decomposition performs (masked and
+    triangular products at dense size, the triangular inverse at n^3/6).
+    """
+    C, dk, dv = spec.chunk, spec.dk, spec.dv
+    na, nk = C * spec.r_ab, C * spec.r_kv
+    BH = spec.B * spec.H
+    N = -(-spec.T // C)
+    e = 2 if spec.dtype == "bf16" else 4
+    em = 4 if kernels == "general_fp32" else e  # element size of the stored chunk operator
+    m_elems = (dk + C) * (dk + nk)
+    dec = 4 if spec.scalar_decay else 4 * dk
+    prep_in = (e * (dk + spec.r_kv * dk + 2 * spec.r_ab * dk) + dec) * BH * spec.T
+    prep_bytes = prep_in + em * m_elems * BH * N
+    prep_mac = ((na + C) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (C + dk) * na * (dk + nk))
+    scan_bytes = em * m_elems * BH * N + e * (spec.r_kv * dv + dv) * BH * spec.T + 4 * BH * dk * dv
+    scan_mac = (dk + C) * (dk + nk) * dv
+    return {
+        "prepare": dict(flops=2.0 * prep_mac * BH * N, bytes=float(prep_bytes)),
+        "scan": dict(flops=2.0 * scan_mac * BH * N, bytes=float(scan_bytes)),
+    }
+
+
+def kernel_peak(kernels, dtype, bound):
+    if bound == "hbm":
+        return PEAK["hbm_GBs"], "GB/s"
+    if kernels == "general_fp32":
+        return PEAK["fp32_valu_TFs"], "TFLOP/s"
+    return (PEAK["bf16_mfma_TFs"] if dtype == "bf16" else PEAK["fp32_mfma_TFs"]), "TFLOP/s"
+
+
+def source_hash(kernels):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(kernels, []) + ["structured_decay_sequence_amd/csrc/common.hpp"]:
+        path = os.path.join(ROOT, rel)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernels, kernel, workload):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernels}:{kernel}:{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_hash(kernels):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def build_inputs(spec, torch, lattn, dev):
+    """Host-generated seeded inputs -> device; decay operands built on the device."""
+    raw = workloads.raw_for(spec)
+    td = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    t = lambda x, d=td: torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
+    q = t(raw["q"])
+    if spec.family == "hdla":
+        k, v = t(raw["k"]), t(raw["v"])
+        ld = t(raw["log_lambda"], torch.float32)
+        A, B, V = lattn.hdla_params(k, v, ld, t(raw["beta"], torch.float32))
+        K = k
+    elif spec.family == "gdn":
+        k, v = t(raw["k"]), t(raw["v"])
+        ld = t(raw["g"], torch.float32)
+        A, B, V = lattn.gdn_params(k, v, ld, t(raw["beta"], torch.float32))
+        K = k
+    else:
+        K, V = t(raw["K"]), t(raw["V"])
+        ld = t(raw["log_decay"], torch.float32)
+        A = None if raw["A"] is None else t(raw["A"])
+        B = None if raw["B"] is None else t(raw["B"])
+    torch.cuda.synchronize(dev)
+    return raw, (q, K, V, ld, A, B)
+
+
+def cpu_baseline(spec, raw, budget_s):
+    """Time the fp64 oracle (generic form, as used for parity) on a bounded sample of
+    (batch, head) rows of the same workload, on all host cores."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    per_head_core_s = spec.T * (spec.dk * spec.dk * spec.dv) * 2 / 7.8e9  # rough cost model
+    n = int(max(1, min(spec.B * spec.H, round(budget_s * cores / max(per_head_core_s, 1e-9)))))
+    n = max(1, min(n, spec.B * spec.H))
+    flat = lambda x: x.reshape((spec.B * spec.H,) + x.shape[2:])[:n]
+    if spec.family == "hdla":
+        ld, A, B, K, V = oracle.hdla_to_generic(flat(raw["k"]), flat(raw["v"]), flat(raw["log_lambda"]),
+                                               flat(raw["beta"]))
+    elif spec.family == "gdn":
+        ld, A, B, K, V = oracle.gdn_to_generic(flat(raw["k"]), flat(raw["v"]), flat(raw["g"]), flat(raw["beta"]))
+    else:
+        ld, A, B, K, V = (flat(raw["log_decay"]), flat(raw["A"]), flat(raw["B"]), flat(raw["K"]),
+                          flat(raw["V"]))
+    q = flat(raw["q"])
+    t0 = time.perf_counter()
+    oracle.generic(q, K, V, ld, A, B, nthreads=cores)
+    wall = time.perf_counter() - t0
+    head_tok_s = n * spec.T / wall
+    return {
+        "value": head_tok_s / spec.H,
+        "unit": "tokens/s",
+        "cores": int(oracle.max_threads()),
+        "kind": "oracle",
+        "sample": f"{n} of {spec.B * spec.H} (batch, head) rows x {spec.T} tokens, fp64 explicit-P_t recurrence, "
+                  f"{wall:.1f} s wall; tokens/s = head-tokens/s / H",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=workloads.HEADLINE, choices=workloads.CONFIG_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0, help="target oracle wall time")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the (batch, head) rows shard with no communication, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structured_decay_sequence_amd as lattn
+
+    spec = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    print(f"[bench] {spec.describe()}: generating inputs", file=sys.stderr, flush=True)
+    raw, (q, K, V, ld, A, B) = build_inputs(spec, torch, lattn, dev)
+    plan = lattn.ChunkPlan(q, K, V, ld, A, B, chunk=spec.chunk)
+    kernels = lattn._lib.load().lattn_chunk_fwd_kernels(
+        __import__("ctypes").byref(plan.dims), plan.r_ab, plan.r_kv, plan.chunk).decode()
+
+    for _ in range(args.warmup):
+        plan.prepare()
+        plan.scan()
+    torch.cuda.synchronize(dev)
+    print(f"[bench] kernels {kernels}: warmup {args.warmup} done, timing {args.steps} steps",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        plan.prepare()
+        e[1].record(stream)
+        plan.scan()
+        e[2].record(stream)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_scan = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
+
+    tokens = spec.B * spec.T
+    value = tokens / (ms_step / 1e3)
+    flops, nbytes = canonical_work(spec)
+    kw = kernel_work(spec, kernels)
+    times = {"prepare": ms_prep, "scan": ms_scan}
+    dom = max(times, key=times.get)
+    work = kw[dom]
+    e_dtype = spec.dtype
+    # the roofline a kernel sits under: the larger of its time at peak compute and at peak HBM
+    comp_peak, _ = kernel_peak(kernels, e_dtype, "compute")
+    t_comp = work["flops"] / (comp_peak * 1e12)
+    t_mem = work["bytes"] / (PEAK["hbm_GBs"] * 1e9)
+    if t_mem >= t_comp:
+        bound, achieved, unit = "hbm", work["bytes"] / (times[dom] / 1e3) / 1e9, "GB/s"
+        peak = PEAK["hbm_GBs"]
+    else:
+        bound = "alu" if kernels == "general_fp32" else "mfma"
+        achieved, unit, peak = work["flops"] / (times[dom] / 1e3) / 1e12, "TFLOP/s", comp_peak
+    traffic = measured_traffic(kernels, dom, spec.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32" if kernels == "general_fp32" else spec.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "family": spec.family, "batch": spec.B, "heads": spec.H, "seq_len": spec.T,
+            "d_k": spec.dk, "d_v": spec.dv, "chunk": spec.chunk, "r_ab": spec.r_ab, "r_kv": spec.r_kv,
+            "storage": spec.dtype, "kernels": kernels, "parallelism": "single-gpu",
+        },
+        "mfma_frac_canonical": round(flops / (ms_step / 1e3) / (PEAK["bf16_mfma_TFs"] * 1e12), 4),
+        "hbm_frac_algorithmic": round(nbytes / (ms_step / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
+        "canonical_gflop": round(flops / 1e9, 2),
+        "algorithmic_gb": round(nbytes / 1e9, 4),
+        "kernel_ms": {"prepare": round(ms_prep, 4), "scan": round(ms_scan, 4)},
+        "roofline": {
+            "kernel": dom,
+            "bound": bound,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(spec, raw, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * lattn.h -- C ABI of the MI355X (gfx950) chunk-wise forward of the generalized
+ * linear-attention recurrence
+ *
+ *     S_t = (D_t - A_t B_t^T) S_{t-1} + K_t V_t^T,        o_t = S_t^T q_t
+ *
+ * (HDLA note, "Key design 3": decay of rank r_ab written as diagonal minus
+ * low rank, write of rank r_kv; HDLA note, "Overall framework": chunks of C
+ * tokens, chunk-state checkpoints, then per-chunk outputs).  D_t is diagonal,
+ * D_t = diag(exp(log_decay_t)).  The three named decays map onto it as:
+ *   GLA     r_ab = 0                 D_t = Diag(lambda_t)
+ *   GDN     r_ab = 1 (scalar decay)  D_t = exp(g_t) I, A_t = exp(g_t) beta_t k_t, B_t = k_t
+ *   HDLA    r_ab = 2                 D_t = Diag(lambda_t), A_t = [b k, b u], B_t = [u - b c k, k]
+ *                                    (u = lambda (.) k, c = k^T u)
+ * lattn_hdla_params / lattn_gdn_params build those operands on the device.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer to contiguous row-major memory,
+ *   aligned to 16 bytes.  The caller owns all memory, including the
+ *   workspace; the library allocates nothing, keeps no pointer after a call
+ *   returns and holds no global mutable state, so calls are reentrant.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *   stream) and is asynchronous: outputs are valid once the stream is
+ *   synchronized.  No entry point synchronizes the host except
+ *   lattn_check_decay_range.
+ * - Results are deterministic: the kernels use no atomics and no
+ *   order-dependent reductions.
+ * - Arguments are validated on the host before anything is launched; a
+ *   failure returns a negative lattn_status and lattn_last_error() gives a
+ *   thread-local message.  NaN/Inf inputs are not checked and propagate.
+ * - Element types: q, K, V, A, B and out share dims->dtype (fp32 or bf16);
+ *   log_decay and every state tensor are fp32.  Internal accumulation is
+ *   fp32 for both dtypes.
+ * - No 1/sqrt(d_k) scale is applied: o_t uses the state after token t's
+ *   update, as written above; a caller wanting a scaled readout pre-scales q.
+ */
+#ifndef LATTN_H_
+#define LATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LATTN_OK = 0,
+  LATTN_EINVAL = -1,        /* bad pointer, shape or rank                          */
+  LATTN_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement    */
+  LATTN_EWORKSPACE = -3,    /* workspace missing or smaller than required         */
+  LATTN_EHIP = -4,          /* a HIP runtime call or kernel launch failed         */
+  LATTN_EDECAY_RANGE = -5   /* cumulative log-decay in one chunk exceeds the limit */
+} lattn_status;
+
+typedef enum { LATTN_FP32 = 0, LATTN_BF16 = 1 } lattn_dtype;
+
+typedef enum {
+  LATTN_DECAY_PER_CHANNEL = 0, /* log_decay [B,H,T,d_k]                 */
+  LATTN_DECAY_SCALAR = 1       /* log_decay [B,H,T], broadcast over d_k */
+} lattn_decay_mode;
+
+typedef struct {
+  int64_t batch;     /* B >= 1                                   */
+  int64_t heads;     /* H >= 1                                   */
+  int64_t seqlen;    /* T >= 0 (T = 0 is a no-op that copies the initial state) */
+  int32_t d_k;       /* 16 <= d_k <= 256, multiple of 16         */
+  int32_t d_v;       /* 16 <= d_v <= 256, multiple of 16         */
+  lattn_dtype dtype;
+  lattn_decay_mode decay_mode;
+} lattn_dims;
+
+/* Largest cumulative |log-decay| one chunk may accumulate (exp(80) ~ 5.5e34
+ * stays inside fp32); lattn_check_decay_range tests inputs against it. */
+#define LATTN_MAX_CHUNK_LOG_DECAY 80.0f
+
+/*
+ * lattn_chunk_fwd -- chunk-wise forward over a whole sequence (HDLA note,
+ * "Key design 3": rank-generalized chunk-wise algorithm; HLA note, "Affine
+ * maps and closure under composition": each chunk's exact affine summary).
+ *
+ *   q          [B,H,T,d_k]                 dtype
+ *   k          K_t   [B,H,T,r_kv,d_k]      dtype
+ *   v          V_t   [B,H,T,r_kv,d_v]      dtype
+ *   log_decay  [B,H,T,d_k] or [B,H,T]      fp32 (per dims->decay_mode)
+ *   A, B       [B,H,T,r_ab,d_k]            dtype; both NULL iff r_ab == 0
+ *   r_ab       0..8;  r_kv 1..4
+ *   chunk      C in {16, 32, 64, 128}; T need not be a multiple of C (the
+ *              last chunk is shorter); C*r_ab <= 512 and C*r_kv <= 256
+ *   out        [B,H,T,d_v]                 dtype (written)
+ *   final_state    [B,H,d_k,d_v] fp32 (written); NULL = not returned
+ *   initial_state  [B,H,d_k,d_v] fp32 (read);    NULL = zero state
+ *   workspace  device scratch of at least lattn_chunk_fwd_workspace_size()
+ *              bytes, owned by the caller, contents ignored on entry
+ * Returns LATTN_OK or a negative lattn_status.
+ */
+int lattn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                    const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                    int chunk, void* out, float* final_state, const float* initial_state,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lattn_chunk_fwd needs for these arguments (0 on invalid
+ * arguments; host-only, launches nothing). */
+size_t lattn_chunk_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
+
+/* Host-only validation of lattn_chunk_fwd's arguments (the same checks the
+ * call performs before launching).  Pointers are only tested for NULL and
+ * 16-byte alignment, never dereferenced. */
+int lattn_chunk_fwd_check(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                          const float* log_decay, const void* A, const void* B, int r_ab,
+                          int r_kv, int chunk, const void* out, const void* workspace,
+                          size_t workspace_bytes);
+
+/*
+ * The two stages lattn_chunk_fwd runs, callable one by one (same arguments,
+ * same workspace; calling both in order on one stream is lattn_chunk_fwd):
+ *
+ * lattn_chunk_prepare -- for every chunk in parallel, the exact chunk operator
+ *   built from q, K, A, B and the log-decay (HDLA note, "Key design 3": the
+ *   rank-generalized WY form; HLA note, "Affine maps and closure under
+ *   composition"), written into the workspace.  v is not read.
+ * lattn_chunk_scan -- walks the chunks of each (batch, head) in order,
+ *   carrying the d_k x d_v state: per chunk one product gives the next state
+ *   and the chunk's outputs (HDLA note, "Overall framework": serial chunk-state
+ *   checkpoints, then chunk outputs).  Reads v and the workspace written by
+ *   lattn_chunk_prepare with the same dims, ranks and chunk.
+ */
+int lattn_chunk_prepare(const lattn_dims* dims, const void* q, const void* k,
+                        const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                        int chunk, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int lattn_chunk_scan(const lattn_dims* dims, const void* v, int r_ab, int r_kv, int chunk,
+                     void* out, float* final_state, const float* initial_state, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lattn_chunk_summaries -- the exact affine pair of every chunk (HLA note,
+ * "Affine maps and closure under composition"): after chunk j,
+ * S_j = sum_A[j] S_{j-1} + sum_B[j].  Inputs as lattn_chunk_fwd (q unused).
+ *   sum_A [B,H,N,d_k,d_k] fp32, sum_B [B,H,N,d_k,d_v] fp32, N = ceil(T/C).
+ * Needs the same workspace as lattn_chunk_fwd.
+ */
+int lattn_chunk_summaries(const lattn_dims* dims, const void* k, const void* v,
+                          const float* log_decay, const void* A, const void* B, int r_ab,
+                          int r_kv, int chunk, float* sum_A, float* sum_B, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lattn_step -- one recurrent token for decoding (HLA note, "Reproduction":
+ * a prefill algorithm and a dynamic decoding algorithm; the recurrence of
+ * HDLA note, "Key design 3", applied once):
+ *   state <- (D - A B^T) state + K V^T,   out = state^T q.
+ * dims->seqlen must be 1.  q [B,H,d_k]; k [B,H,r_kv,d_k]; v [B,H,r_kv,d_v];
+ * log_decay [B,H,d_k] or [B,H]; A, B [B,H,r_ab,d_k] (NULL iff r_ab == 0);
+ * state [B,H,d_k,d_v] fp32 read and written in place; out [B,H,d_v] dtype.
+ */
+int lattn_step(const lattn_dims* dims, const void* q, const void* k, const void* v,
+               const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+               float* state, void* out, hipStream_t stream);
+
+/*
+ * lattn_hdla_params -- HDLA's decay written as diagonal minus rank 2 (HDLA
+ * note, "Key design 2" and "Key design 3"), on the device:
+ *   u = exp(log_lambda) (.) k,  c = k^T u,
+ *   A = [beta k, beta u],  B = [u - beta c k, k],  V_out = beta v.
+ * k [B,H,T,d_k] dtype; v [B,H,T,d_v] dtype; log_lambda [B,H,T,d_k] fp32;
+ * beta [B,H,T] fp32.  Outputs (dtype): A, B [B,H,T,2,d_k]; V_out [B,H,T,1,d_v].
+ * The generic call then takes K = k, log_decay = log_lambda, r_ab = 2, r_kv = 1.
+ * dims->decay_mode must be LATTN_DECAY_PER_CHANNEL.
+ */
+int lattn_hdla_params(const lattn_dims* dims, const void* k, const void* v,
+                      const float* log_lambda, const float* beta, void* A, void* B, void* V_out,
+                      hipStream_t stream);
+
+/*
+ * lattn_gdn_params -- Gated DeltaNet's decay exp(g)(I - beta k k^T) written as
+ * exp(g) I - (exp(g) beta k) k^T (HLA note, "Prerequisites: Gated DeltaNet"):
+ *   A = exp(g) beta k,  B = k,  V_out = beta v.
+ * k [B,H,T,d_k]; v [B,H,T,d_v] dtype; g, beta [B,H,T] fp32.
+ * Outputs (dtype): A, B [B,H,T,1,d_k]; V_out [B,H,T,1,d_v].  The generic call
+ * then takes K = k, log_decay = g (scalar mode), r_ab = 1, r_kv = 1.
+ */
+int lattn_gdn_params(const lattn_dims* dims, const void* k, const void* v, const float* g,
+                     const float* beta, void* A, void* B, void* V_out, hipStream_t stream);
+
+/*
+ * lattn_decay_range -- per chunk, the largest -G over the chunk's tokens and
+ * channels, where G is the chunk-local inclusive cumulative log-decay.  The
+ * chunk-wise form scales operands by exp(-G); the result must stay below
+ * LATTN_MAX_CHUNK_LOG_DECAY.  chunk_max [B,H,N] fp32 (written).  Asynchronous.
+ */
+int lattn_decay_range(const lattn_dims* dims, const float* log_decay, int chunk,
+                      float* chunk_max, hipStream_t stream);
+
+/* Synchronous convenience check built on lattn_decay_range: returns LATTN_OK
+ * or LATTN_EDECAY_RANGE.  `scratch` holds B*H*ceil(T/C) floats (device). */
+int lattn_check_decay_range(const lattn_dims* dims, const float* log_decay, int chunk,
+                            float* scratch, hipStream_t stream);
+
+/* Name of the kernel pair lattn_chunk_fwd runs for these arguments (host-only;
+ * "" on invalid arguments): "general_fp32" (fp32 arithmetic, every shape) or
+ * "mfma_bf16" (bf16 MFMA with fp32 accumulation). */
+const char* lattn_chunk_fwd_kernels(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
+
+/* Static description of a status code. */
+const char* lattn_status_str(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* lattn_last_error(void);
+
+/* Library version string. */
+const char* lattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATTN_H_ */

@@ -1,0 +1,303 @@
+"""MI355X-native chunk-wise forward of the generalized linear-attention recurrence.
+
+    S_t = (D_t - A_t B_t^T) S_{t-1} + K_t V_t^T,   o_t = S_t^T q_t
+
+Thin Python binding over ``liblattn.so`` (C ABI in ``include/lattn.h``).
+Torch tensors supply device memory and the current HIP stream; every step of
+the computation runs in the library's HIP kernels.  The functions below only
+check shapes/dtypes, allocate outputs and marshal pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import LattnError, LATTN_BF16, LATTN_FP32, LATTN_DECAY_PER_CHANNEL, LATTN_DECAY_SCALAR
+
+__all__ = [
+    "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
+    "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
+]
+
+
+def version() -> str:
+    return _lib.load().lattn_version().decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LATTN_BF16
+    if t.dtype == torch.float32:
+        return LATTN_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.float32 or torch.bfloat16")
+
+
+def make_dims(batch, heads, seqlen, d_k, d_v, dtype_code, scalar_decay) -> _lib.lattn_dims:
+    return _lib.lattn_dims(int(batch), int(heads), int(seqlen), int(d_k), int(d_v), int(dtype_code),
+                           LATTN_DECAY_SCALAR if scalar_decay else LATTN_DECAY_PER_CHANNEL)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to lattn must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+_workspaces = {}
+
+
+def _workspace(device, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    key = torch.device(device).index
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _ranked(x: torch.Tensor, lead, T, d):
+    """Accept [*lead, T, d] as rank 1 or [*lead, T, r, d]."""
+    if x.dim() == len(lead) + 2:
+        return x.unsqueeze(-2)
+    return x
+
+
+def workspace_size(batch, heads, seqlen, d_k, d_v, r_ab, r_kv, chunk, dtype=torch.bfloat16,
+                   scalar_decay=False) -> int:
+    code = LATTN_BF16 if dtype == torch.bfloat16 else LATTN_FP32
+    dims = make_dims(batch, heads, seqlen, d_k, d_v, code, scalar_decay)
+    return int(_lib.load().lattn_chunk_fwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+              A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None, chunk: int = 64,
+              initial_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None, return_final_state: bool = True,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunk-wise forward.  q [B,H,T,dk]; k [B,H,T,(r_kv,)dk]; v [B,H,T,(r_kv,)dv];
+    log_decay fp32 [B,H,T,dk] or [B,H,T]; A, B [B,H,T,r_ab,dk] or None.
+    Returns (out [B,H,T,dv], final_state [B,H,dk,dv] fp32 or None)."""
+    Bb, H, T, dk = q.shape
+    dt = q.dtype
+    lead = (Bb, H)
+    k = _ranked(k, lead, T, dk)
+    v = _ranked(v, lead, T, None)
+    r_kv, dv = k.shape[-2], v.shape[-1]
+    _need(q, dt, (Bb, H, T, dk), "q")
+    _need(k, dt, (Bb, H, T, r_kv, dk), "k")
+    _need(v, dt, (Bb, H, T, r_kv, dv), "v")
+    scalar = log_decay.dim() == 3
+    _need(log_decay, torch.float32, (Bb, H, T) if scalar else (Bb, H, T, dk), "log_decay")
+    r_ab = 0
+    if A is not None:
+        r_ab = A.shape[-2]
+        _need(A, dt, (Bb, H, T, r_ab, dk), "A")
+        _need(B, dt, (Bb, H, T, r_ab, dk), "B")
+    if initial_state is not None:
+        _need(initial_state, torch.float32, (Bb, H, dk, dv), "initial_state")
+    if out is None:
+        out = torch.empty((Bb, H, T, dv), dtype=dt, device=q.device)
+    _need(out, dt, (Bb, H, T, dv), "out")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((Bb, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, torch.float32, (Bb, H, dk, dv), "final_state")
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+    ws_bytes = int(lib.lattn_chunk_fwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk))
+    if workspace is None:
+        workspace = _workspace(q.device, ws_bytes)
+    rc = lib.lattn_chunk_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A),
+                             _ptr(B), r_ab, r_kv, chunk, _ptr(out), _ptr(final_state),
+                             _ptr(initial_state), _ptr(workspace),
+                             0 if workspace is None else workspace.numel(), _stream(q.device))
+    _lib.check(rc, "lattn_chunk_fwd")
+    return out, final_state
+
+
+def chunk_summaries(k, v, log_decay, A=None, B=None, chunk: int = 64):
+    """Exact affine pair of every chunk: (sum_A [B,H,N,dk,dk], sum_B [B,H,N,dk,dv]) fp32."""
+    Bb, H, T = k.shape[:3]
+    dk = k.shape[-1]
+    k = _ranked(k, (Bb, H), T, dk)
+    v = _ranked(v, (Bb, H), T, None)
+    r_kv, dv = k.shape[-2], v.shape[-1]
+    dt = k.dtype
+    _need(v, dt, (Bb, H, T, r_kv, dv), "v")
+    scalar = log_decay.dim() == 3
+    _need(log_decay, torch.float32, (Bb, H, T) if scalar else (Bb, H, T, dk), "log_decay")
+    r_ab = 0 if A is None else A.shape[-2]
+    N = -(-T // chunk)
+    sA = torch.empty((Bb, H, N, dk, dk), dtype=torch.float32, device=k.device)
+    sB = torch.empty((Bb, H, N, dk, dv), dtype=torch.float32, device=k.device)
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(k), scalar)
+    ws_bytes = int(lib.lattn_chunk_fwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk))
+    ws = _workspace(k.device, ws_bytes)
+    rc = lib.lattn_chunk_summaries(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A),
+                                   _ptr(B), r_ab, r_kv, chunk, _ptr(sA), _ptr(sB), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(k.device))
+    _lib.check(rc, "lattn_chunk_summaries")
+    return sA, sB
+
+
+def step(q, k, v, log_decay, A, B, state, out=None):
+    """One recurrent token.  q [B,H,dk]; k [B,H,(r_kv,)dk]; v [B,H,(r_kv,)dv];
+    log_decay [B,H,dk] or [B,H]; A, B [B,H,r_ab,dk] or None; state [B,H,dk,dv]
+    fp32 updated in place.  Returns out [B,H,dv]."""
+    Bb, H, dk = q.shape
+    if k.dim() == 3:
+        k = k.unsqueeze(-2)
+    if v.dim() == 3:
+        v = v.unsqueeze(-2)
+    r_kv, dv = k.shape[-2], v.shape[-1]
+    scalar = log_decay.dim() == 2
+    _need(log_decay, torch.float32, (Bb, H) if scalar else (Bb, H, dk), "log_decay")
+    _need(state, torch.float32, (Bb, H, dk, dv), "state")
+    r_ab = 0 if A is None else A.shape[-2]
+    if out is None:
+        out = torch.empty((Bb, H, dv), dtype=q.dtype, device=q.device)
+    lib = _lib.load()
+    dims = make_dims(Bb, H, 1, dk, dv, _dtype_code(q), scalar)
+    rc = lib.lattn_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A),
+                        _ptr(B), r_ab, r_kv, _ptr(state), _ptr(out), _stream(q.device))
+    _lib.check(rc, "lattn_step")
+    return out
+
+
+def hdla_params(k, v, log_lambda, beta):
+    """HDLA decay operands on the device: returns (A, B [B,H,T,2,dk], V [B,H,T,1,dv])."""
+    Bb, H, T, dk = k.shape
+    dv = v.shape[-1]
+    A = torch.empty((Bb, H, T, 2, dk), dtype=k.dtype, device=k.device)
+    Bm = torch.empty_like(A)
+    V = torch.empty((Bb, H, T, 1, dv), dtype=k.dtype, device=k.device)
+    _need(log_lambda, torch.float32, (Bb, H, T, dk), "log_lambda")
+    _need(beta, torch.float32, (Bb, H, T), "beta")
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(k), False)
+    rc = lib.lattn_hdla_params(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(log_lambda), _ptr(beta),
+                               _ptr(A), _ptr(Bm), _ptr(V), _stream(k.device))
+    _lib.check(rc, "lattn_hdla_params")
+    return A, Bm, V
+
+
+def gdn_params(k, v, g, beta):
+    """Gated DeltaNet decay operands: returns (A, B [B,H,T,1,dk], V [B,H,T,1,dv])."""
+    Bb, H, T, dk = k.shape
+    dv = v.shape[-1]
+    A = torch.empty((Bb, H, T, 1, dk), dtype=k.dtype, device=k.device)
+    Bm = torch.empty_like(A)
+    V = torch.empty((Bb, H, T, 1, dv), dtype=k.dtype, device=k.device)
+    _need(g, torch.float32, (Bb, H, T), "g")
+    _need(beta, torch.float32, (Bb, H, T), "beta")
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(k), True)
+    rc = lib.lattn_gdn_params(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A),
+                              _ptr(Bm), _ptr(V), _stream(k.device))
+    _lib.check(rc, "lattn_gdn_params")
+    return A, Bm, V
+
+
+def decay_range(log_decay, chunk: int, d_k: Optional[int] = None):
+    """Per chunk, the largest -G (chunk-local inclusive cumulative log-decay): [B,H,N] fp32."""
+    scalar = log_decay.dim() == 3
+    Bb, H, T = log_decay.shape[:3]
+    dk = d_k if scalar else log_decay.shape[-1]
+    dk = 16 if dk is None else dk
+    N = -(-T // chunk)
+    res = torch.empty((Bb, H, N), dtype=torch.float32, device=log_decay.device)
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, 16, LATTN_FP32, scalar)
+    rc = lib.lattn_decay_range(ctypes.byref(dims), _ptr(log_decay), chunk, _ptr(res),
+                               _stream(log_decay.device))
+    _lib.check(rc, "lattn_decay_range")
+    return res
+
+
+def check_decay_range(log_decay, chunk: int, d_k: Optional[int] = None) -> None:
+    """Raise LattnError(LATTN_EDECAY_RANGE) if any chunk's -G exceeds the supported limit."""
+    scalar = log_decay.dim() == 3
+    Bb, H, T = log_decay.shape[:3]
+    dk = d_k if scalar else log_decay.shape[-1]
+    dk = 16 if dk is None else dk
+    N = -(-T // chunk)
+    scratch = torch.empty((max(1, Bb * H * N),), dtype=torch.float32, device=log_decay.device)
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, 16, LATTN_FP32, scalar)
+    rc = lib.lattn_check_decay_range(ctypes.byref(dims), _ptr(log_decay), chunk, _ptr(scratch),
+                                     _stream(log_decay.device))
+    _lib.check(rc, "lattn_check_decay_range")
+
+
+class ChunkPlan:
+    """Pre-marshalled arguments of one chunk-wise forward, for calling its two
+    stages (prepare, scan) repeatedly with no per-call Python shape work.
+
+    ``prepare()`` + ``scan()`` on one stream is exactly ``chunk_fwd``.
+    """
+
+    def __init__(self, q, k, v, log_decay, A=None, B=None, chunk=64, initial_state=None,
+                 return_final_state=True):
+        Bb, H, T, dk = q.shape
+        k = _ranked(k, (Bb, H), T, dk)
+        v = _ranked(v, (Bb, H), T, None)
+        self.r_kv, dv = k.shape[-2], v.shape[-1]
+        self.r_ab = 0 if A is None else A.shape[-2]
+        self.chunk = chunk
+        scalar = log_decay.dim() == 3
+        self.dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+        self.lib = _lib.load()
+        self.ws_bytes = int(self.lib.lattn_chunk_fwd_workspace_size(ctypes.byref(self.dims), self.r_ab,
+                                                                   self.r_kv, chunk))
+        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        self.out = torch.empty((Bb, H, T, dv), dtype=q.dtype, device=q.device)
+        self.final_state = (torch.empty((Bb, H, dk, dv), dtype=torch.float32, device=q.device)
+                            if return_final_state else None)
+        self._keep = (q, k, v, log_decay, A, B, initial_state)
+        self.p = dict(q=_ptr(q), k=_ptr(k), v=_ptr(v), ld=_ptr(log_decay), A=_ptr(A), B=_ptr(B),
+                      S0=_ptr(initial_state), out=_ptr(self.out), Sf=_ptr(self.final_state),
+                      ws=_ptr(self.workspace))
+        self.device = q.device
+
+    def prepare(self):
+        p = self.p
+        rc = self.lib.lattn_chunk_prepare(ctypes.byref(self.dims), p["q"], p["k"], p["ld"], p["A"], p["B"],
+                                          self.r_ab, self.r_kv, self.chunk, p["ws"], self.ws_bytes,
+                                          _stream(self.device))
+        _lib.check(rc, "lattn_chunk_prepare")
+
+    def scan(self):
+        p = self.p
+        rc = self.lib.lattn_chunk_scan(ctypes.byref(self.dims), p["v"], self.r_ab, self.r_kv, self.chunk,
+                                       p["out"], p["Sf"], p["S0"], p["ws"], self.ws_bytes,
+                                       _stream(self.device))
+        _lib.check(rc, "lattn_chunk_scan")
+
+    def forward(self):
+        p = self.p
+        rc = self.lib.lattn_chunk_fwd(ctypes.byref(self.dims), p["q"], p["k"], p["v"], p["ld"], p["A"], p["B"],
+                                      self.r_ab, self.r_kv, self.chunk, p["out"], p["Sf"], p["S0"], p["ws"],
+                                      self.ws_bytes, _stream(self.device))
+        _lib.check(rc, "lattn_chunk_fwd")
+        return self.out, self.final_state

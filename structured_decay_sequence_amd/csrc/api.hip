@@ -1,0 +1,326 @@
+// C ABI of liblattn: host-side validation, workspace planning and dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/lattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return LATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const lattn_dims* d) {
+  if (d == nullptr) return fail(LATTN_EINVAL, "dims is NULL");
+  if (d->batch < 1 || d->heads < 1 || d->seqlen < 0)
+    return fail(LATTN_EINVAL, "batch (%lld) and heads (%lld) must be >= 1, seqlen (%lld) >= 0",
+                (long long)d->batch, (long long)d->heads, (long long)d->seqlen);
+  if (d->d_k < 16 || d->d_k > 256 || d->d_k % 16 != 0)
+    return fail(LATTN_EINVAL, "d_k = %d must be a multiple of 16 in [16, 256]", d->d_k);
+  if (d->d_v < 16 || d->d_v > 256 || d->d_v % 16 != 0)
+    return fail(LATTN_EINVAL, "d_v = %d must be a multiple of 16 in [16, 256]", d->d_v);
+  if (d->dtype != LATTN_FP32 && d->dtype != LATTN_BF16)
+    return fail(LATTN_EINVAL, "dtype = %d is neither LATTN_FP32 nor LATTN_BF16", (int)d->dtype);
+  if (d->decay_mode != LATTN_DECAY_PER_CHANNEL && d->decay_mode != LATTN_DECAY_SCALAR)
+    return fail(LATTN_EINVAL, "decay_mode = %d is not a lattn_decay_mode", (int)d->decay_mode);
+  return LATTN_OK;
+}
+
+int check_ranks(int r_ab, int r_kv) {
+  if (r_ab < 0 || r_ab > 8) return fail(LATTN_EINVAL, "r_ab = %d must be in [0, 8]", r_ab);
+  if (r_kv < 1 || r_kv > 4) return fail(LATTN_EINVAL, "r_kv = %d must be in [1, 4]", r_kv);
+  return LATTN_OK;
+}
+
+int check_chunk(int chunk, int r_ab, int r_kv) {
+  if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
+    return fail(LATTN_EINVAL, "chunk = %d must be one of 16, 32, 64, 128", chunk);
+  if (chunk * r_ab > 512)
+    return fail(LATTN_EUNSUPPORTED, "chunk * r_ab = %d exceeds 512", chunk * r_ab);
+  if (chunk * r_kv > 256)
+    return fail(LATTN_EUNSUPPORTED, "chunk * r_kv = %d exceeds 256", chunk * r_kv);
+  return LATTN_OK;
+}
+
+int check_ptr(const void* p, const char* name, bool required) {
+  if (p == nullptr) {
+    if (required) return fail(LATTN_EINVAL, "%s is NULL", name);
+    return LATTN_OK;
+  }
+  if (!aligned16(p)) return fail(LATTN_EINVAL, "%s is not 16-byte aligned", name);
+  return LATTN_OK;
+}
+
+lattn::Problem make_problem(const lattn_dims* d, int r_ab, int r_kv, int chunk) {
+  lattn::Problem p{};
+  p.BH = d->batch * d->heads;
+  p.T = d->seqlen;
+  p.dk = d->d_k;
+  p.dv = d->d_v;
+  p.r_ab = r_ab;
+  p.r_kv = r_kv;
+  p.C = chunk;
+  p.N = chunk > 0 ? (d->seqlen + chunk - 1) / chunk : 0;
+  p.scalar = d->decay_mode == LATTN_DECAY_SCALAR ? 1 : 0;
+  p.bf16 = d->dtype == LATTN_BF16 ? 1 : 0;
+  return p;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return LATTN_OK;
+}
+
+#define LATTN_TRY(expr)        \
+  do {                         \
+    const int _rc = (expr);    \
+    if (_rc != LATTN_OK) return _rc; \
+  } while (0)
+
+int check_operands(const lattn_dims* dims, const void* k, const void* v, const float* log_decay,
+                   const void* A, const void* B, int r_ab, int r_kv, int chunk) {
+  LATTN_TRY(check_dims(dims));
+  LATTN_TRY(check_ranks(r_ab, r_kv));
+  LATTN_TRY(check_chunk(chunk, r_ab, r_kv));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(k, "k", need));
+  LATTN_TRY(check_ptr(v, "v", need));
+  LATTN_TRY(check_ptr(log_decay, "log_decay", need));
+  if (r_ab == 0) {
+    if (A != nullptr || B != nullptr) return fail(LATTN_EINVAL, "A and B must be NULL when r_ab == 0");
+  } else {
+    LATTN_TRY(check_ptr(A, "A", need));
+    LATTN_TRY(check_ptr(B, "B", need));
+  }
+  return LATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lattn_version(void) { return "lattn 0.1 (gfx950)"; }
+
+const char* lattn_status_str(int status) {
+  switch (status) {
+    case LATTN_OK: return "LATTN_OK";
+    case LATTN_EINVAL: return "LATTN_EINVAL: invalid argument";
+    case LATTN_EUNSUPPORTED: return "LATTN_EUNSUPPORTED: valid but unsupported configuration";
+    case LATTN_EWORKSPACE: return "LATTN_EWORKSPACE: workspace missing or too small";
+    case LATTN_EHIP: return "LATTN_EHIP: HIP runtime error";
+    case LATTN_EDECAY_RANGE: return "LATTN_EDECAY_RANGE: chunk cumulative log-decay out of range";
+    default: return "unknown lattn status";
+  }
+}
+
+const char* lattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* lattn_chunk_fwd_kernels(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return "";
+  return "general_fp32";
+}
+
+size_t lattn_chunk_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return 0;
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  return lattn::general_plan(p).total_bytes;
+}
+
+int lattn_chunk_fwd_check(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                          const float* log_decay, const void* A, const void* B, int r_ab,
+                          int r_kv, int chunk, const void* out, const void* workspace,
+                          size_t workspace_bytes) {
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", need));
+  LATTN_TRY(check_ptr(out, "out", need));
+  if (need) {
+    const size_t ws = lattn_chunk_fwd_workspace_size(dims, r_ab, r_kv, chunk);
+    if (ws > 0 && workspace == nullptr) return fail(LATTN_EWORKSPACE, "workspace is NULL (%zu bytes needed)", ws);
+    if (workspace_bytes < ws)
+      return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
+    LATTN_TRY(check_ptr(workspace, "workspace", ws > 0));
+  }
+  return ok();
+}
+
+int lattn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                    const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                    int chunk, void* out, float* final_state, const float* initial_state,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(lattn_chunk_fwd_check(dims, q, k, v, log_decay, A, B, r_ab, r_kv, chunk, out,
+                                  workspace, workspace_bytes));
+  LATTN_TRY(check_ptr(final_state, "final_state", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  if (p.T == 0) return hip_status(lattn::launch_copy_state(p, initial_state, final_state, stream), "copy state");
+  LATTN_TRY(hip_status(lattn::general_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
+  LATTN_TRY(hip_status(lattn::general_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
+  return ok();
+}
+
+int lattn_chunk_prepare(const lattn_dims* dims, const void* q, const void* k,
+                        const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                        int chunk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(lattn_chunk_fwd_check(dims, q, k, k, log_decay, A, B, r_ab, r_kv, chunk, q, workspace,
+                                  workspace_bytes));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  if (p.T == 0) return ok();
+  LATTN_TRY(hip_status(lattn::general_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
+  return ok();
+}
+
+int lattn_chunk_scan(const lattn_dims* dims, const void* v, int r_ab, int r_kv, int chunk,
+                     void* out, float* final_state, const float* initial_state, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(check_dims(dims));
+  LATTN_TRY(check_ranks(r_ab, r_kv));
+  LATTN_TRY(check_chunk(chunk, r_ab, r_kv));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(v, "v", need));
+  LATTN_TRY(check_ptr(out, "out", need));
+  LATTN_TRY(check_ptr(final_state, "final_state", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  if (p.T == 0) return hip_status(lattn::launch_copy_state(p, initial_state, final_state, stream), "copy state");
+  const size_t ws = lattn_chunk_fwd_workspace_size(dims, r_ab, r_kv, chunk);
+  if (workspace == nullptr || workspace_bytes < ws)
+    return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
+  LATTN_TRY(check_ptr(workspace, "workspace", true));
+  LATTN_TRY(hip_status(lattn::general_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
+  return ok();
+}
+
+int lattn_chunk_summaries(const lattn_dims* dims, const void* k, const void* v,
+                          const float* log_decay, const void* A, const void* B, int r_ab,
+                          int r_kv, int chunk, float* sum_A, float* sum_B, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(sum_A, "sum_A", need));
+  LATTN_TRY(check_ptr(sum_B, "sum_B", need));
+  if (!need) return ok();
+  const size_t ws = lattn_chunk_fwd_workspace_size(dims, r_ab, r_kv, chunk);
+  if (workspace == nullptr || workspace_bytes < ws)
+    return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
+  LATTN_TRY(check_ptr(workspace, "workspace", true));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  LATTN_TRY(hip_status(lattn::general_prepare(p, nullptr, k, log_decay, A, B, workspace, stream), "prepare launch"));
+  LATTN_TRY(hip_status(lattn::general_summaries(p, workspace, v, sum_A, sum_B, stream), "summaries launch"));
+  return ok();
+}
+
+int lattn_step(const lattn_dims* dims, const void* q, const void* k, const void* v,
+               const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+               float* state, void* out, hipStream_t stream) {
+  LATTN_TRY(check_dims(dims));
+  if (dims->seqlen != 1) return fail(LATTN_EINVAL, "lattn_step needs seqlen == 1 (got %lld)", (long long)dims->seqlen);
+  LATTN_TRY(check_ranks(r_ab, r_kv));
+  LATTN_TRY(check_ptr(q, "q", true));
+  LATTN_TRY(check_ptr(k, "k", true));
+  LATTN_TRY(check_ptr(v, "v", true));
+  LATTN_TRY(check_ptr(log_decay, "log_decay", true));
+  LATTN_TRY(check_ptr(state, "state", true));
+  LATTN_TRY(check_ptr(out, "out", true));
+  if (r_ab == 0) {
+    if (A != nullptr || B != nullptr) return fail(LATTN_EINVAL, "A and B must be NULL when r_ab == 0");
+  } else {
+    LATTN_TRY(check_ptr(A, "A", true));
+    LATTN_TRY(check_ptr(B, "B", true));
+  }
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, 1);
+  LATTN_TRY(hip_status(lattn::launch_step(p, q, k, v, log_decay, A, B, state, out, stream), "step launch"));
+  return ok();
+}
+
+int lattn_hdla_params(const lattn_dims* dims, const void* k, const void* v,
+                      const float* log_lambda, const float* beta, void* A, void* B, void* V_out,
+                      hipStream_t stream) {
+  LATTN_TRY(check_dims(dims));
+  if (dims->decay_mode != LATTN_DECAY_PER_CHANNEL)
+    return fail(LATTN_EINVAL, "lattn_hdla_params needs LATTN_DECAY_PER_CHANNEL");
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(k, "k", need));
+  LATTN_TRY(check_ptr(v, "v", need));
+  LATTN_TRY(check_ptr(log_lambda, "log_lambda", need));
+  LATTN_TRY(check_ptr(beta, "beta", need));
+  LATTN_TRY(check_ptr(A, "A", need));
+  LATTN_TRY(check_ptr(B, "B", need));
+  LATTN_TRY(check_ptr(V_out, "V_out", need));
+  const lattn::Problem p = make_problem(dims, 2, 1, 1);
+  LATTN_TRY(hip_status(lattn::launch_hdla_params(p, k, v, log_lambda, beta, A, B, V_out, stream), "hdla params launch"));
+  return ok();
+}
+
+int lattn_gdn_params(const lattn_dims* dims, const void* k, const void* v, const float* g,
+                     const float* beta, void* A, void* B, void* V_out, hipStream_t stream) {
+  LATTN_TRY(check_dims(dims));
+  if (dims->decay_mode != LATTN_DECAY_SCALAR)
+    return fail(LATTN_EINVAL, "lattn_gdn_params needs LATTN_DECAY_SCALAR");
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(k, "k", need));
+  LATTN_TRY(check_ptr(v, "v", need));
+  LATTN_TRY(check_ptr(g, "g", need));
+  LATTN_TRY(check_ptr(beta, "beta", need));
+  LATTN_TRY(check_ptr(A, "A", need));
+  LATTN_TRY(check_ptr(B, "B", need));
+  LATTN_TRY(check_ptr(V_out, "V_out", need));
+  const lattn::Problem p = make_problem(dims, 1, 1, 1);
+  LATTN_TRY(hip_status(lattn::launch_gdn_params(p, k, v, g, beta, A, B, V_out, stream), "gdn params launch"));
+  return ok();
+}
+
+int lattn_decay_range(const lattn_dims* dims, const float* log_decay, int chunk, float* chunk_max,
+                      hipStream_t stream) {
+  LATTN_TRY(check_dims(dims));
+  LATTN_TRY(check_chunk(chunk, 0, 1));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(log_decay, "log_decay", need));
+  LATTN_TRY(check_ptr(chunk_max, "chunk_max", need));
+  const lattn::Problem p = make_problem(dims, 0, 1, chunk);
+  LATTN_TRY(hip_status(lattn::launch_decay_range(p, log_decay, chunk_max, stream), "decay range launch"));
+  return ok();
+}
+
+int lattn_check_decay_range(const lattn_dims* dims, const float* log_decay, int chunk,
+                            float* scratch, hipStream_t stream) {
+  LATTN_TRY(lattn_decay_range(dims, log_decay, chunk, scratch, stream));
+  const lattn::Problem p = make_problem(dims, 0, 1, chunk);
+  const size_t n = static_cast<size_t>(p.BH * p.N);
+  if (n == 0) return ok();
+  std::vector<float> host(n);
+  LATTN_TRY(hip_status(hipMemcpyAsync(host.data(), scratch, n * sizeof(float), hipMemcpyDeviceToHost, stream), "copy chunk maxima"));
+  LATTN_TRY(hip_status(hipStreamSynchronize(stream), "synchronize"));
+  float m = 0.f;
+  for (float x : host) m = x > m ? x : m;
+  if (!(m <= LATTN_MAX_CHUNK_LOG_DECAY))
+    return fail(LATTN_EDECAY_RANGE, "chunk cumulative -log-decay reaches %g (limit %g)", (double)m,
+                (double)LATTN_MAX_CHUNK_LOG_DECAY);
+  return ok();
+}
+
+}  // extern "C"

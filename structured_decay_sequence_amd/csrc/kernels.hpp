@@ -1,0 +1,56 @@
+// Launch interface between the C ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lattn {
+
+// One chunk-wise problem, with every size the kernels need.
+struct Problem {
+  int64_t BH;      // batch * heads
+  int64_t T;       // tokens per (batch, head)
+  int dk, dv;
+  int r_ab, r_kv;
+  int C;           // chunk length
+  int64_t N;       // chunks per (batch, head) = ceil(T / C)
+  int scalar;      // 1: log_decay is [BH, T]; 0: [BH, T, dk]
+  int bf16;        // 1: q, K, V, A, B, out are bf16; 0: fp32
+  __host__ __device__ int na() const { return C * r_ab; }
+  __host__ __device__ int nk() const { return C * r_kv; }
+  // Chunk operator M_j = [[Acal, Z], [Qbar, R]] is (dk + C) x (dk + nk).
+  __host__ __device__ int mrows() const { return dk + C; }
+  __host__ __device__ int mcols() const { return dk + C * r_kv; }
+};
+
+// Workspace plan of the general (fp32-internal) path.
+struct GeneralPlan {
+  int slots;              // number of per-workgroup scratch slots of the prepare kernel
+  size_t slot_floats;     // floats per slot
+  size_t m_bytes;         // bytes of the chunk-operator buffer
+  size_t total_bytes;
+};
+
+GeneralPlan general_plan(const Problem& p);
+
+// General path: every shape the ABI accepts, fp32 internally.
+hipError_t general_prepare(const Problem& p, const void* q, const void* k, const float* ld,
+                           const void* A, const void* B, void* workspace, hipStream_t s);
+hipError_t general_scan(const Problem& p, const void* workspace, const void* v, void* out,
+                        float* Sfin, const float* S0, hipStream_t s);
+hipError_t general_summaries(const Problem& p, const void* workspace, const void* v, float* sumA,
+                             float* sumB, hipStream_t s);
+
+hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
+                       const float* ld, const void* A, const void* B, float* state, void* out,
+                       hipStream_t s);
+hipError_t launch_hdla_params(const Problem& p, const void* k, const void* v,
+                              const float* log_lambda, const float* beta, void* A, void* B,
+                              void* V_out, hipStream_t s);
+hipError_t launch_gdn_params(const Problem& p, const void* k, const void* v, const float* g,
+                             const float* beta, void* A, void* B, void* V_out, hipStream_t s);
+hipError_t launch_decay_range(const Problem& p, const float* ld, float* chunk_max, hipStream_t s);
+hipError_t launch_copy_state(const Problem& p, const float* S0, float* Sfin, hipStream_t s);
+
+}  // namespace lattn

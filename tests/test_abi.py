@@ -1,0 +1,112 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+entry point, and its host-side validation rejects bad arguments before any
+launch (only the pure host functions are called here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from structured_decay_sequence_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "lattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["lattn_chunk_fwd", "lattn_step", "lattn_chunk_fwd_workspace_size", "lattn_status_str",
+              "lattn_last_error", "lattn_chunk_summaries", "lattn_hdla_params", "lattn_gdn_params",
+              "lattn_check_decay_range", "lattn_decay_range", "lattn_chunk_fwd_check", "lattn_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks a signature for {name}"
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in [0, -1, -2, -3, -4, -5]:
+        assert lib.lattn_status_str(code)
+    assert b"unknown" in lib.lattn_status_str(-99)
+    assert lib.lattn_version().startswith(b"lattn")
+
+
+def _dims(**kw):
+    d = dict(batch=1, heads=2, seqlen=128, d_k=64, d_v=64, dtype=_lib.LATTN_BF16,
+             decay_mode=_lib.LATTN_DECAY_PER_CHANNEL)
+    d.update(kw)
+    return _lib.lattn_dims(d["batch"], d["heads"], d["seqlen"], d["d_k"], d["d_v"], d["dtype"],
+                           d["decay_mode"])
+
+
+FAKE = 0x100000  # never dereferenced: validation only tests NULL and alignment
+
+
+def _check(dims, r_ab=2, r_kv=1, chunk=64, ws_bytes=None, **ptrs):
+    lib = _lib.load()
+    p = {n: FAKE for n in ["q", "k", "v", "ld", "A", "B", "out", "ws"]}
+    if r_ab == 0:
+        p["A"] = p["B"] = None
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.lattn_chunk_fwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk)
+    return lib.lattn_chunk_fwd_check(ctypes.byref(dims), p["q"], p["k"], p["v"], p["ld"], p["A"], p["B"],
+                                     r_ab, r_kv, chunk, p["out"], p["ws"], ws_bytes)
+
+
+def test_valid_arguments_pass():
+    assert _check(_dims()) == _lib.LATTN_OK
+    assert _check(_dims(dtype=_lib.LATTN_FP32, decay_mode=_lib.LATTN_DECAY_SCALAR), r_ab=1) == _lib.LATTN_OK
+    assert _check(_dims(), r_ab=0, r_kv=2, chunk=16) == _lib.LATTN_OK
+    assert _check(_dims(seqlen=0), q=None, k=None, v=None, ld=None, A=None, B=None, out=None, ws=None,
+                  ws_bytes=0) == _lib.LATTN_OK
+
+
+@pytest.mark.parametrize("kw,args,code", [
+    (dict(d_k=24), {}, _lib.LATTN_EINVAL),
+    (dict(d_k=272), {}, _lib.LATTN_EINVAL),
+    (dict(d_v=8), {}, _lib.LATTN_EINVAL),
+    (dict(batch=0), {}, _lib.LATTN_EINVAL),
+    (dict(seqlen=-1), {}, _lib.LATTN_EINVAL),
+    (dict(dtype=7), {}, _lib.LATTN_EINVAL),
+    (dict(decay_mode=3), {}, _lib.LATTN_EINVAL),
+    ({}, dict(chunk=48), _lib.LATTN_EINVAL),
+    ({}, dict(r_ab=-1), _lib.LATTN_EINVAL),
+    ({}, dict(r_kv=0), _lib.LATTN_EINVAL),
+    ({}, dict(r_ab=8, chunk=128), _lib.LATTN_EUNSUPPORTED),
+    ({}, dict(r_kv=4, chunk=128), _lib.LATTN_EUNSUPPORTED),
+    ({}, dict(q=None), _lib.LATTN_EINVAL),
+    ({}, dict(A=None), _lib.LATTN_EINVAL),
+    ({}, dict(r_ab=0), _lib.LATTN_OK),
+    ({}, dict(v=FAKE + 2), _lib.LATTN_EINVAL),
+    ({}, dict(ws=None), _lib.LATTN_EWORKSPACE),
+    ({}, dict(ws_bytes=16), _lib.LATTN_EWORKSPACE),
+])
+def test_invalid_arguments_are_rejected(kw, args, code):
+    rc = _check(_dims(**kw), **args)
+    assert rc == code, (rc, _lib.last_error())
+    if code != _lib.LATTN_OK:
+        assert _lib.last_error()
+
+
+def test_ab_must_be_null_without_decay_rank():
+    assert _check(_dims(), r_ab=0, A=FAKE, B=FAKE) == _lib.LATTN_EINVAL
+
+
+def test_workspace_size_is_zero_for_invalid_and_grows_with_length():
+    lib = _lib.load()
+    bad = _dims(d_k=20)
+    assert lib.lattn_chunk_fwd_workspace_size(ctypes.byref(bad), 2, 1, 64) == 0
+    a = lib.lattn_chunk_fwd_workspace_size(ctypes.byref(_dims(seqlen=256)), 2, 1, 64)
+    b = lib.lattn_chunk_fwd_workspace_size(ctypes.byref(_dims(seqlen=512)), 2, 1, 64)
+    assert 0 < a < b
