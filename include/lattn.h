@@ -140,12 +140,15 @@ int lattn_chunk_scan(const lattn_dims* dims, const void* v, int r_ab, int r_kv, 
  * "Affine maps and closure under composition"): after chunk j,
  * S_j = sum_A[j] S_{j-1} + sum_B[j].  Inputs as lattn_chunk_fwd (q unused).
  *   sum_A [B,H,N,d_k,d_k] fp32, sum_B [B,H,N,d_k,d_v] fp32, N = ceil(T/C).
- * Needs the same workspace as lattn_chunk_fwd.
+ * Needs lattn_chunk_summaries_workspace_size() bytes of workspace.
  */
 int lattn_chunk_summaries(const lattn_dims* dims, const void* k, const void* v,
                           const float* log_decay, const void* A, const void* B, int r_ab,
                           int r_kv, int chunk, float* sum_A, float* sum_B, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lattn_chunk_summaries needs (0 on invalid arguments). */
+size_t lattn_chunk_summaries_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
 
 /*
  * lattn_step -- one recurrent token for decoding (HLA note, "Reproduction":

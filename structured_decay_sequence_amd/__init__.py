@@ -152,7 +152,7 @@ def chunk_summaries(k, v, log_decay, A=None, B=None, chunk: int = 64):
     sB = torch.empty((Bb, H, N, dk, dv), dtype=torch.float32, device=k.device)
     lib = _lib.load()
     dims = make_dims(Bb, H, T, dk, dv, _dtype_code(k), scalar)
-    ws_bytes = int(lib.lattn_chunk_fwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk))
+    ws_bytes = int(lib.lattn_chunk_summaries_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk))
     ws = _workspace(k.device, ws_bytes)
     rc = lib.lattn_chunk_summaries(ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A),
                                    _ptr(B), r_ab, r_kv, chunk, _ptr(sA), _ptr(sB), _ptr(ws),

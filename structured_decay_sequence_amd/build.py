@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
     # Packed fp32 VALU ops are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA sources and results stay in ordinary VGPRs (no accumulation-register
+    # forms): the solve feeds MFMA results straight back in as B operands.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

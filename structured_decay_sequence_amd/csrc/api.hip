@@ -115,6 +115,18 @@ int check_operands(const lattn_dims* dims, const void* k, const void* v, const f
   return LATTN_OK;
 }
 
+hipError_t run_prepare(const lattn::Problem& p, const void* q, const void* k, const float* ld,
+                       const void* A, const void* B, void* ws, hipStream_t s) {
+  if (lattn::fast_supported(p)) return lattn::fast_prepare(p, q, k, ld, A, B, ws, s);
+  return lattn::general_prepare(p, q, k, ld, A, B, ws, s);
+}
+
+hipError_t run_scan(const lattn::Problem& p, void* ws, const void* v, void* out, float* Sfin,
+                    const float* S0, hipStream_t s) {
+  if (lattn::fast_supported(p)) return lattn::fast_scan(p, ws, v, out, Sfin, S0, s);
+  return lattn::general_scan(p, ws, v, out, Sfin, S0, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,7 +151,7 @@ const char* lattn_chunk_fwd_kernels(const lattn_dims* dims, int r_ab, int r_kv, 
   if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
       check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
     return "";
-  return "general_fp32";
+  return lattn::fast_supported(make_problem(dims, r_ab, r_kv, chunk)) ? "mfma_bf16" : "general_fp32";
 }
 
 size_t lattn_chunk_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
@@ -147,7 +159,14 @@ size_t lattn_chunk_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv
       check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
     return 0;
   const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
-  return lattn::general_plan(p).total_bytes;
+  return lattn::fast_supported(p) ? lattn::fast_workspace_bytes(p) : lattn::general_plan(p).total_bytes;
+}
+
+size_t lattn_chunk_summaries_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return 0;
+  return lattn::general_plan(make_problem(dims, r_ab, r_kv, chunk)).total_bytes;
 }
 
 int lattn_chunk_fwd_check(const lattn_dims* dims, const void* q, const void* k, const void* v,
@@ -178,8 +197,8 @@ int lattn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const 
   LATTN_TRY(check_ptr(initial_state, "initial_state", false));
   const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
   if (p.T == 0) return hip_status(lattn::launch_copy_state(p, initial_state, final_state, stream), "copy state");
-  LATTN_TRY(hip_status(lattn::general_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
-  LATTN_TRY(hip_status(lattn::general_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
+  LATTN_TRY(hip_status(run_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
+  LATTN_TRY(hip_status(run_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
   return ok();
 }
 
@@ -190,7 +209,7 @@ int lattn_chunk_prepare(const lattn_dims* dims, const void* q, const void* k,
                                   workspace_bytes));
   const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
   if (p.T == 0) return ok();
-  LATTN_TRY(hip_status(lattn::general_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
+  LATTN_TRY(hip_status(run_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
   return ok();
 }
 
@@ -211,7 +230,7 @@ int lattn_chunk_scan(const lattn_dims* dims, const void* v, int r_ab, int r_kv, 
   if (workspace == nullptr || workspace_bytes < ws)
     return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
   LATTN_TRY(check_ptr(workspace, "workspace", true));
-  LATTN_TRY(hip_status(lattn::general_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
+  LATTN_TRY(hip_status(run_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
   return ok();
 }
 
@@ -224,7 +243,7 @@ int lattn_chunk_summaries(const lattn_dims* dims, const void* k, const void* v,
   LATTN_TRY(check_ptr(sum_A, "sum_A", need));
   LATTN_TRY(check_ptr(sum_B, "sum_B", need));
   if (!need) return ok();
-  const size_t ws = lattn_chunk_fwd_workspace_size(dims, r_ab, r_kv, chunk);
+  const size_t ws = lattn_chunk_summaries_workspace_size(dims, r_ab, r_kv, chunk);
   if (workspace == nullptr || workspace_bytes < ws)
     return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
   LATTN_TRY(check_ptr(workspace, "workspace", true));

@@ -57,6 +57,41 @@ def test_generic_parity(case):
     assert rel_err(S, ref_S) <= TOL[dtype]
 
 
+# Shapes the bf16 MFMA path takes (C = 64, r_kv = 1, r_ab in {1, 2}, d_k in {64, 128},
+# d_v a multiple of 64): ragged tails, a sequence shorter than one chunk, both decay
+# modes, batch*heads not a multiple of 8, and wide d_v.
+FAST_CASES = [
+    # B, H, T, dk, dv, r_ab, decay
+    (1, 3, 200, 128, 128, 2, "channel"),
+    (1, 2, 64, 128, 128, 2, "channel"),
+    (2, 1, 37, 128, 64, 2, "channel"),
+    (1, 2, 300, 128, 128, 1, "scalar"),
+    (1, 2, 150, 128, 128, 1, "channel"),
+    (1, 5, 257, 64, 64, 2, "channel"),
+    (1, 2, 100, 64, 64, 1, "scalar"),
+    (3, 3, 130, 64, 128, 2, "channel"),
+    (1, 2, 129, 128, 256, 2, "channel"),
+    (1, 9, 128, 128, 192, 1, "channel"),
+]
+
+
+@pytest.mark.parametrize("case", FAST_CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}{}".format(*c))
+def test_mfma_path_parity(case):
+    Bb, H, T, dk, dv, r_ab, decay = case
+    print(f"mfma case {case}", flush=True)
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, r_ab, 1, "bf16", decay, seed=3 * T + dk)
+    dims = lattn.make_dims(Bb, H, T, dk, dv, 1, decay == "scalar")
+    import ctypes
+    assert lattn._lib.load().lattn_chunk_fwd_kernels(ctypes.byref(dims), r_ab, 1, 64) == b"mfma_bf16"
+    S0 = (np.random.default_rng(7).standard_normal((Bb, H, dk, dv)) * 0.1).astype(np.float32)
+    out, S = _gpu_generic(raw, "bf16", 64, S0)
+    ref_out, ref_S = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"],
+                                    initial_state=S0)
+    e_o, e_s = rel_err(out, ref_out), rel_err(S, ref_S)
+    print(f"out {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+
+
 def _hdla_ref_inputs(raw, dtype):
     ll, A, B, K, V = oracle.hdla_to_generic(raw["k"], raw["v"], raw["log_lambda"], raw["beta"])
     return dict(q=raw["q"], log_decay=raw["log_lambda"], A=store_like(A, dtype), B=store_like(B, dtype),
