@@ -33,6 +33,15 @@ constexpr int kNK = 64;   // C * r_kv
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier that orders LDS only.  The waves of these kernels talk to
+// each other through LDS alone, so a barrier need not wait for in-flight
+// global loads (the register prefetch of the next chunk stays in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -79,9 +88,9 @@ struct PrepCfg {
   static constexpr int ROUT = DK + kC;           // operator output height
   static constexpr int KT = KIN / 16;
   static constexpr int MT = ROUT / 16;
-  static constexpr int NW = KIN / 32;            // two input tiles per wave
+  static constexpr int NW = KT;                  // one wave per 16-column input tile
   static constexpr int NT = 64 * NW;
-  static constexpr int WW = DK / 32;             // waves owning W columns
+  static constexpr int TPW = 1;
   static constexpr int LD = DK + 8;              // padded row of Xl / Xr (bf16)
   static constexpr int LDA = NA + 8;             // padded row of At^T and M_A (bf16)
   // LDS regions (bytes)
@@ -116,104 +125,184 @@ struct FastPrepArgs {
 template <int DK, int RAB>
 __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(FastPrepArgs a) {
   using Cfg = PrepCfg<DK, RAB>;
-  constexpr int NA = Cfg::NA, NB = Cfg::NB, LD = Cfg::LD, LDA = Cfg::LDA, NW = Cfg::NW;
-  constexpr int MT = Cfg::MT, KT = Cfg::KT, WW = Cfg::WW;
+  constexpr int NA = Cfg::NA, NB = Cfg::NB, LD = Cfg::LD, LDA = Cfg::LDA, NW = Cfg::NW, NT = Cfg::NT;
+  constexpr int MT = Cfg::MT, KT = Cfg::KT, TPW = Cfg::TPW;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* Xl = reinterpret_cast<__bf16*>(smem);                      // [B~ ; Q~]   rows x LD
-  __bf16* AT = Cfg::AT_OVER_B ? Xl                                   // A~^T        DK x LDA (after GEMM1)
-                              : reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::R3 + Cfg::R4);
   __bf16* Xr = reinterpret_cast<__bf16*>(smem + Cfg::R1);            // [A~ ; K~]   rows x LD
   float* G = reinterpret_cast<float*>(smem + Cfg::R1 + Cfg::R2);     // C x DK (or C) cumulative log-decay
   float* Ldg = G;                                                    // NB x 16 x 16 fp32 diagonal blocks
   __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::LDIAG);  // -L blocks below the diagonal
   __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::LDIAG + Cfg::LPACK);  // M_A  C x LDA
   float* eGC = reinterpret_cast<float*>(smem + Cfg::R1 + Cfg::R2 + Cfg::R3);                   // exp(G_C) per channel
+  __bf16* AT = Cfg::AT_OVER_B ? Xl                                   // A~^T        DK x LDA (after the solve)
+                              : reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::R3 + Cfg::R4);
 
   const Problem& p = a.p;
   const int tid = threadIdx.x;
+  const bool scalar = p.scalar != 0;
+  const int64_t total = p.BH * p.N;
+
+  // Raw inputs are staged in registers: q, K and the log-decay one chunk ahead
+  // (prefetch), the decay operands A, B at the top of each chunk (fetch_ab).
+  constexpr int CG = DK / 8;                                       // 8-channel groups per row
+  constexpr int QK_ITEMS = (kC + kNK) * CG;                        // q rows, then K rows
+  constexpr int QK_IT = (QK_ITEMS + NT - 1) / NT;
+  constexpr int AB_ITEMS = 2 * NA * CG;                            // B rows, then A rows
+  constexpr int AB_IT = (AB_ITEMS + NT - 1) / NT;
+  constexpr int LITEMS = kC * DK / 4;                              // log-decay float4s (per channel)
+  constexpr int LIT = (LITEMS + NT - 1) / NT;
+  bf16x8 qkbuf[QK_IT];
+  bf16x8 abbuf[AB_IT];
+  f32x4 lbuf[LIT];
+  float lscal = 0.f;
+
+  auto chunk_n = [&](int64_t jb, int64_t& tok0) {
+    const int64_t bh = jb / p.N, jc = jb % p.N;
+    const int64_t t0 = jc * kC;
+    tok0 = bh * p.T + t0;
+    return static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
+  };
+  // Loads are unconditional (an invalid item reads the chunk's first row, which
+  // always exists) so that no branch waits on them; the consumer zeroes the
+  // items of padded tokens.
+  auto prefetch = [&](int64_t jb) {
+    int64_t tok0;
+    const int n = chunk_n(jb, tok0);
+#pragma unroll
+    for (int q = 0; q < QK_IT; ++q) {
+      const int it = tid + q * NT;
+      const int row = it / CG, cg = it % CG;
+      const int t = row < kC ? row : row - kC;
+      const bool ok = it < QK_ITEMS && t < n;
+      const __bf16* src = (row < kC ? a.q : a.k) + (tok0 + (ok ? t : 0)) * DK + (ok ? cg : 0) * 8;
+      qkbuf[q] = *reinterpret_cast<const bf16x8*>(src);
+    }
+    if (!scalar) {
+#pragma unroll
+      for (int q = 0; q < LIT; ++q) {
+        const int e4 = tid + q * NT;
+        const bool ok = e4 < LITEMS && (e4 * 4) / DK < n;
+        lbuf[q] = *reinterpret_cast<const f32x4*>(a.ld + tok0 * DK + (ok ? e4 * 4 : 0));
+      }
+    } else {
+      lscal = a.ld[tok0 + (tid < n ? tid : 0)];
+    }
+  };
+  auto fetch_ab = [&](int64_t jb) {
+    int64_t tok0;
+    const int n = chunk_n(jb, tok0);
+#pragma unroll
+    for (int q = 0; q < AB_IT; ++q) {
+      const int it = tid + q * NT;
+      const int row = it / CG, cg = it % CG;
+      const int r = row < NA ? row : row - NA;
+      const int t = r / RAB;
+      const bool ok = it < AB_ITEMS && t < n;
+      const __bf16* src = (row < NA ? a.B : a.A) +
+                          ((tok0 + (ok ? t : 0)) * RAB + (ok ? r % RAB : 0)) * DK + (ok ? cg : 0) * 8;
+      abbuf[q] = *reinterpret_cast<const bf16x8*>(src);
+    }
+  };
+
+  // One workgroup per chunk: every load of the chunk is issued up front.
+  const int64_t job = blockIdx.x;
+  if (job >= total) return;
+  prefetch(job);
+  {
+  int64_t tok0_cur;
+  const int ncur = chunk_n(job, tok0_cur);   // tokens of this chunk (the rest are padding)
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int64_t job = blockIdx.x;
-  const int64_t bh = job / p.N;
-  const int64_t j = job % p.N;
-  const int64_t t0 = j * kC;
-  const int n = static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
-  const int64_t tok0 = bh * p.T + t0;
-  const bool scalar = p.scalar != 0;
-
+  // Wave w owns input tiles kt0 .. kt0 + ntw - 1; a tile below DK/16 is a "W"
+  // tile (channel columns), the others are "X" tiles (chunk-write rows).
+  const int ntw = TPW;
+  const int kt0 = TPW * wave;
+  fetch_ab(job);
   // ---- P0: chunk-local inclusive cumulative log-decay (padded tokens add 0).
   if (!scalar) {
-    for (int i = tid; i < DK; i += Cfg::NT) {
+#pragma unroll
+    for (int q = 0; q < LIT; ++q) {
+      const int e4 = tid + q * NT;
+      if (e4 < LITEMS) *reinterpret_cast<f32x4*>(G + e4 * 4) = (e4 * 4) / DK < ncur ? lbuf[q] : zero4();
+    }
+    lds_barrier();
+    for (int i = tid; i < DK; i += NT) {
       float g = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < kC; ++t) {
-        const float l = t < n ? a.ld[(tok0 + t) * DK + i] : 0.f;
-        g += l;
-        G[t * DK + i] = g;
+#pragma unroll
+      for (int t0 = 0; t0 < kC; t0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) v[t] = G[(t0 + t) * DK + i];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          g += v[t];
+          G[(t0 + t) * DK + i] = g;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       eGC[i] = __expf(g);
     }
-  } else if (wave == 0) {
-    float g = lane < n ? a.ld[tok0 + lane] : 0.f;
+  } else {
+    if (wave == 0) {
+      float g = lane < ncur ? lscal : 0.f;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(g, off, 64);
-      if (lane >= off) g += o;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(g, off, 64);
+        if (lane >= off) g += o;
+      }
+      G[lane] = g;
+      const float gc = __shfl(g, 63, 64);
+      for (int i = lane; i < DK; i += 64) eGC[i] = __expf(gc);
     }
-    G[lane] = g;
-    const float gc = __shfl(g, 63, 64);
-    for (int i = lane; i < DK; i += 64) eGC[i] = __expf(gc);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P1: decay-scaled bf16 operands.  Xl = [B~ ; Q~], Xr = [A~ ; K~].
-  {
-    constexpr int CG = DK / 8;
-    constexpr int ITEMS = (Cfg::XL_ROWS + Cfg::XR_ROWS) * CG;
-    for (int it = tid; it < ITEMS; it += Cfg::NT) {
+  //      B~ = B (.) exp(G_{t-1}), Q~ = q (.) exp(G_t), A~ = A (.) exp(-G_t), K~ = K (.) exp(-G_t).
+  auto scale_store = [&](const bf16x8& raw, int gt, float sign, int cg, __bf16* dst, bool valid) {
+    float g[8];
+    if (gt < 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = 0.f;
+    } else if (scalar) {
+      const float gs = G[gt];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = gs;
+    } else {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + gt * DK + cg * 8);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + gt * DK + cg * 8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g[e] = g0[e];
+        g[e + 4] = g1[e];
+      }
+    }
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(valid ? (float)raw[e] * __expf(sign * g[e]) : 0.f);
+    *reinterpret_cast<bf16x8*>(dst + cg * 8) = out;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int q = 0; q < QK_IT; ++q) {
+    const int it = tid + q * NT;
+    if (it < QK_ITEMS) {
       const int row = it / CG, cg = it % CG;
-      const __bf16* src;
-      int t, gt, sign;        // token, cumulative-decay row to use (-1: none), exponent sign
-      __bf16* dst;
-      if (row < NA) {                         // B~ = B (.) exp(G_{t-1})
-        t = row / RAB;
-        src = a.B + ((tok0 + t) * RAB + (row % RAB)) * DK;
-        gt = t - 1; sign = 1; dst = Xl + row * LD;
-      } else if (row < NA + kC) {             // Q~ = q (.) exp(G_t)
-        t = row - NA;
-        src = a.q + (tok0 + t) * DK;
-        gt = t; sign = 1; dst = Xl + row * LD;
-      } else if (row < 2 * NA + kC) {         // A~ = A (.) exp(-G_t)
-        const int r = row - NA - kC;
-        t = r / RAB;
-        src = a.A + ((tok0 + t) * RAB + (r % RAB)) * DK;
-        gt = t; sign = -1; dst = Xr + r * LD;
-      } else {                                // K~ = K (.) exp(-G_t)
-        const int r = row - 2 * NA - kC;
-        t = r;
-        src = a.k + (tok0 + t) * DK;
-        gt = t; sign = -1; dst = Xr + (NA + r) * LD;
-      }
-      bf16x8 out;
-      if (t < n) {
-        const bf16x8 raw = *reinterpret_cast<const bf16x8*>(src + cg * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float g = 0.f;
-          if (gt >= 0) g = scalar ? G[gt] : G[gt * DK + cg * 8 + e];
-          out[e] = (__bf16)((float)raw[e] * __expf(sign > 0 ? g : -g));
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = (__bf16)0.f;
-      }
-      *reinterpret_cast<bf16x8*>(dst + cg * 8) = out;
+      if (row < kC) scale_store(qkbuf[q], row, 1.f, cg, Xl + (NA + row) * LD, row < ncur);
+      else scale_store(qkbuf[q], row - kC, -1.f, cg, Xr + (NA + row - kC) * LD, row - kC < ncur);
     }
   }
-  __syncthreads();
-
-  const bool wrole = wave < WW;          // owns W columns (channels) or X columns (chunk write rows)
-  const int kt0 = 2 * wave;              // first of the wave's two input tiles
+#pragma unroll
+  for (int q = 0; q < AB_IT; ++q) {
+    const int it = tid + q * NT;
+    if (it < AB_ITEMS) {
+      const int row = it / CG, cg = it % CG;
+      if (row < NA) scale_store(abbuf[q], row / RAB - 1, 1.f, cg, Xl + row * LD, row / RAB < ncur);
+      else scale_store(abbuf[q], (row - NA) / RAB, -1.f, cg, Xr + (row - NA) * LD, (row - NA) / RAB < ncur);
+    }
+  }
+  lds_barrier();
 
   // ---- P2: Gram blocks.  (a) P^T = A~ [B~ ; Q~]^T, tiles (rs, cs), cs >= rs,
   //      split over all waves and written straight to LDS region 3.
@@ -257,7 +346,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P3: fp32 inverses of the unit lower-triangular diagonal blocks
   //      (I + L_ii), in place.
@@ -273,32 +362,34 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
 #pragma unroll
         for (int m = 0; m < r; ++m) v -= Lb[r * 16 + m] * x[m];
         x[r] = v;
+        __builtin_amdgcn_sched_barrier(0);  // one row of loads in flight at a time
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (active) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) Ldg[blk * 256 + r * 16 + c] = x[r];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P4: blocked forward substitution on this wave's columns:
   //      WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
-  bf16x4 wx[NB][2];
+  bf16x4 wx[NB][TPW];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    f32x4 acc[2];
-    if (wrole) {
-      // W columns: B~ itself (4 rows of one channel column per lane).
+    f32x4 acc[TPW];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        acc[u] = to_f32x4(lds_col4(Xl + (i * 16 + 4 * lg) * LD + (kt0 + u) * 16 + lr, LD));
-    } else {
-      // X columns: L_K = B~ K~^T on this block of rows, token(row) > chunk-write row.
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int x = kt0 + u - DK / 16;
+    for (int u = 0; u < TPW; ++u) {
+      const int kt = kt0 + u;
+      if (u >= ntw) {
+        acc[u] = zero4();
+      } else if (kt < DK / 16) {
+        // W columns: B~ itself (4 rows of one channel column per lane).
+        acc[u] = to_f32x4(lds_col4(Xl + (i * 16 + 4 * lg) * LD + kt * 16 + lr, LD));
+      } else {
+        // X columns: L_K = B~ K~^T on this block of rows, token(row) > chunk-write row.
+        const int x = kt - DK / 16;
         f32x4 g = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
@@ -320,34 +411,40 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
     for (int jb = 0; jb + 1 < i; jb += 2) {
       const bf16x8 av = cat(lds4(Lrow + jb * 256), lds4(Lrow + (jb + 1) * 256));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) acc[u] = mfma32(av, cat(wx[jb][u], wx[jb + 1][u]), acc[u]);
+      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(av, cat(wx[jb][u], wx[jb + 1][u]), acc[u]);
     }
     if (i % 2 == 1) {
-      const bf16x4 av = lds4(Lrow + (i - 1) * 256);
+      // Odd leftover block: padded to a 16x16x32 product with a zero half.  The
+      // K=16 instruction is kept out of this chain: interleaved with the K=32
+      // products it gave run-to-run differences in the last blocks.
+      bf16x4 zb;
+      zb[0] = zb[1] = zb[2] = zb[3] = (__bf16)0.f;
+      const bf16x8 av = cat(lds4(Lrow + (i - 1) * 256), zb);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) acc[u] = mfma16(av, wx[i - 1][u], acc[u]);
+      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(av, cat(wx[i - 1][u], zb), acc[u]);
     }
     const float* Dv = Ldg + i * 256 + lr * 16 + 4 * lg;
     float dv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) dv[e] = Dv[e];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < TPW; ++u) {
       f32x4 o = zero4();
 #pragma unroll
       for (int e = 0; e < 4; ++e) o = mfma_f32(dv[e], acc[u][e], o);
       wx[i][u] = to_bf16x4(o);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- A~^T (B~ rows of Xl are dead once every wave has finished its solve).
-  __syncthreads();
+  lds_barrier();
   for (int it = tid; it < DK * (NA / 4); it += Cfg::NT) {
     const int i = it % DK, s4 = it / DK;
     const bf16x4 v = lds_col4(Xr + (s4 * 4) * LD + i, LD);
     *reinterpret_cast<bf16x4*>(AT + i * LDA + s4 * 4) = v;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P5: operator tiles, transposed product: rows = this wave's input
   //      columns, columns = output rows m (channels, then tokens):
@@ -357,20 +454,23 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
 #pragma unroll 1
   for (int mt = 0; mt < DK / 16; ++mt) {
     const __bf16* Brow = AT + (mt * 16 + lr) * LDA;
-    f32x4 acc[2] = {zero4(), zero4()};
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u] = zero4();
 #pragma unroll
     for (int jb = 0; jb < NB; jb += 2) {
       const bf16x8 bv = cat(lds4(Brow + jb * 16 + 4 * lg), lds4(Brow + (jb + 1) * 16 + 4 * lg));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) acc[u] = mfma32(cat(wx[jb][u], wx[jb + 1][u]), bv, acc[u]);
+      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(cat(wx[jb][u], wx[jb + 1][u]), bv, acc[u]);
     }
     const int m = mt * 16 + lr;
     const float sc = eGC[m];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < TPW; ++u) {
       const int kt = kt0 + u;
+      if (u >= ntw) continue;
       f32x4 base;
-      if (wrole) {
+      if (kt < DK / 16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) base[e] = (kt * 16 + 4 * lg + e == m) ? 1.f : 0.f;
       } else {
@@ -387,18 +487,21 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
   for (int tt = 0; tt < kC / 16; ++tt) {
     const int mt = DK / 16 + tt;
     const __bf16* Brow = MAs + (tt * 16 + lr) * LDA;
-    f32x4 acc[2] = {zero4(), zero4()};
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u] = zero4();
 #pragma unroll
     for (int jb = 0; jb < NB; jb += 2) {
       const bf16x8 bv = cat(lds4(Brow + jb * 16 + 4 * lg), lds4(Brow + (jb + 1) * 16 + 4 * lg));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) acc[u] = mfma32(cat(wx[jb][u], wx[jb + 1][u]), bv, acc[u]);
+      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(cat(wx[jb][u], wx[jb + 1][u]), bv, acc[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < TPW; ++u) {
       const int kt = kt0 + u;
+      if (u >= ntw) continue;
       f32x4 base;
-      if (wrole) {
+      if (kt < DK / 16) {
         base = to_f32x4(lds4(Xl + (NA + tt * 16 + lr) * LD + kt * 16 + 4 * lg));
       } else {
         // M_K^T = K~ Q~^T on (chunk-write rows of this tile) x (tokens of tt), t >= s.
@@ -423,6 +526,9 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
       for (int e = 0; e < 4; ++e) v[e] = base[e] - acc[u][e];
       *reinterpret_cast<bf16x4*>(Mout + (mt * KT + kt) * 256 + lane * 4) = to_bf16x4(v);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   }
 }
 
@@ -467,14 +573,15 @@ __global__ __launch_bounds__(256) void fast_scan_kernel(FastScanArgs a) {
   const int64_t bh = static_cast<int64_t>(grp) * 8 + rem % 8;
   if (bh >= p.BH) return;
   const int c0 = vt * BV;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x;
 
   for (int it = tid; it < DK * BV; it += 256) {
     const int i = it / BV, c = it % BV;
     const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
     Xt[c * LDX + i] = (__bf16)s;
   }
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
 
   const __bf16* Mbh = a.M + static_cast<size_t>(bh) * p.N * (MT * KT * 256);
   bf16x4 mf[MPW][KT];
@@ -486,26 +593,46 @@ __global__ __launch_bounds__(256) void fast_scan_kernel(FastScanArgs a) {
       for (int kt = 0; kt < KT; ++kt)
         mf[q][kt] = *reinterpret_cast<const bf16x4*>(Mj + ((wave * MPW + q) * KT + kt) * 256 + lane * 4);
   };
-  if (p.N > 0) load_m(0);
+  // V_j rows staged in registers one chunk ahead.
+  constexpr int VITEMS = kNK * (BV / 8);
+  constexpr int VIT = (VITEMS + 255) / 256;
+  bf16x8 vbuf[VIT];
+  auto load_v = [&](int64_t jj) {
+    const int64_t t0 = jj * kC;
+    const int n = static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
+    const int64_t tok0 = bh * p.T + t0;
+#pragma unroll
+    for (int q = 0; q < VIT; ++q) {
+      const int it = tid + q * 256;
+      const int s = it / (BV / 8), cg = it % (BV / 8);
+      if (it < VITEMS && s < n) {
+        vbuf[q] = *reinterpret_cast<const bf16x8*>(a.v + (tok0 + s) * dv + c0 + cg * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vbuf[q][e] = (__bf16)0.f;
+      }
+    }
+  };
+  if (p.N > 0) {
+    load_m(0);
+    load_v(0);
+  }
 
   for (int64_t j = 0; j < p.N; ++j) {
     const int64_t t0 = j * kC;
     const int n = static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
     const int64_t tok0 = bh * p.T + t0;
     // V_j^T into columns DK.. of X^T.
-    for (int it = tid; it < kNK * (BV / 8); it += 256) {
-      const int s = it / (BV / 8), cg = it % (BV / 8);
-      bf16x8 raw;
-      if (s < n) {
-        raw = *reinterpret_cast<const bf16x8*>(a.v + (tok0 + s) * dv + c0 + cg * 8);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw[e] = (__bf16)0.f;
+    for (int q = 0; q < VIT; ++q) {
+      const int it = tid + q * 256;
+      if (it < VITEMS) {
+        const int s = it / (BV / 8), cg = it % (BV / 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Xt[(cg * 8 + e) * LDX + DK + s] = vbuf[q][e];
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Xt[(cg * 8 + e) * LDX + DK + s] = raw[e];
     }
-    __syncthreads();
+    lds_barrier();
     f32x4 acc[MPW][NTN];
 #pragma unroll
     for (int q = 0; q < MPW; ++q)
@@ -520,8 +647,11 @@ __global__ __launch_bounds__(256) void fast_scan_kernel(FastScanArgs a) {
         for (int q = 0; q < MPW; ++q) acc[q][nt] = mfma16(mf[q][kt], bv, acc[q][nt]);
       }
     }
-    if (j + 1 < p.N) load_m(j + 1);
-    __syncthreads();
+    if (j + 1 < p.N) {
+      load_m(j + 1);
+      load_v(j + 1);
+    }
+    lds_barrier();
     const bool last = (j + 1 == p.N);
 #pragma unroll
     for (int q = 0; q < MPW; ++q) {
@@ -554,8 +684,8 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
   using Cfg = PrepCfg<DK, RAB>;
   FastPrepArgs a{p, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ld,
                  static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), static_cast<__bf16*>(M)};
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fast_prepare_kernel<DK, RAB>), dim3(p.BH * p.N), dim3(Cfg::NT), Cfg::LDS, s, a);
   return hipGetLastError();
