@@ -8,13 +8,14 @@
 // with bf16 MFMA operands and fp32 accumulation; the triangular solve applies
 // its 16x16 diagonal inverses in fp32.
 //
-// prepare kernel: one workgroup per (batch*head, chunk), NW = (d_k + 64) / 32
-// waves.  Wave w owns two 16-column tiles of the chunk operator's input side
-// (the d_k "W" columns, then the 64 "X" columns); the solve and the final
-// product run per wave on its own columns with no barrier.  The operator is
-// stored transposed-by-construction: each 16x16 tile is written as the A-operand
-// fragment of a 16x16x16 MFMA (64 lanes x 4 bf16 = 512 bytes, lane order),
-// which is exactly how the scan kernel reads it.
+// prepare kernel: one workgroup per (batch*head, chunk), one wave per
+// 16-column tile of the chunk operator's input side (the d_k "W" columns,
+// then the 64 "X" columns); the solve and the final product run per wave on
+// its own columns with no barrier.  The operator is stored in MFMA operand
+// order: each 16x16 tile is the A-operand fragment of a 16x16x16 MFMA (lane
+// l holds row l%16, columns 4*(l/16)..+3), and the tiles of columns 2m and
+// 2m+1 are interleaved per lane, so one 16-byte load gives a lane the eight
+// K values of a 16x16x32 MFMA over both.
 //
 // scan kernel: one workgroup per (batch*head, d_v slice); chunks in order, the
 // state slice kept in LDS as the bf16 B operand, per chunk one MFMA product.
@@ -479,7 +480,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = sc * (base[e] - acc[u][e]);
-      *reinterpret_cast<bf16x4*>(Mout + (mt * KT + kt) * 256 + lane * 4) = to_bf16x4(v);
+      *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) =
+          to_bf16x4(v);
     }
   }
   // Output rows that are tokens (Qbar, R): base Q~ or M_K.
@@ -524,7 +526,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = base[e] - acc[u][e];
-      *reinterpret_cast<bf16x4*>(Mout + (mt * KT + kt) * 256 + lane * 4) = to_bf16x4(v);
+      *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) =
+          to_bf16x4(v);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -535,18 +538,43 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(Fa
 // ---------------------------------------------------------------------------
 // Scan kernel: per (batch*head, BV-wide d_v slice), chunks in order,
 // Y = M_j [S ; V_j] with the operator fragments read straight from HBM.
-template <int DK, int BV>
+//
+// The right operand X = [S ; V_j] (KIN x BV) lives in LDS as X^T, bf16, with
+// its K index permuted inside every 32-wide block so that one 16-byte read
+// gives a lane the eight K values of a 16x16x32 MFMA that pairs two stored
+// 16x16 operator tiles: position 8*g + 4*h + e of block b holds
+// k = 32*b + 16*h + 4*g + e.  Two such buffers alternate between chunks, so
+// one barrier per chunk orders the state write against the next product.
+// The operator and V of the next PD chunks are held in registers (a ring of
+// PD buffers), so HBM latency overlaps PD chunk steps.  Output rows go
+// through an LDS staging buffer and leave as 16-byte row stores one chunk
+// later.
+template <int DK, int BV, int NWV, int PD>
 struct ScanCfg {
   static constexpr int KIN = DK + kNK;
   static constexpr int ROUT = DK + kC;
   static constexpr int KT = KIN / 16;
+  static constexpr int KP = KT / 2;
   static constexpr int MT = ROUT / 16;
-  static constexpr int NWV = 4;
-  static constexpr int MPW = MT / NWV;     // output tiles (rows) per wave
-  static constexpr int NTN = BV / 16;      // output tiles (columns)
+  static constexpr int NT = 64 * NWV;
+  static constexpr int MPW = MT / NWV;     // output row tiles per wave
+  static constexpr int NTN = BV / 16;      // output column tiles
   static constexpr int LDX = KIN + 8;      // padded row of X^T (bf16)
-  static constexpr int LDS = BV * LDX * 2;
+  static constexpr int XBUF = BV * LDX;    // elements of one X^T buffer
+  static constexpr int LDO = BV + 8;       // padded row of the output stage
+  static constexpr int OBUF = kC * LDO;
+  static constexpr int LDS = 2 * (XBUF + OBUF) * 2;
+  static constexpr int MSZ = MT * KT * 256;          // operator elements per chunk
+  static constexpr int VITEMS = (kC / 4) * (BV / 8); // 4 tokens x 8 columns each
+  static constexpr int VIT = (VITEMS + NT - 1) / NT;
+  static constexpr int OITEMS = kC * (BV / 8);       // 16-byte output pieces
+  static constexpr int OIT = (OITEMS + NT - 1) / NT;
+  static_assert(MT % NWV == 0 && KT % 2 == 0 && BV % 16 == 0 && PD % 2 == 0, "scan tiling");
 };
+
+__device__ __forceinline__ int kperm(int k) {
+  return (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+}
 
 struct FastScanArgs {
   Problem p;
@@ -557,12 +585,16 @@ struct FastScanArgs {
   const float* S0;
 };
 
-template <int DK, int BV>
-__global__ __launch_bounds__(256) void fast_scan_kernel(FastScanArgs a) {
-  using Cfg = ScanCfg<DK, BV>;
-  constexpr int KT = Cfg::KT, MT = Cfg::MT, MPW = Cfg::MPW, NTN = Cfg::NTN, LDX = Cfg::LDX;
+template <int DK, int BV, int NWV, int PD>
+__global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
+  using Cfg = ScanCfg<DK, BV, NWV, PD>;
+  constexpr int KP = Cfg::KP, MPW = Cfg::MPW, NTN = Cfg::NTN, LDX = Cfg::LDX, NT = Cfg::NT;
+  constexpr int XBUF = Cfg::XBUF, LDO = Cfg::LDO, OBUF = Cfg::OBUF, MSZ = Cfg::MSZ;
+  constexpr int VITEMS = Cfg::VITEMS, OITEMS = Cfg::OITEMS, OIT = Cfg::OIT;
+  static_assert(Cfg::VIT == 1, "one V piece per thread");
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* Xt = reinterpret_cast<__bf16*>(smem);   // [BV][KIN]: columns 0..DK state^T, DK.. V_j^T
+  __bf16* X0 = reinterpret_cast<__bf16*>(smem);
+  __bf16* O0 = X0 + 2 * XBUF;
   const Problem& p = a.p;
   const int dv = p.dv;
   const int nvt = dv / BV;
@@ -571,88 +603,115 @@ __global__ __launch_bounds__(256) void fast_scan_kernel(FastScanArgs a) {
   const int grp = b / (8 * nvt), rem = b % (8 * nvt);
   const int vt = rem / 8;
   const int64_t bh = static_cast<int64_t>(grp) * 8 + rem % 8;
-  if (bh >= p.BH) return;
+  const int64_t N = p.N;
+  if (bh >= p.BH || N == 0) return;
   const int c0 = vt * BV;
   const int tid = threadIdx.x;
-
-  for (int it = tid; it < DK * BV; it += 256) {
-    const int i = it / BV, c = it % BV;
-    const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
-    Xt[c * LDX + i] = (__bf16)s;
-  }
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
 
-  const __bf16* Mbh = a.M + static_cast<size_t>(bh) * p.N * (MT * KT * 256);
-  bf16x4 mf[MPW][KT];
-  auto load_m = [&](int64_t jj) {
-    const __bf16* Mj = Mbh + static_cast<size_t>(jj) * (MT * KT * 256);
+  const __bf16* Mbh = a.M + static_cast<size_t>(bh) * N * MSZ;
+  const int moff = wave * MPW * KP * 512 + lane * 8;
+  // V piece of this thread: tokens 4*vs .. 4*vs+3, columns 8*vc .. 8*vc+7.
+  const int vitem = tid < VITEMS ? tid : VITEMS - 1;
+  const int vs = vitem / (BV / 8), vc = vitem % (BV / 8);
+  const __bf16* vbh = a.v + static_cast<size_t>(bh) * p.T * dv + c0;
+  __bf16* obh = a.out + static_cast<size_t>(bh) * p.T * dv + c0;
+
+  bf16x8 mf[PD][MPW][KP];
+  bf16x8 vb[PD][4];
+  auto chunk_len = [&](int64_t jj) {
+    const int64_t r = p.T - jj * kC;
+    return static_cast<int>(r < kC ? r : kC);   // <= 0 past the last chunk
+  };
+  // Loads are unconditional (chunk and token indices are clamped), so no
+  // control flow separates a prefetch from the work it overlaps.
+  auto load_m = [&](bf16x8 (&dst)[MPW][KP], int64_t jj) {
+    jj = jj < N ? jj : N - 1;
+    const __bf16* Mj = Mbh + static_cast<size_t>(jj) * MSZ;
 #pragma unroll
     for (int q = 0; q < MPW; ++q)
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-        mf[q][kt] = *reinterpret_cast<const bf16x4*>(Mj + ((wave * MPW + q) * KT + kt) * 256 + lane * 4);
+      for (int kp = 0; kp < KP; ++kp)
+        dst[q][kp] = *reinterpret_cast<const bf16x8*>(Mj + moff + (q * KP + kp) * 512);
   };
-  // V_j rows staged in registers one chunk ahead.
-  constexpr int VITEMS = kNK * (BV / 8);
-  constexpr int VIT = (VITEMS + 255) / 256;
-  bf16x8 vbuf[VIT];
-  auto load_v = [&](int64_t jj) {
-    const int64_t t0 = jj * kC;
-    const int n = static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
-    const int64_t tok0 = bh * p.T + t0;
+  auto load_v = [&](bf16x8 (&dst)[4], int64_t jj) {
+    jj = jj < N ? jj : N - 1;
+    const __bf16* vj = vbh + static_cast<size_t>(jj) * kC * dv;
+    const int last = chunk_len(jj) - 1;
 #pragma unroll
-    for (int q = 0; q < VIT; ++q) {
-      const int it = tid + q * 256;
-      const int s = it / (BV / 8), cg = it % (BV / 8);
-      if (it < VITEMS && s < n) {
-        vbuf[q] = *reinterpret_cast<const bf16x8*>(a.v + (tok0 + s) * dv + c0 + cg * 8);
-      } else {
+    for (int r = 0; r < 4; ++r) {
+      const int s = 4 * vs + r < last ? 4 * vs + r : last;
+      dst[r] = *reinterpret_cast<const bf16x8*>(vj + (s * dv + vc * 8));
+    }
+  };
+  // V_jj^T into the V rows of an X^T buffer (four tokens per 8-byte write);
+  // rows past the chunk's end are zero.
+  auto put_v = [&](__bf16* X, const bf16x8 (&src)[4], int64_t jj) {
+    const int n = chunk_len(jj);
+    if (tid < VITEMS) {
+      const int pos = kperm(DK + 4 * vs);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vbuf[q][e] = (__bf16)0.f;
+      for (int e = 0; e < 8; ++e) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = 4 * vs + r < n ? src[r][e] : (__bf16)0.f;
+        *reinterpret_cast<bf16x4*>(X + (vc * 8 + e) * LDX + pos) = w;
       }
     }
   };
-  if (p.N > 0) {
-    load_m(0);
-    load_v(0);
-  }
+  // Output rows of chunk jj from a staging buffer to HBM (none past the end).
+  auto flush_out = [&](const __bf16* O, int64_t jj) {
+    const int n = chunk_len(jj);
+    __bf16* oj = obh + static_cast<size_t>(jj) * kC * dv;
+#pragma unroll
+    for (int q = 0; q < OIT; ++q) {
+      const int it = tid + q * NT;
+      const int t = it / (BV / 8), cg = it % (BV / 8);
+      if (it < OITEMS && t < n) *reinterpret_cast<bf16x8*>(oj + (t * dv + cg * 8)) = lds8(O + t * LDO + cg * 8);
+    }
+  };
 
-  for (int64_t j = 0; j < p.N; ++j) {
-    const int64_t t0 = j * kC;
-    const int n = static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
-    const int64_t tok0 = bh * p.T + t0;
-    // V_j^T into columns DK.. of X^T.
 #pragma unroll
-    for (int q = 0; q < VIT; ++q) {
-      const int it = tid + q * 256;
-      if (it < VITEMS) {
-        const int s = it / (BV / 8), cg = it % (BV / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Xt[(cg * 8 + e) * LDX + DK + s] = vbuf[q][e];
-      }
-    }
-    lds_barrier();
+  for (int u = 0; u < PD; ++u) {
+    load_m(mf[u], u);
+    load_v(vb[u], u);
+  }
+  for (int it = tid; it < DK * BV; it += NT) {
+    const int i = it / BV, c = it % BV;
+    const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
+    X0[c * LDX + kperm(i)] = (__bf16)s;
+  }
+  put_v(X0, vb[0], 0);
+  // Ring invariant from here on: at chunk jj, vb[(jj + 1) % PD] holds V_{jj+1}.
+  load_v(vb[0], PD);
+  lds_barrier();
+
+  // One chunk: product from X buffer u&1; state and V_{jj+1} into the other,
+  // outputs into stage u&1; the previous chunk's stage goes out meanwhile.
+  // Steps past the last chunk (to finish a group of PD) compute on clamped
+  // data and store nothing.
+  auto step = [&](const int u, const int64_t jj) {
+    const __bf16* Xc = X0 + (u & 1) * XBUF;
+    __bf16* Xn = X0 + ((u + 1) & 1) * XBUF;
+    __bf16* Oc = O0 + (u & 1) * OBUF;
     f32x4 acc[MPW][NTN];
 #pragma unroll
     for (int q = 0; q < MPW; ++q)
 #pragma unroll
       for (int nt = 0; nt < NTN; ++nt) acc[q][nt] = zero4();
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kp = 0; kp < KP; ++kp) {
+      bf16x8 bv[NTN];
 #pragma unroll
-      for (int nt = 0; nt < NTN; ++nt) {
-        const bf16x4 bv = lds4(Xt + (nt * 16 + lr) * LDX + kt * 16 + 4 * lg);
+      for (int nt = 0; nt < NTN; ++nt) bv[nt] = lds8(Xc + (nt * 16 + lr) * LDX + kp * 32 + 8 * lg);
 #pragma unroll
-        for (int q = 0; q < MPW; ++q) acc[q][nt] = mfma16(mf[q][kt], bv, acc[q][nt]);
-      }
+      for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+        for (int q = 0; q < MPW; ++q) acc[q][nt] = mfma32(mf[u][q][kp], bv[nt], acc[q][nt]);
     }
-    if (j + 1 < p.N) {
-      load_m(j + 1);
-      load_v(j + 1);
-    }
-    lds_barrier();
-    const bool last = (j + 1 == p.N);
+    load_m(mf[u], jj + PD);
+    if (jj > 0) flush_out(O0 + ((u + 1) & 1) * OBUF, jj - 1);
 #pragma unroll
     for (int q = 0; q < MPW; ++q) {
       const int mt = wave * MPW + q;
@@ -660,22 +719,40 @@ __global__ __launch_bounds__(256) void fast_scan_kernel(FastScanArgs a) {
       for (int nt = 0; nt < NTN; ++nt) {
         const int c = nt * 16 + lr;
         if (mt < DK / 16) {
-          const int i0 = mt * 16 + 4 * lg;
-          *reinterpret_cast<bf16x4*>(Xt + c * LDX + i0) = to_bf16x4(acc[q][nt]);
-          if (last && a.Sfin) {
+          *reinterpret_cast<bf16x4*>(Xn + c * LDX + kperm(mt * 16 + 4 * lg)) = to_bf16x4(acc[q][nt]);
+        } else {
+          const int t = (mt - DK / 16) * 16 + 4 * lg;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Oc[(t + e) * LDO + c] = (__bf16)acc[q][nt][e];
+        }
+      }
+    }
+    if (jj == N - 1 && a.Sfin) {
+#pragma unroll
+      for (int q = 0; q < MPW; ++q) {
+        const int mt = wave * MPW + q;
+        if (mt < DK / 16) {
+#pragma unroll
+          for (int nt = 0; nt < NTN; ++nt) {
+            const int i0 = mt * 16 + 4 * lg, c = nt * 16 + lr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) a.Sfin[(bh * DK + i0 + e) * dv + c0 + c] = acc[q][nt][e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = (mt - DK / 16) * 16 + 4 * lg + e;
-            if (t < n) a.out[(tok0 + t) * dv + c0 + c] = (__bf16)acc[q][nt][e];
           }
         }
       }
     }
+    const int un = (u + 1) % PD;
+    put_v(Xn, vb[un], jj + 1);
+    load_v(vb[un], jj + 1 + PD);
+    lds_barrier();
+  };
+
+  for (int64_t j = 0; j < N; j += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) step(u, j + u);
   }
+  // The last chunk's outputs, unless a step past the end already sent them.
+  if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
 }
 
 template <int DK, int RAB>
@@ -691,18 +768,19 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
   return hipGetLastError();
 }
 
-template <int DK, int BV>
+template <int DK, int BV, int NWV, int PD>
 hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out, float* Sfin,
                        const float* S0, hipStream_t s) {
-  using Cfg = ScanCfg<DK, BV>;
+  using Cfg = ScanCfg<DK, BV, NWV, PD>;
   FastScanArgs a{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(v),
                  static_cast<__bf16*>(out), Sfin, S0};
   const int nvt = p.dv / BV;
   const int64_t groups = (p.BH + 7) / 8;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fast_scan_kernel<DK, BV>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fast_scan_kernel<DK, BV>), dim3(groups * 8 * nvt), dim3(256), Cfg::LDS, s, a);
+  hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD>), dim3(groups * 8 * nvt), dim3(Cfg::NT), Cfg::LDS,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -731,8 +809,11 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s) {
   if (p.BH == 0) return hipSuccess;
-  if (p.dk == 128) return launch_scan<128, 64>(p, workspace, v, out, Sfin, S0, s);
-  if (p.dk == 64) return launch_scan<64, 16>(p, workspace, v, out, Sfin, S0, s);
+  // Wider d_v slices share each operator load among more columns; narrower
+  // ones are used when that leaves too few workgroups to fill the chip.
+  if (p.dk == 128 && p.BH * (p.dv / 64) >= 256) return launch_scan<128, 64, 12, 2>(p, workspace, v, out, Sfin, S0, s);
+  if (p.dk == 128) return launch_scan<128, 32, 4, 2>(p, workspace, v, out, Sfin, S0, s);
+  if (p.dk == 64) return launch_scan<64, 16, 4, 4>(p, workspace, v, out, Sfin, S0, s);
   return hipErrorInvalidValue;
 }
 
