@@ -43,14 +43,8 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
@@ -72,16 +66,61 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 }
 __device__ __forceinline__ bf16x4 lds4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ bf16x8 lds8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-// Four values of one column, rows r, r+ld, r+2ld, r+3ld.
-__device__ __forceinline__ bf16x4 lds_col4(const __bf16* p, int ld) {
-  bf16x4 r;
-  r[0] = p[0]; r[1] = p[ld]; r[2] = p[2 * ld]; r[3] = p[3 * ld];
-  return r;
+// The transposing 64-bit LDS read (16-bit elements) works on groups of 16
+// lanes: element e of lane (g, i) is the (i%4)-th value fetched by lane
+// (g, 4e + i/4).  Lane (g, j) therefore supplies the address of
+// X[4g + j/4][4(j%4) .. 4(j%4)+3] so that lane (g, i) receives X[4g+e][i]:
+// a tile's transpose in MFMA operand order.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Row layout of the prepare kernel's operand arrays, chosen so that both a
+// 16-row x 16-byte MFMA fragment read and a transposing tile read run at the
+// LDS's full rate (measured on gfx950): d_k = 128 rows are padded to 144
+// bf16 (addresses stay additive, so lane offsets fold into immediates);
+// d_k = 64 rows are unpadded with their 16-byte pieces XOR-permuted by the
+// row index (piece q of row r at q ^ ((r >> 1) & 7)).
+template <int DK>
+struct XRow {
+  static constexpr int LD = DK == 128 ? 144 : DK;   // bf16 per row
+};
+// Element offset of the 16-byte piece q of row `row`.
+template <int DK>
+__device__ __forceinline__ int xoff(int row, int q) {
+  if (DK == 128) return row * XRow<DK>::LD + 8 * q;
+  return row * DK + 8 * (q ^ ((row >> 1) & 7));
+}
+// MFMA row fragment: rows r0 + lane%16, 16-byte piece q0 + lane/16.
+template <int DK>
+__device__ __forceinline__ bf16x8 xrow8(const __bf16* X, int r0, int q0, int lane) {
+  return lds8(X + xoff<DK>(r0 + (lane & 15), q0 + (lane >> 4)));
+}
+// Transposing read of the 16x16 tile at rows r0.., columns c0.. (c0 % 16 == 0)
+// of a swizzled operand array: lane (g, i) receives X[r0 + 4g + e][c0 + i].
+template <int DK>
+__device__ __forceinline__ bf16x4 xtr4(const __bf16* X, int r0, int c0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = r0 + 4 * g + (j >> 2);
+  const __bf16* ptr = X + xoff<DK>(row, (c0 >> 3) + ((j & 3) >> 1)) + 4 * (j & 1);
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(ptr));
+  return __builtin_bit_cast(bf16x4, r);
 }
 
 // ---------------------------------------------------------------------------
-// Prepare kernel.
-template <int DK, int RAB>
+// Prepare kernel.  Persistent: each workgroup walks chunks blockIdx.x,
+// blockIdx.x + gridDim.x, ...; the next chunk's raw inputs are loaded into
+// registers while the current one is being solved.
+//
+// Roles inside a chunk (DK/8 or KT waves, whichever is more):
+//  * scaling: wave w owns tokens TPWV*w .. TPWV*w + TPWV-1, lane (g, c) owns
+//    the 8-channel piece c of token TPWV*w + g, so that every load reads whole
+//    rows.  The chunk-local cumulative log-decay is a prefix sum over tokens:
+//    inside the wave by lane shuffles, across waves through per-wave totals in
+//    LDS.  It is kept in base-2 units so that every decay factor is one exp2.
+//  * Gram blocks: the upper-triangular tiles of A~ [B~ ; Q~]^T, spread evenly
+//    over all waves.
+//  * solve and operator: wave w < KT owns the 16-column input tile w.
+template <int DK, int RAB, bool SCAL>
 struct PrepCfg {
   static constexpr int NA = kC * RAB;            // decay rows of a chunk
   static constexpr int NB = NA / 16;             // 16-row blocks of the solve
@@ -89,28 +128,27 @@ struct PrepCfg {
   static constexpr int ROUT = DK + kC;           // operator output height
   static constexpr int KT = KIN / 16;
   static constexpr int MT = ROUT / 16;
-  static constexpr int NW = KT;                  // one wave per 16-column input tile
+  static constexpr int NO = DK / 8;              // 16-byte channel pieces per row
+  static constexpr int NW = NO > KT ? NO : KT;
   static constexpr int NT = 64 * NW;
-  static constexpr int TPW = 1;
-  static constexpr int LD = DK + 8;              // padded row of Xl / Xr (bf16)
-  static constexpr int LDA = NA + 8;             // padded row of At^T and M_A (bf16)
+  static constexpr int TPWV = 64 / NO;           // tokens per wave in the scaling phase
+  static constexpr int LDA = NA + 8;             // padded row of M_A (bf16)
+  static constexpr int LDB = 260;                // floats per diagonal block (padded)
+  static constexpr int NCS = NB + kC / 16;       // column blocks of the Gram tiles
+  static constexpr int NTILE = NB * NCS - NB * (NB - 1) / 2;
+  static constexpr int FULL_SLOTS = NTILE / NW;  // tile slots every wave has
   // LDS regions (bytes)
-  static constexpr int XL_ROWS = NA + kC;
-  static constexpr int XR_ROWS = NA + kNK;
-  // A~^T overwrites the B~ rows of Xl once those are dead; when it does not fit
-  // there it gets a region of its own (R5), so the Q~ rows stay readable.
-  static constexpr bool AT_OVER_B = DK * LDA <= NA * LD;
-  static constexpr int R1 = XL_ROWS * LD * 2;
-  static constexpr int R2 = XR_ROWS * LD * 2;
-  static constexpr int LDIAG = NB * 256 * 4;
-  static constexpr int LPACK = (NB * (NB - 1) / 2) * 256 * 2;
-  static constexpr int MA = kC * LDA * 2;
-  static constexpr int R3_OUT = LDIAG + LPACK + MA;
-  static constexpr int R3_G = kC * DK * 4;
-  static constexpr int R3 = R3_OUT > R3_G ? R3_OUT : R3_G;
-  static constexpr int R4 = DK * 4;
-  static constexpr int R5 = AT_OVER_B ? 0 : DK * LDA * 2;
-  static constexpr int LDS = R1 + R2 + R3 + R4 + R5;
+  static constexpr int R_XL = (NA + kC) * XRow<DK>::LD * 2;
+  static constexpr int R_XR = (NA + kNK) * XRow<DK>::LD * 2;
+  static constexpr int R_LD = NB * LDB * 4;
+  static constexpr int R_LP = (NB * (NB - 1) / 2) * 256 * 2;
+  static constexpr int R_MA = kC * LDA * 2;
+  static_assert(R_MA >= NW * DK * 4, "per-wave decay totals alias the M_A region");
+  static constexpr int R_EG = DK * 4;
+  static constexpr int DIB = 520;                // bf16 per inverse block (hi, lo; padded)
+  static constexpr int R_DI = NB * DIB * 2;
+  static constexpr int LDS = R_XL + R_XR + R_LD + R_LP + R_MA + R_EG + R_DI;
+  static_assert(NO == NW && KT <= NW, "wave roles: one wave per channel piece");
 };
 
 struct FastPrepArgs {
@@ -123,415 +161,342 @@ struct FastPrepArgs {
   __bf16* M;   // fragment-ordered chunk operators
 };
 
-template <int DK, int RAB>
-__global__ __launch_bounds__((PrepCfg<DK, RAB>::NT)) void fast_prepare_kernel(FastPrepArgs a) {
-  using Cfg = PrepCfg<DK, RAB>;
-  constexpr int NA = Cfg::NA, NB = Cfg::NB, LD = Cfg::LD, LDA = Cfg::LDA, NW = Cfg::NW, NT = Cfg::NT;
-  constexpr int MT = Cfg::MT, KT = Cfg::KT, TPW = Cfg::TPW;
+__device__ __forceinline__ bf16x8 scale8(const bf16x8& raw, const float (&f)[8]) {
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (__bf16)((float)raw[e] * f[e]);
+  return out;
+}
+
+template <int DK, int RAB, bool SCAL>
+__global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_kernel(FastPrepArgs a) {
+  using Cfg = PrepCfg<DK, RAB, SCAL>;
+  constexpr int NA = Cfg::NA, NB = Cfg::NB, LDA = Cfg::LDA, NW = Cfg::NW, LDB = Cfg::LDB;
+  constexpr int MT = Cfg::MT, KT = Cfg::KT, NCS = Cfg::NCS, NTILE = Cfg::NTILE;
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* Xl = reinterpret_cast<__bf16*>(smem);                      // [B~ ; Q~]   rows x LD
-  __bf16* Xr = reinterpret_cast<__bf16*>(smem + Cfg::R1);            // [A~ ; K~]   rows x LD
-  float* G = reinterpret_cast<float*>(smem + Cfg::R1 + Cfg::R2);     // C x DK (or C) cumulative log-decay
-  float* Ldg = G;                                                    // NB x 16 x 16 fp32 diagonal blocks
-  __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::LDIAG);  // -L blocks below the diagonal
-  __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::LDIAG + Cfg::LPACK);  // M_A  C x LDA
-  float* eGC = reinterpret_cast<float*>(smem + Cfg::R1 + Cfg::R2 + Cfg::R3);                   // exp(G_C) per channel
-  __bf16* AT = Cfg::AT_OVER_B ? Xl                                   // A~^T        DK x LDA (after the solve)
-                              : reinterpret_cast<__bf16*>(smem + Cfg::R1 + Cfg::R2 + Cfg::R3 + Cfg::R4);
+  __bf16* Xl = reinterpret_cast<__bf16*>(smem);                             // [B~ ; Q~]
+  __bf16* Xr = reinterpret_cast<__bf16*>(smem + Cfg::R_XL);                 // [A~ ; K~]
+  float* Ldg = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR);      // diagonal blocks
+  __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD);  // -L below diagonal
+  __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP);
+  float* eGC = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA);
+  __bf16* Dinv = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG);
 
   const Problem& p = a.p;
-  const int tid = threadIdx.x;
-  const bool scalar = p.scalar != 0;
+  const int lane0 = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int64_t total = p.BH * p.N;
+  constexpr float kLog2e = 1.4426950408889634f;
 
-  // Raw inputs are staged in registers: q, K and the log-decay one chunk ahead
-  // (prefetch), the decay operands A, B at the top of each chunk (fetch_ab).
-  constexpr int CG = DK / 8;                                       // 8-channel groups per row
-  constexpr int QK_ITEMS = (kC + kNK) * CG;                        // q rows, then K rows
-  constexpr int QK_IT = (QK_ITEMS + NT - 1) / NT;
-  constexpr int AB_ITEMS = 2 * NA * CG;                            // B rows, then A rows
-  constexpr int AB_IT = (AB_ITEMS + NT - 1) / NT;
-  constexpr int LITEMS = kC * DK / 4;                              // log-decay float4s (per channel)
-  constexpr int LIT = (LITEMS + NT - 1) / NT;
-  bf16x8 qkbuf[QK_IT];
-  bf16x8 abbuf[AB_IT];
-  f32x4 lbuf[LIT];
-  float lscal = 0.f;
-
+  // ---- raw inputs of one chunk for this lane's (token, channel piece).
+  constexpr int NO = Cfg::NO, TPWV = Cfg::TPWV;
+  f32x4 ldv[2];
+  bf16x8 qv, kv, av[RAB], bv[RAB];
   auto chunk_n = [&](int64_t jb, int64_t& tok0) {
     const int64_t bh = jb / p.N, jc = jb % p.N;
     const int64_t t0 = jc * kC;
     tok0 = bh * p.T + t0;
     return static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
   };
-  // Loads are unconditional (an invalid item reads the chunk's first row, which
-  // always exists) so that no branch waits on them; the consumer zeroes the
-  // items of padded tokens.
-  auto prefetch = [&](int64_t jb) {
+  // Loads are unconditional: a padded token reads the chunk's last row (the
+  // values are discarded), so no branch separates the loads from their use.
+  auto load = [&](int64_t jb, int ln) {
     int64_t tok0;
     const int n = chunk_n(jb, tok0);
-#pragma unroll
-    for (int q = 0; q < QK_IT; ++q) {
-      const int it = tid + q * NT;
-      const int row = it / CG, cg = it % CG;
-      const int t = row < kC ? row : row - kC;
-      const bool ok = it < QK_ITEMS && t < n;
-      const __bf16* src = (row < kC ? a.q : a.k) + (tok0 + (ok ? t : 0)) * DK + (ok ? cg : 0) * 8;
-      qkbuf[q] = *reinterpret_cast<const bf16x8*>(src);
-    }
-    if (!scalar) {
-#pragma unroll
-      for (int q = 0; q < LIT; ++q) {
-        const int e4 = tid + q * NT;
-        const bool ok = e4 < LITEMS && (e4 * 4) / DK < n;
-        lbuf[q] = *reinterpret_cast<const f32x4*>(a.ld + tok0 * DK + (ok ? e4 * 4 : 0));
-      }
+    const int t = wave * TPWV + ln / NO;
+    const int64_t tok = tok0 + (t < n ? t : n - 1);
+    const int c0 = (ln % NO) * 8;
+    if (SCAL) {
+      ldv[0][0] = a.ld[tok];
     } else {
-      lscal = a.ld[tok0 + (tid < n ? tid : 0)];
+      ldv[0] = *reinterpret_cast<const f32x4*>(a.ld + tok * DK + c0);
+      ldv[1] = *reinterpret_cast<const f32x4*>(a.ld + tok * DK + c0 + 4);
     }
-  };
-  auto fetch_ab = [&](int64_t jb) {
-    int64_t tok0;
-    const int n = chunk_n(jb, tok0);
+    qv = *reinterpret_cast<const bf16x8*>(a.q + tok * DK + c0);
+    kv = *reinterpret_cast<const bf16x8*>(a.k + tok * DK + c0);
 #pragma unroll
-    for (int q = 0; q < AB_IT; ++q) {
-      const int it = tid + q * NT;
-      const int row = it / CG, cg = it % CG;
-      const int r = row < NA ? row : row - NA;
-      const int t = r / RAB;
-      const bool ok = it < AB_ITEMS && t < n;
-      const __bf16* src = (row < NA ? a.B : a.A) +
-                          ((tok0 + (ok ? t : 0)) * RAB + (ok ? r % RAB : 0)) * DK + (ok ? cg : 0) * 8;
-      abbuf[q] = *reinterpret_cast<const bf16x8*>(src);
+    for (int r = 0; r < RAB; ++r) {
+      av[r] = *reinterpret_cast<const bf16x8*>(a.A + (tok * RAB + r) * DK + c0);
+      bv[r] = *reinterpret_cast<const bf16x8*>(a.B + (tok * RAB + r) * DK + c0);
     }
   };
 
-  // One workgroup per chunk: every load of the chunk is issued up front.
-  const int64_t job = blockIdx.x;
+  int64_t job = blockIdx.x;
   if (job >= total) return;
-  prefetch(job);
-  {
-  int64_t tok0_cur;
-  const int ncur = chunk_n(job, tok0_cur);   // tokens of this chunk (the rest are padding)
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  // Wave w owns input tiles kt0 .. kt0 + ntw - 1; a tile below DK/16 is a "W"
-  // tile (channel columns), the others are "X" tiles (chunk-write rows).
-  const int ntw = TPW;
-  const int kt0 = TPW * wave;
-  fetch_ab(job);
-  // ---- P0: chunk-local inclusive cumulative log-decay (padded tokens add 0).
-  if (!scalar) {
+  load(job, lane0);
+  for (; job < total; job += gridDim.x) {
+    // Lane-derived values are recomputed per chunk from an opaque copy of the
+    // lane index: hoisted out of this loop they would all stay live at once.
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int lr = lane & 15, lg = lane >> 4;
+    const int tid = wave * 64 + lane;
+    int64_t tok0_cur;
+    const int ncur = chunk_n(job, tok0_cur);   // tokens of this chunk (the rest are padding)
+    __bf16* Mout = a.M + static_cast<size_t>(job) * (MT * KT * 256);
+
+    // ---- P0/P1: cumulative log-decay (base 2) and the decay-scaled operands
+    //      B~ = B exp(G_{t-1}), Q~ = q exp(G_t), A~ = A exp(-G_t), K~ = K exp(-G_t).
+    {
+      const int tg = lane / NO, pc = lane % NO;
+      const int t = wave * TPWV + tg;
+      const bool pad = t >= ncur;
+      constexpr int NL = SCAL ? 1 : 8;
+      float* wtot = reinterpret_cast<float*>(MAs);   // per-wave totals (M_A is not live yet)
+      float l2[NL], x[NL];
 #pragma unroll
-    for (int q = 0; q < LIT; ++q) {
-      const int e4 = tid + q * NT;
-      if (e4 < LITEMS) *reinterpret_cast<f32x4*>(G + e4 * 4) = (e4 * 4) / DK < ncur ? lbuf[q] : zero4();
+      for (int c = 0; c < NL; ++c) {
+        const float v = SCAL ? ldv[0][0] : ldv[c / 4][c % 4];
+        l2[c] = pad ? 0.f : v * kLog2e;
+        x[c] = l2[c];
+      }
+      // inclusive prefix over this wave's tokens
+#pragma unroll
+      for (int sh = NO; sh < 64; sh *= 2) {
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+          const float y = __shfl_up(x[c], sh, 64);
+          if (lane >= sh) x[c] += y;
+        }
+      }
+      if (tg == TPWV - 1) {
+#pragma unroll
+        for (int c = 0; c < NL; ++c) wtot[wave * DK + pc * 8 + c] = x[c];
+      }
+      lds_barrier();
+      // totals of the earlier waves: token group g sums waves g, g + TPWV, ...
+      float part[NL];
+#pragma unroll
+      for (int c = 0; c < NL; ++c) part[c] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NW / TPWV; ++k) {
+        const int w2 = tg + k * TPWV;
+        if (w2 < wave) {
+#pragma unroll
+          for (int c = 0; c < NL; ++c) part[c] += wtot[w2 * DK + pc * 8 + c];
+        }
+      }
+#pragma unroll
+      for (int sh = NO; sh < 64; sh *= 2) {
+#pragma unroll
+        for (int c = 0; c < NL; ++c) part[c] += __shfl_xor(part[c], sh, 64);
+      }
+      float g2[NL];
+#pragma unroll
+      for (int c = 0; c < NL; ++c) g2[c] = part[c] + x[c];
+      float fp[8], fn[8], fx[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int cc = SCAL ? 0 : c;
+        fp[c] = pad ? 0.f : __builtin_amdgcn_exp2f(g2[cc]);
+        fn[c] = pad ? 0.f : __builtin_amdgcn_exp2f(-g2[cc]);
+        fx[c] = pad ? 0.f : __builtin_amdgcn_exp2f(g2[cc] - l2[cc]);
+      }
+      if (t == kC - 1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) eGC[pc * 8 + c] = __builtin_amdgcn_exp2f(g2[SCAL ? 0 : c]);
+      }
+      *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(NA + t, pc)) = scale8(qv, fp);
+      *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(NA + t, pc)) = scale8(kv, fn);
+#pragma unroll
+      for (int r = 0; r < RAB; ++r) {
+        *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(RAB * t + r, pc)) = scale8(av[r], fn);
+        *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(RAB * t + r, pc)) = scale8(bv[r], fx);
+      }
+    }
+    // The next chunk's inputs travel while this one is solved.
+    {
+      const int64_t nx = job + gridDim.x;
+      load(nx < total ? nx : total - 1, lane);
     }
     lds_barrier();
-    for (int i = tid; i < DK; i += NT) {
-      float g = 0.f;
-#pragma unroll
-      for (int t0 = 0; t0 < kC; t0 += 16) {
-        float v[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) v[t] = G[(t0 + t) * DK + i];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          g += v[t];
-          G[(t0 + t) * DK + i] = g;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      eGC[i] = __expf(g);
-    }
-  } else {
-    if (wave == 0) {
-      float g = lane < ncur ? lscal : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(g, off, 64);
-        if (lane >= off) g += o;
-      }
-      G[lane] = g;
-      const float gc = __shfl(g, 63, 64);
-      for (int i = lane; i < DK; i += 64) eGC[i] = __expf(gc);
-    }
-  }
-  lds_barrier();
 
-  // ---- P1: decay-scaled bf16 operands.  Xl = [B~ ; Q~], Xr = [A~ ; K~].
-  //      B~ = B (.) exp(G_{t-1}), Q~ = q (.) exp(G_t), A~ = A (.) exp(-G_t), K~ = K (.) exp(-G_t).
-  auto scale_store = [&](const bf16x8& raw, int gt, float sign, int cg, __bf16* dst, bool valid) {
-    float g[8];
-    if (gt < 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = 0.f;
-    } else if (scalar) {
-      const float gs = G[gt];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = gs;
-    } else {
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(G + gt * DK + cg * 8);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(G + gt * DK + cg * 8 + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        g[e] = g0[e];
-        g[e + 4] = g1[e];
+    // ---- P2: Gram blocks.  P^T = A~ [B~ ; Q~]^T, tiles (rs, cs) with cs >= rs,
+    //      spread evenly over all waves and written straight to LDS.
+    auto gram_tile = [&](int idx) {
+      int rs = 0;
+      while (idx >= NCS - rs) {
+        idx -= NCS - rs;
+        ++rs;
       }
-    }
-    bf16x8 out;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(valid ? (float)raw[e] * __expf(sign * g[e]) : 0.f);
-    *reinterpret_cast<bf16x8*>(dst + cg * 8) = out;
-    __builtin_amdgcn_sched_barrier(0);
-  };
-#pragma unroll
-  for (int q = 0; q < QK_IT; ++q) {
-    const int it = tid + q * NT;
-    if (it < QK_ITEMS) {
-      const int row = it / CG, cg = it % CG;
-      if (row < kC) scale_store(qkbuf[q], row, 1.f, cg, Xl + (NA + row) * LD, row < ncur);
-      else scale_store(qkbuf[q], row - kC, -1.f, cg, Xr + (NA + row - kC) * LD, row - kC < ncur);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < AB_IT; ++q) {
-    const int it = tid + q * NT;
-    if (it < AB_ITEMS) {
-      const int row = it / CG, cg = it % CG;
-      if (row < NA) scale_store(abbuf[q], row / RAB - 1, 1.f, cg, Xl + row * LD, row / RAB < ncur);
-      else scale_store(abbuf[q], (row - NA) / RAB, -1.f, cg, Xr + (row - NA) * LD, (row - NA) / RAB < ncur);
-    }
-  }
-  lds_barrier();
-
-  // ---- P2: Gram blocks.  (a) P^T = A~ [B~ ; Q~]^T, tiles (rs, cs), cs >= rs,
-  //      split over all waves and written straight to LDS region 3.
-  {
-    constexpr int CS = NB + kC / 16;
-    for (int tile = wave; tile < NB * CS; tile += NW) {
-      const int rs = tile / CS, cs = tile % CS;
-      if (cs < rs) continue;
+      const int cs = rs + idx;
+      // Which entries survive the token masks is uniform per tile except on
+      // the diagonal: L tiles below it keep everything; an M_A tile (tokens tt)
+      // keeps everything when its first token is >= the last token of the s
+      // rows, nothing when its last token is < their first.
+      const int tt = cs - NB;
+      const bool zero = cs >= NB && 16 * tt + 15 < (16 * rs) / RAB;
+      const bool masked = cs < NB ? cs == rs : (!zero && 16 * tt < (16 * rs + 15) / RAB);
       f32x4 acc = zero4();
+      if (!zero) {
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        const bf16x8 av = lds8(Xr + (rs * 16 + lr) * LD + kb * 32 + 8 * lg);
-        const bf16x8 bv = lds8(Xl + (cs * 16 + lr) * LD + kb * 32 + 8 * lg);
-        acc = mfma32(av, bv, acc);
+        for (int kb = 0; kb < DK / 32; ++kb)
+          acc = mfma32(xrow8<DK>(Xr, rs * 16, kb * 4, lane), xrow8<DK>(Xl, cs * 16, kb * 4, lane), acc);
       }
       // lane holds P^T[s = rs*16 + 4lg + e][col = cs*16 + lr]
-      if (cs < NB) {
-        const int sp = cs * 16 + lr;           // row of L (B~ index)
-        f32x4 v;
+      if (masked) {
+        const int row = cs < NB ? (cs * 16 + lr) / RAB : tt * 16 + lr + 1;  // token bound: keep s/RAB < row
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = rs * 16 + 4 * lg + e;  // column of L (A~ index)
-          v[e] = (sp / RAB > s / RAB) ? acc[e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e)
+          if (!((rs * 16 + 4 * lg + e) / RAB < row)) acc[e] = 0.f;
+      }
+      if (cs < NB) {
         if (cs == rs) {
-          *reinterpret_cast<f32x4*>(Ldg + cs * 256 + lr * 16 + 4 * lg) = v;
+          *reinterpret_cast<f32x4*>(Ldg + cs * LDB + lr * 16 + 4 * lg) = acc;
         } else {
           const int blk = cs * (cs - 1) / 2 + rs;
-          f32x4 nv = f32x4{-v[0], -v[1], -v[2], -v[3]};
-          *reinterpret_cast<bf16x4*>(Lpk + blk * 256 + lr * 16 + 4 * lg) = to_bf16x4(nv);
+          *reinterpret_cast<bf16x4*>(Lpk + blk * 256 + lr * 16 + 4 * lg) =
+              to_bf16x4(f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
         }
       } else {
-        const int t = (cs - NB) * 16 + lr;
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = rs * 16 + 4 * lg + e;
-          v[e] = (t >= s / RAB) ? acc[e] : 0.f;
-        }
-        *reinterpret_cast<bf16x4*>(MAs + t * LDA + rs * 16 + 4 * lg) = to_bf16x4(v);
+        *reinterpret_cast<bf16x4*>(MAs + (tt * 16 + lr) * LDA + rs * 16 + 4 * lg) = to_bf16x4(acc);
       }
-    }
-  }
-  lds_barrier();
+    };
+#pragma unroll
+    for (int sl = 0; sl < Cfg::FULL_SLOTS; ++sl) gram_tile(wave + sl * NW);
+    if (Cfg::FULL_SLOTS * NW + wave < NTILE) gram_tile(Cfg::FULL_SLOTS * NW + wave);
+    lds_barrier();
 
-  // ---- P3: fp32 inverses of the unit lower-triangular diagonal blocks
-  //      (I + L_ii), in place.
-  {
-    float x[16];
-    const bool active = tid < NB * 16;
-    const int blk = tid / 16, c = tid % 16;
-    if (active) {
-      const float* Lb = Ldg + blk * 256;
+    // ---- P3: inverses of the unit lower-triangular diagonal blocks (I + L_ii),
+    //      fp32, stored as a bf16 pair (hi + lo) per entry so that the diagonal
+    //      apply below runs as two 16x16x32 MFMAs.  Thread (blk, c) forms
+    //      column c of block blk by forward substitution.
+    if (tid < NB * 16) {
+      const int blk = tid / 16, c = tid % 16;
+      const float* Lb = Ldg + blk * LDB;
+      __bf16* Dh = Dinv + blk * Cfg::DIB;
+      float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float v = (r == c) ? 1.f : 0.f;
 #pragma unroll
         for (int m = 0; m < r; ++m) v -= Lb[r * 16 + m] * x[m];
         x[r] = v;
-        __builtin_amdgcn_sched_barrier(0);  // one row of loads in flight at a time
+        const __bf16 h = (__bf16)v;
+        Dh[r * 16 + c] = h;
+        Dh[256 + r * 16 + c] = (__bf16)(v - (float)h);
+      }
+    }
+    // Meanwhile each X wave forms the parts of its columns that need no solve:
+    // L_K = B~ K~^T (its right-hand side, token(row) > chunk-write row) and
+    // M_K^T = K~ Q~^T (the base of R, t >= s), from one copy of its K~ rows.
+    bf16x4 lk[NB], mk[kC / 16];
+    if (wave >= DK / 16 && wave < KT) {
+      const int x = wave - DK / 16;
+      bf16x8 kf[DK / 32];
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) kf[kb] = xrow8<DK>(Xr, NA + x * 16, kb * 4, lane);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        f32x4 g = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(xrow8<DK>(Xl, i * 16, kb * 4, lane), kf[kb], g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!((i * 16 + 4 * lg + e) / RAB > x * 16 + lr)) g[e] = 0.f;
+        lk[i] = to_bf16x4(g);
+      }
+#pragma unroll
+      for (int tt = 0; tt < kC / 16; ++tt) {
+        f32x4 g = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(kf[kb], xrow8<DK>(Xl, NA + tt * 16, kb * 4, lane), g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!(tt * 16 + lr >= x * 16 + 4 * lg + e)) g[e] = 0.f;
+        mk[tt] = to_bf16x4(g);
       }
     }
     lds_barrier();
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ldg[blk * 256 + r * 16 + c] = x[r];
-    }
-  }
-  lds_barrier();
 
-  // ---- P4: blocked forward substitution on this wave's columns:
-  //      WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
-  bf16x4 wx[NB][TPW];
+    if (wave < KT) {
+      const int kt = wave;
+      // ---- P4: blocked forward substitution on this wave's columns:
+      //      WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
+      bf16x4 wx[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    f32x4 acc[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int kt = kt0 + u;
-      if (u >= ntw) {
-        acc[u] = zero4();
-      } else if (kt < DK / 16) {
-        // W columns: B~ itself (4 rows of one channel column per lane).
-        acc[u] = to_f32x4(lds_col4(Xl + (i * 16 + 4 * lg) * LD + kt * 16 + lr, LD));
-      } else {
-        // X columns: L_K = B~ K~^T on this block of rows, token(row) > chunk-write row.
-        const int x = kt - DK / 16;
-        f32x4 g = zero4();
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          const bf16x8 av = lds8(Xl + (i * 16 + lr) * LD + kb * 32 + 8 * lg);
-          const bf16x8 bv = lds8(Xr + (NA + x * 16 + lr) * LD + kb * 32 + 8 * lg);
-          g = mfma32(av, bv, g);
+      for (int i = 0; i < NB; ++i) {
+        f32x4 acc;
+        if (kt < DK / 16) {
+          // W columns: B~ itself.
+          acc = to_f32x4(xtr4<DK>(Xl, i * 16, kt * 16, lane));
+        } else {
+          acc = to_f32x4(lk[i]);   // X columns: L_K
         }
-        const int sx = x * 16 + lr;
+        const __bf16* Lrow = Lpk + (i * (i - 1) / 2) * 256 + lr * 16 + 4 * lg;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int sp = i * 16 + 4 * lg + e;
-          if (!(sp / RAB > sx)) g[e] = 0.f;
+        for (int jb = 0; jb + 1 < i; jb += 2)
+          acc = mfma32(cat(lds4(Lrow + jb * 256), lds4(Lrow + (jb + 1) * 256)), cat(wx[jb], wx[jb + 1]), acc);
+        if (i % 2 == 1) {
+          // Odd leftover block: padded to a 16x16x32 product with a zero half
+          // (the whole chain uses one MFMA shape).
+          bf16x4 zb;
+          zb[0] = zb[1] = zb[2] = zb[3] = (__bf16)0.f;
+          acc = mfma32(cat(lds4(Lrow + (i - 1) * 256), zb), cat(wx[i - 1], zb), acc);
         }
-        acc[u] = g;
+        // (I + L_ii)^{-1} acc with both factors split into bf16 hi + lo parts:
+        // [Dh Dl] x [ah ; ah] + [Dh Dl] x [al ; al].
+        const __bf16* Dp = Dinv + i * Cfg::DIB + lr * 16 + 4 * lg;
+        const bf16x8 dA = cat(lds4(Dp), lds4(Dp + 256));
+        const bf16x4 ah = to_bf16x4(acc);
+        const f32x4 ahf = to_f32x4(ah);
+        const bf16x4 al = to_bf16x4(f32x4{acc[0] - ahf[0], acc[1] - ahf[1], acc[2] - ahf[2], acc[3] - ahf[3]});
+        f32x4 o = mfma32(dA, cat(ah, ah), zero4());
+        o = mfma32(dA, cat(al, al), o);
+        wx[i] = to_bf16x4(o);
       }
-    }
-    const __bf16* Lrow = Lpk + (i * (i - 1) / 2) * 256 + lr * 16 + 4 * lg;
-#pragma unroll
-    for (int jb = 0; jb + 1 < i; jb += 2) {
-      const bf16x8 av = cat(lds4(Lrow + jb * 256), lds4(Lrow + (jb + 1) * 256));
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(av, cat(wx[jb][u], wx[jb + 1][u]), acc[u]);
-    }
-    if (i % 2 == 1) {
-      // Odd leftover block: padded to a 16x16x32 product with a zero half.  The
-      // K=16 instruction is kept out of this chain: interleaved with the K=32
-      // products it gave run-to-run differences in the last blocks.
-      bf16x4 zb;
-      zb[0] = zb[1] = zb[2] = zb[3] = (__bf16)0.f;
-      const bf16x8 av = cat(lds4(Lrow + (i - 1) * 256), zb);
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(av, cat(wx[i - 1][u], zb), acc[u]);
-    }
-    const float* Dv = Ldg + i * 256 + lr * 16 + 4 * lg;
-    float dv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dv[e] = Dv[e];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      f32x4 o = zero4();
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o = mfma_f32(dv[e], acc[u][e], o);
-      wx[i][u] = to_bf16x4(o);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
 
-  // ---- A~^T (B~ rows of Xl are dead once every wave has finished its solve).
-  lds_barrier();
-  for (int it = tid; it < DK * (NA / 4); it += Cfg::NT) {
-    const int i = it % DK, s4 = it / DK;
-    const bf16x4 v = lds_col4(Xr + (s4 * 4) * LD + i, LD);
-    *reinterpret_cast<bf16x4*>(AT + i * LDA + s4 * 4) = v;
-  }
-  lds_barrier();
-
-  // ---- P5: operator tiles, transposed product: rows = this wave's input
-  //      columns, columns = output rows m (channels, then tokens):
-  //      acc = sum_s WX[s][k] Bmat[m][s],  Bmat = [A~^T ; M_A].
-  __bf16* Mout = a.M + static_cast<size_t>(job) * (MT * KT * 256);
-  // Output rows that are channels (Acal, Z): base I or K~^T, scaled by exp(G_C).
+      // ---- P5: operator tiles, transposed product: rows = this wave's input
+      //      column tile, columns = output rows m (channels, then tokens):
+      //      acc = sum_s WX[s][k] Bmat[m][s],  Bmat = [A~^T ; M_A].
+      auto store = [&](int mt, const f32x4& v) {
+        *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) = to_bf16x4(v);
+      };
+      // Output rows that are channels (Acal, Z): base I or K~^T, scaled by exp(G_C).
 #pragma unroll 1
-  for (int mt = 0; mt < DK / 16; ++mt) {
-    const __bf16* Brow = AT + (mt * 16 + lr) * LDA;
-    f32x4 acc[TPW];
+      for (int mt = 0; mt < DK / 16; ++mt) {
+        f32x4 acc = zero4();
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) acc[u] = zero4();
+        for (int jb = 0; jb < NB; jb += 2)
+          acc = mfma32(cat(wx[jb], wx[jb + 1]),
+                       cat(xtr4<DK>(Xr, jb * 16, mt * 16, lane), xtr4<DK>(Xr, jb * 16 + 16, mt * 16, lane)), acc);
+        const float sc = eGC[mt * 16 + lr];
+        f32x4 base = zero4();
+        if (kt < DK / 16) {
+          if (kt == mt) {
 #pragma unroll
-    for (int jb = 0; jb < NB; jb += 2) {
-      const bf16x8 bv = cat(lds4(Brow + jb * 16 + 4 * lg), lds4(Brow + (jb + 1) * 16 + 4 * lg));
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(cat(wx[jb][u], wx[jb + 1][u]), bv, acc[u]);
-    }
-    const int m = mt * 16 + lr;
-    const float sc = eGC[m];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int kt = kt0 + u;
-      if (u >= ntw) continue;
-      f32x4 base;
-      if (kt < DK / 16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) base[e] = (kt * 16 + 4 * lg + e == m) ? 1.f : 0.f;
-      } else {
-        base = to_f32x4(lds_col4(Xr + (NA + kt * 16 - DK + 4 * lg) * LD + m, LD));
-      }
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = sc * (base[e] - acc[u][e]);
-      *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) =
-          to_bf16x4(v);
-    }
-  }
-  // Output rows that are tokens (Qbar, R): base Q~ or M_K.
-#pragma unroll
-  for (int tt = 0; tt < kC / 16; ++tt) {
-    const int mt = DK / 16 + tt;
-    const __bf16* Brow = MAs + (tt * 16 + lr) * LDA;
-    f32x4 acc[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) acc[u] = zero4();
-#pragma unroll
-    for (int jb = 0; jb < NB; jb += 2) {
-      const bf16x8 bv = cat(lds4(Brow + jb * 16 + 4 * lg), lds4(Brow + (jb + 1) * 16 + 4 * lg));
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) acc[u] = mfma32(cat(wx[jb][u], wx[jb + 1][u]), bv, acc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int kt = kt0 + u;
-      if (u >= ntw) continue;
-      f32x4 base;
-      if (kt < DK / 16) {
-        base = to_f32x4(lds4(Xl + (NA + tt * 16 + lr) * LD + kt * 16 + 4 * lg));
-      } else {
-        // M_K^T = K~ Q~^T on (chunk-write rows of this tile) x (tokens of tt), t >= s.
-        const int x = kt - DK / 16;
-        f32x4 g = zero4();
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          const bf16x8 av = lds8(Xr + (NA + x * 16 + lr) * LD + kb * 32 + 8 * lg);
-          const bf16x8 bv = lds8(Xl + (NA + tt * 16 + lr) * LD + kb * 32 + 8 * lg);
-          g = mfma32(av, bv, g);
+            for (int e = 0; e < 4; ++e) base[e] = (4 * lg + e == lr) ? 1.f : 0.f;
+          }
+        } else {
+          base = to_f32x4(xtr4<DK>(Xr, NA + kt * 16 - DK, mt * 16, lane));
         }
-        const int t = tt * 16 + lr;
+        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int sx = x * 16 + 4 * lg + e;
-          if (!(t >= sx)) g[e] = 0.f;
-        }
-        base = g;
+        for (int e = 0; e < 4; ++e) v[e] = sc * (base[e] - acc[e]);
+        store(mt, v);
       }
-      f32x4 v;
+      // Output rows that are tokens (Qbar, R): base Q~ or M_K.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = base[e] - acc[u][e];
-      *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) =
-          to_bf16x4(v);
+      for (int tt = 0; tt < kC / 16; ++tt) {
+        const __bf16* Brow = MAs + (tt * 16 + lr) * LDA;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int jb = 0; jb < NB; jb += 2)
+          acc = mfma32(cat(wx[jb], wx[jb + 1]), cat(lds4(Brow + jb * 16 + 4 * lg), lds4(Brow + (jb + 1) * 16 + 4 * lg)), acc);
+        f32x4 base;
+        if (kt < DK / 16) {
+          base = to_f32x4(lds4(Xl + xoff<DK>(NA + tt * 16 + lr, 2 * kt + (lg >> 1)) + 4 * (lg & 1)));
+        } else {
+          base = to_f32x4(mk[tt]);   // M_K^T
+        }
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = base[e] - acc[e];
+        store(DK / 16 + tt, v);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
+    // P5 reads Xl, Xr and M_A, which the next chunk overwrites.
+    lds_barrier();
   }
 }
 
@@ -755,17 +720,31 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
 }
 
+template <int DK, int RAB, bool SCAL>
+hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
+                       const void* A, const void* B, void* M, hipStream_t s) {
+  using Cfg = PrepCfg<DK, RAB, SCAL>;
+  FastPrepArgs a{p, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ld,
+                 static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), static_cast<__bf16*>(M)};
+  const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB, SCAL>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // One resident workgroup per compute unit, each walking a strided set of chunks.
+  const int64_t jobs = p.BH * p.N;
+  const int64_t grid = jobs < cus ? jobs : cus;
+  hipLaunchKernelGGL((fast_prepare_kernel<DK, RAB, SCAL>), dim3(grid), dim3(Cfg::NT), Cfg::LDS, s, a);
+  return hipGetLastError();
+}
+
 template <int DK, int RAB>
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
                        const void* A, const void* B, void* M, hipStream_t s) {
-  using Cfg = PrepCfg<DK, RAB>;
-  FastPrepArgs a{p, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ld,
-                 static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), static_cast<__bf16*>(M)};
-  const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fast_prepare_kernel<DK, RAB>), dim3(p.BH * p.N), dim3(Cfg::NT), Cfg::LDS, s, a);
-  return hipGetLastError();
+  return p.scalar ? launch_prep<DK, RAB, true>(p, q, k, ld, A, B, M, s)
+                  : launch_prep<DK, RAB, false>(p, q, k, ld, A, B, M, s);
 }
 
 template <int DK, int BV, int NWV, int PD>
