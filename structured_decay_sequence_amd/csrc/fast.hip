@@ -530,7 +530,8 @@ struct ScanCfg {
   static constexpr int OBUF = kC * LDO;
   static constexpr int LDS = 2 * (XBUF + OBUF) * 2;
   static constexpr int MSZ = MT * KT * 256;          // operator elements per chunk
-  static constexpr int VITEMS = (kC / 4) * (BV / 8); // 4 tokens x 8 columns each
+  static constexpr int VT = 2;                       // tokens per V piece
+  static constexpr int VITEMS = (kC / VT) * (BV / 8); // VT tokens x 8 columns each
   static constexpr int VIT = (VITEMS + NT - 1) / NT;
   static constexpr int OITEMS = kC * (BV / 8);       // 16-byte output pieces
   static constexpr int OIT = (OITEMS + NT - 1) / NT;
@@ -577,14 +578,15 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
 
   const __bf16* Mbh = a.M + static_cast<size_t>(bh) * N * MSZ;
   const int moff = wave * MPW * KP * 512 + lane * 8;
-  // V piece of this thread: tokens 4*vs .. 4*vs+3, columns 8*vc .. 8*vc+7.
+  // V piece of this thread: tokens VT*vs .. VT*vs+VT-1, columns 8*vc .. 8*vc+7.
+  constexpr int VT = Cfg::VT;
   const int vitem = tid < VITEMS ? tid : VITEMS - 1;
   const int vs = vitem / (BV / 8), vc = vitem % (BV / 8);
   const __bf16* vbh = a.v + static_cast<size_t>(bh) * p.T * dv + c0;
   __bf16* obh = a.out + static_cast<size_t>(bh) * p.T * dv + c0;
 
   bf16x8 mf[PD][MPW][KP];
-  bf16x8 vb[PD][4];
+  bf16x8 vb[2][VT];   // V ring: two chunks ahead is enough for its few KB
   auto chunk_len = [&](int64_t jj) {
     const int64_t r = p.T - jj * kC;
     return static_cast<int>(r < kC ? r : kC);   // <= 0 past the last chunk
@@ -600,28 +602,29 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
       for (int kp = 0; kp < KP; ++kp)
         dst[q][kp] = *reinterpret_cast<const bf16x8*>(Mj + moff + (q * KP + kp) * 512);
   };
-  auto load_v = [&](bf16x8 (&dst)[4], int64_t jj) {
+  auto load_v = [&](bf16x8 (&dst)[VT], int64_t jj) {
     jj = jj < N ? jj : N - 1;
     const __bf16* vj = vbh + static_cast<size_t>(jj) * kC * dv;
     const int last = chunk_len(jj) - 1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = 4 * vs + r < last ? 4 * vs + r : last;
+    for (int r = 0; r < VT; ++r) {
+      const int s = VT * vs + r < last ? VT * vs + r : last;
       dst[r] = *reinterpret_cast<const bf16x8*>(vj + (s * dv + vc * 8));
     }
   };
-  // V_jj^T into the V rows of an X^T buffer (four tokens per 8-byte write);
-  // rows past the chunk's end are zero.
-  auto put_v = [&](__bf16* X, const bf16x8 (&src)[4], int64_t jj) {
+  // V_jj^T into the V rows of an X^T buffer (VT tokens per write); rows past
+  // the chunk's end are zero.
+  typedef __attribute__((__vector_size__(VT * sizeof(__bf16)))) __bf16 bf16xVT;
+  auto put_v = [&](__bf16* X, const bf16x8 (&src)[VT], int64_t jj) {
     const int n = chunk_len(jj);
     if (tid < VITEMS) {
-      const int pos = kperm(DK + 4 * vs);
+      const int pos = kperm(DK + VT * vs);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16x4 w;
+        bf16xVT w;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = 4 * vs + r < n ? src[r][e] : (__bf16)0.f;
-        *reinterpret_cast<bf16x4*>(X + (vc * 8 + e) * LDX + pos) = w;
+        for (int r = 0; r < VT; ++r) w[r] = VT * vs + r < n ? src[r][e] : (__bf16)0.f;
+        *reinterpret_cast<bf16xVT*>(X + (vc * 8 + e) * LDX + pos) = w;
       }
     }
   };
@@ -638,18 +641,17 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   };
 
 #pragma unroll
-  for (int u = 0; u < PD; ++u) {
-    load_m(mf[u], u);
-    load_v(vb[u], u);
-  }
+  for (int u = 0; u < PD; ++u) load_m(mf[u], u);
+  load_v(vb[0], 0);
+  load_v(vb[1], 1);
   for (int it = tid; it < DK * BV; it += NT) {
     const int i = it / BV, c = it % BV;
     const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
     X0[c * LDX + kperm(i)] = (__bf16)s;
   }
   put_v(X0, vb[0], 0);
-  // Ring invariant from here on: at chunk jj, vb[(jj + 1) % PD] holds V_{jj+1}.
-  load_v(vb[0], PD);
+  // Ring invariant from here on: at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
+  load_v(vb[0], 2);
   lds_barrier();
 
   // One chunk: product from X buffer u&1; state and V_{jj+1} into the other,
@@ -706,9 +708,9 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
         }
       }
     }
-    const int un = (u + 1) % PD;
+    const int un = (u + 1) % 2;
     put_v(Xn, vb[un], jj + 1);
-    load_v(vb[un], jj + 1 + PD);
+    load_v(vb[un], jj + 3);
     lds_barrier();
   };
 
