@@ -147,6 +147,42 @@ def build_inputs(spec, torch, lattn, dev):
     return raw, (q, K, V, ld, A, B)
 
 
+def fused_leg(spec, raw, torch, lattn, dev, steps, warmup):
+    """The same workload through the fused family entry point (decay operands
+    formed inside the chunk kernel from the raw parameters; nothing excluded
+    from the timed region), timed the same way."""
+    td = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    t = lambda x, d=td: torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
+    decay = raw["log_lambda"] if spec.family == "hdla" else raw["g"]
+    plan = lattn.FamilyPlan(spec.family, t(raw["q"]), t(raw["k"]), t(raw["v"]), t(decay, torch.float32),
+                            t(raw["beta"], torch.float32), chunk=spec.chunk)
+    for _ in range(warmup):
+        plan.forward()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        plan.forward()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    flops, _ = canonical_work(spec)
+    e = 2 if spec.dtype == "bf16" else 4
+    dec = 4 if spec.scalar_decay else 4 * spec.dk
+    per_tok = e * (2 * spec.dk + 2 * spec.dv) + dec + 4
+    nbytes = per_tok * spec.B * spec.H * spec.T + spec.B * spec.H * spec.dk * spec.dv * 4
+    return {
+        "entry": f"lattn_{spec.family}_chunk_fwd",
+        "ms_per_step": round(ms, 4),
+        "value": round(spec.B * spec.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "mfma_frac_canonical": round(flops / (ms / 1e3) / (PEAK["bf16_mfma_TFs"] * 1e12), 4),
+        "algorithmic_gb": round(nbytes / 1e9, 4),
+        "hbm_frac_algorithmic": round(nbytes / (ms / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
+    }
+
+
 def cpu_baseline(spec, raw, budget_s):
     """Time the fp64 oracle (generic form, as used for parity) on a bounded sample of
     (batch, head) rows of the same workload, on all host cores."""
@@ -295,6 +331,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if spec.family in ("hdla", "gdn") and kernels == "mfma_bf16":
+        result["fused_family"] = fused_leg(spec, raw, torch, lattn, dev, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, raw, args.cpu_budget_s)

@@ -189,6 +189,42 @@ int lattn_gdn_params(const lattn_dims* dims, const void* k, const void* v, const
                      const float* beta, void* A, void* B, void* V_out, hipStream_t stream);
 
 /*
+ * lattn_hdla_chunk_fwd -- the whole HDLA forward from its raw parameters, with
+ * the decay operands formed inside the chunk kernel instead of materialized
+ * (HDLA note, "Key design 2": the Householder congruence of a sigmoid-gated
+ * diagonal; "Key design 3": its diagonal-minus-rank-2 form and the chunk-wise
+ * algorithm).  Computes exactly what lattn_hdla_params followed by
+ * lattn_chunk_fwd (r_ab = 2, r_kv = 1, K = k, log_decay = log_lambda)
+ * computes, up to rounding: the decay operands and beta v are never rounded
+ * to the storage dtype.
+ *   q, k [B,H,T,d_k] dtype; v [B,H,T,d_v] dtype; log_lambda [B,H,T,d_k] fp32;
+ *   beta [B,H,T] fp32; out [B,H,T,d_v] dtype; final_state, initial_state as
+ *   lattn_chunk_fwd.  dims->decay_mode must be LATTN_DECAY_PER_CHANNEL.
+ * Workspace: lattn_hdla_chunk_fwd_workspace_size() bytes.  Errors as
+ * lattn_chunk_fwd.
+ */
+int lattn_hdla_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                         const float* log_lambda, const float* beta, int chunk, void* out,
+                         float* final_state, const float* initial_state, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+size_t lattn_hdla_chunk_fwd_workspace_size(const lattn_dims* dims, int chunk);
+
+/*
+ * lattn_gdn_chunk_fwd -- the whole Gated DeltaNet forward from its raw
+ * parameters (HLA note, "Prerequisites: Gated DeltaNet": decay
+ * exp(g)(I - beta k k^T), write beta k v^T), decay operands formed inside the
+ * chunk kernel.  Same result as lattn_gdn_params followed by lattn_chunk_fwd
+ * (r_ab = 1, r_kv = 1, K = k, log_decay = g), up to rounding.
+ *   q, k [B,H,T,d_k] dtype; v [B,H,T,d_v] dtype; g, beta [B,H,T] fp32.
+ *   dims->decay_mode must be LATTN_DECAY_SCALAR.
+ */
+int lattn_gdn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, int chunk, void* out,
+                        float* final_state, const float* initial_state, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+size_t lattn_gdn_chunk_fwd_workspace_size(const lattn_dims* dims, int chunk);
+
+/*
  * lattn_decay_range -- per chunk, the largest -G over the chunk's tokens and
  * channels, where G is the chunk-local inclusive cumulative log-decay.  The
  * chunk-wise form scales operands by exp(-G); the result must stay below

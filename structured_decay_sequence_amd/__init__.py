@@ -20,6 +20,7 @@ from ._lib import LattnError, LATTN_BF16, LATTN_FP32, LATTN_DECAY_PER_CHANNEL, L
 __all__ = [
     "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
     "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
+    "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan",
 ]
 
 
@@ -133,6 +134,56 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torc
                              0 if workspace is None else workspace.numel(), _stream(q.device))
     _lib.check(rc, "lattn_chunk_fwd")
     return out, final_state
+
+
+def _family_fwd(name: str, q, k, v, decay, beta, chunk, initial_state, out, final_state,
+                return_final_state, workspace):
+    Bb, H, T, dk = q.shape
+    dt = q.dtype
+    dv = v.shape[-1]
+    scalar = name == "gdn"
+    _need(q, dt, (Bb, H, T, dk), "q")
+    _need(k, dt, (Bb, H, T, dk), "k")
+    _need(v, dt, (Bb, H, T, dv), "v")
+    _need(decay, torch.float32, (Bb, H, T) if scalar else (Bb, H, T, dk), "g" if scalar else "log_lambda")
+    _need(beta, torch.float32, (Bb, H, T), "beta")
+    if initial_state is not None:
+        _need(initial_state, torch.float32, (Bb, H, dk, dv), "initial_state")
+    if out is None:
+        out = torch.empty((Bb, H, T, dv), dtype=dt, device=q.device)
+    _need(out, dt, (Bb, H, T, dv), "out")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((Bb, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, torch.float32, (Bb, H, dk, dv), "final_state")
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+    ws_bytes = int(getattr(lib, f"lattn_{name}_chunk_fwd_workspace_size")(ctypes.byref(dims), chunk))
+    if workspace is None:
+        workspace = _workspace(q.device, ws_bytes)
+    rc = getattr(lib, f"lattn_{name}_chunk_fwd")(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), chunk, _ptr(out),
+        _ptr(final_state), _ptr(initial_state), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(q.device))
+    _lib.check(rc, f"lattn_{name}_chunk_fwd")
+    return out, final_state
+
+
+def hdla_chunk_fwd(q, k, v, log_lambda, beta, chunk: int = 64, initial_state=None, out=None,
+                   final_state=None, return_final_state: bool = True, workspace=None):
+    """HDLA forward from its raw parameters (decay operands formed in the kernel).
+    q, k [B,H,T,dk]; v [B,H,T,dv]; log_lambda fp32 [B,H,T,dk]; beta fp32 [B,H,T].
+    Returns (out [B,H,T,dv], final_state [B,H,dk,dv] fp32 or None)."""
+    return _family_fwd("hdla", q, k, v, log_lambda, beta, chunk, initial_state, out, final_state,
+                       return_final_state, workspace)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, chunk: int = 64, initial_state=None, out=None, final_state=None,
+                  return_final_state: bool = True, workspace=None):
+    """Gated DeltaNet forward from its raw parameters.  q, k [B,H,T,dk]; v [B,H,T,dv];
+    g, beta fp32 [B,H,T].  Returns (out, final_state)."""
+    return _family_fwd("gdn", q, k, v, g, beta, chunk, initial_state, out, final_state,
+                       return_final_state, workspace)
 
 
 def chunk_summaries(k, v, log_decay, A=None, B=None, chunk: int = 64):
@@ -300,4 +351,35 @@ class ChunkPlan:
                                       self.r_ab, self.r_kv, self.chunk, p["out"], p["Sf"], p["S0"], p["ws"],
                                       self.ws_bytes, _stream(self.device))
         _lib.check(rc, "lattn_chunk_fwd")
+        return self.out, self.final_state
+
+
+class FamilyPlan:
+    """Pre-marshalled arguments of one fused family forward (``"hdla"``: decay
+    ``log_lambda`` [B,H,T,dk]; ``"gdn"``: decay ``g`` [B,H,T]), for repeated
+    timed calls.  ``forward()`` is exactly ``hdla_chunk_fwd`` / ``gdn_chunk_fwd``."""
+
+    def __init__(self, family, q, k, v, decay, beta, chunk=64, initial_state=None, return_final_state=True):
+        assert family in ("hdla", "gdn")
+        Bb, H, T, dk = q.shape
+        dv = v.shape[-1]
+        self.name = family
+        self.chunk = chunk
+        self.dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), family == "gdn")
+        self.lib = _lib.load()
+        self.fn = getattr(self.lib, f"lattn_{family}_chunk_fwd")
+        self.ws_bytes = int(getattr(self.lib, f"lattn_{family}_chunk_fwd_workspace_size")(ctypes.byref(self.dims),
+                                                                                            chunk))
+        self.workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        self.out = torch.empty((Bb, H, T, dv), dtype=q.dtype, device=q.device)
+        self.final_state = (torch.empty((Bb, H, dk, dv), dtype=torch.float32, device=q.device)
+                            if return_final_state else None)
+        self._keep = (q, k, v, decay, beta, initial_state)
+        self.args = (_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), chunk, _ptr(self.out),
+                     _ptr(self.final_state), _ptr(initial_state), _ptr(self.workspace), self.ws_bytes)
+        self.device = q.device
+
+    def forward(self):
+        rc = self.fn(ctypes.byref(self.dims), *self.args, _stream(self.device))
+        _lib.check(rc, f"lattn_{self.name}_chunk_fwd")
         return self.out, self.final_state

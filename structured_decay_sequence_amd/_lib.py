@@ -48,6 +48,10 @@ SIGNATURES = {
     "lattn_step": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "lattn_hdla_params": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "lattn_gdn_params": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "lattn_hdla_chunk_fwd": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "lattn_hdla_chunk_fwd_workspace_size": (_SZ, [_D, _I]),
+    "lattn_gdn_chunk_fwd": (_I, [_D, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "lattn_gdn_chunk_fwd_workspace_size": (_SZ, [_D, _I]),
     "lattn_decay_range": (_I, [_D, _P, _I, _P, _P]),
     "lattn_check_decay_range": (_I, [_D, _P, _I, _P, _P]),
     "lattn_chunk_fwd_kernels": (ctypes.c_char_p, [_D, _I, _I, _I]),

@@ -127,9 +127,115 @@ hipError_t run_scan(const lattn::Problem& p, void* ws, const void* v, void* out,
   return lattn::general_scan(p, ws, v, out, Sfin, S0, s);
 }
 
+// The fused family forwards (HDLA, Gated DeltaNet from their raw parameters).
+// On the MFMA path the decay operands are formed inside the prepare kernel;
+// elsewhere the parameter kernel materializes A, B and beta v in the front of
+// the workspace and the generic path runs on them.
+struct FusedPlan {
+  lattn::Problem p;
+  bool fast;
+  size_t a_bytes, v_bytes, gen_offset, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+FusedPlan fused_plan(const lattn_dims* d, int family, int chunk) {
+  FusedPlan f{};
+  const int r_ab = family == 1 ? 2 : 1;
+  f.p = make_problem(d, r_ab, 1, chunk);
+  f.fast = lattn::fast_supported(f.p);
+  if (f.fast) {
+    f.total = lattn::fast_workspace_bytes(f.p);
+    return f;
+  }
+  const size_t e = f.p.bf16 ? 2 : 4;
+  const size_t tok = static_cast<size_t>(f.p.BH * f.p.T);
+  f.a_bytes = round256(tok * r_ab * f.p.dk * e);
+  f.v_bytes = round256(tok * f.p.dv * e);
+  f.gen_offset = 2 * f.a_bytes + f.v_bytes;
+  f.total = f.gen_offset + lattn::general_plan(f.p).total_bytes;
+  return f;
+}
+
+int check_fused(int family, const lattn_dims* dims, int chunk) {
+  LATTN_TRY(check_dims(dims));
+  const int r_ab = family == 1 ? 2 : 1;
+  LATTN_TRY(check_chunk(chunk, r_ab, 1));
+  if (family == 1 && dims->decay_mode != LATTN_DECAY_PER_CHANNEL)
+    return fail(LATTN_EINVAL, "the HDLA forward needs LATTN_DECAY_PER_CHANNEL");
+  if (family == 2 && dims->decay_mode != LATTN_DECAY_SCALAR)
+    return fail(LATTN_EINVAL, "the Gated DeltaNet forward needs LATTN_DECAY_SCALAR");
+  return LATTN_OK;
+}
+
+int fused_fwd(int family, const lattn_dims* dims, const void* q, const void* k, const void* v,
+              const float* ld, const float* beta, int chunk, void* out, float* final_state,
+              const float* initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(check_fused(family, dims, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", need));
+  LATTN_TRY(check_ptr(k, "k", need));
+  LATTN_TRY(check_ptr(v, "v", need));
+  LATTN_TRY(check_ptr(ld, family == 1 ? "log_lambda" : "g", need));
+  LATTN_TRY(check_ptr(beta, "beta", need));
+  LATTN_TRY(check_ptr(out, "out", need));
+  LATTN_TRY(check_ptr(final_state, "final_state", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  const FusedPlan f = fused_plan(dims, family, chunk);
+  if (f.p.T == 0) return hip_status(lattn::launch_copy_state(f.p, initial_state, final_state, stream), "copy state");
+  if (workspace == nullptr || workspace_bytes < f.total)
+    return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, f.total);
+  LATTN_TRY(check_ptr(workspace, "workspace", true));
+  if (f.fast) {
+    LATTN_TRY(hip_status(lattn::fast_prepare_fused(f.p, family, q, k, ld, beta, workspace, stream), "prepare launch"));
+    LATTN_TRY(hip_status(lattn::fast_scan(f.p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
+    return ok();
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* A = ws;
+  void* B = ws + f.a_bytes;
+  void* V = ws + 2 * f.a_bytes;
+  void* gws = ws + f.gen_offset;
+  const lattn::Problem pp = make_problem(dims, family == 1 ? 2 : 1, 1, 1);
+  if (family == 1)
+    LATTN_TRY(hip_status(lattn::launch_hdla_params(pp, k, v, ld, beta, A, B, V, stream), "hdla params launch"));
+  else
+    LATTN_TRY(hip_status(lattn::launch_gdn_params(pp, k, v, ld, beta, A, B, V, stream), "gdn params launch"));
+  LATTN_TRY(hip_status(run_prepare(f.p, q, k, ld, A, B, gws, stream), "prepare launch"));
+  LATTN_TRY(hip_status(run_scan(f.p, gws, V, out, final_state, initial_state, stream), "scan launch"));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+int lattn_hdla_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                         const float* log_lambda, const float* beta, int chunk, void* out,
+                         float* final_state, const float* initial_state, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return fused_fwd(1, dims, q, k, v, log_lambda, beta, chunk, out, final_state, initial_state, workspace,
+                   workspace_bytes, stream);
+}
+
+size_t lattn_hdla_chunk_fwd_workspace_size(const lattn_dims* dims, int chunk) {
+  if (check_fused(1, dims, chunk) != LATTN_OK) return 0;
+  return fused_plan(dims, 1, chunk).total;
+}
+
+int lattn_gdn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, int chunk, void* out,
+                        float* final_state, const float* initial_state, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return fused_fwd(2, dims, q, k, v, g, beta, chunk, out, final_state, initial_state, workspace,
+                   workspace_bytes, stream);
+}
+
+size_t lattn_gdn_chunk_fwd_workspace_size(const lattn_dims* dims, int chunk) {
+  if (check_fused(2, dims, chunk) != LATTN_OK) return 0;
+  return fused_plan(dims, 2, chunk).total;
+}
+
 
 const char* lattn_version(void) { return "lattn 0.1 (gfx950)"; }
 

@@ -120,7 +120,11 @@ __device__ __forceinline__ bf16x4 xtr4(const __bf16* X, int r0, int c0, int lane
 //  * Gram blocks: the upper-triangular tiles of A~ [B~ ; Q~]^T, spread evenly
 //    over all waves.
 //  * solve and operator: wave w < KT owns the 16-column input tile w.
-template <int DK, int RAB, bool SCAL>
+// Operand source of the prepare kernel: the decay operands A, B given
+// (generic), or formed on the fly from a family's raw parameters.
+enum PrepMode { kGeneric = 0, kHdla = 1, kGdn = 2 };
+
+template <int DK, int RAB, bool SCAL, int MODE>
 struct PrepCfg {
   static constexpr int NA = kC * RAB;            // decay rows of a chunk
   static constexpr int NB = NA / 16;             // 16-row blocks of the solve
@@ -147,7 +151,10 @@ struct PrepCfg {
   static constexpr int R_EG = DK * 4;
   static constexpr int DIB = 520;                // bf16 per inverse block (hi, lo; padded)
   static constexpr int R_DI = NB * DIB * 2;
-  static constexpr int LDS = R_XL + R_XR + R_LD + R_LP + R_MA + R_EG + R_DI;
+  static constexpr int R_BT = MODE == kGeneric ? 0 : kC * 4;   // beta per token
+  static constexpr int LDS = R_XL + R_XR + R_LD + R_LP + R_MA + R_EG + R_DI + R_BT;
+  static_assert(MODE == kGeneric || (MODE == kHdla && RAB == 2 && !SCAL) || (MODE == kGdn && RAB == 1 && SCAL),
+                "fused modes: HDLA is rank 2 per channel, Gated DeltaNet rank 1 scalar");
   static_assert(NO == NW && KT <= NW, "wave roles: one wave per channel piece");
 };
 
@@ -158,6 +165,7 @@ struct FastPrepArgs {
   const float* ld;
   const __bf16* A;
   const __bf16* B;
+  const float* beta;   // fused modes: per-token beta [BH, T]
   __bf16* M;   // fragment-ordered chunk operators
 };
 
@@ -168,9 +176,9 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& raw, const float (&f)[8])
   return out;
 }
 
-template <int DK, int RAB, bool SCAL>
-__global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_kernel(FastPrepArgs a) {
-  using Cfg = PrepCfg<DK, RAB, SCAL>;
+template <int DK, int RAB, bool SCAL, int MODE>
+__global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepare_kernel(FastPrepArgs a) {
+  using Cfg = PrepCfg<DK, RAB, SCAL, MODE>;
   constexpr int NA = Cfg::NA, NB = Cfg::NB, LDA = Cfg::LDA, NW = Cfg::NW, LDB = Cfg::LDB;
   constexpr int MT = Cfg::MT, KT = Cfg::KT, NCS = Cfg::NCS, NTILE = Cfg::NTILE;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -181,6 +189,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_ker
   __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP);
   float* eGC = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA);
   __bf16* Dinv = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG);
+  float* betas = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG + Cfg::R_DI);
 
   const Problem& p = a.p;
   const int lane0 = threadIdx.x & 63;
@@ -192,6 +201,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_ker
   constexpr int NO = Cfg::NO, TPWV = Cfg::TPWV;
   f32x4 ldv[2];
   bf16x8 qv, kv, av[RAB], bv[RAB];
+  float btv = 0.f;
   auto chunk_n = [&](int64_t jb, int64_t& tok0) {
     const int64_t bh = jb / p.N, jc = jb % p.N;
     const int64_t t0 = jc * kC;
@@ -214,10 +224,14 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_ker
     }
     qv = *reinterpret_cast<const bf16x8*>(a.q + tok * DK + c0);
     kv = *reinterpret_cast<const bf16x8*>(a.k + tok * DK + c0);
+    if (MODE == kGeneric) {
 #pragma unroll
-    for (int r = 0; r < RAB; ++r) {
-      av[r] = *reinterpret_cast<const bf16x8*>(a.A + (tok * RAB + r) * DK + c0);
-      bv[r] = *reinterpret_cast<const bf16x8*>(a.B + (tok * RAB + r) * DK + c0);
+      for (int r = 0; r < RAB; ++r) {
+        av[r] = *reinterpret_cast<const bf16x8*>(a.A + (tok * RAB + r) * DK + c0);
+        bv[r] = *reinterpret_cast<const bf16x8*>(a.B + (tok * RAB + r) * DK + c0);
+      }
+    } else {
+      btv = a.beta[tok];
     }
   };
 
@@ -298,10 +312,51 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_ker
       }
       *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(NA + t, pc)) = scale8(qv, fp);
       *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(NA + t, pc)) = scale8(kv, fn);
+      if (MODE == kGeneric) {
 #pragma unroll
-      for (int r = 0; r < RAB; ++r) {
-        *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(RAB * t + r, pc)) = scale8(av[r], fn);
-        *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(RAB * t + r, pc)) = scale8(bv[r], fx);
+        for (int r = 0; r < RAB; ++r) {
+          *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(RAB * t + r, pc)) = scale8(av[r], fn);
+          *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(RAB * t + r, pc)) = scale8(bv[r], fx);
+        }
+      } else {
+        // Decay operands from the raw parameters.  With lambda = exp(l) and
+        // exp(G_{t-1}) lambda = exp(G_t):
+        //   HDLA  A = [b k, b u], B = [u - b c k, k], u = lambda k, c = k^T u
+        //         A~ = [b k e^{-G_t}, b k e^{-G_{t-1}}],
+        //         B~ = [k (e^{G_t} - b c e^{G_{t-1}}), k e^{G_{t-1}}]
+        //   GDN   A = e^g b k, B = k:  A~ = b k e^{-G_{t-1}},  B~ = k e^{G_{t-1}}
+        // The write K V^T = k (b v)^T keeps k here; b scales the operator's
+        // value columns instead (below), so V is the raw v.
+        const float b = pad ? 0.f : btv;
+        if (pc == 0) betas[t] = b;
+        float fnx[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) fnx[c] = b * fn[c] * __builtin_amdgcn_exp2f(l2[SCAL ? 0 : c]);
+        if (MODE == kGdn) {
+          *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(t, pc)) = scale8(kv, fnx);
+          *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(t, pc)) = scale8(kv, fx);
+        } else {
+          // c = sum_i k_i^2 lambda_i over all channels: this lane's piece, then
+          // the pieces of the same token (NO consecutive lanes).
+          float cp = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float kc = (float)kv[c];
+            cp += kc * kc * __builtin_amdgcn_exp2f(l2[c]);
+          }
+#pragma unroll
+          for (int sh = 1; sh < NO; sh *= 2) cp += __shfl_xor(cp, sh, 64);
+          float fb0[8], fa0[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            fb0[c] = fp[c] - b * cp * fx[c];
+            fa0[c] = b * fn[c];
+          }
+          *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(2 * t, pc)) = scale8(kv, fa0);
+          *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(2 * t + 1, pc)) = scale8(kv, fnx);
+          *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(2 * t, pc)) = scale8(kv, fb0);
+          *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(2 * t + 1, pc)) = scale8(kv, fx);
+        }
       }
     }
     // The next chunk's inputs travel while this one is solved.
@@ -449,8 +504,12 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL>::NT)) void fast_prepare_ker
       // ---- P5: operator tiles, transposed product: rows = this wave's input
       //      column tile, columns = output rows m (channels, then tokens):
       //      acc = sum_s WX[s][k] Bmat[m][s],  Bmat = [A~^T ; M_A].
+      // Fused modes: the value columns (chunk tokens) carry beta of their token.
+      f32x4 vsc = f32x4{1.f, 1.f, 1.f, 1.f};
+      if (MODE != kGeneric && kt >= DK / 16) vsc = *reinterpret_cast<const f32x4*>(betas + (kt - DK / 16) * 16 + 4 * lg);
       auto store = [&](int mt, const f32x4& v) {
-        *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) = to_bf16x4(v);
+        const f32x4 w = f32x4{v[0] * vsc[0], v[1] * vsc[1], v[2] * vsc[2], v[3] * vsc[3]};
+        *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) = to_bf16x4(w);
       };
       // Output rows that are channels (Acal, Z): base I or K~^T, scaled by exp(G_C).
 #pragma unroll 1
@@ -722,13 +781,13 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
 }
 
-template <int DK, int RAB, bool SCAL>
+template <int DK, int RAB, bool SCAL, int MODE>
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
-                       const void* A, const void* B, void* M, hipStream_t s) {
-  using Cfg = PrepCfg<DK, RAB, SCAL>;
+                       const void* A, const void* B, const float* beta, void* M, hipStream_t s) {
+  using Cfg = PrepCfg<DK, RAB, SCAL, MODE>;
   FastPrepArgs a{p, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ld,
-                 static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), static_cast<__bf16*>(M)};
-  const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB, SCAL>);
+                 static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), beta, static_cast<__bf16*>(M)};
+  const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB, SCAL, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (e != hipSuccess) return e;
   int dev = 0, cus = 0;
@@ -738,15 +797,15 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
   // One resident workgroup per compute unit, each walking a strided set of chunks.
   const int64_t jobs = p.BH * p.N;
   const int64_t grid = jobs < cus ? jobs : cus;
-  hipLaunchKernelGGL((fast_prepare_kernel<DK, RAB, SCAL>), dim3(grid), dim3(Cfg::NT), Cfg::LDS, s, a);
+  hipLaunchKernelGGL((fast_prepare_kernel<DK, RAB, SCAL, MODE>), dim3(grid), dim3(Cfg::NT), Cfg::LDS, s, a);
   return hipGetLastError();
 }
 
 template <int DK, int RAB>
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
                        const void* A, const void* B, void* M, hipStream_t s) {
-  return p.scalar ? launch_prep<DK, RAB, true>(p, q, k, ld, A, B, M, s)
-                  : launch_prep<DK, RAB, false>(p, q, k, ld, A, B, M, s);
+  return p.scalar ? launch_prep<DK, RAB, true, kGeneric>(p, q, k, ld, A, B, nullptr, M, s)
+                  : launch_prep<DK, RAB, false, kGeneric>(p, q, k, ld, A, B, nullptr, M, s);
 }
 
 template <int DK, int BV, int NWV, int PD>
@@ -784,6 +843,20 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
   if (p.dk == 128 && p.r_ab == 1) return launch_prep<128, 1>(p, q, k, ld, A, B, workspace, s);
   if (p.dk == 64 && p.r_ab == 2) return launch_prep<64, 2>(p, q, k, ld, A, B, workspace, s);
   if (p.dk == 64 && p.r_ab == 1) return launch_prep<64, 1>(p, q, k, ld, A, B, workspace, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const void* k, const float* ld,
+                              const float* beta, void* workspace, hipStream_t s) {
+  if (p.BH * p.N == 0) return hipSuccess;
+  if (family == kHdla && p.r_ab == 2 && !p.scalar) {
+    if (p.dk == 128) return launch_prep<128, 2, false, kHdla>(p, q, k, ld, nullptr, nullptr, beta, workspace, s);
+    if (p.dk == 64) return launch_prep<64, 2, false, kHdla>(p, q, k, ld, nullptr, nullptr, beta, workspace, s);
+  }
+  if (family == kGdn && p.r_ab == 1 && p.scalar) {
+    if (p.dk == 128) return launch_prep<128, 1, true, kGdn>(p, q, k, ld, nullptr, nullptr, beta, workspace, s);
+    if (p.dk == 64) return launch_prep<64, 1, true, kGdn>(p, q, k, ld, nullptr, nullptr, beta, workspace, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -50,6 +50,12 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s);
+// Fused-parameter prepare (family 1: HDLA from log-lambda and beta, rank 2,
+// per-channel decay; family 2: Gated DeltaNet from g and beta, rank 1,
+// scalar decay).  The operator's value columns carry beta, so the scan reads
+// the raw v.
+hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const void* k, const float* ld,
+                              const float* beta, void* workspace, hipStream_t s);
 
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, float* state, void* out,

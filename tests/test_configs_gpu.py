@@ -76,3 +76,27 @@ def test_workload_full_size(name):
         print(msg, flush=True)
         assert e_o <= tol and e_s <= tol, msg
         assert np.all(np.isfinite(g_out))
+
+
+@pytest.mark.parametrize("name", [n for n in workloads.CONFIG_ORDER if workloads.CONFIGS[n].family != "generic"])
+def test_workload_full_size_fused(name):
+    """The fused family forward on the same full-size workloads, sampled heads
+    against the structured oracle (which sees only the raw parameters)."""
+    spec = workloads.CONFIGS[name]
+    print(f"workload {name} (fused): {spec.describe()}", flush=True)
+    raw = workloads.raw_for(spec)
+    td = torch_dtype(spec.dtype)
+    q, k, v = dev(raw["q"], td), dev(raw["k"], td), dev(raw["v"], td)
+    if spec.family == "hdla":
+        out, S = lattn.hdla_chunk_fwd(q, k, v, dev(raw["log_lambda"]), dev(raw["beta"]), chunk=spec.chunk)
+    else:
+        out, S = lattn.gdn_chunk_fwd(q, k, v, dev(raw["g"]), dev(raw["beta"]), chunk=spec.chunk)
+    torch.cuda.synchronize()
+    tol = TOL[spec.dtype]
+    for b, h in _sample_heads(spec):
+        _, (r_out, r_S) = _oracle_head(spec, raw, b, h)
+        e_o = rel_err(host(out[b:b + 1, h:h + 1]), r_out)
+        e_s = rel_err(host(S[b:b + 1, h:h + 1]), r_S)
+        msg = f"{name} fused head ({b},{h}): out {e_o:.2e} state {e_s:.2e}"
+        print(msg, flush=True)
+        assert e_o <= tol and e_s <= tol, msg
