@@ -583,7 +583,9 @@ struct ScanCfg {
   static constexpr int NT = 64 * NWV;
   static constexpr int MPW = MT / NWV;     // output row tiles per wave
   static constexpr int NTN = BV / 16;      // output column tiles
-  static constexpr int LDX = KIN + 8;      // padded row of X^T (bf16)
+  // padded row of X^T (bf16): a row stride of 32 mod 64 bytes keeps the
+  // 16-row fragment reads free of LDS bank conflicts (measured on gfx950)
+  static constexpr int LDX = KIN + 16;
   static constexpr int XBUF = BV * LDX;    // elements of one X^T buffer
   static constexpr int LDO = BV + 8;       // padded row of the output stage
   static constexpr int OBUF = kC * LDO;
@@ -726,6 +728,10 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     for (int q = 0; q < MPW; ++q)
 #pragma unroll
       for (int nt = 0; nt < NTN; ++nt) acc[q][nt] = zero4();
+    // The next use of each operator register is chunk jj + PD: its load is
+    // issued as soon as this chunk's MFMAs have read it, spreading the loads
+    // over the product instead of bunching them after it.
+    const __bf16* Mnext = Mbh + static_cast<size_t>(jj + PD < N ? jj + PD : N - 1) * MSZ;
 #pragma unroll
     for (int kp = 0; kp < KP; ++kp) {
       bf16x8 bv[NTN];
@@ -735,8 +741,10 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
       for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
         for (int q = 0; q < MPW; ++q) acc[q][nt] = mfma32(mf[u][q][kp], bv[nt], acc[q][nt]);
+#pragma unroll
+      for (int q = 0; q < MPW; ++q)
+        mf[u][q][kp] = *reinterpret_cast<const bf16x8*>(Mnext + moff + (q * KP + kp) * 512);
     }
-    load_m(mf[u], jj + PD);
     if (jj > 0) flush_out(O0 + ((u + 1) & 1) * OBUF, jj - 1);
 #pragma unroll
     for (int q = 0; q < MPW; ++q) {
