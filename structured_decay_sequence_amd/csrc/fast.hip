@@ -210,12 +210,19 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
   };
   // Loads are unconditional: a padded token reads the chunk's last row (the
   // values are discarded), so no branch separates the loads from their use.
-  auto load = [&](int64_t jb, int ln) {
+  // Two parts, issued at different points of the previous chunk so that the
+  // load issue does not bunch up behind one barrier.
+  auto load_tok = [&](int64_t jb, int ln, int64_t& tok, int& c0) {
     int64_t tok0;
     const int n = chunk_n(jb, tok0);
     const int t = wave * TPWV + ln / NO;
-    const int64_t tok = tok0 + (t < n ? t : n - 1);
-    const int c0 = (ln % NO) * 8;
+    tok = tok0 + (t < n ? t : n - 1);
+    c0 = (ln % NO) * 8;
+  };
+  auto load_a = [&](int64_t jb, int ln) {
+    int64_t tok;
+    int c0;
+    load_tok(jb, ln, tok, c0);
     if (SCAL) {
       ldv[0][0] = a.ld[tok];
     } else {
@@ -224,6 +231,11 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     }
     qv = *reinterpret_cast<const bf16x8*>(a.q + tok * DK + c0);
     kv = *reinterpret_cast<const bf16x8*>(a.k + tok * DK + c0);
+  };
+  auto load_b = [&](int64_t jb, int ln) {
+    int64_t tok;
+    int c0;
+    load_tok(jb, ln, tok, c0);
     if (MODE == kGeneric) {
 #pragma unroll
       for (int r = 0; r < RAB; ++r) {
@@ -237,7 +249,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
 
   int64_t job = blockIdx.x;
   if (job >= total) return;
-  load(job, lane0);
+  load_a(job, lane0);
+  load_b(job, lane0);
   for (; job < total; job += gridDim.x) {
     // Lane-derived values are recomputed per chunk from an opaque copy of the
     // lane index: hoisted out of this loop they would all stay live at once.
@@ -360,10 +373,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       }
     }
     // The next chunk's inputs travel while this one is solved.
-    {
-      const int64_t nx = job + gridDim.x;
-      load(nx < total ? nx : total - 1, lane);
-    }
+    const int64_t nxt = job + gridDim.x < total ? job + gridDim.x : total - 1;
+    load_a(nxt, lane);
     lds_barrier();
 
     // ---- P2: Gram blocks.  P^T = A~ [B~ ; Q~]^T, tiles (rs, cs) with cs >= rs,
@@ -411,6 +422,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     for (int sl = 0; sl < Cfg::FULL_SLOTS; ++sl) gram_tile(wave + sl * NW);
     if (Cfg::FULL_SLOTS * NW + wave < NTILE) gram_tile(Cfg::FULL_SLOTS * NW + wave);
     lds_barrier();
+
+    load_b(nxt, lane);
 
     // ---- P3: inverses of the unit lower-triangular diagonal blocks (I + L_ii),
     //      fp32, stored as a bf16 pair (hi + lo) per entry so that the diagonal
