@@ -126,8 +126,10 @@ enum PrepMode { kGeneric = 0, kHdla = 1, kGdn = 2 };
 
 template <int DK, int RAB, bool SCAL, int MODE>
 struct PrepCfg {
-  static constexpr int NA = kC * RAB;            // decay rows of a chunk
+  static constexpr int NA = kC * RAB;            // decay rows of a chunk (0: diagonal decay only)
   static constexpr int NB = NA / 16;             // 16-row blocks of the solve
+  static constexpr int NBA = NB > 0 ? NB : 1;    // array extent
+  static constexpr int RB = RAB > 0 ? RAB : 1;   // divisor in code that rank 0 never runs
   static constexpr int KIN = DK + kNK;           // operator input width
   static constexpr int ROUT = DK + kC;           // operator output height
   static constexpr int KT = KIN / 16;
@@ -146,8 +148,8 @@ struct PrepCfg {
   static constexpr int R_XR = (NA + kNK) * XRow<DK>::LD * 2;
   static constexpr int R_LD = NB * LDB * 4;
   static constexpr int R_LP = (NB * (NB - 1) / 2) * 256 * 2;
-  static constexpr int R_MA = kC * LDA * 2;
-  static_assert(R_MA >= NW * DK * 4, "per-wave decay totals alias the M_A region");
+  // M_A; also holds the per-wave decay totals of the scaling phase
+  static constexpr int R_MA = kC * LDA * 2 > NW * DK * 4 ? kC * LDA * 2 : NW * DK * 4;
   static constexpr int R_EG = DK * 4;
   static constexpr int DIB = 520;                // bf16 per inverse block (hi, lo; padded)
   static constexpr int R_DI = NB * DIB * 2;
@@ -179,7 +181,8 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& raw, const float (&f)[8])
 template <int DK, int RAB, bool SCAL, int MODE>
 __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepare_kernel(FastPrepArgs a) {
   using Cfg = PrepCfg<DK, RAB, SCAL, MODE>;
-  constexpr int NA = Cfg::NA, NB = Cfg::NB, LDA = Cfg::LDA, NW = Cfg::NW, LDB = Cfg::LDB;
+  constexpr int NA = Cfg::NA, NB = Cfg::NB, NBA = Cfg::NBA, RB = Cfg::RB, LDA = Cfg::LDA, NW = Cfg::NW,
+                LDB = Cfg::LDB;
   constexpr int MT = Cfg::MT, KT = Cfg::KT, NCS = Cfg::NCS, NTILE = Cfg::NTILE;
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* Xl = reinterpret_cast<__bf16*>(smem);                             // [B~ ; Q~]
@@ -200,7 +203,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
   // ---- raw inputs of one chunk for this lane's (token, channel piece).
   constexpr int NO = Cfg::NO, TPWV = Cfg::TPWV;
   f32x4 ldv[2];
-  bf16x8 qv, kv, av[RAB], bv[RAB];
+  bf16x8 qv, kv, av[RAB > 0 ? RAB : 1], bv[RAB > 0 ? RAB : 1];
   float btv = 0.f;
   auto chunk_n = [&](int64_t jb, int64_t& tok0) {
     const int64_t bh = jb / p.N, jc = jb % p.N;
@@ -391,8 +394,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       // keeps everything when its first token is >= the last token of the s
       // rows, nothing when its last token is < their first.
       const int tt = cs - NB;
-      const bool zero = cs >= NB && 16 * tt + 15 < (16 * rs) / RAB;
-      const bool masked = cs < NB ? cs == rs : (!zero && 16 * tt < (16 * rs + 15) / RAB);
+      const bool zero = cs >= NB && 16 * tt + 15 < (16 * rs) / RB;
+      const bool masked = cs < NB ? cs == rs : (!zero && 16 * tt < (16 * rs + 15) / RB);
       f32x4 acc = zero4();
       if (!zero) {
 #pragma unroll
@@ -401,10 +404,10 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       }
       // lane holds P^T[s = rs*16 + 4lg + e][col = cs*16 + lr]
       if (masked) {
-        const int row = cs < NB ? (cs * 16 + lr) / RAB : tt * 16 + lr + 1;  // token bound: keep s/RAB < row
+        const int row = cs < NB ? (cs * 16 + lr) / RB : tt * 16 + lr + 1;  // token bound: keep s/RAB < row
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (!((rs * 16 + 4 * lg + e) / RAB < row)) acc[e] = 0.f;
+          if (!((rs * 16 + 4 * lg + e) / RB < row)) acc[e] = 0.f;
       }
       if (cs < NB) {
         if (cs == rs) {
@@ -448,7 +451,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     // Meanwhile each X wave forms the parts of its columns that need no solve:
     // L_K = B~ K~^T (its right-hand side, token(row) > chunk-write row) and
     // M_K^T = K~ Q~^T (the base of R, t >= s), from one copy of its K~ rows.
-    bf16x4 lk[NB], mk[kC / 16];
+    bf16x4 lk[NBA], mk[kC / 16];
     if (wave >= DK / 16 && wave < KT) {
       const int x = wave - DK / 16;
       bf16x8 kf[DK / 32];
@@ -461,7 +464,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(xrow8<DK>(Xl, i * 16, kb * 4, lane), kf[kb], g);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (!((i * 16 + 4 * lg + e) / RAB > x * 16 + lr)) g[e] = 0.f;
+          if (!((i * 16 + 4 * lg + e) / RB > x * 16 + lr)) g[e] = 0.f;
         lk[i] = to_bf16x4(g);
       }
 #pragma unroll
@@ -481,7 +484,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       const int kt = wave;
       // ---- P4: blocked forward substitution on this wave's columns:
       //      WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
-      bf16x4 wx[NB];
+      bf16x4 wx[NBA];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         f32x4 acc;
@@ -848,7 +851,7 @@ hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out
 }  // namespace
 
 bool fast_supported(const Problem& p) {
-  return p.bf16 && p.C == kC && p.r_kv == 1 && (p.r_ab == 1 || p.r_ab == 2) &&
+  return p.bf16 && p.C == kC && p.r_kv == 1 && (p.r_ab >= 0 && p.r_ab <= 2) &&
          (p.dk == 64 || p.dk == 128) && (p.dv % 64 == 0);
 }
 
@@ -864,6 +867,8 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
   if (p.dk == 128 && p.r_ab == 1) return launch_prep<128, 1>(p, q, k, ld, A, B, workspace, s);
   if (p.dk == 64 && p.r_ab == 2) return launch_prep<64, 2>(p, q, k, ld, A, B, workspace, s);
   if (p.dk == 64 && p.r_ab == 1) return launch_prep<64, 1>(p, q, k, ld, A, B, workspace, s);
+  if (p.dk == 128 && p.r_ab == 0) return launch_prep<128, 0>(p, q, k, ld, A, B, workspace, s);
+  if (p.dk == 64 && p.r_ab == 0) return launch_prep<64, 0>(p, q, k, ld, A, B, workspace, s);
   return hipErrorInvalidValue;
 }
 

@@ -42,7 +42,7 @@ hipError_t general_scan(const Problem& p, const void* workspace, const void* v, 
 hipError_t general_summaries(const Problem& p, const void* workspace, const void* v, float* sumA,
                              float* sumB, hipStream_t s);
 
-// bf16 MFMA path: bf16 storage, C = 64, r_kv = 1, r_ab in {1, 2}, d_k in {64, 128},
+// bf16 MFMA path: bf16 storage, C = 64, r_kv = 1, r_ab in {0, 1, 2}, d_k in {64, 128},
 // d_v a multiple of 64.  The workspace holds the fragment-ordered chunk operators.
 bool fast_supported(const Problem& p);
 size_t fast_workspace_bytes(const Problem& p);

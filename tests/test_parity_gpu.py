@@ -72,6 +72,10 @@ FAST_CASES = [
     (3, 3, 130, 64, 128, 2, "channel"),
     (1, 2, 129, 128, 256, 2, "channel"),
     (1, 9, 128, 128, 192, 1, "channel"),
+    # diagonal decay only (GLA, r_ab = 0)
+    (1, 2, 200, 128, 128, 0, "channel"),
+    (2, 2, 130, 64, 64, 0, "scalar"),
+    (1, 3, 64, 128, 192, 0, "channel"),
     # enough (batch, head) rows for the wide d_v slices of the scan (128 rows x 2 slices)
     (2, 64, 130, 128, 128, 2, "channel"),
     (4, 32, 192, 128, 128, 1, "scalar"),
