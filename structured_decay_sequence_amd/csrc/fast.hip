@@ -143,6 +143,13 @@ struct PrepCfg {
   static constexpr int NCS = NB + kC / 16;       // column blocks of the Gram tiles
   static constexpr int NTILE = NB * NCS - NB * (NB - 1) / 2;
   static constexpr int FULL_SLOTS = NTILE / NW;  // tile slots every wave has
+  // d_k = 128: the inversion and the X-wave products overlap the Gram tiles
+  // (NINV waves invert, NXW waves are X columns, NWORK waves take the
+  // off-diagonal tiles).  d_k = 64 has too few waves for that split.
+  static constexpr bool OVERLAP = DK == 128;
+  static constexpr int NINV = NB * 16 / 64;
+  static constexpr int NXW = KT - DK / 16;
+  static constexpr int NWORK = NW - NINV - NXW;
   // LDS regions (bytes)
   static constexpr int R_XL = (NA + kC) * XRow<DK>::LD * 2;
   static constexpr int R_XR = (NA + kNK) * XRow<DK>::LD * 2;
@@ -158,6 +165,7 @@ struct PrepCfg {
   static_assert(MODE == kGeneric || (MODE == kHdla && RAB == 2 && !SCAL) || (MODE == kGdn && RAB == 1 && SCAL),
                 "fused modes: HDLA is rank 2 per channel, Gated DeltaNet rank 1 scalar");
   static_assert(NO == NW && KT <= NW, "wave roles: one wave per channel piece");
+  static_assert(!OVERLAP || (NB % 4 == 0 && NWORK > 0), "overlapped Gram phase: four diagonal blocks per inverting wave");
 };
 
 struct FastPrepArgs {
@@ -381,14 +389,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     lds_barrier();
 
     // ---- P2: Gram blocks.  P^T = A~ [B~ ; Q~]^T, tiles (rs, cs) with cs >= rs,
-    //      spread evenly over all waves and written straight to LDS.
-    auto gram_tile = [&](int idx) {
-      int rs = 0;
-      while (idx >= NCS - rs) {
-        idx -= NCS - rs;
-        ++rs;
-      }
-      const int cs = rs + idx;
+    //      written straight to LDS.
+    auto gram_tile = [&](int rs, int cs) {
       // Which entries survive the token masks is uniform per tile except on
       // the diagonal: L tiles below it keep everything; an M_A tile (tokens tt)
       // keeps everything when its first token is >= the last token of the s
@@ -421,38 +423,43 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         *reinterpret_cast<bf16x4*>(MAs + (tt * 16 + lr) * LDA + rs * 16 + 4 * lg) = to_bf16x4(acc);
       }
     };
-#pragma unroll
-    for (int sl = 0; sl < Cfg::FULL_SLOTS; ++sl) gram_tile(wave + sl * NW);
-    if (Cfg::FULL_SLOTS * NW + wave < NTILE) gram_tile(Cfg::FULL_SLOTS * NW + wave);
-    lds_barrier();
-
-    load_b(nxt, lane);
+    // Tile idx of the row-major list of tiles (rs, cs), cs >= rs + skip.
+    auto gram_tile_at = [&](int idx, int skip) {
+      int rs = 0;
+      while (idx >= NCS - skip - rs) {
+        idx -= NCS - skip - rs;
+        ++rs;
+      }
+      gram_tile(rs, rs + skip + idx);
+    };
 
     // ---- P3: inverses of the unit lower-triangular diagonal blocks (I + L_ii),
     //      fp32, stored as a bf16 pair (hi + lo) per entry so that the diagonal
     //      apply below runs as two 16x16x32 MFMAs.  Thread (blk, c) forms
     //      column c of block blk by forward substitution.
-    if (tid < NB * 16) {
-      const int blk = tid / 16, c = tid % 16;
-      const float* Lb = Ldg + blk * LDB;
-      __bf16* Dh = Dinv + blk * Cfg::DIB;
-      float x[16];
+    auto invert_blocks = [&]() {
+      if (tid < NB * 16) {
+        const int blk = tid / 16, c = tid % 16;
+        const float* Lb = Ldg + blk * LDB;
+        __bf16* Dh = Dinv + blk * Cfg::DIB;
+        float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = (r == c) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float v = (r == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int m = 0; m < r; ++m) v -= Lb[r * 16 + m] * x[m];
-        x[r] = v;
-        const __bf16 h = (__bf16)v;
-        Dh[r * 16 + c] = h;
-        Dh[256 + r * 16 + c] = (__bf16)(v - (float)h);
+          for (int m = 0; m < r; ++m) v -= Lb[r * 16 + m] * x[m];
+          x[r] = v;
+          const __bf16 h = (__bf16)v;
+          Dh[r * 16 + c] = h;
+          Dh[256 + r * 16 + c] = (__bf16)(v - (float)h);
+        }
       }
-    }
-    // Meanwhile each X wave forms the parts of its columns that need no solve:
-    // L_K = B~ K~^T (its right-hand side, token(row) > chunk-write row) and
-    // M_K^T = K~ Q~^T (the base of R, t >= s), from one copy of its K~ rows.
+    };
+    // The parts of an X wave's columns that need no solve: L_K = B~ K~^T (its
+    // right-hand side, token(row) > chunk-write row) and M_K^T = K~ Q~^T (the
+    // base of R, t >= s), from one copy of its K~ rows.
     bf16x4 lk[NBA], mk[kC / 16];
-    if (wave >= DK / 16 && wave < KT) {
+    auto x_products = [&]() {
       const int x = wave - DK / 16;
       bf16x8 kf[DK / 32];
 #pragma unroll
@@ -477,8 +484,45 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
           if (!(tt * 16 + lr >= x * 16 + 4 * lg + e)) g[e] = 0.f;
         mk[tt] = to_bf16x4(g);
       }
+    };
+
+    if (Cfg::OVERLAP) {
+      // One phase for P2 and P3: the first NINV waves form the diagonal Gram
+      // blocks that their own lanes invert (four blocks per wave, so no
+      // other wave's result is waited for), the X waves form L_K and M_K, and
+      // the remaining waves share the off-diagonal Gram tiles.
+      constexpr int NINV = Cfg::NINV, NXW = Cfg::NXW, NWORK = Cfg::NWORK;
+      if (wave < NINV) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (wave * 4 + j < NB) gram_tile(wave * 4 + j, wave * 4 + j);
+        // the inversion reads entries written by other lanes of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        invert_blocks();
+      } else if (wave >= DK / 16 && wave < KT) {
+        x_products();
+      } else {
+        const int widx = wave < DK / 16 ? wave - NINV : wave - NINV - NXW;
+        constexpr int NOFF = NTILE - NB, FULL = NOFF / NWORK;
+#pragma unroll
+        for (int sl = 0; sl < FULL; ++sl) gram_tile_at(widx + sl * NWORK, 1);
+        if (FULL * NWORK + widx < NOFF) gram_tile_at(FULL * NWORK + widx, 1);
+      }
+      lds_barrier();
+      load_b(nxt, lane);
+    } else {
+      // All waves share the Gram tiles; then the inversion and the X-wave
+      // products run side by side.
+#pragma unroll
+      for (int sl = 0; sl < Cfg::FULL_SLOTS; ++sl) gram_tile_at(wave + sl * NW, 0);
+      if (Cfg::FULL_SLOTS * NW + wave < NTILE) gram_tile_at(Cfg::FULL_SLOTS * NW + wave, 0);
+      lds_barrier();
+      load_b(nxt, lane);
+      invert_blocks();
+      if (wave >= DK / 16 && wave < KT) x_products();
+      lds_barrier();
     }
-    lds_barrier();
 
     if (wave < KT) {
       const int kt = wave;
