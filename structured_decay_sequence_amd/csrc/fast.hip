@@ -158,8 +158,8 @@ struct PrepCfg {
   // M_A; also holds the per-wave decay totals of the scaling phase
   static constexpr int R_MA = kC * LDA * 2 > NW * DK * 4 ? kC * LDA * 2 : NW * DK * 4;
   static constexpr int R_EG = DK * 4;
-  static constexpr int DIB = 520;                // bf16 per inverse block (hi, lo; padded)
-  static constexpr int R_DI = NB * DIB * 2;
+  static constexpr int DIB = 260;                // floats per inverse block (padded)
+  static constexpr int R_DI = NB * DIB * 4;
   static constexpr int R_BT = MODE == kGeneric ? 0 : kC * 4;   // beta per token
   static constexpr int LDS = R_XL + R_XR + R_LD + R_LP + R_MA + R_EG + R_DI + R_BT;
   static_assert(MODE == kGeneric || (MODE == kHdla && RAB == 2 && !SCAL) || (MODE == kGdn && RAB == 1 && SCAL),
@@ -199,7 +199,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
   __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD);  // -L below diagonal
   __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP);
   float* eGC = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA);
-  __bf16* Dinv = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG);
+  float* Dinv = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG);
   float* betas = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG + Cfg::R_DI);
 
   const Problem& p = a.p;
@@ -434,14 +434,13 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     };
 
     // ---- P3: inverses of the unit lower-triangular diagonal blocks (I + L_ii),
-    //      fp32, stored as a bf16 pair (hi + lo) per entry so that the diagonal
-    //      apply below runs as two 16x16x32 MFMAs.  Thread (blk, c) forms
-    //      column c of block blk by forward substitution.
+    //      fp32, kept in fp32 for the diagonal apply below (fp32 MFMAs).
+    //      Thread (blk, c) forms column c of block blk by forward substitution.
     auto invert_blocks = [&]() {
       if (tid < NB * 16) {
         const int blk = tid / 16, c = tid % 16;
         const float* Lb = Ldg + blk * LDB;
-        __bf16* Dh = Dinv + blk * Cfg::DIB;
+        float* Db = Dinv + blk * Cfg::DIB;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -449,9 +448,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
 #pragma unroll
           for (int m = 0; m < r; ++m) v -= Lb[r * 16 + m] * x[m];
           x[r] = v;
-          const __bf16 h = (__bf16)v;
-          Dh[r * 16 + c] = h;
-          Dh[256 + r * 16 + c] = (__bf16)(v - (float)h);
+          Db[r * 16 + c] = v;
         }
       }
     };
@@ -549,15 +546,13 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
           zb[0] = zb[1] = zb[2] = zb[3] = (__bf16)0.f;
           acc = mfma32(cat(lds4(Lrow + (i - 1) * 256), zb), cat(wx[i - 1], zb), acc);
         }
-        // (I + L_ii)^{-1} acc with both factors split into bf16 hi + lo parts:
-        // [Dh Dl] x [ah ; ah] + [Dh Dl] x [al ; al].
-        const __bf16* Dp = Dinv + i * Cfg::DIB + lr * 16 + 4 * lg;
-        const bf16x8 dA = cat(lds4(Dp), lds4(Dp + 256));
-        const bf16x4 ah = to_bf16x4(acc);
-        const f32x4 ahf = to_f32x4(ah);
-        const bf16x4 al = to_bf16x4(f32x4{acc[0] - ahf[0], acc[1] - ahf[1], acc[2] - ahf[2], acc[3] - ahf[3]});
-        f32x4 o = mfma32(dA, cat(ah, ah), zero4());
-        o = mfma32(dA, cat(al, al), o);
+        // (I + L_ii)^{-1} acc in fp32: four 16x16x4 MFMAs over a permuted K,
+        // product e pairing column 4*lg + e of the inverse (this lane's row
+        // lr) with row 4*lg + e of acc (this lane's acc[e]).
+        const f32x4 dF = *reinterpret_cast<const f32x4*>(Dinv + i * Cfg::DIB + lr * 16 + 4 * lg);
+        f32x4 o = zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dF[e], acc[e], o, 0, 0, 0);
         wx[i] = to_bf16x4(o);
       }
 
