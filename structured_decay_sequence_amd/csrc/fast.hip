@@ -275,10 +275,14 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
 
     // ---- P0/P1: cumulative log-decay (base 2) and the decay-scaled operands
     //      B~ = B exp(G_{t-1}), Q~ = q exp(G_t), A~ = A exp(-G_t), K~ = K exp(-G_t).
-    {
+    //      Only the last chunk of a sequence can hold padding tokens; the
+    //      other chunks run a copy of this phase with the padding masks
+    //      compiled out.
+    auto scale_phase = [&](auto padded) {
+      constexpr bool PADDED = decltype(padded)::value;
       const int tg = lane / NO, pc = lane % NO;
       const int t = wave * TPWV + tg;
-      const bool pad = t >= ncur;
+      const bool pad = PADDED && t >= ncur;
       constexpr int NL = SCAL ? 1 : 8;
       float* wtot = reinterpret_cast<float*>(MAs);   // per-wave totals (M_A is not live yet)
       float l2[NL], x[NL];
@@ -382,6 +386,11 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
           *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(2 * t + 1, pc)) = scale8(kv, fx);
         }
       }
+    };
+    if (ncur < kC) {
+      scale_phase(std::integral_constant<bool, true>{});
+    } else {
+      scale_phase(std::integral_constant<bool, false>{});
     }
     // The next chunk's inputs travel while this one is solved.
     const int64_t nxt = job + gridDim.x < total ? job + gridDim.x : total - 1;
