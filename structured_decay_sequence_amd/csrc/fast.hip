@@ -394,12 +394,17 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     }
     // The next chunk's inputs travel while this one is solved.
     const int64_t nxt = job + gridDim.x < total ? job + gridDim.x : total - 1;
-    load_a(nxt, lane);
+    if (!Cfg::OVERLAP) load_a(nxt, lane);
     lds_barrier();
 
     // ---- P2: Gram blocks.  P^T = A~ [B~ ; Q~]^T, tiles (rs, cs) with cs >= rs,
     //      written straight to LDS.
-    auto gram_tile = [&](int rs, int cs) {
+    // A~ fragments of row block rs (the A operand of every tile in that row).
+    auto gram_a = [&](int rs, bf16x8 (&af)[DK / 32]) {
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) af[kb] = xrow8<DK>(Xr, rs * 16, kb * 4, lane);
+    };
+    auto gram_tile = [&](int rs, int cs, const bf16x8 (&af)[DK / 32]) {
       // Which entries survive the token masks is uniform per tile except on
       // the diagonal: L tiles below it keep everything; an M_A tile (tokens tt)
       // keeps everything when its first token is >= the last token of the s
@@ -411,7 +416,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       if (!zero) {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb)
-          acc = mfma32(xrow8<DK>(Xr, rs * 16, kb * 4, lane), xrow8<DK>(Xl, cs * 16, kb * 4, lane), acc);
+          acc = mfma32(af[kb], xrow8<DK>(Xl, cs * 16, kb * 4, lane), acc);
       }
       // lane holds P^T[s = rs*16 + 4lg + e][col = cs*16 + lr]
       if (masked) {
@@ -439,7 +444,9 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         idx -= NCS - skip - rs;
         ++rs;
       }
-      gram_tile(rs, rs + skip + idx);
+      bf16x8 af[DK / 32];
+      gram_a(rs, af);
+      gram_tile(rs, rs + skip + idx, af);
     };
 
     // ---- P3: inverses of the unit lower-triangular diagonal blocks (I + L_ii),
@@ -479,6 +486,10 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         for (int e = 0; e < 4; ++e)
           if (!((i * 16 + 4 * lg + e) / RB > x * 16 + lr)) g[e] = 0.f;
         lk[i] = to_bf16x4(g);
+        // One tile at a time, converted to bf16 right away: interleaved tiles
+        // kept in fp32 to the end only raise register pressure.
+        asm volatile("" : "+v"(lk[i]));
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int tt = 0; tt < kC / 16; ++tt) {
@@ -489,6 +500,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         for (int e = 0; e < 4; ++e)
           if (!(tt * 16 + lr >= x * 16 + 4 * lg + e)) g[e] = 0.f;
         mk[tt] = to_bf16x4(g);
+        asm volatile("" : "+v"(mk[tt]));
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -500,8 +513,13 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       constexpr int NINV = Cfg::NINV, NXW = Cfg::NXW, NWORK = Cfg::NWORK;
       if (wave < NINV) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (wave * 4 + j < NB) gram_tile(wave * 4 + j, wave * 4 + j);
+        for (int j = 0; j < 4; ++j) {
+          if (wave * 4 + j < NB) {
+            bf16x8 af[DK / 32];
+            gram_a(wave * 4 + j, af);
+            gram_tile(wave * 4 + j, wave * 4 + j, af);
+          }
+        }
         // the inversion reads entries written by other lanes of this wave
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -509,13 +527,35 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       } else if (wave >= DK / 16 && wave < KT) {
         x_products();
       } else {
+        // A contiguous run of the row-major list of off-diagonal tiles, so
+        // that consecutive tiles share their A~ row block (read once per row).
         const int widx = wave < DK / 16 ? wave - NINV : wave - NINV - NXW;
-        constexpr int NOFF = NTILE - NB, FULL = NOFF / NWORK;
-#pragma unroll
-        for (int sl = 0; sl < FULL; ++sl) gram_tile_at(widx + sl * NWORK, 1);
-        if (FULL * NWORK + widx < NOFF) gram_tile_at(FULL * NWORK + widx, 1);
+        constexpr int NOFF = NTILE - NB;
+        const int lo = widx * NOFF / NWORK, hi = (widx + 1) * NOFF / NWORK;
+        int rs = 0, k = lo;
+        while (k >= NCS - 1 - rs) {
+          k -= NCS - 1 - rs;
+          ++rs;
+        }
+        int cs = rs + 1 + k, ars = -1;
+        bf16x8 af[DK / 32];
+#pragma unroll 1
+        for (int idx = lo; idx < hi; ++idx) {
+          if (rs != ars) {
+            gram_a(rs, af);
+            ars = rs;
+          }
+          gram_tile(rs, cs, af);
+          if (++cs == NCS) {
+            ++rs;
+            cs = rs + 1;
+          }
+        }
       }
       lds_barrier();
+      // Issued only now, so that these registers are free during the Gram
+      // phase; the solve and the operator product still cover their latency.
+      load_a(nxt, lane);
       load_b(nxt, lane);
     } else {
       // All waves share the Gram tiles; then the inversion and the X-wave
