@@ -138,7 +138,7 @@ struct PrepCfg {
   static constexpr int NW = NO > KT ? NO : KT;
   static constexpr int NT = 64 * NW;
   static constexpr int TPWV = 64 / NO;           // tokens per wave in the scaling phase
-  static constexpr int LDA = NA + 8;             // padded row of M_A (bf16)
+  static constexpr int LDA = NA + 16;            // padded row of M_A (bf16; 32 mod 64 bytes)
   static constexpr int LDB = 260;                // floats per diagonal block (padded)
   static constexpr int NCS = NB + kC / 16;       // column blocks of the Gram tiles
   static constexpr int NTILE = NB * NCS - NB * (NB - 1) / 2;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
   __bf16* Xl = reinterpret_cast<__bf16*>(smem);                             // [B~ ; Q~]
   __bf16* Xr = reinterpret_cast<__bf16*>(smem + Cfg::R_XL);                 // [A~ ; K~]
   float* Ldg = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR);      // diagonal blocks
-  __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD);  // -L below diagonal
+  __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD);  // L below diagonal
   __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP);
   float* eGC = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA);
   float* Dinv = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG);
@@ -430,11 +430,11 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
           *reinterpret_cast<f32x4*>(Ldg + cs * LDB + lr * 16 + 4 * lg) = acc;
         } else {
           const int blk = cs * (cs - 1) / 2 + rs;
-          *reinterpret_cast<bf16x4*>(Lpk + blk * 256 + lr * 16 + 4 * lg) =
-              to_bf16x4(f32x4{-acc[0], -acc[1], -acc[2], -acc[3]});
+          *reinterpret_cast<bf16x4*>(Lpk + blk * 256 + lr * 16 + 4 * lg) = to_bf16x4(acc);
         }
       } else {
-        *reinterpret_cast<bf16x4*>(MAs + (tt * 16 + lr) * LDA + rs * 16 + 4 * lg) = to_bf16x4(acc);
+        // columns s = 32b + 16h + 4g + e at 32b + 8g + 4h + e (the K order of the operator product)
+        *reinterpret_cast<bf16x4*>(MAs + (tt * 16 + lr) * LDA + (rs >> 1) * 32 + (rs & 1) * 4 + 8 * lg) = to_bf16x4(acc);
       }
     };
     // Tile idx of the row-major list of tiles (rs, cs), cs >= rs + skip.
@@ -602,7 +602,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         f32x4 o = zero4();
 #pragma unroll
         for (int e = 0; e < 4; ++e) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dF[e], acc[e], o, 0, 0, 0);
-        wx[i] = to_bf16x4(o);
+        wx[i] = to_bf16x4(f32x4{-o[0], -o[1], -o[2], -o[3]});   // -WX_i
       }
 
       // ---- P5: operator tiles, transposed product: rows = this wave's input
@@ -618,44 +618,36 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       // Output rows that are channels (Acal, Z): base I or K~^T, scaled by exp(G_C).
 #pragma unroll 1
       for (int mt = 0; mt < DK / 16; ++mt) {
+        // The product accumulates onto the base: base + sum (-WX) Bmat.
         f32x4 acc = zero4();
+        if (kt < DK / 16) {
+          if (kt == mt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = (4 * lg + e == lr) ? 1.f : 0.f;
+          }
+        } else {
+          acc = to_f32x4(xtr4<DK>(Xr, NA + kt * 16 - DK, mt * 16, lane));
+        }
 #pragma unroll
         for (int jb = 0; jb < NB; jb += 2)
           acc = mfma32(cat(wx[jb], wx[jb + 1]),
                        cat(xtr4<DK>(Xr, jb * 16, mt * 16, lane), xtr4<DK>(Xr, jb * 16 + 16, mt * 16, lane)), acc);
         const float sc = eGC[mt * 16 + lr];
-        f32x4 base = zero4();
-        if (kt < DK / 16) {
-          if (kt == mt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) base[e] = (4 * lg + e == lr) ? 1.f : 0.f;
-          }
-        } else {
-          base = to_f32x4(xtr4<DK>(Xr, NA + kt * 16 - DK, mt * 16, lane));
-        }
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = sc * (base[e] - acc[e]);
-        store(mt, v);
+        store(mt, f32x4{sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]});
       }
       // Output rows that are tokens (Qbar, R): base Q~ or M_K.
 #pragma unroll
       for (int tt = 0; tt < kC / 16; ++tt) {
-        const __bf16* Brow = MAs + (tt * 16 + lr) * LDA;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int jb = 0; jb < NB; jb += 2)
-          acc = mfma32(cat(wx[jb], wx[jb + 1]), cat(lds4(Brow + jb * 16 + 4 * lg), lds4(Brow + (jb + 1) * 16 + 4 * lg)), acc);
-        f32x4 base;
+        const __bf16* Brow = MAs + (tt * 16 + lr) * LDA + 8 * lg;
+        f32x4 acc;
         if (kt < DK / 16) {
-          base = to_f32x4(lds4(Xl + xoff<DK>(NA + tt * 16 + lr, 2 * kt + (lg >> 1)) + 4 * (lg & 1)));
+          acc = to_f32x4(lds4(Xl + xoff<DK>(NA + tt * 16 + lr, 2 * kt + (lg >> 1)) + 4 * (lg & 1)));
         } else {
-          base = to_f32x4(mk[tt]);   // M_K^T
+          acc = to_f32x4(mk[tt]);   // M_K^T
         }
-        f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = base[e] - acc[e];
-        store(DK / 16 + tt, v);
+        for (int jb = 0; jb < NB; jb += 2) acc = mfma32(cat(wx[jb], wx[jb + 1]), lds8(Brow + jb * 16), acc);
+        store(DK / 16 + tt, acc);
       }
     }
     // P5 reads Xl, Xr and M_A, which the next chunk overwrites.
