@@ -230,7 +230,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the (batch, head) rows shard with no communication, see DESIGN.md",
+              f"WORLD_SIZE {world}); across GPUs the (batch, head) rows would shard with no communication",
               file=sys.stderr)
         sys.exit(2)
 
