@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -98,12 +99,21 @@ def kernel_peak(kernels, dtype, bound):
     return (PEAK["bf16_mfma_TFs"] if dtype == "bf16" else PEAK["fp32_mfma_TFs"]), "TFLOP/s"
 
 
+def _code_tokens(text):
+    """Source text without comments and with whitespace collapsed, so that an
+    edit of comments or layout alone leaves the hash (and the counters keyed
+    on it) valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernels):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES.get(kernels, []) + ["structured_decay_sequence_amd/csrc/common.hpp"]:
         path = os.path.join(ROOT, rel)
         if os.path.exists(path):
-            h.update(open(path, "rb").read())
+            h.update(_code_tokens(open(path).read()).encode())
     return h.hexdigest()[:16]
 
 

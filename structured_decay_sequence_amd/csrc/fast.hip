@@ -1,5 +1,5 @@
 // bf16 MFMA path (gfx950) for chunk C = 64, write rank r_kv = 1, decay rank
-// r_ab in {1, 2}, d_k in {64, 128}: the Gated DeltaNet and HDLA shapes.
+// r_ab in {0, 1, 2}, d_k in {64, 128}: the GLA, Gated DeltaNet and HDLA shapes.
 //
 // It computes the same chunk operator as the general path (HDLA note, "Key
 // design 3": rank-generalized WY form; HLA note, "Affine maps and closure
@@ -8,10 +8,11 @@
 // with bf16 MFMA operands and fp32 accumulation; the triangular solve applies
 // its 16x16 diagonal inverses in fp32.
 //
-// prepare kernel: one workgroup per (batch*head, chunk), one wave per
-// 16-column tile of the chunk operator's input side (the d_k "W" columns,
-// then the 64 "X" columns); the solve and the final product run per wave on
-// its own columns with no barrier.  The operator is stored in MFMA operand
+// prepare kernel: persistent, one workgroup per compute unit walking the
+// (batch*head, chunk) jobs; in the solve and the final product one wave owns
+// each 16-column tile of the chunk operator's input side (the d_k "W"
+// columns, then the 64 "X" columns) and runs on its own columns with no
+// barrier.  The operator is stored in MFMA operand
 // order: each 16x16 tile is the A-operand fragment of a 16x16x16 MFMA (lane
 // l holds row l%16, columns 4*(l/16)..+3), and the tiles of columns 2m and
 // 2m+1 are interleaved per lane, so one 16-byte load gives a lane the eight
@@ -117,8 +118,10 @@ __device__ __forceinline__ bf16x4 xtr4(const __bf16* X, int r0, int c0, int lane
 //    rows.  The chunk-local cumulative log-decay is a prefix sum over tokens:
 //    inside the wave by lane shuffles, across waves through per-wave totals in
 //    LDS.  It is kept in base-2 units so that every decay factor is one exp2.
-//  * Gram blocks: the upper-triangular tiles of A~ [B~ ; Q~]^T, spread evenly
-//    over all waves.
+//  * Gram blocks: the upper-triangular tiles of A~ [B~ ; Q~]^T.  At d_k = 128
+//    the diagonal blocks go to the waves that invert them and the rest to the
+//    waves with no X column, in contiguous runs; at d_k = 64 all waves share
+//    them, then invert.
 //  * solve and operator: wave w < KT owns the 16-column input tile w.
 // Operand source of the prepare kernel: the decay operands A, B given
 // (generic), or formed on the fly from a family's raw parameters.
