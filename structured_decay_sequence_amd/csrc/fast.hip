@@ -483,8 +483,12 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         f32x4 g = zero4();
+        // A tile whose rows all belong to tokens at or before the column
+        // block's first token is all masked: skip its product.
+        if ((i * 16 + 15) / RB > x * 16) {
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(xrow8<DK>(Xl, i * 16, kb * 4, lane), kf[kb], g);
+          for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(xrow8<DK>(Xl, i * 16, kb * 4, lane), kf[kb], g);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (!((i * 16 + 4 * lg + e) / RB > x * 16 + lr)) g[e] = 0.f;
@@ -497,8 +501,10 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
 #pragma unroll
       for (int tt = 0; tt < kC / 16; ++tt) {
         f32x4 g = zero4();
+        if (tt >= x) {   // earlier token blocks are all masked
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(kf[kb], xrow8<DK>(Xl, NA + tt * 16, kb * 4, lane), g);
+          for (int kb = 0; kb < DK / 32; ++kb) g = mfma32(kf[kb], xrow8<DK>(Xl, NA + tt * 16, kb * 4, lane), g);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (!(tt * 16 + lr >= x * 16 + 4 * lg + e)) g[e] = 0.f;
