@@ -35,8 +35,6 @@ PEAK = {  # MI355X published peaks
     "hbm_GBs": 8000.0,
     "bf16_mfma_TFs": 2500.0,
     "fp32_mfma_TFs": 157.3,
-    # fp32 vector without packed-fp32 issue: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
-    "fp32_valu_TFs": 78.6,
 }
 KERNEL_SOURCES = {
     "general_fp32": ["structured_decay_sequence_amd/csrc/general.hip"],
@@ -94,9 +92,11 @@ def kernel_work(spec, kernels):
 def kernel_peak(kernels, dtype, bound):
     if bound == "hbm":
         return PEAK["hbm_GBs"], "GB/s"
+    # The bf16 path multiplies on bf16 MFMAs; the general path keeps fp32
+    # operands and multiplies on fp32 MFMAs (whatever the storage dtype).
     if kernels == "general_fp32":
-        return PEAK["fp32_valu_TFs"], "TFLOP/s"
-    return (PEAK["bf16_mfma_TFs"] if dtype == "bf16" else PEAK["fp32_mfma_TFs"]), "TFLOP/s"
+        return PEAK["fp32_mfma_TFs"], "TFLOP/s"
+    return PEAK["bf16_mfma_TFs"], "TFLOP/s"
 
 
 def _code_tokens(text):
@@ -302,7 +302,7 @@ def main():
         bound, achieved, unit = "hbm", work["bytes"] / (times[dom] / 1e3) / 1e9, "GB/s"
         peak = PEAK["hbm_GBs"]
     else:
-        bound = "alu" if kernels == "general_fp32" else "mfma"
+        bound = "mfma"
         achieved, unit, peak = work["flops"] / (times[dom] / 1e3) / 1e12, "TFLOP/s", comp_peak
     traffic = measured_traffic(kernels, dom, spec.name)
 
@@ -325,7 +325,8 @@ def main():
             "d_k": spec.dk, "d_v": spec.dv, "chunk": spec.chunk, "r_ab": spec.r_ab, "r_kv": spec.r_kv,
             "storage": spec.dtype, "kernels": kernels, "parallelism": "single-gpu",
         },
-        "mfma_frac_canonical": round(flops / (ms_step / 1e3) / (PEAK["bf16_mfma_TFs"] * 1e12), 4),
+        # against the matrix peak of the type the path multiplies in (bf16, or fp32 on the general path)
+        "mfma_frac_canonical": round(flops / (ms_step / 1e3) / (comp_peak * 1e12), 4),
         "hbm_frac_algorithmic": round(nbytes / (ms_step / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
         "canonical_gflop": round(flops / 1e9, 2),
         "algorithmic_gb": round(nbytes / 1e9, 4),

@@ -14,13 +14,66 @@
 //   [S_j ; O_j] = M_j [S_{j-1} ; V_j].
 // The prepare kernel forms M_j for every chunk in parallel; the scan kernel
 // walks the chunks of one (batch, head, d_v slice) in order.
+//
+// Every product is a wave-level 16x16 tile on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32), so the path keeps fp32 operands and fp32
+// accumulation.  A 16-deep slice of K is taken as four such MFMAs over a
+// permuted K: lane (i, g) reads the 16-byte piece k0 + 4g .. k0 + 4g + 3 of
+// its row of each operand, and product e pairs the e-th value of both.  The
+// same permutation makes a tile in accumulator layout (lane (i, g) holding
+// rows 4g .. 4g + 3 of column i) usable as the right operand of the next
+// product with no data exchange between lanes.
+//
+// The prepare kernel's operands live in a per-workgroup slot of the
+// workspace (row-major fp32); M_j is stored row-major fp32.
 #include "common.hpp"
 #include "kernels.hpp"
+
 
 namespace lattn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;   // four waves
+constexpr int kWaves = kThreads / 64;
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// acc += A B over one 16-deep K slice, in the permuted-K form described above:
+// a = this lane's 4 values of its A row, b = its 4 values of its B column.
+__device__ __forceinline__ f32x4 mfma16(const f32x4& a, const f32x4& b, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// Offsets (floats) of the prepare kernel's per-slot arrays, all row-major.
+struct SlotLayout {
+  size_t G, Bt, At, AtT, Kt, KtT, Qt, L, LK, MA, MK, WXT, total;
+  __host__ __device__ explicit SlotLayout(const Problem& p) {
+    const size_t C = p.C, dk = p.dk, na = p.na(), nk = p.nk(), nc = p.mcols();
+    size_t o = 0;
+    G = o;   o += C * dk;     // chunk-local inclusive cumulative log-decay
+    Bt = o;  o += na * dk;    // B (.) exp(G_{t-1})
+    At = o;  o += na * dk;    // A (.) exp(-G_t)
+    AtT = o; o += dk * na;    // At transposed
+    Kt = o;  o += nk * dk;    // K (.) exp(-G_t)
+    KtT = o; o += dk * nk;    // Kt transposed
+    Qt = o;  o += C * dk;     // q (.) exp(G_t)
+    L = o;   o += na * na;    // Bt At^T, token(row) > token(col); lower 16x16 blocks only
+    LK = o;  o += na * nk;    // Bt Kt^T, token(row) > token(col)
+    MA = o;  o += C * na;     // Qt At^T, token(row) >= token(col)
+    MK = o;  o += C * nk;     // Qt Kt^T, token(row) >= token(col)
+    WXT = o; o += nc * na;    // [W X] transposed: column c of the solve at row c
+    total = (o + 63) & ~static_cast<size_t>(63);
+  }
+};
+
+constexpr int kMaxNB = 32;   // 16-row blocks of the solve: chunk * r_ab <= 512
+constexpr int kDIB = 260;    // floats per stored 16x16 inverse (padded)
 
 struct PrepArgs {
   Problem p;
@@ -36,25 +89,37 @@ struct PrepArgs {
 
 template <typename TI>
 __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
+  __shared__ __align__(16) float Dinv[kMaxNB * kDIB];   // (I + L_ii)^{-1}, fp32
+  __shared__ float eGC[256];                             // exp(G_C) per channel
   const Problem& p = a.p;
   const int dk = p.dk, C = p.C, r_ab = p.r_ab, r_kv = p.r_kv;
   const int na = p.na(), nk = p.nk(), ncol = p.mcols();
-  const int tid = threadIdx.x;
-  float* G = a.scratch + static_cast<size_t>(blockIdx.x) * a.slot_floats;
-  float* Bt = G + static_cast<size_t>(C) * dk;
-  float* At = Bt + static_cast<size_t>(na) * dk;
-  float* Kt = At + static_cast<size_t>(na) * dk;
-  float* Qt = Kt + static_cast<size_t>(nk) * dk;
-  float* L = Qt + static_cast<size_t>(C) * dk;
-  float* LK = L + static_cast<size_t>(na) * na;
-  float* MA = LK + static_cast<size_t>(na) * nk;
-  float* MK = MA + static_cast<size_t>(C) * na;
-  float* WX = MK + static_cast<size_t>(C) * nk;
+  const int nbA = na / 16, nbK = nk / 16, nbC = C / 16, dkT = dk / 16;
+  const int MT = p.mrows() / 16, KTc = ncol / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const SlotLayout S(p);
+  float* slot = a.scratch + static_cast<size_t>(blockIdx.x) * a.slot_floats;
+  float* G = slot + S.G;
+  float* Bt = slot + S.Bt;
+  float* At = slot + S.At;
+  float* AtT = slot + S.AtT;
+  float* Kt = slot + S.Kt;
+  float* KtT = slot + S.KtT;
+  float* Qt = slot + S.Qt;
+  float* L = slot + S.L;
+  float* LK = slot + S.LK;
+  float* MA = slot + S.MA;
+  float* MK = slot + S.MK;
+  float* WXT = slot + S.WXT;
   const TI* q = static_cast<const TI*>(a.q);
   const TI* kp = static_cast<const TI*>(a.k);
   const TI* Ap = static_cast<const TI*>(a.A);
   const TI* Bp = static_cast<const TI*>(a.B);
   const int64_t total = p.BH * p.N;
+  const int nL = nbA * (nbA + 1) / 2, nLK = nbA * nbK, nMA = nbC * nbA, nMK = nbC * nbK;
+  const int ntile = nL + nLK + nMA + nMK;
 
   for (int64_t job = blockIdx.x; job < total; job += gridDim.x) {
     const int64_t bh = job / p.N;
@@ -72,94 +137,190 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
         g += l;
         G[t * dk + i] = g;
       }
+      eGC[i] = expf(g);
     }
     __syncthreads();
 
-    // 2. decay-scaled operands (zero rows for padded tokens).
+    // 2. decay-scaled operands (zero rows for padded tokens), with the
+    //    transposed copies that the operator product reads as row operands.
     for (int e = tid; e < na * dk; e += kThreads) {
       const int s = e / dk, i = e % dk, t = s / r_ab;
       float bv = 0.f, av = 0.f;
       if (t < n) {
         const size_t idx = (static_cast<size_t>(tok0 + t) * r_ab + (s % r_ab)) * dk + i;
-        bv = Elem<TI>::load(Bp, idx);
-        av = Elem<TI>::load(Ap, idx);
+        bv = Elem<TI>::load(Bp, idx) * (t > 0 ? expf(G[(t - 1) * dk + i]) : 1.f);
+        av = Elem<TI>::load(Ap, idx) * expf(-G[t * dk + i]);
       }
-      const float gex = t > 0 ? G[(t - 1) * dk + i] : 0.f;
-      Bt[e] = bv * expf(gex);
-      At[e] = av * expf(-G[t * dk + i]);
+      Bt[e] = bv;
+      At[e] = av;
+      AtT[static_cast<size_t>(i) * na + s] = av;
     }
     for (int e = tid; e < nk * dk; e += kThreads) {
       const int s = e / dk, i = e % dk, t = s / r_kv;
       float kv = 0.f;
-      if (t < n) kv = Elem<TI>::load(kp, (static_cast<size_t>(tok0 + t) * r_kv + (s % r_kv)) * dk + i);
-      Kt[e] = kv * expf(-G[t * dk + i]);
+      if (t < n)
+        kv = Elem<TI>::load(kp, (static_cast<size_t>(tok0 + t) * r_kv + (s % r_kv)) * dk + i) * expf(-G[t * dk + i]);
+      Kt[e] = kv;
+      KtT[static_cast<size_t>(i) * nk + s] = kv;
     }
     for (int e = tid; e < C * dk; e += kThreads) {
       const int t = e / dk, i = e % dk;
       float qv = 0.f;
-      if (q != nullptr && t < n) qv = Elem<TI>::load(q, static_cast<size_t>(tok0 + t) * dk + i);
-      Qt[e] = qv * expf(G[e]);
+      if (q != nullptr && t < n) qv = Elem<TI>::load(q, static_cast<size_t>(tok0 + t) * dk + i) * expf(G[e]);
+      Qt[e] = qv;
     }
     __syncthreads();
 
-    // 3. masked Gram blocks.
-    for (int e = tid; e < na * na; e += kThreads) {
-      const int r = e / na, c = e % na;
-      float s = 0.f;
-      if (r / r_ab > c / r_ab)
-        for (int i = 0; i < dk; ++i) s += Bt[r * dk + i] * At[c * dk + i];
-      L[e] = s;
-    }
-    for (int e = tid; e < na * nk; e += kThreads) {
-      const int r = e / nk, c = e % nk;
-      float s = 0.f;
-      if (r / r_ab > c / r_kv)
-        for (int i = 0; i < dk; ++i) s += Bt[r * dk + i] * Kt[c * dk + i];
-      LK[e] = s;
-    }
-    for (int e = tid; e < C * na; e += kThreads) {
-      const int t = e / na, c = e % na;
-      float s = 0.f;
-      if (t >= c / r_ab)
-        for (int i = 0; i < dk; ++i) s += Qt[t * dk + i] * At[c * dk + i];
-      MA[e] = s;
-    }
-    for (int e = tid; e < C * nk; e += kThreads) {
-      const int t = e / nk, c = e % nk;
-      float s = 0.f;
-      if (t >= c / r_kv)
-        for (int i = 0; i < dk; ++i) s += Qt[t * dk + i] * Kt[c * dk + i];
-      MK[e] = s;
-    }
-    __syncthreads();
-
-    // 4. forward substitution, one token (r_ab rows) at a time: rows of one token
-    //    do not couple (L is zero inside a token's block).
-    for (int t = 0; t < C; ++t) {
-      for (int e = tid; e < r_ab * ncol; e += kThreads) {
-        const int row = t * r_ab + e / ncol, c = e % ncol;
-        float v = c < dk ? Bt[row * dk + c] : LK[row * nk + (c - dk)];
-        for (int b = 0; b < t * r_ab; ++b) v -= L[row * na + b] * WX[b * ncol + c];
-        WX[row * ncol + c] = v;
+    // 3. masked Gram tiles: L (lower blocks, diagonal included), L_K, M_A, M_K.
+    //    Lane (lr, lg) holds rows 4lg + e, column lr of its tile.
+    for (int idx = wave; idx < ntile; idx += kWaves) {
+      int kind, rb, cb;
+      if (idx < nL) {
+        kind = 0;
+        int x = idx;
+        rb = 0;
+        while (x > rb) {
+          x -= rb + 1;
+          ++rb;
+        }
+        cb = x;
+      } else if (idx < nL + nLK) {
+        kind = 1;
+        rb = (idx - nL) / nbK;
+        cb = (idx - nL) % nbK;
+      } else if (idx < nL + nLK + nMA) {
+        kind = 2;
+        rb = (idx - nL - nLK) / nbA;
+        cb = (idx - nL - nLK) % nbA;
+      } else {
+        kind = 3;
+        rb = (idx - nL - nLK - nMA) / nbK;
+        cb = (idx - nL - nLK - nMA) % nbK;
       }
-      __syncthreads();
+      // token of a row / column: decay rows carry r_ab rows per token, write
+      // rows r_kv, query rows one.
+      const int rdiv = kind <= 1 ? r_ab : 1;
+      const int cdiv = (kind == 0 || kind == 2) ? r_ab : r_kv;
+      const bool strict = kind <= 1;
+      const int rtok_max = (rb * 16 + 15) / rdiv, ctok_min = (cb * 16) / cdiv;
+      const bool any = strict ? rtok_max > ctok_min : rtok_max >= ctok_min;
+      const float* lhs = kind <= 1 ? Bt : Qt;
+      const float* rhs = (kind == 0 || kind == 2) ? At : Kt;
+      f32x4 acc = zero4();
+      if (any) {
+        const float* lrow = lhs + static_cast<size_t>(rb * 16 + lr) * dk + 4 * lg;
+        const float* rrow = rhs + static_cast<size_t>(cb * 16 + lr) * dk + 4 * lg;
+#pragma unroll 4
+        for (int kk = 0; kk < dk; kk += 16) acc = mfma16(ld4(lrow + kk), ld4(rrow + kk), acc);
+      }
+      const int c = cb * 16 + lr, ctok = c / cdiv;
+      float* dst;
+      int ld;
+      if (kind == 0) {
+        dst = L;
+        ld = na;
+      } else if (kind == 1) {
+        dst = LK;
+        ld = nk;
+      } else if (kind == 2) {
+        dst = MA;
+        ld = na;
+      } else {
+        dst = MK;
+        ld = nk;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rb * 16 + 4 * lg + e, rtok = r / rdiv;
+        const bool keep = strict ? rtok > ctok : rtok >= ctok;
+        dst[static_cast<size_t>(r) * ld + c] = keep ? acc[e] : 0.f;
+      }
     }
+    __syncthreads();
 
-    // 5. chunk operator M_j.
-    float* Mo = a.M + static_cast<size_t>(job) * p.mrows() * ncol;
-    for (int e = tid; e < dk * ncol; e += kThreads) {
-      const int i = e / ncol, c = e % ncol;
-      float s = 0.f;
-      for (int b = 0; b < na; ++b) s += At[b * dk + i] * WX[b * ncol + c];
-      const float base = c < dk ? (i == c ? 1.f : 0.f) : Kt[(c - dk) * dk + i];
-      Mo[e] = expf(G[(C - 1) * dk + i]) * (base - s);
+    // 4. inverses of the unit lower-triangular diagonal blocks (I + L_ii), fp32:
+    //    thread (blk, c) forms column c by forward substitution.
+    for (int it = tid; it < na; it += kThreads) {
+      const int blk = it / 16, c = it % 16;
+      const float* Lb = L + static_cast<size_t>(blk * 16) * na + blk * 16;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = (r == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) v -= Lb[static_cast<size_t>(r) * na + m] * x[m];
+        x[r] = v;
+        Dinv[blk * kDIB + r * 16 + c] = v;
+      }
     }
-    for (int e = tid; e < C * ncol; e += kThreads) {
-      const int t = e / ncol, c = e % ncol;
-      float s = 0.f;
-      for (int b = 0; b < na; ++b) s += MA[t * na + b] * WX[b * ncol + c];
-      const float base = c < dk ? Qt[t * dk + c] : MK[t * nk + (c - dk)];
-      Mo[static_cast<size_t>(dk + t) * ncol + c] = base - s;
+    __syncthreads();
+
+    // 5. blocked forward substitution, one wave per 16-column tile of [Bt | LK]:
+    //    WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
+    //    Each lane re-reads only the WX pieces it stored itself.
+    for (int ct = wave; ct < KTc; ct += kWaves) {
+      float* wcol = WXT + static_cast<size_t>(ct * 16 + lr) * na + 4 * lg;
+      for (int i = 0; i < nbA; ++i) {
+        f32x4 rhs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = i * 16 + 4 * lg + e;
+          rhs[e] = ct < dkT ? Bt[static_cast<size_t>(r) * dk + ct * 16 + lr]
+                            : LK[static_cast<size_t>(r) * nk + (ct - dkT) * 16 + lr];
+        }
+        f32x4 s = zero4();
+        const float* lrow = L + static_cast<size_t>(i * 16 + lr) * na + 4 * lg;
+        for (int jb = 0; jb < i; ++jb) s = mfma16(ld4(lrow + jb * 16), ld4(wcol + jb * 16), s);
+        const f32x4 r4 = f32x4{rhs[0] - s[0], rhs[1] - s[1], rhs[2] - s[2], rhs[3] - s[3]};
+        const f32x4 w = mfma16(ld4(Dinv + i * kDIB + lr * 16 + 4 * lg), r4, zero4());
+        st4(wcol + i * 16, w);
+      }
+    }
+    // The operator product below reads the WX columns of the same wave only.
+
+    // 6. chunk operator M_j, one wave per 16-column tile, four row tiles at a time:
+    //    rows of channels  base - At^T WX, base I | Kt^T, scaled by exp(G_C);
+    //    rows of tokens    base - M_A WX,  base Qt | M_K.
+    float* Mo = a.M + static_cast<size_t>(job) * p.mrows() * ncol;
+    for (int ct = wave; ct < KTc; ct += kWaves) {
+      const float* wcol = WXT + static_cast<size_t>(ct * 16 + lr) * na + 4 * lg;
+      const int c = ct * 16 + lr;
+      for (int mg = 0; mg < MT; mg += 4) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = zero4();
+        for (int kb = 0; kb < nbA; ++kb) {
+          const f32x4 b = ld4(wcol + kb * 16);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int mt = mg + u;
+            if (mt < MT) {
+              const float* arow = mt < dkT ? AtT + static_cast<size_t>(mt * 16 + lr) * na
+                                           : MA + static_cast<size_t>((mt - dkT) * 16 + lr) * na;
+              acc[u] = mfma16(ld4(arow + kb * 16 + 4 * lg), b, acc[u]);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int mt = mg + u;
+          if (mt >= MT) break;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = mt * 16 + 4 * lg + e;
+            float v;
+            if (mt < dkT) {
+              const float base = c < dk ? (r == c ? 1.f : 0.f) : KtT[static_cast<size_t>(r) * nk + (c - dk)];
+              v = eGC[r] * (base - acc[u][e]);
+            } else {
+              const int t = r - dk;
+              const float base = c < dk ? Qt[static_cast<size_t>(t) * dk + c] : MK[static_cast<size_t>(t) * nk + (c - dk)];
+              v = base - acc[u][e];
+            }
+            Mo[static_cast<size_t>(r) * ncol + c] = v;
+          }
+        }
+      }
     }
     __syncthreads();
   }
@@ -172,61 +333,103 @@ struct ScanArgs {
   void* out;
   float* Sfin;
   const float* S0;
-  int BV;
 };
 
-// One workgroup per (batch*head, d_v slice of BV columns); chunks in order.
+constexpr int kBV = 16;   // d_v columns per scan workgroup
+
+// Scan: one workgroup per (batch*head, 16-column d_v slice); chunks in order.
+// Per chunk one product Y = M_j X with X = [S ; V_j] kept in LDS as X^T
+// (column-major in k, so each lane's 4 permuted K values are one 16-byte
+// read), double-buffered so that one barrier per chunk orders the state
+// write against the next product.  Wave w takes output row tiles w, w+4, ...
 template <typename TI>
 __global__ __launch_bounds__(kThreads) void general_scan_kernel(ScanArgs a) {
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float xs[];
   const Problem& p = a.p;
   const int dk = p.dk, dv = p.dv, C = p.C, r_kv = p.r_kv, nk = p.nk(), ncol = p.mcols();
-  const int BV = a.BV;
-  const int nvt = dv / BV;
-  const int64_t bh = blockIdx.x / nvt;
-  const int c0 = (blockIdx.x % nvt) * BV;
-  const int tid = threadIdx.x;
-  float* S = smem;                       // dk x BV
-  float* Vj = S + dk * BV;               // nk x BV
-  float* Y = Vj + nk * BV;               // (dk + C) x BV
+  const int MT = p.mrows() / 16, KTc = ncol / 16, dkT = dk / 16;
+  const int LDX = ncol + 4;
+  const int nvt = dv / kBV;
+  // Slices of one (batch, head) get block ids that land on one XCD
+  // (consecutive ids go round-robin over the 8 XCDs), so they share its L2.
+  const int b = blockIdx.x;
+  const int grp = b / (8 * nvt), rem = b % (8 * nvt);
+  const int64_t bh = static_cast<int64_t>(grp) * 8 + rem % 8;
+  const int c0 = (rem / 8) * kBV;
+  if (bh >= p.BH) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
   const TI* vp = static_cast<const TI*>(a.v);
   TI* op = static_cast<TI*>(a.out);
+  float* X0 = xs;
+  float* X1 = xs + kBV * LDX;
 
-  for (int e = tid; e < dk * BV; e += kThreads) {
-    const int i = e / BV, c = e % BV;
-    S[e] = a.S0 ? a.S0[(bh * dk + i) * dv + c0 + c] : 0.f;
-  }
-  __syncthreads();
-  for (int64_t j = 0; j < p.N; ++j) {
-    const int64_t t0 = j * C;
+  // V_jj^T into rows dk.. of an X^T buffer (zero past the chunk's end).
+  auto put_v = [&](float* X, int64_t jj) {
+    const int64_t t0 = jj * C;
     const int n = static_cast<int>(p.T - t0 < C ? p.T - t0 : C);
-    const int64_t tok0 = bh * p.T + t0;
-    for (int e = tid; e < nk * BV; e += kThreads) {
-      const int s = e / BV, c = e % BV, t = s / r_kv;
-      Vj[e] = t < n ? Elem<TI>::load(vp, (static_cast<size_t>(tok0 + t) * r_kv + (s % r_kv)) * dv + c0 + c) : 0.f;
+    for (int e = tid; e < nk * kBV; e += kThreads) {
+      const int s = e / kBV, c = e % kBV, t = s / r_kv;
+      float v = 0.f;
+      if (t < n) v = Elem<TI>::load(vp, (static_cast<size_t>(bh * p.T + t0 + t) * r_kv + (s % r_kv)) * dv + c0 + c);
+      X[c * LDX + dk + s] = v;
     }
-    __syncthreads();
-    const float* Mj = a.M + static_cast<size_t>(bh * p.N + j) * p.mrows() * ncol;
-    for (int e = tid; e < (dk + C) * BV; e += kThreads) {
-      const int r = e / BV, c = e % BV;
-      const float* mr = Mj + static_cast<size_t>(r) * ncol;
-      float s = 0.f;
-      for (int m = 0; m < dk; ++m) s += mr[m] * S[m * BV + c];
-      for (int m = 0; m < nk; ++m) s += mr[dk + m] * Vj[m * BV + c];
-      Y[e] = s;
+  };
+  for (int e = tid; e < dk * kBV; e += kThreads) {
+    const int i = e / kBV, c = e % kBV;
+    X0[c * LDX + i] = a.S0 ? a.S0[(bh * dk + i) * dv + c0 + c] : 0.f;
+  }
+  if (p.N > 0) put_v(X0, 0);
+  __syncthreads();
+
+  constexpr int kMaxQ = 6;   // row tiles per wave: (d_k + C) / 16 <= 24
+  for (int64_t jj = 0; jj < p.N; ++jj) {
+    const float* X = (jj & 1) ? X1 : X0;
+    float* Xn = (jj & 1) ? X0 : X1;
+    const float* Mj = a.M + static_cast<size_t>(bh * p.N + jj) * p.mrows() * ncol;
+    const int64_t t0 = jj * C;
+    const int n = static_cast<int>(p.T - t0 < C ? p.T - t0 : C);
+    f32x4 acc[kMaxQ];
+#pragma unroll
+    for (int u = 0; u < kMaxQ; ++u) acc[u] = zero4();
+    const float* xcol = X + lr * LDX + 4 * lg;
+#pragma unroll 2
+    for (int kb = 0; kb < KTc; ++kb) {
+      const f32x4 bx = ld4(xcol + kb * 16);
+#pragma unroll
+      for (int u = 0; u < kMaxQ; ++u) {
+        const int mt = wave + kWaves * u;
+        if (mt < MT) acc[u] = mfma16(ld4(Mj + static_cast<size_t>(mt * 16 + lr) * ncol + kb * 16 + 4 * lg), bx, acc[u]);
+      }
     }
-    __syncthreads();
-    for (int e = tid; e < n * BV; e += kThreads) {
-      const int t = e / BV, c = e % BV;
-      Elem<TI>::store(op, static_cast<size_t>(tok0 + t) * dv + c0 + c, Y[(dk + t) * BV + c]);
+    const bool last = jj == p.N - 1;
+#pragma unroll
+    for (int u = 0; u < kMaxQ; ++u) {
+      const int mt = wave + kWaves * u;
+      if (mt >= MT) break;
+      if (mt < dkT) {
+        // state rows 4lg.. of column lr: one 16-byte write of X^T
+        st4(Xn + lr * LDX + mt * 16 + 4 * lg, acc[u]);
+        if (last && a.Sfin) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a.Sfin[(bh * dk + mt * 16 + 4 * lg + e) * dv + c0 + lr] = acc[u][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = (mt - dkT) * 16 + 4 * lg + e;
+          if (t < n) Elem<TI>::store(op, static_cast<size_t>(bh * p.T + t0 + t) * dv + c0 + lr, acc[u][e]);
+        }
+      }
     }
-    for (int e = tid; e < dk * BV; e += kThreads) S[e] = Y[e];
+    if (jj + 1 < p.N) put_v(Xn, jj + 1);
     __syncthreads();
   }
-  if (a.Sfin) {
-    for (int e = tid; e < dk * BV; e += kThreads) {
-      const int i = e / BV, c = e % BV;
-      a.Sfin[(bh * dk + i) * dv + c0 + c] = S[e];
+  if (p.N == 0 && a.Sfin) {
+    for (int e = tid; e < dk * kBV; e += kThreads) {
+      const int i = e / kBV, c = e % kBV;
+      a.Sfin[(bh * dk + i) * dv + c0 + c] = X0[c * LDX + i];
     }
   }
 }
@@ -272,10 +475,8 @@ __global__ __launch_bounds__(kThreads) void general_summaries_kernel(SumArgs a) 
 
 GeneralPlan general_plan(const Problem& p) {
   GeneralPlan g{};
-  const size_t na = p.na(), nk = p.nk(), C = p.C, dk = p.dk;
-  g.slot_floats = C * dk + 2 * na * dk + nk * dk + C * dk + na * na + na * nk + C * na + C * nk +
-                  na * (dk + nk);
-  g.slot_floats = (g.slot_floats + 63) & ~static_cast<size_t>(63);
+  g.slot_floats = SlotLayout(p).total;
+  // Up to four resident prepare workgroups per compute unit, each with a slot.
   const int64_t jobs = p.BH * p.N;
   g.slots = static_cast<int>(jobs < 1024 ? (jobs > 0 ? jobs : 1) : 1024);
   g.m_bytes = static_cast<size_t>(jobs) * p.mrows() * p.mcols() * sizeof(float);
@@ -299,21 +500,20 @@ hipError_t general_prepare(const Problem& p, const void* q, const void* k, const
 
 hipError_t general_scan(const Problem& p, const void* workspace, const void* v, void* out,
                         float* Sfin, const float* S0, hipStream_t s) {
-  const int BV = (p.dv % 32 == 0) ? 32 : 16;
-  ScanArgs a{p, static_cast<const float*>(workspace), v, out, Sfin, S0, BV};
-  const size_t lds = static_cast<size_t>(p.dk + p.nk() + p.dk + p.C) * BV * sizeof(float);
-  const int64_t blocks = p.BH * (p.dv / BV);
-  if (blocks == 0) return hipSuccess;
+  ScanArgs a{p, static_cast<const float*>(workspace), v, out, Sfin, S0};
+  const size_t lds = static_cast<size_t>(2 * kBV) * (p.mcols() + 4) * sizeof(float);
+  const int64_t nvt = p.dv / kBV;
+  const int64_t blocks = (p.BH + 7) / 8 * 8 * nvt;
+  if (p.BH == 0) return hipSuccess;
   // Dynamic LDS above 64 KiB must be opted into per kernel.
-  if (p.bf16) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(general_scan_kernel<bf16_raw>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  const void* fn = p.bf16 ? reinterpret_cast<const void*>(general_scan_kernel<bf16_raw>)
+                          : reinterpret_cast<const void*>(general_scan_kernel<float>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  if (p.bf16)
     hipLaunchKernelGGL(general_scan_kernel<bf16_raw>, dim3(blocks), dim3(kThreads), lds, s, a);
-  } else {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(general_scan_kernel<float>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  else
     hipLaunchKernelGGL(general_scan_kernel<float>, dim3(blocks), dim3(kThreads), lds, s, a);
-  }
   return hipGetLastError();
 }
 
