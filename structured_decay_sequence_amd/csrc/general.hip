@@ -33,8 +33,10 @@
 namespace lattn {
 namespace {
 
-constexpr int kThreads = 256;   // four waves
+constexpr int kThreads = 256;        // scan and summaries: four waves
 constexpr int kWaves = kThreads / 64;
+constexpr int kPrepThreads = 512;    // prepare: eight waves (two per SIMD at 256 VGPRs)
+constexpr int kPrepWaves = kPrepThreads / 64;
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
@@ -52,9 +54,9 @@ __device__ __forceinline__ f32x4 mfma16(const f32x4& a, const f32x4& b, f32x4 ac
 
 // Offsets (floats) of the prepare kernel's per-slot arrays, all row-major.
 struct SlotLayout {
-  size_t G, Bt, At, AtT, Kt, KtT, Qt, L, LK, MA, MK, WXT, total;
+  size_t G, Bt, At, AtT, Kt, KtT, Qt, L, LK, MA, MK, total;
   __host__ __device__ explicit SlotLayout(const Problem& p) {
-    const size_t C = p.C, dk = p.dk, na = p.na(), nk = p.nk(), nc = p.mcols();
+    const size_t C = p.C, dk = p.dk, na = p.na(), nk = p.nk();
     size_t o = 0;
     G = o;   o += C * dk;     // chunk-local inclusive cumulative log-decay
     Bt = o;  o += na * dk;    // B (.) exp(G_{t-1})
@@ -67,7 +69,6 @@ struct SlotLayout {
     LK = o;  o += na * nk;    // Bt Kt^T, token(row) > token(col)
     MA = o;  o += C * na;     // Qt At^T, token(row) >= token(col)
     MK = o;  o += C * nk;     // Qt Kt^T, token(row) >= token(col)
-    WXT = o; o += nc * na;    // [W X] transposed: column c of the solve at row c
     total = (o + 63) & ~static_cast<size_t>(63);
   }
 };
@@ -87,15 +88,19 @@ struct PrepArgs {
   size_t slot_floats;
 };
 
-template <typename TI>
-__global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
+// NBMAX: 16-row solve blocks covered (chunk * r_ab <= 16 * NBMAX); NCT: column
+// tiles a wave solves at once (NCT * NBMAX tiles per lane stay in registers).
+template <typename TI, int NBMAX, int NCT>
+__global__ __launch_bounds__(kPrepThreads) void general_prepare_kernel(PrepArgs a) {
   __shared__ __align__(16) float Dinv[kMaxNB * kDIB];   // (I + L_ii)^{-1}, fp32
   __shared__ float eGC[256];                             // exp(G_C) per channel
   const Problem& p = a.p;
   const int dk = p.dk, C = p.C, r_ab = p.r_ab, r_kv = p.r_kv;
   const int na = p.na(), nk = p.nk(), ncol = p.mcols();
-  const int nbA = na / 16, nbK = nk / 16, nbC = C / 16, dkT = dk / 16;
+  const int nbA = na / 16, dkT = dk / 16;
   const int MT = p.mrows() / 16, KTc = ncol / 16;
+  const int RT = (na + C) / 16, CTg = (na + nk) / 16;   // tile rows / columns of the Gram matrix
+  const int SR = (RT + 3) / 4, SC = (CTg + 3) / 4;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -112,14 +117,11 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
   float* LK = slot + S.LK;
   float* MA = slot + S.MA;
   float* MK = slot + S.MK;
-  float* WXT = slot + S.WXT;
   const TI* q = static_cast<const TI*>(a.q);
   const TI* kp = static_cast<const TI*>(a.k);
   const TI* Ap = static_cast<const TI*>(a.A);
   const TI* Bp = static_cast<const TI*>(a.B);
   const int64_t total = p.BH * p.N;
-  const int nL = nbA * (nbA + 1) / 2, nLK = nbA * nbK, nMA = nbC * nbA, nMK = nbC * nbK;
-  const int ntile = nL + nLK + nMA + nMK;
 
   for (int64_t job = blockIdx.x; job < total; job += gridDim.x) {
     const int64_t bh = job / p.N;
@@ -129,8 +131,10 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
     const int64_t tok0 = bh * p.T + t0;
 
     // 1. chunk-local inclusive cumulative log-decay; padded tokens decay by 0.
-    for (int i = tid; i < dk; i += kThreads) {
+    for (int i = tid; i < dk; i += kPrepThreads) {
       float g = 0.f;
+      // unrolled so that the loads of 16 tokens are in flight together
+#pragma unroll 16
       for (int t = 0; t < C; ++t) {
         float l = 0.f;
         if (t < n) l = p.scalar ? a.ld[tok0 + t] : a.ld[(tok0 + t) * dk + i];
@@ -143,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
 
     // 2. decay-scaled operands (zero rows for padded tokens), with the
     //    transposed copies that the operator product reads as row operands.
-    for (int e = tid; e < na * dk; e += kThreads) {
+#pragma unroll 4
+    for (int e = tid; e < na * dk; e += kPrepThreads) {
       const int s = e / dk, i = e % dk, t = s / r_ab;
       float bv = 0.f, av = 0.f;
       if (t < n) {
@@ -155,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
       At[e] = av;
       AtT[static_cast<size_t>(i) * na + s] = av;
     }
-    for (int e = tid; e < nk * dk; e += kThreads) {
+#pragma unroll 4
+    for (int e = tid; e < nk * dk; e += kPrepThreads) {
       const int s = e / dk, i = e % dk, t = s / r_kv;
       float kv = 0.f;
       if (t < n)
@@ -163,7 +169,8 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
       Kt[e] = kv;
       KtT[static_cast<size_t>(i) * nk + s] = kv;
     }
-    for (int e = tid; e < C * dk; e += kThreads) {
+#pragma unroll 4
+    for (int e = tid; e < C * dk; e += kPrepThreads) {
       const int t = e / dk, i = e % dk;
       float qv = 0.f;
       if (q != nullptr && t < n) qv = Elem<TI>::load(q, static_cast<size_t>(tok0 + t) * dk + i) * expf(G[e]);
@@ -171,76 +178,78 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
     }
     __syncthreads();
 
-    // 3. masked Gram tiles: L (lower blocks, diagonal included), L_K, M_A, M_K.
-    //    Lane (lr, lg) holds rows 4lg + e, column lr of its tile.
-    for (int idx = wave; idx < ntile; idx += kWaves) {
-      int kind, rb, cb;
-      if (idx < nL) {
-        kind = 0;
-        int x = idx;
-        rb = 0;
-        while (x > rb) {
-          x -= rb + 1;
-          ++rb;
-        }
-        cb = x;
-      } else if (idx < nL + nLK) {
-        kind = 1;
-        rb = (idx - nL) / nbK;
-        cb = (idx - nL) % nbK;
-      } else if (idx < nL + nLK + nMA) {
-        kind = 2;
-        rb = (idx - nL - nLK) / nbA;
-        cb = (idx - nL - nLK) % nbA;
-      } else {
-        kind = 3;
-        rb = (idx - nL - nLK - nMA) / nbK;
-        cb = (idx - nL - nLK - nMA) % nbK;
+    // 3. masked Gram tiles of [Bt ; Qt] [At ; Kt]^T: L (lower blocks, diagonal
+    //    included), L_K, M_A, M_K.  Each wave takes 4x4 groups of 16x16 tiles,
+    //    so every operand fragment it loads feeds four products.
+    for (int st = wave; st < SR * SC; st += kPrepWaves) {
+      const int rt0 = 4 * (st / SC), ct0 = 4 * (st % SC);
+      // a group wholly above the diagonal of L is never read
+      if (rt0 + 3 < nbA && ct0 + 3 < nbA && ct0 > rt0 + 3) continue;
+      const float* lp[4];
+      const float* rp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rt = rt0 + u < RT ? rt0 + u : RT - 1, ctl = ct0 + u < CTg ? ct0 + u : CTg - 1;
+        const int row = rt * 16 + lr, col = ctl * 16 + lr;
+        lp[u] = (row < na ? Bt + static_cast<size_t>(row) * dk : Qt + static_cast<size_t>(row - na) * dk) + 4 * lg;
+        rp[u] = (col < na ? At + static_cast<size_t>(col) * dk : Kt + static_cast<size_t>(col - na) * dk) + 4 * lg;
       }
-      // token of a row / column: decay rows carry r_ab rows per token, write
-      // rows r_kv, query rows one.
-      const int rdiv = kind <= 1 ? r_ab : 1;
-      const int cdiv = (kind == 0 || kind == 2) ? r_ab : r_kv;
-      const bool strict = kind <= 1;
-      const int rtok_max = (rb * 16 + 15) / rdiv, ctok_min = (cb * 16) / cdiv;
-      const bool any = strict ? rtok_max > ctok_min : rtok_max >= ctok_min;
-      const float* lhs = kind <= 1 ? Bt : Qt;
-      const float* rhs = (kind == 0 || kind == 2) ? At : Kt;
-      f32x4 acc = zero4();
-      if (any) {
-        const float* lrow = lhs + static_cast<size_t>(rb * 16 + lr) * dk + 4 * lg;
-        const float* rrow = rhs + static_cast<size_t>(cb * 16 + lr) * dk + 4 * lg;
+      f32x4 acc[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = zero4();
 #pragma unroll 4
-        for (int kk = 0; kk < dk; kk += 16) acc = mfma16(ld4(lrow + kk), ld4(rrow + kk), acc);
-      }
-      const int c = cb * 16 + lr, ctok = c / cdiv;
-      float* dst;
-      int ld;
-      if (kind == 0) {
-        dst = L;
-        ld = na;
-      } else if (kind == 1) {
-        dst = LK;
-        ld = nk;
-      } else if (kind == 2) {
-        dst = MA;
-        ld = na;
-      } else {
-        dst = MK;
-        ld = nk;
+      for (int kk = 0; kk < dk; kk += 16) {
+        f32x4 fa[4], fb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          fa[u] = ld4(lp[u] + kk);
+          fb[u] = ld4(rp[u] + kk);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[u][v] = mfma16(fa[u], fb[v], acc[u][v]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rb * 16 + 4 * lg + e, rtok = r / rdiv;
-        const bool keep = strict ? rtok > ctok : rtok >= ctok;
-        dst[static_cast<size_t>(r) * ld + c] = keep ? acc[e] : 0.f;
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rt = rt0 + u, ctl = ct0 + v;
+          if (rt >= RT || ctl >= CTg) continue;
+          const bool drow = rt < nbA, dcol = ctl < nbA;   // decay rows / decay columns
+          if (drow && dcol && ctl > rt) continue;         // upper blocks of L: never read
+          // Token of a row or column: decay rows and columns carry r_ab per
+          // token, write columns r_kv, query rows one.  L and L_K keep
+          // token(row) > token(col); M_A and M_K keep token(row) >= token(col).
+          const int rdiv = drow ? r_ab : 1, cdiv = dcol ? r_ab : r_kv;
+          const int r0 = drow ? rt * 16 : rt * 16 - na;
+          const int c = (dcol ? ctl * 16 : ctl * 16 - na) + lr;
+          const int ctok = c / cdiv;
+          float* dst;
+          int ldd;
+          if (drow) {
+            dst = dcol ? L : LK;
+            ldd = dcol ? na : nk;
+          } else {
+            dst = dcol ? MA : MK;
+            ldd = dcol ? na : nk;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = r0 + 4 * lg + e, rtok = r / rdiv;
+            const bool keep = drow ? rtok > ctok : rtok >= ctok;
+            dst[static_cast<size_t>(r) * ldd + c] = keep ? acc[u][v][e] : 0.f;
+          }
+        }
       }
     }
     __syncthreads();
 
     // 4. inverses of the unit lower-triangular diagonal blocks (I + L_ii), fp32:
     //    thread (blk, c) forms column c by forward substitution.
-    for (int it = tid; it < na; it += kThreads) {
+    for (int it = tid; it < na; it += kPrepThreads) {
       const int blk = it / 16, c = it % 16;
       const float* Lb = L + static_cast<size_t>(blk * 16) * na + blk * 16;
       float x[16];
@@ -255,67 +264,82 @@ __global__ __launch_bounds__(kThreads) void general_prepare_kernel(PrepArgs a) {
     }
     __syncthreads();
 
-    // 5. blocked forward substitution, one wave per 16-column tile of [Bt | LK]:
-    //    WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
-    //    Each lane re-reads only the WX pieces it stored itself.
-    for (int ct = wave; ct < KTc; ct += kWaves) {
-      float* wcol = WXT + static_cast<size_t>(ct * 16 + lr) * na + 4 * lg;
-      for (int i = 0; i < nbA; ++i) {
-        f32x4 rhs;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = i * 16 + 4 * lg + e;
-          rhs[e] = ct < dkT ? Bt[static_cast<size_t>(r) * dk + ct * 16 + lr]
-                            : LK[static_cast<size_t>(r) * nk + (ct - dkT) * 16 + lr];
-        }
-        f32x4 s = zero4();
-        const float* lrow = L + static_cast<size_t>(i * 16 + lr) * na + 4 * lg;
-        for (int jb = 0; jb < i; ++jb) s = mfma16(ld4(lrow + jb * 16), ld4(wcol + jb * 16), s);
-        const f32x4 r4 = f32x4{rhs[0] - s[0], rhs[1] - s[1], rhs[2] - s[2], rhs[3] - s[3]};
-        const f32x4 w = mfma16(ld4(Dinv + i * kDIB + lr * 16 + 4 * lg), r4, zero4());
-        st4(wcol + i * 16, w);
-      }
-    }
-    // The operator product below reads the WX columns of the same wave only.
-
-    // 6. chunk operator M_j, one wave per 16-column tile, four row tiles at a time:
+    // 5. blocked forward substitution, per wave NCT 16-column tiles of
+    //    [Bt | LK] at a time:  WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j),
+    //    with the WX tiles kept in registers (accumulator layout, which is the
+    //    right-operand layout of the next product) and each L fragment feeding
+    //    all NCT tiles.
+    // 6. then, from the same registers, the chunk operator's columns:
     //    rows of channels  base - At^T WX, base I | Kt^T, scaled by exp(G_C);
     //    rows of tokens    base - M_A WX,  base Qt | M_K.
     float* Mo = a.M + static_cast<size_t>(job) * p.mrows() * ncol;
-    for (int ct = wave; ct < KTc; ct += kWaves) {
-      const float* wcol = WXT + static_cast<size_t>(ct * 16 + lr) * na + 4 * lg;
-      const int c = ct * 16 + lr;
-      for (int mg = 0; mg < MT; mg += 4) {
-        f32x4 acc[4];
+    for (int ct0 = NCT * wave; ct0 < KTc; ct0 += NCT * kPrepWaves) {
+      f32x4 wx[NCT][NBMAX];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = zero4();
-        for (int kb = 0; kb < nbA; ++kb) {
-          const f32x4 b = ld4(wcol + kb * 16);
+      for (int i = 0; i < NBMAX; ++i) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int mt = mg + u;
-            if (mt < MT) {
-              const float* arow = mt < dkT ? AtT + static_cast<size_t>(mt * 16 + lr) * na
-                                           : MA + static_cast<size_t>((mt - dkT) * 16 + lr) * na;
-              acc[u] = mfma16(ld4(arow + kb * 16 + 4 * lg), b, acc[u]);
+        for (int h = 0; h < NCT; ++h) wx[h][i] = zero4();
+      }
+#pragma unroll
+      for (int i = 0; i < NBMAX; ++i) {
+        if (i < nbA) {
+          f32x4 sm[NCT];
+#pragma unroll
+          for (int h = 0; h < NCT; ++h) sm[h] = zero4();
+          const float* lrow = L + static_cast<size_t>(i * 16 + lr) * na + 4 * lg;
+#pragma unroll
+          for (int jb = 0; jb < i; ++jb) {
+            const f32x4 la = ld4(lrow + jb * 16);
+#pragma unroll
+            for (int h = 0; h < NCT; ++h) sm[h] = mfma16(la, wx[h][jb], sm[h]);
+          }
+          const f32x4 dA = ld4(Dinv + i * kDIB + lr * 16 + 4 * lg);
+#pragma unroll
+          for (int h = 0; h < NCT; ++h) {
+            const int ct = ct0 + h < KTc ? ct0 + h : ct0;   // a missing last tile repeats the first
+            f32x4 r4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = i * 16 + 4 * lg + e;
+              const float rhs = ct < dkT ? Bt[static_cast<size_t>(r) * dk + ct * 16 + lr]
+                                         : LK[static_cast<size_t>(r) * nk + (ct - dkT) * 16 + lr];
+              r4[e] = rhs - sm[h][e];
             }
+            wx[h][i] = mfma16(dA, r4, zero4());
+          }
+        }
+      }
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc[NCT];
+#pragma unroll
+        for (int h = 0; h < NCT; ++h) acc[h] = zero4();
+        const float* arow = (mt < dkT ? AtT + static_cast<size_t>(mt * 16 + lr) * na
+                                      : MA + static_cast<size_t>((mt - dkT) * 16 + lr) * na) + 4 * lg;
+        // No guard on kb, so that all the loads can be issued ahead: slices
+        // past chunk * r_ab read a valid fragment and meet a zero WX tile.
+        if (nbA > 0) {
+#pragma unroll
+          for (int kb = 0; kb < NBMAX; ++kb) {
+            const f32x4 fa = ld4(arow + (kb < nbA ? kb : 0) * 16);
+#pragma unroll
+            for (int h = 0; h < NCT; ++h) acc[h] = mfma16(fa, wx[h][kb], acc[h]);
           }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int mt = mg + u;
-          if (mt >= MT) break;
+        for (int h = 0; h < NCT; ++h) {
+          if (ct0 + h >= KTc) break;
+          const int c = (ct0 + h) * 16 + lr;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = mt * 16 + 4 * lg + e;
             float v;
             if (mt < dkT) {
               const float base = c < dk ? (r == c ? 1.f : 0.f) : KtT[static_cast<size_t>(r) * nk + (c - dk)];
-              v = eGC[r] * (base - acc[u][e]);
+              v = eGC[r] * (base - acc[h][e]);
             } else {
               const int t = r - dk;
               const float base = c < dk ? Qt[static_cast<size_t>(t) * dk + c] : MK[static_cast<size_t>(t) * nk + (c - dk)];
-              v = base - acc[u][e];
+              v = base - acc[h][e];
             }
             Mo[static_cast<size_t>(r) * ncol + c] = v;
           }
@@ -336,20 +360,28 @@ struct ScanArgs {
 };
 
 constexpr int kBV = 16;   // d_v columns per scan workgroup
+constexpr int kVMAX = 4;  // V values per thread prefetched into registers
 
 // Scan: one workgroup per (batch*head, 16-column d_v slice); chunks in order.
 // Per chunk one product Y = M_j X with X = [S ; V_j] kept in LDS as X^T
 // (column-major in k, so each lane's 4 permuted K values are one 16-byte
 // read), double-buffered so that one barrier per chunk orders the state
-// write against the next product.  Wave w takes output row tiles w, w+4, ...
-template <typename TI>
-__global__ __launch_bounds__(kThreads) void general_scan_kernel(ScanArgs a) {
+// write against the next product.  Wave w takes output row tiles w, w + nw,
+// ... (QW of them).  The operator is read from HBM in batches of KB K slices
+// held in registers; the next batch (the next chunk's first, at the end of a
+// chunk) is issued as soon as the current one has been multiplied, since the
+// operator does not depend on the state.  V of the next chunk is loaded into
+// registers before the product and written to LDS after it.
+template <typename TI, int QW, int KB>
+__global__ __launch_bounds__(768) void general_scan_kernel(ScanArgs a) {
   extern __shared__ __align__(16) float xs[];
   const Problem& p = a.p;
   const int dk = p.dk, dv = p.dv, C = p.C, r_kv = p.r_kv, nk = p.nk(), ncol = p.mcols();
   const int MT = p.mrows() / 16, KTc = ncol / 16, dkT = dk / 16;
   const int LDX = ncol + 4;
   const int nvt = dv / kBV;
+  const int nthr = blockDim.x, nw = nthr / 64;
+  const int64_t N = p.N;
   // Slices of one (batch, head) get block ids that land on one XCD
   // (consecutive ids go round-robin over the 8 XCDs), so they share its L2.
   const int b = blockIdx.x;
@@ -365,48 +397,87 @@ __global__ __launch_bounds__(kThreads) void general_scan_kernel(ScanArgs a) {
   float* X0 = xs;
   float* X1 = xs + kBV * LDX;
 
-  // V_jj^T into rows dk.. of an X^T buffer (zero past the chunk's end).
-  auto put_v = [&](float* X, int64_t jj) {
+  // V_jj: item e is (write row s = e / kBV, column e % kBV); zero past the chunk's end.
+  auto v_at = [&](int64_t jj, int e) {
     const int64_t t0 = jj * C;
     const int n = static_cast<int>(p.T - t0 < C ? p.T - t0 : C);
-    for (int e = tid; e < nk * kBV; e += kThreads) {
-      const int s = e / kBV, c = e % kBV, t = s / r_kv;
-      float v = 0.f;
-      if (t < n) v = Elem<TI>::load(vp, (static_cast<size_t>(bh * p.T + t0 + t) * r_kv + (s % r_kv)) * dv + c0 + c);
-      X[c * LDX + dk + s] = v;
+    const int s = e / kBV, c = e % kBV, t = s / r_kv;
+    return t < n ? Elem<TI>::load(vp, (static_cast<size_t>(bh * p.T + t0 + t) * r_kv + (s % r_kv)) * dv + c0 + c) : 0.f;
+  };
+  float vr[kVMAX];
+  auto load_v = [&](int64_t jj) {
+#pragma unroll
+    for (int q = 0; q < kVMAX; ++q) {
+      const int e = tid + q * nthr;
+      vr[q] = e < nk * kBV ? v_at(jj, e) : 0.f;
     }
   };
-  for (int e = tid; e < dk * kBV; e += kThreads) {
+  auto store_v = [&](float* X, int64_t jj) {
+#pragma unroll
+    for (int q = 0; q < kVMAX; ++q) {
+      const int e = tid + q * nthr;
+      if (e < nk * kBV) X[(e % kBV) * LDX + dk + e / kBV] = vr[q];
+    }
+    // shapes with more values than the register copy holds
+    for (int e = tid + kVMAX * nthr; e < nk * kBV; e += nthr) X[(e % kBV) * LDX + dk + e / kBV] = v_at(jj, e);
+  };
+  // Operator fragments of K slices kb0 .. kb0 + KB - 1 of chunk jj (indices
+  // clamped into range: the extra fragments are loaded but not used).
+  f32x4 fa[QW][KB];
+  auto load_batch = [&](int64_t jj, int kb0) {
+    jj = jj < N ? jj : N - 1;
+    const float* Mj = a.M + static_cast<size_t>(bh * N + jj) * p.mrows() * ncol + 4 * lg;
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+      const int mt = wave + nw * u < MT ? wave + nw * u : MT - 1;
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int kb = kb0 + i < KTc ? kb0 + i : KTc - 1;
+        fa[u][i] = ld4(Mj + static_cast<size_t>(mt * 16 + lr) * ncol + kb * 16);
+      }
+    }
+  };
+  for (int e = tid; e < dk * kBV; e += nthr) {
     const int i = e / kBV, c = e % kBV;
     X0[c * LDX + i] = a.S0 ? a.S0[(bh * dk + i) * dv + c0 + c] : 0.f;
   }
-  if (p.N > 0) put_v(X0, 0);
+  if (N > 0) {
+    load_v(0);
+    store_v(X0, 0);
+    load_batch(0, 0);
+  }
   __syncthreads();
 
-  constexpr int kMaxQ = 6;   // row tiles per wave: (d_k + C) / 16 <= 24
-  for (int64_t jj = 0; jj < p.N; ++jj) {
+  for (int64_t jj = 0; jj < N; ++jj) {
     const float* X = (jj & 1) ? X1 : X0;
     float* Xn = (jj & 1) ? X0 : X1;
-    const float* Mj = a.M + static_cast<size_t>(bh * p.N + jj) * p.mrows() * ncol;
     const int64_t t0 = jj * C;
     const int n = static_cast<int>(p.T - t0 < C ? p.T - t0 : C);
-    f32x4 acc[kMaxQ];
+    if (jj + 1 < N) load_v(jj + 1);
+    f32x4 acc[QW];
 #pragma unroll
-    for (int u = 0; u < kMaxQ; ++u) acc[u] = zero4();
+    for (int u = 0; u < QW; ++u) acc[u] = zero4();
     const float* xcol = X + lr * LDX + 4 * lg;
-#pragma unroll 2
-    for (int kb = 0; kb < KTc; ++kb) {
-      const f32x4 bx = ld4(xcol + kb * 16);
+    for (int kb0 = 0; kb0 < KTc; kb0 += KB) {
 #pragma unroll
-      for (int u = 0; u < kMaxQ; ++u) {
-        const int mt = wave + kWaves * u;
-        if (mt < MT) acc[u] = mfma16(ld4(Mj + static_cast<size_t>(mt * 16 + lr) * ncol + kb * 16 + 4 * lg), bx, acc[u]);
+      for (int i = 0; i < KB; ++i) {
+        if (kb0 + i < KTc) {
+          const f32x4 bx = ld4(xcol + (kb0 + i) * 16);
+#pragma unroll
+          for (int u = 0; u < QW; ++u)
+            if (wave + nw * u < MT) acc[u] = mfma16(fa[u][i], bx, acc[u]);
+        }
+      }
+      if (kb0 + KB < KTc) {
+        load_batch(jj, kb0 + KB);
+      } else {
+        load_batch(jj + 1, 0);
       }
     }
-    const bool last = jj == p.N - 1;
+    const bool last = jj == N - 1;
 #pragma unroll
-    for (int u = 0; u < kMaxQ; ++u) {
-      const int mt = wave + kWaves * u;
+    for (int u = 0; u < QW; ++u) {
+      const int mt = wave + nw * u;
       if (mt >= MT) break;
       if (mt < dkT) {
         // state rows 4lg.. of column lr: one 16-byte write of X^T
@@ -423,11 +494,11 @@ __global__ __launch_bounds__(kThreads) void general_scan_kernel(ScanArgs a) {
         }
       }
     }
-    if (jj + 1 < p.N) put_v(Xn, jj + 1);
+    if (jj + 1 < N) store_v(Xn, jj + 1);
     __syncthreads();
   }
-  if (p.N == 0 && a.Sfin) {
-    for (int e = tid; e < dk * kBV; e += kThreads) {
+  if (N == 0 && a.Sfin) {
+    for (int e = tid; e < dk * kBV; e += nthr) {
       const int i = e / kBV, c = e % kBV;
       a.Sfin[(bh * dk + i) * dv + c0 + c] = X0[c * LDX + i];
     }
@@ -476,13 +547,32 @@ __global__ __launch_bounds__(kThreads) void general_summaries_kernel(SumArgs a) 
 GeneralPlan general_plan(const Problem& p) {
   GeneralPlan g{};
   g.slot_floats = SlotLayout(p).total;
-  // Up to four resident prepare workgroups per compute unit, each with a slot.
+  // One resident prepare workgroup per compute unit, each with its own slot.
   const int64_t jobs = p.BH * p.N;
-  g.slots = static_cast<int>(jobs < 1024 ? (jobs > 0 ? jobs : 1) : 1024);
+  g.slots = static_cast<int>(jobs < 256 ? (jobs > 0 ? jobs : 1) : 256);
   g.m_bytes = static_cast<size_t>(jobs) * p.mrows() * p.mcols() * sizeof(float);
   g.m_bytes = (g.m_bytes + 255) & ~static_cast<size_t>(255);
   g.total_bytes = g.m_bytes + static_cast<size_t>(g.slots) * g.slot_floats * sizeof(float);
   return g;
+}
+
+template <typename TI, int NBMAX, int NCT>
+void launch_prepare(const GeneralPlan& g, const PrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((general_prepare_kernel<TI, NBMAX, NCT>), dim3(g.slots), dim3(kPrepThreads), 0, s, a);
+}
+
+template <typename TI>
+void launch_prepare(const GeneralPlan& g, const PrepArgs& a, hipStream_t s) {
+  // The solve keeps NCT x NBMAX tiles per lane in registers: the smallest
+  // instantiation that covers chunk * r_ab.
+  const int nb = a.p.na() / 16;
+  if (nb <= 8) {
+    launch_prepare<TI, 8, 2>(g, a, s);
+  } else if (nb <= 16) {
+    launch_prepare<TI, 16, 1>(g, a, s);
+  } else {
+    launch_prepare<TI, kMaxNB, 1>(g, a, s);
+  }
 }
 
 hipError_t general_prepare(const Problem& p, const void* q, const void* k, const float* ld,
@@ -491,11 +581,32 @@ hipError_t general_prepare(const Problem& p, const void* q, const void* k, const
   PrepArgs a{p, q, k, ld, A, B, static_cast<float*>(workspace),
              reinterpret_cast<float*>(static_cast<char*>(workspace) + g.m_bytes), g.slot_floats};
   if (p.BH * p.N == 0) return hipSuccess;
+  if (p.na() > 16 * kMaxNB) return hipErrorInvalidValue;
   if (p.bf16)
-    hipLaunchKernelGGL(general_prepare_kernel<bf16_raw>, dim3(g.slots), dim3(kThreads), 0, s, a);
+    launch_prepare<bf16_raw>(g, a, s);
   else
-    hipLaunchKernelGGL(general_prepare_kernel<float>, dim3(g.slots), dim3(kThreads), 0, s, a);
+    launch_prepare<float>(g, a, s);
   return hipGetLastError();
+}
+
+template <typename TI, int QW, int KB>
+hipError_t launch_scan(const Problem& p, const ScanArgs& a, size_t lds, int64_t blocks, hipStream_t s) {
+  // Dynamic LDS above 64 KiB must be opted into per kernel.
+  const void* fn = reinterpret_cast<const void*>(general_scan_kernel<TI, QW, KB>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  // One wave per QW output row tiles: (d_k + C) / 16 <= 24 tiles, at most 12 waves.
+  const int mt = p.mrows() / 16;
+  const int nw = (mt + QW - 1) / QW;
+  hipLaunchKernelGGL((general_scan_kernel<TI, QW, KB>), dim3(blocks), dim3(64 * nw), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename TI>
+hipError_t launch_scan(const Problem& p, const ScanArgs& a, size_t lds, int64_t blocks, hipStream_t s) {
+  // Up to 12 row tiles: one per wave, a whole chunk's operator per load batch
+  // (K slices <= 32: two batches); more: two per wave, half-size batches.
+  return p.mrows() / 16 <= 12 ? launch_scan<TI, 1, 16>(p, a, lds, blocks, s) : launch_scan<TI, 2, 8>(p, a, lds, blocks, s);
 }
 
 hipError_t general_scan(const Problem& p, const void* workspace, const void* v, void* out,
@@ -505,16 +616,7 @@ hipError_t general_scan(const Problem& p, const void* workspace, const void* v, 
   const int64_t nvt = p.dv / kBV;
   const int64_t blocks = (p.BH + 7) / 8 * 8 * nvt;
   if (p.BH == 0) return hipSuccess;
-  // Dynamic LDS above 64 KiB must be opted into per kernel.
-  const void* fn = p.bf16 ? reinterpret_cast<const void*>(general_scan_kernel<bf16_raw>)
-                          : reinterpret_cast<const void*>(general_scan_kernel<float>);
-  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  if (p.bf16)
-    hipLaunchKernelGGL(general_scan_kernel<bf16_raw>, dim3(blocks), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(general_scan_kernel<float>, dim3(blocks), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return p.bf16 ? launch_scan<bf16_raw>(p, a, lds, blocks, s) : launch_scan<float>(p, a, lds, blocks, s);
 }
 
 hipError_t general_summaries(const Problem& p, const void* workspace, const void* v, float* sumA,
