@@ -174,3 +174,15 @@ def raw_for(spec: Spec, B=None, H=None, T=None) -> Dict[str, np.ndarray]:
         return gdn_raw(B, H, T, spec.dk, spec.dv, spec.dtype, spec.seed)
     return generic_raw(B, H, T, spec.dk, spec.dv, spec.r_ab, spec.r_kv, spec.dtype, "channel",
                        spec.lam_mu, 0.5, spec.seed)
+
+
+def hla_gates(B, H, T, chunk, mu=-4.0, sd=1.5, seed=0) -> np.ndarray:
+    """Per (query token, chunk) routing gates w = sigmoid(s), s ~ N(mu, sd), float32
+    [B, H, T, ceil(T / chunk)].  The HLA note ("Method steps", step 4) forms each gate
+    as a sigmoid of a query-to-chunk score and keeps about three history chunks per
+    query active (its routing budget, step 6); with mu = -4, sd = 1.5 about one gate
+    in nine is at or above the inference threshold 0.1 (step 7)."""
+    rng = np.random.default_rng(seed)
+    N = -(-T // chunk)
+    s = rng.standard_normal((B, H, T, N), dtype=np.float32) * np.float32(sd) + np.float32(mu)
+    return _sigmoid(s)
