@@ -151,6 +151,35 @@ int lattn_chunk_summaries(const lattn_dims* dims, const void* k, const void* v,
 size_t lattn_chunk_summaries_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
 
 /*
+ * lattn_hla_fwd -- query-conditioned composition of the exact chunk transitions
+ * (HLA note, "Core method" and "Method steps", steps 2, 5 and 7).  For query
+ * token i in chunk c = i / chunk, from a zero state, every earlier chunk j in
+ * time order is applied with the query's gate w = gates[i, j]:
+ *   S <- ((1 - w) I + w A_j) S + w B_j      (A_j, B_j: the chunk's exact pair),
+ * a gate below theta counting as 0 (no renormalisation); then the tokens of
+ * chunk c up to and including i advance S by the recurrence of
+ * lattn_chunk_fwd, and out[i] = S^T q_i (no 1/sqrt(d_k) scale).  All gates 1
+ * give lattn_chunk_fwd's output; all gates 0 give each chunk's output from a
+ * zero state.
+ * Inputs as lattn_chunk_fwd, plus
+ *   gates [B,H,T,N] fp32, N = ceil(T / chunk); entries j >= i / chunk unused.
+ * out [B,H,T,d_v] in dims->dtype.  No state in or out (the history of every
+ * query starts from zero).  d_k and d_v must be <= 128 (LATTN_EUNSUPPORTED).
+ * Arithmetic is fp32 for both storage dtypes.
+ * Needs lattn_hla_fwd_workspace_size() bytes of caller-owned workspace (the
+ * chunk operators and, per chunk, A_j^T, B_j^T and its zero-state outputs).
+ * Validation, ownership and stream ordering as lattn_chunk_fwd; NaN gates
+ * propagate.
+ */
+int lattn_hla_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                  const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                  int chunk, const float* gates, float theta, void* out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lattn_hla_fwd needs (0 on invalid arguments). */
+size_t lattn_hla_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
+
+/*
  * lattn_step -- one recurrent token for decoding (HLA note, "Reproduction":
  * a prefill algorithm and a dynamic decoding algorithm; the recurrence of
  * HDLA note, "Key design 3", applied once):

@@ -16,18 +16,13 @@
 // walks the chunks of one (batch, head, d_v slice) in order.
 //
 // Every product is a wave-level 16x16 tile on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32), so the path keeps fp32 operands and fp32
-// accumulation.  A 16-deep slice of K is taken as four such MFMAs over a
-// permuted K: lane (i, g) reads the 16-byte piece k0 + 4g .. k0 + 4g + 3 of
-// its row of each operand, and product e pairs the e-th value of both.  The
-// same permutation makes a tile in accumulator layout (lane (i, g) holding
-// rows 4g .. 4g + 3 of column i) usable as the right operand of the next
-// product with no data exchange between lanes.
+// (tile_f32.hpp), so the path keeps fp32 operands and fp32 accumulation.
 //
 // The prepare kernel's operands live in a per-workgroup slot of the
 // workspace (row-major fp32); M_j is stored row-major fp32.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile_f32.hpp"
 
 
 namespace lattn {
@@ -37,20 +32,6 @@ constexpr int kThreads = 256;        // scan and summaries: four waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kPrepThreads = 512;    // prepare: eight waves (two per SIMD at 256 VGPRs)
 constexpr int kPrepWaves = kPrepThreads / 64;
-
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ void st4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
-
-// acc += A B over one 16-deep K slice, in the permuted-K form described above:
-// a = this lane's 4 values of its A row, b = its 4 values of its B column.
-__device__ __forceinline__ f32x4 mfma16(const f32x4& a, const f32x4& b, f32x4 acc) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
-  return acc;
-}
 
 // Offsets (floats) of the prepare kernel's per-slot arrays, all row-major.
 struct SlotLayout {

@@ -57,6 +57,18 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
 hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const void* k, const float* ld,
                               const float* beta, void* workspace, hipStream_t s);
 
+// Query-conditioned composition (HLA) on the general path's chunk operators:
+// d_k, d_v <= 128.  Workspace: the general path's, then Acal^T, B^T and the
+// chunk-local outputs of every chunk (fp32).
+struct HlaPlan {
+  size_t gen_bytes, at_bytes, bt_bytes, oi_bytes, total_bytes;
+};
+bool hla_supported(const Problem& p);
+HlaPlan hla_plan(const Problem& p);
+hipError_t launch_hla(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
+                      const void* B, const void* v, const float* gates, float theta, void* out,
+                      void* workspace, hipStream_t s);
+
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, float* state, void* out,
                        hipStream_t s);

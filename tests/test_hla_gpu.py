@@ -1,0 +1,79 @@
+"""GPU parity of the query-conditioned chunk composition (lattn_hla_fwd) against
+the fp64 HLA oracle, through the C ABI.
+
+Gate as for the base path: max|gpu - ref| / max|ref| <= 1e-4 for fp32 storage
+and <= 2e-2 for bf16 storage (the arithmetic is fp32 in both).  Inputs are the
+seeded generic recurrence inputs and seeded sigmoid gates; the oracle runs on
+the same stored values.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import hla as hla_oracle
+import workloads
+from tests.helpers import TOL, dev, host, rel_err, torch_dtype
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+lattn = pytest.importorskip("structured_decay_sequence_amd")
+
+
+def _gpu(raw, gates, dtype, chunk, theta):
+    td = torch_dtype(dtype)
+    out = lattn.hla_fwd(dev(raw["q"], td), dev(raw["K"], td), dev(raw["V"], td), dev(raw["log_decay"]),
+                        dev(raw["A"], td), dev(raw["B"], td), dev(gates), chunk=chunk, theta=theta)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+CASES = [
+    # B, H, T, dk, dv, r_ab, r_kv, C, dtype, decay, gate mean
+    (1, 2, 200, 64, 64, 2, 1, 64, "fp32", "channel", -2.0),
+    (1, 2, 300, 32, 32, 1, 1, 32, "fp32", "scalar", -4.0),
+    (2, 1, 77, 48, 32, 2, 2, 16, "fp32", "channel", -1.0),
+    (1, 1, 300, 32, 64, 0, 1, 128, "fp32", "channel", -2.0),
+    (1, 1, 40, 16, 16, 1, 1, 64, "fp32", "channel", 0.0),
+    (1, 2, 130, 64, 64, 2, 1, 64, "bf16", "channel", -2.0),
+    (1, 1, 161, 32, 128, 1, 1, 32, "bf16", "scalar", -3.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}-{}C{}{}{}mu{}".format(*c))
+def test_hla_parity(case):
+    Bb, H, T, dk, dv, r_ab, r_kv, C, dtype, decay, mu = case
+    print(f"hla case {case}", flush=True)
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, r_ab, r_kv, dtype, decay, seed=T + dk)
+    gates = workloads.hla_gates(Bb, H, T, C, mu=mu, seed=T)
+    out = _gpu(raw, gates, dtype, C, 0.1)
+    ref = hla_oracle.hla(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], gates, C, 0.1)
+    e = rel_err(out, ref)
+    print(f"out {e:.2e}", flush=True)
+    assert e <= TOL[dtype]
+
+
+def test_hla_all_gates_one_is_base_forward():
+    Bb, H, T, dk, dv, C = 1, 2, 200, 64, 64, 32
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 2, 1, "fp32", "channel", seed=1)
+    gates = np.ones((Bb, H, T, -(-T // C)), dtype=np.float32)
+    out = _gpu(raw, gates, "fp32", C, 0.1)
+    ref, _ = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"])
+    assert rel_err(out, ref) <= TOL["fp32"]
+
+
+def test_hla_gates_below_threshold_are_chunk_local():
+    Bb, H, T, dk, dv, C = 1, 1, 150, 32, 32, 64
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 1, 1, "fp32", "channel", seed=2)
+    gates = np.full((Bb, H, T, -(-T // C)), 0.09, dtype=np.float32)
+    out = _gpu(raw, gates, "fp32", C, 0.1)
+    zero = hla_oracle.hla(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"],
+                          np.zeros_like(gates), C, 0.0)
+    assert rel_err(out, zero) <= TOL["fp32"]
+
+
+def test_hla_rejects_wide_heads():
+    raw = workloads.generic_raw(1, 1, 32, 256, 64, 1, 1, "fp32", "channel", seed=0)
+    gates = workloads.hla_gates(1, 1, 32, 16, seed=0)
+    with pytest.raises(lattn.LattnError):
+        _gpu(raw, gates, "fp32", 16, 0.1)
