@@ -193,6 +193,62 @@ def fused_leg(spec, raw, torch, lattn, dev, steps, warmup):
     }
 
 
+# Query-conditioned composition (HLA note, "Method steps"): Gated DeltaNet, the
+# family the note builds on, at B=1, H=16, T=4096, d_k = d_v = 128, bf16 storage;
+# chunks of 128 tokens (the note uses 256; 128 is the largest chunk this path
+# takes); gates sigmoid(N(-4, 1.5)) with the note's threshold 0.1.
+HLA_WORKLOAD = dict(B=1, H=16, T=4096, dk=128, dv=128, chunk=128, mu=-4.0, theta=0.1)
+
+
+def hla_leg(torch, lattn, dev, steps, warmup):
+    """lattn_hla_fwd on the HLA workload, timed with HIP events on its stream.
+    The decay operands come from the device parameter kernel before timing (as
+    for the generic forward).  flops: the pair products (one C x d_k x (d_k + d_v)
+    product per (query chunk, earlier chunk) pair with a gate at or above the
+    threshold) plus the chunk operators and chunk writes."""
+    w = HLA_WORKLOAD
+    Bb, H, T, dk, dv, C = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["chunk"]
+    raw = workloads.gdn_raw(Bb, H, T, dk, dv, "bf16", seed=0)
+    gates = workloads.hla_gates(Bb, H, T, C, mu=w["mu"], seed=0)
+    t = lambda x, d: torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
+    q, k, v = (t(raw[n], torch.bfloat16) for n in ("q", "k", "v"))
+    A, B, V = lattn.gdn_params(k, v, t(raw["g"], torch.float32), t(raw["beta"], torch.float32))
+    ld = t(raw["g"], torch.float32)
+    gt = t(gates, torch.float32)
+    out = torch.empty((Bb, H, T, dv), dtype=torch.bfloat16, device=dev)
+    run = lambda: lattn.hla_fwd(q, k, V, ld, A, B, gt, chunk=C, theta=w["theta"], out=out)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    N = -(-T // C)
+    act = gates.reshape(Bb * H, N, C, N) >= w["theta"]          # [head, query chunk, query, chunk]
+    pairs = sum(int(act[:, c, :, :c].any(axis=1).sum()) for c in range(N))
+    na, nk = C, C
+    pair_mac = C * dk * (dk + dv)
+    prep_mac = (na + C) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (C + dk) * na * (dk + nk)
+    sum_mac = (dk + C) * nk * dv
+    flops = 2.0 * (pairs * pair_mac + Bb * H * N * (prep_mac + sum_mac))
+    return {
+        "entry": "lattn_hla_fwd",
+        "workload": f"gdn B{Bb} H{H} T{T} d{dk} C{C} bf16, gates sigmoid(N({w['mu']}, 1.5)), theta {w['theta']}",
+        "ms_per_step": round(ms, 4),
+        "value": round(Bb * T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "active_pairs": pairs,
+        "all_pairs": Bb * H * N * (N - 1) // 2,
+        "gflop": round(flops / 1e9, 2),
+        "fp32_mfma_frac": round(flops / (ms / 1e3) / (PEAK["fp32_mfma_TFs"] * 1e12), 4),
+    }
+
+
 def cpu_baseline(spec, raw, budget_s):
     """Time the fp64 oracle (generic form, as used for parity) on a bounded sample of
     (batch, head) rows of the same workload, on all host cores."""
@@ -232,6 +288,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=workloads.HEADLINE, choices=workloads.CONFIG_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hla", action="store_true", help="skip the query-conditioned composition leg")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0, help="target oracle wall time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -344,6 +401,9 @@ def main():
     }
     if spec.family in ("hdla", "gdn") and kernels == "mfma_bf16":
         result["fused_family"] = fused_leg(spec, raw, torch, lattn, dev, args.steps, args.warmup)
+    if spec.name == workloads.HEADLINE and not args.no_hla:
+        print("[bench] query-conditioned composition leg", file=sys.stderr, flush=True)
+        result["hla"] = hla_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, raw, args.cpu_budget_s)

@@ -46,14 +46,15 @@ def _token_maps(K, V, log_decay, A, B):
     return P, W
 
 
-def hla(q, K, V, log_decay, A, B, gates, chunk: int, theta: float = 0.0):
+def hla(q, K, V, log_decay, A, B, gates, chunk: int, theta: float = 0.0, queries=None):
     """Query-conditioned composition of exact chunk transitions.
 
     Shapes (``lead`` = batch/head dims): q [*lead, T, dk]; K [*lead, T, r_kv, dk];
     V [*lead, T, r_kv, dv]; log_decay [*lead, T, dk] or [*lead, T]; A, B
     [*lead, T, r_ab, dk] or None; gates [*lead, T, N] with N = ceil(T / chunk)
     (entry [i, j] is query i's gate for chunk j; entries j >= i // chunk are
-    not used).  Returns out [*lead, T, dv] in fp64.
+    not used).  ``queries``: token indices to evaluate (default all; the other
+    rows of the result stay zero).  Returns out [*lead, T, dv] in fp64.
     """
     q, K, V, ld, A, B, gates = (_f64(x) for x in (q, K, V, log_decay, A, B, gates))
     lead = q.shape[:-2]
@@ -80,7 +81,7 @@ def hla(q, K, V, log_decay, A, B, gates, chunk: int, theta: float = 0.0):
                 Aj = P[t] @ Aj
                 Bj = P[t] @ Bj + W[t]
             sumA[j], sumB[j] = Aj, Bj
-        for i in range(T):
+        for i in (range(T) if queries is None else queries):
             c = i // chunk
             S = np.zeros((dk, dv))
             # step 5: gated history chunks in time order (step 7: gates below theta are zero)

@@ -77,3 +77,31 @@ def test_hla_rejects_wide_heads():
     gates = workloads.hla_gates(1, 1, 32, 16, seed=0)
     with pytest.raises(lattn.LattnError):
         _gpu(raw, gates, "fp32", 16, 0.1)
+
+
+@pytest.mark.slow
+def test_hla_bench_workload_sampled():
+    """The bench's HLA workload (Gated DeltaNet, B1 H16 T4096 d128, C 128, bf16) in
+    the launch configuration bench.py times; one head's queries sampled across the
+    sequence (first chunk, chunk boundaries, the ragged-free last chunk) against
+    the oracle on the same stored decay operands."""
+    import bench
+    w = bench.HLA_WORKLOAD
+    Bb, H, T, dk, dv, C = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["chunk"]
+    raw = workloads.gdn_raw(Bb, H, T, dk, dv, "bf16", seed=0)
+    gates = workloads.hla_gates(Bb, H, T, C, mu=w["mu"], seed=0)
+    td = torch.bfloat16
+    k, v = dev(raw["k"], td), dev(raw["v"], td)
+    A, B, V = lattn.gdn_params(k, v, dev(raw["g"]), dev(raw["beta"]))
+    out = lattn.hla_fwd(dev(raw["q"], td), k, V, dev(raw["g"]), A, B, dev(gates), chunk=C, theta=w["theta"])
+    torch.cuda.synchronize()
+    out = host(out)
+    h = 5
+    qs = [0, 1, 127, 128, 129, 1000, 2047, 2048, 3071, 4000, 4095]
+    sl = lambda x: x[:, h:h + 1]
+    ref = hla_oracle.hla(sl(raw["q"]), host(sl(k))[..., None, :], host(sl(V)), sl(raw["g"]), host(sl(A)),
+                         host(sl(B)), sl(gates), C, w["theta"], queries=qs)
+    got = out[:, h:h + 1][:, :, qs]
+    e = rel_err(got, ref[:, :, qs])
+    print(f"sampled queries {qs}: out {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
