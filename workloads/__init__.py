@@ -186,3 +186,14 @@ def hla_gates(B, H, T, chunk, mu=-4.0, sd=1.5, seed=0) -> np.ndarray:
     N = -(-T // chunk)
     s = rng.standard_normal((B, H, T, N), dtype=np.float32) * np.float32(sd) + np.float32(mu)
     return _sigmoid(s)
+
+
+def loglinear_lambdas(B, H, T, seed=0) -> np.ndarray:
+    """Per (token, level) non-negative weights lam = softplus(N(0, 1)), float32
+    [B, H, T, 1 + bit_length(T - 1)] (levels 0 .. that of position T - 1).  The
+    Log-Linear note ("Key design" 2) makes each level's weight a non-negative
+    function of the token's input; here they are drawn independently."""
+    rng = np.random.default_rng(seed)
+    L = 1 + int(T - 1).bit_length() if T > 0 else 0
+    x = rng.standard_normal((B, H, T, L), dtype=np.float32)
+    return (-_log_sigmoid(-x).astype(np.float64)).astype(np.float32)   # softplus(x) = -log sigmoid(-x)
