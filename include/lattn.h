@@ -180,6 +180,36 @@ int lattn_hla_fwd(const lattn_dims* dims, const void* q, const void* k, const vo
 size_t lattn_hla_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
 
 /*
+ * lattn_loglinear_fwd -- log-linear lift of the recurrence (Log-Linear note,
+ * "Key design" 1-3).  The prefix of position t (counted from 0) is split
+ * Fenwick-style: the token itself at level 0, then from the right one bucket
+ * per set bit 2^(l-1) of t at level l, so key s < t sits at level
+ * l(t, s) = (highest bit where t and s differ) + 1.  Every key is weighted by
+ * the query's weight for its level, with the recurrence's transport
+ * Phi(t, s) = P_t ... P_{s+1}, P = D - A B^T, between them:
+ *   out[t] = sum_{s <= t} lambda[t, l(t, s)] (Phi(t, s) K_s V_s^T)^T q_t.
+ * lambda all 1 gives lattn_chunk_fwd's output.
+ * Inputs as lattn_chunk_fwd (zero initial state), plus
+ *   lambda [B,H,T,L] fp32, L = lattn_loglinear_levels(T).
+ * out [B,H,T,d_v] in dims->dtype; no final state (each level keeps its own).
+ * Needs d_k, d_v <= 128 and d_k + chunk <= 192 (LATTN_EUNSUPPORTED); the
+ * per-level states of one (batch, head) slice live in LDS, which bounds the
+ * number of chunks at 2^17 for d_k = 128.  Arithmetic is fp32.
+ * Needs lattn_loglinear_fwd_workspace_size() bytes of caller-owned workspace.
+ * Validation, ownership and stream ordering as lattn_chunk_fwd.
+ */
+int lattn_loglinear_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                        const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                        int chunk, const float* lambda, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lattn_loglinear_fwd needs (0 on invalid arguments). */
+size_t lattn_loglinear_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
+
+/* Levels L of a sequence of seqlen tokens: 1 + bit length of (seqlen - 1); 0 for seqlen 0. */
+int lattn_loglinear_levels(int64_t seqlen);
+
+/*
  * lattn_step -- one recurrent token for decoding (HLA note, "Reproduction":
  * a prefill algorithm and a dynamic decoding algorithm; the recurrence of
  * HDLA note, "Key design 3", applied once):

@@ -20,7 +20,7 @@ from ._lib import LattnError, LATTN_BF16, LATTN_FP32, LATTN_DECAY_PER_CHANNEL, L
 __all__ = [
     "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
     "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
-    "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd",
+    "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd", "loglinear_fwd", "loglinear_levels",
 ]
 
 
@@ -247,6 +247,49 @@ def hla_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.
                            r_ab, r_kv, chunk, _ptr(gates), float(theta), _ptr(out), _ptr(workspace),
                            0 if workspace is None else workspace.numel(), _stream(q.device))
     _lib.check(rc, "lattn_hla_fwd")
+    return out
+
+
+def loglinear_levels(seqlen: int) -> int:
+    """Levels L of the log-linear lift for a sequence of ``seqlen`` tokens."""
+    return int(_lib.load().lattn_loglinear_levels(int(seqlen)))
+
+
+def loglinear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+                  A: Optional[torch.Tensor], B: Optional[torch.Tensor], lam: torch.Tensor, chunk: int = 64,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Log-linear lift of the recurrence (lattn_loglinear_fwd).  Inputs as chunk_fwd,
+    plus lam fp32 [B,H,T,loglinear_levels(T)] (per-token weight of each Fenwick
+    level).  Returns out [B,H,T,dv]."""
+    Bb, H, T, dk = q.shape
+    dt = q.dtype
+    lead = (Bb, H)
+    k = _ranked(k, lead, T, dk)
+    v = _ranked(v, lead, T, None)
+    r_kv, dv = k.shape[-2], v.shape[-1]
+    _need(q, dt, (Bb, H, T, dk), "q")
+    _need(k, dt, (Bb, H, T, r_kv, dk), "k")
+    _need(v, dt, (Bb, H, T, r_kv, dv), "v")
+    scalar = log_decay.dim() == 3
+    _need(log_decay, torch.float32, (Bb, H, T) if scalar else (Bb, H, T, dk), "log_decay")
+    r_ab = 0
+    if A is not None:
+        r_ab = A.shape[-2]
+        _need(A, dt, (Bb, H, T, r_ab, dk), "A")
+        _need(B, dt, (Bb, H, T, r_ab, dk), "B")
+    _need(lam, torch.float32, (Bb, H, T, loglinear_levels(T)), "lam")
+    if out is None:
+        out = torch.empty((Bb, H, T, dv), dtype=dt, device=q.device)
+    _need(out, dt, (Bb, H, T, dv), "out")
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+    if workspace is None:
+        workspace = _workspace(q.device, int(lib.lattn_loglinear_fwd_workspace_size(ctypes.byref(dims), r_ab, r_kv,
+                                                                                        chunk)))
+    rc = lib.lattn_loglinear_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A), _ptr(B),
+                                 r_ab, r_kv, chunk, _ptr(lam), _ptr(out), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream(q.device))
+    _lib.check(rc, "lattn_loglinear_fwd")
     return out
 
 

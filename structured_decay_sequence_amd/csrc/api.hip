@@ -304,6 +304,39 @@ int lattn_hla_fwd(const lattn_dims* dims, const void* q, const void* k, const vo
   return ok();
 }
 
+size_t lattn_loglinear_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return 0;
+  return lattn::loglinear_plan(make_problem(dims, r_ab, r_kv, chunk)).total_bytes;
+}
+
+int lattn_loglinear_levels(int64_t seqlen) { return lattn::loglinear_levels(seqlen); }
+
+int lattn_loglinear_fwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                        const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                        int chunk, const float* lambda, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", need));
+  LATTN_TRY(check_ptr(lambda, "lambda", need));
+  LATTN_TRY(check_ptr(out, "out", need));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  if (!lattn::loglinear_supported(p))
+    return fail(LATTN_EUNSUPPORTED, "lattn_loglinear_fwd needs d_k, d_v <= 128, d_k + chunk <= 192 and at most "
+                "2^17 chunks at d_k = 128 (got d_k %d, d_v %d, chunk %d, %lld chunks)", p.dk, p.dv, p.C,
+                (long long)p.N);
+  if (!need) return ok();
+  const size_t ws = lattn::loglinear_plan(p).total_bytes;
+  if (workspace == nullptr || workspace_bytes < ws)
+    return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
+  LATTN_TRY(check_ptr(workspace, "workspace", true));
+  LATTN_TRY(hip_status(lattn::launch_loglinear(p, q, k, log_decay, A, B, v, lambda, out, workspace, stream),
+                       "log-linear launch"));
+  return ok();
+}
+
 int lattn_chunk_fwd_check(const lattn_dims* dims, const void* q, const void* k, const void* v,
                           const float* log_decay, const void* A, const void* B, int r_ab,
                           int r_kv, int chunk, const void* out, const void* workspace,

@@ -69,6 +69,19 @@ hipError_t launch_hla(const Problem& p, const void* q, const void* k, const floa
                       const void* B, const void* v, const float* gates, float theta, void* out,
                       void* workspace, hipStream_t s);
 
+// Log-linear lift on the general path's chunk operators: d_k, d_v <= 128,
+// d_k + C <= 192, every inter-chunk level's state resident in LDS.  Workspace:
+// the general path's, then (Z V)^T and the weighted chunk-local outputs.
+struct LlPlan {
+  size_t gen_bytes, zv_bytes, oi_bytes, total_bytes;
+};
+int loglinear_levels(int64_t T);
+bool loglinear_supported(const Problem& p);
+LlPlan loglinear_plan(const Problem& p);
+hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
+                            const void* B, const void* v, const float* lam, void* out, void* workspace,
+                            hipStream_t s);
+
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, float* state, void* out,
                        hipStream_t s);

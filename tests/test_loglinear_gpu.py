@@ -1,0 +1,83 @@
+"""GPU parity of the log-linear lift (lattn_loglinear_fwd) against the fp64
+oracle, through the C ABI.
+
+Gate as for the base path: max|gpu - ref| / max|ref| <= 1e-4 for fp32 storage
+and <= 2e-2 for bf16 storage (fp32 arithmetic in both).  Inputs: the seeded
+generic recurrence inputs and seeded per-level weights softplus(N(0, 1)).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import loglinear as ll_oracle
+import workloads
+from tests.helpers import TOL, dev, host, rel_err, torch_dtype
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+lattn = pytest.importorskip("structured_decay_sequence_amd")
+
+
+def _gpu(raw, lam, dtype, chunk):
+    td = torch_dtype(dtype)
+    out = lattn.loglinear_fwd(dev(raw["q"], td), dev(raw["K"], td), dev(raw["V"], td), dev(raw["log_decay"]),
+                              dev(raw["A"], td), dev(raw["B"], td), dev(lam), chunk=chunk)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def _ref(raw, lam):
+    return ll_oracle.loglinear(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], lam)
+
+
+CASES = [
+    # B, H, T, dk, dv, r_ab, r_kv, C, dtype, decay
+    (1, 2, 200, 32, 32, 2, 1, 16, "fp32", "channel"),
+    (1, 1, 300, 64, 64, 1, 1, 32, "fp32", "scalar"),
+    (1, 1, 257, 64, 48, 2, 2, 64, "fp32", "channel"),
+    (2, 1, 100, 16, 32, 0, 1, 16, "fp32", "channel"),
+    (1, 1, 40, 32, 32, 1, 1, 64, "fp32", "channel"),
+    (1, 1, 1, 16, 16, 1, 1, 16, "fp32", "channel"),
+    (1, 2, 130, 64, 64, 2, 1, 32, "bf16", "channel"),
+    (1, 1, 160, 64, 128, 1, 1, 128, "bf16", "scalar"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}-{}C{}{}{}".format(*c))
+def test_loglinear_parity(case):
+    Bb, H, T, dk, dv, r_ab, r_kv, C, dtype, decay = case
+    print(f"log-linear case {case}", flush=True)
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, r_ab, r_kv, dtype, decay, seed=T + dk)
+    lam = workloads.loglinear_lambdas(Bb, H, T, seed=T)
+    out = _gpu(raw, lam, dtype, C)
+    e = rel_err(out, _ref(raw, lam))
+    print(f"out {e:.2e}", flush=True)
+    assert e <= TOL[dtype]
+
+
+def test_loglinear_equal_weights_is_base_forward():
+    Bb, H, T, dk, dv = 1, 2, 200, 64, 64
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 2, 1, "fp32", "channel", seed=4)
+    lam = np.ones((Bb, H, T, lattn.loglinear_levels(T)), dtype=np.float32)
+    out = _gpu(raw, lam, "fp32", 16)
+    ref, _ = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"])
+    assert rel_err(out, ref) <= TOL["fp32"]
+
+
+def test_loglinear_chunk_size_invariance():
+    Bb, H, T, dk, dv = 1, 1, 230, 32, 32
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 1, 1, "fp32", "channel", seed=6)
+    lam = workloads.loglinear_lambdas(Bb, H, T, seed=6)
+    outs = [_gpu(raw, lam, "fp32", C) for C in (16, 32, 64, 128)]
+    for o in outs[1:]:
+        assert rel_err(o, outs[0]) <= TOL["fp32"]
+
+
+def test_loglinear_levels_and_rejects():
+    assert lattn.loglinear_levels(4096) == ll_oracle.num_levels(4096) == 13
+    assert lattn.loglinear_levels(1) == 1 and lattn.loglinear_levels(5) == 4
+    raw = workloads.generic_raw(1, 1, 32, 256, 64, 1, 1, "fp32", "channel", seed=0)
+    lam = workloads.loglinear_lambdas(1, 1, 32, seed=0)
+    with pytest.raises(lattn.LattnError):
+        _gpu(raw, lam, "fp32", 16)
