@@ -249,6 +249,64 @@ def hla_leg(torch, lattn, dev, steps, warmup):
     }
 
 
+# Log-linear lift (Log-Linear note, "Key design"; its throughput runs use 48
+# heads of dimension 64 at 8K-32K tokens): Gated DeltaNet B=1, H=48, T=32768,
+# d_k = d_v = 64, chunks of 64, bf16 storage, level weights softplus(N(0, 1)).
+LOGLINEAR_WORKLOAD = dict(B=1, H=48, T=32768, dk=64, dv=64, chunk=64)
+
+
+def loglinear_leg(torch, lattn, dev, steps, warmup):
+    """lattn_loglinear_fwd on the log-linear workload, timed with HIP events on its
+    stream (decay operands from the device parameter kernel before timing).
+    flops: the chunk operators, the weighted chunk-local products and, per chunk
+    and inter-chunk level, the state transport (d_k rows) and, where the level is
+    read, the output rows."""
+    w = LOGLINEAR_WORKLOAD
+    Bb, H, T, dk, dv, C = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["chunk"]
+    raw = workloads.gdn_raw(Bb, H, T, dk, dv, "bf16", seed=0)
+    lam = workloads.loglinear_lambdas(Bb, H, T, seed=0)
+    t = lambda x, d: torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
+    q, k, v = (t(raw[n], torch.bfloat16) for n in ("q", "k", "v"))
+    A, B, V = lattn.gdn_params(k, v, t(raw["g"], torch.float32), t(raw["beta"], torch.float32))
+    ld = t(raw["g"], torch.float32)
+    lt = t(lam, torch.float32)
+    out = torch.empty((Bb, H, T, dv), dtype=torch.bfloat16, device=dev)
+    run = lambda: lattn.loglinear_fwd(q, k, V, ld, A, B, lt, chunk=C, out=out)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    N = -(-T // C)
+    nlev = int(N - 1).bit_length()
+    na, nk = C, C
+    prep_mac = (na + C) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (C + dk) * na * (dk + nk)
+    intra_mac = (dk + C) * nk * dv
+    scan_mac = 0
+    for J in range(N):
+        for m in range(nlev):
+            if (J >> m) & 1:
+                scan_mac += (dk + C) * dk * dv
+            elif J % (2 << m):
+                scan_mac += dk * dk * dv
+    flops = 2.0 * Bb * H * (N * (prep_mac + intra_mac) + scan_mac)
+    return {
+        "entry": "lattn_loglinear_fwd",
+        "workload": f"gdn B{Bb} H{H} T{T} d{dk} C{C} bf16, {lattn.loglinear_levels(T)} levels, weights softplus(N(0,1))",
+        "ms_per_step": round(ms, 4),
+        "value": round(Bb * T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "gflop": round(flops / 1e9, 2),
+        "fp32_mfma_frac": round(flops / (ms / 1e3) / (PEAK["fp32_mfma_TFs"] * 1e12), 4),
+    }
+
+
 def cpu_baseline(spec, raw, budget_s):
     """Time the fp64 oracle (generic form, as used for parity) on a bounded sample of
     (batch, head) rows of the same workload, on all host cores."""
@@ -289,6 +347,7 @@ def main():
     ap.add_argument("--config", default=workloads.HEADLINE, choices=workloads.CONFIG_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hla", action="store_true", help="skip the query-conditioned composition leg")
+    ap.add_argument("--no-loglinear", action="store_true", help="skip the log-linear lift leg")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0, help="target oracle wall time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -404,6 +463,9 @@ def main():
     if spec.name == workloads.HEADLINE and not args.no_hla:
         print("[bench] query-conditioned composition leg", file=sys.stderr, flush=True)
         result["hla"] = hla_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))
+    if spec.name == workloads.HEADLINE and not args.no_loglinear:
+        print("[bench] log-linear lift leg", file=sys.stderr, flush=True)
+        result["loglinear"] = loglinear_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a host sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, raw, args.cpu_budget_s)

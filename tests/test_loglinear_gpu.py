@@ -81,3 +81,30 @@ def test_loglinear_levels_and_rejects():
     lam = workloads.loglinear_lambdas(1, 1, 32, seed=0)
     with pytest.raises(lattn.LattnError):
         _gpu(raw, lam, "fp32", 16)
+
+
+@pytest.mark.slow
+def test_loglinear_bench_workload_sampled():
+    """The bench's log-linear workload (Gated DeltaNet B1 H48 T32768 d64, C 64, bf16)
+    in the launch configuration bench.py times, checked on the first 1100 tokens of
+    two heads (17 chunks: level states up to m = 4 in use) against the oracle on
+    the same stored decay operands.  The lift is causal, so a prefix of the output
+    depends only on the same prefix of the inputs."""
+    import bench
+    w = bench.LOGLINEAR_WORKLOAD
+    Bb, H, T, dk, dv, C = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["chunk"]
+    raw = workloads.gdn_raw(Bb, H, T, dk, dv, "bf16", seed=0)
+    lam = workloads.loglinear_lambdas(Bb, H, T, seed=0)
+    td = torch.bfloat16
+    k, v = dev(raw["k"], td), dev(raw["v"], td)
+    A, B, V = lattn.gdn_params(k, v, dev(raw["g"]), dev(raw["beta"]))
+    out = host(lattn.loglinear_fwd(dev(raw["q"], td), k, V, dev(raw["g"]), A, B, dev(lam), chunk=C))
+    torch.cuda.synchronize()
+    P = 1100
+    for h in (0, 31):
+        sl = lambda x: x[:, h:h + 1, :P]
+        ref = ll_oracle.loglinear(sl(raw["q"]), host(sl(k))[..., None, :], host(sl(V)), sl(raw["g"]),
+                                  host(sl(A)), host(sl(B)), sl(lam))
+        e = rel_err(out[:, h:h + 1, :P], ref)
+        print(f"head {h} first {P} tokens: out {e:.2e}", flush=True)
+        assert e <= TOL["bf16"]
