@@ -600,6 +600,28 @@ hipError_t general_scan(const Problem& p, const void* workspace, const void* v, 
   return p.bf16 ? launch_scan<bf16_raw>(p, a, lds, blocks, s) : launch_scan<float>(p, a, lds, blocks, s);
 }
 
+size_t f32_operators_bytes(const Problem& p) {
+  if (p.bf16 && fast_supported(p)) {
+    const size_t fb = (fast_workspace_bytes(p) + 255) & ~static_cast<size_t>(255);
+    return fb + static_cast<size_t>(p.BH * p.N) * p.mrows() * p.mcols() * sizeof(float);
+  }
+  return general_plan(p).total_bytes;
+}
+
+hipError_t f32_operators(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
+                         const void* B, void* workspace, const float** M, hipStream_t s) {
+  if (p.bf16 && fast_supported(p)) {
+    const size_t fb = (fast_workspace_bytes(p) + 255) & ~static_cast<size_t>(255);
+    float* Mf = reinterpret_cast<float*>(static_cast<char*>(workspace) + fb);
+    *M = Mf;
+    hipError_t e = fast_prepare(p, q, k, ld, A, B, workspace, s);
+    if (e != hipSuccess) return e;
+    return fast_operator_to_f32(p, workspace, Mf, s);
+  }
+  *M = static_cast<const float*>(workspace);   // the general prepare stores them at the front
+  return general_prepare(p, q, k, ld, A, B, workspace, s);
+}
+
 hipError_t general_summaries(const Problem& p, const void* workspace, const void* v, float* sumA,
                              float* sumB, hipStream_t s) {
   SumArgs a{p, static_cast<const float*>(workspace), v, sumA, sumB};

@@ -1,6 +1,7 @@
 // Query-conditioned composition of exact chunk transitions (HLA note, "Core
-// method" and "Method steps", steps 5 and 7), on the chunk operators of the
-// general path.
+// method" and "Method steps", steps 5 and 7), on the chunk operators in
+// row-major fp32 (from the bf16 MFMA prepare where it takes the shape and the
+// storage is bf16, else from the general prepare).
 //
 // With the chunk operator M_j = [[Acal_j, Z_j], [Qbar_j, R_j]] of the base
 // path (Acal_j the chunk's exact transition, B_j = Z_j V_j its exact write,
@@ -207,7 +208,7 @@ bool hla_supported(const Problem& p) { return p.dk <= 128 && p.dv <= 128; }
 HlaPlan hla_plan(const Problem& p) {
   HlaPlan h{};
   const size_t chunks = static_cast<size_t>(p.BH * p.N);
-  h.gen_bytes = align256(general_plan(p).total_bytes);
+  h.gen_bytes = align256(f32_operators_bytes(p));
   h.at_bytes = align256(chunks * p.dk * p.dk * sizeof(float));
   h.bt_bytes = align256(chunks * p.dv * p.dk * sizeof(float));
   h.oi_bytes = align256(chunks * p.C * p.dv * sizeof(float));
@@ -225,9 +226,9 @@ hipError_t launch_hla(const Problem& p, const void* q, const void* k, const floa
   float* AT = reinterpret_cast<float*>(ws + h.gen_bytes);
   float* BT = reinterpret_cast<float*>(ws + h.gen_bytes + h.at_bytes);
   float* OI = reinterpret_cast<float*>(ws + h.gen_bytes + h.at_bytes + h.bt_bytes);
-  hipError_t e = general_prepare(p, q, k, ld, A, B, workspace, s);
+  const float* M = nullptr;   // fp32 chunk operators inside the workspace
+  hipError_t e = f32_operators(p, q, k, ld, A, B, workspace, &M, s);
   if (e != hipSuccess) return e;
-  const float* M = static_cast<const float*>(workspace);   // chunk operators at the front
   HlaSumArgs sa{p, M, v, AT, BT, OI};
   const dim3 grid(static_cast<unsigned>(p.BH * p.N));
   if (p.bf16)

@@ -50,12 +50,23 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s);
+// The fragment-ordered bf16 chunk operators of fast_prepare expanded to the
+// general path's row-major fp32 layout (M: BH * N * (d_k + C) * (d_k + C) floats).
+hipError_t fast_operator_to_f32(const Problem& p, const void* workspace, float* M, hipStream_t s);
 // Fused-parameter prepare (family 1: HDLA from log-lambda and beta, rank 2,
 // per-channel decay; family 2: Gated DeltaNet from g and beta, rank 1,
 // scalar decay).  The operator's value columns carry beta, so the scan reads
 // the raw v.
 hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const void* k, const float* ld,
                               const float* beta, void* workspace, hipStream_t s);
+
+// Chunk operators as row-major fp32 (the general path's layout), for the kernels
+// that read them (HLA composition, log-linear lift): from the bf16 MFMA prepare
+// (expanded to fp32) where it takes the shape and the storage is bf16, else from
+// the general prepare.  *M receives their address inside the workspace.
+size_t f32_operators_bytes(const Problem& p);
+hipError_t f32_operators(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
+                         const void* B, void* workspace, const float** M, hipStream_t s);
 
 // Query-conditioned composition (HLA) on the general path's chunk operators:
 // d_k, d_v <= 128.  Workspace: the general path's, then Acal^T, B^T and the

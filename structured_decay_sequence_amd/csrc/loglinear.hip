@@ -1,5 +1,6 @@
 // Log-linear lift of the recurrence (Log-Linear note, "Key design" 1-4), on
-// the chunk operators of the general path.
+// the chunk operators in row-major fp32 (from the bf16 MFMA prepare where it
+// takes the shape and the storage is bf16, else from the general prepare).
 //
 // Query t weights key s by lam[t, l(t, s)], l the level of s in the Fenwick
 // split of t's prefix: 0 for s = t, else the highest bit where t and s differ
@@ -232,7 +233,7 @@ bool loglinear_supported(const Problem& p) {
 LlPlan loglinear_plan(const Problem& p) {
   LlPlan h{};
   const size_t chunks = static_cast<size_t>(p.BH * p.N);
-  h.gen_bytes = align256(general_plan(p).total_bytes);
+  h.gen_bytes = align256(f32_operators_bytes(p));
   h.zv_bytes = align256(chunks * p.dv * p.dk * sizeof(float));
   h.oi_bytes = align256(chunks * p.C * p.dv * sizeof(float));
   h.total_bytes = h.gen_bytes + h.zv_bytes + h.oi_bytes;
@@ -248,9 +249,9 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
   char* ws = static_cast<char*>(workspace);
   float* ZVT = reinterpret_cast<float*>(ws + h.gen_bytes);
   float* OI = reinterpret_cast<float*>(ws + h.gen_bytes + h.zv_bytes);
-  hipError_t e = general_prepare(p, q, k, ld, A, B, workspace, s);
+  const float* M = nullptr;   // fp32 chunk operators inside the workspace
+  hipError_t e = f32_operators(p, q, k, ld, A, B, workspace, &M, s);
   if (e != hipSuccess) return e;
-  const float* M = static_cast<const float*>(workspace);   // chunk operators at the front
   const int L = loglinear_levels(p.T);
   LlIntraArgs ia{p, M, v, lam, L, ZVT, OI};
   const dim3 grid(static_cast<unsigned>(p.BH * p.N));

@@ -35,7 +35,8 @@ CASES = [
     (2, 1, 77, 48, 32, 2, 2, 16, "fp32", "channel", -1.0),
     (1, 1, 300, 32, 64, 0, 1, 128, "fp32", "channel", -2.0),
     (1, 1, 40, 16, 16, 1, 1, 64, "fp32", "channel", 0.0),
-    (1, 2, 130, 64, 64, 2, 1, 64, "bf16", "channel", -2.0),
+    (1, 2, 130, 64, 64, 2, 1, 64, "bf16", "channel", -2.0),      # operators from the bf16 MFMA prepare
+    (1, 1, 200, 128, 128, 2, 1, 64, "bf16", "channel", -2.0),    # the same at d_k = 128
     (1, 1, 161, 32, 128, 1, 1, 32, "bf16", "scalar", -3.0),
 ]
 

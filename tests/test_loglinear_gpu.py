@@ -40,6 +40,8 @@ CASES = [
     (1, 1, 40, 32, 32, 1, 1, 64, "fp32", "channel"),
     (1, 1, 1, 16, 16, 1, 1, 16, "fp32", "channel"),
     (1, 2, 130, 64, 64, 2, 1, 32, "bf16", "channel"),
+    (1, 1, 200, 128, 128, 2, 1, 64, "bf16", "channel"),   # operators from the bf16 MFMA prepare
+    (1, 2, 150, 64, 64, 1, 1, 64, "bf16", "scalar"),      # the same at d_k = 64
     (1, 1, 160, 64, 128, 1, 1, 128, "bf16", "scalar"),
 ]
 
