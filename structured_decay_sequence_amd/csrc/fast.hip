@@ -894,30 +894,6 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
 }
 
-// The chunk operators in fragment order (bf16) expanded to row-major fp32
-// ((d_k + C) x (d_k + C) per chunk-head), the layout of the general path: one
-// thread per 8-value fragment piece (lane l of the stored pair of 16x16 tiles
-// (mt, 2kp), (mt, 2kp + 1) holds row l % 16, columns 4(l / 16) .. +3 of both).
-__global__ __launch_bounds__(256) void fast_operator_to_f32_kernel(const __bf16* Mb, float* Mf, int MT, int KT,
-                                                                   int64_t pieces) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= pieces) return;
-  const int lane = static_cast<int>(i % 64);
-  const int64_t pr = i / 64;                 // (chunk-head, mt, kp) pair index
-  const int KP = KT / 2;
-  const int kp = static_cast<int>(pr % KP);
-  const int mt = static_cast<int>((pr / KP) % MT);
-  const int64_t job = pr / (static_cast<int64_t>(KP) * MT);
-  const bf16x8 v = *reinterpret_cast<const bf16x8*>(Mb + i * 8);
-  const int ncol = KT * 16;
-  float* row = Mf + (static_cast<size_t>(job) * MT * 16 + mt * 16 + (lane & 15)) * ncol + 4 * (lane >> 4);
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x4 w = f32x4{(float)v[4 * h], (float)v[4 * h + 1], (float)v[4 * h + 2], (float)v[4 * h + 3]};
-    *reinterpret_cast<f32x4*>(row + (2 * kp + h) * 16) = w;
-  }
-}
-
 template <int DK, int RAB, bool SCAL, int MODE>
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
                        const void* A, const void* B, const float* beta, void* M, hipStream_t s) {
@@ -997,15 +973,6 @@ hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const
     if (p.dk == 64) return launch_prep<64, 1, true, kGdn>(p, q, k, ld, nullptr, nullptr, beta, workspace, s);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t fast_operator_to_f32(const Problem& p, const void* workspace, float* M, hipStream_t s) {
-  const int MT = (p.dk + kC) / 16, KT = (p.dk + kNK) / 16;
-  const int64_t pieces = p.BH * p.N * MT * (KT / 2) * 64;
-  if (pieces == 0) return hipSuccess;
-  hipLaunchKernelGGL(fast_operator_to_f32_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const __bf16*>(workspace), M, MT, KT, pieces);
-  return hipGetLastError();
 }
 
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,

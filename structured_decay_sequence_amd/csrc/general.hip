@@ -600,6 +600,37 @@ hipError_t general_scan(const Problem& p, const void* workspace, const void* v, 
   return p.bf16 ? launch_scan<bf16_raw>(p, a, lds, blocks, s) : launch_scan<float>(p, a, lds, blocks, s);
 }
 
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+
+// The bf16 path's chunk operators expanded to row-major fp32 ((d_k + C) x
+// (d_k + C) per chunk-head).  The bf16 path stores every pair of 16x16 tiles
+// (mt, 2kp), (mt, 2kp + 1) as 64 lanes x 8 values: lane l holds row l % 16,
+// columns 4(l / 16) .. +3 of the first tile, then the same of the second.
+// One thread per lane piece.
+__global__ __launch_bounds__(256) void operator_bf16_to_f32_kernel(const __bf16* Mb, float* Mf, int MT, int KT,
+                                                                   int64_t pieces) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int lane = static_cast<int>(i % 64);
+  const int64_t pr = i / 64;   // (chunk-head, mt, kp)
+  const int KP = KT / 2;
+  const int kp = static_cast<int>(pr % KP);
+  const int mt = static_cast<int>((pr / KP) % MT);
+  const int64_t job = pr / (static_cast<int64_t>(KP) * MT);
+  const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(Mb + i * 8);
+  const int ncol = KT * 16;
+  float* row = Mf + (static_cast<size_t>(job) * MT * 16 + mt * 16 + (lane & 15)) * ncol + 4 * (lane >> 4);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 w = f32x4{(float)v[4 * h], (float)v[4 * h + 1], (float)v[4 * h + 2], (float)v[4 * h + 3]};
+    st4(row + (2 * kp + h) * 16, w);
+  }
+}
+
+}  // namespace
+
 size_t f32_operators_bytes(const Problem& p) {
   if (p.bf16 && fast_supported(p)) {
     const size_t fb = (fast_workspace_bytes(p) + 255) & ~static_cast<size_t>(255);
@@ -616,7 +647,11 @@ hipError_t f32_operators(const Problem& p, const void* q, const void* k, const f
     *M = Mf;
     hipError_t e = fast_prepare(p, q, k, ld, A, B, workspace, s);
     if (e != hipSuccess) return e;
-    return fast_operator_to_f32(p, workspace, Mf, s);
+    const int MT = p.mrows() / 16, KT = p.mcols() / 16;
+    const int64_t pieces = p.BH * p.N * MT * (KT / 2) * 64;
+    hipLaunchKernelGGL(operator_bf16_to_f32_kernel, dim3(static_cast<unsigned>((pieces + 255) / 256)), dim3(256), 0,
+                       s, static_cast<const __bf16*>(workspace), Mf, MT, KT, pieces);
+    return hipGetLastError();
   }
   *M = static_cast<const float*>(workspace);   // the general prepare stores them at the front
   return general_prepare(p, q, k, ld, A, B, workspace, s);

@@ -50,9 +50,6 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s);
-// The fragment-ordered bf16 chunk operators of fast_prepare expanded to the
-// general path's row-major fp32 layout (M: BH * N * (d_k + C) * (d_k + C) floats).
-hipError_t fast_operator_to_f32(const Problem& p, const void* workspace, float* M, hipStream_t s);
 // Fused-parameter prepare (family 1: HDLA from log-lambda and beta, rank 2,
 // per-channel decay; family 2: Gated DeltaNet from g and beta, rank 1,
 // scalar decay).  The operator's value columns carry beta, so the scan reads
