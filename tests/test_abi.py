@@ -110,3 +110,45 @@ def test_workspace_size_is_zero_for_invalid_and_grows_with_length():
     a = lib.lattn_chunk_fwd_workspace_size(ctypes.byref(_dims(seqlen=256)), 2, 1, 64)
     b = lib.lattn_chunk_fwd_workspace_size(ctypes.byref(_dims(seqlen=512)), 2, 1, 64)
     assert 0 < a < b
+
+
+def test_hla_and_loglinear_entry_points_declared():
+    names = _declared()
+    for n in ["lattn_hla_fwd", "lattn_hla_fwd_workspace_size", "lattn_loglinear_fwd",
+              "lattn_loglinear_fwd_workspace_size", "lattn_loglinear_levels"]:
+        assert n in names
+
+
+def test_loglinear_levels_host():
+    lib = _lib.load()
+    # 1 + bit length of (T - 1): levels 0 .. that of position T - 1
+    for T, L in [(0, 0), (1, 1), (2, 2), (3, 3), (4, 3), (5, 4), (4096, 13), (4097, 14), (32768, 16)]:
+        assert lib.lattn_loglinear_levels(T) == L, T
+
+
+def test_hla_and_loglinear_validation_before_launch():
+    lib = _lib.load()
+    d = _dims(d_k=256, d_v=64, dtype=_lib.LATTN_FP32)
+    F = ctypes.c_void_p(FAKE)
+    # d_k = 256 is outside both kernels' register plans: rejected on the host
+    rc = lib.lattn_hla_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 64, F, ctypes.c_float(0.1), F, F, 1 << 40, None)
+    assert rc == _lib.LATTN_EUNSUPPORTED
+    rc = lib.lattn_loglinear_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 64, F, F, F, 1 << 40, None)
+    assert rc == _lib.LATTN_EUNSUPPORTED
+    d = _dims(dtype=_lib.LATTN_FP32)
+    # gates / lambda are required
+    rc = lib.lattn_hla_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 64, None, ctypes.c_float(0.1), F, F, 1 << 40, None)
+    assert rc == _lib.LATTN_EINVAL and b"gates" in lib.lattn_last_error()
+    rc = lib.lattn_loglinear_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 64, None, F, F, 1 << 40, None)
+    assert rc == _lib.LATTN_EINVAL and b"lambda" in lib.lattn_last_error()
+    # workspace too small
+    rc = lib.lattn_hla_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 64, F, ctypes.c_float(0.1), F, F, 16, None)
+    assert rc == _lib.LATTN_EWORKSPACE
+    rc = lib.lattn_loglinear_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 64, F, F, F, 16, None)
+    assert rc == _lib.LATTN_EWORKSPACE
+    # d_k + chunk > 192 is outside the log-linear scan's register plan
+    d = _dims(d_k=128, d_v=64, dtype=_lib.LATTN_FP32)
+    rc = lib.lattn_loglinear_fwd(ctypes.byref(d), F, F, F, F, F, F, 2, 1, 128, F, F, F, 1 << 40, None)
+    assert rc == _lib.LATTN_EUNSUPPORTED
+    assert lib.lattn_hla_fwd_workspace_size(ctypes.byref(d), 2, 1, 64) > 0
+    assert lib.lattn_loglinear_fwd_workspace_size(ctypes.byref(d), 2, 1, 64) > 0
