@@ -210,6 +210,31 @@ size_t lattn_loglinear_fwd_workspace_size(const lattn_dims* dims, int r_ab, int 
 int lattn_loglinear_levels(int64_t seqlen);
 
 /*
+ * lattn_chunk_bwd -- backward pass of lattn_chunk_fwd: the gradients of
+ *   L = sum_t <dout_t, out_t> + <dfinal, final_state>
+ * with respect to every input, by the chain rule of the recurrence (the HDLA
+ * note, "Key design 3", trains through it; the pages give no backward
+ * formulas).  Token-serial in reverse, with the state stored at every chunk
+ * start and each chunk's states recomputed from there.
+ * Inputs as lattn_chunk_fwd (initial_state NULL = zero), plus
+ *   dout [B,H,T,d_v] in dims->dtype;  dfinal [B,H,d_k,d_v] fp32 or NULL (zero).
+ * Outputs, fp32, each in its input's layout: dq [B,H,T,d_k]; dk [B,H,T,r_kv,d_k];
+ *   dv [B,H,T,r_kv,d_v]; dlog_decay [B,H,T,d_k] or [B,H,T]; dA, dB [B,H,T,r_ab,d_k]
+ *   (NULL iff r_ab == 0); dinitial_state [B,H,d_k,d_v].
+ * Needs d_k, d_v <= 128, r_ab <= 4, r_kv <= 2 (LATTN_EUNSUPPORTED), and
+ * lattn_chunk_bwd_workspace_size() bytes of caller-owned workspace.
+ * Validation, ownership and stream ordering as lattn_chunk_fwd.
+ */
+int lattn_chunk_bwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                    const float* log_decay, const void* A, const void* B, int r_ab, int r_kv, int chunk,
+                    const void* dout, const float* dfinal, const float* initial_state, float* dq, float* dk,
+                    float* dv, float* dlog_decay, float* dA, float* dB, float* dinitial_state, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace lattn_chunk_bwd needs (0 on invalid arguments). */
+size_t lattn_chunk_bwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
+
+/*
  * lattn_step -- one recurrent token for decoding (HLA note, "Reproduction":
  * a prefill algorithm and a dynamic decoding algorithm; the recurrence of
  * HDLA note, "Key design 3", applied once):

@@ -10,7 +10,7 @@ check shapes/dtypes, allocate outputs and marshal pointers.
 from __future__ import annotations
 
 import ctypes
-from typing import Optional, Tuple
+from typing import Dict, Optional, Tuple
 
 import torch
 
@@ -20,7 +20,7 @@ from ._lib import LattnError, LATTN_BF16, LATTN_FP32, LATTN_DECAY_PER_CHANNEL, L
 __all__ = [
     "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
     "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
-    "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd", "loglinear_fwd", "loglinear_levels",
+    "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd", "loglinear_fwd", "loglinear_levels", "chunk_bwd",
 ]
 
 
@@ -291,6 +291,54 @@ def loglinear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: 
                                  0 if workspace is None else workspace.numel(), _stream(q.device))
     _lib.check(rc, "lattn_loglinear_fwd")
     return out
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+              A: Optional[torch.Tensor], B: Optional[torch.Tensor], dout: torch.Tensor, chunk: int = 64,
+              dfinal: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Backward pass of chunk_fwd (lattn_chunk_bwd): gradients of
+    sum <dout, out> + <dfinal, final_state>.  Inputs as chunk_fwd plus dout
+    [B,H,T,dv] (dtype of q) and dfinal [B,H,dk,dv] fp32 or None.  Returns fp32
+    tensors dq, dk, dv, dlog_decay, dA, dB (None when A is None), dinitial_state,
+    each shaped like its input (k, v with the rank axis)."""
+    Bb, H, T, dk = q.shape
+    dt = q.dtype
+    lead = (Bb, H)
+    k = _ranked(k, lead, T, dk)
+    v = _ranked(v, lead, T, None)
+    r_kv, dv = k.shape[-2], v.shape[-1]
+    _need(q, dt, (Bb, H, T, dk), "q")
+    _need(k, dt, (Bb, H, T, r_kv, dk), "k")
+    _need(v, dt, (Bb, H, T, r_kv, dv), "v")
+    _need(dout, dt, (Bb, H, T, dv), "dout")
+    scalar = log_decay.dim() == 3
+    _need(log_decay, torch.float32, (Bb, H, T) if scalar else (Bb, H, T, dk), "log_decay")
+    r_ab = 0
+    if A is not None:
+        r_ab = A.shape[-2]
+        _need(A, dt, (Bb, H, T, r_ab, dk), "A")
+        _need(B, dt, (Bb, H, T, r_ab, dk), "B")
+    for t, n in ((dfinal, "dfinal"), (initial_state, "initial_state")):
+        if t is not None:
+            _need(t, torch.float32, (Bb, H, dk, dv), n)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = dict(dq=torch.empty((Bb, H, T, dk), **f32), dk=torch.empty((Bb, H, T, r_kv, dk), **f32),
+             dv=torch.empty((Bb, H, T, r_kv, dv), **f32), dlog_decay=torch.empty(tuple(log_decay.shape), **f32),
+             dA=None if A is None else torch.empty(tuple(A.shape), **f32),
+             dB=None if A is None else torch.empty(tuple(A.shape), **f32),
+             dinitial_state=torch.empty((Bb, H, dk, dv), **f32))
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+    if workspace is None:
+        workspace = _workspace(q.device, int(lib.lattn_chunk_bwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk)))
+    rc = lib.lattn_chunk_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A), _ptr(B), r_ab,
+                             r_kv, chunk, _ptr(dout), _ptr(dfinal), _ptr(initial_state), _ptr(g["dq"]), _ptr(g["dk"]),
+                             _ptr(g["dv"]), _ptr(g["dlog_decay"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                             _ptr(g["dinitial_state"]), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                             _stream(q.device))
+    _lib.check(rc, "lattn_chunk_bwd")
+    return g
 
 
 def step(q, k, v, log_decay, A, B, state, out=None):

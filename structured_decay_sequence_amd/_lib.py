@@ -50,6 +50,9 @@ SIGNATURES = {
     "lattn_loglinear_fwd": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "lattn_loglinear_fwd_workspace_size": (_SZ, [_D, _I, _I, _I]),
     "lattn_loglinear_levels": (_I, [ctypes.c_int64]),
+    "lattn_chunk_bwd": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _SZ, _P]),
+    "lattn_chunk_bwd_workspace_size": (_SZ, [_D, _I, _I, _I]),
     "lattn_step": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "lattn_hdla_params": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "lattn_gdn_params": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),

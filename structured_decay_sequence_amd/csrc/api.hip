@@ -337,6 +337,50 @@ int lattn_loglinear_fwd(const lattn_dims* dims, const void* q, const void* k, co
   return ok();
 }
 
+size_t lattn_chunk_bwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return 0;
+  return lattn::backward_workspace_bytes(make_problem(dims, r_ab, r_kv, chunk));
+}
+
+int lattn_chunk_bwd(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                    const float* log_decay, const void* A, const void* B, int r_ab, int r_kv, int chunk,
+                    const void* dout, const float* dfinal, const float* initial_state, float* dq, float* dk,
+                    float* dv, float* dlog_decay, float* dA, float* dB, float* dinitial_state, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", need));
+  LATTN_TRY(check_ptr(dout, "dout", need));
+  LATTN_TRY(check_ptr(dfinal, "dfinal", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  LATTN_TRY(check_ptr(dq, "dq", need));
+  LATTN_TRY(check_ptr(dk, "dk", need));
+  LATTN_TRY(check_ptr(dv, "dv", need));
+  LATTN_TRY(check_ptr(dlog_decay, "dlog_decay", need));
+  LATTN_TRY(check_ptr(dinitial_state, "dinitial_state", true));
+  if (r_ab == 0) {
+    if (dA != nullptr || dB != nullptr) return fail(LATTN_EINVAL, "dA and dB must be NULL when r_ab == 0");
+  } else {
+    LATTN_TRY(check_ptr(dA, "dA", need));
+    LATTN_TRY(check_ptr(dB, "dB", need));
+  }
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  if (!lattn::backward_supported(p))
+    return fail(LATTN_EUNSUPPORTED, "lattn_chunk_bwd needs d_k, d_v <= 128, r_ab <= 4, r_kv <= 2 "
+                "(got d_k %d, d_v %d, r_ab %d, r_kv %d)", p.dk, p.dv, r_ab, r_kv);
+  if (!need) return hip_status(lattn::launch_copy_state(p, dfinal, dinitial_state, stream), "copy state");
+  const size_t ws = lattn::backward_workspace_bytes(p);
+  if (workspace == nullptr || workspace_bytes < ws)
+    return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
+  LATTN_TRY(check_ptr(workspace, "workspace", true));
+  LATTN_TRY(hip_status(lattn::launch_backward(p, q, k, v, log_decay, A, B, dout, dfinal, initial_state, dq, dk, dv,
+                                              dlog_decay, dA, dB, dinitial_state, workspace, stream),
+                       "backward launch"));
+  return ok();
+}
+
 int lattn_chunk_fwd_check(const lattn_dims* dims, const void* q, const void* k, const void* v,
                           const float* log_decay, const void* A, const void* B, int r_ab,
                           int r_kv, int chunk, const void* out, const void* workspace,

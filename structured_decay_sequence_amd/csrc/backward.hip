@@ -1,0 +1,373 @@
+// Backward pass of the recurrence (the chain rule of the HDLA note's "Key
+// design 3" token recurrence, in reverse; the pages print no backward
+// formulas):
+//   forward   P_t = D_t - A_t B_t^T,  S_t = P_t S_{t-1} + K_t V_t^T,  o_t = S_t^T q_t
+//   backward  G <- dS_T;  for t = T-1 .. 0:
+//               G += q_t do_t^T;  dq_t = S_t do_t;  dK_t = G V_t;  dV_t = G^T K_t
+//               with dP_t = G S_{t-1}^T:  dA_t = -dP_t B_t,  dB_t = -dP_t^T A_t,
+//               dlog_decay_t = diag(dP_t) (.) exp(log_decay_t)
+//               G <- P_t^T G
+//             dS_init = G
+// Everything is expressed with matrix-vector products over the state, so dP_t
+// (d_k x d_k) is never formed: dA_t = -G (S_{t-1}^T B_t), dB_t = -S_{t-1} (G^T A_t),
+// and diag(dP_t) is the row-wise dot of G and S_{t-1}.
+//
+// One workgroup (512 threads, a 32 x 16 grid) per (batch, head), token by
+// token.  Thread (tr, tc) holds rows tr, tr+32, .. and columns tc, tc+16, ..
+// of S_t, S_{t-1} and G in registers.  Sums over columns are shuffles inside
+// a row group of 16 lanes; sums over rows are shuffles inside the wave, then
+// an LDS exchange between the eight waves.  A first pass stores the state at
+// every chunk start; then, chunk by chunk from the end, the chunk's states
+// are recomputed into a workspace buffer (each thread reads back only the
+// values it wrote) and the chunk's tokens are walked in reverse.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lattn {
+namespace {
+
+constexpr int kBwThreads = 512;
+constexpr int kNTR = 32, kNTC = 16;      // thread grid: row groups x column groups
+constexpr int kRB = 4, kCB = 8;          // rows / columns per thread: d_k, d_v <= 128
+constexpr int kRab = 4, kRkv = 2;        // rank limits of this kernel
+constexpr int kQ = 2 * kRab + kRkv;      // column sums per token: A^T G, B^T S_{t-1}, K^T G
+constexpr int kWv = kBwThreads / 64;
+
+struct BwArgs {
+  Problem p;
+  const void* q;
+  const void* K;
+  const void* V;
+  const float* ld;
+  const void* A;
+  const void* B;
+  const void* dout;
+  const float* dfinal;
+  const float* S0;
+  float* dq;
+  float* dK;
+  float* dV;
+  float* dld;
+  float* dA;
+  float* dB;
+  float* dS0;
+  float* ws;
+  size_t ws_head;   // floats of workspace per (batch, head)
+};
+
+template <typename TI>
+__global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
+  // per-wave row sums [parity][wave][quantity][column], double-buffered by token
+  // parity, then the scalar-decay per-row terms [parity][row]
+  extern __shared__ __align__(16) float lds[];
+  auto red = [&](int par, int w, int q, int n) -> float& { return lds[((par * kWv + w) * kQ + q) * 128 + n]; };
+  float* dsum0 = lds + 2 * kWv * kQ * 128;
+  auto dsum = [&](int par, int i) -> float& { return dsum0[par * 128 + i]; };
+  const Problem& p = a.p;
+  const int dk = p.dk, dv = p.dv, C = p.C, r_ab = p.r_ab, r_kv = p.r_kv;
+  const int64_t T = p.T, N = p.N;
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tr = tid / kNTC, tc = tid % kNTC;
+  const TI* qp = static_cast<const TI*>(a.q);
+  const TI* Kp = static_cast<const TI*>(a.K);
+  const TI* Vp = static_cast<const TI*>(a.V);
+  const TI* Ap = static_cast<const TI*>(a.A);
+  const TI* Bp = static_cast<const TI*>(a.B);
+  const TI* dop = static_cast<const TI*>(a.dout);
+  const int nst = kRB * kCB;                                       // register slots per state
+  const size_t sstride = static_cast<size_t>(nst) * kBwThreads;   // floats per stored state
+  float* ckpt = a.ws + static_cast<size_t>(bh) * a.ws_head;       // N states, thread-major
+  float* buf = ckpt + static_cast<size_t>(N) * sstride;            // C + 1 states of one chunk
+  auto rowi = [&](int r) { return tr + kNTR * r; };
+  auto coln = [&](int c) { return tc + kNTC * c; };
+  auto rok = [&](int r) { return tr + kNTR * r < dk; };
+  auto cok = [&](int c) { return tc + kNTC * c < dv; };
+  // thread-major storage of one state: slot (r, c) of thread tid at (r * kCB + c) * 512 + tid
+  auto st_state = [&](float* base, const float (&S)[kRB][kCB]) {
+#pragma unroll
+    for (int r = 0; r < kRB; ++r)
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) base[(r * kCB + c) * kBwThreads + tid] = S[r][c];
+  };
+  auto ld_state = [&](const float* base, float (&S)[kRB][kCB]) {
+#pragma unroll
+    for (int r = 0; r < kRB; ++r)
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) S[r][c] = base[(r * kCB + c) * kBwThreads + tid];
+  };
+  // sum over the 16 column groups of a row group (lanes differing in bits 0..3)
+  auto rowsum = [&](float v) {
+#pragma unroll
+    for (int s = 1; s < kNTC; s <<= 1) v += __shfl_xor(v, s, 64);
+    return v;
+  };
+  // Per-token operands of this thread's rows and columns.
+  float lam[kRB], Av[kRab][kRB], Bv[kRab][kRB], Kv[kRkv][kRB], Vv[kRkv][kCB];
+  auto load_tok = [&](int64_t t) {
+    const int64_t tok = bh * T + t;
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+      const int i = rok(r) ? rowi(r) : 0;
+      lam[r] = expf(p.scalar ? a.ld[tok] : a.ld[tok * dk + i]);
+#pragma unroll
+      for (int x = 0; x < kRab; ++x) {
+        const bool ok = x < r_ab && rok(r);
+        Av[x][r] = ok ? Elem<TI>::load(Ap, (static_cast<size_t>(tok) * r_ab + x) * dk + i) : 0.f;
+        Bv[x][r] = ok ? Elem<TI>::load(Bp, (static_cast<size_t>(tok) * r_ab + x) * dk + i) : 0.f;
+      }
+#pragma unroll
+      for (int x = 0; x < kRkv; ++x)
+        Kv[x][r] = (x < r_kv && rok(r)) ? Elem<TI>::load(Kp, (static_cast<size_t>(tok) * r_kv + x) * dk + i) : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kCB; ++c) {
+      const int n = cok(c) ? coln(c) : 0;
+#pragma unroll
+      for (int x = 0; x < kRkv; ++x)
+        Vv[x][c] = (x < r_kv && cok(c)) ? Elem<TI>::load(Vp, (static_cast<size_t>(tok) * r_kv + x) * dv + n) : 0.f;
+    }
+  };
+  // Sums over rows of this thread's columns, for nq quantities whose per-thread
+  // partials are in part[q][c]: inside the wave (lane bits 4, 5), then across
+  // the waves through LDS.  One barrier.
+  auto colsum = [&](float (&part)[kQ][kCB], int nq, int par) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      if (q >= nq) break;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+        float v = part[q][c];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        part[q][c] = v;
+        if ((lane >> 4) == 0 && cok(c)) red(par, wave, q, coln(c)) = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      if (q >= nq) break;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+        float v = 0.f;
+        if (cok(c)) {
+#pragma unroll
+          for (int w = 0; w < kWv; ++w) v += red(par, w, q, coln(c));
+        }
+        part[q][c] = v;
+      }
+    }
+  };
+  // One forward token: S <- D S - A (B^T S) + K V^T.
+  auto fwd_step = [&](float (&S)[kRB][kCB], int par) {
+    float part[kQ][kCB];
+#pragma unroll
+    for (int x = 0; x < kRab; ++x)
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) v += Bv[x][r] * S[r][c];
+        part[x][c] = v;
+      }
+    colsum(part, r_ab, par);
+#pragma unroll
+    for (int r = 0; r < kRB; ++r)
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+        float v = lam[r] * S[r][c];
+#pragma unroll
+        for (int x = 0; x < kRab; ++x) v -= Av[x][r] * part[x][c];
+#pragma unroll
+        for (int x = 0; x < kRkv; ++x) v += Kv[x][r] * Vv[x][c];
+        S[r][c] = v;
+      }
+  };
+
+  float S[kRB][kCB], Sp[kRB][kCB], G[kRB][kCB];
+  // pass 1: the state entering every chunk
+#pragma unroll
+  for (int r = 0; r < kRB; ++r)
+#pragma unroll
+    for (int c = 0; c < kCB; ++c)
+      S[r][c] = (a.S0 && rok(r) && cok(c)) ? a.S0[(bh * dk + rowi(r)) * dv + coln(c)] : 0.f;
+  int par = 0;
+  for (int64_t j = 0; j < N; ++j) {
+    st_state(ckpt + j * sstride, S);
+    const int64_t t1 = (j + 1) * C < T ? (j + 1) * C : T;
+    for (int64_t t = j * C; t < t1; ++t) {
+      load_tok(t);
+      fwd_step(S, par);
+      par ^= 1;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRB; ++r)
+#pragma unroll
+    for (int c = 0; c < kCB; ++c)
+      G[r][c] = (a.dfinal && rok(r) && cok(c)) ? a.dfinal[(bh * dk + rowi(r)) * dv + coln(c)] : 0.f;
+
+  // pass 2: chunks from the end; recompute the chunk's states, then walk back
+  for (int64_t j = N - 1; j >= 0; --j) {
+    const int64_t t0 = j * C, t1 = (j + 1) * C < T ? (j + 1) * C : T;
+    ld_state(ckpt + j * sstride, S);
+    st_state(buf, S);
+    for (int64_t t = t0; t < t1; ++t) {
+      load_tok(t);
+      fwd_step(S, par);
+      par ^= 1;
+      st_state(buf + (t - t0 + 1) * sstride, S);
+    }
+    // S holds S_{t1-1}
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+      const int64_t tok = bh * T + t;
+      load_tok(t);
+      ld_state(buf + (t - t0) * sstride, Sp);   // S_{t-1}
+      float qv[kRB], dov[kCB];
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) qv[r] = rok(r) ? Elem<TI>::load(qp, static_cast<size_t>(tok) * dk + rowi(r)) : 0.f;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) dov[c] = cok(c) ? Elem<TI>::load(dop, static_cast<size_t>(tok) * dv + coln(c)) : 0.f;
+      // G += q do^T
+#pragma unroll
+      for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int c = 0; c < kCB; ++c) G[r][c] += qv[r] * dov[c];
+      // row sums: dq = S_t do, dlog_decay terms = rowdot(G, S_{t-1})
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < kCB; ++c) {
+          s1 += S[r][c] * dov[c];
+          s2 += G[r][c] * Sp[r][c];
+        }
+        s1 = rowsum(s1);
+        s2 = rowsum(s2) * lam[r];
+        if (tc == 0 && rok(r)) {
+          a.dq[static_cast<size_t>(tok) * dk + rowi(r)] = s1;
+          if (!p.scalar) a.dld[static_cast<size_t>(tok) * dk + rowi(r)] = s2;
+          else dsum(par, rowi(r)) = s2;
+        }
+      }
+      // column sums: z = A^T G, w = B^T S_{t-1}, dV = K^T G
+      float part[kQ][kCB];
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+#pragma unroll
+        for (int x = 0; x < kRab; ++x) {
+          float z = 0.f, w = 0.f;
+#pragma unroll
+          for (int r = 0; r < kRB; ++r) {
+            z += Av[x][r] * G[r][c];
+            w += Bv[x][r] * Sp[r][c];
+          }
+          part[x][c] = z;
+          part[kRab + x][c] = w;
+        }
+#pragma unroll
+        for (int x = 0; x < kRkv; ++x) {
+          float d = 0.f;
+#pragma unroll
+          for (int r = 0; r < kRB; ++r) d += Kv[x][r] * G[r][c];
+          part[2 * kRab + x][c] = d;
+        }
+      }
+      colsum(part, kQ, par);
+      if (p.scalar && tid == 0) {
+        float s = 0.f;
+        for (int i = 0; i < dk; ++i) s += dsum(par, i);
+        a.dld[tok] = s;
+      }
+      if (tr == 0) {
+#pragma unroll
+        for (int c = 0; c < kCB; ++c)
+#pragma unroll
+          for (int x = 0; x < kRkv; ++x)
+            if (x < r_kv && cok(c)) a.dV[(static_cast<size_t>(tok) * r_kv + x) * dv + coln(c)] = part[2 * kRab + x][c];
+      }
+      // row sums: dK = G V, dA = -G w, dB = -S_{t-1} z
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+#pragma unroll
+        for (int x = 0; x < kRkv; ++x) {
+          float s = 0.f;
+#pragma unroll
+          for (int c = 0; c < kCB; ++c) s += G[r][c] * Vv[x][c];
+          s = rowsum(s);
+          if (tc == 0 && x < r_kv && rok(r)) a.dK[(static_cast<size_t>(tok) * r_kv + x) * dk + rowi(r)] = s;
+        }
+#pragma unroll
+        for (int x = 0; x < kRab; ++x) {
+          float sa = 0.f, sb = 0.f;
+#pragma unroll
+          for (int c = 0; c < kCB; ++c) {
+            sa += G[r][c] * part[kRab + x][c];
+            sb += Sp[r][c] * part[x][c];
+          }
+          sa = rowsum(sa);
+          sb = rowsum(sb);
+          if (tc == 0 && x < r_ab && rok(r)) {
+            a.dA[(static_cast<size_t>(tok) * r_ab + x) * dk + rowi(r)] = -sa;
+            a.dB[(static_cast<size_t>(tok) * r_ab + x) * dk + rowi(r)] = -sb;
+          }
+        }
+      }
+      // G <- P_t^T G = D G - B (A^T G)
+#pragma unroll
+      for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int c = 0; c < kCB; ++c) {
+          float v = lam[r] * G[r][c];
+#pragma unroll
+          for (int x = 0; x < kRab; ++x) v -= Bv[x][r] * part[x][c];
+          G[r][c] = v;
+        }
+#pragma unroll
+      for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int c = 0; c < kCB; ++c) S[r][c] = Sp[r][c];
+      par ^= 1;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRB; ++r)
+#pragma unroll
+    for (int c = 0; c < kCB; ++c)
+      if (rok(r) && cok(c)) a.dS0[(bh * dk + rowi(r)) * dv + coln(c)] = G[r][c];
+}
+
+}  // namespace
+
+bool backward_supported(const Problem& p) {
+  return p.dk <= kNTR * kRB && p.dv <= kNTC * kCB && p.r_ab <= kRab && p.r_kv <= kRkv;
+}
+
+size_t backward_workspace_bytes(const Problem& p) {
+  const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored state
+  return static_cast<size_t>(p.BH) * (static_cast<size_t>(p.N) + p.C + 1) * st * sizeof(float);
+}
+
+hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
+                           const void* A, const void* B, const void* dout, const float* dfinal, const float* S0,
+                           float* dq, float* dK, float* dV, float* dld, float* dA, float* dB, float* dS0,
+                           void* workspace, hipStream_t s) {
+  if (p.BH == 0) return hipSuccess;
+  if (!backward_supported(p)) return hipErrorInvalidValue;
+  const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;
+  BwArgs a{p, q, k, v, ld, A, B, dout, dfinal, S0, dq, dK, dV, dld, dA, dB, dS0,
+           static_cast<float*>(workspace), (static_cast<size_t>(p.N) + p.C + 1) * st};
+  const size_t lds = (static_cast<size_t>(2) * kWv * kQ * 128 + 2 * 128) * sizeof(float);
+  const void* fn = p.bf16 ? reinterpret_cast<const void*>(backward_kernel<bf16_raw>)
+                          : reinterpret_cast<const void*>(backward_kernel<float>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  if (p.bf16)
+    hipLaunchKernelGGL(backward_kernel<bf16_raw>, dim3(static_cast<unsigned>(p.BH)), dim3(kBwThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(backward_kernel<float>, dim3(static_cast<unsigned>(p.BH)), dim3(kBwThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lattn

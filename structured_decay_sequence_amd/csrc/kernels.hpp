@@ -90,6 +90,15 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
                             const void* B, const void* v, const float* lam, void* out, void* workspace,
                             hipStream_t s);
 
+// Backward pass, token-serial with chunk checkpoints: d_k, d_v <= 128,
+// r_ab <= 4, r_kv <= 2; gradients in fp32.
+bool backward_supported(const Problem& p);
+size_t backward_workspace_bytes(const Problem& p);
+hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
+                           const void* A, const void* B, const void* dout, const float* dfinal, const float* S0,
+                           float* dq, float* dK, float* dV, float* dld, float* dA, float* dB, float* dS0,
+                           void* workspace, hipStream_t s);
+
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, float* state, void* out,
                        hipStream_t s);

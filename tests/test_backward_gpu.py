@@ -1,0 +1,62 @@
+"""GPU parity of the backward pass (lattn_chunk_bwd) against the fp64 BPTT oracle
+(itself pinned by finite differences), through the C ABI.
+
+Gate per gradient tensor: max|gpu - ref| / max|ref| <= 1e-4 for fp32 storage and
+<= 2e-2 for bf16 storage (fp32 arithmetic and fp32 gradients in both).
+"""
+import numpy as np
+import pytest
+
+from oracle import backward as bwd_oracle
+import workloads
+from tests.helpers import TOL, dev, host, rel_err, torch_dtype
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+lattn = pytest.importorskip("structured_decay_sequence_amd")
+
+CASES = [
+    # B, H, T, dk, dv, r_ab, r_kv, C, dtype, decay, state terms
+    (1, 2, 100, 32, 32, 2, 1, 32, "fp32", "channel", True),
+    (1, 1, 77, 64, 48, 1, 2, 16, "fp32", "scalar", True),
+    (2, 1, 64, 16, 16, 0, 1, 64, "fp32", "channel", False),
+    (1, 1, 90, 48, 64, 4, 2, 64, "fp32", "channel", True),
+    (1, 1, 130, 128, 128, 2, 1, 64, "fp32", "channel", True),
+    (1, 2, 70, 64, 64, 2, 1, 32, "bf16", "channel", True),
+    (1, 1, 1, 32, 32, 1, 1, 16, "fp32", "channel", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}-{}C{}{}{}s{}".format(*c))
+def test_backward_parity(case):
+    Bb, H, T, dk, dv, r_ab, r_kv, C, dtype, decay, state = case
+    print(f"backward case {case}", flush=True)
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, r_ab, r_kv, dtype, decay, seed=T + dk)
+    rng = np.random.default_rng(T)
+    dout = workloads.round_bf16(rng.standard_normal((Bb, H, T, dv)).astype(np.float32)) if dtype == "bf16" \
+        else rng.standard_normal((Bb, H, T, dv)).astype(np.float32)
+    S0 = (rng.standard_normal((Bb, H, dk, dv)) * 0.1).astype(np.float32) if state else None
+    dfin = rng.standard_normal((Bb, H, dk, dv)).astype(np.float32) if state else None
+    td = torch_dtype(dtype)
+    g = lattn.chunk_bwd(dev(raw["q"], td), dev(raw["K"], td), dev(raw["V"], td), dev(raw["log_decay"]),
+                        dev(raw["A"], td), dev(raw["B"], td), dev(dout, td), chunk=C, dfinal=dev(dfin),
+                        initial_state=dev(S0))
+    torch.cuda.synchronize()
+    ref = bwd_oracle.backward(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], dout, dfin, S0)
+    pairs = [("dq", "dq"), ("dk", "dK"), ("dv", "dV"), ("dlog_decay", "dlog_decay"), ("dA", "dA"), ("dB", "dB"),
+             ("dinitial_state", "dS0")]
+    for gn, rn in pairs:
+        if ref[rn] is None:
+            assert g[gn] is None
+            continue
+        e = rel_err(host(g[gn]), ref[rn])
+        print(f"{gn} {e:.2e}", flush=True)
+        assert e <= TOL[dtype], gn
+
+
+def test_backward_rejects_unsupported():
+    raw = workloads.generic_raw(1, 1, 16, 256, 64, 1, 1, "fp32", "channel", seed=0)
+    with pytest.raises(lattn.LattnError):
+        lattn.chunk_bwd(dev(raw["q"]), dev(raw["K"]), dev(raw["V"]), dev(raw["log_decay"]), dev(raw["A"]),
+                        dev(raw["B"]), dev(np.zeros((1, 1, 16, 64), np.float32)), chunk=16)
