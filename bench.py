@@ -35,6 +35,8 @@ PEAK = {  # MI355X published peaks
     "hbm_GBs": 8000.0,
     "bf16_mfma_TFs": 2500.0,
     "fp32_mfma_TFs": 157.3,
+    # fp32 vector without packed-fp32 issue: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+    "fp32_valu_TFs": 78.6,
 }
 KERNEL_SOURCES = {
     "general_fp32": ["structured_decay_sequence_amd/csrc/general.hip"],
@@ -312,6 +314,42 @@ def loglinear_leg(torch, lattn, dev, steps, warmup):
     }
 
 
+def backward_leg(spec, raw, inputs, torch, lattn, dev):
+    """lattn_chunk_bwd on the benchmark workload (same inputs as the forward,
+    seeded output cotangents and a final-state cotangent), one timed call after
+    one warm-up, HIP events on its stream.  flops: the token-serial reverse
+    recurrence's multiply-adds (the forward recompute twice, the backward's
+    state products), priced against the fp32 vector peak it runs on."""
+    q, K, V, ld, A, B = inputs
+    td = q.dtype
+    rng = np.random.default_rng(1)
+    dout = torch.from_numpy(rng.standard_normal((spec.B, spec.H, spec.T, spec.dv), dtype=np.float32)).to(td).to(dev)
+    dfin = torch.from_numpy(rng.standard_normal((spec.B, spec.H, spec.dk, spec.dv), dtype=np.float32)).to(dev)
+    run = lambda: lattn.chunk_bwd(q, K, V, ld, A, B, dout, chunk=spec.chunk, dfinal=dfin)
+    run()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1)
+    dk, dv, ra, rk = spec.dk, spec.dv, spec.r_ab, spec.r_kv
+    fwd_mac = dk * dv * (2 * ra + rk + 1)                    # B^T S, D S - A u + K V^T
+    bwd_mac = dk * dv * (1 + 1 + 1 + 3 * ra + 2 * rk + 1 + 2 * ra + 1)
+    flops = 2.0 * spec.B * spec.H * spec.T * (2 * fwd_mac + bwd_mac)
+    return {
+        "entry": "lattn_chunk_bwd",
+        "kind": "token-serial reverse recurrence with chunk checkpoints",
+        "ms_per_step": round(ms, 3),
+        "value": round(spec.B * spec.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "gflop": round(flops / 1e9, 2),
+        "fp32_valu_frac": round(flops / (ms / 1e3) / (PEAK["fp32_valu_TFs"] * 1e12), 4),
+    }
+
+
 def cpu_baseline(spec, raw, budget_s):
     """Time the fp64 oracle (generic form, as used for parity) on a bounded sample of
     (batch, head) rows of the same workload, on all host cores."""
@@ -353,6 +391,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hla", action="store_true", help="skip the query-conditioned composition leg")
     ap.add_argument("--no-loglinear", action="store_true", help="skip the log-linear lift leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0, help="target oracle wall time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -468,6 +507,9 @@ def main():
     if spec.name == workloads.HEADLINE and not args.no_hla:
         print("[bench] query-conditioned composition leg", file=sys.stderr, flush=True)
         result["hla"] = hla_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))
+    if spec.name == workloads.HEADLINE and not args.no_backward:
+        print("[bench] backward leg", file=sys.stderr, flush=True)
+        result["backward"] = backward_leg(spec, raw, (q, K, V, ld, A, B), torch, lattn, dev)
     if spec.name == workloads.HEADLINE and not args.no_loglinear:
         print("[bench] log-linear lift leg", file=sys.stderr, flush=True)
         result["loglinear"] = loglinear_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))

@@ -60,3 +60,40 @@ def test_backward_rejects_unsupported():
     with pytest.raises(lattn.LattnError):
         lattn.chunk_bwd(dev(raw["q"]), dev(raw["K"]), dev(raw["V"]), dev(raw["log_decay"]), dev(raw["A"]),
                         dev(raw["B"]), dev(np.zeros((1, 1, 16, 64), np.float32)), chunk=16)
+
+
+@pytest.mark.slow
+def test_backward_headline_workload_sampled():
+    """The headline HDLA workload (B8 H16 T4096 d128, C 64, bf16) through
+    lattn_chunk_bwd as bench.py calls it, with output cotangents on the first P
+    tokens only and no final-state cotangent: gradients of tokens < P must equal
+    those of the P-token problem (checked on one head against the oracle), and
+    every gradient of a later token must be exactly zero (no cotangent reaches
+    it)."""
+    spec = workloads.CONFIGS[workloads.HEADLINE]
+    raw = workloads.raw_for(spec)
+    td = torch.bfloat16
+    k, v = dev(raw["k"], td), dev(raw["v"], td)
+    ll = dev(raw["log_lambda"])
+    A, B, V = lattn.hdla_params(k, v, ll, dev(raw["beta"]))
+    P = 300
+    rng = np.random.default_rng(2)
+    dout = np.zeros((spec.B, spec.H, spec.T, spec.dv), np.float32)
+    dout[:, :, :P] = workloads.round_bf16(rng.standard_normal((spec.B, spec.H, P, spec.dv)).astype(np.float32))
+    g = lattn.chunk_bwd(dev(raw["q"], td), k, V, ll, A, B, dev(dout, td), chunk=spec.chunk)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dlog_decay", "dA", "dB"):
+        assert float(g[n][:, :, P:].abs().max()) == 0.0, n
+    b, h = 3, 11
+    sl = lambda x: x[b:b + 1, h:h + 1, :P]
+    ref = bwd_oracle.backward(sl(raw["q"]), host(sl(k))[..., None, :], host(sl(V)), sl(raw["log_lambda"]),
+                              host(sl(A)), host(sl(B)), sl(dout))
+    pairs = [("dq", "dq"), ("dk", "dK"), ("dv", "dV"), ("dlog_decay", "dlog_decay"), ("dA", "dA"), ("dB", "dB")]
+    for gn, rn in pairs:
+        got = host(g[gn][b:b + 1, h:h + 1, :P])
+        e = rel_err(got, ref[rn])
+        print(f"{gn} first {P} tokens of (b {b}, h {h}): {e:.2e}", flush=True)
+        assert e <= TOL["bf16"], gn
+    e = rel_err(host(g["dinitial_state"][b:b + 1, h:h + 1]), ref["dS0"])
+    print(f"dinitial_state {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
