@@ -97,3 +97,26 @@ def test_backward_headline_workload_sampled():
     e = rel_err(host(g["dinitial_state"][b:b + 1, h:h + 1]), ref["dS0"])
     print(f"dinitial_state {e:.2e}", flush=True)
     assert e <= TOL["bf16"]
+
+
+def test_backward_empty_sequence_passes_the_state_gradient():
+    """T = 0: no token, so the initial state's gradient is the final state's cotangent."""
+    raw = workloads.generic_raw(1, 2, 0, 32, 32, 1, 1, "fp32", "channel", seed=0)
+    dfin = np.random.default_rng(0).standard_normal((1, 2, 32, 32)).astype(np.float32)
+    g = lattn.chunk_bwd(dev(raw["q"]), dev(raw["K"]), dev(raw["V"]), dev(raw["log_decay"]), dev(raw["A"]),
+                        dev(raw["B"]), dev(np.zeros((1, 2, 0, 32), np.float32)), chunk=16, dfinal=dev(dfin))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(g["dinitial_state"]), dfin)
+
+
+def test_backward_repeatable():
+    raw = workloads.generic_raw(1, 2, 90, 64, 64, 2, 1, "bf16", "channel", seed=4)
+    dout = workloads.round_bf16(np.random.default_rng(4).standard_normal((1, 2, 90, 64)).astype(np.float32))
+    run = lambda: lattn.chunk_bwd(dev(raw["q"], torch.bfloat16), dev(raw["K"], torch.bfloat16),
+                                  dev(raw["V"], torch.bfloat16), dev(raw["log_decay"]), dev(raw["A"], torch.bfloat16),
+                                  dev(raw["B"], torch.bfloat16), dev(dout, torch.bfloat16), chunk=32)
+    a, b = run(), run()
+    torch.cuda.synchronize()
+    for n in a:
+        if a[n] is not None:
+            assert torch.equal(a[n], b[n]), n

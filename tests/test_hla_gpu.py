@@ -106,3 +106,14 @@ def test_hla_bench_workload_sampled():
     e = rel_err(got, ref[:, :, qs])
     print(f"sampled queries {qs}: out {e:.2e}", flush=True)
     assert e <= TOL["bf16"]
+
+
+def test_hla_empty_and_repeatable():
+    raw = workloads.generic_raw(1, 2, 0, 32, 32, 1, 1, "fp32", "channel", seed=0)
+    gates = np.zeros((1, 2, 0, 0), np.float32)
+    assert _gpu(raw, gates, "fp32", 32, 0.1).shape == (1, 2, 0, 32)
+    raw = workloads.generic_raw(1, 2, 150, 64, 64, 2, 1, "bf16", "channel", seed=9)
+    gates = workloads.hla_gates(1, 2, 150, 64, mu=-1.0, seed=9)
+    a = _gpu(raw, gates, "bf16", 64, 0.1)
+    b = _gpu(raw, gates, "bf16", 64, 0.1)
+    assert np.array_equal(a, b)

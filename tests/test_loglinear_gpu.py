@@ -110,3 +110,14 @@ def test_loglinear_bench_workload_sampled():
         e = rel_err(out[:, h:h + 1, :P], ref)
         print(f"head {h} first {P} tokens: out {e:.2e}", flush=True)
         assert e <= TOL["bf16"]
+
+
+def test_loglinear_empty_and_repeatable():
+    raw = workloads.generic_raw(1, 2, 0, 32, 32, 1, 1, "fp32", "channel", seed=0)
+    lam = np.zeros((1, 2, 0, 0), np.float32)
+    assert _gpu(raw, lam, "fp32", 16).shape == (1, 2, 0, 32)
+    raw = workloads.generic_raw(1, 2, 150, 64, 64, 2, 1, "bf16", "channel", seed=9)
+    lam = workloads.loglinear_lambdas(1, 2, 150, seed=9)
+    a = _gpu(raw, lam, "bf16", 64)
+    b = _gpu(raw, lam, "bf16", 64)
+    assert np.array_equal(a, b)
