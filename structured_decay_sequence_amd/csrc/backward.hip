@@ -16,10 +16,12 @@
 // token.  Thread (tr, tc) holds rows tr, tr+32, .. and columns tc, tc+16, ..
 // of S_t, S_{t-1} and G in registers.  Sums over columns are shuffles inside
 // a row group of 16 lanes; sums over rows are shuffles inside the wave, then
-// an LDS exchange between the eight waves.  A first pass stores the state at
+// an LDS exchange between the eight waves (each sum formed once, then read
+// back by the threads of its column).  A first pass stores the state at
 // every chunk start; then, chunk by chunk from the end, the chunk's states
 // are recomputed into a workspace buffer (each thread reads back only the
-// values it wrote) and the chunk's tokens are walked in reverse.
+// values it wrote, stored contiguously per thread) and the chunk's tokens are
+// walked in reverse.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,8 +31,8 @@ namespace {
 constexpr int kBwThreads = 512;
 constexpr int kNTR = 32, kNTC = 16;      // thread grid: row groups x column groups
 constexpr int kRB = 4, kCB = 8;          // rows / columns per thread: d_k, d_v <= 128
-constexpr int kRab = 4, kRkv = 2;        // rank limits of this kernel
-constexpr int kQ = 2 * kRab + kRkv;      // column sums per token: A^T G, B^T S_{t-1}, K^T G
+constexpr int kRabMax = 4, kRkvMax = 2;  // rank limits of this kernel
+constexpr int kQMax = 2 * kRabMax + kRkvMax;   // LDS stride: column sums per token
 constexpr int kWv = kBwThreads / 64;
 
 struct BwArgs {
@@ -55,14 +57,20 @@ struct BwArgs {
   size_t ws_head;   // floats of workspace per (batch, head)
 };
 
-template <typename TI>
+// RAB, RKV: the ranks the per-thread operand arrays are sized for (r_ab <= RAB,
+// r_kv <= RKV); kQ column sums per token: A^T G, B^T S_{t-1}, K^T G.
+template <typename TI, int RAB, int RKV>
 __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
+  constexpr int kRab = RAB > 0 ? RAB : 1, kRkv = RKV;
+  constexpr int kQ = 2 * kRab + kRkv;
   // per-wave row sums [parity][wave][quantity][column], double-buffered by token
   // parity, then the scalar-decay per-row terms [parity][row]
   extern __shared__ __align__(16) float lds[];
-  auto red = [&](int par, int w, int q, int n) -> float& { return lds[((par * kWv + w) * kQ + q) * 128 + n]; };
-  float* dsum0 = lds + 2 * kWv * kQ * 128;
+  auto red = [&](int par, int w, int q, int n) -> float& { return lds[((par * kWv + w) * kQMax + q) * 128 + n]; };
+  float* dsum0 = lds + 2 * kWv * kQMax * 128;
   auto dsum = [&](int par, int i) -> float& { return dsum0[par * 128 + i]; };
+  float* fin0 = dsum0 + 2 * 128;   // column sums [parity][quantity][column]
+  auto colfin = [&](int par, int q, int n) -> float& { return fin0[(par * kQMax + q) * 128 + n]; };
   const Problem& p = a.p;
   const int dk = p.dk, dv = p.dv, C = p.C, r_ab = p.r_ab, r_kv = p.r_kv;
   const int64_t T = p.T, N = p.N;
@@ -77,24 +85,34 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   const TI* dop = static_cast<const TI*>(a.dout);
   const int nst = kRB * kCB;                                       // register slots per state
   const size_t sstride = static_cast<size_t>(nst) * kBwThreads;   // floats per stored state
-  float* ckpt = a.ws + static_cast<size_t>(bh) * a.ws_head;       // N states, thread-major
+  float* ckpt = a.ws + static_cast<size_t>(bh) * a.ws_head;       // N states
   float* buf = ckpt + static_cast<size_t>(N) * sstride;            // C + 1 states of one chunk
   auto rowi = [&](int r) { return tr + kNTR * r; };
   auto coln = [&](int c) { return tc + kNTC * c; };
   auto rok = [&](int r) { return tr + kNTR * r < dk; };
   auto cok = [&](int c) { return tc + kNTC * c < dv; };
-  // thread-major storage of one state: slot (r, c) of thread tid at (r * kCB + c) * 512 + tid
+  // storage of one state: the 32 register slots of thread tid contiguous at
+  // tid * 32 (16-byte pieces with immediate offsets from one address)
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
   auto st_state = [&](float* base, const float (&S)[kRB][kCB]) {
+    f4* d = reinterpret_cast<f4*>(base + static_cast<size_t>(tid) * nst);
 #pragma unroll
     for (int r = 0; r < kRB; ++r)
 #pragma unroll
-      for (int c = 0; c < kCB; ++c) base[(r * kCB + c) * kBwThreads + tid] = S[r][c];
+      for (int c = 0; c < kCB; c += 4) d[(r * kCB + c) / 4] = f4{S[r][c], S[r][c + 1], S[r][c + 2], S[r][c + 3]};
   };
   auto ld_state = [&](const float* base, float (&S)[kRB][kCB]) {
+    const f4* d = reinterpret_cast<const f4*>(base + static_cast<size_t>(tid) * nst);
 #pragma unroll
     for (int r = 0; r < kRB; ++r)
 #pragma unroll
-      for (int c = 0; c < kCB; ++c) S[r][c] = base[(r * kCB + c) * kBwThreads + tid];
+      for (int c = 0; c < kCB; c += 4) {
+        const f4 v = d[(r * kCB + c) / 4];
+        S[r][c] = v[0];
+        S[r][c + 1] = v[1];
+        S[r][c + 2] = v[2];
+        S[r][c + 3] = v[3];
+      }
   };
   // sum over the 16 column groups of a row group (lanes differing in bits 0..3)
   auto rowsum = [&](float v) {
@@ -130,7 +148,8 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   };
   // Sums over rows of this thread's columns, for nq quantities whose per-thread
   // partials are in part[q][c]: inside the wave (lane bits 4, 5), then across
-  // the waves through LDS.  One barrier.
+  // the waves through LDS: each column sum is formed once from the eight wave
+  // partials and read back by the threads of that column.  Two barriers.
   auto colsum = [&](float (&part)[kQ][kCB], int nq, int par) {
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
@@ -140,23 +159,23 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
         float v = part[q][c];
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
-        part[q][c] = v;
         if ((lane >> 4) == 0 && cok(c)) red(par, wave, q, coln(c)) = v;
       }
+    }
+    __syncthreads();
+    for (int e = tid; e < nq * dv; e += kBwThreads) {
+      const int q = e / dv, n = e % dv;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWv; ++w) v += red(par, w, q, n);
+      colfin(par, q, n) = v;
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       if (q >= nq) break;
 #pragma unroll
-      for (int c = 0; c < kCB; ++c) {
-        float v = 0.f;
-        if (cok(c)) {
-#pragma unroll
-          for (int w = 0; w < kWv; ++w) v += red(par, w, q, coln(c));
-        }
-        part[q][c] = v;
-      }
+      for (int c = 0; c < kCB; ++c) part[q][c] = cok(c) ? colfin(par, q, coln(c)) : 0.f;
     }
   };
   // One forward token: S <- D S - A (B^T S) + K V^T.
@@ -341,13 +360,34 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
 }  // namespace
 
 bool backward_supported(const Problem& p) {
-  return p.dk <= kNTR * kRB && p.dv <= kNTC * kCB && p.r_ab <= kRab && p.r_kv <= kRkv;
+  return p.dk <= kNTR * kRB && p.dv <= kNTC * kCB && p.r_ab <= kRabMax && p.r_kv <= kRkvMax;
 }
 
 size_t backward_workspace_bytes(const Problem& p) {
   const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored state
   return static_cast<size_t>(p.BH) * (static_cast<size_t>(p.N) + p.C + 1) * st * sizeof(float);
 }
+
+namespace {
+
+template <typename TI, int RAB, int RKV>
+hipError_t launch_bw_t(const Problem& p, const BwArgs& a, size_t lds, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(backward_kernel<TI, RAB, RKV>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((backward_kernel<TI, RAB, RKV>), dim3(static_cast<unsigned>(p.BH)), dim3(kBwThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+// The smallest instantiation whose operand arrays cover the ranks.
+template <int RAB>
+hipError_t launch_bw(const Problem& p, const BwArgs& a, size_t lds, hipStream_t s) {
+  if (p.bf16)
+    return p.r_kv <= 1 ? launch_bw_t<bf16_raw, RAB, 1>(p, a, lds, s) : launch_bw_t<bf16_raw, RAB, 2>(p, a, lds, s);
+  return p.r_kv <= 1 ? launch_bw_t<float, RAB, 1>(p, a, lds, s) : launch_bw_t<float, RAB, 2>(p, a, lds, s);
+}
+
+}  // namespace
 
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                            const void* A, const void* B, const void* dout, const float* dfinal, const float* S0,
@@ -358,16 +398,11 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;
   BwArgs a{p, q, k, v, ld, A, B, dout, dfinal, S0, dq, dK, dV, dld, dA, dB, dS0,
            static_cast<float*>(workspace), (static_cast<size_t>(p.N) + p.C + 1) * st};
-  const size_t lds = (static_cast<size_t>(2) * kWv * kQ * 128 + 2 * 128) * sizeof(float);
-  const void* fn = p.bf16 ? reinterpret_cast<const void*>(backward_kernel<bf16_raw>)
-                          : reinterpret_cast<const void*>(backward_kernel<float>);
-  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  if (p.bf16)
-    hipLaunchKernelGGL(backward_kernel<bf16_raw>, dim3(static_cast<unsigned>(p.BH)), dim3(kBwThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(backward_kernel<float>, dim3(static_cast<unsigned>(p.BH)), dim3(kBwThreads), lds, s, a);
-  return hipGetLastError();
+  const size_t lds = (static_cast<size_t>(2) * kWv * kQMax * 128 + 2 * 128 + 2 * kQMax * 128) * sizeof(float);
+  if (p.r_ab == 0) return launch_bw<0>(p, a, lds, s);
+  if (p.r_ab == 1) return launch_bw<1>(p, a, lds, s);
+  if (p.r_ab == 2) return launch_bw<2>(p, a, lds, s);
+  return launch_bw<4>(p, a, lds, s);
 }
 
 }  // namespace lattn
