@@ -34,6 +34,10 @@ constexpr int kRB = 4, kCB = 8;          // rows / columns per thread: d_k, d_v 
 constexpr int kRabMax = 4, kRkvMax = 2;  // rank limits of this kernel
 constexpr int kQMax = 2 * kRabMax + kRkvMax;   // LDS stride: column sums per token
 constexpr int kWv = kBwThreads / 64;
+constexpr int kTokGroup = 8;             // tokens whose operands are staged in LDS at once
+
+// floats of one staged token's operands for ranks (RAB, RKV)
+constexpr int tok_ops(int rab, int rkv) { return 128 * (3 + 2 * (rab > 0 ? rab : 1) + rkv) + 128 * rkv; }
 
 struct BwArgs {
   Problem p;
@@ -71,6 +75,12 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   auto dsum = [&](int par, int i) -> float& { return dsum0[par * 128 + i]; };
   float* fin0 = dsum0 + 2 * 128;   // column sums [parity][quantity][column]
   auto colfin = [&](int par, int q, int n) -> float& { return fin0[(par * kQMax + q) * 128 + n]; };
+  // operands of a group of up to kTokGroup tokens, staged by all threads with
+  // coalesced loads: per token exp(log_decay), A, B, K, q (rows), V, dout (columns)
+  constexpr int oLam = 0, oA = 128, oB = oA + 128 * kRab, oK = oB + 128 * kRab, oQ = oK + 128 * kRkv,
+                oV = oQ + 128, oDo = oV + 128 * kRkv, kOps = oDo + 128;
+  float* tokb = fin0 + 2 * kQMax * 128;
+  auto tk = [&](int u, int off) -> float& { return tokb[u * kOps + off]; };
   const Problem& p = a.p;
   const int dk = p.dk, dv = p.dv, C = p.C, r_ab = p.r_ab, r_kv = p.r_kv;
   const int64_t T = p.T, N = p.N;
@@ -120,30 +130,54 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
     for (int s = 1; s < kNTC; s <<= 1) v += __shfl_xor(v, s, 64);
     return v;
   };
-  // Per-token operands of this thread's rows and columns.
+  // Stage tokens t0 .. t0 + cnt - 1 (cnt <= kTokGroup); callers put a barrier
+  // before (the previous group has been read) and after.
+  auto stage = [&](int64_t t0, int cnt) {
+    const int64_t tok0 = bh * T + t0;
+    for (int e = tid; e < cnt * dk; e += kBwThreads) {
+      const int u = e / dk, i = e % dk;
+      tk(u, oLam + i) = expf(p.scalar ? a.ld[tok0 + u] : a.ld[(tok0 + u) * dk + i]);
+      tk(u, oQ + i) = Elem<TI>::load(qp, static_cast<size_t>(tok0 + u) * dk + i);
+    }
+    for (int e = tid; e < cnt * r_ab * dk; e += kBwThreads) {
+      const int u = e / (r_ab * dk), x = (e / dk) % r_ab, i = e % dk;
+      tk(u, oA + 128 * x + i) = Elem<TI>::load(Ap, static_cast<size_t>(tok0) * r_ab * dk + e);
+      tk(u, oB + 128 * x + i) = Elem<TI>::load(Bp, static_cast<size_t>(tok0) * r_ab * dk + e);
+    }
+    for (int e = tid; e < cnt * r_kv * dk; e += kBwThreads) {
+      const int u = e / (r_kv * dk), x = (e / dk) % r_kv, i = e % dk;
+      tk(u, oK + 128 * x + i) = Elem<TI>::load(Kp, static_cast<size_t>(tok0) * r_kv * dk + e);
+    }
+    for (int e = tid; e < cnt * r_kv * dv; e += kBwThreads) {
+      const int u = e / (r_kv * dv), x = (e / dv) % r_kv, n = e % dv;
+      tk(u, oV + 128 * x + n) = Elem<TI>::load(Vp, static_cast<size_t>(tok0) * r_kv * dv + e);
+    }
+    for (int e = tid; e < cnt * dv; e += kBwThreads) {
+      const int u = e / dv, n = e % dv;
+      tk(u, oDo + n) = Elem<TI>::load(dop, static_cast<size_t>(tok0 + u) * dv + n);
+    }
+  };
+  // Per-token operands of this thread's rows and columns, from staged slot u.
   float lam[kRB], Av[kRab][kRB], Bv[kRab][kRB], Kv[kRkv][kRB], Vv[kRkv][kCB];
-  auto load_tok = [&](int64_t t) {
-    const int64_t tok = bh * T + t;
+  auto load_tok = [&](int u) {
 #pragma unroll
     for (int r = 0; r < kRB; ++r) {
       const int i = rok(r) ? rowi(r) : 0;
-      lam[r] = expf(p.scalar ? a.ld[tok] : a.ld[tok * dk + i]);
+      lam[r] = tk(u, oLam + i);
 #pragma unroll
       for (int x = 0; x < kRab; ++x) {
         const bool ok = x < r_ab && rok(r);
-        Av[x][r] = ok ? Elem<TI>::load(Ap, (static_cast<size_t>(tok) * r_ab + x) * dk + i) : 0.f;
-        Bv[x][r] = ok ? Elem<TI>::load(Bp, (static_cast<size_t>(tok) * r_ab + x) * dk + i) : 0.f;
+        Av[x][r] = ok ? tk(u, oA + 128 * x + i) : 0.f;
+        Bv[x][r] = ok ? tk(u, oB + 128 * x + i) : 0.f;
       }
 #pragma unroll
-      for (int x = 0; x < kRkv; ++x)
-        Kv[x][r] = (x < r_kv && rok(r)) ? Elem<TI>::load(Kp, (static_cast<size_t>(tok) * r_kv + x) * dk + i) : 0.f;
+      for (int x = 0; x < kRkv; ++x) Kv[x][r] = (x < r_kv && rok(r)) ? tk(u, oK + 128 * x + i) : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < kCB; ++c) {
       const int n = cok(c) ? coln(c) : 0;
 #pragma unroll
-      for (int x = 0; x < kRkv; ++x)
-        Vv[x][c] = (x < r_kv && cok(c)) ? Elem<TI>::load(Vp, (static_cast<size_t>(tok) * r_kv + x) * dv + n) : 0.f;
+      for (int x = 0; x < kRkv; ++x) Vv[x][c] = (x < r_kv && cok(c)) ? tk(u, oV + 128 * x + n) : 0.f;
     }
   };
   // Sums over rows of this thread's columns, for nq quantities whose per-thread
@@ -215,10 +249,16 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   for (int64_t j = 0; j < N; ++j) {
     st_state(ckpt + j * sstride, S);
     const int64_t t1 = (j + 1) * C < T ? (j + 1) * C : T;
-    for (int64_t t = j * C; t < t1; ++t) {
-      load_tok(t);
-      fwd_step(S, par);
-      par ^= 1;
+    for (int64_t tg = j * C; tg < t1; tg += kTokGroup) {
+      const int cnt = static_cast<int>(t1 - tg < kTokGroup ? t1 - tg : kTokGroup);
+      __syncthreads();
+      stage(tg, cnt);
+      __syncthreads();
+      for (int u = 0; u < cnt; ++u) {
+        load_tok(u);
+        fwd_step(S, par);
+        par ^= 1;
+      }
     }
   }
 #pragma unroll
@@ -232,22 +272,36 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
     const int64_t t0 = j * C, t1 = (j + 1) * C < T ? (j + 1) * C : T;
     ld_state(ckpt + j * sstride, S);
     st_state(buf, S);
-    for (int64_t t = t0; t < t1; ++t) {
-      load_tok(t);
-      fwd_step(S, par);
-      par ^= 1;
-      st_state(buf + (t - t0 + 1) * sstride, S);
+    for (int64_t tg = t0; tg < t1; tg += kTokGroup) {
+      const int cnt = static_cast<int>(t1 - tg < kTokGroup ? t1 - tg : kTokGroup);
+      __syncthreads();
+      stage(tg, cnt);
+      __syncthreads();
+      for (int u = 0; u < cnt; ++u) {
+        load_tok(u);
+        fwd_step(S, par);
+        par ^= 1;
+        st_state(buf + (tg + u - t0 + 1) * sstride, S);
+      }
     }
-    // S holds S_{t1-1}
-    for (int64_t t = t1 - 1; t >= t0; --t) {
+    // S holds S_{t1-1}; groups of tokens from the end of the chunk
+    for (int64_t th = t1; th > t0;) {
+      const int64_t tl = th - kTokGroup > t0 ? th - kTokGroup : t0;
+      const int cnt = static_cast<int>(th - tl);
+      __syncthreads();
+      stage(tl, cnt);
+      __syncthreads();
+      th = tl;
+      for (int u = cnt - 1; u >= 0; --u) {
+      const int64_t t = tl + u;
       const int64_t tok = bh * T + t;
-      load_tok(t);
+      load_tok(u);
       ld_state(buf + (t - t0) * sstride, Sp);   // S_{t-1}
       float qv[kRB], dov[kCB];
 #pragma unroll
-      for (int r = 0; r < kRB; ++r) qv[r] = rok(r) ? Elem<TI>::load(qp, static_cast<size_t>(tok) * dk + rowi(r)) : 0.f;
+      for (int r = 0; r < kRB; ++r) qv[r] = rok(r) ? tk(u, oQ + rowi(r)) : 0.f;
 #pragma unroll
-      for (int c = 0; c < kCB; ++c) dov[c] = cok(c) ? Elem<TI>::load(dop, static_cast<size_t>(tok) * dv + coln(c)) : 0.f;
+      for (int c = 0; c < kCB; ++c) dov[c] = cok(c) ? tk(u, oDo + coln(c)) : 0.f;
       // G += q do^T
 #pragma unroll
       for (int r = 0; r < kRB; ++r)
@@ -348,6 +402,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
 #pragma unroll
         for (int c = 0; c < kCB; ++c) S[r][c] = Sp[r][c];
       par ^= 1;
+      }
     }
   }
 #pragma unroll
@@ -371,7 +426,8 @@ size_t backward_workspace_bytes(const Problem& p) {
 namespace {
 
 template <typename TI, int RAB, int RKV>
-hipError_t launch_bw_t(const Problem& p, const BwArgs& a, size_t lds, hipStream_t s) {
+hipError_t launch_bw_t(const Problem& p, const BwArgs& a, size_t lds_base, hipStream_t s) {
+  const size_t lds = lds_base + static_cast<size_t>(kTokGroup) * tok_ops(RAB, RKV) * sizeof(float);
   const void* fn = reinterpret_cast<const void*>(backward_kernel<TI, RAB, RKV>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
