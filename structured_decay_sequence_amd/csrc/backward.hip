@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
       }
   };
 
-  float S[kRB][kCB], Sp[kRB][kCB], G[kRB][kCB];
+  float S[kRB][kCB], Sp[kRB][kCB], Sn[kRB][kCB], G[kRB][kCB];
   // pass 1: the state entering every chunk
 #pragma unroll
   for (int r = 0; r < kRB; ++r)
@@ -296,7 +296,16 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
       const int64_t t = tl + u;
       const int64_t tok = bh * T + t;
       load_tok(u);
-      ld_state(buf + (t - t0) * sstride, Sp);   // S_{t-1}
+      // S_{t-1}: loaded during the previous step (the first token of a chunk's
+      // walk loads it here)
+      if (t == t1 - 1) {
+        ld_state(buf + (t - t0) * sstride, Sn);
+      }
+#pragma unroll
+      for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int c = 0; c < kCB; ++c) Sp[r][c] = Sn[r][c];
+      if (t > t0) ld_state(buf + (t - 1 - t0) * sstride, Sn);   // S_{t-2}, for the next step
       float qv[kRB], dov[kCB];
 #pragma unroll
       for (int r = 0; r < kRB; ++r) qv[r] = rok(r) ? tk(u, oQ + rowi(r)) : 0.f;
