@@ -317,9 +317,11 @@ def loglinear_leg(torch, lattn, dev, steps, warmup):
 def backward_leg(spec, raw, inputs, torch, lattn, dev):
     """lattn_chunk_bwd on the benchmark workload (same inputs as the forward,
     seeded output cotangents and a final-state cotangent), one timed call after
-    one warm-up, HIP events on its stream.  flops: the token-serial reverse
-    recurrence's multiply-adds (the forward recompute twice, the backward's
-    state products), priced against the fp32 vector peak it runs on."""
+    one warm-up, HIP events on its stream.  flops: the multiply-adds of the
+    two chunk-boundary scans (states forward, cotangents in reverse) and of the
+    chunk-parallel token walks (the forward recompute, then the reverse
+    recurrence's state products), priced against the fp32 vector peak they
+    run on; the chunk operators' prepare is not counted."""
     q, K, V, ld, A, B = inputs
     td = q.dtype
     rng = np.random.default_rng(1)
@@ -338,10 +340,12 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
     dk, dv, ra, rk = spec.dk, spec.dv, spec.r_ab, spec.r_kv
     fwd_mac = dk * dv * (2 * ra + rk + 1)                    # B^T S, D S - A u + K V^T
     bwd_mac = dk * dv * (1 + 1 + 1 + 3 * ra + 2 * rk + 1 + 2 * ra + 1)
-    flops = 2.0 * spec.B * spec.H * spec.T * (2 * fwd_mac + bwd_mac)
+    n_chunks = -(-spec.T // spec.chunk)
+    bound_mac = n_chunks * dk * dv * ((dk + spec.chunk * rk) + (dk + spec.chunk))
+    flops = 2.0 * spec.B * spec.H * (spec.T * (fwd_mac + bwd_mac) + bound_mac)
     return {
         "entry": "lattn_chunk_bwd",
-        "kind": "token-serial reverse recurrence with chunk checkpoints",
+        "kind": "chunk-boundary scans over the chunk operators, then chunk-parallel token walks",
         "ms_per_step": round(ms, 3),
         "value": round(spec.B * spec.T / (ms / 1e3), 1),
         "unit": "tokens/s",

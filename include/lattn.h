@@ -214,8 +214,11 @@ int lattn_loglinear_levels(int64_t seqlen);
  *   L = sum_t <dout_t, out_t> + <dfinal, final_state>
  * with respect to every input, by the chain rule of the recurrence (the HDLA
  * note, "Key design 3", trains through it; the pages give no backward
- * formulas).  Token-serial in reverse, with the state stored at every chunk
- * start and each chunk's states recomputed from there.
+ * formulas).  The state entering and the cotangent leaving every chunk come
+ * from two chunk-level scans over the forward's chunk operators; each chunk's
+ * tokens are then walked in reverse, all chunks in parallel.  As for
+ * lattn_chunk_fwd, every chunk's cumulative -log-decay must stay within
+ * LATTN_MAX_CHUNK_LOG_DECAY (lattn_check_decay_range).
  * Inputs as lattn_chunk_fwd (initial_state NULL = zero), plus
  *   dout [B,H,T,d_v] in dims->dtype;  dfinal [B,H,d_k,d_v] fp32 or NULL (zero).
  * Outputs, fp32, each in its input's layout: dq [B,H,T,d_k]; dk [B,H,T,r_kv,d_k];

@@ -12,16 +12,23 @@
 // (d_k x d_k) is never formed: dA_t = -G (S_{t-1}^T B_t), dB_t = -S_{t-1} (G^T A_t),
 // and diag(dP_t) is the row-wise dot of G and S_{t-1}.
 //
-// One workgroup (512 threads, a 32 x 16 grid) per (batch, head), token by
-// token.  Thread (tr, tc) holds rows tr, tr+32, .. and columns tc, tc+16, ..
-// of S_t, S_{t-1} and G in registers.  Sums over columns are shuffles inside
-// a row group of 16 lanes; sums over rows are shuffles inside the wave, then
-// an LDS exchange between the eight waves (each sum formed once, then read
-// back by the threads of its column).  A first pass stores the state at
-// every chunk start; then, chunk by chunk from the end, the chunk's states
-// are recomputed into a workspace buffer (each thread reads back only the
-// values it wrote, stored contiguously per thread) and the chunk's tokens are
-// walked in reverse.
+// Chunk-parallel schedule.  The forward's chunk operators
+// M_j = [[Acal_j, Z_j], [Qbar_j, R_j]] (row-major fp32, from the prepare kernels)
+// give every chunk boundary without a token walk:
+//   states      S_j     = Acal_j S_{j-1} + Z_j V_j             (j = 0 .. N-1)
+//   cotangents  dS_{j-1} = Acal_j^T dS_j + Qbar_j^T dO_j        (j = N-1 .. 0)
+// one scan each (bw_bound_kernel, fp32 FMAs, one workgroup per (batch, head,
+// 32 value columns); the d_v columns of the state are independent).  With the
+// state entering chunk j and the cotangent leaving it known, the token-level
+// walks of all chunks are independent: backward_kernel takes (batch, head,
+// chunk) jobs.  Per job, one 512-thread workgroup (a 32 x 16 grid; thread
+// (tr, tc) holds rows tr, tr+32, .. and columns tc, tc+16, .. of S_t, S_{t-1}
+// and G in registers) recomputes the chunk's states into its workspace buffer
+// (each thread reads back only the values it wrote, stored contiguously per
+// thread) and walks the chunk's tokens in reverse.  Sums over columns are
+// shuffles inside a row group of 16 lanes; sums over rows are shuffles inside
+// the wave, then an LDS exchange between the eight waves (each sum formed
+// once, then read back by the threads of its column).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,6 +42,16 @@ constexpr int kRabMax = 4, kRkvMax = 2;  // rank limits of this kernel
 constexpr int kQMax = 2 * kRabMax + kRkvMax;   // LDS stride: column sums per token
 constexpr int kWv = kBwThreads / 64;
 constexpr int kTokGroup = 8;             // tokens whose operands are staged in LDS at once
+
+// Workgroup barrier that orders LDS only.  The waves exchange data through
+// LDS alone (the chunk's recomputed states in global memory are read back by
+// the thread that wrote them), so a barrier need not wait for the global
+// loads in flight (the next step's state) or for the gradient stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // floats of one staged token's operands for ranks (RAB, RKV)
 constexpr int tok_ops(int rab, int rkv) { return 128 * (3 + 2 * (rab > 0 ? rab : 1) + rkv) + 128 * rkv; }
@@ -57,9 +74,126 @@ struct BwArgs {
   float* dA;
   float* dB;
   float* dS0;
-  float* ws;
-  size_t ws_head;   // floats of workspace per (batch, head)
+  const float* ckpt;   // [BH, N, dk, dv]: the state entering each chunk
+  const float* gend;   // [BH, N, dk, dv]: the cotangent of the state leaving each chunk
+  float* bufs;         // per workgroup: C + 1 states of one chunk
 };
+
+// Chunk-boundary scans over the row-major fp32 chunk operators M_j
+// ((dk + C) x (dk + C r_kv)).  Forward (REV false): X <- Acal_j X + Z_j V_j,
+// storing the X entering chunk j.  Reverse: X <- Acal_j^T X + Qbar_j^T dO_j
+// from j = N-1 down, storing the X leaving chunk j.  Padding tokens of a
+// ragged last chunk are left out of the sums.
+constexpr int kBdThreads = 256, kBdBN = 32;   // 32 row blocks of 4 x 8 column blocks of 4
+struct BdArgs {
+  Problem p;
+  const float* M;
+  const void* Y;      // V [BH, T, r_kv, dv] or dO [BH, T, dv]
+  const float* init;  // [BH, dk, dv] or null (zero)
+  float* out;         // [BH, N, dk, dv]
+};
+
+template <typename TI, bool REV>
+__global__ __launch_bounds__(kBdThreads) void bw_bound_kernel(BdArgs a) {
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
+  constexpr int BN = kBdBN;
+  __shared__ __align__(16) float xs[(128 + 256) * BN];   // state rows, then the chunk's input rows
+  const Problem& p = a.p;
+  const int dk = p.dk, dv = p.dv, C = p.C, ncol = p.mcols(), yw = REV ? 1 : p.r_kv;
+  const int64_t T = p.T, N = p.N;
+  const int nsplit = (dv + BN - 1) / BN;
+  const int64_t bh = blockIdx.x / nsplit;
+  const int n0 = static_cast<int>(blockIdx.x % nsplit) * BN;
+  const int tid = threadIdx.x, ni = tid % (BN / 4), ri = tid / (BN / 4);
+  const bool rowok = 4 * ri < dk;   // d_k is a multiple of 16
+  const TI* yp = static_cast<const TI*>(a.Y);
+  float acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int n = n0 + 4 * ni + c;
+      acc[r][c] = (a.init && rowok && n < dv) ? a.init[(bh * dk + 4 * ri + r) * dv + n] : 0.f;
+    }
+  for (int64_t st = 0; st < N; ++st) {
+    const int64_t j = REV ? N - 1 - st : st;
+    const int64_t t0 = j * C;
+    const int n = static_cast<int>(T - t0 < C ? T - t0 : C);
+    const int nin = n * yw;
+    float* o = a.out + static_cast<size_t>(bh * N + j) * dk * dv;
+    if (rowok) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int col = n0 + 4 * ni + c;
+          if (col < dv) o[static_cast<size_t>(4 * ri + r) * dv + col] = acc[r][c];
+        }
+    }
+    lds_barrier();   // the previous step's reads of xs are done
+    if (rowok) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<f4*>(&xs[(4 * ri + r) * BN + 4 * ni]) = f4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+    }
+    const int64_t y0 = (bh * T + t0) * yw;
+    for (int e = tid; e < nin * BN; e += kBdThreads) {
+      const int m = e / BN, c = e % BN;
+      xs[(dk + m) * BN + c] = n0 + c < dv ? Elem<TI>::load(yp, static_cast<size_t>(y0 + m) * dv + n0 + c) : 0.f;
+    }
+    lds_barrier();
+    if (rowok) {
+      const float* Mj = a.M + static_cast<size_t>(bh * N + j) * p.mrows() * ncol;
+      const int KE = dk + nin;
+      float nx[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nx[r][c] = 0.f;
+      if (!REV) {
+        // (Acal_j | Z_j) row i, column m: Mj[i * ncol + m]
+        int m = 0;
+        for (; m + 4 <= KE; m += 4) {
+          f4 w[4], x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = *reinterpret_cast<const f4*>(Mj + static_cast<size_t>(4 * ri + r) * ncol + m);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = *reinterpret_cast<const f4*>(&xs[(m + k) * BN + 4 * ni]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) nx[r][c] += w[r][k] * x[k][c];
+        }
+        for (; m < KE; ++m) {
+          const f4 x = *reinterpret_cast<const f4*>(&xs[m * BN + 4 * ni]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w = Mj[static_cast<size_t>(4 * ri + r) * ncol + m];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) nx[r][c] += w * x[c];
+          }
+        }
+      } else {
+        // (Acal_j^T | Qbar_j^T) row i, column m: Mj[m * ncol + i]
+#pragma unroll 4
+        for (int m = 0; m < KE; ++m) {
+          const f4 w = *reinterpret_cast<const f4*>(Mj + static_cast<size_t>(m) * ncol + 4 * ri);
+          const f4 x = *reinterpret_cast<const f4*>(&xs[m * BN + 4 * ni]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) nx[r][c] += w[r] * x[c];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = nx[r][c];
+    }
+  }
+}
 
 // RAB, RKV: the ranks the per-thread operand arrays are sized for (r_ab <= RAB,
 // r_kv <= RKV); kQ column sums per token: A^T G, B^T S_{t-1}, K^T G.
@@ -84,7 +218,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   const Problem& p = a.p;
   const int dk = p.dk, dv = p.dv, C = p.C, r_ab = p.r_ab, r_kv = p.r_kv;
   const int64_t T = p.T, N = p.N;
-  const int64_t bh = blockIdx.x;
+  int64_t bh = 0;   // the job's (batch, head), set per job
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tr = tid / kNTC, tc = tid % kNTC;
   const TI* qp = static_cast<const TI*>(a.q);
@@ -95,8 +229,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   const TI* dop = static_cast<const TI*>(a.dout);
   const int nst = kRB * kCB;                                       // register slots per state
   const size_t sstride = static_cast<size_t>(nst) * kBwThreads;   // floats per stored state
-  float* ckpt = a.ws + static_cast<size_t>(bh) * a.ws_head;       // N states
-  float* buf = ckpt + static_cast<size_t>(N) * sstride;            // C + 1 states of one chunk
+  float* buf = a.bufs + static_cast<size_t>(blockIdx.x) * (C + 1) * sstride;   // C + 1 states of one chunk
   auto rowi = [&](int r) { return tr + kNTR * r; };
   auto coln = [&](int c) { return tc + kNTC * c; };
   auto rok = [&](int r) { return tr + kNTR * r < dk; };
@@ -196,7 +329,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
         if ((lane >> 4) == 0 && cok(c)) red(par, wave, q, coln(c)) = v;
       }
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < nq * dv; e += kBwThreads) {
       const int q = e / dv, n = e % dv;
       float v = 0.f;
@@ -204,7 +337,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
       for (int w = 0; w < kWv; ++w) v += red(par, w, q, n);
       colfin(par, q, n) = v;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       if (q >= nq) break;
@@ -239,44 +372,28 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
   };
 
   float S[kRB][kCB], Sp[kRB][kCB], Sn[kRB][kCB], G[kRB][kCB];
-  // pass 1: the state entering every chunk
-#pragma unroll
-  for (int r = 0; r < kRB; ++r)
-#pragma unroll
-    for (int c = 0; c < kCB; ++c)
-      S[r][c] = (a.S0 && rok(r) && cok(c)) ? a.S0[(bh * dk + rowi(r)) * dv + coln(c)] : 0.f;
   int par = 0;
-  for (int64_t j = 0; j < N; ++j) {
-    st_state(ckpt + j * sstride, S);
-    const int64_t t1 = (j + 1) * C < T ? (j + 1) * C : T;
-    for (int64_t tg = j * C; tg < t1; tg += kTokGroup) {
-      const int cnt = static_cast<int>(t1 - tg < kTokGroup ? t1 - tg : kTokGroup);
-      __syncthreads();
-      stage(tg, cnt);
-      __syncthreads();
-      for (int u = 0; u < cnt; ++u) {
-        load_tok(u);
-        fwd_step(S, par);
-        par ^= 1;
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < kRB; ++r)
-#pragma unroll
-    for (int c = 0; c < kCB; ++c)
-      G[r][c] = (a.dfinal && rok(r) && cok(c)) ? a.dfinal[(bh * dk + rowi(r)) * dv + coln(c)] : 0.f;
-
-  // pass 2: chunks from the end; recompute the chunk's states, then walk back
-  for (int64_t j = N - 1; j >= 0; --j) {
+  for (int64_t job = blockIdx.x; job < p.BH * N; job += gridDim.x) {
+    bh = job / N;
+    const int64_t j = job % N;
     const int64_t t0 = j * C, t1 = (j + 1) * C < T ? (j + 1) * C : T;
-    ld_state(ckpt + j * sstride, S);
+    // the state entering the chunk and the cotangent of the state leaving it
+    const float* sb = a.ckpt + static_cast<size_t>(job) * dk * dv;
+    const float* gb = a.gend + static_cast<size_t>(job) * dk * dv;
+#pragma unroll
+    for (int r = 0; r < kRB; ++r)
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+        const bool ok = rok(r) && cok(c);
+        S[r][c] = ok ? sb[rowi(r) * dv + coln(c)] : 0.f;
+        G[r][c] = ok ? gb[rowi(r) * dv + coln(c)] : 0.f;
+      }
     st_state(buf, S);
     for (int64_t tg = t0; tg < t1; tg += kTokGroup) {
       const int cnt = static_cast<int>(t1 - tg < kTokGroup ? t1 - tg : kTokGroup);
-      __syncthreads();
+      lds_barrier();
       stage(tg, cnt);
-      __syncthreads();
+      lds_barrier();
       for (int u = 0; u < cnt; ++u) {
         load_tok(u);
         fwd_step(S, par);
@@ -284,13 +401,14 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
         st_state(buf + (tg + u - t0 + 1) * sstride, S);
       }
     }
+    __syncthreads();   // once per chunk: the recomputed states are in memory
     // S holds S_{t1-1}; groups of tokens from the end of the chunk
     for (int64_t th = t1; th > t0;) {
       const int64_t tl = th - kTokGroup > t0 ? th - kTokGroup : t0;
       const int cnt = static_cast<int>(th - tl);
-      __syncthreads();
+      lds_barrier();
       stage(tl, cnt);
-      __syncthreads();
+      lds_barrier();
       th = tl;
       for (int u = cnt - 1; u >= 0; --u) {
       const int64_t t = tl + u;
@@ -413,12 +531,14 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
       par ^= 1;
       }
     }
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < kRB; ++r)
+#pragma unroll
+        for (int c = 0; c < kCB; ++c)
+          if (rok(r) && cok(c)) a.dS0[(bh * dk + rowi(r)) * dv + coln(c)] = G[r][c];
+    }
   }
-#pragma unroll
-  for (int r = 0; r < kRB; ++r)
-#pragma unroll
-    for (int c = 0; c < kCB; ++c)
-      if (rok(r) && cok(c)) a.dS0[(bh * dk + rowi(r)) * dv + coln(c)] = G[r][c];
 }
 
 }  // namespace
@@ -427,10 +547,38 @@ bool backward_supported(const Problem& p) {
   return p.dk <= kNTR * kRB && p.dv <= kNTC * kCB && p.r_ab <= kRabMax && p.r_kv <= kRkvMax;
 }
 
-size_t backward_workspace_bytes(const Problem& p) {
-  const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored state
-  return static_cast<size_t>(p.BH) * (static_cast<size_t>(p.N) + p.C + 1) * st * sizeof(float);
+namespace {
+
+constexpr size_t kBwAlign = 256;
+size_t bw_align(size_t x) { return (x + kBwAlign - 1) & ~(kBwAlign - 1); }
+
+// Workgroups of the token walk: one resident per compute unit, each with its
+// own buffer of C + 1 states.
+int64_t bw_walk_groups(const Problem& p) {
+  const int64_t jobs = p.BH * p.N;
+  return jobs < 256 ? jobs : 256;
 }
+
+// Workspace: the chunk operators (and what their prepare needs), the states
+// entering the chunks, the cotangents leaving them, then the walk buffers.
+struct BwLayout {
+  size_t ops, ckpt, gend, bufs, total;
+};
+BwLayout bw_layout(const Problem& p) {
+  BwLayout l{};
+  const size_t states = static_cast<size_t>(p.BH * p.N) * p.dk * p.dv * sizeof(float);
+  const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored walk state
+  l.ops = 0;
+  l.ckpt = bw_align(f32_operators_bytes(p));
+  l.gend = l.ckpt + bw_align(states);
+  l.bufs = l.gend + bw_align(states);
+  l.total = l.bufs + static_cast<size_t>(bw_walk_groups(p)) * (p.C + 1) * st * sizeof(float);
+  return l;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Problem& p) { return bw_layout(p).total; }
 
 namespace {
 
@@ -440,7 +588,8 @@ hipError_t launch_bw_t(const Problem& p, const BwArgs& a, size_t lds_base, hipSt
   const void* fn = reinterpret_cast<const void*>(backward_kernel<TI, RAB, RKV>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((backward_kernel<TI, RAB, RKV>), dim3(static_cast<unsigned>(p.BH)), dim3(kBwThreads), lds, s, a);
+  hipLaunchKernelGGL((backward_kernel<TI, RAB, RKV>), dim3(static_cast<unsigned>(bw_walk_groups(p))),
+                     dim3(kBwThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -452,6 +601,18 @@ hipError_t launch_bw(const Problem& p, const BwArgs& a, size_t lds, hipStream_t 
   return p.r_kv <= 1 ? launch_bw_t<float, RAB, 1>(p, a, lds, s) : launch_bw_t<float, RAB, 2>(p, a, lds, s);
 }
 
+template <typename TI>
+hipError_t launch_boundary_scans(const Problem& p, const float* M, const void* v, const void* dout, const float* S0,
+                         const float* dfinal, float* ckpt, float* gend, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(p.BH * ((p.dv + kBdBN - 1) / kBdBN));
+  hipLaunchKernelGGL((bw_bound_kernel<TI, false>), dim3(grid), dim3(kBdThreads), 0, s, BdArgs{p, M, v, S0, ckpt});
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bw_bound_kernel<TI, true>), dim3(grid), dim3(kBdThreads), 0, s,
+                     BdArgs{p, M, dout, dfinal, gend});
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_backward(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
@@ -460,9 +621,18 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            void* workspace, hipStream_t s) {
   if (p.BH == 0) return hipSuccess;
   if (!backward_supported(p)) return hipErrorInvalidValue;
-  const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;
-  BwArgs a{p, q, k, v, ld, A, B, dout, dfinal, S0, dq, dK, dV, dld, dA, dB, dS0,
-           static_cast<float*>(workspace), (static_cast<size_t>(p.N) + p.C + 1) * st};
+  const BwLayout l = bw_layout(p);
+  char* ws = static_cast<char*>(workspace);
+  float* ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+  float* gend = reinterpret_cast<float*>(ws + l.gend);
+  const float* M = nullptr;
+  hipError_t e = f32_operators(p, q, k, ld, A, B, ws + l.ops, &M, s);
+  if (e != hipSuccess) return e;
+  e = p.bf16 ? launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, s)
+             : launch_boundary_scans<float>(p, M, v, dout, S0, dfinal, ckpt, gend, s);
+  if (e != hipSuccess) return e;
+  BwArgs a{p, q, k, v, ld, A, B, dout, dfinal, S0, dq, dK, dV, dld, dA, dB, dS0, ckpt, gend,
+           reinterpret_cast<float*>(ws + l.bufs)};
   const size_t lds = (static_cast<size_t>(2) * kWv * kQMax * 128 + 2 * 128 + 2 * kQMax * 128) * sizeof(float);
   if (p.r_ab == 0) return launch_bw<0>(p, a, lds, s);
   if (p.r_ab == 1) return launch_bw<1>(p, a, lds, s);

@@ -25,6 +25,10 @@ CASES = [
     (1, 1, 130, 128, 128, 2, 1, 64, "fp32", "channel", True),
     (1, 2, 70, 64, 64, 2, 1, 32, "bf16", "channel", True),
     (1, 1, 1, 32, 32, 1, 1, 16, "fp32", "channel", True),
+    # more (batch, head, chunk) jobs than resident workgroups (276 > 256)
+    (1, 4, 1100, 32, 32, 2, 1, 16, "fp32", "channel", True),
+    # bf16 operators from the MFMA prepare, 65 chunks per head with a 4-token tail
+    (2, 3, 4100, 64, 64, 1, 1, 64, "bf16", "scalar", True),
 ]
 
 
