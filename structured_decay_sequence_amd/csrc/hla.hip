@@ -90,9 +90,10 @@ struct HlaArgs {
 constexpr int kHlaThreads = 512;   // eight waves
 constexpr int kHlaTiles = 8;       // tiles of R and of O per wave: (C/16)(d/16) <= 64
 
-// One workgroup per (batch*head, query chunk c).  R (C x d_k, fp32) lives in
-// LDS; wave w owns O tiles w, w+8, ... (in registers for the whole walk) and
-// the same R tiles, whose new values are written back after a barrier.
+// One workgroup per (batch*head, query chunk c), longest walks first.  R
+// (C x d_k, fp32) lives in LDS; wave w owns O tiles w, w+8, ... (in registers
+// for the whole walk) and the same R tiles, whose new values are written back
+// after a barrier.
 template <typename TI>
 __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
   extern __shared__ __align__(16) float Rs[];
@@ -100,9 +101,11 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
   const int dk = p.dk, dv = p.dv, C = p.C, ncol = p.mcols();
   const int N = static_cast<int>(p.N);
   const int LDR = dk + 4;
-  const int64_t job = blockIdx.x;
-  const int64_t bh = job / N;
-  const int c = static_cast<int>(job % N);
+  // Query chunk c walks c history chunks: the workgroups are dispatched
+  // longest walk first (c descending), so short walks fill in at the end.
+  const int c = N - 1 - static_cast<int>(blockIdx.x / p.BH);
+  const int64_t bh = blockIdx.x % p.BH;
+  const int64_t job = bh * N + c;
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const int n = static_cast<int>(p.T - t0 < C ? p.T - t0 : C);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -131,43 +134,69 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
         O[u][e] = a.OI[(static_cast<size_t>(job) * C + rt * 16 + 4 * lg + e) * dv + ct * 16 + lr];
     }
   }
-  // gate of chunk j for row t of this chunk (rows past its end: 0)
-  auto gate = [&](int t, int j) {
-    float w = t < n ? gb[static_cast<size_t>(t) * N + j] : 0.f;
-    return w < theta ? 0.f : w;
-  };
+  float* gs = Rs + C * LDR;   // gates of the current history chunk per row (below theta, or past the end: 0)
   __syncthreads();
 
+  // Per history chunk, wave w runs up to 2 kHlaTiles tile products: task 2u is
+  // its O tile w + 8u (B_j^T fragments), task 2u + 1 its R tile w + 8u
+  // (Acal_j^T fragments).  The next task's fragments are loaded while the
+  // current task's MFMAs run.
+  auto task = [&](const float* ATj, const float* BTj, int k, int& rt, int& ct, const float*& bp) {
+    const int idx = wave + 8 * (k >> 1);
+    if ((k & 1) == 0) {
+      if (idx >= nO) return false;
+      rt = idx / nctv;
+      ct = idx % nctv;
+      bp = BTj + static_cast<size_t>(ct * 16 + lr) * dk + 4 * lg;
+    } else {
+      if (idx >= nR) return false;
+      rt = idx / nctk;
+      ct = idx % nctk;
+      bp = ATj + static_cast<size_t>(ct * 16 + lr) * dk + 4 * lg;
+    }
+    return true;
+  };
   for (int j = c - 1; j >= 0; --j) {
     int act = 0;
-    for (int t = tid; t < n; t += kHlaThreads) act |= gb[static_cast<size_t>(t) * N + j] >= theta;
+    for (int t = tid; t < C; t += kHlaThreads) {
+      const float w = t < n ? gb[static_cast<size_t>(t) * N + j] : 0.f;
+      act |= w >= theta;
+      gs[t] = w < theta ? 0.f : w;
+    }
     if (!__syncthreads_or(act)) continue;
     const float* ATj = a.AT + static_cast<size_t>(bh * N + j) * dk * dk;
     const float* BTj = a.BT + static_cast<size_t>(bh * N + j) * dv * dk;
+    f32x4 bf[2][8];
+    auto fetch = [&](int k, f32x4 (&f)[8]) {
+      int rt, ct;
+      const float* bp;
+      if (!task(ATj, BTj, k, rt, ct, bp)) return;
 #pragma unroll
-    for (int u = 0; u < kHlaTiles; ++u) {
-      const int o = wave + 8 * u;
-      if (o < nO) {
-        const int rt = o / nctv, ct = o % nctv;
-        const float* arow = Rs + (rt * 16 + lr) * LDR + 4 * lg;
-        const float* brow = BTj + static_cast<size_t>(ct * 16 + lr) * dk + 4 * lg;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < nctk; ++kb) acc = mfma16(ld4(arow + kb * 16), ld4(brow + kb * 16), acc);
+      for (int kb = 0; kb < 8; ++kb)
+        if (kb < nctk) f[kb] = ld4(bp + kb * 16);
+    };
+    fetch(0, bf[0]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[u][e] += gate(rt * 16 + 4 * lg + e, j) * acc[e];
-      }
-      const int r = wave + 8 * u;
-      if (r < nR) {
-        const int rt = r / nctk, ct = r % nctk;
-        const float* arow = Rs + (rt * 16 + lr) * LDR + 4 * lg;
-        const float* brow = ATj + static_cast<size_t>(ct * 16 + lr) * dk + 4 * lg;
-        f32x4 acc = zero4();
-        for (int kb = 0; kb < nctk; ++kb) acc = mfma16(ld4(arow + kb * 16), ld4(brow + kb * 16), acc);
+    for (int k = 0; k < 2 * kHlaTiles; ++k) {
+      if (k + 1 < 2 * kHlaTiles) fetch(k + 1, bf[(k + 1) & 1]);
+      int rt, ct;
+      const float* bp;
+      if (!task(ATj, BTj, k, rt, ct, bp)) continue;
+      const float* arow = Rs + (rt * 16 + lr) * LDR + 4 * lg;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        if (kb < nctk) acc = mfma16(ld4(arow + kb * 16), bf[k & 1][kb], acc);
+      const int u = k >> 1;
+      if ((k & 1) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[u][e] += gs[rt * 16 + 4 * lg + e] * acc[e];
+      } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = rt * 16 + 4 * lg + e;
           const float old = Rs[t * LDR + ct * 16 + lr];
-          Rn[u][e] = old + gate(t, j) * (acc[e] - old);
+          Rn[u][e] = old + gs[t] * (acc[e] - old);
         }
       }
     }
@@ -238,7 +267,7 @@ hipError_t launch_hla(const Problem& p, const void* q, const void* k, const floa
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   HlaArgs ca{p, M, AT, BT, OI, gates, theta, out};
-  const size_t lds = static_cast<size_t>(p.C) * (p.dk + 4) * sizeof(float);
+  const size_t lds = static_cast<size_t>(p.C) * (p.dk + 4 + 1) * sizeof(float);   // R, then the row gates
   const void* fn = p.bf16 ? reinterpret_cast<const void*>(hla_compose_kernel<bf16_raw>)
                           : reinterpret_cast<const void*>(hla_compose_kernel<float>);
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
