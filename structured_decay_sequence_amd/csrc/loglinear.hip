@@ -98,6 +98,7 @@ struct LlScanArgs {
   int L;
   int c;       // log2(C)
   int nlev;    // inter-chunk levels: bit_length(N - 1)
+  int nbuf;    // copies of each level state: 2 (read one, write the other by chunk parity) or 1
   void* out;
 };
 
@@ -108,7 +109,10 @@ constexpr int kLlKB = 8;      // K slices of the state product: d_k <= 128
 // One workgroup (four waves) per (batch*head, 16-column d_v slice); chunks in
 // order.  Every level's state S^(m) (d_k x 16, fp32) is kept in LDS as S^T.
 // Wave w owns row tiles w, w+4, w+8 of [Acal ; Qbar] and holds their operator
-// fragments in registers for all levels of a chunk.
+// fragments in registers for all levels of a chunk.  With two copies of each
+// state (where they fit in LDS), chunk J reads copy J mod 2 and writes the
+// other, so the levels run back to back with one barrier per chunk; with one
+// copy, each level waits for every wave's reads before its writes.
 template <typename TI>
 __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
   extern __shared__ __align__(16) float ls[];
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  for (int e = tid; e < a.nlev * kLlBV * LDS_; e += 256) ls[e] = 0.f;
+  for (int e = tid; e < a.nbuf * a.nlev * kLlBV * LDS_; e += 256) ls[e] = 0.f;
   __syncthreads();
   TI* op = static_cast<TI*>(a.out);
 
@@ -155,7 +159,9 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
     for (int m = 0; m < a.nlev; ++m) {
       const bool right = (J >> m) & 1;
       const bool reset = !right && (J & ((2LL << m) - 1)) == 0;
-      float* S = ls + m * kLlBV * LDS_;
+      const bool two = a.nbuf == 2;
+      float* S = ls + (m * a.nbuf + (two ? static_cast<int>(J & 1) : 0)) * kLlBV * LDS_;        // read
+      float* Sw = two ? ls + (m * 2 + static_cast<int>((J + 1) & 1)) * kLlBV * LDS_ : S;    // written
       f32x4 acc[kLlQW];
 #pragma unroll
       for (int u = 0; u < kLlQW; ++u) {
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
             if (kb < KB) acc[u] = mfma16(fa[u][kb], ld4(S + lr * LDS_ + kb * 16 + 4 * lg), acc[u]);
         }
       }
-      __syncthreads();   // every product has read S^(m)
+      if (!two) __syncthreads();   // every product has read S^(m)
 #pragma unroll
       for (int u = 0; u < kLlQW; ++u) {
         const int mt = wave + 4 * u;
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[e] += zv[u][e];
           }
-          st4(S + lr * LDS_ + mt * 16 + 4 * lg, s);
+          st4(Sw + lr * LDS_ + mt * 16 + 4 * lg, s);
         } else if (right) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -222,12 +228,16 @@ static int inter_levels(int64_t N) {
   return b;
 }
 
+// LDS of one copy of the level states
 size_t loglinear_scan_lds(const Problem& p) {
   return static_cast<size_t>(inter_levels(p.N)) * kLlBV * (p.dk + 4) * sizeof(float);
 }
+constexpr size_t kLlLdsMax = 150 * 1024;
+// copies of each level state the scan keeps: two where they fit
+int loglinear_scan_bufs(const Problem& p) { return 2 * loglinear_scan_lds(p) <= kLlLdsMax ? 2 : 1; }
 
 bool loglinear_supported(const Problem& p) {
-  return p.dk <= 128 && p.dv <= 128 && p.mrows() <= 16 * 4 * kLlQW && loglinear_scan_lds(p) <= 150 * 1024;
+  return p.dk <= 128 && p.dv <= 128 && p.mrows() <= 16 * 4 * kLlQW && loglinear_scan_lds(p) <= kLlLdsMax;
 }
 
 LlPlan loglinear_plan(const Problem& p) {
@@ -263,8 +273,9 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
   if (e != hipSuccess) return e;
   int c = 0;
   while ((1 << c) < p.C) ++c;
-  LlScanArgs sa{p, M, ZVT, OI, lam, L, c, inter_levels(p.N), out};
-  const size_t lds = loglinear_scan_lds(p);
+  const int nbuf = loglinear_scan_bufs(p);
+  LlScanArgs sa{p, M, ZVT, OI, lam, L, c, inter_levels(p.N), nbuf, out};
+  const size_t lds = loglinear_scan_lds(p) * nbuf;
   const void* fn = p.bf16 ? reinterpret_cast<const void*>(ll_scan_kernel<bf16_raw>)
                           : reinterpret_cast<const void*>(ll_scan_kernel<float>);
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds > 0 ? lds : 16));

@@ -76,6 +76,21 @@ def test_loglinear_chunk_size_invariance():
         assert rel_err(o, outs[0]) <= TOL["fp32"]
 
 
+def test_loglinear_long_sequence_one_and_two_state_copies():
+    """d_k 128 over 8300 tokens.  At C 16 (519 chunks, 10 inter-chunk levels)
+    two copies of the level states would need 169 KB of LDS, so the scan keeps
+    one and orders each level's reads before its writes; at C 64 (130 chunks,
+    8 levels, 135 KB) it keeps two and alternates them by chunk parity.  The
+    outputs must agree."""
+    Bb, H, T, dk, dv = 1, 1, 8300, 128, 16
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 1, 1, "fp32", "channel", seed=8)
+    lam = workloads.loglinear_lambdas(Bb, H, T, seed=8)
+    a, b = _gpu(raw, lam, "fp32", 16), _gpu(raw, lam, "fp32", 64)
+    e = rel_err(b, a)
+    print(f"C 16 vs C 64 over {T} tokens: {e:.2e}", flush=True)
+    assert e <= TOL["fp32"]
+
+
 def test_loglinear_levels_and_rejects():
     assert lattn.loglinear_levels(4096) == ll_oracle.num_levels(4096) == 13
     assert lattn.loglinear_levels(1) == 1 and lattn.loglinear_levels(5) == 4
