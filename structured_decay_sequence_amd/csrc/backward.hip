@@ -53,6 +53,32 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One DPP lane move inside rows of 16 lanes (no LDS traffic): lane i reads
+// the lane that the control word names.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over a row of 16 lanes, left in every lane of the row: swap neighbours
+// (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror each half row
+// (the other quad of the half), mirror the row (the other half).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  return v;
+}
+
+// Sum over the four rows of 16 lanes of a wave, left in every lane: swap odd
+// and even rows (permlane16 swap), then the two halves (permlane32 swap).
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // floats of one staged token's operands for ranks (RAB, RKV)
 constexpr int tok_ops(int rab, int rkv) { return 128 * (3 + 2 * (rab > 0 ? rab : 1) + rkv) + 128 * rkv; }
 
@@ -258,11 +284,8 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
       }
   };
   // sum over the 16 column groups of a row group (lanes differing in bits 0..3)
-  auto rowsum = [&](float v) {
-#pragma unroll
-    for (int s = 1; s < kNTC; s <<= 1) v += __shfl_xor(v, s, 64);
-    return v;
-  };
+  static_assert(kNTC == 16, "row sums are DPP moves inside rows of 16 lanes");
+  auto rowsum = [&](float v) { return row16_sum(v); };
   // Stage tokens t0 .. t0 + cnt - 1 (cnt <= kTokGroup); callers put a barrier
   // before (the previous group has been read) and after.
   auto stage = [&](int64_t t0, int cnt) {
@@ -323,9 +346,7 @@ __global__ __launch_bounds__(kBwThreads) void backward_kernel(BwArgs a) {
       if (q >= nq) break;
 #pragma unroll
       for (int c = 0; c < kCB; ++c) {
-        float v = part[q][c];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        const float v = rows4_sum(part[q][c]);
         if ((lane >> 4) == 0 && cok(c)) red(par, wave, q, coln(c)) = v;
       }
     }
