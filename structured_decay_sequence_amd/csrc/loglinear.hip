@@ -143,11 +143,14 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
 #pragma unroll
     for (int u = 0; u < kLlQW; ++u) {
       const int mt = wave + 4 * u < MT ? wave + 4 * u : MT - 1;
+      // only the fragments the products read: tiles in range, K slices below d_k
 #pragma unroll
       for (int kb = 0; kb < kLlKB; ++kb)
-        fa[u][kb] = ld4(MJ + static_cast<size_t>(mt * 16 + lr) * ncol + (kb < KB ? kb : 0) * 16 + 4 * lg);
+        fa[u][kb] = kb < KB && wave + 4 * u < MT ? ld4(MJ + static_cast<size_t>(mt * 16 + lr) * ncol + kb * 16 + 4 * lg)
+                                                 : zero4();
       zv[u] = zero4();
       oacc[u] = zero4();
+      if (wave + 4 * u >= MT) continue;
       if (mt < dkT) {
         zv[u] = ld4(a.ZVT + (static_cast<size_t>(job) * dv + c0 + lr) * dk + mt * 16 + 4 * lg);
       } else {
