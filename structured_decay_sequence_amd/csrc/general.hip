@@ -402,19 +402,19 @@ __global__ __launch_bounds__(768) void general_scan_kernel(ScanArgs a) {
     // shapes with more values than the register copy holds
     for (int e = tid + kVMAX * nthr; e < nk * kBV; e += nthr) X[(e % kBV) * LDX + dk + e / kBV] = v_at(jj, e);
   };
-  // Operator fragments of K slices kb0 .. kb0 + KB - 1 of chunk jj (indices
-  // clamped into range: the extra fragments are loaded but not used).
+  // Operator fragments of K slices kb0 .. kb0 + KB - 1 of chunk jj; only the
+  // (row tile, slice) pairs the products use are loaded.
   f32x4 fa[QW][KB];
   auto load_batch = [&](int64_t jj, int kb0) {
     jj = jj < N ? jj : N - 1;
     const float* Mj = a.M + static_cast<size_t>(bh * N + jj) * p.mrows() * ncol + 4 * lg;
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
-      const int mt = wave + nw * u < MT ? wave + nw * u : MT - 1;
+      const int mt = wave + nw * u;
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
-        const int kb = kb0 + i < KTc ? kb0 + i : KTc - 1;
-        fa[u][i] = ld4(Mj + static_cast<size_t>(mt * 16 + lr) * ncol + kb * 16);
+        const int kb = kb0 + i;
+        fa[u][i] = mt < MT && kb < KTc ? ld4(Mj + static_cast<size_t>(mt * 16 + lr) * ncol + kb * 16) : zero4();
       }
     }
   };
