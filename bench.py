@@ -64,31 +64,40 @@ def canonical_work(spec):
 
 
 def kernel_work(spec, kernels):
-    """Per-launch work of each kernel of the two-stage decomposition.
+    """Per-launch algorithmic work of each kernel of the two-stage decomposition,
+    on the survey's per-token-head byte count split by which kernel reads or
+    writes each tensor:
 
-    prepare: reads q, K, A, B, log-decay once; writes the chunk operator
-             M_j ((dk + C) x (dk + C r_kv)) once per chunk.
-    scan:    reads M_j and V once, writes out and the final state once.
-    flops: the multiply-adds each kernel's decomposition performs (masked and
-    triangular products at dense size, the triangular inverse at n^3/6).
-    """
+    prepare: reads q, K, A, B and the log-decay;
+    scan:    reads V, writes out and the final state.
+
+    The chunk operator M_j that the prepare hands to the scan is not an
+    algorithmic byte (the method does not need it in memory); its round trip
+    shows up in the counter traffic, reported beside.  flops: the multiply-adds
+    each kernel's decomposition performs (masked and triangular products at
+    dense size, the triangular inverse at n^3/6)."""
     C, dk, dv = spec.chunk, spec.dk, spec.dv
     na, nk = C * spec.r_ab, C * spec.r_kv
     BH = spec.B * spec.H
     N = -(-spec.T // C)
     e = 2 if spec.dtype == "bf16" else 4
-    em = 4 if kernels == "general_fp32" else e  # element size of the stored chunk operator
-    m_elems = (dk + C) * (dk + nk)
     dec = 4 if spec.scalar_decay else 4 * dk
     prep_in = (e * (dk + spec.r_kv * dk + 2 * spec.r_ab * dk) + dec) * BH * spec.T
-    prep_bytes = prep_in + em * m_elems * BH * N
+    scan_bytes = e * (spec.r_kv * dv + dv) * BH * spec.T + 4 * BH * dk * dv
     prep_mac = ((na + C) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (C + dk) * na * (dk + nk))
-    scan_bytes = em * m_elems * BH * N + e * (spec.r_kv * dv + dv) * BH * spec.T + 4 * BH * dk * dv
     scan_mac = (dk + C) * (dk + nk) * dv
     return {
-        "prepare": dict(flops=2.0 * prep_mac * BH * N, bytes=float(prep_bytes)),
+        "prepare": dict(flops=2.0 * prep_mac * BH * N, bytes=float(prep_in)),
         "scan": dict(flops=2.0 * scan_mac * BH * N, bytes=float(scan_bytes)),
     }
+
+
+def operator_bytes(spec, kernels):
+    """Bytes of the chunk operators one forward writes (and the scan reads back)."""
+    C, dk = spec.chunk, spec.dk
+    em = 4 if kernels == "general_fp32" else (2 if spec.dtype == "bf16" else 4)
+    N = -(-spec.T // C)
+    return float(em * (dk + C) * (dk + C * spec.r_kv) * spec.B * spec.H * N)
 
 
 def kernel_peak(kernels, dtype, bound):
@@ -159,15 +168,12 @@ def build_inputs(spec, torch, lattn, dev):
     return raw, (q, K, V, ld, A, B)
 
 
-def fused_leg(spec, raw, torch, lattn, dev, steps, warmup):
+def fused_leg(spec, draw, torch, lattn, dev, steps, warmup):
     """The same workload through the fused family entry point (decay operands
     formed inside the chunk kernel from the raw parameters; nothing excluded
-    from the timed region), timed the same way."""
-    td = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
-    t = lambda x, d=td: torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
-    decay = raw["log_lambda"] if spec.family == "hdla" else raw["g"]
-    plan = lattn.FamilyPlan(spec.family, t(raw["q"]), t(raw["k"]), t(raw["v"]), t(decay, torch.float32),
-                            t(raw["beta"], torch.float32), chunk=spec.chunk)
+    from the timed region), timed the same way.  ``draw``: device tensors."""
+    decay = draw["log_lambda"] if spec.family == "hdla" else draw["g"]
+    plan = lattn.FamilyPlan(spec.family, draw["q"], draw["k"], draw["v"], decay, draw["beta"], chunk=spec.chunk)
     for _ in range(warmup):
         plan.forward()
     stream = torch.cuda.current_stream(dev)
@@ -180,10 +186,7 @@ def fused_leg(spec, raw, torch, lattn, dev, steps, warmup):
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
     flops, _ = canonical_work(spec)
-    e = 2 if spec.dtype == "bf16" else 4
-    dec = 4 if spec.scalar_decay else 4 * spec.dk
-    per_tok = e * (2 * spec.dk + 2 * spec.dv) + dec + 4
-    nbytes = per_tok * spec.B * spec.H * spec.T + spec.B * spec.H * spec.dk * spec.dv * 4
+    nbytes = fused_bytes(spec)
     return {
         "entry": f"lattn_{spec.family}_chunk_fwd",
         "ms_per_step": round(ms, 4),
@@ -193,6 +196,15 @@ def fused_leg(spec, raw, torch, lattn, dev, steps, warmup):
         "algorithmic_gb": round(nbytes / 1e9, 4),
         "hbm_frac_algorithmic": round(nbytes / (ms / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
     }
+
+
+def fused_bytes(spec):
+    """Inputs + outputs of the fused family forward: q, k, v, the log-decay and
+    beta in, out and the final state out."""
+    e = 2 if spec.dtype == "bf16" else 4
+    dec = 4 if spec.scalar_decay else 4 * spec.dk
+    per_tok = e * (2 * spec.dk + 2 * spec.dv) + dec + 4
+    return float(per_tok * spec.B * spec.H * spec.T + spec.B * spec.H * spec.dk * spec.dv * 4)
 
 
 # Query-conditioned composition (HLA note, "Method steps"): Gated DeltaNet, the
@@ -354,6 +366,16 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
     }
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, raw, budget_s):
     """Time the fp64 oracle (generic form, as used for parity) on a bounded sample of
     (batch, head) rows of the same workload, on all host cores."""
@@ -380,10 +402,120 @@ def cpu_baseline(spec, raw, budget_s):
         "value": head_tok_s / spec.H,
         "unit": "tokens/s",
         "cores": int(oracle.max_threads()),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{n} of {spec.B * spec.H} (batch, head) rows x {spec.T} tokens, fp64 explicit-P_t recurrence, "
                   f"{wall:.1f} s wall; tokens/s = head-tokens/s / H",
     }
+
+
+def generic_inputs(spec, draw, lattn):
+    """Forward inputs from a workload's device tensors: HDLA / Gated DeltaNet decay
+    operands from the device parameter kernel (outside any timed region)."""
+    if spec.family == "hdla":
+        A, B, V = lattn.hdla_params(draw["k"], draw["v"], draw["log_lambda"], draw["beta"])
+        return draw["q"], draw["k"], V, draw["log_lambda"], A, B
+    if spec.family == "gdn":
+        A, B, V = lattn.gdn_params(draw["k"], draw["v"], draw["g"], draw["beta"])
+        return draw["q"], draw["k"], V, draw["g"], A, B
+    return draw["q"], draw["K"], draw["V"], draw["log_decay"], draw["A"], draw["B"]
+
+
+def time_forward(plan, torch, dev, steps, warmup):
+    """W untimed forwards, then K timed ones between device synchronizations.
+    Each stage is bracketed by HIP events on the stream its kernels run on.
+    Returns (ms per step by the host clock, {stage: mean event ms})."""
+    for _ in range(warmup):
+        plan.prepare()
+        plan.scan()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        plan.prepare()
+        e[1].record(stream)
+        plan.scan()
+        e[2].record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    return ms_step, {"prepare": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+                     "scan": float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))}
+
+
+def roofline(spec, kernels, kernel_ms):
+    """The dominant kernel against the roofline that bounds it: its share of the
+    survey's algorithmic bytes (or of the flops its decomposition performs)
+    divided by its event-timed duration, against the published peak."""
+    kw = kernel_work(spec, kernels)
+    dom = max(kernel_ms, key=kernel_ms.get)
+    work = kw[dom]
+    comp_peak, _ = kernel_peak(kernels, spec.dtype, "compute")
+    t_comp = work["flops"] / (comp_peak * 1e12)
+    t_mem = work["bytes"] / (PEAK["hbm_GBs"] * 1e9)
+    sec = kernel_ms[dom] / 1e3
+    if t_mem >= t_comp:
+        bound, achieved, unit, peak = "hbm", work["bytes"] / sec / 1e9, "GB/s", PEAK["hbm_GBs"]
+    else:
+        bound, achieved, unit, peak = "mfma", work["flops"] / sec / 1e12, "TFLOP/s", comp_peak
+    traffic = measured_traffic(kernels, dom, spec.name)
+    out = {
+        "kernel": dom,
+        "bound": bound,
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": unit,
+        "frac": round(achieved / peak, 4),
+        "algorithmic_bytes_per_launch": work["bytes"],
+        "flops_per_launch": work["flops"],
+        "launch_ms": round(kernel_ms[dom], 4),
+        "traffic": traffic,
+    }
+    if traffic:
+        out["traffic_over_algorithmic"] = round(traffic / work["bytes"], 3)
+    return out
+
+
+def workload_entry(spec, kernels, ms_step, kernel_ms):
+    flops, nbytes = canonical_work(spec)
+    comp_peak, _ = kernel_peak(kernels, spec.dtype, "compute")
+    return {
+        "kernels": kernels,
+        "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(spec.B * spec.T / (ms_step / 1e3), 1),
+        "head_tokens_per_s": round(spec.B * spec.H * spec.T / (ms_step / 1e3), 1),
+        # against the matrix peak of the type the path multiplies in (bf16, or fp32 on the general path)
+        "mfma_frac_canonical": round(flops / (ms_step / 1e3) / (comp_peak * 1e12), 4),
+        "hbm_frac_algorithmic": round(nbytes / (ms_step / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
+        "canonical_gflop": round(flops / 1e9, 2),
+        "algorithmic_gb": round(nbytes / 1e9, 4),
+        "operator_gb_round_trip": round(2 * operator_bytes(spec, kernels) / 1e9, 4),
+        "kernel_ms": {k: round(v, 4) for k, v in kernel_ms.items()},
+        "roofline": roofline(spec, kernels, kernel_ms),
+    }
+
+
+def config_leg(spec, torch, lattn, dev, steps, warmup):
+    """One workload timed on device-drawn inputs of its shape and distributions,
+    through the generic entry point and (HDLA, Gated DeltaNet) the fused one."""
+    draw = workloads.device_raw(spec, torch, dev, seed=spec.seed)
+    plan = lattn.ChunkPlan(*generic_inputs(spec, draw, lattn), chunk=spec.chunk)
+    kernels = plan_kernels(plan, lattn)
+    ms_step, kms = time_forward(plan, torch, dev, steps, warmup)
+    entry = workload_entry(spec, kernels, ms_step, kms)
+    entry["workload"] = spec.describe()
+    del plan
+    if spec.family in ("hdla", "gdn") and kernels == "mfma_bf16":
+        entry["fused_family"] = fused_leg(spec, draw, torch, lattn, dev, steps, warmup)
+    return entry
+
+
+def plan_kernels(plan, lattn):
+    import ctypes
+    return lattn._lib.load().lattn_chunk_fwd_kernels(ctypes.byref(plan.dims), plan.r_ab, plan.r_kv,
+                                                     plan.chunk).decode()
 
 
 def main():
@@ -393,9 +525,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=workloads.HEADLINE, choices=workloads.CONFIG_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the timing of the other workloads")
     ap.add_argument("--no-hla", action="store_true", help="skip the query-conditioned composition leg")
     ap.add_argument("--no-loglinear", action="store_true", help="skip the log-linear lift leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0, help="target oracle wall time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -414,33 +548,11 @@ def main():
     spec = workloads.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     print(f"[bench] {spec.describe()}: generating inputs", file=sys.stderr, flush=True)
-    raw, (q, K, V, ld, A, B) = build_inputs(spec, torch, lattn, dev)
-    plan = lattn.ChunkPlan(q, K, V, ld, A, B, chunk=spec.chunk)
-    kernels = lattn._lib.load().lattn_chunk_fwd_kernels(
-        __import__("ctypes").byref(plan.dims), plan.r_ab, plan.r_kv, plan.chunk).decode()
-
-    for _ in range(args.warmup):
-        plan.prepare()
-        plan.scan()
-    torch.cuda.synchronize(dev)
-    print(f"[bench] kernels {kernels}: warmup {args.warmup} done, timing {args.steps} steps",
-          file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream(dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for e in evs:
-        e[0].record(stream)
-        plan.prepare()
-        e[1].record(stream)
-        plan.scan()
-        e[2].record(stream)
-    torch.cuda.synchronize(dev)
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    ms_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ms_scan = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    raw, inputs = build_inputs(spec, torch, lattn, dev)
+    plan = lattn.ChunkPlan(*inputs, chunk=spec.chunk)
+    kernels = plan_kernels(plan, lattn)
+    print(f"[bench] kernels {kernels}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms_step, kms = time_forward(plan, torch, dev, args.steps, args.warmup)
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -450,29 +562,10 @@ def main():
         torch.cuda.synchronize(dev)
         del src, dst
 
-    tokens = spec.B * spec.T
-    value = tokens / (ms_step / 1e3)
-    flops, nbytes = canonical_work(spec)
-    kw = kernel_work(spec, kernels)
-    times = {"prepare": ms_prep, "scan": ms_scan}
-    dom = max(times, key=times.get)
-    work = kw[dom]
-    e_dtype = spec.dtype
-    # the roofline a kernel sits under: the larger of its time at peak compute and at peak HBM
-    comp_peak, _ = kernel_peak(kernels, e_dtype, "compute")
-    t_comp = work["flops"] / (comp_peak * 1e12)
-    t_mem = work["bytes"] / (PEAK["hbm_GBs"] * 1e9)
-    if t_mem >= t_comp:
-        bound, achieved, unit = "hbm", work["bytes"] / (times[dom] / 1e3) / 1e9, "GB/s"
-        peak = PEAK["hbm_GBs"]
-    else:
-        bound = "mfma"
-        achieved, unit, peak = work["flops"] / (times[dom] / 1e3) / 1e12, "TFLOP/s", comp_peak
-    traffic = measured_traffic(kernels, dom, spec.name)
-
+    head = workload_entry(spec, kernels, ms_step, kms)
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -489,31 +582,38 @@ def main():
             "d_k": spec.dk, "d_v": spec.dv, "chunk": spec.chunk, "r_ab": spec.r_ab, "r_kv": spec.r_kv,
             "storage": spec.dtype, "kernels": kernels, "parallelism": "single-gpu",
         },
-        # against the matrix peak of the type the path multiplies in (bf16, or fp32 on the general path)
-        "mfma_frac_canonical": round(flops / (ms_step / 1e3) / (comp_peak * 1e12), 4),
-        "hbm_frac_algorithmic": round(nbytes / (ms_step / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
-        "canonical_gflop": round(flops / 1e9, 2),
-        "algorithmic_gb": round(nbytes / 1e9, 4),
-        "kernel_ms": {"prepare": round(ms_prep, 4), "scan": round(ms_scan, 4)},
-        "roofline": {
-            "kernel": dom,
-            "bound": bound,
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": unit,
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic,
-        },
-        "cpu_baseline": None,
     }
+    for k in ("mfma_frac_canonical", "hbm_frac_algorithmic", "canonical_gflop", "algorithmic_gb",
+              "operator_gb_round_trip", "kernel_ms", "roofline"):
+        result[k] = head[k]
+    result["cpu_baseline"] = None
+    del plan
     if spec.family in ("hdla", "gdn") and kernels == "mfma_bf16":
-        result["fused_family"] = fused_leg(spec, raw, torch, lattn, dev, args.steps, args.warmup)
+        td = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+        t = lambda x, d=td: torch.from_numpy(np.ascontiguousarray(x)).to(d).to(dev)
+        decay = "log_lambda" if spec.family == "hdla" else "g"
+        draw = {"q": t(raw["q"]), "k": t(raw["k"]), "v": t(raw["v"]), decay: t(raw[decay], torch.float32),
+                "beta": t(raw["beta"], torch.float32)}
+        result["fused_family"] = fused_leg(spec, draw, torch, lattn, dev, args.steps, args.warmup)
+        del draw
+    if not args.no_configs:
+        result["configs"] = {}
+        for name in workloads.CONFIG_ORDER:
+            if name == spec.name:
+                result["configs"][name] = dict(head, workload=spec.describe(),
+                                               **({"fused_family": result["fused_family"]}
+                                                  if "fused_family" in result else {}))
+                continue
+            print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+            result["configs"][name] = config_leg(workloads.CONFIGS[name], torch, lattn, dev,
+                                                 max(3, args.steps // 2), min(args.warmup, 3))
+            torch.cuda.empty_cache()
     if spec.name == workloads.HEADLINE and not args.no_hla:
         print("[bench] query-conditioned composition leg", file=sys.stderr, flush=True)
         result["hla"] = hla_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))
     if spec.name == workloads.HEADLINE and not args.no_backward:
         print("[bench] backward leg", file=sys.stderr, flush=True)
-        result["backward"] = backward_leg(spec, raw, (q, K, V, ld, A, B), torch, lattn, dev)
+        result["backward"] = backward_leg(spec, raw, inputs, torch, lattn, dev)
     if spec.name == workloads.HEADLINE and not args.no_loglinear:
         print("[bench] log-linear lift leg", file=sys.stderr, flush=True)
         result["loglinear"] = loglinear_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))

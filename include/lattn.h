@@ -315,13 +315,17 @@ size_t lattn_gdn_chunk_fwd_workspace_size(const lattn_dims* dims, int chunk);
  * lattn_decay_range -- per chunk, the largest -G over the chunk's tokens and
  * channels, where G is the chunk-local inclusive cumulative log-decay.  The
  * chunk-wise form scales operands by exp(-G); the result must stay below
- * LATTN_MAX_CHUNK_LOG_DECAY.  chunk_max [B,H,N] fp32 (written).  Asynchronous.
+ * LATTN_MAX_CHUNK_LOG_DECAY.  chunk_max [B,H,N] fp32 (written); an entry is
+ * NaN when the chunk's log-decay holds a NaN.  Asynchronous.
  */
 int lattn_decay_range(const lattn_dims* dims, const float* log_decay, int chunk,
                       float* chunk_max, hipStream_t stream);
 
 /* Synchronous convenience check built on lattn_decay_range: returns LATTN_OK
- * or LATTN_EDECAY_RANGE.  `scratch` holds B*H*ceil(T/C) floats (device). */
+ * or LATTN_EDECAY_RANGE (a chunk beyond the limit, or a NaN log-decay).
+ * `scratch` is caller-owned device memory of B*H*ceil(T/C) floats that
+ * receives the per-chunk maxima: the library allocates nothing, so the
+ * buffer the check reduces on the host comes from the caller. */
 int lattn_check_decay_range(const lattn_dims* dims, const float* log_decay, int chunk,
                             float* scratch, hipStream_t stream);
 

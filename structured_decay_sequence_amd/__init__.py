@@ -62,18 +62,14 @@ def _need(t: torch.Tensor, dtype, shape, name):
         raise ValueError(f"{name} must be a device tensor")
 
 
-_workspaces = {}
-
-
 def _workspace(device, nbytes: int) -> Optional[torch.Tensor]:
+    """A fresh workspace for one call, from torch's caching allocator on the
+    current stream.  The tensor lives until the caller drops it; the allocator
+    hands its memory to a later request only in stream order, so calls on
+    different streams never share a buffer that one of them still uses."""
     if nbytes == 0:
         return None
-    key = torch.device(device).index
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
-    return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def _ranked(x: torch.Tensor, lead, T, d):

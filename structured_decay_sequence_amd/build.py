@@ -33,20 +33,42 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
 
-def build(verbose: bool = False, extra=None) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature name; that warning is harmless.
     noise = "packed-fp32-ops"
     errs = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+    return res.returncode, errs
+
+
+def build(verbose: bool = False, extra=None, jobs: int = 0) -> str:
+    """Compile every source to an object in parallel (each carries its own gfx950
+    code object), then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra or [])
+    inc = ["-I", os.path.join(ROOT, "include")]
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+    cmds = [[hipcc, *flags, *inc, "-c", "-o", o, s] for s, o in zip(srcs, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    for (rc, errs), s in zip(results, srcs):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(s)} ({rc}):\n{errs}")
+        if verbose and errs.strip():
+            print(errs, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, errs = _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{errs}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -546,8 +546,14 @@ int lattn_check_decay_range(const lattn_dims* dims, const float* log_decay, int 
   std::vector<float> host(n);
   LATTN_TRY(hip_status(hipMemcpyAsync(host.data(), scratch, n * sizeof(float), hipMemcpyDeviceToHost, stream), "copy chunk maxima"));
   LATTN_TRY(hip_status(hipStreamSynchronize(stream), "synchronize"));
+  // A NaN entry (a NaN log-decay in that chunk) fails the check as well.
   float m = 0.f;
-  for (float x : host) m = x > m ? x : m;
+  bool nan_seen = false;
+  for (float x : host) {
+    if (x != x) nan_seen = true;
+    else if (x > m) m = x;
+  }
+  if (nan_seen) return fail(LATTN_EDECAY_RANGE, "log_decay holds NaN");
   if (!(m <= LATTN_MAX_CHUNK_LOG_DECAY))
     return fail(LATTN_EDECAY_RANGE, "chunk cumulative -log-decay reaches %g (limit %g)", (double)m,
                 (double)LATTN_MAX_CHUNK_LOG_DECAY);

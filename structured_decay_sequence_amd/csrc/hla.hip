@@ -160,7 +160,9 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
     int act = 0;
     for (int t = tid; t < C; t += kHlaThreads) {
       const float w = t < n ? gb[static_cast<size_t>(t) * N + j] : 0.f;
-      act |= w >= theta;
+      // Only a gate below the threshold counts as 0; a NaN gate is applied
+      // (and propagates), so it keeps the chunk active.
+      act |= !(w < theta);
       gs[t] = w < theta ? 0.f : w;
     }
     if (!__syncthreads_or(act)) continue;

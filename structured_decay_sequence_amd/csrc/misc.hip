@@ -156,6 +156,11 @@ __global__ __launch_bounds__(kThreads) void gdn_params_kernel(GdnArgs a) {
 // ---------------------------------------------------------------------------
 // Per chunk: max over tokens and channels of -G (chunk-local inclusive
 // cumulative log-decay).  One workgroup per chunk, one thread per channel.
+// A NaN anywhere in the chunk makes its entry NaN (fmaxf alone would drop it).
+__device__ __forceinline__ float nan_max(float a, float b) {
+  return (a != a || b != b) ? __builtin_nanf("") : fmaxf(a, b);
+}
+
 __global__ __launch_bounds__(kThreads) void decay_range_kernel(Problem p, const float* ld,
                                                                float* chunk_max) {
   __shared__ float red[kThreads / 64];
@@ -170,15 +175,16 @@ __global__ __launch_bounds__(kThreads) void decay_range_kernel(Problem p, const 
     float g = 0.f;
     for (int t = 0; t < n; ++t) {
       g += p.scalar ? ld[tok0 + t] : ld[(tok0 + t) * p.dk + i];
-      m = fmaxf(m, -g);
+      m = nan_max(m, -g);
     }
   }
-  m = wave_max(m);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = nan_max(m, __shfl_xor(m, off, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     float r = red[0];
-    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+    for (int w = 1; w < kThreads / 64; ++w) r = nan_max(r, red[w]);
     chunk_max[job] = r;
   }
 }

@@ -117,3 +117,19 @@ def test_hla_empty_and_repeatable():
     a = _gpu(raw, gates, "bf16", 64, 0.1)
     b = _gpu(raw, gates, "bf16", 64, 0.1)
     assert np.array_equal(a, b)
+
+
+def test_hla_nan_gate_propagates_like_the_oracle():
+    """A NaN gate is not below the threshold, so it is applied (and poisons only
+    its own query's row), as in the oracle; every other row stays finite and
+    matches."""
+    Bb, H, T, dk, dv, C = 1, 1, 150, 32, 32, 32
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 1, 1, "fp32", "channel", seed=12)
+    gates = workloads.hla_gates(Bb, H, T, C, mu=-1.0, seed=12)
+    gates[0, 0, 100, 1] = np.nan       # query 100 (chunk 3), history chunk 1
+    out = _gpu(raw, gates, "fp32", C, 0.1)
+    ref = hla_oracle.hla(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], gates, C, 0.1)
+    assert np.array_equal(np.isnan(out), np.isnan(ref))
+    assert np.isnan(out[0, 0, 100]).all()
+    keep = ~np.isnan(ref)
+    assert rel_err(out[keep], ref[keep]) <= TOL["fp32"]

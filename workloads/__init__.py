@@ -197,3 +197,37 @@ def loglinear_lambdas(B, H, T, seed=0) -> np.ndarray:
     L = 1 + int(T - 1).bit_length() if T > 0 else 0
     x = rng.standard_normal((B, H, T, L), dtype=np.float32)
     return (-_log_sigmoid(-x).astype(np.float64)).astype(np.float32)   # softplus(x) = -log sigmoid(-x)
+
+
+def device_raw(spec: Spec, torch, device, seed: int = 0):
+    """The same distributions as :func:`raw_for`, drawn on the device with a seeded
+    torch generator (used where only timing needs the inputs: the values differ
+    from the numpy stream, the shapes and distributions do not).  Returns a dict
+    of device tensors in the storage dtype (decay, beta in float32)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    td = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    B, H, T, dk, dv = spec.B, spec.H, spec.T, spec.dk, spec.dv
+    f32 = dict(dtype=torch.float32, device=device, generator=g)
+    normal = lambda *shape: torch.randn(shape, **f32)
+    l2n = lambda x: x / x.norm(dim=-1, keepdim=True)
+    logsig = torch.nn.functional.logsigmoid
+    if spec.family == "hdla":
+        q, k, v = normal(B, H, T, dk), l2n(normal(B, H, T, dk)), normal(B, H, T, dv)
+        ll = logsig(normal(B, H, T, dk) + spec.lam_mu)
+        beta = 2.0 * torch.sigmoid(normal(B, H, T))
+        return dict(q=q.to(td), k=k.to(td), v=v.to(td), log_lambda=ll, beta=beta)
+    if spec.family == "gdn":
+        q, k, v = l2n(normal(B, H, T, dk)), l2n(normal(B, H, T, dk)), normal(B, H, T, dv)
+        gg = 0.1 * logsig(-normal(B, H, T))
+        beta = torch.sigmoid(normal(B, H, T))
+        return dict(q=q.to(td), k=k.to(td), v=v.to(td), g=gg, beta=beta)
+    s = 1.0 / float(np.sqrt(dk))
+    q = normal(B, H, T, dk)
+    ld = logsig(normal(B, H, T, dk) + spec.lam_mu)
+    A = normal(B, H, T, spec.r_ab, dk) * (s * 0.5) if spec.r_ab > 0 else None
+    Bm = normal(B, H, T, spec.r_ab, dk) * (s * 0.5) if spec.r_ab > 0 else None
+    K = normal(B, H, T, spec.r_kv, dk) * s
+    V = normal(B, H, T, spec.r_kv, dv) * s
+    return dict(q=q.to(td), log_decay=ld, A=None if A is None else A.to(td), B=None if Bm is None else Bm.to(td),
+                K=K.to(td), V=V.to(td))
