@@ -105,6 +105,31 @@ int lattn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const 
  * arguments; host-only, launches nothing). */
 size_t lattn_chunk_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk);
 
+/* Size of the library's static per-GPU scratch used by lattn_chunk_fwd_noalloc. */
+#define LATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * lattn_chunk_fwd_noalloc -- lattn_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as lattn_chunk_fwd, minus
+ * the workspace: the chunk operators go to a static device array of
+ * LATTN_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends (its address is looked up once per device, on the first
+ * call with that device current).  The call allocates nothing and calls no
+ * allocating routine.
+ *   - A problem whose lattn_chunk_fwd_workspace_size() exceeds
+ *     LATTN_NOALLOC_SCRATCH_BYTES is rejected with LATTN_EWORKSPACE before
+ *     any launch (use lattn_chunk_fwd with a caller-owned workspace).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (the kernels overwrite what they read, so nothing needs
+ *     clearing).  Calls that overlap in time on one GPU (different streams or
+ *     host threads without ordering) race on it; order them on one stream.
+ */
+int lattn_chunk_fwd_noalloc(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                            const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                            int chunk, void* out, float* final_state, const float* initial_state,
+                            hipStream_t stream);
+
 /* Host-only validation of lattn_chunk_fwd's arguments (the same checks the
  * call performs before launching).  Pointers are only tested for NULL and
  * 16-byte alignment, never dereferenced. */

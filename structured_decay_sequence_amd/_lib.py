@@ -40,6 +40,7 @@ _D = ctypes.POINTER(lattn_dims)
 SIGNATURES = {
     "lattn_chunk_fwd": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "lattn_chunk_fwd_workspace_size": (_SZ, [_D, _I, _I, _I]),
+    "lattn_chunk_fwd_noalloc": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "lattn_chunk_fwd_check": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _SZ]),
     "lattn_chunk_prepare": (_I, [_D, _P, _P, _P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "lattn_chunk_scan": (_I, [_D, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),

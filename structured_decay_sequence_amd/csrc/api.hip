@@ -3,6 +3,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -125,6 +126,33 @@ hipError_t run_scan(const lattn::Problem& p, void* ws, const void* v, void* out,
                     const float* S0, hipStream_t s) {
   if (lattn::fast_supported(p)) return lattn::fast_scan(p, ws, v, out, Sfin, S0, s);
   return lattn::general_scan(p, ws, v, out, Sfin, S0, s);
+}
+
+// Static scratch of lattn_chunk_fwd_noalloc: each GPU holds its own copy of
+// this array, at its own address, for the life of the process.  In host code
+// the name stands for a host-side shadow, not device memory, so host code
+// only ever uses the device address looked up below.
+__device__ __align__(256) unsigned char scratch[LATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch, looked up once per device with
+// that device current.
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  LATTN_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LATTN_EHIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    LATTN_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (p == nullptr) return fail(LATTN_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return LATTN_OK;
 }
 
 // The fused family forwards (HDLA, Gated DeltaNet from their raw parameters).
@@ -411,6 +439,31 @@ int lattn_chunk_fwd(const lattn_dims* dims, const void* q, const void* k, const 
   if (p.T == 0) return hip_status(lattn::launch_copy_state(p, initial_state, final_state, stream), "copy state");
   LATTN_TRY(hip_status(run_prepare(p, q, k, log_decay, A, B, workspace, stream), "prepare launch"));
   LATTN_TRY(hip_status(run_scan(p, workspace, v, out, final_state, initial_state, stream), "scan launch"));
+  return ok();
+}
+
+int lattn_chunk_fwd_noalloc(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                            const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
+                            int chunk, void* out, float* final_state, const float* initial_state,
+                            hipStream_t stream) {
+  // Validation and the size check come first: a rejected call touches no device.
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool nonempty = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", nonempty));
+  LATTN_TRY(check_ptr(out, "out", nonempty));
+  const size_t need = lattn_chunk_fwd_workspace_size(dims, r_ab, r_kv, chunk);
+  LATTN_TRY(check_ptr(final_state, "final_state", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  if (need > LATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(LATTN_EWORKSPACE, "lattn_chunk_fwd_noalloc: this problem needs %zu bytes of scratch, the static "
+                "scratch holds %zu; call lattn_chunk_fwd with a caller-owned workspace", need,
+                (size_t)LATTN_NOALLOC_SCRATCH_BYTES);
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  if (p.T == 0) return hip_status(lattn::launch_copy_state(p, initial_state, final_state, stream), "copy state");
+  void* ws = nullptr;
+  LATTN_TRY(noalloc_scratch(&ws));
+  LATTN_TRY(hip_status(run_prepare(p, q, k, log_decay, A, B, ws, stream), "prepare launch"));
+  LATTN_TRY(hip_status(run_scan(p, ws, v, out, final_state, initial_state, stream), "scan launch"));
   return ok();
 }
 
