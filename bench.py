@@ -366,6 +366,48 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
     }
 
 
+def decode_leg(spec, torch, lattn, dev, steps, warmup):
+    """lattn_step (one recurrent token per (batch, head)) at the workload's
+    shape, HIP events on its stream.  The step is memory-bound: its roofline
+    is the fp32 state read and written once per token plus the token's
+    vectors.  The state rotates over enough distinct buffers that their sum
+    exceeds the 256 MB MALL, so every step reads the state from HBM."""
+    Bb, H, dk, dv = spec.B, spec.H, spec.dk, spec.dv
+    state_bytes = Bb * H * dk * dv * 4
+    nstates = max(2, -(-(384 << 20) // state_bytes))
+    draw = workloads.device_raw(workloads.Spec(spec.name, spec.family, Bb, H, 1, dk, dv, spec.chunk, spec.r_ab,
+                                               spec.r_kv, spec.dtype, spec.lam_mu), torch, dev, seed=1)
+    q, K, V, ld, A, B = (x[:, :, 0].contiguous() if x is not None else None for x in generic_inputs(spec, draw, lattn))
+    states = [torch.zeros((Bb, H, dk, dv), dtype=torch.float32, device=dev) for _ in range(nstates)]
+    out = torch.empty((Bb, H, dv), dtype=q.dtype, device=dev)
+    for i in range(warmup):
+        lattn.step(q, K, V, ld, A, B, states[i % nstates], out=out)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for i in range(steps):
+        lattn.step(q, K, V, ld, A, B, states[i % nstates], out=out)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    e = 2 if spec.dtype == "bf16" else 4
+    dec = 4 if spec.scalar_decay else 4 * dk
+    tok_bytes = e * (dk + spec.r_kv * (dk + dv) + 2 * spec.r_ab * dk + dv) + dec
+    nbytes = 2 * state_bytes + Bb * H * tok_bytes
+    gbs = nbytes / (us / 1e6) / 1e9
+    return {
+        "entry": "lattn_step",
+        "workload": f"{spec.family} B{Bb} H{H} d_k {dk} d_v {dv} r_ab {spec.r_ab} {spec.dtype}, one token per (batch, head), "
+                    f"state rotated over {nstates} buffers ({nstates * state_bytes / 2**20:.0f} MiB)",
+        "us_per_step": round(us, 3),
+        "value": round(Bb / (us / 1e6), 1),
+        "unit": "tokens/s",
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK["hbm_GBs"], "unit": "GB/s",
+                     "frac": round(gbs / PEAK["hbm_GBs"], 4), "bytes_per_step": nbytes},
+    }
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -608,6 +650,9 @@ def main():
             result["configs"][name] = config_leg(workloads.CONFIGS[name], torch, lattn, dev,
                                                  max(3, args.steps // 2), min(args.warmup, 3))
             torch.cuda.empty_cache()
+    if not args.no_decode:
+        print("[bench] decode-step leg", file=sys.stderr, flush=True)
+        result["decode"] = decode_leg(spec, torch, lattn, dev, max(50, 10 * args.steps), 10)
     if spec.name == workloads.HEADLINE and not args.no_hla:
         print("[bench] query-conditioned composition leg", file=sys.stderr, flush=True)
         result["hla"] = hla_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))

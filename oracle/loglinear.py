@@ -21,8 +21,17 @@ What it computes (Log-Linear note, "Key design" 1-3):
   case).
 
 Nothing is blocked or reordered: per query, the keys are walked from t down
-to 0, carrying Phi(t, s) as a running product.  Pins:
-``tests/test_loglinear_oracle_pins.py``.
+to 0, carrying Phi(t, s) as a running product.
+
+``loglinear_recurrent`` computes the same output a second, independent way,
+from the note's recurrent form ("Key design" 1-2): one state per bucket level,
+advanced token by token.  At every step each bucket state is transported by
+P_t; when t - 1 ends in z one-bits, the buckets of levels 0 .. z of t - 1
+together make up the single bucket of level z + 1 of t, so their states are
+summed into it (the Fenwick merge), and the new token's write K_t V_t^T
+starts level 0.  Its cost is O(T log T) state products, so it reaches every
+level of long sequences.  The two are pinned against each other (and each
+against the plain recurrence) by ``tests/test_loglinear_oracle_pins.py``.
 """
 from __future__ import annotations
 
@@ -80,4 +89,48 @@ def loglinear(q, K, V, log_decay, A, B, lam):
                 S += lf[h, t, lev[s]] * (Phi @ (Kf[h, s].T @ Vf[h, s]))
                 Phi = Phi @ P[s]    # Phi(t, s - 1) = Phi(t, s) P_s
             out[h, t] = S.T @ qf[h, t]
+    return out.reshape(lead + (T, dv))
+
+
+def loglinear_recurrent(q, K, V, log_decay, A, B, lam):
+    """Lifted output from per-level bucket states (the recurrent form).  Same
+    arguments and result as :func:`loglinear`."""
+    q, K, V, ld, A, B, lam = (_f64(x) for x in (q, K, V, log_decay, A, B, lam))
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = V.shape[-1]
+    flat = int(np.prod(lead)) if lead else 1
+    qf = q.reshape(flat, T, dk)
+    Kf = K.reshape((flat,) + K.shape[-3:])
+    Vf = V.reshape((flat,) + V.shape[-3:])
+    ldf = ld.reshape((flat,) + ld.shape[len(lead):])
+    Af = None if A is None else A.reshape((flat,) + A.shape[-3:])
+    Bf = None if B is None else B.reshape((flat,) + B.shape[-3:])
+    lf = lam.reshape(flat, T, lam.shape[-1])
+    out = np.zeros((flat, T, dv))
+    for h in range(flat):
+        states = {}                                   # level -> bucket state (d_k x d_v)
+        for t in range(T):
+            if t > 0:
+                z = 0                                 # trailing one-bits of t - 1
+                while ((t - 1) >> z) & 1:
+                    z += 1
+                merged = np.zeros((dk, dv))
+                for l in range(z + 1):
+                    if l in states:
+                        merged += states.pop(l)
+                states[z + 1] = merged
+                d = np.exp(ldf[h, t])
+                P = np.diag(d) if np.ndim(d) == 1 else d * np.eye(dk)
+                if Af is not None:
+                    P = P - Af[h, t].T @ Bf[h, t]
+                levels = sorted(states)
+                moved = np.matmul(P, np.stack([states[l] for l in levels]))
+                for i, l in enumerate(levels):
+                    states[l] = moved[i]
+            states[0] = Kf[h, t].T @ Vf[h, t]
+            o = np.zeros(dv)
+            for l, S in states.items():
+                o += lf[h, t, l] * (S.T @ qf[h, t])
+            out[h, t] = o
     return out.reshape(lead + (T, dv))

@@ -10,8 +10,17 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // Single recurrent token (HDLA note, "Key design 3", one step of the general
 // recurrence):  state <- D state - A (B^T state) + K V^T,  out = state^T q.
-// One workgroup per (batch*head, d_v slice of BV columns); the slice of the
-// state is staged in LDS, B^T state is reduced over d_k per column.
+// Memory-bound: every state element is read and written once.  One workgroup
+// of four waves per (batch*head, 64-column slice of d_v): lane c owns column
+// c of the slice, wave w owns rows w, w + 4, w + 8, ... (so every state load
+// or store of a wave is one contiguous row piece).  Each thread keeps its
+// rows in registers; the two sums over d_k (B^T state and state^T q) are a
+// per-thread partial over its rows, then a fixed-order sum of the four
+// waves' partials through LDS.  The token's vectors (q, K, A, B, exp(l)) are
+// staged in LDS once per workgroup.
+constexpr int kStepWaves = 4;
+constexpr int kStepCols = 64;
+
 struct StepArgs {
   Problem p;
   const void* q;
@@ -22,54 +31,104 @@ struct StepArgs {
   const void* B;
   float* state;
   void* out;
-  int BV;
 };
 
-template <typename TI>
-__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
+template <typename TI, int RPT>
+__global__ __launch_bounds__(kStepWaves * 64) void step_kernel(StepArgs a) {
   extern __shared__ float smem[];
   const Problem& p = a.p;
-  const int dk = p.dk, dv = p.dv, r_ab = p.r_ab, r_kv = p.r_kv, BV = a.BV;
-  const int nvt = dv / BV;
-  const int64_t bh = blockIdx.x / nvt;
-  const int c0 = (blockIdx.x % nvt) * BV;
-  const int tid = threadIdx.x;
-  float* S = smem;              // dk x BV
-  float* Wr = S + dk * BV;      // r_ab x BV : (B^T S)
-  const TI* qp = static_cast<const TI*>(a.q);
-  const TI* kp = static_cast<const TI*>(a.k);
-  const TI* vp = static_cast<const TI*>(a.v);
-  const TI* Ap = static_cast<const TI*>(a.A);
-  const TI* Bp = static_cast<const TI*>(a.B);
+  const int dk = p.dk, dv = p.dv, r_ab = p.r_ab, r_kv = p.r_kv;
+  const int nsl = (dv + kStepCols - 1) / kStepCols;
+  const int64_t bh = blockIdx.x / nsl;
+  const int c0 = (blockIdx.x % nsl) * kStepCols;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = c0 + lane;
+  const bool col = c < dv;
+  // LDS: q [dk], exp(l) [dk], K [r_kv][dk], A [r_ab][dk], B [r_ab][dk], then the
+  // wave partials of B^T state [4][r_ab][64] and of the readout [4][64].
+  float* qs = smem;
+  float* es = qs + dk;
+  float* ks = es + dk;
+  float* as = ks + r_kv * dk;
+  float* bs = as + r_ab * dk;
+  float* wpart = bs + r_ab * dk;
+  float* opart = wpart + kStepWaves * r_ab * kStepCols;
+  const TI* qp = static_cast<const TI*>(a.q) + static_cast<size_t>(bh) * dk;
+  const TI* kp = static_cast<const TI*>(a.k) + static_cast<size_t>(bh) * r_kv * dk;
+  const TI* Ap = static_cast<const TI*>(a.A) + static_cast<size_t>(bh) * r_ab * dk;
+  const TI* Bp = static_cast<const TI*>(a.B) + static_cast<size_t>(bh) * r_ab * dk;
+  for (int i = threadIdx.x; i < dk; i += kStepWaves * 64) {
+    qs[i] = Elem<TI>::load(qp, i);
+    es[i] = expf(p.scalar ? a.ld[bh] : a.ld[static_cast<size_t>(bh) * dk + i]);
+  }
+  for (int i = threadIdx.x; i < r_kv * dk; i += kStepWaves * 64) ks[i] = Elem<TI>::load(kp, i);
+  for (int i = threadIdx.x; i < r_ab * dk; i += kStepWaves * 64) {
+    as[i] = Elem<TI>::load(Ap, i);
+    bs[i] = Elem<TI>::load(Bp, i);
+  }
+  // This thread's state rows i = wave + 4m (m < RPT), column c.
   float* st = a.state + static_cast<size_t>(bh) * dk * dv;
-
-  for (int e = tid; e < dk * BV; e += kThreads) S[e] = st[(e / BV) * dv + c0 + e % BV];
-  __syncthreads();
-  for (int e = tid; e < r_ab * BV; e += kThreads) {
-    const int r = e / BV, c = e % BV;
-    float s = 0.f;
-    for (int i = 0; i < dk; ++i)
-      s += Elem<TI>::load(Bp, (static_cast<size_t>(bh) * r_ab + r) * dk + i) * S[i * BV + c];
-    Wr[e] = s;
+  float S[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = wave + kStepWaves * m;
+    S[m] = (col && i < dk) ? st[static_cast<size_t>(i) * dv + c] : 0.f;
   }
   __syncthreads();
-  for (int e = tid; e < dk * BV; e += kThreads) {
-    const int i = e / BV, c = e % BV;
-    const float l = p.scalar ? a.ld[bh] : a.ld[static_cast<size_t>(bh) * dk + i];
-    float s = expf(l) * S[e];
-    for (int r = 0; r < r_ab; ++r)
-      s -= Elem<TI>::load(Ap, (static_cast<size_t>(bh) * r_ab + r) * dk + i) * Wr[r * BV + c];
-    for (int r = 0; r < r_kv; ++r)
-      s += Elem<TI>::load(kp, (static_cast<size_t>(bh) * r_kv + r) * dk + i) *
-           Elem<TI>::load(vp, (static_cast<size_t>(bh) * r_kv + r) * dv + c0 + c);
-    S[e] = s;
+  // B^T state: partial over this thread's rows, one per decay rank.
+  for (int r = 0; r < r_ab; ++r) {
+    float w = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int i = wave + kStepWaves * m;
+      if (i < dk) w += bs[r * dk + i] * S[m];
+    }
+    wpart[(wave * r_ab + r) * kStepCols + lane] = w;
+  }
+  // V_t[r][c] for this column.
+  float vv[4];
+  const TI* vp = static_cast<const TI*>(a.v) + static_cast<size_t>(bh) * r_kv * dv;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vv[r] = (r < r_kv && col) ? Elem<TI>::load(vp, static_cast<size_t>(r) * dv + c) : 0.f;
+  __syncthreads();
+  float W[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    W[r] = 0.f;
+    if (r < r_ab) {
+#pragma unroll
+      for (int w = 0; w < kStepWaves; ++w) W[r] += wpart[(w * r_ab + r) * kStepCols + lane];
+    }
+  }
+  // The update of this thread's rows, and the readout partial over them.
+  float o = 0.f;
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = wave + kStepWaves * m;
+    if (i < dk) {
+      float s = es[i] * S[m];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r < r_ab) s -= as[r * dk + i] * W[r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < r_kv) s += ks[r * dk + i] * vv[r];
+      S[m] = s;
+      o += s * qs[i];
+    }
+  }
+  opart[wave * kStepCols + lane] = o;
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int i = wave + kStepWaves * m;
+    if (col && i < dk) st[static_cast<size_t>(i) * dv + c] = S[m];
   }
   __syncthreads();
-  for (int e = tid; e < dk * BV; e += kThreads) st[(e / BV) * dv + c0 + e % BV] = S[e];
-  for (int c = tid; c < BV; c += kThreads) {
-    float s = 0.f;
-    for (int i = 0; i < dk; ++i) s += S[i * BV + c] * Elem<TI>::load(qp, static_cast<size_t>(bh) * dk + i);
-    Elem<TI>::store(static_cast<TI*>(a.out), static_cast<size_t>(bh) * dv + c0 + c, s);
+  if (wave == 0 && col) {
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStepWaves; ++w) r += opart[w * kStepCols + lane];
+    Elem<TI>::store(static_cast<TI*>(a.out), static_cast<size_t>(bh) * dv + c, r);
   }
 }
 
@@ -196,19 +255,28 @@ __global__ __launch_bounds__(kThreads) void copy_state_kernel(int64_t n, const f
 
 }  // namespace
 
+template <typename TI>
+hipError_t launch_step_t(const Problem& p, const StepArgs& a, size_t lds, int64_t blocks, hipStream_t s) {
+  // Rows per thread: the smallest bucket with 4 * RPT >= d_k.
+  if (p.dk <= 64)
+    hipLaunchKernelGGL((step_kernel<TI, 16>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+  else if (p.dk <= 128)
+    hipLaunchKernelGGL((step_kernel<TI, 32>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+  else
+    hipLaunchKernelGGL((step_kernel<TI, 64>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, float* state, void* out,
                        hipStream_t s) {
-  const int BV = (p.dv % 32 == 0) ? 32 : 16;
-  StepArgs a{p, q, k, v, ld, A, B, state, out, BV};
-  const size_t lds = static_cast<size_t>(p.dk + p.r_ab) * BV * sizeof(float);
-  const int64_t blocks = p.BH * (p.dv / BV);
+  if (p.r_ab > 8 || p.r_kv > 4 || p.dk > 256) return hipErrorInvalidValue;
+  StepArgs a{p, q, k, v, ld, A, B, state, out};
+  const size_t lds = (static_cast<size_t>(2 + p.r_kv + 2 * p.r_ab) * p.dk +
+                      static_cast<size_t>(kStepWaves) * (p.r_ab + 1) * kStepCols) * sizeof(float);
+  const int64_t blocks = p.BH * ((p.dv + kStepCols - 1) / kStepCols);
   if (blocks == 0) return hipSuccess;
-  if (p.bf16)
-    hipLaunchKernelGGL(step_kernel<bf16_raw>, dim3(blocks), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(step_kernel<float>, dim3(blocks), dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  return p.bf16 ? launch_step_t<bf16_raw>(p, a, lds, blocks, s) : launch_step_t<float>(p, a, lds, blocks, s);
 }
 
 hipError_t launch_hdla_params(const Problem& p, const void* k, const void* v,

@@ -84,3 +84,37 @@ def test_level_zero_only_is_current_token():
     k, v, q = raw["K"][..., 0, :].astype(np.float64), raw["V"][..., 0, :].astype(np.float64), raw["q"].astype(np.float64)
     ref = np.sum(k * q, axis=-1, keepdims=True) * v
     assert np.abs(out - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("T,dk,dv,r_ab,r_kv,decay", [(70, 6, 5, 2, 1, "channel"), (129, 4, 3, 1, 2, "scalar"),
+                                                     (64, 5, 4, 0, 1, "channel"), (33, 3, 3, 3, 1, "channel")])
+def test_recurrent_form_equals_per_query_definition(T, dk, dv, r_ab, r_kv, decay):
+    """The note's recurrent form (bucket states merged as t advances) against the
+    per-query walk over keys: two independent computations of the lift."""
+    raw = _raw(T, dk, dv, r_ab, r_kv, decay, seed=T + dk)
+    lam = workloads.loglinear_lambdas(1, 2, T, seed=T)
+    a = _run(raw, lam)
+    b = ll_oracle.loglinear_recurrent(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], lam)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_recurrent_form_single_level_weights():
+    """Weight 1 on one level l only: the output reads exactly the keys at level l
+    of each query (brute force over the closed-form level), for every l in use."""
+    T, dk, dv = 45, 4, 3
+    raw = _raw(T, dk, dv, 0, 1, "channel", seed=3)
+    L = ll_oracle.num_levels(T)
+    K = raw["K"][0, 0, :, 0].astype(np.float64)
+    V = raw["V"][0, 0, :, 0].astype(np.float64)
+    q = raw["q"][0, 0].astype(np.float64)
+    G = np.cumsum(raw["log_decay"][0, 0].astype(np.float64), axis=0)   # diagonal decay: Phi(t, s) = exp(G_t - G_s)
+    for l in range(L):
+        lam = np.zeros((1, 2, T, L))
+        lam[..., l] = 1.0
+        got = ll_oracle.loglinear_recurrent(raw["q"], raw["K"], raw["V"], raw["log_decay"], None, None, lam)[0, 0]
+        ref = np.zeros((T, dv))
+        for t in range(T):
+            for s in range(t + 1):
+                if (0 if s == t else (t ^ s).bit_length()) == l:
+                    ref[t] += (q[t] * np.exp(G[t] - G[s])) @ K[s] * V[s]
+        assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), l
