@@ -164,7 +164,25 @@ struct PrepCfg {
   static constexpr int DIB = 260;                // floats per inverse block (padded)
   static constexpr int R_DI = NB * DIB * 4;
   static constexpr int R_BT = MODE == kGeneric ? 0 : kC * 4;   // beta per token
-  static constexpr int LDS = R_XL + R_XR + R_LD + R_LP + R_MA + R_EG + R_DI + R_BT;
+  // d_k = 64 runs two resident workgroups per compute unit, so one chunk's
+  // VALU scaling overlaps the other's MFMA phases.  To fit two in LDS it keeps
+  // a compact layout: the diagonal blocks are inverted in place, and M_A is
+  // formed after the solve, into the region of L and B~ (dead by then):
+  //   [ L below diagonal | diagonal blocks = inverses | B~ ; Q~ | A~ ; K~ | exp(G_C) | beta ]
+  //   [ M_A (after the solve) ........................ )
+  static constexpr bool COMPACT = DK == 64 && RAB > 0;
+  static constexpr int O_LP = COMPACT ? 0 : R_XL + R_XR + R_LD;
+  static constexpr int O_LD = COMPACT ? R_LP : R_XL + R_XR;
+  static constexpr int O_XL = COMPACT ? R_LP + R_LD : 0;
+  static constexpr int O_XR = O_XL + R_XL;
+  static constexpr int O_MA = COMPACT ? 0 : O_LP + R_LP;
+  static constexpr int O_EG = COMPACT ? O_XR + R_XR : O_MA + R_MA;
+  static constexpr int O_DI = COMPACT ? O_LD : O_EG + R_EG;
+  static constexpr int O_BT = COMPACT ? O_EG + R_EG : O_DI + R_DI;
+  static constexpr int LDS = O_BT + R_BT;
+  static_assert(!COMPACT || R_MA <= R_LP + R_LD + NA * XRow<DK>::LD * 2,
+                "compact layout: M_A fits the region of L and B~");
+  static_assert(!COMPACT || DIB == LDB, "compact layout: inverses overwrite the diagonal blocks");
   static_assert(MODE == kGeneric || (MODE == kHdla && RAB == 2 && !SCAL) || (MODE == kGdn && RAB == 1 && SCAL),
                 "fused modes: HDLA is rank 2 per channel, Gated DeltaNet rank 1 scalar");
   static_assert(NO == NW && KT <= NW, "wave roles: one wave per channel piece");
@@ -196,14 +214,14 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
                 LDB = Cfg::LDB;
   constexpr int MT = Cfg::MT, KT = Cfg::KT, NCS = Cfg::NCS, NTILE = Cfg::NTILE;
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* Xl = reinterpret_cast<__bf16*>(smem);                             // [B~ ; Q~]
-  __bf16* Xr = reinterpret_cast<__bf16*>(smem + Cfg::R_XL);                 // [A~ ; K~]
-  float* Ldg = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR);      // diagonal blocks
-  __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD);  // L below diagonal
-  __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP);
-  float* eGC = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA);
-  float* Dinv = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG);
-  float* betas = reinterpret_cast<float*>(smem + Cfg::R_XL + Cfg::R_XR + Cfg::R_LD + Cfg::R_LP + Cfg::R_MA + Cfg::R_EG + Cfg::R_DI);
+  __bf16* Xl = reinterpret_cast<__bf16*>(smem + Cfg::O_XL);     // [B~ ; Q~]
+  __bf16* Xr = reinterpret_cast<__bf16*>(smem + Cfg::O_XR);     // [A~ ; K~]
+  float* Ldg = reinterpret_cast<float*>(smem + Cfg::O_LD);      // diagonal blocks
+  __bf16* Lpk = reinterpret_cast<__bf16*>(smem + Cfg::O_LP);    // L below diagonal
+  __bf16* MAs = reinterpret_cast<__bf16*>(smem + Cfg::O_MA);
+  float* eGC = reinterpret_cast<float*>(smem + Cfg::O_EG);
+  float* Dinv = reinterpret_cast<float*>(smem + Cfg::O_DI);
+  float* betas = reinterpret_cast<float*>(smem + Cfg::O_BT);
 
   const Problem& p = a.p;
   const int lane0 = threadIdx.x & 63;
@@ -569,9 +587,25 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     } else {
       // All waves share the Gram tiles; then the inversion and the X-wave
       // products run side by side.
+      if (Cfg::COMPACT) {
+        // Only the L tiles (rs <= cs < NB) here; M_A comes after the solve.
+        constexpr int NL = NB * (NB + 1) / 2;
+#pragma unroll 1
+        for (int idx = wave; idx < NL; idx += NW) {
+          int rs = 0, k = idx;
+          while (k >= NB - rs) {
+            k -= NB - rs;
+            ++rs;
+          }
+          bf16x8 af[DK / 32];
+          gram_a(rs, af);
+          gram_tile(rs, rs + k, af);
+        }
+      } else {
 #pragma unroll
-      for (int sl = 0; sl < Cfg::FULL_SLOTS; ++sl) gram_tile_at(wave + sl * NW, 0);
-      if (Cfg::FULL_SLOTS * NW + wave < NTILE) gram_tile_at(Cfg::FULL_SLOTS * NW + wave, 0);
+        for (int sl = 0; sl < Cfg::FULL_SLOTS; ++sl) gram_tile_at(wave + sl * NW, 0);
+        if (Cfg::FULL_SLOTS * NW + wave < NTILE) gram_tile_at(Cfg::FULL_SLOTS * NW + wave, 0);
+      }
       lds_barrier();
       load_b(nxt, lane);
       invert_blocks();
@@ -579,11 +613,9 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       lds_barrier();
     }
 
-    if (wave < KT) {
-      const int kt = wave;
-      // ---- P4: blocked forward substitution on this wave's columns:
-      //      WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
-      bf16x4 wx[NBA];
+    // ---- P4: blocked forward substitution on wave kt's columns:
+    //      WX_i = (I + L_ii)^{-1} (RHS_i - sum_{j<i} L_ij WX_j).
+    auto solve = [&](const int kt, bf16x4 (&wx)[NBA]) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         f32x4 acc;
@@ -613,7 +645,8 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         for (int e = 0; e < 4; ++e) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dF[e], acc[e], o, 0, 0, 0);
         wx[i] = to_bf16x4(f32x4{-o[0], -o[1], -o[2], -o[3]});   // -WX_i
       }
-
+    };
+    auto operator_tiles = [&](const int kt, const bf16x4 (&wx)[NBA]) {
       // ---- P5: operator tiles, transposed product: rows = this wave's input
       //      column tile, columns = output rows m (channels, then tokens):
       //      acc = sum_s WX[s][k] Bmat[m][s],  Bmat = [A~^T ; M_A].
@@ -658,6 +691,27 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         for (int jb = 0; jb < NB; jb += 2) acc = mfma32(cat(wx[jb], wx[jb + 1]), lds8(Brow + jb * 16), acc);
         store(DK / 16 + tt, acc);
       }
+    };
+    if (!Cfg::COMPACT) {
+      if (wave < KT) {
+        bf16x4 wx[NBA];
+        solve(wave, wx);
+        operator_tiles(wave, wx);
+      }
+    } else {
+      bf16x4 wx[NBA];
+      if (wave < KT) solve(wave, wx);
+      // M_A = Q~ A~^T into the region of L, the inverses and B~, which every
+      // wave's solve has finished reading after this barrier.  Wave w forms
+      // the four token-column tiles of row block w % NB.
+      static_assert(!Cfg::COMPACT || NW % NB == 0, "compact M_A phase: whole row blocks per wave");
+      lds_barrier();
+      bf16x8 af[DK / 32];
+      gram_a(wave % NB, af);
+#pragma unroll
+      for (int idx = wave; idx < NB * (kC / 16); idx += NW) gram_tile(wave % NB, NB + idx / NB, af);
+      lds_barrier();
+      if (wave < KT) operator_tiles(wave, wx);
     }
     // P5 reads Xl, Xr and M_A, which the next chunk overwrites.
     lds_barrier();
@@ -907,9 +961,16 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
   e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // One resident workgroup per compute unit, each walking a strided set of chunks.
+  // As many persistent workgroups as can be resident at once (one per compute
+  // unit, two with the compact d_k = 64 layout), each walking a strided set of
+  // chunks.
+  int per_cu = 1;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, Cfg::NT, Cfg::LDS);
+  if (e != hipSuccess) return e;
+  per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
   const int64_t jobs = p.BH * p.N;
-  const int64_t grid = jobs < cus ? jobs : cus;
+  const int64_t slots = static_cast<int64_t>(cus) * per_cu;
+  const int64_t grid = jobs < slots ? jobs : slots;
   hipLaunchKernelGGL((fast_prepare_kernel<DK, RAB, SCAL, MODE>), dim3(grid), dim3(Cfg::NT), Cfg::LDS, s, a);
   return hipGetLastError();
 }
