@@ -128,9 +128,9 @@ def source_hash(kernels):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernels, kernel, workload):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on the
-    current kernel source; else None."""
+def _counter_record(kernels, kernel, workload):
+    """The committed PMC record of a kernel, if it was taken on the current kernel
+    source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -140,7 +140,19 @@ def measured_traffic(kernels, kernel, workload):
         return None
     if not rec or rec.get("source_sha") != source_hash(kernels):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(kernels, kernel, workload):
+    """HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE) from the committed PMC summary."""
+    rec = _counter_record(kernels, kernel, workload)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def measured_mfma(kernels, kernel, workload):
+    """Executed MFMA flops and MFMA-busy fraction per launch from the committed PMC summary."""
+    rec = _counter_record(kernels, kernel, workload)
+    return None if rec is None else rec.get("mfma")
 
 
 def build_inputs(spec, torch, lattn, dev):
@@ -539,6 +551,12 @@ def roofline(spec, kernels, kernel_ms):
     }
     if traffic:
         out["traffic_over_algorithmic"] = round(traffic / work["bytes"], 3)
+    mf = measured_mfma(kernels, dom, spec.name)
+    if mf:
+        # counter view: the MFMA flops the kernel executed (bf16 + fp32) over its
+        # event-timed duration, against the bf16 peak, and the MFMA-busy fraction
+        out["mfma_counters"] = dict(mf, frac_of_bf16_peak=round(
+            (mf.get("bf16_gflop", 0.0) + mf.get("fp32_gflop", 0.0)) * 1e9 / sec / (PEAK["bf16_mfma_TFs"] * 1e12), 4))
     return out
 
 

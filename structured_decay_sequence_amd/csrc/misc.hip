@@ -33,7 +33,9 @@ struct StepArgs {
   void* out;
 };
 
-template <typename TI, int RPT>
+// RPT is the register bucket of rows per thread; EXACT means d_k == 4 * RPT,
+// so no row of the bucket is unused and every row loop runs unguarded.
+template <typename TI, int RPT, bool EXACT>
 __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(StepArgs a) {
   extern __shared__ float smem[];
   const Problem& p = a.p;
@@ -44,6 +46,8 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = c0 + lane;
   const bool col = c < dv;
+  const int cl = col ? c : dv - 1;        // loads of a column past d_v read a valid one
+  const int nm = EXACT ? RPT : dk / kStepWaves;   // rows per thread: d_k is a multiple of 16
   // LDS: q [dk], exp(l) [dk], K [r_kv][dk], A [r_ab][dk], B [r_ab][dk], then the
   // wave partials of B^T state [4][r_ab][64] and of the readout [4][64].
   float* qs = smem;
@@ -53,81 +57,99 @@ __global__ __launch_bounds__(kStepWaves * 64) void step_kernel(StepArgs a) {
   float* bs = as + r_ab * dk;
   float* wpart = bs + r_ab * dk;
   float* opart = wpart + kStepWaves * r_ab * kStepCols;
-  const TI* qp = static_cast<const TI*>(a.q) + static_cast<size_t>(bh) * dk;
-  const TI* kp = static_cast<const TI*>(a.k) + static_cast<size_t>(bh) * r_kv * dk;
-  const TI* Ap = static_cast<const TI*>(a.A) + static_cast<size_t>(bh) * r_ab * dk;
-  const TI* Bp = static_cast<const TI*>(a.B) + static_cast<size_t>(bh) * r_ab * dk;
-  for (int i = threadIdx.x; i < dk; i += kStepWaves * 64) {
-    qs[i] = Elem<TI>::load(qp, i);
-    es[i] = expf(p.scalar ? a.ld[bh] : a.ld[static_cast<size_t>(bh) * dk + i]);
-  }
-  for (int i = threadIdx.x; i < r_kv * dk; i += kStepWaves * 64) ks[i] = Elem<TI>::load(kp, i);
-  for (int i = threadIdx.x; i < r_ab * dk; i += kStepWaves * 64) {
-    as[i] = Elem<TI>::load(Ap, i);
-    bs[i] = Elem<TI>::load(Bp, i);
-  }
-  // This thread's state rows i = wave + 4m (m < RPT), column c.
-  float* st = a.state + static_cast<size_t>(bh) * dk * dv;
+  // Every global load is issued before any is waited on, so the step costs one
+  // memory round trip: this thread's state rows i = wave + 4m (m < nm) of
+  // column c first, then the token's vectors (thread t holds element t; d_k is
+  // at most the 256 threads), then V_t for this column.
+  float* srow = a.state + bh * dk * dv + static_cast<int64_t>(wave) * dv + cl;
+  const int64_t rstride = static_cast<int64_t>(kStepWaves) * dv;
   float S[RPT];
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = wave + kStepWaves * m;
-    S[m] = (col && i < dk) ? st[static_cast<size_t>(i) * dv + c] : 0.f;
+  for (int m = 0; m < RPT; ++m) S[m] = m < nm ? srow[m * rstride] : 0.f;
+  const int t = threadIdx.x < dk ? threadIdx.x : dk - 1;
+  // The loads are unconditional (rank indices clamped, rank-0 A and B read q
+  // instead) and the unused values are dropped afterwards, so no branch holds
+  // a load back.
+  const TI* qp = static_cast<const TI*>(a.q) + bh * dk;
+  const TI* kp = static_cast<const TI*>(a.k) + bh * r_kv * dk;
+  const int ra = r_ab > 0 ? r_ab : 1;
+  const TI* Ap = r_ab > 0 ? static_cast<const TI*>(a.A) + bh * r_ab * dk : qp;
+  const TI* Bp = r_ab > 0 ? static_cast<const TI*>(a.B) + bh * r_ab * dk : qp;
+  const float qv = Elem<TI>::load(qp, t);
+  const float lv = p.scalar ? a.ld[bh] : a.ld[bh * dk + t];
+  float kv[4], av[8], bv[8], vv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) kv[r] = Elem<TI>::load(kp, (r < r_kv ? r : r_kv - 1) * dk + t);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    av[r] = Elem<TI>::load(Ap, (r < ra ? r : ra - 1) * dk + t);
+    bv[r] = Elem<TI>::load(Bp, (r < ra ? r : ra - 1) * dk + t);
+  }
+  const TI* vp = static_cast<const TI*>(a.v) + bh * r_kv * dv + cl;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vv[r] = Elem<TI>::load(vp, static_cast<size_t>(r < r_kv ? r : r_kv - 1) * dv);
+  if (threadIdx.x < dk) {
+    qs[t] = qv;
+    es[t] = expf(lv);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r < r_kv) ks[r * dk + t] = kv[r];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (r < r_ab) {
+        as[r * dk + t] = av[r];
+        bs[r * dk + t] = bv[r];
+      }
   }
   __syncthreads();
-  // B^T state: partial over this thread's rows, one per decay rank.
+  // B^T state: partial over this thread's rows, per decay rank.
+  for (int r = 0; r < r_ab; ++r) {
+    const float* br = bs + r * dk + wave;
+    float w = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+      if (m < nm) w += br[kStepWaves * m] * S[m];
+    wpart[(wave * r_ab + r) * kStepCols + lane] = w;
+  }
+  __syncthreads();
+  // The update of this thread's rows: decay, the low-rank correction with the
+  // summed partials, the write.
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    if (m < nm) S[m] *= es[wave + kStepWaves * m];
   for (int r = 0; r < r_ab; ++r) {
     float w = 0.f;
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-      const int i = wave + kStepWaves * m;
-      if (i < dk) w += bs[r * dk + i] * S[m];
-    }
-    wpart[(wave * r_ab + r) * kStepCols + lane] = w;
+    for (int u = 0; u < kStepWaves; ++u) w += wpart[(u * r_ab + r) * kStepCols + lane];
+    const float* ar = as + r * dk + wave;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+      if (m < nm) S[m] -= ar[kStepWaves * m] * w;
   }
-  // V_t[r][c] for this column.
-  float vv[4];
-  const TI* vp = static_cast<const TI*>(a.v) + static_cast<size_t>(bh) * r_kv * dv;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) vv[r] = (r < r_kv && col) ? Elem<TI>::load(vp, static_cast<size_t>(r) * dv + c) : 0.f;
-  __syncthreads();
-  float W[8];
+  for (int r = 0; r < 4; ++r) {
+    if (r < r_kv) {
+      const float* kr = ks + r * dk + wave;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    W[r] = 0.f;
-    if (r < r_ab) {
-#pragma unroll
-      for (int w = 0; w < kStepWaves; ++w) W[r] += wpart[(w * r_ab + r) * kStepCols + lane];
+      for (int m = 0; m < RPT; ++m)
+        if (m < nm) S[m] += kr[kStepWaves * m] * vv[r];
     }
   }
-  // The update of this thread's rows, and the readout partial over them.
   float o = 0.f;
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = wave + kStepWaves * m;
-    if (i < dk) {
-      float s = es[i] * S[m];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r < r_ab) s -= as[r * dk + i] * W[r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r < r_kv) s += ks[r * dk + i] * vv[r];
-      S[m] = s;
-      o += s * qs[i];
-    }
-  }
+  for (int m = 0; m < RPT; ++m)
+    if (m < nm) o += S[m] * qs[wave + kStepWaves * m];
   opart[wave * kStepCols + lane] = o;
+  if (col) {
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = wave + kStepWaves * m;
-    if (col && i < dk) st[static_cast<size_t>(i) * dv + c] = S[m];
+    for (int m = 0; m < RPT; ++m)
+      if (m < nm) srow[m * rstride] = S[m];
   }
   __syncthreads();
   if (wave == 0 && col) {
     float r = 0.f;
 #pragma unroll
-    for (int w = 0; w < kStepWaves; ++w) r += opart[w * kStepCols + lane];
+    for (int u = 0; u < kStepWaves; ++u) r += opart[u * kStepCols + lane];
     Elem<TI>::store(static_cast<TI*>(a.out), static_cast<size_t>(bh) * dv + c, r);
   }
 }
@@ -255,15 +277,27 @@ __global__ __launch_bounds__(kThreads) void copy_state_kernel(int64_t n, const f
 
 }  // namespace
 
+template <typename TI, int RPT>
+void launch_step_rows(const Problem& p, const StepArgs& a, size_t lds, int64_t blocks, hipStream_t s) {
+  if (p.dk == kStepWaves * RPT)
+    hipLaunchKernelGGL((step_kernel<TI, RPT, true>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+  else
+    hipLaunchKernelGGL((step_kernel<TI, RPT, false>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+}
+
 template <typename TI>
 hipError_t launch_step_t(const Problem& p, const StepArgs& a, size_t lds, int64_t blocks, hipStream_t s) {
   // Rows per thread: the smallest bucket with 4 * RPT >= d_k.
-  if (p.dk <= 64)
-    hipLaunchKernelGGL((step_kernel<TI, 16>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+  if (p.dk <= 16)
+    launch_step_rows<TI, 4>(p, a, lds, blocks, s);
+  else if (p.dk <= 32)
+    launch_step_rows<TI, 8>(p, a, lds, blocks, s);
+  else if (p.dk <= 64)
+    launch_step_rows<TI, 16>(p, a, lds, blocks, s);
   else if (p.dk <= 128)
-    hipLaunchKernelGGL((step_kernel<TI, 32>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+    launch_step_rows<TI, 32>(p, a, lds, blocks, s);
   else
-    hipLaunchKernelGGL((step_kernel<TI, 64>), dim3(blocks), dim3(kStepWaves * 64), lds, s, a);
+    launch_step_rows<TI, 64>(p, a, lds, blocks, s);
   return hipGetLastError();
 }
 
