@@ -221,9 +221,9 @@ def fused_bytes(spec):
 
 # Query-conditioned composition (HLA note, "Method steps"): Gated DeltaNet, the
 # family the note builds on, at B=1, H=16, T=4096, d_k = d_v = 128, bf16 storage;
-# chunks of 128 tokens (the note uses 256; 128 is the largest chunk this path
-# takes); gates sigmoid(N(-4, 1.5)) with the note's threshold 0.1.
-HLA_WORKLOAD = dict(B=1, H=16, T=4096, dk=128, dv=128, chunk=128, mu=-4.0, theta=0.1)
+# gating chunks of 256 tokens (the note's length), each summarised from four
+# 64-token chunk operators; gates sigmoid(N(-4, 1.5)) with the note's threshold 0.1.
+HLA_WORKLOAD = dict(B=1, H=16, T=4096, dk=128, dv=128, chunk=256, mu=-4.0, theta=0.1)
 
 
 def hla_leg(torch, lattn, dev, steps, warmup):
@@ -257,11 +257,15 @@ def hla_leg(torch, lattn, dev, steps, warmup):
     N = -(-T // C)
     act = gates.reshape(Bb * H, N, C, N) >= w["theta"]          # [head, query chunk, query, chunk]
     pairs = sum(int(act[:, c, :, :c].any(axis=1).sum()) for c in range(N))
-    na, nk = C, C
+    # the pair products on fp32 MFMAs; the 64-token chunk operators and the
+    # gating-chunk summaries (scan products over d_k + d_v columns) on bf16 MFMAs
+    c64 = 64
+    n64 = -(-T // c64)
+    na, nk = c64, c64
     pair_mac = C * dk * (dk + dv)
-    prep_mac = (na + C) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (C + dk) * na * (dk + nk)
-    sum_mac = (dk + C) * nk * dv
-    flops = 2.0 * (pairs * pair_mac + Bb * H * N * (prep_mac + sum_mac))
+    prep_mac = (na + c64) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (c64 + dk) * na * (dk + nk)
+    gate_mac = (dk + c64) * (dk + nk) * (dk + dv)
+    flops = 2.0 * (pairs * pair_mac + Bb * H * n64 * (prep_mac + gate_mac))
     return {
         "entry": "lattn_hla_fwd",
         "workload": f"gdn B{Bb} H{H} T{T} d{dk} C{C} bf16, gates sigmoid(N({w['mu']}, 1.5)), theta {w['theta']}",
@@ -271,7 +275,8 @@ def hla_leg(torch, lattn, dev, steps, warmup):
         "active_pairs": pairs,
         "all_pairs": Bb * H * N * (N - 1) // 2,
         "gflop": round(flops / 1e9, 2),
-        "fp32_mfma_frac": round(flops / (ms / 1e3) / (PEAK["fp32_mfma_TFs"] * 1e12), 4),
+        "pair_gflop_fp32": round(2.0 * pairs * pair_mac / 1e9, 2),
+        "fp32_mfma_frac_pairs": round(2.0 * pairs * pair_mac / (ms / 1e3) / (PEAK["fp32_mfma_TFs"] * 1e12), 4),
     }
 
 

@@ -234,6 +234,17 @@ int fused_fwd(int family, const lattn_dims* dims, const void* q, const void* k, 
   return ok();
 }
 
+// The gating chunk of lattn_hla_fwd may also be 256 tokens (the HLA note's
+// length) where the bf16 path composes it from 64-token operators.
+int check_hla_chunk(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (chunk != 256) return check_chunk(chunk, r_ab, r_kv);
+  LATTN_TRY(check_chunk(64, r_ab, r_kv));
+  if (!lattn::hla_fast(make_problem(dims, r_ab, r_kv, chunk)))
+    return fail(LATTN_EUNSUPPORTED, "a 256-token gating chunk needs bf16 storage, d_k 64 or 128, r_kv 1, r_ab <= 2 "
+                "and d_v a multiple of 64 up to 128");
+  return LATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,7 +316,7 @@ size_t lattn_chunk_summaries_workspace_size(const lattn_dims* dims, int r_ab, in
 
 size_t lattn_hla_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
   if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
-      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+      check_hla_chunk(dims, r_ab, r_kv, chunk) != LATTN_OK)
     return 0;
   return lattn::hla_plan(make_problem(dims, r_ab, r_kv, chunk)).total_bytes;
 }
@@ -314,7 +325,9 @@ int lattn_hla_fwd(const lattn_dims* dims, const void* q, const void* k, const vo
                   const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
                   int chunk, const float* gates, float theta, void* out, void* workspace,
                   size_t workspace_bytes, hipStream_t stream) {
-  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  LATTN_TRY(check_dims(dims));
+  LATTN_TRY(check_hla_chunk(dims, r_ab, r_kv, chunk));
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk == 256 ? 64 : chunk));
   const bool need = dims->seqlen > 0;
   LATTN_TRY(check_ptr(q, "q", need));
   LATTN_TRY(check_ptr(gates, "gates", need));

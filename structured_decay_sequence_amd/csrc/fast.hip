@@ -948,6 +948,135 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
 }
 
+// ---------------------------------------------------------------------------
+// Gating-chunk summaries for the query-conditioned composition (HLA note,
+// "Method steps", steps 2 and 5): for a gating chunk of G consecutive 64-token
+// chunks, the exact affine pair of the whole gating chunk and, for each of its
+// queries, the operator on the incoming state and the output from a zero
+// state.  It is the scan's product run over the G chunks from the state
+// [I | 0], with d_k "transport" columns (value rows zero) next to the d_v
+// "write" columns (value rows V):
+//   [P' ; Qp] = M_x [P ; 0],      [W' ; Ow] = M_x [W ; V_x],
+// so after the G steps P = Acal_J and W = B_J, and the bottom rows of step x
+// are its queries' rows: Qp = Qbar_x P (the incoming-state operator) and
+// Ow = Qbar_x W + R_x V_x (the outputs from a zero state).  Operators come
+// straight from the prepare's fragment-ordered bf16 tiles; the state between
+// steps is rounded to bf16 (the MFMA operand), fp32 accumulate; the results
+// are stored in fp32: AT = Acal_J^T [dk][dk], BT = B_J^T [dv][dk], QB [L][dk],
+// OI [L][dv] per gating chunk.  One workgroup per (batch*head, gating chunk,
+// 64-column slice of the d_k + d_v columns), one wave per 16-row tile of M_x.
+struct FastGateArgs {
+  Problem p;        // the 64-token problem: N = ceil(T / 64)
+  int G;            // 64-token chunks per gating chunk
+  int64_t NL;       // gating chunks per (batch, head)
+  const __bf16* M;  // fragment-ordered chunk operators
+  const __bf16* v;  // V [BH, T, dv]
+  float* AT;
+  float* BT;
+  float* QB;
+  float* OI;
+};
+
+template <int DK>
+struct GateCfg {
+  static constexpr int KIN = DK + kNK;
+  static constexpr int MT = (DK + kC) / 16;
+  static constexpr int KP = KIN / 32;
+  static constexpr int NT = 64 * MT;
+  static constexpr int LDX = KIN + 16;      // padded X^T row (bf16), as in the scan
+  static constexpr int XBUF = 64 * LDX;
+  static constexpr int LDS = 2 * XBUF * 2;
+};
+
+template <int DK>
+__global__ __launch_bounds__(GateCfg<DK>::NT) void fast_gate_kernel(FastGateArgs a) {
+  using Cfg = GateCfg<DK>;
+  constexpr int KP = Cfg::KP, LDX = Cfg::LDX, XBUF = Cfg::XBUF, NT = Cfg::NT, DKT = DK / 16;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16* X0 = reinterpret_cast<__bf16*>(smem);
+  const Problem& p = a.p;
+  const int dv = p.dv, G = a.G;
+  const int NS = (DK + dv) / 64;
+  const int s = static_cast<int>(blockIdx.x % NS);
+  const int64_t job = blockIdx.x / NS;            // (batch*head, gating chunk)
+  const int64_t bh = job / a.NL, J = job % a.NL;
+  const int L = G * kC;
+  const bool tr = s * 64 < DK;                    // transport columns (else write columns)
+  const int col0 = tr ? s * 64 : s * 64 - DK;     // first column of the slice in P or W
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t j0 = J * G;
+  const int nsub = static_cast<int>(p.N - j0 < G ? p.N - j0 : G);
+  const size_t MSZ = static_cast<size_t>(Cfg::MT) * (Cfg::KIN / 16) * 256;
+  const __bf16* Mbh = a.M + static_cast<size_t>(bh) * p.N * MSZ;
+  // Initial X^T in both buffers: state [I | 0] of this slice, value rows zero.
+  for (int it = tid; it < 2 * XBUF; it += NT) X0[it] = (__bf16)0.f;
+  __syncthreads();
+  if (tr && tid < 64) {
+    const int c = tid;   // local column; state row col0 + c holds 1
+    X0[c * LDX + kperm(col0 + c)] = (__bf16)1.f;
+  }
+  // V rows of chunk jj (write slices only) into buffer X, rows past the chunk's end zero.
+  auto put_v = [&](__bf16* X, int64_t jj) {
+    if (tr) return;
+    const int64_t t0 = jj * kC;
+    const int n = static_cast<int>(p.T - t0 < kC ? p.T - t0 : kC);
+    if (tid < kC * 8) {
+      const int t = tid / 8, cg = tid % 8;   // token t, columns 8 cg .. 8 cg + 7 of the slice
+      bf16x8 w;
+      if (t < n) {
+        w = *reinterpret_cast<const bf16x8*>(a.v + (static_cast<size_t>(bh) * p.T + t0 + t) * dv + col0 + 8 * cg);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) X[(8 * cg + e) * LDX + kperm(DK + t)] = w[e];
+    }
+  };
+  put_v(X0, j0);
+  __syncthreads();
+  const int mt = wave;
+  for (int x = 0; x < nsub; ++x) {
+    const __bf16* Xc = X0 + (x & 1) * XBUF;
+    __bf16* Xn = X0 + ((x + 1) & 1) * XBUF;
+    const __bf16* Mj = Mbh + static_cast<size_t>(j0 + x) * MSZ;
+    bf16x8 mf[KP];
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) mf[kp] = *reinterpret_cast<const bf16x8*>(Mj + ((mt * KP + kp) * 64 + lane) * 8);
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = mfma32(mf[kp], lds8(Xc + (nt * 16 + lr) * LDX + kp * 32 + 8 * lg), acc[nt]);
+    }
+    const bool last = x + 1 == nsub;
+    if (mt < DKT) {
+      // new state rows mt*16 + 4 lg + e of columns c
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int c = nt * 16 + lr;
+        if (!last) *reinterpret_cast<bf16x4*>(Xn + c * LDX + kperm(mt * 16 + 4 * lg)) = to_bf16x4(acc[nt]);
+        else if (tr) *reinterpret_cast<f32x4*>(a.AT + (static_cast<size_t>(job) * DK + col0 + c) * DK + mt * 16 + 4 * lg) = acc[nt];
+        else *reinterpret_cast<f32x4*>(a.BT + (static_cast<size_t>(job) * dv + col0 + c) * DK + mt * 16 + 4 * lg) = acc[nt];
+      }
+    } else {
+      // query rows: token x*64 + (mt - DKT)*16 + 4 lg + e of the gating chunk
+      float* dst = tr ? a.QB + static_cast<size_t>(job) * L * DK : a.OI + static_cast<size_t>(job) * L * dv;
+      const int ld = tr ? DK : dv;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[static_cast<size_t>(x * kC + (mt - DKT) * 16 + 4 * lg + e) * ld + col0 + nt * 16 + lr] = acc[nt][e];
+    }
+    if (!last) put_v(Xn, j0 + x + 1);
+    __syncthreads();
+  }
+}
+
 template <int DK, int RAB, bool SCAL, int MODE>
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
                        const void* A, const void* B, const float* beta, void* M, hipStream_t s) {
@@ -1045,6 +1174,26 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
   if (p.dk == 128) return launch_scan<128, 32, 4, 2>(p, workspace, v, out, Sfin, S0, s);
   if (p.dk == 64) return launch_scan<64, 16, 4, 4>(p, workspace, v, out, Sfin, S0, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t fast_gate_summaries(const Problem& p, int G, const void* workspace, const void* v, float* AT, float* BT,
+                               float* QB, float* OI, hipStream_t s) {
+  if (p.BH * p.N == 0) return hipSuccess;
+  if (G < 1 || G > 4 || p.dv % 64 != 0 || p.r_kv != 1) return hipErrorInvalidValue;
+  const int64_t NL = (p.N + G - 1) / G;
+  FastGateArgs a{p, G, NL, static_cast<const __bf16*>(workspace), static_cast<const __bf16*>(v), AT, BT, QB, OI};
+  const int64_t blocks = p.BH * NL * ((p.dk + p.dv) / 64);
+  if (p.dk == 128) {
+    const void* fn = reinterpret_cast<const void*>(fast_gate_kernel<128>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, GateCfg<128>::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fast_gate_kernel<128>, dim3(blocks), dim3(GateCfg<128>::NT), GateCfg<128>::LDS, s, a);
+  } else if (p.dk == 64) {
+    hipLaunchKernelGGL(fast_gate_kernel<64>, dim3(blocks), dim3(GateCfg<64>::NT), GateCfg<64>::LDS, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace lattn

@@ -17,6 +17,15 @@
 // which is one C x d_k x (d_k + d_v) product per (query chunk, history chunk)
 // pair.  A history chunk whose gates are all below the threshold (taken as
 // zero) leaves R and O unchanged and is skipped.
+//
+// The gating chunk may be longer than the summary chunk: on the bf16 path a
+// gating chunk of L = 64, 128 or 256 tokens is summarised from 1, 2 or 4
+// consecutive 64-token chunk operators by fast_gate_summaries (bf16 MFMAs on
+// the prepare's fragment-ordered tiles); elsewhere the summary chunk is the
+// gating chunk (at most 128 tokens) and hla_summaries_kernel reads the general
+// path's fp32 operators.  Either way the composition below sees, per gating
+// chunk, Acal^T, B^T, the queries' incoming-state operator QB and their
+// zero-state outputs OI.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_f32.hpp"
@@ -30,10 +39,11 @@ struct HlaSumArgs {
   const void* v;
   float* AT;        // Acal_j^T   [BH, N, dk, dk]
   float* BT;        // B_j^T      [BH, N, dv, dk]
+  float* QB;        // Qbar_j     [BH, N, C, dk]
   float* OI;        // R_j V_j    [BH, N, C, dv]
 };
 
-// Per chunk: Acal^T, and [Z ; R] V_j with the top rows stored transposed.
+// Per chunk: Acal^T, Qbar, and [Z ; R] V_j with the top rows stored transposed.
 template <typename TI>
 __global__ __launch_bounds__(256) void hla_summaries_kernel(HlaSumArgs a) {
   const Problem& p = a.p;
@@ -50,6 +60,8 @@ __global__ __launch_bounds__(256) void hla_summaries_kernel(HlaSumArgs a) {
   const TI* vp = static_cast<const TI*>(a.v);
   float* AT = a.AT + static_cast<size_t>(job) * dk * dk;
   for (int e = tid; e < dk * dk; e += 256) AT[e] = Mj[static_cast<size_t>(e % dk) * ncol + e / dk];
+  float* QB = a.QB + static_cast<size_t>(job) * C * dk;
+  for (int e = tid; e < C * dk; e += 256) QB[e] = Mj[static_cast<size_t>(dk + e / dk) * ncol + e % dk];
   for (int tile = wave; tile < MT * CT; tile += 4) {
     const int rt = tile / CT, ct = tile % CT;
     const float* arow = Mj + static_cast<size_t>(rt * 16 + lr) * ncol + dk + 4 * lg;
@@ -77,8 +89,8 @@ __global__ __launch_bounds__(256) void hla_summaries_kernel(HlaSumArgs a) {
 }
 
 struct HlaArgs {
-  Problem p;
-  const float* M;
+  Problem p;        // C is the gating chunk, N the gating chunks per (batch, head)
+  const float* QB;
   const float* AT;
   const float* BT;
   const float* OI;
@@ -87,18 +99,18 @@ struct HlaArgs {
   void* out;
 };
 
-constexpr int kHlaThreads = 512;   // eight waves
-constexpr int kHlaTiles = 8;       // tiles of R and of O per wave: (C/16)(d/16) <= 64
+constexpr int kHlaTiles = 8;       // tiles of R and of O per wave: (C/16)(d/16) <= 8 NWV
 
 // One workgroup per (batch*head, query chunk c), longest walks first.  R
-// (C x d_k, fp32) lives in LDS; wave w owns O tiles w, w+8, ... (in registers
+// (C x d_k, fp32) lives in LDS; wave w owns O tiles w, w+NWV, ... (in registers
 // for the whole walk) and the same R tiles, whose new values are written back
-// after a barrier.
-template <typename TI>
-__global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
+// after a barrier.  NWV = 8 waves for chunks up to 128 tokens, 16 for 256.
+template <typename TI, int NWV>
+__global__ __launch_bounds__(64 * NWV) void hla_compose_kernel(HlaArgs a) {
+  constexpr int kHlaThreads = 64 * NWV;
   extern __shared__ __align__(16) float Rs[];
   const Problem& p = a.p;
-  const int dk = p.dk, dv = p.dv, C = p.C, ncol = p.mcols();
+  const int dk = p.dk, dv = p.dv, C = p.C;
   const int N = static_cast<int>(p.N);
   const int LDR = dk + 4;
   // Query chunk c walks c history chunks: the workgroups are dispatched
@@ -113,25 +125,27 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int nrt = C / 16, nctv = dv / 16, nctk = dk / 16;
   const int nO = nrt * nctv, nR = nrt * nctk;
-  const float* Mc = a.M + static_cast<size_t>(job) * p.mrows() * ncol;
+  const float* Qc = a.QB + static_cast<size_t>(job) * C * dk;
   const float* gb = a.gates + static_cast<size_t>(bh * p.T + t0) * N;   // row t: gb[t * N + j]
   const float theta = a.theta;
 
   for (int e = tid; e < C * dk; e += kHlaThreads) {
     const int t = e / dk, i = e % dk;
-    Rs[t * LDR + i] = Mc[static_cast<size_t>(dk + t) * ncol + i];   // Qbar_c
+    Rs[t * LDR + i] = t < n ? Qc[static_cast<size_t>(t) * dk + i] : 0.f;   // Qbar_c
   }
   f32x4 O[kHlaTiles], Rn[kHlaTiles];
 #pragma unroll
   for (int u = 0; u < kHlaTiles; ++u) {
     O[u] = zero4();
     Rn[u] = zero4();
-    const int o = wave + 8 * u;
+    const int o = wave + NWV * u;
     if (o < nO) {
       const int rt = o / nctv, ct = o % nctv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        O[u][e] = a.OI[(static_cast<size_t>(job) * C + rt * 16 + 4 * lg + e) * dv + ct * 16 + lr];
+      for (int e = 0; e < 4; ++e) {
+        const int t = rt * 16 + 4 * lg + e;
+        O[u][e] = t < n ? a.OI[(static_cast<size_t>(job) * C + t) * dv + ct * 16 + lr] : 0.f;
+      }
     }
   }
   float* gs = Rs + C * LDR;   // gates of the current history chunk per row (below theta, or past the end: 0)
@@ -142,7 +156,7 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
   // (Acal_j^T fragments).  The next task's fragments are loaded while the
   // current task's MFMAs run.
   auto task = [&](const float* ATj, const float* BTj, int k, int& rt, int& ct, const float*& bp) {
-    const int idx = wave + 8 * (k >> 1);
+    const int idx = wave + NWV * (k >> 1);
     if ((k & 1) == 0) {
       if (idx >= nO) return false;
       rt = idx / nctv;
@@ -205,7 +219,7 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
     __syncthreads();   // every product has read R
 #pragma unroll
     for (int u = 0; u < kHlaTiles; ++u) {
-      const int r = wave + 8 * u;
+      const int r = wave + NWV * u;
       if (r < nR) {
         const int rt = r / nctk, ct = r % nctk;
 #pragma unroll
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(kHlaThreads) void hla_compose_kernel(HlaArgs a) {
   TI* op = static_cast<TI*>(a.out);
 #pragma unroll
   for (int u = 0; u < kHlaTiles; ++u) {
-    const int o = wave + 8 * u;
+    const int o = wave + NWV * u;
     if (o < nO) {
       const int rt = o / nctv, ct = o % nctv;
 #pragma unroll
@@ -234,16 +248,33 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-bool hla_supported(const Problem& p) { return p.dk <= 128 && p.dv <= 128; }
+// The bf16 path: the 64-token operators of the MFMA prepare, summarised per
+// gating chunk of 64, 128 or 256 tokens.
+bool hla_fast(const Problem& p) {
+  return p.bf16 && (p.dk == 64 || p.dk == 128) && p.r_kv == 1 && p.r_ab >= 0 && p.r_ab <= 2 && p.dv % 64 == 0 &&
+         p.dv <= 128 && (p.C == 64 || p.C == 128 || p.C == 256);
+}
+
+Problem hla_sub_problem(const Problem& p) {
+  Problem q = p;
+  q.C = 64;
+  q.N = (p.T + 63) / 64;
+  return q;
+}
+
+bool hla_supported(const Problem& p) {
+  return p.dk <= 128 && p.dv <= 128 && (p.C <= 128 || hla_fast(p));
+}
 
 HlaPlan hla_plan(const Problem& p) {
   HlaPlan h{};
-  const size_t chunks = static_cast<size_t>(p.BH * p.N);
-  h.gen_bytes = align256(f32_operators_bytes(p));
+  const size_t chunks = static_cast<size_t>(p.BH * p.N);   // gating chunks
+  h.gen_bytes = align256(hla_fast(p) ? fast_workspace_bytes(hla_sub_problem(p)) : f32_operators_bytes(p));
   h.at_bytes = align256(chunks * p.dk * p.dk * sizeof(float));
   h.bt_bytes = align256(chunks * p.dv * p.dk * sizeof(float));
+  h.qb_bytes = align256(chunks * p.C * p.dk * sizeof(float));
   h.oi_bytes = align256(chunks * p.C * p.dv * sizeof(float));
-  h.total_bytes = h.gen_bytes + h.at_bytes + h.bt_bytes + h.oi_bytes;
+  h.total_bytes = h.gen_bytes + h.at_bytes + h.bt_bytes + h.qb_bytes + h.oi_bytes;
   return h;
 }
 
@@ -256,28 +287,48 @@ hipError_t launch_hla(const Problem& p, const void* q, const void* k, const floa
   char* ws = static_cast<char*>(workspace);
   float* AT = reinterpret_cast<float*>(ws + h.gen_bytes);
   float* BT = reinterpret_cast<float*>(ws + h.gen_bytes + h.at_bytes);
-  float* OI = reinterpret_cast<float*>(ws + h.gen_bytes + h.at_bytes + h.bt_bytes);
-  const float* M = nullptr;   // fp32 chunk operators inside the workspace
-  hipError_t e = f32_operators(p, q, k, ld, A, B, workspace, &M, s);
+  float* QB = reinterpret_cast<float*>(ws + h.gen_bytes + h.at_bytes + h.bt_bytes);
+  float* OI = reinterpret_cast<float*>(ws + h.gen_bytes + h.at_bytes + h.bt_bytes + h.qb_bytes);
+  hipError_t e;
+  if (hla_fast(p)) {
+    const Problem ps = hla_sub_problem(p);
+    e = fast_prepare(ps, q, k, ld, A, B, workspace, s);
+    if (e == hipSuccess) e = fast_gate_summaries(ps, p.C / 64, workspace, v, AT, BT, QB, OI, s);
+  } else {
+    const float* M = nullptr;   // fp32 chunk operators inside the workspace
+    e = f32_operators(p, q, k, ld, A, B, workspace, &M, s);
+    if (e == hipSuccess) {
+      HlaSumArgs sa{p, M, v, AT, BT, QB, OI};
+      const dim3 grid(static_cast<unsigned>(p.BH * p.N));
+      if (p.bf16)
+        hipLaunchKernelGGL(hla_summaries_kernel<bf16_raw>, grid, dim3(256), 0, s, sa);
+      else
+        hipLaunchKernelGGL(hla_summaries_kernel<float>, grid, dim3(256), 0, s, sa);
+      e = hipGetLastError();
+    }
+  }
   if (e != hipSuccess) return e;
-  HlaSumArgs sa{p, M, v, AT, BT, OI};
-  const dim3 grid(static_cast<unsigned>(p.BH * p.N));
-  if (p.bf16)
-    hipLaunchKernelGGL(hla_summaries_kernel<bf16_raw>, grid, dim3(256), 0, s, sa);
-  else
-    hipLaunchKernelGGL(hla_summaries_kernel<float>, grid, dim3(256), 0, s, sa);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  HlaArgs ca{p, M, AT, BT, OI, gates, theta, out};
+  HlaArgs ca{p, QB, AT, BT, OI, gates, theta, out};
   const size_t lds = static_cast<size_t>(p.C) * (p.dk + 4 + 1) * sizeof(float);   // R, then the row gates
-  const void* fn = p.bf16 ? reinterpret_cast<const void*>(hla_compose_kernel<bf16_raw>)
-                          : reinterpret_cast<const void*>(hla_compose_kernel<float>);
+  const dim3 grid(static_cast<unsigned>(p.BH * p.N));
+  const bool wide = p.C > 128;
+  const void* fn = wide ? (p.bf16 ? reinterpret_cast<const void*>(hla_compose_kernel<bf16_raw, 16>)
+                                  : reinterpret_cast<const void*>(hla_compose_kernel<float, 16>))
+                        : (p.bf16 ? reinterpret_cast<const void*>(hla_compose_kernel<bf16_raw, 8>)
+                                  : reinterpret_cast<const void*>(hla_compose_kernel<float, 8>));
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  if (p.bf16)
-    hipLaunchKernelGGL(hla_compose_kernel<bf16_raw>, grid, dim3(kHlaThreads), lds, s, ca);
-  else
-    hipLaunchKernelGGL(hla_compose_kernel<float>, grid, dim3(kHlaThreads), lds, s, ca);
+  if (wide) {
+    if (p.bf16)
+      hipLaunchKernelGGL((hla_compose_kernel<bf16_raw, 16>), grid, dim3(1024), lds, s, ca);
+    else
+      hipLaunchKernelGGL((hla_compose_kernel<float, 16>), grid, dim3(1024), lds, s, ca);
+  } else {
+    if (p.bf16)
+      hipLaunchKernelGGL((hla_compose_kernel<bf16_raw, 8>), grid, dim3(512), lds, s, ca);
+    else
+      hipLaunchKernelGGL((hla_compose_kernel<float, 8>), grid, dim3(512), lds, s, ca);
+  }
   return hipGetLastError();
 }
 

@@ -50,6 +50,13 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s);
+// Gating-chunk summaries for the query-conditioned composition, from the bf16
+// prepare's operators of the 64-token problem p: per gating chunk of G
+// consecutive chunks (G <= 4), Acal^T [dk][dk], B^T [dv][dk], the queries'
+// incoming-state operator QB [64 G][dk] and zero-state outputs OI [64 G][dv],
+// all fp32.  v is V [BH, T, dv] (r_kv = 1, d_v a multiple of 64).
+hipError_t fast_gate_summaries(const Problem& p, int G, const void* workspace, const void* v, float* AT, float* BT,
+                               float* QB, float* OI, hipStream_t s);
 // Fused-parameter prepare (family 1: HDLA from log-lambda and beta, rank 2,
 // per-channel decay; family 2: Gated DeltaNet from g and beta, rank 1,
 // scalar decay).  The operator's value columns carry beta, so the scan reads
@@ -65,12 +72,16 @@ size_t f32_operators_bytes(const Problem& p);
 hipError_t f32_operators(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
                          const void* B, void* workspace, const float** M, hipStream_t s);
 
-// Query-conditioned composition (HLA) on the general path's chunk operators:
-// d_k, d_v <= 128.  Workspace: the general path's, then Acal^T, B^T and the
-// chunk-local outputs of every chunk (fp32).
+// Query-conditioned composition (HLA): d_k, d_v <= 128; p.C is the gating
+// chunk.  Workspace: the chunk operators (bf16 64-token ones, or the general
+// path's fp32 ones), then per gating chunk Acal^T, B^T, the queries'
+// incoming-state operator and zero-state outputs (fp32).
 struct HlaPlan {
-  size_t gen_bytes, at_bytes, bt_bytes, oi_bytes, total_bytes;
+  size_t gen_bytes, at_bytes, bt_bytes, qb_bytes, oi_bytes, total_bytes;
 };
+// Gating chunks of 64, 128 or 256 tokens on the bf16 path (from the 64-token
+// MFMA operators), else a gating chunk equal to the summary chunk (<= 128).
+bool hla_fast(const Problem& p);
 bool hla_supported(const Problem& p);
 HlaPlan hla_plan(const Problem& p);
 hipError_t launch_hla(const Problem& p, const void* q, const void* k, const float* ld, const void* A,

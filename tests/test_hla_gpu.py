@@ -38,6 +38,13 @@ CASES = [
     (1, 2, 130, 64, 64, 2, 1, 64, "bf16", "channel", -2.0),      # operators from the bf16 MFMA prepare
     (1, 1, 200, 128, 128, 2, 1, 64, "bf16", "channel", -2.0),    # the same at d_k = 128
     (1, 1, 161, 32, 128, 1, 1, 32, "bf16", "scalar", -3.0),
+    # gating chunks of 128 and 256 tokens on the bf16 path: composed from 2 or 4
+    # 64-token operators (the HLA note's length is 256), ragged tails
+    (1, 2, 600, 128, 128, 2, 1, 256, "bf16", "channel", -2.0),
+    (1, 1, 300, 64, 64, 1, 1, 256, "bf16", "scalar", -3.0),
+    (2, 1, 330, 64, 128, 2, 1, 128, "bf16", "channel", -1.0),
+    (1, 1, 200, 128, 64, 0, 1, 128, "bf16", "channel", -2.0),
+    (1, 1, 100, 64, 64, 2, 1, 256, "bf16", "channel", 0.0),
 ]
 
 
@@ -73,6 +80,14 @@ def test_hla_gates_below_threshold_are_chunk_local():
     assert rel_err(out, zero) <= TOL["fp32"]
 
 
+def test_hla_256_token_chunks_need_the_bf16_path():
+    raw = workloads.generic_raw(1, 1, 300, 64, 64, 1, 1, "fp32", "channel", seed=0)
+    gates = workloads.hla_gates(1, 1, 300, 256, seed=0)
+    with pytest.raises(lattn.LattnError) as ei:
+        _gpu(raw, gates, "fp32", 256, 0.1)
+    assert ei.value.status == -2
+
+
 def test_hla_rejects_wide_heads():
     raw = workloads.generic_raw(1, 1, 32, 256, 64, 1, 1, "fp32", "channel", seed=0)
     gates = workloads.hla_gates(1, 1, 32, 16, seed=0)
@@ -83,11 +98,11 @@ def test_hla_rejects_wide_heads():
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_hla_bench_workload_two_heads():
-    """The bench's HLA workload (Gated DeltaNet, B1 H16 T4096 d128, C 128, bf16) in
-    the launch configuration bench.py times.  On the first and last head: every
-    query of four whole query chunks (the first, the second, a middle and the
-    last) and every 16th query elsewhere, against the oracle on its own decay
-    operands (the fp64 Gated DeltaNet rewrite rounded to bf16)."""
+    """The bench's HLA workload (Gated DeltaNet, B1 H16 T4096 d128, 256-token gating
+    chunks, bf16) in the launch configuration bench.py times.  On the first and
+    last head: every query of four whole gating chunks (the first, the second, a
+    middle and the last) and every 16th query elsewhere, against the oracle on
+    its own decay operands (the fp64 Gated DeltaNet rewrite rounded to bf16)."""
     import bench
     w = bench.HLA_WORKLOAD
     Bb, H, T, dk, dv, C = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["chunk"]
@@ -100,8 +115,8 @@ def test_hla_bench_workload_two_heads():
     torch.cuda.synchronize()
     out = host(out)
     N = T // C
-    qs = sorted(set(range(0, C)) | set(range(C, 2 * C)) | set(range(15 * C, 16 * C)) | set(range((N - 1) * C, T))
-                | set(range(0, T, 16)))
+    qs = sorted(set(range(0, C)) | set(range(C, 2 * C)) | set(range((N // 2) * C, (N // 2 + 1) * C))
+                | set(range((N - 1) * C, T)) | set(range(0, T, 16)))
     for h in (0, H - 1):
         sl = lambda x: x[:, h:h + 1]
         g, rA, rB, rK, rV = oracle.gdn_to_generic(sl(raw["k"]), sl(raw["v"]), sl(raw["g"]), sl(raw["beta"]))
