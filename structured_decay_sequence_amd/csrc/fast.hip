@@ -961,9 +961,10 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
 // are its queries' rows: Qp = Qbar_x P (the incoming-state operator) and
 // Ow = Qbar_x W + R_x V_x (the outputs from a zero state).  Operators come
 // straight from the prepare's fragment-ordered bf16 tiles; the state between
-// steps is rounded to bf16 (the MFMA operand), fp32 accumulate; the results
-// are stored in fp32: AT = Acal_J^T [dk][dk], BT = B_J^T [dv][dk], QB [L][dk],
-// OI [L][dv] per gating chunk.  One workgroup per (batch*head, gating chunk,
+// steps is rounded to bf16 (the MFMA operand), fp32 accumulate.  Stored per
+// gating chunk: AT = Acal_J^T [dk][dk] and BT = B_J^T [dv][dk] in bf16 (the B
+// operands of the composition's bf16 products), QB [L][dk] and OI [L][dv] in
+// fp32.  One workgroup per (batch*head, gating chunk,
 // 64-column slice of the d_k + d_v columns), one wave per 16-row tile of M_x.
 struct FastGateArgs {
   Problem p;        // the 64-token problem: N = ceil(T / 64)
@@ -971,8 +972,8 @@ struct FastGateArgs {
   int64_t NL;       // gating chunks per (batch, head)
   const __bf16* M;  // fragment-ordered chunk operators
   const __bf16* v;  // V [BH, T, dv]
-  float* AT;
-  float* BT;
+  __bf16* AT;
+  __bf16* BT;
   float* QB;
   float* OI;
 };
@@ -1059,8 +1060,8 @@ __global__ __launch_bounds__(GateCfg<DK>::NT) void fast_gate_kernel(FastGateArgs
       for (int nt = 0; nt < 4; ++nt) {
         const int c = nt * 16 + lr;
         if (!last) *reinterpret_cast<bf16x4*>(Xn + c * LDX + kperm(mt * 16 + 4 * lg)) = to_bf16x4(acc[nt]);
-        else if (tr) *reinterpret_cast<f32x4*>(a.AT + (static_cast<size_t>(job) * DK + col0 + c) * DK + mt * 16 + 4 * lg) = acc[nt];
-        else *reinterpret_cast<f32x4*>(a.BT + (static_cast<size_t>(job) * dv + col0 + c) * DK + mt * 16 + 4 * lg) = acc[nt];
+        else if (tr) *reinterpret_cast<bf16x4*>(a.AT + (static_cast<size_t>(job) * DK + col0 + c) * DK + mt * 16 + 4 * lg) = to_bf16x4(acc[nt]);
+        else *reinterpret_cast<bf16x4*>(a.BT + (static_cast<size_t>(job) * dv + col0 + c) * DK + mt * 16 + 4 * lg) = to_bf16x4(acc[nt]);
       }
     } else {
       // query rows: token x*64 + (mt - DKT)*16 + 4 lg + e of the gating chunk
@@ -1176,12 +1177,13 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
   return hipErrorInvalidValue;
 }
 
-hipError_t fast_gate_summaries(const Problem& p, int G, const void* workspace, const void* v, float* AT, float* BT,
+hipError_t fast_gate_summaries(const Problem& p, int G, const void* workspace, const void* v, void* AT, void* BT,
                                float* QB, float* OI, hipStream_t s) {
   if (p.BH * p.N == 0) return hipSuccess;
   if (G < 1 || G > 4 || p.dv % 64 != 0 || p.r_kv != 1) return hipErrorInvalidValue;
   const int64_t NL = (p.N + G - 1) / G;
-  FastGateArgs a{p, G, NL, static_cast<const __bf16*>(workspace), static_cast<const __bf16*>(v), AT, BT, QB, OI};
+  FastGateArgs a{p, G, NL, static_cast<const __bf16*>(workspace), static_cast<const __bf16*>(v),
+                 static_cast<__bf16*>(AT), static_cast<__bf16*>(BT), QB, OI};
   const int64_t blocks = p.BH * NL * ((p.dk + p.dv) / 64);
   if (p.dk == 128) {
     const void* fn = reinterpret_cast<const void*>(fast_gate_kernel<128>);

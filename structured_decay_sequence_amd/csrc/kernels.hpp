@@ -52,10 +52,10 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
                      const float* S0, hipStream_t s);
 // Gating-chunk summaries for the query-conditioned composition, from the bf16
 // prepare's operators of the 64-token problem p: per gating chunk of G
-// consecutive chunks (G <= 4), Acal^T [dk][dk], B^T [dv][dk], the queries'
-// incoming-state operator QB [64 G][dk] and zero-state outputs OI [64 G][dv],
-// all fp32.  v is V [BH, T, dv] (r_kv = 1, d_v a multiple of 64).
-hipError_t fast_gate_summaries(const Problem& p, int G, const void* workspace, const void* v, float* AT, float* BT,
+// consecutive chunks (G <= 4), Acal^T [dk][dk] and B^T [dv][dk] in bf16, the
+// queries' incoming-state operator QB [64 G][dk] and zero-state outputs OI
+// [64 G][dv] in fp32.  v is V [BH, T, dv] (r_kv = 1, d_v a multiple of 64).
+hipError_t fast_gate_summaries(const Problem& p, int G, const void* workspace, const void* v, void* AT, void* BT,
                                float* QB, float* OI, hipStream_t s);
 // Fused-parameter prepare (family 1: HDLA from log-lambda and beta, rank 2,
 // per-channel decay; family 2: Gated DeltaNet from g and beta, rank 1,

@@ -152,3 +152,19 @@ def test_hla_nan_gate_propagates_like_the_oracle():
     assert np.isnan(out[0, 0, 100]).all()
     keep = ~np.isnan(ref)
     assert rel_err(out[keep], ref[keep]) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_hla_bf16_all_gates_one_over_many_gating_chunks(dk, dv):
+    """Gates all 1 over eight 256-token gating chunks on the bf16 path: every query's
+    history is the full exact prefix, so the output is the plain recurrence (the
+    C oracle).  This stresses the composition's carried R over seven history
+    chunks, each step a bf16 product with fp32 accumulation."""
+    Bb, H, T, C = 1, 2, 2048, 256
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, 2, 1, "bf16", "channel", seed=13)
+    gates = np.ones((Bb, H, T, T // C), dtype=np.float32)
+    out = _gpu(raw, gates, "bf16", C, 0.1)
+    ref, _ = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"])
+    e = rel_err(out, ref)
+    print(f"all gates 1, d_k {dk}: out {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
