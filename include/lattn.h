@@ -219,7 +219,12 @@ size_t lattn_hla_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, 
  * out [B,H,T,d_v] in dims->dtype; no final state (each level keeps its own).
  * Needs d_k, d_v <= 128 and d_k + chunk <= 192 (LATTN_EUNSUPPORTED); the
  * per-level states of one (batch, head) slice live in LDS, which bounds the
- * number of chunks at 2^17 for d_k = 128.  Arithmetic is fp32.
+ * number of chunks at 2^17 for d_k = 128.  Arithmetic: for bf16 storage with
+ * d_k = 64, chunk 64, r_kv = 1, r_ab <= 2, d_v a multiple of 64 and at most
+ * 2^16 chunks, bf16 MFMA operands (the chunk operators and the level states
+ * rounded to bf16) with fp32 accumulation and fp32 level states; otherwise
+ * fp32 (bf16 storage at other shapes: operators rounded to bf16 where the bf16
+ * MFMA prepare forms them, as for lattn_chunk_fwd).
  * Needs lattn_loglinear_fwd_workspace_size() bytes of caller-owned workspace.
  * Validation, ownership and stream ordering as lattn_chunk_fwd.
  */

@@ -214,6 +214,270 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same lift on the bf16 MFMA prepare's operators (bf16 storage, C = 64,
+// d_k = 64), read in their fragment order with no fp32 copy, on bf16 MFMAs
+// (16x16x32, fp32 accumulate).  A fragment (row tile mt, K pair kp) is 64
+// lanes x 8 bf16: lane (g, i) holds row 16 mt + i at the columns
+// 32 kp + 16 h + 4 g + e (h = 0, 1; e = 0..3).  A 16x16 result tile in
+// accumulator layout (lane (g, i): rows 4 g + e, column i) of row tiles 2 kp
+// and 2 kp + 1 is therefore, side by side, the B operand of K pair kp: a level
+// state feeds the next chunk's product with no lane exchange.
+//
+// One workgroup of four waves per (batch*head, 16-column d_v slice), chunks in
+// order.  Wave w
+//  * owns the inter-chunk levels m = w, w + 4, ... and carries their states
+//    in fp32 registers (the transport S <- Acal S, plus Z V in a left half);
+//  * forms the output of the chunk's tokens 16 w .. 16 w + 15: the
+//    chunk-local part (R (.) Lam) V and, for every level in a right half, the
+//    level-weighted Qbar S, reading the states' bf16 copies in LDS.
+// The next chunk's operator (32 KB), V slice and level weights are loaded into
+// registers at the start of a chunk and written to the other half of a
+// double-buffered LDS stage at its end; the bf16 state copies alternate the
+// same way, so each chunk needs one barrier.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 lbf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lbf16x4;
+typedef unsigned int lu32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int lu32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFC = 64;     // chunk of the bf16 operators
+constexpr int kFW = 4;      // waves: one per 16-token tile of the chunk
+constexpr int kFLPW = 4;    // inter-chunk levels per wave (up to 16 levels)
+constexpr int kFBV = 16;    // d_v columns per workgroup
+constexpr int kFLamIt = 6;  // staged weights per lane: 64 tokens x (c + 1 + 16) <= 6 x 256
+
+template <int DK>
+struct LlFastCfg {
+  static constexpr int MT = (DK + kFC) / 16;         // operator row tiles
+  static constexpr int KP = (DK + kFC) / 32;         // operator K pairs
+  static constexpr int DT = DK / 16;                 // channel row tiles
+  static constexpr int DP = DK / 32;                 // channel K pairs
+  static constexpr int TP = kFC / 32;                // token K pairs
+  static constexpr int OPB = MT * KP * 1024;         // bytes of one chunk operator
+  static constexpr int OPIT = OPB / (16 * 64 * kFW); // 16-byte operator pieces per lane
+  static constexpr int VB = TP * 1024;               // V slice as B fragments
+  static constexpr int SB = DP * 1024;               // one level state as B fragments
+  static_assert(OPB % (16 * 64 * kFW) == 0 && DT % 2 == 0, "bf16 log-linear tiling");
+};
+
+__device__ __forceinline__ lbf16x4 f4_to_b4(const f32x4& v) {
+  lbf16x4 r;
+  r[0] = (__bf16)v[0];
+  r[1] = (__bf16)v[1];
+  r[2] = (__bf16)v[2];
+  r[3] = (__bf16)v[3];
+  return r;
+}
+__device__ __forceinline__ lbf16x8 cat8(const lbf16x4& x, const lbf16x4& y) {
+  lbf16x8 r;
+  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
+  return r;
+}
+__device__ __forceinline__ f32x4 mfma_bf16(const lbf16x8& x, const lbf16x8& y, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+}
+// Workgroup barrier ordering LDS only (global stores stay in flight).
+__device__ __forceinline__ void ll_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct LlFastArgs {
+  Problem p;
+  const __bf16* M;     // fragment-ordered chunk operators
+  const __bf16* v;
+  const float* lam;    // [BH, T, L]
+  int L;
+  int c;               // log2(C)
+  int nlev;            // inter-chunk levels
+  int LS;              // weights staged per token: min(L, c + 1 + nlev)
+  __bf16* out;
+};
+
+template <int DK>
+__global__ __launch_bounds__(64 * kFW) void ll_fast_kernel(LlFastArgs a) {
+  using Cfg = LlFastCfg<DK>;
+  constexpr int DT = Cfg::DT, DP = Cfg::DP, TP = Cfg::TP, KP = Cfg::KP;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Problem& p = a.p;
+  const int nvt = p.dv / kFBV;
+  const int b = blockIdx.x;
+  // the d_v slices of one (batch, head) share blockIdx % 8, hence an XCD and its L2
+  const int grp = b / (8 * nvt), rem = b % (8 * nvt);
+  const int64_t bh = static_cast<int64_t>(grp) * 8 + rem % 8;
+  const int c0 = (rem / 8) * kFBV;
+  if (bh >= p.BH) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t N = p.N, T = p.T;
+  const int nlev = a.nlev, LS = a.LS;
+  unsigned char* opL = smem;                                        // [2][OPB]
+  unsigned char* vL = opL + 2 * Cfg::OPB;                           // [2][VB]
+  unsigned char* sL = vL + 2 * Cfg::VB;                             // [2][nlev][SB]
+  float* wL = reinterpret_cast<float*>(sL + 2 * nlev * Cfg::SB);    // [2][LS][64]
+
+  // ---- staging of one chunk: global -> registers, then registers -> LDS
+  lu32x4 opr[Cfg::OPIT];
+  lu32x2 vr;
+  float wr[kFLamIt];
+  auto load_chunk = [&](int64_t J) {
+    const int64_t job = bh * N + J;
+    const lu32x4* src = reinterpret_cast<const lu32x4*>(a.M + static_cast<size_t>(job) * (Cfg::OPB / 2));
+#pragma unroll
+    for (int i = 0; i < Cfg::OPIT; ++i) opr[i] = src[i * 64 * kFW + tid];
+    const int64_t t0 = J * kFC;
+    const int n = static_cast<int>(T - t0 < kFC ? T - t0 : kFC);
+    const int tv = tid >> 2;   // token of this lane's V piece; columns 4 (tid % 4) .. + 3
+    vr = lu32x2{0u, 0u};
+    if (tv < n) vr = *reinterpret_cast<const lu32x2*>(a.v + static_cast<size_t>(bh * T + t0 + tv) * p.dv + c0 + 4 * (tid & 3));
+#pragma unroll
+    for (int i = 0; i < kFLamIt; ++i) {
+      const int idx = tid + 64 * kFW * i;
+      const int t = idx / LS, l = idx - t * LS;
+      wr[i] = idx < kFC * LS ? a.lam[static_cast<size_t>(bh * T + t0 + (t < n ? t : n - 1)) * a.L + l] : 0.f;
+    }
+  };
+  auto stage_chunk = [&](int buf) {
+    lu32x4* od = reinterpret_cast<lu32x4*>(opL + buf * Cfg::OPB);
+#pragma unroll
+    for (int i = 0; i < Cfg::OPIT; ++i) od[i * 64 * kFW + tid] = opr[i];
+    // V piece -> B fragments of the token K pairs: token t sits in pair t / 32,
+    // half (t / 16) % 2, lane group (t / 4) % 4, element t % 4
+    __bf16* vd = reinterpret_cast<__bf16*>(vL + buf * Cfg::VB);
+    const int tv = tid >> 2;
+    const int pos = (tv >> 5) * 64 * 8 + ((tv >> 2) & 3) * 16 * 8 + ((tv >> 4) & 1) * 4 + (tv & 3);
+    const lbf16x4 vv = __builtin_bit_cast(lbf16x4, vr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vd[pos + (4 * (tid & 3) + j) * 8] = vv[j];
+    // level weights transposed: [level][token]
+    float* wd = wL + buf * LS * kFC;
+#pragma unroll
+    for (int i = 0; i < kFLamIt; ++i) {
+      const int idx = tid + 64 * kFW * i;
+      const int t = idx / LS, l = idx - t * LS;
+      if (idx < kFC * LS) wd[l * kFC + t] = wr[i];
+    }
+  };
+
+  f32x4 S[kFLPW][DT];
+#pragma unroll
+  for (int u = 0; u < kFLPW; ++u)
+#pragma unroll
+    for (int i = 0; i < DT; ++i) S[u][i] = zero4();
+  __bf16* op_out = a.out;
+  const int tt = wave;   // this wave's token tile
+
+  load_chunk(0);
+  stage_chunk(0);
+  ll_lds_barrier();
+  for (int64_t J = 0; J < N; ++J) {
+    const int buf = static_cast<int>(J & 1);
+    load_chunk(J + 1 < N ? J + 1 : J);   // the last chunk stages a copy of itself, unread
+    const lbf16x8* opf = reinterpret_cast<const lbf16x8*>(opL + buf * Cfg::OPB);
+    auto frag = [&](int mt, int kp) { return opf[(mt * KP + kp) * 64 + lane]; };
+    const lbf16x8* vb = reinterpret_cast<const lbf16x8*>(vL + buf * Cfg::VB);
+    const float* wb = wL + buf * LS * kFC;
+    lbf16x8 vfr[TP];
+#pragma unroll
+    for (int q = 0; q < TP; ++q) vfr[q] = vb[q * 64 + lane];
+
+    // ---- level states of this wave
+    if (wave < nlev) {
+      f32x4 zv[DT];
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
+        zv[i] = zero4();
+#pragma unroll
+        for (int q = 0; q < TP; ++q) zv[i] = mfma_bf16(frag(i, DP + q), vfr[q], zv[i]);
+      }
+      lbf16x8 af[DT][DP];
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int kp = 0; kp < DP; ++kp) af[i][kp] = frag(i, kp);
+#pragma unroll
+      for (int u = 0; u < kFLPW; ++u) {
+        const int m = wave + kFW * u;
+        if (m < nlev) {
+        const bool right = (J >> m) & 1;
+        const bool reset = !right && (J & ((2LL << m) - 1)) == 0;
+        if (reset) {
+#pragma unroll
+          for (int i = 0; i < DT; ++i) S[u][i] = zv[i];
+        } else {
+          lbf16x8 sb[DP];
+#pragma unroll
+          for (int kp = 0; kp < DP; ++kp) sb[kp] = cat8(f4_to_b4(S[u][2 * kp]), f4_to_b4(S[u][2 * kp + 1]));
+#pragma unroll
+          for (int i = 0; i < DT; ++i) {
+            f32x4 acc = right ? zero4() : zv[i];
+#pragma unroll
+            for (int kp = 0; kp < DP; ++kp) acc = mfma_bf16(af[i][kp], sb[kp], acc);
+            S[u][i] = acc;
+          }
+        }
+        // the bf16 copy that the next chunk's readouts use (read only if that
+        // chunk is in a right half of this level)
+        if (((J + 1) >> m) & 1) {
+          lbf16x8* sd = reinterpret_cast<lbf16x8*>(sL + ((buf ^ 1) * nlev + m) * Cfg::SB);
+#pragma unroll
+          for (int kp = 0; kp < DP; ++kp) sd[kp * 64 + lane] = cat8(f4_to_b4(S[u][2 * kp]), f4_to_b4(S[u][2 * kp + 1]));
+        }
+        }
+      }
+    }
+
+    // ---- output of tokens 16 tt .. 16 tt + 15
+    const int tq = 16 * tt + lr;   // this lane's row of the R fragments
+    f32x4 o = zero4();
+#pragma unroll
+    for (int q = 0; q < TP; ++q) {
+      lbf16x8 rf = frag(DT + tt, DP + q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = 32 * q + 16 * (j >> 2) + 4 * lg + (j & 3);
+        const int lev = 32 - __clz(tq ^ s);   // 0 on the diagonal
+        const float w = (s <= tq && lev < LS) ? wb[lev * kFC + tq] : 0.f;
+        rf[j] = (__bf16)((float)rf[j] * w);
+      }
+      o = mfma_bf16(rf, vfr[q], o);
+    }
+    lbf16x8 qf[DP];
+#pragma unroll
+    for (int kp = 0; kp < DP; ++kp) qf[kp] = frag(DT + tt, kp);
+    for (int m = 0; m < nlev; ++m) {
+      if (!((J >> m) & 1)) continue;
+      const lbf16x8* sr = reinterpret_cast<const lbf16x8*>(sL + (buf * nlev + m) * Cfg::SB);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kp = 0; kp < DP; ++kp) acc = mfma_bf16(qf[kp], sr[kp * 64 + lane], acc);
+      const f32x4 w = *reinterpret_cast<const f32x4*>(wb + (a.c + 1 + m) * kFC + 16 * tt + 4 * lg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += w[e] * acc[e];
+    }
+    {
+      const int64_t t0 = J * kFC;
+      const int n = static_cast<int>(T - t0 < kFC ? T - t0 : kFC);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tt + 4 * lg + e;
+        if (t < n) op_out[static_cast<size_t>(bh * T + t0 + t) * p.dv + c0 + lr] = (__bf16)o[e];
+      }
+    }
+    stage_chunk(buf ^ 1);
+    ll_lds_barrier();
+  }
+}
+
+size_t ll_fast_lds(int nlev, int LS) {
+  using Cfg = LlFastCfg<64>;
+  return 2 * static_cast<size_t>(Cfg::OPB + Cfg::VB) + 2 * static_cast<size_t>(nlev) * Cfg::SB +
+         2 * static_cast<size_t>(LS) * kFC * sizeof(float);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
@@ -239,12 +503,24 @@ constexpr size_t kLlLdsMax = 150 * 1024;
 // copies of each level state the scan keeps: two where they fit
 int loglinear_scan_bufs(const Problem& p) { return 2 * loglinear_scan_lds(p) <= kLlLdsMax ? 2 : 1; }
 
+// The bf16 route: the bf16 MFMA prepare's shapes at d_k = 64, up to 16
+// inter-chunk levels (2^16 chunks).
+static bool loglinear_fast(const Problem& p) {
+  return fast_supported(p) && p.dk == 64 && inter_levels(p.N) <= kFW * kFLPW;
+}
+
 bool loglinear_supported(const Problem& p) {
+  if (loglinear_fast(p)) return true;
   return p.dk <= 128 && p.dv <= 128 && p.mrows() <= 16 * 4 * kLlQW && loglinear_scan_lds(p) <= kLlLdsMax;
 }
 
 LlPlan loglinear_plan(const Problem& p) {
   LlPlan h{};
+  if (loglinear_fast(p)) {
+    h.gen_bytes = align256(fast_workspace_bytes(p));
+    h.total_bytes = h.gen_bytes;
+    return h;
+  }
   const size_t chunks = static_cast<size_t>(p.BH * p.N);
   h.gen_bytes = align256(f32_operators_bytes(p));
   h.zv_bytes = align256(chunks * p.dv * p.dk * sizeof(float));
@@ -258,6 +534,23 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
                             hipStream_t s) {
   if (p.BH * p.N == 0) return hipSuccess;
   if (!loglinear_supported(p)) return hipErrorInvalidValue;
+  if (loglinear_fast(p)) {
+    hipError_t e = fast_prepare(p, q, k, ld, A, B, workspace, s);
+    if (e != hipSuccess) return e;
+    const int nlev = inter_levels(p.N);
+    const int L = loglinear_levels(p.T);
+    const int LS = L < 7 + nlev ? L : 7 + nlev;   // weights read per token: c = 6
+    LlFastArgs fa{p, static_cast<const __bf16*>(workspace), static_cast<const __bf16*>(v), lam, L, 6, nlev, LS,
+                  static_cast<__bf16*>(out)};
+    const size_t lds = ll_fast_lds(nlev, LS);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(ll_fast_kernel<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    const int64_t nvt = p.dv / kFBV;
+    const dim3 grid(static_cast<unsigned>((p.BH + 7) / 8 * 8 * nvt));
+    hipLaunchKernelGGL(ll_fast_kernel<64>, grid, dim3(64 * kFW), lds, s, fa);
+    return hipGetLastError();
+  }
   const LlPlan h = loglinear_plan(p);
   char* ws = static_cast<char*>(workspace);
   float* ZVT = reinterpret_cast<float*>(ws + h.gen_bytes);

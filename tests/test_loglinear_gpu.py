@@ -2,8 +2,13 @@
 oracle, through the C ABI.
 
 Gate as for the base path: max|gpu - ref| / max|ref| <= 1e-4 for fp32 storage
-and <= 2e-2 for bf16 storage (fp32 arithmetic in both).  Inputs: the seeded
-generic recurrence inputs and seeded per-level weights softplus(N(0, 1)).
+and <= 2e-2 for bf16 storage.  Inputs: the seeded generic recurrence inputs and
+seeded per-level weights softplus(N(0, 1)).
+
+Two routes are exercised: fp32 arithmetic on row-major fp32 chunk operators
+(fp32 storage, and bf16 storage at d_k = 128), and, for bf16 storage at the
+bf16 MFMA prepare's shapes with d_k = 64, the scan on that prepare's bf16
+operators with bf16 MFMAs (cases marked "bf16 route").
 """
 import numpy as np
 import pytest
@@ -28,7 +33,10 @@ def _gpu(raw, lam, dtype, chunk):
 
 
 def _ref(raw, lam):
-    return ll_oracle.loglinear(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], lam)
+    T = raw["q"].shape[-2]
+    # the per-query definition is O(T^2) transports; longer cases use the recurrent form
+    f = ll_oracle.loglinear if T <= 400 else ll_oracle.loglinear_recurrent
+    return f(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], lam)
 
 
 CASES = [
@@ -41,8 +49,16 @@ CASES = [
     (1, 1, 1, 16, 16, 1, 1, 16, "fp32", "channel"),
     (1, 2, 130, 64, 64, 2, 1, 32, "bf16", "channel"),
     (1, 1, 200, 128, 128, 2, 1, 64, "bf16", "channel"),   # operators from the bf16 MFMA prepare
-    (1, 2, 150, 64, 64, 1, 1, 64, "bf16", "scalar"),      # the same at d_k = 64
+    (1, 2, 150, 64, 64, 1, 1, 64, "bf16", "scalar"),      # bf16 route
     (1, 1, 160, 64, 128, 1, 1, 128, "bf16", "scalar"),
+    # bf16 route: rank 0, 6 (batch, head) slices (not a multiple of 8), ragged tail
+    (2, 3, 1000, 64, 64, 0, 1, 64, "bf16", "channel"),
+    # bf16 route: rank 2, d_v 128 (eight column slices), 38 chunks (6 inter-chunk levels)
+    (1, 2, 2373, 64, 128, 2, 1, 64, "bf16", "channel"),
+    # bf16 route: one token, one exact chunk, one chunk and one token
+    (1, 1, 1, 64, 64, 1, 1, 64, "bf16", "scalar"),
+    (1, 1, 64, 64, 64, 1, 1, 64, "bf16", "channel"),
+    (1, 1, 65, 64, 64, 2, 1, 64, "bf16", "channel"),
 ]
 
 
@@ -164,3 +180,43 @@ def test_loglinear_empty_and_repeatable():
     a = _gpu(raw, lam, "bf16", 64)
     b = _gpu(raw, lam, "bf16", 64)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_loglinear_sixteen_levels_sparse_writes():
+    """bf16 route at its largest level count: 2^15 + 1 chunks of 64 tokens plus
+    36 (2097252 tokens, 16 inter-chunk levels, 23 in all).  Keys and values are
+    zero before H - 256 (H = 2^21), so:
+      * outputs before H - 256 are exactly zero;
+      * on [H - 256, H) (a 256-aligned block, so levels are those of the block
+        taken on its own) the output is the recurrent oracle's on that block;
+      * on [H, T) it is the recurrent oracle's on [H, T) plus, at the top level
+        (index 22, the bucket [0, H) of every such query), the state of the
+        writes on [H - 256, H) carried by the recurrence's transport: the
+        oracle's token recurrence over [H - 256, H), then over [H, T) from that
+        state with no writes, read out and weighted by lambda[t, 22]."""
+    T, H0, W = (1 << 21) + 100, 1 << 21, 256
+    dk = dv = 64
+    raw = workloads.generic_raw(1, 1, T, dk, dv, 1, 1, "bf16", "scalar", seed=12)
+    raw["K"][:, :, :H0 - W] = 0
+    raw["V"][:, :, :H0 - W] = 0
+    lam = workloads.loglinear_lambdas(1, 1, T, seed=12)
+    assert lam.shape[-1] == 23 and lattn.loglinear_levels(T) == 23
+    out = _gpu(raw, lam, "bf16", 64)
+    assert not np.any(out[:, :, :H0 - W]), "outputs before the first write must be zero"
+    sl = lambda d, a, b: {k: (None if v is None else v[:, :, a:b]) for k, v in d.items()}
+    blk = sl(raw, H0 - W, H0)
+    ref1 = ll_oracle.loglinear_recurrent(blk["q"], blk["K"], blk["V"], blk["log_decay"], blk["A"], blk["B"],
+                                         lam[:, :, H0 - W:H0, :9])
+    e1 = rel_err(out[:, :, H0 - W:H0], ref1)
+    tail = sl(raw, H0, T)
+    ref2 = ll_oracle.loglinear_recurrent(tail["q"], tail["K"], tail["V"], tail["log_decay"], tail["A"], tail["B"],
+                                         lam[:, :, H0:T, :8])
+    _, S = oracle.generic(blk["q"], blk["K"], blk["V"], blk["log_decay"], blk["A"], blk["B"])
+    carried, _ = oracle.generic(tail["q"], np.zeros_like(tail["K"]), tail["V"], tail["log_decay"], tail["A"],
+                                tail["B"], initial_state=S)
+    ref2 = ref2 + lam[:, :, H0:T, 22:23] * carried
+    e2 = rel_err(out[:, :, H0:T], ref2)
+    print(f"{T} tokens, 16 inter-chunk levels: block before H {e1:.2e}, after H {e2:.2e}", flush=True)
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
