@@ -224,27 +224,38 @@ __global__ __launch_bounds__(256) void ll_scan_kernel(LlScanArgs a) {
 // and 2 kp + 1 is therefore, side by side, the B operand of K pair kp: a level
 // state feeds the next chunk's product with no lane exchange.
 //
-// One workgroup of four waves per (batch*head, 16-column d_v slice), chunks in
-// order.  Wave w
-//  * owns the inter-chunk levels m = w, w + 4, ... and carries their states
-//    in fp32 registers (the transport S <- Acal S, plus Z V in a left half);
-//  * forms the output of the chunk's tokens 16 w .. 16 w + 15: the
-//    chunk-local part (R (.) Lam) V and, for every level in a right half, the
-//    level-weighted Qbar S, reading the states' bf16 copies in LDS.
-// The next chunk's operator (32 KB), V slice and level weights are loaded into
-// registers at the start of a chunk and written to the other half of a
-// double-buffered LDS stage at its end; the bf16 state copies alternate the
-// same way, so each chunk needs one barrier.
+// One workgroup of eight waves per (batch*head, 16-column d_v slice), chunks
+// in order; two waves per SIMD, one of each role:
+//  * level waves (w < 4) own the inter-chunk levels m = w, w + 4, ... and
+//    carry their states in fp32 registers: in a right half of level m they
+//    read the state out (Qbar S, weighted per token by the level's weight)
+//    into a partial output of the chunk's 64 tokens, then transport it
+//    (S <- Acal S, plus Z V in a left half);
+//  * token waves (w >= 4) form the chunk-local output (R (.) Lam) V of the
+//    tokens 16 (w - 4) .. + 15, add the level waves' partials one chunk later
+//    (after the barrier that publishes them) and store the result.
+// The token waves, which hold few registers, also stage the inputs: a chunk's
+// operator (32 KB), V slice and level weights are loaded into a ring of PD
+// register sets PD chunks ahead, and written to the other half of a
+// double-buffered LDS stage at the end of the chunk before their use; the
+// partial outputs alternate the same way, so each chunk needs one barrier.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 lbf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lbf16x4;
 typedef unsigned int lu32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int lu32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFC = 64;     // chunk of the bf16 operators
-constexpr int kFW = 4;      // waves: one per 16-token tile of the chunk
-constexpr int kFLPW = 4;    // inter-chunk levels per wave (up to 16 levels)
+constexpr int kFLW = 4;     // level waves
+constexpr int kFTW = 4;     // token waves: one per 16-token tile of the chunk
+constexpr int kFW = kFLW + kFTW;
+constexpr int kFLPW = 4;    // inter-chunk levels per level wave (up to 16 levels)
 constexpr int kFBV = 16;    // d_v columns per workgroup
-constexpr int kFLamIt = 6;  // staged weights per lane: 64 tokens x (c + 1 + 16) <= 6 x 256
+constexpr int kFLamIt = 6;  // staged weights per token-wave lane: 64 tokens x (c + 1 + 16) <= 6 x 256
+constexpr int kFPD = 2;     // chunks in flight ahead of the one being staged
+// Row stride (floats) of the staged level weights [level][token]: 4 mod 64,
+// so that the staging writes (levels of a few consecutive tokens across the
+// lanes) fall in distinct LDS banks, and rows stay 16-byte aligned.
+constexpr int kFWS = kFC + 4;
 
 template <int DK>
 struct LlFastCfg {
@@ -254,10 +265,11 @@ struct LlFastCfg {
   static constexpr int DP = DK / 32;                 // channel K pairs
   static constexpr int TP = kFC / 32;                // token K pairs
   static constexpr int OPB = MT * KP * 1024;         // bytes of one chunk operator
-  static constexpr int OPIT = OPB / (16 * 64 * kFW); // 16-byte operator pieces per lane
+  static constexpr int OPIT = OPB / (16 * 64 * kFTW); // 16-byte operator pieces per token-wave lane
   static constexpr int VB = TP * 1024;               // V slice as B fragments
-  static constexpr int SB = DP * 1024;               // one level state as B fragments
-  static_assert(OPB % (16 * 64 * kFW) == 0 && DT % 2 == 0, "bf16 log-linear tiling");
+  static constexpr int PB = kFLW * (kFC / 16) * 1024; // partial outputs of the level waves (fp32 tiles)
+  static_assert(OPB % (16 * 64 * kFTW) == 0 && DT % 2 == 0 && kFC * kFBV == 4 * 64 * kFTW,
+                "bf16 log-linear tiling");
 };
 
 __device__ __forceinline__ lbf16x4 f4_to_b4(const f32x4& v) {
@@ -300,6 +312,7 @@ template <int DK>
 __global__ __launch_bounds__(64 * kFW) void ll_fast_kernel(LlFastArgs a) {
   using Cfg = LlFastCfg<DK>;
   constexpr int DT = Cfg::DT, DP = Cfg::DP, TP = Cfg::TP, KP = Cfg::KP;
+  constexpr int NTH = 64 * kFTW, NTT = kFC / 16;   // staging threads: the token waves
   extern __shared__ __align__(16) unsigned char smem[];
   const Problem& p = a.p;
   const int nvt = p.dv / kFBV;
@@ -314,168 +327,228 @@ __global__ __launch_bounds__(64 * kFW) void ll_fast_kernel(LlFastArgs a) {
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t N = p.N, T = p.T;
   const int nlev = a.nlev, LS = a.LS;
-  unsigned char* opL = smem;                                        // [2][OPB]
-  unsigned char* vL = opL + 2 * Cfg::OPB;                           // [2][VB]
-  unsigned char* sL = vL + 2 * Cfg::VB;                             // [2][nlev][SB]
-  float* wL = reinterpret_cast<float*>(sL + 2 * nlev * Cfg::SB);    // [2][LS][64]
+  const int nlw = nlev < kFLW ? nlev : kFLW;   // level waves that own a level
+  unsigned char* opL = smem;                                   // [2][OPB]
+  unsigned char* vL = opL + 2 * Cfg::OPB;                      // [2][VB]
+  f32x4* pL = reinterpret_cast<f32x4*>(vL + 2 * Cfg::VB);      // [2][level wave][token tile][lane]
+  float* wL = reinterpret_cast<float*>(vL + 2 * Cfg::VB + 2 * Cfg::PB);   // [2][LS][kFWS]
 
-  // ---- staging of one chunk: global -> registers, then registers -> LDS
-  lu32x4 opr[Cfg::OPIT];
-  lu32x2 vr;
-  float wr[kFLamIt];
-  auto load_chunk = [&](int64_t J) {
+  // ---- staging of one chunk (token waves): global -> registers, then
+  // registers -> LDS.  sid: this lane's index among the token waves' lanes.
+  const int sid = tid - 64 * kFLW;
+  // This lane's level weights: (token, level) pairs sid + NTH i of the chunk's
+  // token-major block, fixed for the whole walk (-1: none).
+  int wtk[kFLamIt], wlv[kFLamIt];
+  // This lane's V piece: token sid / 4, columns 4 (sid % 4) .. + 3; and its
+  // place in the B fragments of the token K pairs (token t sits in pair
+  // t / 32, half (t / 16) % 2, lane group (t / 4) % 4, element t % 4).
+  const int tv = sid >> 2, cv = 4 * (sid & 3);
+  const int vpos = (tv >> 5) * 64 * 8 + ((tv >> 2) & 3) * 16 * 8 + ((tv >> 4) & 1) * 4 + (tv & 3) + cv * 8;
+  struct Stage {
+    lu32x4 op[Cfg::OPIT];
+    lu32x2 v;
+    float w[kFLamIt];
+  };
+  auto load_chunk = [&](Stage& st, int64_t J) {
     const int64_t job = bh * N + J;
     const lu32x4* src = reinterpret_cast<const lu32x4*>(a.M + static_cast<size_t>(job) * (Cfg::OPB / 2));
 #pragma unroll
-    for (int i = 0; i < Cfg::OPIT; ++i) opr[i] = src[i * 64 * kFW + tid];
+    for (int i = 0; i < Cfg::OPIT; ++i) st.op[i] = src[i * NTH + sid];
     const int64_t t0 = J * kFC;
     const int n = static_cast<int>(T - t0 < kFC ? T - t0 : kFC);
-    const int tv = tid >> 2;   // token of this lane's V piece; columns 4 (tid % 4) .. + 3
-    vr = lu32x2{0u, 0u};
-    if (tv < n) vr = *reinterpret_cast<const lu32x2*>(a.v + static_cast<size_t>(bh * T + t0 + tv) * p.dv + c0 + 4 * (tid & 3));
+    st.v = lu32x2{0u, 0u};
+    if (tv < n) st.v = *reinterpret_cast<const lu32x2*>(a.v + static_cast<size_t>(bh * T + t0 + tv) * p.dv + c0 + cv);
 #pragma unroll
     for (int i = 0; i < kFLamIt; ++i) {
-      const int idx = tid + 64 * kFW * i;
-      const int t = idx / LS, l = idx - t * LS;
-      wr[i] = idx < kFC * LS ? a.lam[static_cast<size_t>(bh * T + t0 + (t < n ? t : n - 1)) * a.L + l] : 0.f;
+      const int t = wtk[i] < 0 ? 0 : (wtk[i] < n ? wtk[i] : n - 1);   // padded tokens read the last one
+      st.w[i] = a.lam[static_cast<size_t>(bh * T + t0 + t) * a.L + (wtk[i] < 0 ? 0 : wlv[i])];
     }
   };
-  auto stage_chunk = [&](int buf) {
+  auto stage_chunk = [&](const Stage& st, int buf) {
     lu32x4* od = reinterpret_cast<lu32x4*>(opL + buf * Cfg::OPB);
 #pragma unroll
-    for (int i = 0; i < Cfg::OPIT; ++i) od[i * 64 * kFW + tid] = opr[i];
-    // V piece -> B fragments of the token K pairs: token t sits in pair t / 32,
-    // half (t / 16) % 2, lane group (t / 4) % 4, element t % 4
+    for (int i = 0; i < Cfg::OPIT; ++i) od[i * NTH + sid] = st.op[i];
     __bf16* vd = reinterpret_cast<__bf16*>(vL + buf * Cfg::VB);
-    const int tv = tid >> 2;
-    const int pos = (tv >> 5) * 64 * 8 + ((tv >> 2) & 3) * 16 * 8 + ((tv >> 4) & 1) * 4 + (tv & 3);
-    const lbf16x4 vv = __builtin_bit_cast(lbf16x4, vr);
+    const lbf16x4 vv = __builtin_bit_cast(lbf16x4, st.v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vd[pos + (4 * (tid & 3) + j) * 8] = vv[j];
-    // level weights transposed: [level][token]
-    float* wd = wL + buf * LS * kFC;
+    for (int j = 0; j < 4; ++j) vd[vpos + 8 * j] = vv[j];
+    float* wd = wL + buf * LS * kFWS;   // level weights transposed: [level][token]
+#pragma unroll
+    for (int i = 0; i < kFLamIt; ++i)
+      if (wtk[i] >= 0) wd[wlv[i] * kFWS + wtk[i]] = st.w[i];
+  };
+  Stage ring[kFPD];
+  if (wave >= kFLW) {
 #pragma unroll
     for (int i = 0; i < kFLamIt; ++i) {
-      const int idx = tid + 64 * kFW * i;
-      const int t = idx / LS, l = idx - t * LS;
-      if (idx < kFC * LS) wd[l * kFC + t] = wr[i];
+      const int idx = sid + NTH * i;
+      const int t = idx / LS;
+      wtk[i] = idx < kFC * LS ? t : -1;
+      wlv[i] = idx - t * LS;
     }
-  };
-
-  f32x4 S[kFLPW][DT];
+    load_chunk(ring[0], 0);
+    stage_chunk(ring[0], 0);
 #pragma unroll
-  for (int u = 0; u < kFLPW; ++u)
-#pragma unroll
-    for (int i = 0; i < DT; ++i) S[u][i] = zero4();
-  __bf16* op_out = a.out;
-  const int tt = wave;   // this wave's token tile
-
-  load_chunk(0);
-  stage_chunk(0);
+    for (int k = 1; k < kFPD; ++k) load_chunk(ring[k], k < N ? k : N - 1);
+  }
   ll_lds_barrier();
-  for (int64_t J = 0; J < N; ++J) {
-    const int buf = static_cast<int>(J & 1);
-    load_chunk(J + 1 < N ? J + 1 : J);   // the last chunk stages a copy of itself, unread
-    const lbf16x8* opf = reinterpret_cast<const lbf16x8*>(opL + buf * Cfg::OPB);
-    auto frag = [&](int mt, int kp) { return opf[(mt * KP + kp) * 64 + lane]; };
-    const lbf16x8* vb = reinterpret_cast<const lbf16x8*>(vL + buf * Cfg::VB);
-    const float* wb = wL + buf * LS * kFC;
-    lbf16x8 vfr[TP];
+  if (wave < kFLW) {
+    // ================= level wave
+    f32x4 S[kFLPW][DT];
 #pragma unroll
-    for (int q = 0; q < TP; ++q) vfr[q] = vb[q * 64 + lane];
-
-    // ---- level states of this wave
-    if (wave < nlev) {
-      f32x4 zv[DT];
+    for (int u = 0; u < kFLPW; ++u)
 #pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        zv[i] = zero4();
+      for (int i = 0; i < DT; ++i) S[u][i] = zero4();
+    for (int64_t J = 0; J < N; ++J) {
+      const int buf = static_cast<int>(J & 1);
+      if (wave < nlev) {
+        const lbf16x8* opf = reinterpret_cast<const lbf16x8*>(opL + buf * Cfg::OPB);
+        const lbf16x8* vb = reinterpret_cast<const lbf16x8*>(vL + buf * Cfg::VB);
+        const float* wb = wL + buf * LS * kFWS;
+        lbf16x8 vfr[TP];
 #pragma unroll
-        for (int q = 0; q < TP; ++q) zv[i] = mfma_bf16(frag(i, DP + q), vfr[q], zv[i]);
-      }
-      lbf16x8 af[DT][DP];
+        for (int q = 0; q < TP; ++q) vfr[q] = vb[q * 64 + lane];
+        f32x4 zv[DT];
 #pragma unroll
-      for (int i = 0; i < DT; ++i)
+        for (int i = 0; i < DT; ++i) {
+          zv[i] = zero4();
 #pragma unroll
-        for (int kp = 0; kp < DP; ++kp) af[i][kp] = frag(i, kp);
+          for (int q = 0; q < TP; ++q) zv[i] = mfma_bf16(opf[(i * KP + DP + q) * 64 + lane], vfr[q], zv[i]);
+        }
+        lbf16x8 af[DT][DP];
 #pragma unroll
-      for (int u = 0; u < kFLPW; ++u) {
-        const int m = wave + kFW * u;
-        if (m < nlev) {
-        const bool right = (J >> m) & 1;
-        const bool reset = !right && (J & ((2LL << m) - 1)) == 0;
-        if (reset) {
+        for (int i = 0; i < DT; ++i)
 #pragma unroll
-          for (int i = 0; i < DT; ++i) S[u][i] = zv[i];
-        } else {
-          lbf16x8 sb[DP];
+          for (int kp = 0; kp < DP; ++kp) af[i][kp] = opf[(i * KP + kp) * 64 + lane];
+        // Qbar fragments, if a level of this wave is read out in this chunk
+        bool any_right = false;
 #pragma unroll
-          for (int kp = 0; kp < DP; ++kp) sb[kp] = cat8(f4_to_b4(S[u][2 * kp]), f4_to_b4(S[u][2 * kp + 1]));
+        for (int u = 0; u < kFLPW; ++u) {
+          const int m = wave + kFLW * u;
+          any_right |= m < nlev && ((J >> m) & 1);
+        }
+        lbf16x8 qf[NTT][DP];
+        f32x4 part[NTT];
 #pragma unroll
-          for (int i = 0; i < DT; ++i) {
-            f32x4 acc = right ? zero4() : zv[i];
+        for (int tt = 0; tt < NTT; ++tt) {
+          part[tt] = zero4();
 #pragma unroll
-            for (int kp = 0; kp < DP; ++kp) acc = mfma_bf16(af[i][kp], sb[kp], acc);
-            S[u][i] = acc;
+          for (int kp = 0; kp < DP; ++kp)
+            qf[tt][kp] = any_right ? opf[((DT + tt) * KP + kp) * 64 + lane] : lbf16x8{};
+        }
+#pragma unroll
+        for (int u = 0; u < kFLPW; ++u) {
+          const int m = wave + kFLW * u;
+          if (m < nlev) {
+            const bool right = (J >> m) & 1;
+            const bool reset = !right && (J & ((2LL << m) - 1)) == 0;
+            if (reset) {
+#pragma unroll
+              for (int i = 0; i < DT; ++i) S[u][i] = zv[i];
+            } else {
+              lbf16x8 sb[DP];
+#pragma unroll
+              for (int kp = 0; kp < DP; ++kp) sb[kp] = cat8(f4_to_b4(S[u][2 * kp]), f4_to_b4(S[u][2 * kp + 1]));
+              if (right) {
+                // readout of the state entering this chunk, weighted per token
+#pragma unroll
+                for (int tt = 0; tt < NTT; ++tt) {
+                  f32x4 acc = zero4();
+#pragma unroll
+                  for (int kp = 0; kp < DP; ++kp) acc = mfma_bf16(qf[tt][kp], sb[kp], acc);
+                  const f32x4 w = *reinterpret_cast<const f32x4*>(wb + (a.c + 1 + m) * kFWS + 16 * tt + 4 * lg);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) part[tt][e] += w[e] * acc[e];
+                }
+              }
+#pragma unroll
+              for (int i = 0; i < DT; ++i) {
+                f32x4 acc = right ? zero4() : zv[i];
+#pragma unroll
+                for (int kp = 0; kp < DP; ++kp) acc = mfma_bf16(af[i][kp], sb[kp], acc);
+                S[u][i] = acc;
+              }
+            }
           }
         }
-        // the bf16 copy that the next chunk's readouts use (read only if that
-        // chunk is in a right half of this level)
-        if (((J + 1) >> m) & 1) {
-          lbf16x8* sd = reinterpret_cast<lbf16x8*>(sL + ((buf ^ 1) * nlev + m) * Cfg::SB);
 #pragma unroll
-          for (int kp = 0; kp < DP; ++kp) sd[kp * 64 + lane] = cat8(f4_to_b4(S[u][2 * kp]), f4_to_b4(S[u][2 * kp + 1]));
-        }
-        }
+        for (int tt = 0; tt < NTT; ++tt) pL[((buf * kFLW + wave) * NTT + tt) * 64 + lane] = part[tt];
       }
+      ll_lds_barrier();
     }
-
-    // ---- output of tokens 16 tt .. 16 tt + 15
+  } else {
+    // ================= token wave: tokens 16 tt .. 16 tt + 15 of every chunk
+    const int tt = wave - kFLW;
     const int tq = 16 * tt + lr;   // this lane's row of the R fragments
-    f32x4 o = zero4();
+    // The K pair qd = tt / 2 holds the diagonal tile: its weights go element by
+    // element (key s <= tq at level bit_length(tq ^ s), 0 on the diagonal; -1:
+    // masked).  For tt >= 2 the pair 0 (keys 0 .. 31) is at level c = 6 for
+    // every row: its product is scaled by row afterwards.
+    const int qd = tt >> 1;
+    int woff[8];
 #pragma unroll
-    for (int q = 0; q < TP; ++q) {
-      lbf16x8 rf = frag(DT + tt, DP + q);
+    for (int j = 0; j < 8; ++j) {
+      const int s = 32 * qd + 16 * (j >> 2) + 4 * lg + (j & 3);
+      const int lev = 32 - __clz(tq ^ s);
+      woff[j] = (s <= tq && lev < LS) ? lev * kFWS + tq : -1;
+    }
+    const bool lower = tt >= 2 && LS > 6;
+    f32x4 o_prev = zero4();
+    auto finish = [&](int64_t Jp, int pbuf) {
+      // chunk Jp's output: its chunk-local part plus the level waves' partials
+      f32x4 o = o_prev;
+      for (int w = 0; w < nlw; ++w) {
+        const f32x4 pp = pL[((pbuf * kFLW + w) * NTT + tt) * 64 + lane];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int s = 32 * q + 16 * (j >> 2) + 4 * lg + (j & 3);
-        const int lev = 32 - __clz(tq ^ s);   // 0 on the diagonal
-        const float w = (s <= tq && lev < LS) ? wb[lev * kFC + tq] : 0.f;
-        rf[j] = (__bf16)((float)rf[j] * w);
+        for (int e = 0; e < 4; ++e) o[e] += pp[e];
       }
-      o = mfma_bf16(rf, vfr[q], o);
-    }
-    lbf16x8 qf[DP];
-#pragma unroll
-    for (int kp = 0; kp < DP; ++kp) qf[kp] = frag(DT + tt, kp);
-    for (int m = 0; m < nlev; ++m) {
-      if (!((J >> m) & 1)) continue;
-      const lbf16x8* sr = reinterpret_cast<const lbf16x8*>(sL + (buf * nlev + m) * Cfg::SB);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kp = 0; kp < DP; ++kp) acc = mfma_bf16(qf[kp], sr[kp * 64 + lane], acc);
-      const f32x4 w = *reinterpret_cast<const f32x4*>(wb + (a.c + 1 + m) * kFC + 16 * tt + 4 * lg);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] += w[e] * acc[e];
-    }
-    {
-      const int64_t t0 = J * kFC;
+      const int64_t t0 = Jp * kFC;
       const int n = static_cast<int>(T - t0 < kFC ? T - t0 : kFC);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tt + 4 * lg + e;
-        if (t < n) op_out[static_cast<size_t>(bh * T + t0 + t) * p.dv + c0 + lr] = (__bf16)o[e];
+        if (t < n) a.out[static_cast<size_t>(bh * T + t0 + t) * p.dv + c0 + lr] = (__bf16)o[e];
       }
+    };
+    // Chunk J loads chunk J + PD into ring slot J % PD (which held chunk J,
+    // staged at the end of chunk J - 1) and stages chunk J + 1 from slot
+    // (J + 1) % PD; past the end the loads repeat the last chunk, unread.
+    auto step = [&](const int64_t J, Stage& ld_slot, const Stage& st_slot) {
+      const int buf = static_cast<int>(J & 1);
+      load_chunk(ld_slot, J + kFPD < N ? J + kFPD : N - 1);
+      if (J > 0) finish(J - 1, buf ^ 1);
+      const lbf16x8* opf = reinterpret_cast<const lbf16x8*>(opL + buf * Cfg::OPB);
+      const lbf16x8* vb = reinterpret_cast<const lbf16x8*>(vL + buf * Cfg::VB);
+      const float* wb = wL + buf * LS * kFWS;
+      lbf16x8 rf = opf[((DT + tt) * KP + DP + qd) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = woff[j] >= 0 ? wb[woff[j]] : 0.f;
+        rf[j] = (__bf16)((float)rf[j] * w);
+      }
+      f32x4 o = mfma_bf16(rf, vb[qd * 64 + lane], zero4());
+      if (lower) {
+        const f32x4 acc = mfma_bf16(opf[((DT + tt) * KP + DP) * 64 + lane], vb[lane], zero4());
+        const f32x4 w = *reinterpret_cast<const f32x4*>(wb + 6 * kFWS + 16 * tt + 4 * lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += w[e] * acc[e];
+      }
+      o_prev = o;
+      stage_chunk(st_slot, buf ^ 1);
+      ll_lds_barrier();
+    };
+    for (int64_t J = 0; J < N; J += kFPD) {
+#pragma unroll
+      for (int k = 0; k < kFPD; ++k)
+        if (J + k < N) step(J + k, ring[k], ring[(k + 1) % kFPD]);
     }
-    stage_chunk(buf ^ 1);
-    ll_lds_barrier();
+    finish(N - 1, static_cast<int>((N - 1) & 1));
   }
 }
 
-size_t ll_fast_lds(int nlev, int LS) {
+size_t ll_fast_lds(int LS) {
   using Cfg = LlFastCfg<64>;
-  return 2 * static_cast<size_t>(Cfg::OPB + Cfg::VB) + 2 * static_cast<size_t>(nlev) * Cfg::SB +
-         2 * static_cast<size_t>(LS) * kFC * sizeof(float);
+  return 2 * static_cast<size_t>(Cfg::OPB + Cfg::VB + Cfg::PB) + 2 * static_cast<size_t>(LS) * kFWS * sizeof(float);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -506,7 +579,7 @@ int loglinear_scan_bufs(const Problem& p) { return 2 * loglinear_scan_lds(p) <= 
 // The bf16 route: the bf16 MFMA prepare's shapes at d_k = 64, up to 16
 // inter-chunk levels (2^16 chunks).
 static bool loglinear_fast(const Problem& p) {
-  return fast_supported(p) && p.dk == 64 && inter_levels(p.N) <= kFW * kFLPW;
+  return fast_supported(p) && p.dk == 64 && inter_levels(p.N) <= kFLW * kFLPW;
 }
 
 bool loglinear_supported(const Problem& p) {
@@ -542,7 +615,7 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
     const int LS = L < 7 + nlev ? L : 7 + nlev;   // weights read per token: c = 6
     LlFastArgs fa{p, static_cast<const __bf16*>(workspace), static_cast<const __bf16*>(v), lam, L, 6, nlev, LS,
                   static_cast<__bf16*>(out)};
-    const size_t lds = ll_fast_lds(nlev, LS);
+    const size_t lds = ll_fast_lds(LS);
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(ll_fast_kernel<64>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
