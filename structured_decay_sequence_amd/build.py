@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblattn.so")
 ARCH = os.environ.get("LATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "general.hip", "fast.hip", "misc.hip", "hla.hip", "loglinear.hip", "backward.hip"]
+SOURCES = ["api.hip", "general.hip", "fast.hip", "misc.hip", "hla.hip", "loglinear.hip", "backward.hip", "backward_chunk.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

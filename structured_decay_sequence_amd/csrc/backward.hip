@@ -117,6 +117,7 @@ struct BdArgs {
   const void* Y;      // V [BH, T, r_kv, dv] or dO [BH, T, dv]
   const float* init;  // [BH, dk, dv] or null (zero)
   float* out;         // [BH, N, dk, dv]
+  float* fin;         // [BH, dk, dv] or null: the value after the last step (final state, or dS_init)
 };
 
 template <typename TI, bool REV>
@@ -218,6 +219,15 @@ __global__ __launch_bounds__(kBdThreads) void bw_bound_kernel(BdArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[r][c] = nx[r][c];
     }
+  }
+  if (a.fin && rowok) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = n0 + 4 * ni + c;
+        if (col < dv) a.fin[(bh * dk + 4 * ri + r) * dv + col] = acc[r][c];
+      }
   }
 }
 
@@ -582,18 +592,27 @@ int64_t bw_walk_groups(const Problem& p) {
 
 // Workspace: the chunk operators (and what their prepare needs), the states
 // entering the chunks, the cotangents leaving them, then the walk buffers.
+// Workspace: chunk operators, the boundary states and cotangents, then either
+// the token walks' buffers or (chunked route) the final state and the chunked
+// kernels' buffers.
 struct BwLayout {
-  size_t ops, ckpt, gend, bufs, total;
+  size_t ops, ckpt, gend, bufs, sfin, chunk, total;
 };
 BwLayout bw_layout(const Problem& p) {
   BwLayout l{};
   const size_t states = static_cast<size_t>(p.BH * p.N) * p.dk * p.dv * sizeof(float);
-  const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored walk state
   l.ops = 0;
   l.ckpt = bw_align(f32_operators_bytes(p));
   l.gend = l.ckpt + bw_align(states);
   l.bufs = l.gend + bw_align(states);
-  l.total = l.bufs + static_cast<size_t>(bw_walk_groups(p)) * (p.C + 1) * st * sizeof(float);
+  if (backward_chunked(p)) {
+    l.sfin = l.bufs;
+    l.chunk = l.sfin + bw_align(static_cast<size_t>(p.BH) * p.dk * p.dv * sizeof(float));
+    l.total = l.chunk + backward_chunked_bytes(p);
+  } else {
+    const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored walk state
+    l.total = l.bufs + static_cast<size_t>(bw_walk_groups(p)) * (p.C + 1) * st * sizeof(float);
+  }
   return l;
 }
 
@@ -622,15 +641,17 @@ hipError_t launch_bw(const Problem& p, const BwArgs& a, size_t lds, hipStream_t 
   return p.r_kv <= 1 ? launch_bw_t<float, RAB, 1>(p, a, lds, s) : launch_bw_t<float, RAB, 2>(p, a, lds, s);
 }
 
+// sfin, dS0: where the final state and the initial state's cotangent go (or null)
 template <typename TI>
 hipError_t launch_boundary_scans(const Problem& p, const float* M, const void* v, const void* dout, const float* S0,
-                         const float* dfinal, float* ckpt, float* gend, hipStream_t s) {
+                         const float* dfinal, float* ckpt, float* gend, float* sfin, float* dS0, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(p.BH * ((p.dv + kBdBN - 1) / kBdBN));
-  hipLaunchKernelGGL((bw_bound_kernel<TI, false>), dim3(grid), dim3(kBdThreads), 0, s, BdArgs{p, M, v, S0, ckpt});
+  hipLaunchKernelGGL((bw_bound_kernel<TI, false>), dim3(grid), dim3(kBdThreads), 0, s,
+                     BdArgs{p, M, v, S0, ckpt, sfin});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bw_bound_kernel<TI, true>), dim3(grid), dim3(kBdThreads), 0, s,
-                     BdArgs{p, M, dout, dfinal, gend});
+                     BdArgs{p, M, dout, dfinal, gend, dS0});
   return hipGetLastError();
 }
 
@@ -649,8 +670,15 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   const float* M = nullptr;
   hipError_t e = f32_operators(p, q, k, ld, A, B, ws + l.ops, &M, s);
   if (e != hipSuccess) return e;
-  e = p.bf16 ? launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, s)
-             : launch_boundary_scans<float>(p, M, v, dout, S0, dfinal, ckpt, gend, s);
+  if (backward_chunked(p)) {
+    float* sfin = reinterpret_cast<float*>(ws + l.sfin);
+    e = launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, sfin, dS0, s);
+    if (e != hipSuccess) return e;
+    return launch_backward_chunked(p, q, k, v, ld, A, B, dout, ckpt, gend, sfin, dq, dK, dV, dld, dA, dB,
+                                   ws + l.chunk, s);
+  }
+  e = p.bf16 ? launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, nullptr, nullptr, s)
+             : launch_boundary_scans<float>(p, M, v, dout, S0, dfinal, ckpt, gend, nullptr, nullptr, s);
   if (e != hipSuccess) return e;
   BwArgs a{p, q, k, v, ld, A, B, dout, dfinal, S0, dq, dK, dV, dld, dA, dB, dS0, ckpt, gend,
            reinterpret_cast<float*>(ws + l.bufs)};

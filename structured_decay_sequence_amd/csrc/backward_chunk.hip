@@ -1,0 +1,662 @@
+// Chunked backward on bf16 MFMAs: bf16 storage, C = 64, r_kv = 1, r_ab <= 2,
+// d_k and d_v in {64, 128}.  Every chunk's gradients come from matrix
+// products over the chunk (the pages print no backward; this is the chain rule
+// of the chunk form of the HDLA note's "Key design 3" recurrence).
+//
+// Inside a chunk (tokens t = 0 .. C-1, G_t the chunk-local cumulative
+// log-decay, S_in the state entering, dS_end the cotangent of the state
+// leaving), with the decay-scaled operands of the forward
+//   Qt = q e^{G_t},  Kt = k e^{-G_t},  At = A e^{-G_t},  Bt = B e^{G_{t-1}},
+// and Gamma = e^{G_{C-1}}:
+//   forward rank rows  Y = B_t S_{t-1}:   (I + L) Y = Bt S_in + M_<(Bt Kt^T) V,
+//                       L = M_<(Bt At^T)  (strictly earlier tokens);
+//   adjoint rank rows  X = A_t dS_t:      (I + L^T) X = At Gamma dS_end + M_>=(At Qt^T) dO;
+//   gradients of the scaled operands (M_rel: keep key token s rel query token t)
+//     dQt = dO S_in^T     + M_<=(dO V^T) Kt  - M_<=(dO Y^T) At
+//     dKt = V (Gamma dS)^T + M_>=(V dO^T) Qt - M_>(V X^T) Bt
+//     dV  = Kt Gamma dS   + M_>=(Kt Qt^T) dO - M_>(Kt Bt^T) X
+//     dAt = -[Y (Gamma dS)^T + M_>=(Y dO^T) Qt - M_>(Y X^T) Bt]
+//     dBt = -[X S_in^T    + M_<(X V^T) Kt    - M_<(X Y^T) At]
+//   and the raw ones dq = dQt e^{G_t}, dk = dKt e^{-G_t}, dA = dAt e^{-G_t},
+//   dB = dBt e^{G_{t-1}}.  The log-decay enters only through those scalings and
+//   Gamma, so its gradient is (channel-wise, chunk-local reverse sum)
+//     dlog_decay_u = sum_{t >= u} [q dq - k dk - sum_r A dA + sum_r B_{t+1} dB_{t+1}]_t
+//                    + rowdot(dS_end, S_end) on the chunk's last token.
+// S_in and dS_end come from the chunk-boundary scans of the chunk operators.
+//
+// Kernels, each over all chunks: prep (scaled operands and bf16 copies in the
+// orientations their products read), tri (the blocks of L and the inverses
+// of its unit diagonal blocks), fused products (the two right-hand sides and
+// the five gradients: out = A W0 + sum_i s_i mask_i(A B_i^T) C_i, one wave per
+// 16 rows of A), solve (Y forward, X backward substitution, one wave per
+// 16 value columns), decay.  Every MFMA operand is a 16-byte read of a
+// row-major array in memory: A and B^T rows give the K-contiguous pieces of a
+// 16x16x32 product.  The scores A B_i^T are formed transposed, so that their
+// accumulator layout is directly the A operand of the following product.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lattn {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 cb8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 cb4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float cf4;
+
+constexpr int kCC = 64;   // chunk length of this path
+
+__device__ __forceinline__ cf4 cz4() { return cf4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ cf4 mfma_b(const cb8& x, const cb8& y, const cf4& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+}
+__device__ __forceinline__ cb4 to_b4(const cf4& v) {
+  cb4 r;
+  r[0] = (__bf16)v[0];
+  r[1] = (__bf16)v[1];
+  r[2] = (__bf16)v[2];
+  r[3] = (__bf16)v[3];
+  return r;
+}
+__device__ __forceinline__ cb8 cat8(const cb4& x, const cb4& y) {
+  cb8 r;
+  r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
+  r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
+  return r;
+}
+__device__ __forceinline__ cb4 zb4() {
+  cb4 r;
+  r[0] = r[1] = r[2] = r[3] = (__bf16)0.f;
+  return r;
+}
+
+// Per-chunk buffers of the chunked backward (element counts per chunk).
+struct BcBufs {
+  float* gc;                                  // [C][dk] cumulative log-decay
+  __bf16 *qt, *qtT, *kt, *ktT;                // [C][dk], [dk][C]
+  __bf16 *at, *atT, *bt, *btT;                // [NA][dk], [dk][NA]
+  __bf16 *vc, *vcT, *oc, *ocT;                // V, dO: [C][dv], [dv][C] (zero past the sequence)
+  __bf16 *si, *siT, *gd, *gdT;                // S_in, Gamma dS_end: [dk][dv], [dv][dk]
+  __bf16 *lb, *lbT;                           // L blocks below the diagonal, 16x16 tiles, and their transposes
+  float *dinv, *dinvT;                        // inverses of the unit diagonal blocks, and their transposes
+  float *ry, *rx;                             // right-hand sides in tile order [NA/16][dv/16][64 lanes][4]
+  __bf16 *y, *x, *xT;                         // [NA][dv], [NA][dv], [dv][NA]
+};
+
+struct BcSizes {
+  size_t gc, cdk, adk, cdv, kv, lt, dg, rhs, ydv;
+};
+BcSizes bc_sizes(const Problem& p) {
+  const size_t NA = static_cast<size_t>(kCC) * p.r_ab, NB = NA / 16;
+  BcSizes s;
+  s.gc = static_cast<size_t>(kCC) * p.dk;
+  s.cdk = static_cast<size_t>(kCC) * p.dk;
+  s.adk = NA * p.dk;
+  s.cdv = static_cast<size_t>(kCC) * p.dv;
+  s.kv = static_cast<size_t>(p.dk) * p.dv;
+  s.lt = (NB > 0 ? NB * (NB - 1) / 2 : 0) * 256;
+  s.dg = NB * 256;
+  s.rhs = NA * p.dv;
+  s.ydv = NA * p.dv;
+  return s;
+}
+size_t bc_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Lays the buffers out in ws (nullptr: only count).  Returns the bytes used.
+size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
+  const BcSizes z = bc_sizes(p);
+  const size_t J = static_cast<size_t>(p.BH * p.N);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = ws ? ws + off : nullptr;
+    off += bc_align(bytes);
+    return r;
+  };
+  BcBufs t{};
+  t.gc = reinterpret_cast<float*>(take(J * z.gc * 4));
+  __bf16** cd[] = {&t.qt, &t.qtT, &t.kt, &t.ktT};
+  for (auto* q : cd) *q = reinterpret_cast<__bf16*>(take(J * z.cdk * 2));
+  __bf16** ad[] = {&t.at, &t.atT, &t.bt, &t.btT};
+  for (auto* q : ad) *q = reinterpret_cast<__bf16*>(take(J * z.adk * 2));
+  __bf16** cv[] = {&t.vc, &t.vcT, &t.oc, &t.ocT};
+  for (auto* q : cv) *q = reinterpret_cast<__bf16*>(take(J * z.cdv * 2));
+  __bf16** kv[] = {&t.si, &t.siT, &t.gd, &t.gdT};
+  for (auto* q : kv) *q = reinterpret_cast<__bf16*>(take(J * z.kv * 2));
+  t.lb = reinterpret_cast<__bf16*>(take(J * z.lt * 2));
+  t.lbT = reinterpret_cast<__bf16*>(take(J * z.lt * 2));
+  t.dinv = reinterpret_cast<float*>(take(J * z.dg * 4));
+  t.dinvT = reinterpret_cast<float*>(take(J * z.dg * 4));
+  t.ry = reinterpret_cast<float*>(take(J * z.rhs * 4));
+  t.rx = reinterpret_cast<float*>(take(J * z.rhs * 4));
+  t.y = reinterpret_cast<__bf16*>(take(J * z.ydv * 2));
+  t.x = reinterpret_cast<__bf16*>(take(J * z.ydv * 2));
+  t.xT = reinterpret_cast<__bf16*>(take(J * z.ydv * 2));
+  if (b) *b = t;
+  return off;
+}
+
+// ---------------------------------------------------------------------------
+// prep: scaled operands (thread c owns channel c and walks the chunk's tokens,
+// packing eight rows at a time for the transposed copies), V and dO copies,
+// S_in and Gamma dS_end in bf16.
+struct BcPrepArgs {
+  Problem p;
+  const __bf16 *q, *k, *v, *A, *B, *dout;
+  const float* ld;
+  const float* ckpt;   // [BH, N, dk, dv] state entering each chunk
+  const float* gend;   // [BH, N, dk, dv] cotangent of the state leaving each chunk
+  BcBufs w;
+};
+
+template <int DK, int DV, int RAB>
+__global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
+  constexpr int NA = kCC * RAB;
+  __shared__ float gam[DK];   // Gamma = e^{G} at the chunk's last token
+  const Problem& p = a.p;
+  const int64_t job = blockIdx.x, bh = job / p.N, j = job % p.N, t0 = j * kCC;
+  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  const int64_t tok0 = bh * p.T + t0;
+  const int tid = threadIdx.x;
+  const BcBufs& w = a.w;
+  if (tid < DK) {
+    const int c = tid;
+    float g = 0.f;
+    float* gc = w.gc + job * kCC * DK;
+    __bf16 *qt = w.qt + job * kCC * DK, *qtT = w.qtT + job * kCC * DK;
+    __bf16 *kt = w.kt + job * kCC * DK, *ktT = w.ktT + job * kCC * DK;
+    __bf16 *at = w.at + job * NA * DK, *atT = w.atT + job * NA * DK;
+    __bf16 *bt = w.bt + job * NA * DK, *btT = w.btT + job * NA * DK;
+    cb8 pq, pk, pa, pb;
+    for (int t = 0; t < kCC; ++t) {
+      const bool ok = t < n;
+      const int64_t tok = tok0 + (ok ? t : 0);
+      const float l = ok ? (p.scalar ? a.ld[tok] : a.ld[tok * DK + c]) : 0.f;
+      const float gp = g;
+      g += l;
+      gc[t * DK + c] = g;
+      const float eg = expf(g), ng = expf(-g), egp = expf(gp);
+      const __bf16 vq = (__bf16)(ok ? (float)a.q[tok * DK + c] * eg : 0.f);
+      const __bf16 vk = (__bf16)(ok ? (float)a.k[tok * DK + c] * ng : 0.f);
+      qt[t * DK + c] = vq;
+      kt[t * DK + c] = vk;
+      pq[t & 7] = vq;
+      pk[t & 7] = vk;
+      if ((t & 7) == 7) {
+        *reinterpret_cast<cb8*>(qtT + c * kCC + t - 7) = pq;
+        *reinterpret_cast<cb8*>(ktT + c * kCC + t - 7) = pk;
+      }
+#pragma unroll
+      for (int r = 0; r < RAB; ++r) {
+        const int rr = t * RAB + r;
+        const __bf16 va = (__bf16)(ok ? (float)a.A[(tok * RAB + r) * DK + c] * ng : 0.f);
+        const __bf16 vb = (__bf16)(ok ? (float)a.B[(tok * RAB + r) * DK + c] * egp : 0.f);
+        at[rr * DK + c] = va;
+        bt[rr * DK + c] = vb;
+        pa[rr & 7] = va;
+        pb[rr & 7] = vb;
+        if ((rr & 7) == 7) {
+          *reinterpret_cast<cb8*>(atT + c * NA + rr - 7) = pa;
+          *reinterpret_cast<cb8*>(btT + c * NA + rr - 7) = pb;
+        }
+      }
+    }
+    gam[c] = expf(g);   // padding tokens add nothing: g is G at the last token
+  }
+  // V and dO: row-major copies (zero past the sequence) and transposes
+  {
+    __bf16 *vc = w.vc + job * kCC * DV, *oc = w.oc + job * kCC * DV;
+    for (int e = tid; e < kCC * DV / 8; e += 256) {
+      const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
+      cb8 xv, xo;
+      if (t < n) {
+        xv = *reinterpret_cast<const cb8*>(a.v + (tok0 + t) * DV + c8);
+        xo = *reinterpret_cast<const cb8*>(a.dout + (tok0 + t) * DV + c8);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xv[u] = xo[u] = (__bf16)0.f;
+      }
+      *reinterpret_cast<cb8*>(vc + t * DV + c8) = xv;
+      *reinterpret_cast<cb8*>(oc + t * DV + c8) = xo;
+    }
+    if (tid < DV) {
+      const int c = tid;
+      __bf16 *vcT = w.vcT + job * kCC * DV, *ocT = w.ocT + job * kCC * DV;
+      for (int t8 = 0; t8 < kCC; t8 += 8) {
+        cb8 xv, xo;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool ok = t8 + u < n;
+          xv[u] = ok ? a.v[(tok0 + t8 + u) * DV + c] : (__bf16)0.f;
+          xo[u] = ok ? a.dout[(tok0 + t8 + u) * DV + c] : (__bf16)0.f;
+        }
+        *reinterpret_cast<cb8*>(vcT + c * kCC + t8) = xv;
+        *reinterpret_cast<cb8*>(ocT + c * kCC + t8) = xo;
+      }
+    }
+  }
+  __syncthreads();   // gam
+  // S_in and Gamma dS_end, row-major and transposed
+  {
+    const float* S = a.ckpt + job * DK * DV;
+    const float* D = a.gend + job * DK * DV;
+    __bf16 *si = w.si + job * DK * DV, *gd = w.gd + job * DK * DV;
+    for (int e = tid; e < DK * DV / 4; e += 256) {
+      const int i = (e * 4) / DV;
+      const cf4 s4 = *reinterpret_cast<const cf4*>(S + e * 4);
+      const cf4 d4 = *reinterpret_cast<const cf4*>(D + e * 4);
+      const float gi = gam[i];
+      *reinterpret_cast<cb4*>(si + e * 4) = to_b4(s4);
+      *reinterpret_cast<cb4*>(gd + e * 4) = to_b4(cf4{gi * d4[0], gi * d4[1], gi * d4[2], gi * d4[3]});
+    }
+    if (tid < DV) {
+      const int c = tid;
+      __bf16 *siT = w.siT + job * DK * DV, *gdT = w.gdT + job * DK * DV;
+      for (int i8 = 0; i8 < DK; i8 += 8) {
+        cb8 xs, xd;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          xs[u] = (__bf16)S[(i8 + u) * DV + c];
+          xd[u] = (__bf16)(gam[i8 + u] * D[(i8 + u) * DV + c]);
+        }
+        *reinterpret_cast<cb8*>(siT + c * DK + i8) = xs;
+        *reinterpret_cast<cb8*>(gdT + c * DK + i8) = xd;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// tri: blocks (i, j <= i) of L = M_<(Bt At^T) (rank rows; tokens row / r_ab),
+// formed in both orientations so that each tile is stored with 8-byte writes;
+// the diagonal blocks in fp32, then the inverses of I + L_ii by forward
+// substitution (one thread per column).
+struct BcTriArgs {
+  Problem p;
+  BcBufs w;
+};
+
+template <int DK, int RAB>
+__global__ __launch_bounds__(256) void bwc_tri_kernel(BcTriArgs a) {
+  constexpr int NA = kCC * RAB, NB = NA / 16, NT = NB * (NB + 1) / 2, NTI = NB * (NB - 1) / 2;
+  __shared__ float dg[NB][256];
+  const int64_t job = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const __bf16* bt = a.w.bt + job * NA * DK;
+  const __bf16* at = a.w.at + job * NA * DK;
+  for (int idx = wave; idx < NT; idx += 4) {
+    int i = 0, jj = idx;
+    while (jj > i) {
+      jj -= i + 1;
+      ++i;
+    }
+    cf4 P = cz4(), Q = cz4();
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const cb8 bf = *reinterpret_cast<const cb8*>(bt + (16 * i + lr) * DK + 32 * ks + 8 * lg);
+      const cb8 af = *reinterpret_cast<const cb8*>(at + (16 * jj + lr) * DK + 32 * ks + 8 * lg);
+      P = mfma_b(bf, af, P);   // lane: L[16 i + 4 lg + e][16 jj + lr]
+      Q = mfma_b(af, bf, Q);   // lane: L[16 i + lr][16 jj + 4 lg + e]
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!((16 * i + 4 * lg + e) / RAB > (16 * jj + lr) / RAB)) P[e] = 0.f;
+      if (!((16 * i + lr) / RAB > (16 * jj + 4 * lg + e) / RAB)) Q[e] = 0.f;
+    }
+    if (jj < i) {
+      const int blk = i * (i - 1) / 2 + jj;
+      *reinterpret_cast<cb4*>(a.w.lb + (job * NTI + blk) * 256 + lr * 16 + 4 * lg) = to_b4(Q);
+      *reinterpret_cast<cb4*>(a.w.lbT + (job * NTI + blk) * 256 + lr * 16 + 4 * lg) = to_b4(P);
+    } else {
+      *reinterpret_cast<cf4*>(&dg[i][lr * 16 + 4 * lg]) = Q;
+    }
+  }
+  __syncthreads();
+  if (tid < NB * 16) {
+    const int blk = tid / 16, c = tid % 16;
+    float x[16];
+    float* Di = a.w.dinv + (job * NB + blk) * 256;
+    float* DiT = a.w.dinvT + (job * NB + blk) * 256;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) v -= dg[blk][r * 16 + m] * x[m];
+      x[r] = v;
+      Di[r * 16 + c] = v;
+      DiT[c * 16 + r] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i over one chunk,
+// one wave per 16 rows of A.  Kinds: the right-hand sides of Y and X, and the
+// five gradients (see the header).
+enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 };
+enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
+
+template <int KIND, int DK, int DV, int RAB>
+struct BcKindCfg {
+  static constexpr int NA = kCC * RAB;
+  static constexpr bool ROWS_A = KIND == kRhsY || KIND == kRhsX || KIND == kDa || KIND == kDb;
+  static constexpr int M = ROWS_A ? NA : kCC;                                  // rows of A
+  static constexpr int RA = ROWS_A ? RAB : 1;                                  // rows per token of A
+  static constexpr int KA = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? DK : DV;
+  static constexpr int NOUT = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? DV : DK;
+  static constexpr int MSK1 = (KIND == kRhsY || KIND == kDb) ? kLT : (KIND == kDq ? kLE : kGE);
+  static constexpr bool TERM2 = KIND >= kDq && RAB > 0;
+  static constexpr int MSK2 = KIND == kDq ? kLE : (KIND == kDb ? kLT : kGT);
+  static constexpr float SIGN = (KIND == kDa || KIND == kDb) ? -1.f : 1.f;
+};
+
+struct BcFusedArgs {
+  Problem p;
+  const __bf16 *A, *W0t, *B1, *C1T, *B2, *C2T;   // per-chunk arrays (row-major)
+  BcBufs w;
+  float* out;   // right-hand sides (tile order) or the gradient
+};
+
+template <int MASK>
+__device__ __forceinline__ bool bc_keep(int t, int s) {
+  return MASK == kLE ? s <= t : (MASK == kLT ? s < t : (MASK == kGE ? s >= t : s > t));
+}
+// true when no (t, s) of the token ranges survives
+template <int MASK>
+__device__ __forceinline__ bool bc_empty(int ta0, int ta1, int tb0, int tb1) {
+  return MASK == kLE ? tb0 > ta1 : (MASK == kLT ? tb0 >= ta1 : (MASK == kGE ? tb1 < ta0 : tb1 <= ta0));
+}
+
+template <int KIND, int DK, int DV, int RAB>
+__global__ __launch_bounds__(256) void bwc_fused_kernel(BcFusedArgs a) {
+  using K = BcKindCfg<KIND, DK, DV, RAB>;
+  constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
+  constexpr int RBW = K::M / 16;   // row blocks per chunk
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int64_t job = gw / RBW;
+  if (job >= p.BH * p.N) return;   // whole waves; this kernel has no barrier
+  const int rb = static_cast<int>(gw % RBW), r0 = 16 * rb;
+  const int64_t bh = job / p.N, jc = job % p.N, t0 = jc * kCC;
+  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  // rows of padding tokens only: no gradient to write (the right-hand sides
+  // are formed for them too, as zeros, since the solves read every row)
+  if (!(KIND == kRhsY || KIND == kRhsX) && r0 / K::RA >= n) return;
+  const __bf16* A = a.A + job * K::M * K::KA;
+  cb8 af[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const cb8*>(A + (r0 + lr) * K::KA + 32 * ks + 8 * lg);
+  cf4 acc[OT];
+  {
+    const __bf16* W = a.W0t + job * K::NOUT * K::KA;
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) {
+      acc[ot] = cz4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc[ot] = mfma_b(af[ks], *reinterpret_cast<const cb8*>(W + (16 * ot + lr) * K::KA + 32 * ks + 8 * lg), acc[ot]);
+    }
+  }
+  const int ta0 = r0 / K::RA, ta1 = (r0 + 15) / K::RA, trow = (r0 + lr) / K::RA;
+  // one score term: NB columns (R rows of B per token), mask, sign
+  auto term = [&](const __bf16* Bm, const __bf16* CT, auto nb_, auto rb_, auto mask_, float sg) {
+    constexpr int NBc = decltype(nb_)::value, RB = decltype(rb_)::value, MASK = decltype(mask_)::value;
+    const __bf16* Bj = Bm + job * NBc * K::KA;
+    const __bf16* Cj = CT + job * K::NOUT * NBc;
+#pragma unroll 1
+    for (int c0 = 0; c0 < NBc; c0 += 32) {
+      if (bc_empty<MASK>(ta0, ta1, c0 / RB, (c0 + 31) / RB)) continue;
+      cf4 s[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[h] = cz4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[h] = mfma_b(*reinterpret_cast<const cb8*>(Bj + (c0 + 16 * h + lr) * K::KA + 32 * ks + 8 * lg), af[ks], s[h]);
+        // lane: score(row r0 + lr, column c0 + 16 h + 4 lg + e)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[h][e] = bc_keep<MASK>(trow, (c0 + 16 * h + 4 * lg + e) / RB) ? sg * s[h][e] : 0.f;
+      }
+      const cb8 sf = cat8(to_b4(s[0]), to_b4(s[1]));
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) {
+        const __bf16* cr = Cj + (16 * ot + lr) * NBc + c0 + 4 * lg;
+        acc[ot] = mfma_b(sf, cat8(*reinterpret_cast<const cb4*>(cr), *reinterpret_cast<const cb4*>(cr + 16)), acc[ot]);
+      }
+    }
+  };
+  using I1 = std::integral_constant<int, 1>;
+  term(a.B1, a.C1T, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
+  if constexpr (K::TERM2)
+    term(a.B2, a.C2T, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
+         std::integral_constant<int, K::MSK2>{}, -1.f);
+
+  // ---- epilogue: lane holds rows r0 + 4 lg + e, column 16 ot + lr
+  if constexpr (KIND == kRhsY || KIND == kRhsX) {
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot)
+      *reinterpret_cast<cf4*>(a.out + (((job * (NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
+  } else {
+    const float* gc = a.w.gc + job * kCC * DK;
+    const int64_t tok0 = bh * p.T + t0;
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot) {
+      const int col = 16 * ot + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = r0 + 4 * lg + e;
+        const int t = row / K::RA;
+        if (t >= n) continue;
+        float v = K::SIGN * acc[ot][e];
+        if constexpr (KIND == kDq) v *= expf(gc[t * DK + col]);
+        if constexpr (KIND == kDk || KIND == kDa) v *= expf(-gc[t * DK + col]);
+        if constexpr (KIND == kDb) v *= t > 0 ? expf(gc[(t - 1) * DK + col]) : 1.f;
+        // row-major rows of the token's rank rows: dq [T][dk], dK [T][1][dk], dV [T][1][dv], dA/dB [T][r][dk]
+        a.out[(tok0 * K::RA + row) * K::NOUT + col] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// solve: one wave per (chunk, Y or X, 16 value columns).  Y: forward
+// substitution Y_i = D_i (R_i - sum_{j<i} L_ij Y_j); X: backward substitution
+// X_i = D_i^T (R_i - sum_{j>i} L_ji^T X_j).  The products pair two 16-row
+// blocks into one 16x16x32 MFMA (a lone block padded with zeros), with the
+// solved blocks fed back from registers as the B operand; the diagonal
+// inverses apply in fp32.
+struct BcSolveArgs {
+  Problem p;
+  BcBufs w;
+};
+
+template <int DK, int DV, int RAB>
+__global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
+  constexpr int NA = kCC * RAB, NB = NA / 16, NTI = NB * (NB - 1) / 2, NCT = DV / 16;
+  const Problem& p = a.p;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int64_t job = gw / (2 * NCT);
+  if (job >= p.BH * p.N) return;   // whole waves; no barrier in this kernel
+  const int rem = static_cast<int>(gw % (2 * NCT));
+  const bool isx = rem >= NCT;
+  const int ct = rem % NCT;
+  const BcBufs& w = a.w;
+  const float* R = (isx ? w.rx : w.ry) + job * NA * DV;
+  const __bf16* Lt = (isx ? w.lbT : w.lb) + job * NTI * 256;
+  const float* Dg = (isx ? w.dinvT : w.dinv) + job * NB * 256;
+  cb4 nb[NB];   // -solution blocks in bf16, the B operand of later blocks
+  auto ltile = [&](int blk) { return *reinterpret_cast<const cb4*>(Lt + blk * 256 + lr * 16 + 4 * lg); };
+  auto finish = [&](int i, cf4 acc) {
+    const cf4 dF = *reinterpret_cast<const cf4*>(Dg + i * 256 + lr * 16 + 4 * lg);
+    cf4 o = cz4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dF[e], acc[e], o, 0, 0, 0);
+    nb[i] = to_b4(cf4{-o[0], -o[1], -o[2], -o[3]});
+    // lane holds rows 16 i + 4 lg + e, column 16 ct + lr
+    __bf16* out = (isx ? w.x : w.y) + job * NA * DV;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[(16 * i + 4 * lg + e) * DV + 16 * ct + lr] = (__bf16)o[e];
+    if (isx) *reinterpret_cast<cb4*>(w.xT + job * NA * DV + (16 * ct + lr) * NA + 16 * i + 4 * lg) = to_b4(o);
+  };
+  if (!isx) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      cf4 acc = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+      const int base = i * (i - 1) / 2;   // tiles (i, 0 .. i-1)
+#pragma unroll
+      for (int jb = 0; jb + 1 < i; jb += 2)
+        acc = mfma_b(cat8(ltile(base + jb), ltile(base + jb + 1)), cat8(nb[jb], nb[jb + 1]), acc);
+      if (i % 2 == 1) acc = mfma_b(cat8(ltile(base + i - 1), zb4()), cat8(nb[i - 1], zb4()), acc);
+      finish(i, acc);
+    }
+  } else {
+#pragma unroll
+    for (int i = NB - 1; i >= 0; --i) {
+      cf4 acc = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+      // tiles (L_ji)^T for j = i+1 .. NB-1, stored at index j (j - 1) / 2 + i
+      int jb = i + 1;
+#pragma unroll
+      for (; jb + 1 < NB; jb += 2)
+        acc = mfma_b(cat8(ltile(jb * (jb - 1) / 2 + i), ltile((jb + 1) * jb / 2 + i)), cat8(nb[jb], nb[jb + 1]), acc);
+      if (jb < NB) acc = mfma_b(cat8(ltile(jb * (jb - 1) / 2 + i), zb4()), cat8(nb[jb], zb4()), acc);
+      finish(i, acc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decay: thread c owns channel c; reverse sum over the chunk's tokens.
+struct BcDecayArgs {
+  Problem p;
+  const __bf16 *q, *k, *A, *B;
+  const float *dq, *dK, *dA, *dB;
+  const float *ckpt, *gend, *sfin;
+  float* dld;
+};
+
+template <int DK, int DV, int RAB>
+__global__ __launch_bounds__(256) void bwc_decay_kernel(BcDecayArgs a) {
+  __shared__ float red[kCC][DK + 1];
+  const Problem& p = a.p;
+  const int64_t job = blockIdx.x, bh = job / p.N, j = job % p.N, t0 = j * kCC;
+  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  const int64_t tok0 = bh * p.T + t0;
+  const int tid = threadIdx.x;
+  if (tid < DK) {
+    const int c = tid;
+    const float* Se = j + 1 < p.N ? a.ckpt + (job + 1) * DK * DV : a.sfin + bh * DK * DV;
+    const float* dSe = a.gend + job * DK * DV;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int v4 = 0; v4 < DV; v4 += 4) {
+      const cf4 s = *reinterpret_cast<const cf4*>(Se + c * DV + v4);
+      const cf4 d = *reinterpret_cast<const cf4*>(dSe + c * DV + v4);
+      acc += s[0] * d[0] + s[1] * d[1] + s[2] * d[2] + s[3] * d[3];
+    }
+    for (int t = n - 1; t >= 0; --t) {
+      const int64_t tok = tok0 + t;
+      float g = (float)a.q[tok * DK + c] * a.dq[tok * DK + c] - (float)a.k[tok * DK + c] * a.dK[tok * DK + c];
+#pragma unroll
+      for (int r = 0; r < RAB; ++r) {
+        g -= (float)a.A[(tok * RAB + r) * DK + c] * a.dA[(tok * RAB + r) * DK + c];
+        if (t + 1 < n) g += (float)a.B[((tok + 1) * RAB + r) * DK + c] * a.dB[((tok + 1) * RAB + r) * DK + c];
+      }
+      acc += g;
+      if (p.scalar)
+        red[t][c] = acc;
+      else
+        a.dld[tok * DK + c] = acc;
+    }
+  }
+  if (p.scalar) {
+    __syncthreads();
+    if (tid < n) {
+      float s = 0.f;
+      for (int c = 0; c < DK; ++c) s += red[tid][c];
+      a.dld[tok0 + tid] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int RAB>
+hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const void* k, const void* v,
+                       const float* ld, const void* A, const void* B, const void* dout, const float* ckpt,
+                       const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld, float* dA,
+                       float* dB, hipStream_t s) {
+  const int64_t J = p.BH * p.N;
+  const unsigned jobs = static_cast<unsigned>(J);
+  auto bf = [](const void* x) { return static_cast<const __bf16*>(x); };
+  hipLaunchKernelGGL((bwc_prep_kernel<DK, DV, RAB>), dim3(jobs), dim3(256), 0, s,
+                     BcPrepArgs{p, bf(q), bf(k), bf(v), bf(A), bf(B), bf(dout), ld, ckpt, gend, w});
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto fused = [&](auto kind_, const __bf16* Am, const __bf16* W0t, const __bf16* B1, const __bf16* C1T,
+                   const __bf16* B2, const __bf16* C2T, float* out) {
+    constexpr int KIND = decltype(kind_)::value;
+    using K = BcKindCfg<KIND, DK, DV, RAB>;
+    const int64_t waves = J * (K::M / 16);
+    hipLaunchKernelGGL((bwc_fused_kernel<KIND, DK, DV, RAB>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
+                       0, s, BcFusedArgs{p, Am, W0t, B1, C1T, B2, C2T, w, out});
+    return hipGetLastError();
+  };
+  if constexpr (RAB > 0) {
+    hipLaunchKernelGGL((bwc_tri_kernel<DK, RAB>), dim3(jobs), dim3(256), 0, s, BcTriArgs{p, w});
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = fused(std::integral_constant<int, kRhsY>{}, w.bt, w.siT, w.kt, w.vcT, nullptr, nullptr, w.ry)) != hipSuccess)
+      return e;
+    if ((e = fused(std::integral_constant<int, kRhsX>{}, w.at, w.gdT, w.qt, w.ocT, nullptr, nullptr, w.rx)) != hipSuccess)
+      return e;
+    const int64_t sw = J * 2 * (DV / 16);
+    hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(static_cast<unsigned>((sw + 3) / 4)), dim3(256), 0, s,
+                       BcSolveArgs{p, w});
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = fused(std::integral_constant<int, kDq>{}, w.oc, w.si, w.vc, w.ktT, w.y, w.atT, dq)) != hipSuccess) return e;
+  if ((e = fused(std::integral_constant<int, kDk>{}, w.vc, w.gd, w.oc, w.qtT, w.x, w.btT, dK)) != hipSuccess) return e;
+  if ((e = fused(std::integral_constant<int, kDv>{}, w.kt, w.gdT, w.qt, w.ocT, w.bt, w.xT, dV)) != hipSuccess) return e;
+  if constexpr (RAB > 0) {
+    if ((e = fused(std::integral_constant<int, kDa>{}, w.y, w.gd, w.oc, w.qtT, w.x, w.btT, dA)) != hipSuccess) return e;
+    if ((e = fused(std::integral_constant<int, kDb>{}, w.x, w.si, w.vc, w.ktT, w.y, w.atT, dB)) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((bwc_decay_kernel<DK, DV, RAB>), dim3(jobs), dim3(256), 0, s,
+                     BcDecayArgs{p, bf(q), bf(k), bf(A), bf(B), dq, dK, dA, dB, ckpt, gend, sfin, dld});
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_chunked(const Problem& p) {
+  return p.bf16 && p.C == kCC && p.r_kv == 1 && p.r_ab >= 0 && p.r_ab <= 2 && (p.dk == 64 || p.dk == 128) &&
+         (p.dv == 64 || p.dv == 128);
+}
+
+size_t backward_chunked_bytes(const Problem& p) { return bc_layout(p, nullptr, nullptr); }
+
+hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
+                                   const void* A, const void* B, const void* dout, const float* ckpt,
+                                   const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld,
+                                   float* dA, float* dB, void* ws, hipStream_t s) {
+  if (p.BH * p.N == 0) return hipSuccess;
+  if (!backward_chunked(p)) return hipErrorInvalidValue;
+  BcBufs w;
+  bc_layout(p, static_cast<char*>(ws), &w);
+#define LATTN_BC(DK_, DV_, RAB_)                                                                                  \
+  if (p.dk == DK_ && p.dv == DV_ && p.r_ab == RAB_)                                                              \
+    return launch_bc_t<DK_, DV_, RAB_>(p, w, q, k, v, ld, A, B, dout, ckpt, gend, sfin, dq, dK, dV, dld, dA, dB, s);
+  LATTN_BC(128, 128, 2) LATTN_BC(128, 128, 1) LATTN_BC(128, 128, 0)
+  LATTN_BC(64, 64, 2) LATTN_BC(64, 64, 1) LATTN_BC(64, 64, 0)
+  LATTN_BC(128, 64, 2) LATTN_BC(128, 64, 1) LATTN_BC(128, 64, 0)
+  LATTN_BC(64, 128, 2) LATTN_BC(64, 128, 1) LATTN_BC(64, 128, 0)
+#undef LATTN_BC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lattn

@@ -101,6 +101,17 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
                             const void* B, const void* v, const float* lam, void* out, void* workspace,
                             hipStream_t s);
 
+// Chunked backward on bf16 MFMAs (bf16 storage, C = 64, r_kv = 1, r_ab <= 2,
+// d_k, d_v in {64, 128}), from the chunk-boundary states ckpt, cotangents gend
+// and the final state sfin; writes every gradient but dS0 (which the reverse
+// boundary scan gives).  ws: backward_chunked_bytes(p) bytes.
+bool backward_chunked(const Problem& p);
+size_t backward_chunked_bytes(const Problem& p);
+hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
+                                   const void* A, const void* B, const void* dout, const float* ckpt,
+                                   const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld,
+                                   float* dA, float* dB, void* ws, hipStream_t s);
+
 // Backward pass, token-serial with chunk checkpoints: d_k, d_v <= 128,
 // r_ab <= 4, r_kv <= 2; gradients in fp32.
 bool backward_supported(const Problem& p);

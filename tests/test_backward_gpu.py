@@ -28,8 +28,15 @@ CASES = [
     (1, 1, 1, 32, 32, 1, 1, 16, "fp32", "channel", True),
     # more (batch, head, chunk) jobs than resident workgroups (276 > 256)
     (1, 4, 1100, 32, 32, 2, 1, 16, "fp32", "channel", True),
-    # bf16 operators from the MFMA prepare, 65 chunks per head with a 4-token tail
+    # bf16 storage at C 64, r_kv 1, d_k, d_v in {64, 128}: the chunked route on
+    # bf16 MFMAs (65 chunks per head with a 4-token tail here)
     (2, 3, 4100, 64, 64, 1, 1, 64, "bf16", "scalar", True),
+    (1, 2, 150, 64, 64, 2, 1, 64, "bf16", "channel", True),
+    (1, 1, 200, 128, 128, 2, 1, 64, "bf16", "channel", True),
+    (2, 1, 100, 64, 128, 0, 1, 64, "bf16", "channel", False),
+    (1, 1, 130, 128, 64, 1, 1, 64, "bf16", "scalar", True),
+    (1, 1, 1, 64, 64, 2, 1, 64, "bf16", "channel", True),
+    (1, 1, 64, 128, 128, 2, 1, 64, "bf16", "scalar", False),
 ]
 
 
@@ -111,12 +118,14 @@ def test_backward_empty_sequence_passes_the_state_gradient():
     assert np.array_equal(host(g["dinitial_state"]), dfin)
 
 
-def test_backward_repeatable():
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_backward_repeatable(chunk):
+    """Two calls give bitwise equal gradients (chunk 64: the chunked route)."""
     raw = workloads.generic_raw(1, 2, 90, 64, 64, 2, 1, "bf16", "channel", seed=4)
     dout = workloads.round_bf16(np.random.default_rng(4).standard_normal((1, 2, 90, 64)).astype(np.float32))
     run = lambda: lattn.chunk_bwd(dev(raw["q"], torch.bfloat16), dev(raw["K"], torch.bfloat16),
                                   dev(raw["V"], torch.bfloat16), dev(raw["log_decay"]), dev(raw["A"], torch.bfloat16),
-                                  dev(raw["B"], torch.bfloat16), dev(dout, torch.bfloat16), chunk=32)
+                                  dev(raw["B"], torch.bfloat16), dev(dout, torch.bfloat16), chunk=chunk)
     a, b = run(), run()
     torch.cuda.synchronize()
     for n in a:
