@@ -350,11 +350,18 @@ struct BcKindCfg {
   static constexpr float SIGN = (KIND == kDa || KIND == kDb) ? -1.f : 1.f;
 };
 
-struct BcFusedArgs {
+// A group: one or two kinds whose products read the same B-side operands
+// (W0t, B1, C1T, B2, C2T), one workgroup per chunk.  The workgroup stages
+// those operands in LDS once (rows padded by 16 bf16, which keeps the 16-byte
+// fragment reads over 16 rows free of bank conflicts); each wave then forms
+// 16 rows of one kind's output, reading its A rows from memory and every
+// other fragment from LDS.  The pairs: (dK, dA) and (dQ, dB).
+struct BcGroupArgs {
   Problem p;
-  const __bf16 *A, *W0t, *B1, *C1T, *B2, *C2T;   // per-chunk arrays (row-major)
+  const __bf16 *Aa, *Ab;                          // A rows of the two kinds (Ab: null for one kind)
+  const __bf16 *W0t, *B1, *C1T, *B2, *C2T;        // per-chunk arrays (row-major)
   BcBufs w;
-  float* out;   // right-hand sides (tile order) or the gradient
+  float *outa, *outb;                             // right-hand sides (tile order) or gradients
 };
 
 template <int MASK>
@@ -367,81 +374,85 @@ __device__ __forceinline__ bool bc_empty(int ta0, int ta1, int tb0, int tb1) {
   return MASK == kLE ? tb0 > ta1 : (MASK == kLT ? tb0 >= ta1 : (MASK == kGE ? tb1 < ta0 : tb1 <= ta0));
 }
 
+// LDS layout of a group's staged operands (bf16 elements).
 template <int KIND, int DK, int DV, int RAB>
-__global__ __launch_bounds__(256) void bwc_fused_kernel(BcFusedArgs a) {
+struct BcStage {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
+  static constexpr int NA = K::NA, KA = K::KA, NOUT = K::NOUT;
+  static constexpr int LW = KA + 16, L1 = kCC + 16, L2 = NA + 16;
+  static constexpr int OW = 0, OB1 = OW + NOUT * LW, OC1 = OB1 + kCC * LW;
+  static constexpr int OB2 = OC1 + NOUT * L1, OC2 = OB2 + (K::TERM2 ? NA * LW : 0);
+  static constexpr int TOTAL = OC2 + (K::TERM2 ? NOUT * L2 : 0);
+};
+
+// 16 rows (block rb) of kind KIND's output for chunk job, operands in LDS.
+template <int KIND, int DK, int DV, int RAB>
+__device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, const __bf16* Ag,
+                                        const __bf16* lds, const BcBufs& w, float* out, int lane) {
+  using K = BcKindCfg<KIND, DK, DV, RAB>;
+  using L = BcStage<KIND, DK, DV, RAB>;
   constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
-  constexpr int RBW = K::M / 16;   // row blocks per chunk
-  const Problem& p = a.p;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const int64_t job = gw / RBW;
-  if (job >= p.BH * p.N) return;   // whole waves; this kernel has no barrier
-  const int rb = static_cast<int>(gw % RBW), r0 = 16 * rb;
+  const int r0 = 16 * rb;
   const int64_t bh = job / p.N, jc = job % p.N, t0 = jc * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
   // rows of padding tokens only: no gradient to write (the right-hand sides
   // are formed for them too, as zeros, since the solves read every row)
   if (!(KIND == kRhsY || KIND == kRhsX) && r0 / K::RA >= n) return;
-  const __bf16* A = a.A + job * K::M * K::KA;
+  const __bf16* A = Ag + job * K::M * K::KA;
   cb8 af[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const cb8*>(A + (r0 + lr) * K::KA + 32 * ks + 8 * lg);
   cf4 acc[OT];
-  {
-    const __bf16* W = a.W0t + job * K::NOUT * K::KA;
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot) {
-      acc[ot] = cz4();
+  for (int ot = 0; ot < OT; ++ot) {
+    acc[ot] = cz4();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc[ot] = mfma_b(af[ks], *reinterpret_cast<const cb8*>(W + (16 * ot + lr) * K::KA + 32 * ks + 8 * lg), acc[ot]);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      acc[ot] = mfma_b(af[ks], *reinterpret_cast<const cb8*>(lds + L::OW + (16 * ot + lr) * L::LW + 32 * ks + 8 * lg),
+                       acc[ot]);
   }
   const int ta0 = r0 / K::RA, ta1 = (r0 + 15) / K::RA, trow = (r0 + lr) / K::RA;
-  // one score term: NB columns (R rows of B per token), mask, sign
-  auto term = [&](const __bf16* Bm, const __bf16* CT, auto nb_, auto rb_, auto mask_, float sg) {
+  // one score term: NB columns (RB rows of B per token), mask, sign
+  auto term = [&](int oB, int oC, int LC, auto nb_, auto rb_, auto mask_, float sg) {
     constexpr int NBc = decltype(nb_)::value, RB = decltype(rb_)::value, MASK = decltype(mask_)::value;
-    const __bf16* Bj = Bm + job * NBc * K::KA;
-    const __bf16* Cj = CT + job * K::NOUT * NBc;
 #pragma unroll 1
     for (int c0 = 0; c0 < NBc; c0 += 32) {
       if (bc_empty<MASK>(ta0, ta1, c0 / RB, (c0 + 31) / RB)) continue;
-      cf4 s[2];
+      cf4 s2[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        s[h] = cz4();
+        s2[h] = cz4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          s[h] = mfma_b(*reinterpret_cast<const cb8*>(Bj + (c0 + 16 * h + lr) * K::KA + 32 * ks + 8 * lg), af[ks], s[h]);
+          s2[h] = mfma_b(*reinterpret_cast<const cb8*>(lds + oB + (c0 + 16 * h + lr) * L::LW + 32 * ks + 8 * lg), af[ks],
+                         s2[h]);
         // lane: score(row r0 + lr, column c0 + 16 h + 4 lg + e)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s[h][e] = bc_keep<MASK>(trow, (c0 + 16 * h + 4 * lg + e) / RB) ? sg * s[h][e] : 0.f;
+          s2[h][e] = bc_keep<MASK>(trow, (c0 + 16 * h + 4 * lg + e) / RB) ? sg * s2[h][e] : 0.f;
       }
-      const cb8 sf = cat8(to_b4(s[0]), to_b4(s[1]));
+      const cb8 sf = cat8(to_b4(s2[0]), to_b4(s2[1]));
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot) {
-        const __bf16* cr = Cj + (16 * ot + lr) * NBc + c0 + 4 * lg;
+        const __bf16* cr = lds + oC + (16 * ot + lr) * LC + c0 + 4 * lg;
         acc[ot] = mfma_b(sf, cat8(*reinterpret_cast<const cb4*>(cr), *reinterpret_cast<const cb4*>(cr + 16)), acc[ot]);
       }
     }
   };
   using I1 = std::integral_constant<int, 1>;
-  term(a.B1, a.C1T, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
+  term(L::OB1, L::OC1, L::L1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
   if constexpr (K::TERM2)
-    term(a.B2, a.C2T, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
+    term(L::OB2, L::OC2, L::L2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
          std::integral_constant<int, K::MSK2>{}, -1.f);
 
   // ---- epilogue: lane holds rows r0 + 4 lg + e, column 16 ot + lr
   if constexpr (KIND == kRhsY || KIND == kRhsX) {
 #pragma unroll
     for (int ot = 0; ot < OT; ++ot)
-      *reinterpret_cast<cf4*>(a.out + (((job * (NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
+      *reinterpret_cast<cf4*>(out + (((job * (NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
   } else {
-    const float* gc = a.w.gc + job * kCC * DK;
+    const float* gc = w.gc + job * kCC * DK;
     const int64_t tok0 = bh * p.T + t0;
 #pragma unroll
     for (int ot = 0; ot < OT; ++ot) {
@@ -456,9 +467,51 @@ __global__ __launch_bounds__(256) void bwc_fused_kernel(BcFusedArgs a) {
         if constexpr (KIND == kDk || KIND == kDa) v *= expf(-gc[t * DK + col]);
         if constexpr (KIND == kDb) v *= t > 0 ? expf(gc[(t - 1) * DK + col]) : 1.f;
         // row-major rows of the token's rank rows: dq [T][dk], dK [T][1][dk], dV [T][1][dv], dA/dB [T][r][dk]
-        a.out[(tok0 * K::RA + row) * K::NOUT + col] = v;
+        out[(tok0 * K::RA + row) * K::NOUT + col] = v;
       }
     }
+  }
+}
+
+template <int KA_, int KB_>
+struct BcGroupWaves {
+  template <int DK, int DV, int RAB>
+  static constexpr int count() {
+    return BcKindCfg<KA_, DK, DV, RAB>::M / 16 + (KB_ >= 0 ? BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::M / 16 : 0);
+  }
+};
+
+template <int KA_, int KB_, int DK, int DV, int RAB, int NW>
+__global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
+  using K = BcKindCfg<KA_, DK, DV, RAB>;
+  using L = BcStage<KA_, DK, DV, RAB>;
+  constexpr int WA = K::M / 16;
+  extern __shared__ __align__(16) unsigned char smem_[];
+  __bf16* lds = reinterpret_cast<__bf16*>(smem_);
+  const int64_t job = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // stage a per-chunk row-major array (rows x cols) into LDS rows of ld elements
+  auto stage = [&](const __bf16* g, int rows, int cols, int off, int ld) {
+    const __bf16* src = g + job * rows * cols;
+    const int pieces = rows * cols / 8, pr = cols / 8;
+    for (int i = tid; i < pieces; i += 64 * NW) {
+      const int r = i / pr, c8 = (i - r * pr) * 8;
+      *reinterpret_cast<cb8*>(lds + off + r * ld + c8) = *reinterpret_cast<const cb8*>(src + r * cols + c8);
+    }
+  };
+  stage(a.W0t, K::NOUT, K::KA, L::OW, L::LW);
+  stage(a.B1, kCC, K::KA, L::OB1, L::LW);
+  stage(a.C1T, K::NOUT, kCC, L::OC1, L::L1);
+  if constexpr (K::TERM2) {
+    stage(a.B2, K::NA, K::KA, L::OB2, L::LW);
+    stage(a.C2T, K::NOUT, K::NA, L::OC2, L::L2);
+  }
+  __syncthreads();
+  if (wave < WA) {
+    bc_rows<KA_, DK, DV, RAB>(a.p, job, wave, a.Aa, lds, a.w, a.outa, lane);
+  } else if constexpr (KB_ >= 0) {
+    bc_rows<KB_, DK, DV, RAB>(a.p, job, wave - WA, a.Ab, lds, a.w, a.outb, lane);
   }
 }
 
@@ -598,34 +651,51 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
                      BcPrepArgs{p, bf(q), bf(k), bf(v), bf(A), bf(B), bf(dout), ld, ckpt, gend, w});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  auto fused = [&](auto kind_, const __bf16* Am, const __bf16* W0t, const __bf16* B1, const __bf16* C1T,
-                   const __bf16* B2, const __bf16* C2T, float* out) {
-    constexpr int KIND = decltype(kind_)::value;
-    using K = BcKindCfg<KIND, DK, DV, RAB>;
-    const int64_t waves = J * (K::M / 16);
-    hipLaunchKernelGGL((bwc_fused_kernel<KIND, DK, DV, RAB>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256),
-                       0, s, BcFusedArgs{p, Am, W0t, B1, C1T, B2, C2T, w, out});
+  // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
+  auto group = [&](auto ka_, auto kb_, const __bf16* Aa, const __bf16* Ab, const __bf16* W0t, const __bf16* B1,
+                   const __bf16* C1T, const __bf16* B2, const __bf16* C2T, float* outa, float* outb) {
+    constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
+    constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
+    using L = BcStage<KA_, DK, DV, RAB>;
+    const void* fn = reinterpret_cast<const void*>(bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>);
+    const size_t lds = static_cast<size_t>(L::TOTAL) * 2;
+    hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
+                       BcGroupArgs{p, Aa, Ab, W0t, B1, C1T, B2, C2T, w, outa, outb});
     return hipGetLastError();
   };
+  using KN = std::integral_constant<int, -1>;
   if constexpr (RAB > 0) {
     hipLaunchKernelGGL((bwc_tri_kernel<DK, RAB>), dim3(jobs), dim3(256), 0, s, BcTriArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = fused(std::integral_constant<int, kRhsY>{}, w.bt, w.siT, w.kt, w.vcT, nullptr, nullptr, w.ry)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, w.bt, nullptr, w.siT, w.kt, w.vcT, nullptr, nullptr,
+                   w.ry, nullptr)) != hipSuccess)
       return e;
-    if ((e = fused(std::integral_constant<int, kRhsX>{}, w.at, w.gdT, w.qt, w.ocT, nullptr, nullptr, w.rx)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, w.at, nullptr, w.gdT, w.qt, w.ocT, nullptr, nullptr,
+                   w.rx, nullptr)) != hipSuccess)
       return e;
     const int64_t sw = J * 2 * (DV / 16);
     hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(static_cast<unsigned>((sw + 3) / 4)), dim3(256), 0, s,
                        BcSolveArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, w.vc, w.y, w.gd, w.oc,
+                   w.qtT, w.x, w.btT, dK, dA)) != hipSuccess)
+      return e;
+    if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, w.oc, w.x, w.si, w.vc,
+                   w.ktT, w.y, w.atT, dq, dB)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = group(std::integral_constant<int, kDk>{}, KN{}, w.vc, nullptr, w.gd, w.oc, w.qtT, nullptr, nullptr, dK,
+                   nullptr)) != hipSuccess)
+      return e;
+    if ((e = group(std::integral_constant<int, kDq>{}, KN{}, w.oc, nullptr, w.si, w.vc, w.ktT, nullptr, nullptr, dq,
+                   nullptr)) != hipSuccess)
+      return e;
   }
-  if ((e = fused(std::integral_constant<int, kDq>{}, w.oc, w.si, w.vc, w.ktT, w.y, w.atT, dq)) != hipSuccess) return e;
-  if ((e = fused(std::integral_constant<int, kDk>{}, w.vc, w.gd, w.oc, w.qtT, w.x, w.btT, dK)) != hipSuccess) return e;
-  if ((e = fused(std::integral_constant<int, kDv>{}, w.kt, w.gdT, w.qt, w.ocT, w.bt, w.xT, dV)) != hipSuccess) return e;
-  if constexpr (RAB > 0) {
-    if ((e = fused(std::integral_constant<int, kDa>{}, w.y, w.gd, w.oc, w.qtT, w.x, w.btT, dA)) != hipSuccess) return e;
-    if ((e = fused(std::integral_constant<int, kDb>{}, w.x, w.si, w.vc, w.ktT, w.y, w.atT, dB)) != hipSuccess) return e;
-  }
+  if ((e = group(std::integral_constant<int, kDv>{}, KN{}, w.kt, nullptr, w.gdT, w.qt, w.ocT, w.bt, w.xT, dV,
+                 nullptr)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL((bwc_decay_kernel<DK, DV, RAB>), dim3(jobs), dim3(256), 0, s,
                      BcDecayArgs{p, bf(q), bf(k), bf(A), bf(B), dq, dK, dA, dB, ckpt, gend, sfin, dld});
   return hipGetLastError();
