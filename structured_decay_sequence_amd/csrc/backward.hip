@@ -641,15 +641,20 @@ hipError_t launch_bw(const Problem& p, const BwArgs& a, size_t lds, hipStream_t 
   return p.r_kv <= 1 ? launch_bw_t<float, RAB, 1>(p, a, lds, s) : launch_bw_t<float, RAB, 2>(p, a, lds, s);
 }
 
-// sfin, dS0: where the final state and the initial state's cotangent go (or null)
+// sfin, dS0: where the final state and the initial state's cotangent go (or
+// null); fwd false: the cotangent scan only.
 template <typename TI>
 hipError_t launch_boundary_scans(const Problem& p, const float* M, const void* v, const void* dout, const float* S0,
-                         const float* dfinal, float* ckpt, float* gend, float* sfin, float* dS0, hipStream_t s) {
+                         const float* dfinal, float* ckpt, float* gend, float* sfin, float* dS0, hipStream_t s,
+                         bool fwd = true) {
   const unsigned grid = static_cast<unsigned>(p.BH * ((p.dv + kBdBN - 1) / kBdBN));
-  hipLaunchKernelGGL((bw_bound_kernel<TI, false>), dim3(grid), dim3(kBdThreads), 0, s,
-                     BdArgs{p, M, v, S0, ckpt, sfin});
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (fwd) {
+    hipLaunchKernelGGL((bw_bound_kernel<TI, false>), dim3(grid), dim3(kBdThreads), 0, s,
+                       BdArgs{p, M, v, S0, ckpt, sfin});
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((bw_bound_kernel<TI, true>), dim3(grid), dim3(kBdThreads), 0, s,
                      BdArgs{p, M, dout, dfinal, gend, dS0});
   return hipGetLastError();
@@ -671,8 +676,13 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   hipError_t e = f32_operators(p, q, k, ld, A, B, ws + l.ops, &M, s);
   if (e != hipSuccess) return e;
   if (backward_chunked(p)) {
+    // The states entering the chunks come from the bf16 MFMA scan over the
+    // bf16 operators (which f32_operators left at the front of its region);
+    // the cotangents from the fp32 reverse scan.
     float* sfin = reinterpret_cast<float*>(ws + l.sfin);
-    e = launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, sfin, dS0, s);
+    e = fast_scan(p, ws + l.ops, v, nullptr, sfin, S0, s, ckpt);
+    if (e != hipSuccess) return e;
+    e = launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, sfin, dS0, s, false);
     if (e != hipSuccess) return e;
     return launch_backward_chunked(p, q, k, v, ld, A, B, dout, ckpt, gend, sfin, dq, dK, dV, dld, dA, dB,
                                    ws + l.chunk, s);

@@ -22,17 +22,19 @@
 //   Gamma, so its gradient is (channel-wise, chunk-local reverse sum)
 //     dlog_decay_u = sum_{t >= u} [q dq - k dk - sum_r A dA + sum_r B_{t+1} dB_{t+1}]_t
 //                    + rowdot(dS_end, S_end) on the chunk's last token.
-// S_in and dS_end come from the chunk-boundary scans of the chunk operators.
+// S_in and dS_end come from the chunk-boundary scans.
 //
-// Kernels, each over all chunks: prep (scaled operands and bf16 copies in the
-// orientations their products read), tri (the blocks of L and the inverses
-// of its unit diagonal blocks), fused products (the two right-hand sides and
-// the five gradients: out = A W0 + sum_i s_i mask_i(A B_i^T) C_i, one wave per
-// 16 rows of A), solve (Y forward, X backward substitution, one wave per
-// 16 value columns), decay.  Every MFMA operand is a 16-byte read of a
-// row-major array in memory: A and B^T rows give the K-contiguous pieces of a
-// 16x16x32 product.  The scores A B_i^T are formed transposed, so that their
-// accumulator layout is directly the A operand of the following product.
+// Kernels, each over all chunks: prep (G and the scaled operands, row-major
+// bf16), tri (the blocks of L and the inverses of its unit diagonal blocks),
+// grouped products (the two right-hand sides, then the five gradients:
+// out = A W0 + sum_i s_i mask_i(A B_i^T) C_i), solve (Y forward, X backward
+// substitution, one wave per 16 value columns), decay.  A product group stages
+// its chunk's B-side operands in LDS row-major, straight from where they live
+// (the prep's arrays, the V and dO rows of the sequence, the fp32 boundary
+// states); operands needed transposed are read with the transposing LDS read.
+// Every contraction uses one K order: K values 32 ks + 16 h + 4 g + e sit at
+// element 4 h + e of lane group g, so that a score tile pair in accumulator
+// layout is directly the A operand of the product that follows.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,6 +44,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 cb8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 cb4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float cf4;
+typedef short ci16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCC = 64;   // chunk length of this path
 
@@ -68,43 +71,45 @@ __device__ __forceinline__ cb4 zb4() {
   r[0] = r[1] = r[2] = r[3] = (__bf16)0.f;
   return r;
 }
-
-// Per-chunk buffers of the chunked backward (element counts per chunk).
-struct BcBufs {
-  float* gc;                                  // [C][dk] cumulative log-decay
-  __bf16 *qt, *qtT, *kt, *ktT;                // [C][dk], [dk][C]
-  __bf16 *at, *atT, *bt, *btT;                // [NA][dk], [dk][NA]
-  __bf16 *vc, *vcT, *oc, *ocT;                // V, dO: [C][dv], [dv][C] (zero past the sequence)
-  __bf16 *si, *siT, *gd, *gdT;                // S_in, Gamma dS_end: [dk][dv], [dv][dk]
-  __bf16 *lb, *lbT;                           // L blocks below the diagonal, 16x16 tiles, and their transposes
-  float *dinv, *dinvT;                        // inverses of the unit diagonal blocks, and their transposes
-  float *ry, *rx;                             // right-hand sides in tile order [NA/16][dv/16][64 lanes][4]
-  __bf16 *y, *x, *xT;                         // [NA][dv], [NA][dv], [dv][NA]
-};
-
-struct BcSizes {
-  size_t gc, cdk, adk, cdv, kv, lt, dg, rhs, ydv;
-};
-BcSizes bc_sizes(const Problem& p) {
-  const size_t NA = static_cast<size_t>(kCC) * p.r_ab, NB = NA / 16;
-  BcSizes s;
-  s.gc = static_cast<size_t>(kCC) * p.dk;
-  s.cdk = static_cast<size_t>(kCC) * p.dk;
-  s.adk = NA * p.dk;
-  s.cdv = static_cast<size_t>(kCC) * p.dv;
-  s.kv = static_cast<size_t>(p.dk) * p.dv;
-  s.lt = (NB > 0 ? NB * (NB - 1) / 2 : 0) * 256;
-  s.dg = NB * 256;
-  s.rhs = NA * p.dv;
-  s.ydv = NA * p.dv;
-  return s;
+// The fragment of a K-contiguous row in the shared K order: the K values
+// 32 ks + 4 g + (0..3) and 32 ks + 16 + 4 g + (0..3) for lane group g.
+__device__ __forceinline__ cb8 rowfrag(const __bf16* row, int ks, int lane) {
+  const int g = lane >> 4;
+  return cat8(*reinterpret_cast<const cb4*>(row + 32 * ks + 4 * g),
+              *reinterpret_cast<const cb4*>(row + 32 * ks + 16 + 4 * g));
 }
+// Transposing LDS read of a row-major bf16 array (ld elements per row): lane
+// (g, i) receives X[r0 + 4 g + e][c0 + i], e = 0..3.  The 64-bit transposing
+// read works on groups of 16 lanes, element e of lane (g, i) being the
+// (i % 4)-th value fetched by lane (g, 4 e + i / 4); so lane (g, j) fetches
+// X[r0 + 4 g + j / 4][c0 + 4 (j % 4) .. + 3].
+__device__ __forceinline__ cb4 ltr4(const __bf16* X, int ld, int r0, int c0, int lane) {
+  const int g = lane >> 4, jl = lane & 15;
+  const __bf16* ptr = X + (r0 + 4 * g + (jl >> 2)) * ld + c0 + 4 * (jl & 3);
+  const ci16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ci16x4*)(ptr));
+  return __builtin_bit_cast(cb4, r);
+}
+
+// Per-chunk buffers of the chunked backward.
+struct BcBufs {
+  float* gc;                 // [C][dk] cumulative log-decay
+  float* gam;                // [dk] e^{G} at the chunk's last token
+  __bf16 *qt, *kt;           // [C][dk]
+  __bf16 *at, *bt;           // [NA][dk]
+  __bf16 *lb, *lbT;          // L blocks below the diagonal, 16x16 row-major tiles, and their transposes
+  float *dinv, *dinvT;       // inverses of the unit diagonal blocks, and their transposes
+  float *ry, *rx;            // right-hand sides in tile order [NA/16][dv/16][64 lanes][4]
+  __bf16 *y, *x;             // [NA][dv]
+};
+
 size_t bc_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Lays the buffers out in ws (nullptr: only count).  Returns the bytes used.
 size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
-  const BcSizes z = bc_sizes(p);
   const size_t J = static_cast<size_t>(p.BH * p.N);
+  const size_t NA = static_cast<size_t>(kCC) * p.r_ab, NB = NA / 16;
+  const size_t cdk = static_cast<size_t>(kCC) * p.dk, adk = NA * p.dk, ndv = NA * p.dv;
+  const size_t lt = (NB > 0 ? NB * (NB - 1) / 2 : 0) * 256;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* r = ws ? ws + off : nullptr;
@@ -112,154 +117,124 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
     return r;
   };
   BcBufs t{};
-  t.gc = reinterpret_cast<float*>(take(J * z.gc * 4));
-  __bf16** cd[] = {&t.qt, &t.qtT, &t.kt, &t.ktT};
-  for (auto* q : cd) *q = reinterpret_cast<__bf16*>(take(J * z.cdk * 2));
-  __bf16** ad[] = {&t.at, &t.atT, &t.bt, &t.btT};
-  for (auto* q : ad) *q = reinterpret_cast<__bf16*>(take(J * z.adk * 2));
-  __bf16** cv[] = {&t.vc, &t.vcT, &t.oc, &t.ocT};
-  for (auto* q : cv) *q = reinterpret_cast<__bf16*>(take(J * z.cdv * 2));
-  __bf16** kv[] = {&t.si, &t.siT, &t.gd, &t.gdT};
-  for (auto* q : kv) *q = reinterpret_cast<__bf16*>(take(J * z.kv * 2));
-  t.lb = reinterpret_cast<__bf16*>(take(J * z.lt * 2));
-  t.lbT = reinterpret_cast<__bf16*>(take(J * z.lt * 2));
-  t.dinv = reinterpret_cast<float*>(take(J * z.dg * 4));
-  t.dinvT = reinterpret_cast<float*>(take(J * z.dg * 4));
-  t.ry = reinterpret_cast<float*>(take(J * z.rhs * 4));
-  t.rx = reinterpret_cast<float*>(take(J * z.rhs * 4));
-  t.y = reinterpret_cast<__bf16*>(take(J * z.ydv * 2));
-  t.x = reinterpret_cast<__bf16*>(take(J * z.ydv * 2));
-  t.xT = reinterpret_cast<__bf16*>(take(J * z.ydv * 2));
+  t.gc = reinterpret_cast<float*>(take(J * cdk * 4));
+  t.gam = reinterpret_cast<float*>(take(J * p.dk * 4));
+  t.qt = reinterpret_cast<__bf16*>(take(J * cdk * 2));
+  t.kt = reinterpret_cast<__bf16*>(take(J * cdk * 2));
+  t.at = reinterpret_cast<__bf16*>(take(J * adk * 2));
+  t.bt = reinterpret_cast<__bf16*>(take(J * adk * 2));
+  t.lb = reinterpret_cast<__bf16*>(take(J * lt * 2));
+  t.lbT = reinterpret_cast<__bf16*>(take(J * lt * 2));
+  t.dinv = reinterpret_cast<float*>(take(J * NB * 256 * 4));
+  t.dinvT = reinterpret_cast<float*>(take(J * NB * 256 * 4));
+  t.ry = reinterpret_cast<float*>(take(J * ndv * 4));
+  t.rx = reinterpret_cast<float*>(take(J * ndv * 4));
+  t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
+  t.x = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   if (b) *b = t;
   return off;
 }
 
 // ---------------------------------------------------------------------------
-// prep: scaled operands (thread c owns channel c and walks the chunk's tokens,
-// packing eight rows at a time for the transposed copies), V and dO copies,
-// S_in and Gamma dS_end in bf16.
+// prep: G and the scaled operands.  Thread (token group tg, 8-channel piece
+// pc) owns TPG consecutive tokens of 8 channels: a prefix over its tokens,
+// then over the token groups through LDS, then 16-byte loads and stores.
 struct BcPrepArgs {
   Problem p;
-  const __bf16 *q, *k, *v, *A, *B, *dout;
+  const __bf16 *q, *k, *A, *B;
   const float* ld;
-  const float* ckpt;   // [BH, N, dk, dv] state entering each chunk
-  const float* gend;   // [BH, N, dk, dv] cotangent of the state leaving each chunk
   BcBufs w;
 };
 
-template <int DK, int DV, int RAB>
+template <int DK, int RAB>
 __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
-  constexpr int NA = kCC * RAB;
-  __shared__ float gam[DK];   // Gamma = e^{G} at the chunk's last token
+  constexpr int NP = DK / 8, NG = 256 / NP, TPG = kCC / NG;
+  __shared__ float tot[NG][DK];
   const Problem& p = a.p;
   const int64_t job = blockIdx.x, bh = job / p.N, j = job % p.N, t0 = j * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
   const int64_t tok0 = bh * p.T + t0;
-  const int tid = threadIdx.x;
-  const BcBufs& w = a.w;
-  if (tid < DK) {
-    const int c = tid;
-    float g = 0.f;
-    float* gc = w.gc + job * kCC * DK;
-    __bf16 *qt = w.qt + job * kCC * DK, *qtT = w.qtT + job * kCC * DK;
-    __bf16 *kt = w.kt + job * kCC * DK, *ktT = w.ktT + job * kCC * DK;
-    __bf16 *at = w.at + job * NA * DK, *atT = w.atT + job * NA * DK;
-    __bf16 *bt = w.bt + job * NA * DK, *btT = w.btT + job * NA * DK;
-    cb8 pq, pk, pa, pb;
-    for (int t = 0; t < kCC; ++t) {
-      const bool ok = t < n;
-      const int64_t tok = tok0 + (ok ? t : 0);
-      const float l = ok ? (p.scalar ? a.ld[tok] : a.ld[tok * DK + c]) : 0.f;
-      const float gp = g;
-      g += l;
-      gc[t * DK + c] = g;
-      const float eg = expf(g), ng = expf(-g), egp = expf(gp);
-      const __bf16 vq = (__bf16)(ok ? (float)a.q[tok * DK + c] * eg : 0.f);
-      const __bf16 vk = (__bf16)(ok ? (float)a.k[tok * DK + c] * ng : 0.f);
-      qt[t * DK + c] = vq;
-      kt[t * DK + c] = vk;
-      pq[t & 7] = vq;
-      pk[t & 7] = vk;
-      if ((t & 7) == 7) {
-        *reinterpret_cast<cb8*>(qtT + c * kCC + t - 7) = pq;
-        *reinterpret_cast<cb8*>(ktT + c * kCC + t - 7) = pk;
-      }
+  const int tid = threadIdx.x, pc = tid % NP, tg = tid / NP, c0 = 8 * pc;
+  float G[TPG][8], run[8];
 #pragma unroll
-      for (int r = 0; r < RAB; ++r) {
-        const int rr = t * RAB + r;
-        const __bf16 va = (__bf16)(ok ? (float)a.A[(tok * RAB + r) * DK + c] * ng : 0.f);
-        const __bf16 vb = (__bf16)(ok ? (float)a.B[(tok * RAB + r) * DK + c] * egp : 0.f);
-        at[rr * DK + c] = va;
-        bt[rr * DK + c] = vb;
-        pa[rr & 7] = va;
-        pb[rr & 7] = vb;
-        if ((rr & 7) == 7) {
-          *reinterpret_cast<cb8*>(atT + c * NA + rr - 7) = pa;
-          *reinterpret_cast<cb8*>(btT + c * NA + rr - 7) = pb;
-        }
+  for (int c = 0; c < 8; ++c) run[c] = 0.f;
+#pragma unroll
+  for (int u = 0; u < TPG; ++u) {
+    const int t = tg * TPG + u;
+    const int64_t tok = tok0 + (t < n ? t : 0);
+    float l[8];
+    if (t >= n) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) l[c] = 0.f;
+    } else if (p.scalar) {
+      const float s = a.ld[tok];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) l[c] = s;
+    } else {
+      const cf4 x0 = *reinterpret_cast<const cf4*>(a.ld + tok * DK + c0);
+      const cf4 x1 = *reinterpret_cast<const cf4*>(a.ld + tok * DK + c0 + 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        l[c] = x0[c];
+        l[c + 4] = x1[c];
       }
     }
-    gam[c] = expf(g);   // padding tokens add nothing: g is G at the last token
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      run[c] += l[c];
+      G[u][c] = run[c];
+    }
   }
-  // V and dO: row-major copies (zero past the sequence) and transposes
-  {
-    __bf16 *vc = w.vc + job * kCC * DV, *oc = w.oc + job * kCC * DV;
-    for (int e = tid; e < kCC * DV / 8; e += 256) {
-      const int t = e / (DV / 8), c8 = (e % (DV / 8)) * 8;
-      cb8 xv, xo;
-      if (t < n) {
-        xv = *reinterpret_cast<const cb8*>(a.v + (tok0 + t) * DV + c8);
-        xo = *reinterpret_cast<const cb8*>(a.dout + (tok0 + t) * DV + c8);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) tot[tg][c0 + c] = run[c];
+  __syncthreads();
+  float off[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) off[c] = 0.f;
+  for (int g2 = 0; g2 < tg; ++g2)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) off[c] += tot[g2][c0 + c];
+  const BcBufs& w = a.w;
+#pragma unroll
+  for (int u = 0; u < TPG; ++u) {
+    const int t = tg * TPG + u;
+    const bool ok = t < n;
+    const int64_t tok = tok0 + (ok ? t : 0);
+    float g[8], eg[8], ng[8], egp[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      g[c] = G[u][c] + off[c];
+      const float gp = u == 0 ? off[c] : G[u - 1][c] + off[c];   // G_{t-1}, 0 before the first token
+      eg[c] = expf(g[c]);
+      ng[c] = expf(-g[c]);
+      egp[c] = expf(gp);
+    }
+    float* gcr = w.gc + (job * kCC + t) * DK + c0;
+    *reinterpret_cast<cf4*>(gcr) = cf4{g[0], g[1], g[2], g[3]};
+    *reinterpret_cast<cf4*>(gcr + 4) = cf4{g[4], g[5], g[6], g[7]};
+    if (t == kCC - 1) {
+      // padding tokens add nothing: this is G at the chunk's last token
+#pragma unroll
+      for (int c = 0; c < 8; ++c) w.gam[job * DK + c0 + c] = eg[c];
+    }
+    auto scaled = [&](const __bf16* src, const float (&f)[8], __bf16* dst) {
+      cb8 o;
+      if (ok) {
+        const cb8 x = *reinterpret_cast<const cb8*>(src);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = (__bf16)((float)x[c] * f[c]);
       } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) xv[u] = xo[u] = (__bf16)0.f;
+        for (int c = 0; c < 8; ++c) o[c] = (__bf16)0.f;
       }
-      *reinterpret_cast<cb8*>(vc + t * DV + c8) = xv;
-      *reinterpret_cast<cb8*>(oc + t * DV + c8) = xo;
-    }
-    if (tid < DV) {
-      const int c = tid;
-      __bf16 *vcT = w.vcT + job * kCC * DV, *ocT = w.ocT + job * kCC * DV;
-      for (int t8 = 0; t8 < kCC; t8 += 8) {
-        cb8 xv, xo;
+      *reinterpret_cast<cb8*>(dst) = o;
+    };
+    scaled(a.q + tok * DK + c0, eg, w.qt + (job * kCC + t) * DK + c0);
+    scaled(a.k + tok * DK + c0, ng, w.kt + (job * kCC + t) * DK + c0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const bool ok = t8 + u < n;
-          xv[u] = ok ? a.v[(tok0 + t8 + u) * DV + c] : (__bf16)0.f;
-          xo[u] = ok ? a.dout[(tok0 + t8 + u) * DV + c] : (__bf16)0.f;
-        }
-        *reinterpret_cast<cb8*>(vcT + c * kCC + t8) = xv;
-        *reinterpret_cast<cb8*>(ocT + c * kCC + t8) = xo;
-      }
-    }
-  }
-  __syncthreads();   // gam
-  // S_in and Gamma dS_end, row-major and transposed
-  {
-    const float* S = a.ckpt + job * DK * DV;
-    const float* D = a.gend + job * DK * DV;
-    __bf16 *si = w.si + job * DK * DV, *gd = w.gd + job * DK * DV;
-    for (int e = tid; e < DK * DV / 4; e += 256) {
-      const int i = (e * 4) / DV;
-      const cf4 s4 = *reinterpret_cast<const cf4*>(S + e * 4);
-      const cf4 d4 = *reinterpret_cast<const cf4*>(D + e * 4);
-      const float gi = gam[i];
-      *reinterpret_cast<cb4*>(si + e * 4) = to_b4(s4);
-      *reinterpret_cast<cb4*>(gd + e * 4) = to_b4(cf4{gi * d4[0], gi * d4[1], gi * d4[2], gi * d4[3]});
-    }
-    if (tid < DV) {
-      const int c = tid;
-      __bf16 *siT = w.siT + job * DK * DV, *gdT = w.gdT + job * DK * DV;
-      for (int i8 = 0; i8 < DK; i8 += 8) {
-        cb8 xs, xd;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          xs[u] = (__bf16)S[(i8 + u) * DV + c];
-          xd[u] = (__bf16)(gam[i8 + u] * D[(i8 + u) * DV + c]);
-        }
-        *reinterpret_cast<cb8*>(siT + c * DK + i8) = xs;
-        *reinterpret_cast<cb8*>(gdT + c * DK + i8) = xd;
-      }
+    for (int r = 0; r < RAB; ++r) {
+      scaled(a.A + (tok * RAB + r) * DK + c0, ng, w.at + ((job * kCC + t) * RAB + r) * DK + c0);
+      scaled(a.B + (tok * RAB + r) * DK + c0, egp, w.bt + ((job * kCC + t) * RAB + r) * DK + c0);
     }
   }
 }
@@ -330,9 +305,11 @@ __global__ __launch_bounds__(256) void bwc_tri_kernel(BcTriArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i over one chunk,
-// one wave per 16 rows of A.  Kinds: the right-hand sides of Y and X, and the
-// five gradients (see the header).
+// Grouped products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i over one chunk.
+// A group is one or two kinds whose products read the same B-side operands
+// (W0, B1, C1, B2, C2): one workgroup per chunk stages them in LDS once, then
+// each wave forms 16 rows of one kind's output, its A rows read from memory.
+// The pairs: (dK, dA) and (dQ, dB).
 enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 };
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
 
@@ -348,20 +325,42 @@ struct BcKindCfg {
   static constexpr bool TERM2 = KIND >= kDq && RAB > 0;
   static constexpr int MSK2 = KIND == kDq ? kLE : (KIND == kDb ? kLT : kGT);
   static constexpr float SIGN = (KIND == kDa || KIND == kDb) ? -1.f : 1.f;
+  // W0 as it lives in memory: its transpose (S_in or Gamma dS_end for dQ, dK,
+  // dA, dB), read by rows; or W0 itself (dV and the right-hand sides), read
+  // with the transposing LDS read
+  static constexpr bool W0T = KIND == kDq || KIND == kDk || KIND == kDa || KIND == kDb;
 };
 
-// A group: one or two kinds whose products read the same B-side operands
-// (W0t, B1, C1T, B2, C2T), one workgroup per chunk.  The workgroup stages
-// those operands in LDS once (rows padded by 16 bf16, which keeps the 16-byte
-// fragment reads over 16 rows free of bank conflicts); each wave then forms
-// 16 rows of one kind's output, reading its A rows from memory and every
-// other fragment from LDS.  The pairs: (dK, dA) and (dQ, dB).
+// LDS layout of a kind's staged operands (bf16 elements).  Rows read by
+// 8-byte pieces (W0^T, B1, B2) are padded by 8 elements, rows read with the
+// transposing read (W0, C1, C2) by 16: both keep those reads free of LDS bank
+// conflicts.
+template <int KIND, int DK, int DV, int RAB>
+struct BcStage {
+  using K = BcKindCfg<KIND, DK, DV, RAB>;
+  static constexpr int NA = K::NA, KA = K::KA, NOUT = K::NOUT;
+  static constexpr int W0R = K::W0T ? NOUT : KA, W0C = K::W0T ? KA : NOUT;
+  static constexpr int LW0 = W0C + (K::W0T ? 8 : 16), LB = KA + 8, LC = NOUT + 16;
+  static constexpr int OW = 0, OB1 = OW + W0R * LW0, OC1 = OB1 + kCC * LB;
+  static constexpr int OB2 = OC1 + kCC * LC, OC2 = OB2 + (K::TERM2 ? NA * LB : 0);
+  static constexpr int TOTAL = OC2 + (K::TERM2 ? NA * LC : 0);
+};
+
+// Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
+// solve; the sequence's own rows t0 .. t0 + C - 1 (bf16 [T][cols], zero past
+// the sequence); a per-chunk fp32 boundary array; the same scaled by Gamma per row.
+enum BcSrcKind { kSrcChunk = 0, kSrcSeq = 1, kSrcF32 = 2, kSrcF32G = 3 };
+struct BcSrc {
+  const void* ptr;
+  int kind;
+};
+
 struct BcGroupArgs {
   Problem p;
-  const __bf16 *Aa, *Ab;                          // A rows of the two kinds (Ab: null for one kind)
-  const __bf16 *W0t, *B1, *C1T, *B2, *C2T;        // per-chunk arrays (row-major)
+  BcSrc Aa, Ab;                 // A rows of the two kinds (Ab unused for one kind)
+  BcSrc W0, B1, C1, B2, C2;     // the shared B-side operands
   BcBufs w;
-  float *outa, *outb;                             // right-hand sides (tile order) or gradients
+  float *outa, *outb;           // right-hand sides (tile order) or gradients
 };
 
 template <int MASK>
@@ -374,21 +373,10 @@ __device__ __forceinline__ bool bc_empty(int ta0, int ta1, int tb0, int tb1) {
   return MASK == kLE ? tb0 > ta1 : (MASK == kLT ? tb0 >= ta1 : (MASK == kGE ? tb1 < ta0 : tb1 <= ta0));
 }
 
-// LDS layout of a group's staged operands (bf16 elements).
+// 16 rows (block rb) of kind KIND's output for chunk job, B side in LDS.
 template <int KIND, int DK, int DV, int RAB>
-struct BcStage {
-  using K = BcKindCfg<KIND, DK, DV, RAB>;
-  static constexpr int NA = K::NA, KA = K::KA, NOUT = K::NOUT;
-  static constexpr int LW = KA + 16, L1 = kCC + 16, L2 = NA + 16;
-  static constexpr int OW = 0, OB1 = OW + NOUT * LW, OC1 = OB1 + kCC * LW;
-  static constexpr int OB2 = OC1 + NOUT * L1, OC2 = OB2 + (K::TERM2 ? NA * LW : 0);
-  static constexpr int TOTAL = OC2 + (K::TERM2 ? NOUT * L2 : 0);
-};
-
-// 16 rows (block rb) of kind KIND's output for chunk job, operands in LDS.
-template <int KIND, int DK, int DV, int RAB>
-__device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, const __bf16* Ag,
-                                        const __bf16* lds, const BcBufs& w, float* out, int lane) {
+__device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, const BcSrc& As, const __bf16* lds,
+                                        const BcBufs& w, float* out, int lane) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
   using L = BcStage<KIND, DK, DV, RAB>;
   constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
@@ -396,25 +384,37 @@ __device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, c
   const int r0 = 16 * rb;
   const int64_t bh = job / p.N, jc = job % p.N, t0 = jc * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  const int64_t tok0 = bh * p.T + t0;
   // rows of padding tokens only: no gradient to write (the right-hand sides
   // are formed for them too, as zeros, since the solves read every row)
   if (!(KIND == kRhsY || KIND == kRhsX) && r0 / K::RA >= n) return;
-  const __bf16* A = Ag + job * K::M * K::KA;
+  const __bf16* arow;
+  if (As.kind == kSrcSeq) {
+    const int r = r0 + lr < n ? r0 + lr : n - 1;   // a padding row's output is not written
+    arow = static_cast<const __bf16*>(As.ptr) + (tok0 + r) * K::KA;
+  } else {
+    arow = static_cast<const __bf16*>(As.ptr) + (job * K::M + r0 + lr) * K::KA;
+  }
   cb8 af[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) af[ks] = *reinterpret_cast<const cb8*>(A + (r0 + lr) * K::KA + 32 * ks + 8 * lg);
+  for (int ks = 0; ks < KS; ++ks) af[ks] = rowfrag(arow, ks, lane);
   cf4 acc[OT];
 #pragma unroll
   for (int ot = 0; ot < OT; ++ot) {
     acc[ot] = cz4();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc[ot] = mfma_b(af[ks], *reinterpret_cast<const cb8*>(lds + L::OW + (16 * ot + lr) * L::LW + 32 * ks + 8 * lg),
-                       acc[ot]);
+    for (int ks = 0; ks < KS; ++ks) {
+      cb8 bw;
+      if constexpr (K::W0T)
+        bw = rowfrag(lds + L::OW + (16 * ot + lr) * L::LW0, ks, lane);
+      else
+        bw = cat8(ltr4(lds + L::OW, L::LW0, 32 * ks, 16 * ot, lane), ltr4(lds + L::OW, L::LW0, 32 * ks + 16, 16 * ot, lane));
+      acc[ot] = mfma_b(af[ks], bw, acc[ot]);
+    }
   }
   const int ta0 = r0 / K::RA, ta1 = (r0 + 15) / K::RA, trow = (r0 + lr) / K::RA;
   // one score term: NB columns (RB rows of B per token), mask, sign
-  auto term = [&](int oB, int oC, int LC, auto nb_, auto rb_, auto mask_, float sg) {
+  auto term = [&](int oB, int oC, auto nb_, auto rb_, auto mask_, float sg) {
     constexpr int NBc = decltype(nb_)::value, RB = decltype(rb_)::value, MASK = decltype(mask_)::value;
 #pragma unroll 1
     for (int c0 = 0; c0 < NBc; c0 += 32) {
@@ -425,8 +425,7 @@ __device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, c
         s2[h] = cz4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          s2[h] = mfma_b(*reinterpret_cast<const cb8*>(lds + oB + (c0 + 16 * h + lr) * L::LW + 32 * ks + 8 * lg), af[ks],
-                         s2[h]);
+          s2[h] = mfma_b(rowfrag(lds + oB + (c0 + 16 * h + lr) * L::LB, ks, lane), af[ks], s2[h]);
         // lane: score(row r0 + lr, column c0 + 16 h + 4 lg + e)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -434,16 +433,15 @@ __device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, c
       }
       const cb8 sf = cat8(to_b4(s2[0]), to_b4(s2[1]));
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot) {
-        const __bf16* cr = lds + oC + (16 * ot + lr) * LC + c0 + 4 * lg;
-        acc[ot] = mfma_b(sf, cat8(*reinterpret_cast<const cb4*>(cr), *reinterpret_cast<const cb4*>(cr + 16)), acc[ot]);
-      }
+      for (int ot = 0; ot < OT; ++ot)
+        acc[ot] = mfma_b(sf, cat8(ltr4(lds + oC, L::LC, c0, 16 * ot, lane), ltr4(lds + oC, L::LC, c0 + 16, 16 * ot, lane)),
+                         acc[ot]);
     }
   };
   using I1 = std::integral_constant<int, 1>;
-  term(L::OB1, L::OC1, L::L1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
+  term(L::OB1, L::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
   if constexpr (K::TERM2)
-    term(L::OB2, L::OC2, L::L2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
+    term(L::OB2, L::OC2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
          std::integral_constant<int, K::MSK2>{}, -1.f);
 
   // ---- epilogue: lane holds rows r0 + 4 lg + e, column 16 ot + lr
@@ -453,7 +451,6 @@ __device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, c
       *reinterpret_cast<cf4*>(out + (((job * (NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
   } else {
     const float* gc = w.gc + job * kCC * DK;
-    const int64_t tok0 = bh * p.T + t0;
 #pragma unroll
     for (int ot = 0; ot < OT; ++ot) {
       const int col = 16 * ot + lr;
@@ -488,30 +485,52 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   constexpr int WA = K::M / 16;
   extern __shared__ __align__(16) unsigned char smem_[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem_);
-  const int64_t job = blockIdx.x;
+  const Problem& p = a.p;
+  const int64_t job = blockIdx.x, bh = job / p.N, jc = job % p.N;
+  const int n = static_cast<int>(p.T - jc * kCC < kCC ? p.T - jc * kCC : kCC);
+  const int64_t tok0 = bh * p.T + jc * kCC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // stage a per-chunk row-major array (rows x cols) into LDS rows of ld elements
-  auto stage = [&](const __bf16* g, int rows, int cols, int off, int ld) {
-    const __bf16* src = g + job * rows * cols;
+  // stage a chunk's rows x cols operand into LDS rows of ld elements
+  auto stage = [&](const BcSrc& sr, int rows, int cols, int off, int ld) {
     const int pieces = rows * cols / 8, pr = cols / 8;
     for (int i = tid; i < pieces; i += 64 * NW) {
       const int r = i / pr, c8 = (i - r * pr) * 8;
-      *reinterpret_cast<cb8*>(lds + off + r * ld + c8) = *reinterpret_cast<const cb8*>(src + r * cols + c8);
+      cb8 v;
+      if (sr.kind == kSrcChunk) {
+        v = *reinterpret_cast<const cb8*>(static_cast<const __bf16*>(sr.ptr) + (job * rows + r) * cols + c8);
+      } else if (sr.kind == kSrcSeq) {
+        if (r < n) {
+          v = *reinterpret_cast<const cb8*>(static_cast<const __bf16*>(sr.ptr) + (tok0 + r) * cols + c8);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = (__bf16)0.f;
+        }
+      } else {
+        const float* f = static_cast<const float*>(sr.ptr) + (job * rows + r) * cols + c8;
+        const cf4 x0 = *reinterpret_cast<const cf4*>(f), x1 = *reinterpret_cast<const cf4*>(f + 4);
+        const float gsc = sr.kind == kSrcF32G ? a.w.gam[job * DK + r] : 1.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[u] = (__bf16)(gsc * x0[u]);
+          v[u + 4] = (__bf16)(gsc * x1[u]);
+        }
+      }
+      *reinterpret_cast<cb8*>(lds + off + r * ld + c8) = v;
     }
   };
-  stage(a.W0t, K::NOUT, K::KA, L::OW, L::LW);
-  stage(a.B1, kCC, K::KA, L::OB1, L::LW);
-  stage(a.C1T, K::NOUT, kCC, L::OC1, L::L1);
+  stage(a.W0, L::W0R, L::W0C, L::OW, L::LW0);
+  stage(a.B1, kCC, K::KA, L::OB1, L::LB);
+  stage(a.C1, kCC, K::NOUT, L::OC1, L::LC);
   if constexpr (K::TERM2) {
-    stage(a.B2, K::NA, K::KA, L::OB2, L::LW);
-    stage(a.C2T, K::NOUT, K::NA, L::OC2, L::L2);
+    stage(a.B2, K::NA, K::KA, L::OB2, L::LB);
+    stage(a.C2, K::NA, K::NOUT, L::OC2, L::LC);
   }
   __syncthreads();
   if (wave < WA) {
-    bc_rows<KA_, DK, DV, RAB>(a.p, job, wave, a.Aa, lds, a.w, a.outa, lane);
+    bc_rows<KA_, DK, DV, RAB>(p, job, wave, a.Aa, lds, a.w, a.outa, lane);
   } else if constexpr (KB_ >= 0) {
-    bc_rows<KB_, DK, DV, RAB>(a.p, job, wave - WA, a.Ab, lds, a.w, a.outb, lane);
+    bc_rows<KB_, DK, DV, RAB>(p, job, wave - WA, a.Ab, lds, a.w, a.outb, lane);
   }
 }
 
@@ -556,7 +575,6 @@ __global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
     __bf16* out = (isx ? w.x : w.y) + job * NA * DV;
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[(16 * i + 4 * lg + e) * DV + 16 * ct + lr] = (__bf16)o[e];
-    if (isx) *reinterpret_cast<cb4*>(w.xT + job * NA * DV + (16 * ct + lr) * NA + 16 * i + 4 * lg) = to_b4(o);
   };
   if (!isx) {
 #pragma unroll
@@ -585,7 +603,8 @@ __global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// decay: thread c owns channel c; reverse sum over the chunk's tokens.
+// decay: the per-(token, channel) terms in parallel, then one thread per
+// channel sums them in reverse.
 struct BcDecayArgs {
   Problem p;
   const __bf16 *q, *k, *A, *B;
@@ -596,43 +615,60 @@ struct BcDecayArgs {
 
 template <int DK, int DV, int RAB>
 __global__ __launch_bounds__(256) void bwc_decay_kernel(BcDecayArgs a) {
-  __shared__ float red[kCC][DK + 1];
+  constexpr int TPC = 256 / DK;   // threads per channel for the chunk-end term
+  __shared__ float gsm[kCC][DK + 1];
+  __shared__ float ends[DK];
   const Problem& p = a.p;
   const int64_t job = blockIdx.x, bh = job / p.N, j = job % p.N, t0 = j * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
   const int64_t tok0 = bh * p.T + t0;
   const int tid = threadIdx.x;
-  if (tid < DK) {
-    const int c = tid;
+  // per (token, channel) terms, channels across the threads
+  for (int idx = tid; idx < n * DK; idx += 256) {
+    const int t = idx / DK, c = idx - t * DK;
+    const int64_t tok = tok0 + t;
+    float g = (float)a.q[tok * DK + c] * a.dq[tok * DK + c] - (float)a.k[tok * DK + c] * a.dK[tok * DK + c];
+#pragma unroll
+    for (int r = 0; r < RAB; ++r) {
+      g -= (float)a.A[(tok * RAB + r) * DK + c] * a.dA[(tok * RAB + r) * DK + c];
+      if (t + 1 < n) g += (float)a.B[((tok + 1) * RAB + r) * DK + c] * a.dB[((tok + 1) * RAB + r) * DK + c];
+    }
+    gsm[t][c] = g;
+  }
+  // the chunk-end term rowdot(dS_end, S_end): TPC threads per channel
+  {
+    const int c = tid / TPC, part = tid % TPC;
     const float* Se = j + 1 < p.N ? a.ckpt + (job + 1) * DK * DV : a.sfin + bh * DK * DV;
     const float* dSe = a.gend + job * DK * DV;
-    float acc = 0.f;
+    float e = 0.f;
 #pragma unroll 4
-    for (int v4 = 0; v4 < DV; v4 += 4) {
-      const cf4 s = *reinterpret_cast<const cf4*>(Se + c * DV + v4);
-      const cf4 d = *reinterpret_cast<const cf4*>(dSe + c * DV + v4);
-      acc += s[0] * d[0] + s[1] * d[1] + s[2] * d[2] + s[3] * d[3];
+    for (int v4 = part * 4; v4 < DV; v4 += 4 * TPC) {
+      const cf4 sv = *reinterpret_cast<const cf4*>(Se + c * DV + v4);
+      const cf4 dv4 = *reinterpret_cast<const cf4*>(dSe + c * DV + v4);
+      e += sv[0] * dv4[0] + sv[1] * dv4[1] + sv[2] * dv4[2] + sv[3] * dv4[3];
     }
-    for (int t = n - 1; t >= 0; --t) {
-      const int64_t tok = tok0 + t;
-      float g = (float)a.q[tok * DK + c] * a.dq[tok * DK + c] - (float)a.k[tok * DK + c] * a.dK[tok * DK + c];
 #pragma unroll
-      for (int r = 0; r < RAB; ++r) {
-        g -= (float)a.A[(tok * RAB + r) * DK + c] * a.dA[(tok * RAB + r) * DK + c];
-        if (t + 1 < n) g += (float)a.B[((tok + 1) * RAB + r) * DK + c] * a.dB[((tok + 1) * RAB + r) * DK + c];
-      }
-      acc += g;
+    for (int sh = 1; sh < TPC; sh *= 2) e += __shfl_xor(e, sh, 64);
+    if (part == 0) ends[c] = e;
+  }
+  __syncthreads();
+  // reverse sum over the chunk's tokens, one thread per channel
+  if (tid < DK) {
+    const int c = tid;
+    float acc = ends[c];
+    for (int t = n - 1; t >= 0; --t) {
+      acc += gsm[t][c];
       if (p.scalar)
-        red[t][c] = acc;
+        gsm[t][c] = acc;
       else
-        a.dld[tok * DK + c] = acc;
+        a.dld[(tok0 + t) * DK + c] = acc;
     }
   }
   if (p.scalar) {
     __syncthreads();
     if (tid < n) {
       float s = 0.f;
-      for (int c = 0; c < DK; ++c) s += red[tid][c];
+      for (int c = 0; c < DK; ++c) s += gsm[tid][c];
       a.dld[tok0 + tid] = s;
     }
   }
@@ -647,13 +683,16 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const int64_t J = p.BH * p.N;
   const unsigned jobs = static_cast<unsigned>(J);
   auto bf = [](const void* x) { return static_cast<const __bf16*>(x); };
-  hipLaunchKernelGGL((bwc_prep_kernel<DK, DV, RAB>), dim3(jobs), dim3(256), 0, s,
-                     BcPrepArgs{p, bf(q), bf(k), bf(v), bf(A), bf(B), bf(dout), ld, ckpt, gend, w});
+  hipLaunchKernelGGL((bwc_prep_kernel<DK, RAB>), dim3(jobs), dim3(256), 0, s,
+                     BcPrepArgs{p, bf(q), bf(k), bf(A), bf(B), ld, w});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const BcSrc none{nullptr, kSrcChunk};
+  auto chunk = [](const void* x) { return BcSrc{x, kSrcChunk}; };
+  const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcF32}, GdS{gend, kSrcF32G};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
-  auto group = [&](auto ka_, auto kb_, const __bf16* Aa, const __bf16* Ab, const __bf16* W0t, const __bf16* B1,
-                   const __bf16* C1T, const __bf16* B2, const __bf16* C2T, float* outa, float* outb) {
+  auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
+                   float* outa, float* outb) {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
@@ -662,39 +701,39 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0t, B1, C1T, B2, C2T, w, outa, outb});
+                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb});
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
   if constexpr (RAB > 0) {
     hipLaunchKernelGGL((bwc_tri_kernel<DK, RAB>), dim3(jobs), dim3(256), 0, s, BcTriArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, w.bt, nullptr, w.siT, w.kt, w.vcT, nullptr, nullptr,
+    if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
                    w.ry, nullptr)) != hipSuccess)
       return e;
-    if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, w.at, nullptr, w.gdT, w.qt, w.ocT, nullptr, nullptr,
+    if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, chunk(w.at), none, GdS, chunk(w.qt), Os, none, none,
                    w.rx, nullptr)) != hipSuccess)
       return e;
     const int64_t sw = J * 2 * (DV / 16);
     hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(static_cast<unsigned>((sw + 3) / 4)), dim3(256), 0, s,
                        BcSolveArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, w.vc, w.y, w.gd, w.oc,
-                   w.qtT, w.x, w.btT, dK, dA)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
+                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA)) != hipSuccess)
       return e;
-    if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, w.oc, w.x, w.si, w.vc,
-                   w.ktT, w.y, w.atT, dq, dB)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, Os, chunk(w.x), Sin, Vs,
+                   chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB)) != hipSuccess)
       return e;
   } else {
-    if ((e = group(std::integral_constant<int, kDk>{}, KN{}, w.vc, nullptr, w.gd, w.oc, w.qtT, nullptr, nullptr, dK,
+    if ((e = group(std::integral_constant<int, kDk>{}, KN{}, Vs, none, GdS, Os, chunk(w.qt), none, none, dK,
                    nullptr)) != hipSuccess)
       return e;
-    if ((e = group(std::integral_constant<int, kDq>{}, KN{}, w.oc, nullptr, w.si, w.vc, w.ktT, nullptr, nullptr, dq,
+    if ((e = group(std::integral_constant<int, kDq>{}, KN{}, Os, none, Sin, Vs, chunk(w.kt), none, none, dq,
                    nullptr)) != hipSuccess)
       return e;
   }
-  if ((e = group(std::integral_constant<int, kDv>{}, KN{}, w.kt, nullptr, w.gdT, w.qt, w.ocT, w.bt, w.xT, dV,
-                 nullptr)) != hipSuccess)
+  if ((e = group(std::integral_constant<int, kDv>{}, KN{}, chunk(w.kt), none, GdS, chunk(w.qt), Os, chunk(w.bt),
+                 chunk(w.x), dV, nullptr)) != hipSuccess)
     return e;
   hipLaunchKernelGGL((bwc_decay_kernel<DK, DV, RAB>), dim3(jobs), dim3(256), 0, s,
                      BcDecayArgs{p, bf(q), bf(k), bf(A), bf(B), dq, dK, dA, dB, ckpt, gend, sfin, dld});

@@ -766,9 +766,10 @@ struct FastScanArgs {
   Problem p;
   const __bf16* M;
   const __bf16* v;
-  __bf16* out;
+  __bf16* out;         // null: the output rows are not stored
   float* Sfin;
   const float* S0;
+  float* ckpt;         // null, or [BH, N, dk, dv]: the state entering every chunk (fp32)
 };
 
 template <int DK, int BV, int NWV, int PD>
@@ -850,6 +851,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   };
   // Output rows of chunk jj from a staging buffer to HBM (none past the end).
   auto flush_out = [&](const __bf16* O, int64_t jj) {
+    if (a.out == nullptr) return;
     const int n = chunk_len(jj);
     __bf16* oj = obh + static_cast<size_t>(jj) * kC * dv;
 #pragma unroll
@@ -868,6 +870,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     const int i = it / BV, c = it % BV;
     const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
     X0[c * LDX + kperm(i)] = (__bf16)s;
+    if (a.ckpt) a.ckpt[(static_cast<size_t>(bh * N) * DK + i) * dv + c0 + c] = s;
   }
   put_v(X0, vb[0], 0);
   // Ring invariant from here on: at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
@@ -917,6 +920,22 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
           const int t = (mt - DK / 16) * 16 + 4 * lg;
 #pragma unroll
           for (int e = 0; e < 4; ++e) Oc[(t + e) * LDO + c] = (__bf16)acc[q][nt][e];
+        }
+      }
+    }
+    if (a.ckpt && jj + 1 < N) {
+      // the state entering chunk jj + 1: this product's state rows, in fp32
+      float* ck = a.ckpt + static_cast<size_t>(bh * N + jj + 1) * DK * dv;
+#pragma unroll
+      for (int q = 0; q < MPW; ++q) {
+        const int mt = wave * MPW + q;
+        if (mt < DK / 16) {
+#pragma unroll
+          for (int nt = 0; nt < NTN; ++nt) {
+            const int i0 = mt * 16 + 4 * lg, c = nt * 16 + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ck[(i0 + e) * dv + c0 + c] = acc[q][nt][e];
+          }
         }
       }
     }
@@ -1114,10 +1133,10 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
 
 template <int DK, int BV, int NWV, int PD>
 hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out, float* Sfin,
-                       const float* S0, hipStream_t s) {
+                       const float* S0, float* ckpt, hipStream_t s) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
   FastScanArgs a{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(v),
-                 static_cast<__bf16*>(out), Sfin, S0};
+                 static_cast<__bf16*>(out), Sfin, S0, ckpt};
   const int nvt = p.dv / BV;
   const int64_t groups = (p.BH + 7) / 8;
   const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD>);
@@ -1167,13 +1186,14 @@ hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const
 }
 
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
-                     const float* S0, hipStream_t s) {
+                     const float* S0, hipStream_t s, float* ckpt) {
   if (p.BH == 0) return hipSuccess;
   // Wider d_v slices share each operator load among more columns; narrower
   // ones are used when that leaves too few workgroups to fill the chip.
-  if (p.dk == 128 && p.BH * (p.dv / 64) >= 256) return launch_scan<128, 64, 12, 2>(p, workspace, v, out, Sfin, S0, s);
-  if (p.dk == 128) return launch_scan<128, 32, 4, 2>(p, workspace, v, out, Sfin, S0, s);
-  if (p.dk == 64) return launch_scan<64, 16, 4, 4>(p, workspace, v, out, Sfin, S0, s);
+  if (p.dk == 128 && p.BH * (p.dv / 64) >= 256)
+    return launch_scan<128, 64, 12, 2>(p, workspace, v, out, Sfin, S0, ckpt, s);
+  if (p.dk == 128) return launch_scan<128, 32, 4, 2>(p, workspace, v, out, Sfin, S0, ckpt, s);
+  if (p.dk == 64) return launch_scan<64, 16, 4, 4>(p, workspace, v, out, Sfin, S0, ckpt, s);
   return hipErrorInvalidValue;
 }
 

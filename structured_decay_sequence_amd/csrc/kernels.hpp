@@ -44,12 +44,14 @@ hipError_t general_summaries(const Problem& p, const void* workspace, const void
 
 // bf16 MFMA path: bf16 storage, C = 64, r_kv = 1, r_ab in {0, 1, 2}, d_k in {64, 128},
 // d_v a multiple of 64.  The workspace holds the fragment-ordered chunk operators.
+// fast_scan: out may be null (no output rows); ckpt, if given, receives the
+// state entering every chunk [BH, N, dk, dv] in fp32.
 bool fast_supported(const Problem& p);
 size_t fast_workspace_bytes(const Problem& p);
 hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const float* ld,
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
-                     const float* S0, hipStream_t s);
+                     const float* S0, hipStream_t s, float* ckpt = nullptr);
 // Gating-chunk summaries for the query-conditioned composition, from the bf16
 // prepare's operators of the 64-token problem p: per gating chunk of G
 // consecutive chunks (G <= 4), Acal^T [dk][dk] and B^T [dv][dk] in bf16, the
