@@ -602,7 +602,7 @@ BwLayout bw_layout(const Problem& p) {
   BwLayout l{};
   const size_t states = static_cast<size_t>(p.BH * p.N) * p.dk * p.dv * sizeof(float);
   l.ops = 0;
-  l.ckpt = bw_align(f32_operators_bytes(p));
+  l.ckpt = bw_align(backward_chunked(p) ? fast_workspace_bytes(p) : f32_operators_bytes(p));
   l.gend = l.ckpt + bw_align(states);
   l.bufs = l.gend + bw_align(states);
   if (backward_chunked(p)) {
@@ -672,21 +672,23 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   char* ws = static_cast<char*>(workspace);
   float* ckpt = reinterpret_cast<float*>(ws + l.ckpt);
   float* gend = reinterpret_cast<float*>(ws + l.gend);
-  const float* M = nullptr;
-  hipError_t e = f32_operators(p, q, k, ld, A, B, ws + l.ops, &M, s);
-  if (e != hipSuccess) return e;
   if (backward_chunked(p)) {
-    // The states entering the chunks come from the bf16 MFMA scan over the
-    // bf16 operators (which f32_operators left at the front of its region);
-    // the cotangents from the fp32 reverse scan.
+    // Both boundary scans on bf16 MFMAs over the bf16 MFMA prepare's
+    // operators: the states entering the chunks (the forward scan), then the
+    // cotangents leaving them.
     float* sfin = reinterpret_cast<float*>(ws + l.sfin);
+    hipError_t e = fast_prepare(p, q, k, ld, A, B, ws + l.ops, s);
+    if (e != hipSuccess) return e;
     e = fast_scan(p, ws + l.ops, v, nullptr, sfin, S0, s, ckpt);
     if (e != hipSuccess) return e;
-    e = launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, sfin, dS0, s, false);
+    e = launch_backward_rscan(p, ws + l.ops, dout, dfinal, gend, dS0, s);
     if (e != hipSuccess) return e;
     return launch_backward_chunked(p, q, k, v, ld, A, B, dout, ckpt, gend, sfin, dq, dK, dV, dld, dA, dB,
                                    ws + l.chunk, s);
   }
+  const float* M = nullptr;
+  hipError_t e = f32_operators(p, q, k, ld, A, B, ws + l.ops, &M, s);
+  if (e != hipSuccess) return e;
   e = p.bf16 ? launch_boundary_scans<bf16_raw>(p, M, v, dout, S0, dfinal, ckpt, gend, nullptr, nullptr, s)
              : launch_boundary_scans<float>(p, M, v, dout, S0, dfinal, ckpt, gend, nullptr, nullptr, s);
   if (e != hipSuccess) return e;

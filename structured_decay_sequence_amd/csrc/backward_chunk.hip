@@ -675,6 +675,202 @@ __global__ __launch_bounds__(256) void bwc_decay_kernel(BcDecayArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Reverse boundary scan on bf16 MFMAs: the cotangents of the chunk boundary
+// states, dS_{j-1} = Acal_j^T dS_j + Qbar_j^T dO_j, from j = N - 1 down, over
+// the bf16 MFMA prepare's fragment-ordered operators.  The product needs the
+// transpose of the operator's left column block [Acal ; Qbar]: per chunk its
+// 16x16 tiles are staged in LDS row-major (from the fragments, which hold
+// them row by row) and read with the transposing LDS read.  One workgroup of
+// four waves per (batch*head, BV value columns); the cotangent stays in LDS
+// as the bf16 B operand, its columns' K index permuted as the forward scan's
+// (position 32 b + 8 g + 4 h + e holds row 32 b + 16 h + 4 g + e); the next
+// chunk's tiles and dO rows are loaded during the product and staged in the
+// other half of a double buffer.
+template <int DK, int BV>
+struct RsCfg {
+  static constexpr int MT = (DK + kCC) / 16;   // operator row (and column) tiles
+  static constexpr int KPALL = MT / 2;          // fragment pairs per row tile in memory
+  static constexpr int DKT = DK / 16, DP = DK / 32;
+  static constexpr int NF = MT * DP;            // fragments staged per chunk
+  static constexpr int FPW = NF / 4;
+  static constexpr int RPW = DKT / 4;           // output row tiles per wave
+  static constexpr int CTN = BV / 16;
+  static constexpr int LDX = DK + kCC + 16;     // padded row of X^T
+  static constexpr int TBUF = MT * DKT * 256;   // staged tiles (bf16 elements)
+  static constexpr int XBUF = BV * LDX;
+  static constexpr int MSZ = MT * MT * 256;     // operator elements per chunk
+  static constexpr int DITEMS = (kCC / 2) * (BV / 8);   // dO pieces: 2 tokens x 8 columns
+  static constexpr int LDS = 2 * (TBUF + XBUF) * 2;
+  static_assert(NF % 4 == 0 && DKT % 4 == 0 && DITEMS <= 256, "reverse scan tiling");
+};
+
+struct RsArgs {
+  Problem p;
+  const __bf16* M;
+  const __bf16* dout;
+  const float* dfinal;
+  float* gend;   // [BH, N, dk, dv]: the cotangent of the state leaving each chunk
+  float* dS0;    // [BH, dk, dv]
+};
+
+__device__ __forceinline__ int rs_kperm(int m) { return (m & ~31) + 8 * ((m >> 2) & 3) + 4 * ((m >> 4) & 1) + (m & 3); }
+
+template <int DK, int BV>
+__global__ __launch_bounds__(256) void bw_rscan_kernel(RsArgs a) {
+  using Cf = RsCfg<DK, BV>;
+  constexpr int FPW = Cf::FPW, RPW = Cf::RPW, CTN = Cf::CTN, LDX = Cf::LDX, DKT = Cf::DKT, DP = Cf::DP;
+  extern __shared__ __align__(16) unsigned char smem_[];
+  __bf16* Tb = reinterpret_cast<__bf16*>(smem_);
+  __bf16* Xb = Tb + 2 * Cf::TBUF;
+  const Problem& p = a.p;
+  const int dv = p.dv, nvt = dv / BV;
+  const int b = blockIdx.x;
+  // the value slices of one (batch, head) share blockIdx % 8, hence an XCD and its L2
+  const int grp = b / (8 * nvt), rem = b % (8 * nvt);
+  const int64_t bh = static_cast<int64_t>(grp) * 8 + rem % 8;
+  const int64_t N = p.N;
+  if (bh >= p.BH || N == 0) return;
+  const int c0 = (rem / 8) * BV;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const __bf16* Mbh = a.M + static_cast<size_t>(bh) * N * Cf::MSZ;
+  float* gbh = a.gend + static_cast<size_t>(bh) * N * DK * dv;
+
+  cb8 fr[FPW];
+  cb8 dpc[2];
+  const int ditem = tid < Cf::DITEMS ? tid : Cf::DITEMS - 1;
+  const int dvs = ditem / (BV / 8), dvc = ditem % (BV / 8);   // tokens 2 dvs, 2 dvs + 1; columns 8 dvc ..
+  auto chunk_len = [&](int64_t jj) {
+    const int64_t r = p.T - jj * kCC;
+    return static_cast<int>(r < kCC ? r : kCC);
+  };
+  auto load_ops = [&](int64_t jj) {
+    const __bf16* Mj = Mbh + static_cast<size_t>(jj) * Cf::MSZ;
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave * FPW + u, mt = f / DP, pp = f % DP;
+      fr[u] = *reinterpret_cast<const cb8*>(Mj + ((mt * Cf::KPALL + pp) * 64 + lane) * 8);
+    }
+  };
+  // fragment (mt, pair pp): lane (g, i) holds row i, columns 4 g .. 4 g + 3 of
+  // tiles (mt, 2 pp) and (mt, 2 pp + 1)
+  auto put_ops = [&](__bf16* T) {
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave * FPW + u, mt = f / DP, pp = f % DP;
+      cb4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = fr[u][e];
+        hi[e] = fr[u][4 + e];
+      }
+      *reinterpret_cast<cb4*>(T + (mt * DKT + 2 * pp) * 256 + lr * 16 + 4 * lg) = lo;
+      *reinterpret_cast<cb4*>(T + (mt * DKT + 2 * pp + 1) * 256 + lr * 16 + 4 * lg) = hi;
+    }
+  };
+  auto load_do = [&](int64_t jj) {
+    const int n = chunk_len(jj);
+    const __bf16* src = a.dout + (static_cast<size_t>(bh) * p.T + jj * kCC) * dv + c0 + 8 * dvc;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int t = 2 * dvs + r;
+      if (t < n) {
+        dpc[r] = *reinterpret_cast<const cb8*>(src + static_cast<size_t>(t) * dv);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dpc[r][u] = (__bf16)0.f;
+      }
+    }
+  };
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 cb2;
+  auto put_do = [&](__bf16* X) {
+    if (tid < Cf::DITEMS) {
+      const int pos = rs_kperm(DK + 2 * dvs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cb2 w2;
+        w2[0] = dpc[0][e];
+        w2[1] = dpc[1][e];
+        *reinterpret_cast<cb2*>(X + (8 * dvc + e) * LDX + pos) = w2;
+      }
+    }
+  };
+
+  // the cotangent leaving the last chunk: dfinal (or zero)
+  for (int it = tid; it < DK * BV; it += 256) {
+    const int i = it / BV, c = it % BV;
+    const float g = a.dfinal ? a.dfinal[(bh * DK + i) * dv + c0 + c] : 0.f;
+    gbh[(static_cast<size_t>(N - 1) * DK + i) * dv + c0 + c] = g;
+    Xb[c * LDX + rs_kperm(i)] = (__bf16)g;
+  }
+  load_ops(N - 1);
+  put_ops(Tb);
+  load_do(N - 1);
+  put_do(Xb);
+  __syncthreads();
+  for (int64_t st = 0; st < N; ++st) {
+    const int64_t j = N - 1 - st;
+    const int cur = static_cast<int>(st & 1);
+    const __bf16* T = Tb + cur * Cf::TBUF;
+    const __bf16* X = Xb + cur * Cf::XBUF;
+    __bf16* Tn = Tb + (cur ^ 1) * Cf::TBUF;
+    __bf16* Xn = Xb + (cur ^ 1) * Cf::XBUF;
+    const int64_t jn = j > 0 ? j - 1 : 0;   // the first chunk reloads itself, unused
+    load_ops(jn);
+    load_do(jn);
+    cf4 acc[RPW][CTN];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+      for (int ct = 0; ct < CTN; ++ct) acc[rr][ct] = cz4();
+#pragma unroll
+    for (int pp = 0; pp < Cf::MT / 2; ++pp) {
+      cb8 bx[CTN];
+#pragma unroll
+      for (int ct = 0; ct < CTN; ++ct) bx[ct] = *reinterpret_cast<const cb8*>(X + (16 * ct + lr) * LDX + 32 * pp + 8 * lg);
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int kt = wave + 4 * rr;
+        const cb8 af = cat8(ltr4(T + (2 * pp * DKT + kt) * 256, 16, 0, 0, lane),
+                            ltr4(T + ((2 * pp + 1) * DKT + kt) * 256, 16, 0, 0, lane));
+#pragma unroll
+        for (int ct = 0; ct < CTN; ++ct) acc[rr][ct] = mfma_b(af, bx[ct], acc[rr][ct]);
+      }
+    }
+    // lane holds rows 16 kt + 4 lg + e (state channels), column 16 ct + lr
+    float* dst = j > 0 ? gbh + static_cast<size_t>(j - 1) * DK * dv : a.dS0 + static_cast<size_t>(bh) * DK * dv;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int kt = wave + 4 * rr;
+#pragma unroll
+      for (int ct = 0; ct < CTN; ++ct) {
+        const int c = 16 * ct + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(16 * kt + 4 * lg + e) * dv + c0 + c] = acc[rr][ct][e];
+        *reinterpret_cast<cb4*>(Xn + c * LDX + rs_kperm(16 * kt + 4 * lg)) = to_b4(acc[rr][ct]);
+      }
+    }
+    put_ops(Tn);
+    put_do(Xn);
+    __syncthreads();
+  }
+}
+
+template <int DK, int BV>
+hipError_t launch_rscan_t(const Problem& p, const void* M, const void* dout, const float* dfinal, float* gend,
+                          float* dS0, hipStream_t s) {
+  using Cf = RsCfg<DK, BV>;
+  const void* fn = reinterpret_cast<const void*>(bw_rscan_kernel<DK, BV>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cf::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t groups = (p.BH + 7) / 8;
+  hipLaunchKernelGGL((bw_rscan_kernel<DK, BV>), dim3(static_cast<unsigned>(groups * 8 * (p.dv / BV))), dim3(256),
+                     Cf::LDS, s, RsArgs{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(dout), dfinal, gend, dS0});
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 template <int DK, int DV, int RAB>
 hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, const void* dout, const float* ckpt,
@@ -748,6 +944,19 @@ bool backward_chunked(const Problem& p) {
 }
 
 size_t backward_chunked_bytes(const Problem& p) { return bc_layout(p, nullptr, nullptr); }
+
+hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, float* gend,
+                                 float* dS0, hipStream_t s) {
+  if (p.BH * p.N == 0) return hipSuccess;
+  if (!backward_chunked(p)) return hipErrorInvalidValue;
+  // 64 value columns per workgroup where that still gives >= 256 workgroups
+  const bool wide = p.BH * (p.dv / 64) >= 256;
+  if (p.dk == 128) return wide ? launch_rscan_t<128, 64>(p, M, dout, dfinal, gend, dS0, s)
+                               : launch_rscan_t<128, 32>(p, M, dout, dfinal, gend, dS0, s);
+  if (p.dk == 64) return wide ? launch_rscan_t<64, 64>(p, M, dout, dfinal, gend, dS0, s)
+                              : launch_rscan_t<64, 32>(p, M, dout, dfinal, gend, dS0, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                                    const void* A, const void* B, const void* dout, const float* ckpt,

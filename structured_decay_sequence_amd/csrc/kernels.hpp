@@ -109,6 +109,11 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
 // boundary scan gives).  ws: backward_chunked_bytes(p) bytes.
 bool backward_chunked(const Problem& p);
 size_t backward_chunked_bytes(const Problem& p);
+// The cotangent boundary scan of that route on bf16 MFMAs, over the bf16 MFMA
+// prepare's operators M: gend[j] (the cotangent leaving chunk j) for every
+// chunk, and dS0.
+hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, float* gend,
+                                 float* dS0, hipStream_t s);
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                                    const void* A, const void* B, const void* dout, const float* ckpt,
                                    const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld,
