@@ -343,14 +343,33 @@ def loglinear_leg(torch, lattn, dev, steps, warmup):
     }
 
 
+def backward_flops(spec):
+    """Dense-size flops of the chunked backward on MFMAs (bf16 storage, C = 64,
+    r_kv = 1): the prepare's chunk operators, the two boundary scans, the
+    blocks of L, the two right-hand sides and solves, and the five gradient
+    products (each A W0 plus the masked score products, counted dense)."""
+    C, dk, dv = spec.chunk, spec.dk, spec.dv
+    na, nk = C * spec.r_ab, C
+    n_chunks = spec.B * spec.H * -(-spec.T // C)
+    prep = (na + C) * (na + nk) * dk + na ** 3 / 6 + na * na * (dk + nk) + (C + dk) * na * (dk + nk)
+    scans = (dk + C) * dv * (dk + nk) + dk * dv * (dk + C)
+    tri = 2 * na * na * dk
+    rhs = 2 * (na * dv * dk + na * C * dk + na * dv * C)
+    solve = 2 * (na * na / 2) * dv
+    g_tok = lambda kw, nw: C * nw * kw + C * C * kw + C * nw * C + C * na * kw + C * nw * na   # dQ, dK, dV
+    g_rank = lambda kw, nw: na * nw * kw + na * C * kw + na * nw * C + na * na * kw + na * nw * na   # dA, dB
+    grads = 2 * g_tok(dv, dk) + g_tok(dk, dv) + (2 * g_rank(dv, dk) if spec.r_ab else 0)
+    return 2.0 * n_chunks * (prep + scans + tri + rhs + solve + grads)
+
+
 def backward_leg(spec, raw, inputs, torch, lattn, dev):
     """lattn_chunk_bwd on the benchmark workload (same inputs as the forward,
     seeded output cotangents and a final-state cotangent), one timed call after
-    one warm-up, HIP events on its stream.  flops: the multiply-adds of the
-    two chunk-boundary scans (states forward, cotangents in reverse) and of the
-    chunk-parallel token walks (the forward recompute, then the reverse
-    recurrence's state products), priced against the fp32 vector peak they
-    run on; the chunk operators' prepare is not counted."""
+    one warm-up, HIP events on its stream.  At this shape it is the chunked
+    backward on bf16 MFMAs: the chunk operators, the boundary scans (states
+    forward, cotangents in reverse), then per chunk the forward and adjoint UT
+    solves and the gradient products; flops are their dense-size count
+    (backward_flops), priced against the bf16 MFMA peak."""
     q, K, V, ld, A, B = inputs
     td = q.dtype
     rng = np.random.default_rng(1)
@@ -366,20 +385,16 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1)
-    dk, dv, ra, rk = spec.dk, spec.dv, spec.r_ab, spec.r_kv
-    fwd_mac = dk * dv * (2 * ra + rk + 1)                    # B^T S, D S - A u + K V^T
-    bwd_mac = dk * dv * (1 + 1 + 1 + 3 * ra + 2 * rk + 1 + 2 * ra + 1)
-    n_chunks = -(-spec.T // spec.chunk)
-    bound_mac = n_chunks * dk * dv * ((dk + spec.chunk * rk) + (dk + spec.chunk))
-    flops = 2.0 * spec.B * spec.H * (spec.T * (fwd_mac + bwd_mac) + bound_mac)
+    flops = backward_flops(spec)
     return {
         "entry": "lattn_chunk_bwd",
-        "kind": "chunk-boundary scans over the chunk operators, then chunk-parallel token walks",
+        "kind": "chunked backward on bf16 MFMAs: boundary scans, forward and adjoint UT solves, gradient products",
         "ms_per_step": round(ms, 3),
         "value": round(spec.B * spec.T / (ms / 1e3), 1),
         "unit": "tokens/s",
         "gflop": round(flops / 1e9, 2),
-        "fp32_valu_frac": round(flops / (ms / 1e3) / (PEAK["fp32_valu_TFs"] * 1e12), 4),
+        "mfma_frac_bf16": round(flops / (ms / 1e3) / (PEAK["bf16_mfma_TFs"] * 1e12), 4),
+        "ratio_to_forward": None,
     }
 
 
@@ -704,6 +719,7 @@ def main():
     if spec.name == workloads.HEADLINE and not args.no_backward:
         print("[bench] backward leg", file=sys.stderr, flush=True)
         result["backward"] = backward_leg(spec, raw, inputs, torch, lattn, dev)
+        result["backward"]["ratio_to_forward"] = round(result["backward"]["ms_per_step"] / result["ms_per_step"], 2)
     if spec.name == workloads.HEADLINE and not args.no_loglinear:
         print("[bench] log-linear lift leg", file=sys.stderr, flush=True)
         result["loglinear"] = loglinear_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))

@@ -312,6 +312,14 @@ __global__ __launch_bounds__(256) void bwc_tri_kernel(BcTriArgs a) {
 // The pairs: (dK, dA) and (dQ, dB).
 enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 };
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
+// Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
+// solve; the sequence's own rows t0 .. t0 + C - 1 (bf16 [T][cols], zero past
+// the sequence); a per-chunk fp32 boundary array; the same scaled by Gamma per row.
+enum BcSrcKind { kSrcChunk = 0, kSrcSeq = 1, kSrcF32 = 2, kSrcF32G = 3 };
+struct BcSrc {
+  const void* ptr;
+  int kind;
+};
 
 template <int KIND, int DK, int DV, int RAB>
 struct BcKindCfg {
@@ -329,6 +337,10 @@ struct BcKindCfg {
   // dA, dB), read by rows; or W0 itself (dV and the right-hand sides), read
   // with the transposing LDS read
   static constexpr bool W0T = KIND == kDq || KIND == kDk || KIND == kDa || KIND == kDb;
+  // where the shared operands live (see BcSrcKind)
+  static constexpr int SW0 = (KIND == kRhsY || KIND == kDq || KIND == kDb) ? kSrcF32 : kSrcF32G;
+  static constexpr int SB1 = (KIND == kDq || KIND == kDb || KIND == kDk || KIND == kDa) ? kSrcSeq : kSrcChunk;
+  static constexpr int SC1 = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? kSrcSeq : kSrcChunk;
 };
 
 // LDS layout of a kind's staged operands (bf16 elements).  Rows read by
@@ -346,14 +358,6 @@ struct BcStage {
   static constexpr int TOTAL = OC2 + (K::TERM2 ? NA * LC : 0);
 };
 
-// Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
-// solve; the sequence's own rows t0 .. t0 + C - 1 (bf16 [T][cols], zero past
-// the sequence); a per-chunk fp32 boundary array; the same scaled by Gamma per row.
-enum BcSrcKind { kSrcChunk = 0, kSrcSeq = 1, kSrcF32 = 2, kSrcF32G = 3 };
-struct BcSrc {
-  const void* ptr;
-  int kind;
-};
 
 struct BcGroupArgs {
   Problem p;
@@ -373,32 +377,36 @@ __device__ __forceinline__ bool bc_empty(int ta0, int ta1, int tb0, int tb1) {
   return MASK == kLE ? tb0 > ta1 : (MASK == kLT ? tb0 >= ta1 : (MASK == kGE ? tb1 < ta0 : tb1 <= ta0));
 }
 
-// 16 rows (block rb) of kind KIND's output for chunk job, B side in LDS.
+// The A fragments of 16 rows (block rb) of kind KIND for chunk job.
 template <int KIND, int DK, int DV, int RAB>
-__device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, const BcSrc& As, const __bf16* lds,
-                                        const BcBufs& w, float* out, int lane) {
+__device__ __forceinline__ void bc_afrag(const Problem& p, int64_t job, int rb, const BcSrc& As,
+                                         cb8 (&af)[BcKindCfg<KIND, DK, DV, RAB>::KA / 32], int lane) {
+  using K = BcKindCfg<KIND, DK, DV, RAB>;
+  const int lr = lane & 15, r0 = 16 * rb;
+  const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
+  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  const __bf16* arow;
+  if (As.kind == kSrcSeq) {
+    const int r = r0 + lr < n ? r0 + lr : n - 1;   // a padding row's output is not written
+    arow = static_cast<const __bf16*>(As.ptr) + (bh * p.T + t0 + r) * K::KA;
+  } else {
+    arow = static_cast<const __bf16*>(As.ptr) + (job * K::M + r0 + lr) * K::KA;
+  }
+#pragma unroll
+  for (int ks = 0; ks < K::KA / 32; ++ks) af[ks] = rowfrag(arow, ks, lane);
+}
+
+// 16 rows (block rb) of kind KIND's product for chunk job, B side in LDS:
+// acc (accumulator layout: lane holds rows 4 lg + e, column 16 ot + lr).
+template <int KIND, int DK, int DV, int RAB>
+__device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
+                                        const cb8 (&af)[BcKindCfg<KIND, DK, DV, RAB>::KA / 32], const __bf16* lds,
+                                        cf4 (&acc)[BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
   using L = BcStage<KIND, DK, DV, RAB>;
   constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
   const int lr = lane & 15, lg = lane >> 4;
   const int r0 = 16 * rb;
-  const int64_t bh = job / p.N, jc = job % p.N, t0 = jc * kCC;
-  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
-  const int64_t tok0 = bh * p.T + t0;
-  // rows of padding tokens only: no gradient to write (the right-hand sides
-  // are formed for them too, as zeros, since the solves read every row)
-  if (!(KIND == kRhsY || KIND == kRhsX) && r0 / K::RA >= n) return;
-  const __bf16* arow;
-  if (As.kind == kSrcSeq) {
-    const int r = r0 + lr < n ? r0 + lr : n - 1;   // a padding row's output is not written
-    arow = static_cast<const __bf16*>(As.ptr) + (tok0 + r) * K::KA;
-  } else {
-    arow = static_cast<const __bf16*>(As.ptr) + (job * K::M + r0 + lr) * K::KA;
-  }
-  cb8 af[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) af[ks] = rowfrag(arow, ks, lane);
-  cf4 acc[OT];
 #pragma unroll
   for (int ot = 0; ot < OT; ++ot) {
     acc[ot] = cz4();
@@ -443,32 +451,98 @@ __device__ __forceinline__ void bc_rows(const Problem& p, int64_t job, int rb, c
   if constexpr (K::TERM2)
     term(L::OB2, L::OC2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
          std::integral_constant<int, K::MSK2>{}, -1.f);
+}
 
-  // ---- epilogue: lane holds rows r0 + 4 lg + e, column 16 ot + lr
-  if constexpr (KIND == kRhsY || KIND == kRhsX) {
+// A gradient kind's rows from the LDS copy of the products (ep: M rows of
+// NOUT + 4 floats) to memory, four columns per thread: scaled back from the
+// decay-scaled operands (e^{+-G} per token and channel) and signed.
+template <int KIND, int DK, int DV, int RAB, int NT>
+__device__ __forceinline__ void bc_out(const Problem& p, int64_t job, const float* ep, const BcBufs& w, float* out,
+                                       int tid) {
+  using K = BcKindCfg<KIND, DK, DV, RAB>;
+  constexpr int C4 = K::NOUT / 4, LE = K::NOUT + 4, ITEMS = K::M * C4;
+  const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
+  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  const int64_t tok0 = bh * p.T + t0;
+  const float* gc = w.gc + job * kCC * DK;
+#pragma unroll 4
+  for (int it = tid; it < ITEMS; it += NT) {
+    const int row = it / C4, c = (it - row * C4) * 4;
+    const int t = row / K::RA;
+    if (t >= n) continue;
+    cf4 v = *reinterpret_cast<const cf4*>(ep + row * LE + c);
+    if constexpr (KIND == kDq || KIND == kDk || KIND == kDa || KIND == kDb) {
+      const int tg = KIND == kDb ? (t > 0 ? t - 1 : 0) : t;
+      const cf4 g = *reinterpret_cast<const cf4*>(gc + tg * DK + c);
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot)
-      *reinterpret_cast<cf4*>(out + (((job * (NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
-  } else {
-    const float* gc = w.gc + job * kCC * DK;
+      for (int u = 0; u < 4; ++u) {
+        float f;
+        if constexpr (KIND == kDq) f = expf(g[u]);
+        else if constexpr (KIND == kDb) f = t > 0 ? expf(g[u]) : 1.f;
+        else f = expf(-g[u]);
+        v[u] *= K::SIGN * f;
+      }
+    }
+    // row-major rows of the token's rank rows: dq [T][dk], dK [T][1][dk], dV [T][1][dv], dA/dB [T][r][dk]
+    *reinterpret_cast<cf4*>(out + (tok0 * K::RA + row) * K::NOUT + c) = v;
+  }
+}
+
+// One operand's staging: ROWS x COLS from source kind SRC, in pieces of eight
+// elements, IT per thread (NT threads).
+template <int SRC, int ROWS, int COLS, int NT>
+struct BcStg {
+  static constexpr int P = ROWS * COLS / 8, IT = (P + NT - 1) / NT, PR = COLS / 8;
+  static constexpr bool F32 = SRC == kSrcF32 || SRC == kSrcF32G;
+  cf4 x0[IT], x1[F32 ? IT : 1];
+  float gs[SRC == kSrcF32G ? IT : 1];
+  int n_ = 0;
+  __device__ __forceinline__ void load(const void* ptr, const float* gam, int64_t job, int n, int64_t tok0, int tid) {
+    n_ = n;
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot) {
-      const int col = 16 * ot + lr;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = r0 + 4 * lg + e;
-        const int t = row / K::RA;
-        if (t >= n) continue;
-        float v = K::SIGN * acc[ot][e];
-        if constexpr (KIND == kDq) v *= expf(gc[t * DK + col]);
-        if constexpr (KIND == kDk || KIND == kDa) v *= expf(-gc[t * DK + col]);
-        if constexpr (KIND == kDb) v *= t > 0 ? expf(gc[(t - 1) * DK + col]) : 1.f;
-        // row-major rows of the token's rank rows: dq [T][dk], dK [T][1][dk], dV [T][1][dv], dA/dB [T][r][dk]
-        out[(tok0 * K::RA + row) * K::NOUT + col] = v;
+    for (int k = 0; k < IT; ++k) {
+      const int i0 = tid + k * NT, i = i0 < P ? i0 : P - 1;   // the last piece again, not stored
+      const int r = i / PR, c8 = (i - r * PR) * 8;
+      if constexpr (F32) {
+        const float* f = static_cast<const float*>(ptr) + (job * ROWS + r) * COLS + c8;
+        x0[k] = *reinterpret_cast<const cf4*>(f);
+        x1[k] = *reinterpret_cast<const cf4*>(f + 4);
+        if constexpr (SRC == kSrcF32G) gs[k] = gam[r];
+      } else if constexpr (SRC == kSrcSeq) {
+        // rows past the sequence read its last row and are zeroed at the store
+        const int rr = r < n ? r : n - 1;
+        x0[k] = *reinterpret_cast<const cf4*>(static_cast<const __bf16*>(ptr) + (tok0 + rr) * COLS + c8);
+      } else {
+        x0[k] = *reinterpret_cast<const cf4*>(static_cast<const __bf16*>(ptr) + (job * ROWS + r) * COLS + c8);
       }
     }
   }
-}
+  __device__ __forceinline__ void store(__bf16* lds, int ld, int tid) {
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int i = tid + k * NT;
+      if (i < P) {
+        const int r = i / PR, c8 = (i - r * PR) * 8;
+        cb8 v;
+        if constexpr (F32) {
+          const float g = SRC == kSrcF32G ? gs[k] : 1.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            v[u] = (__bf16)(g * x0[k][u]);
+            v[u + 4] = (__bf16)(g * x1[k][u]);
+          }
+        } else {
+          v = __builtin_bit_cast(cb8, x0[k]);
+          if (SRC == kSrcSeq && r >= n_) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = (__bf16)0.f;
+          }
+        }
+        *reinterpret_cast<cb8*>(lds + r * ld + c8) = v;
+      }
+    }
+  }
+};
 
 template <int KA_, int KB_>
 struct BcGroupWaves {
@@ -482,7 +556,8 @@ template <int KA_, int KB_, int DK, int DV, int RAB, int NW>
 __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   using K = BcKindCfg<KA_, DK, DV, RAB>;
   using L = BcStage<KA_, DK, DV, RAB>;
-  constexpr int WA = K::M / 16;
+  constexpr int WA = K::M / 16, KS = K::KA / 32, OT = K::NOUT / 16;
+  constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX;
   extern __shared__ __align__(16) unsigned char smem_[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem_);
   const Problem& p = a.p;
@@ -491,46 +566,69 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   const int64_t tok0 = bh * p.T + jc * kCC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // stage a chunk's rows x cols operand into LDS rows of ld elements
-  auto stage = [&](const BcSrc& sr, int rows, int cols, int off, int ld) {
-    const int pieces = rows * cols / 8, pr = cols / 8;
-    for (int i = tid; i < pieces; i += 64 * NW) {
-      const int r = i / pr, c8 = (i - r * pr) * 8;
-      cb8 v;
-      if (sr.kind == kSrcChunk) {
-        v = *reinterpret_cast<const cb8*>(static_cast<const __bf16*>(sr.ptr) + (job * rows + r) * cols + c8);
-      } else if (sr.kind == kSrcSeq) {
-        if (r < n) {
-          v = *reinterpret_cast<const cb8*>(static_cast<const __bf16*>(sr.ptr) + (tok0 + r) * cols + c8);
-        } else {
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = (__bf16)0.f;
-        }
-      } else {
-        const float* f = static_cast<const float*>(sr.ptr) + (job * rows + r) * cols + c8;
-        const cf4 x0 = *reinterpret_cast<const cf4*>(f), x1 = *reinterpret_cast<const cf4*>(f + 4);
-        const float gsc = sr.kind == kSrcF32G ? a.w.gam[job * DK + r] : 1.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          v[u] = (__bf16)(gsc * x0[u]);
-          v[u + 4] = (__bf16)(gsc * x1[u]);
-        }
-      }
-      *reinterpret_cast<cb8*>(lds + off + r * ld + c8) = v;
-    }
-  };
-  stage(a.W0, L::W0R, L::W0C, L::OW, L::LW0);
-  stage(a.B1, kCC, K::KA, L::OB1, L::LB);
-  stage(a.C1, kCC, K::NOUT, L::OC1, L::LC);
+  const bool isa = wave < WA;
+  const int rb = isa ? wave : wave - WA;
+  // this wave's A rows first, so that their loads overlap the staging's
+  cb8 af[KS];
+  if (isa) {
+    bc_afrag<KA_, DK, DV, RAB>(p, job, rb, a.Aa, af, lane);
+  } else if constexpr (KB_ >= 0) {
+    bc_afrag<KB_, DK, DV, RAB>(p, job, rb, a.Ab, af, lane);
+  }
+  // Staging: every load of every operand is issued before any LDS write, so
+  // their latencies overlap.
+  BcStg<K::SW0, L::W0R, L::W0C, 64 * NW> s0;
+  BcStg<K::SB1, kCC, K::KA, 64 * NW> s1;
+  BcStg<K::SC1, kCC, K::NOUT, 64 * NW> s2;
+  BcStg<kSrcChunk, (K::TERM2 ? K::NA : 16), K::KA, 64 * NW> s3;
+  BcStg<kSrcChunk, (K::TERM2 ? K::NA : 16), K::NOUT, 64 * NW> s4;
+  s0.load(a.W0.ptr, a.w.gam + job * DK, job, n, tok0, tid);
+  s1.load(a.B1.ptr, nullptr, job, n, tok0, tid);
+  s2.load(a.C1.ptr, nullptr, job, n, tok0, tid);
   if constexpr (K::TERM2) {
-    stage(a.B2, K::NA, K::KA, L::OB2, L::LB);
-    stage(a.C2, K::NA, K::NOUT, L::OC2, L::LC);
+    s3.load(a.B2.ptr, nullptr, job, n, tok0, tid);
+    s4.load(a.C2.ptr, nullptr, job, n, tok0, tid);
+  }
+  s0.store(lds + L::OW, L::LW0, tid);
+  s1.store(lds + L::OB1, L::LB, tid);
+  s2.store(lds + L::OC1, L::LC, tid);
+  if constexpr (K::TERM2) {
+    s3.store(lds + L::OB2, L::LB, tid);
+    s4.store(lds + L::OC2, L::LC, tid);
   }
   __syncthreads();
-  if (wave < WA) {
-    bc_rows<KA_, DK, DV, RAB>(p, job, wave, a.Aa, lds, a.w, a.outa, lane);
-  } else if constexpr (KB_ >= 0) {
-    bc_rows<KB_, DK, DV, RAB>(p, job, wave - WA, a.Ab, lds, a.w, a.outb, lane);
+  cf4 acc[OT];
+  // rows of padding tokens only: no gradient to write (the right-hand sides
+  // are formed for them too, as zeros, since the solves read every row)
+  const int ra = isa ? K::RA : BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::RA;
+  const bool live = RHS || 16 * rb / ra < n;
+  if (live) {
+    if (isa) {
+      bc_prod<KA_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane);
+    } else if constexpr (KB_ >= 0) {
+      bc_prod<KB_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane);
+    }
+  }
+  if constexpr (RHS) {
+#pragma unroll
+    for (int ot = 0; ot < OT; ++ot)
+      *reinterpret_cast<cf4*>(a.outa + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
+  } else {
+    // The gradients leave through LDS as whole rows: every wave's 16 x NOUT
+    // block into the (now free) staging space, then 16-byte stores.
+    constexpr int LE = K::NOUT + 4;
+    float* ep = reinterpret_cast<float*>(smem_);
+    __syncthreads();   // every wave is done with the staged operands
+    if (live) {
+      const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ep[(wave * 16 + 4 * lg + e) * LE + 16 * ot + lr] = acc[ot][e];
+    }
+    __syncthreads();
+    bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.w, a.outa, tid);
+    if constexpr (KB_ >= 0) bc_out<KB_, DK, DV, RAB, 64 * NW>(p, job, ep + WA * 16 * LE, a.w, a.outb, tid);
   }
 }
 
@@ -623,17 +721,53 @@ __global__ __launch_bounds__(256) void bwc_decay_kernel(BcDecayArgs a) {
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
   const int64_t tok0 = bh * p.T + t0;
   const int tid = threadIdx.x;
-  // per (token, channel) terms, channels across the threads
-  for (int idx = tid; idx < n * DK; idx += 256) {
-    const int t = idx / DK, c = idx - t * DK;
-    const int64_t tok = tok0 + t;
-    float g = (float)a.q[tok * DK + c] * a.dq[tok * DK + c] - (float)a.k[tok * DK + c] * a.dK[tok * DK + c];
+  // per (token, channel) terms: thread item (token, 8 channels), 16-byte
+  // loads; unconditional (padding tokens read the chunk's last token, and
+  // their terms are not kept) so that the unrolled loop issues them together
+  constexpr int P8 = DK / 8;
+  auto ld8b = [](const __bf16* x, float (&f)[8]) {
+    const cb8 v = *reinterpret_cast<const cb8*>(x);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f[u] = (float)v[u];
+  };
+  auto ld8f = [](const float* x, float (&f)[8]) {
+    const cf4 v0 = *reinterpret_cast<const cf4*>(x), v1 = *reinterpret_cast<const cf4*>(x + 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f[u] = v0[u];
+      f[u + 4] = v1[u];
+    }
+  };
+#pragma unroll 2
+  for (int it = 0; it < kCC * P8 / 256; ++it) {
+    const int idx = tid + 256 * it, t = idx / P8, c = (idx - t * P8) * 8;
+    const int tc = t < n ? t : n - 1;
+    const int64_t tok = tok0 + tc, tb = tok0 + (tc + 1 < n ? tc + 1 : tc);
+    const float nb = tc + 1 < n ? 1.f : 0.f;   // B of the next token, inside the chunk only
+    float x[8], y[8], g[8];
+    ld8b(a.q + tok * DK + c, x);
+    ld8f(a.dq + tok * DK + c, y);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) g[u] = x[u] * y[u];
+    ld8b(a.k + tok * DK + c, x);
+    ld8f(a.dK + tok * DK + c, y);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) g[u] -= x[u] * y[u];
 #pragma unroll
     for (int r = 0; r < RAB; ++r) {
-      g -= (float)a.A[(tok * RAB + r) * DK + c] * a.dA[(tok * RAB + r) * DK + c];
-      if (t + 1 < n) g += (float)a.B[((tok + 1) * RAB + r) * DK + c] * a.dB[((tok + 1) * RAB + r) * DK + c];
+      ld8b(a.A + (tok * RAB + r) * DK + c, x);
+      ld8f(a.dA + (tok * RAB + r) * DK + c, y);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) g[u] -= x[u] * y[u];
+      ld8b(a.B + (tb * RAB + r) * DK + c, x);
+      ld8f(a.dB + (tb * RAB + r) * DK + c, y);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) g[u] += nb * x[u] * y[u];
     }
-    gsm[t][c] = g;
+    if (t < n) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) gsm[t][c + u] = g[u];
+    }
   }
   // the chunk-end term rowdot(dS_end, S_end): TPC threads per channel
   {
@@ -893,7 +1027,9 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
     const void* fn = reinterpret_cast<const void*>(bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>);
-    const size_t lds = static_cast<size_t>(L::TOTAL) * 2;
+    const size_t stage_b = static_cast<size_t>(L::TOTAL) * 2;
+    const size_t ep_b = static_cast<size_t>(NW) * 16 * (L::NOUT + 4) * sizeof(float);   // the output copy
+    const size_t lds = stage_b > ep_b ? stage_b : ep_b;
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
