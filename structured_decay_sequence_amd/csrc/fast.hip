@@ -766,13 +766,15 @@ struct FastScanArgs {
   Problem p;
   const __bf16* M;
   const __bf16* v;
-  __bf16* out;         // null: the output rows are not stored
+  __bf16* out;         // output rows (the forward instance)
   float* Sfin;
   const float* S0;
-  float* ckpt;         // null, or [BH, N, dk, dv]: the state entering every chunk (fp32)
+  float* ckpt;         // [BH, N, dk, dv]: the state entering every chunk, fp32 (the boundary instance)
 };
 
-template <int DK, int BV, int NWV, int PD>
+// CK: the boundary-state instance, which stores the state entering every
+// chunk instead of the output rows (the backward's forward scan).
+template <int DK, int BV, int NWV, int PD, bool CK>
 __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
   constexpr int KP = Cfg::KP, MPW = Cfg::MPW, NTN = Cfg::NTN, LDX = Cfg::LDX, NT = Cfg::NT;
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   };
   // Output rows of chunk jj from a staging buffer to HBM (none past the end).
   auto flush_out = [&](const __bf16* O, int64_t jj) {
-    if (a.out == nullptr) return;
+    if (CK) return;
     const int n = chunk_len(jj);
     __bf16* oj = obh + static_cast<size_t>(jj) * kC * dv;
 #pragma unroll
@@ -870,7 +872,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     const int i = it / BV, c = it % BV;
     const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
     X0[c * LDX + kperm(i)] = (__bf16)s;
-    if (a.ckpt) a.ckpt[(static_cast<size_t>(bh * N) * DK + i) * dv + c0 + c] = s;
+    if (CK) a.ckpt[(static_cast<size_t>(bh * N) * DK + i) * dv + c0 + c] = s;
   }
   put_v(X0, vb[0], 0);
   // Ring invariant from here on: at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
@@ -923,7 +925,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
         }
       }
     }
-    if (a.ckpt && jj + 1 < N) {
+    if (CK && jj + 1 < N) {
       // the state entering chunk jj + 1: this product's state rows, in fp32
       float* ck = a.ckpt + static_cast<size_t>(bh * N + jj + 1) * DK * dv;
 #pragma unroll
@@ -1131,7 +1133,7 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
                   : launch_prep<DK, RAB, false, kGeneric>(p, q, k, ld, A, B, nullptr, M, s);
 }
 
-template <int DK, int BV, int NWV, int PD>
+template <int DK, int BV, int NWV, int PD, bool CK = false>
 hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out, float* Sfin,
                        const float* S0, float* ckpt, hipStream_t s) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
@@ -1139,10 +1141,10 @@ hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out
                  static_cast<__bf16*>(out), Sfin, S0, ckpt};
   const int nvt = p.dv / BV;
   const int64_t groups = (p.BH + 7) / 8;
-  const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD>);
+  const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD, CK>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD>), dim3(groups * 8 * nvt), dim3(Cfg::NT), Cfg::LDS,
+  hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD, CK>), dim3(groups * 8 * nvt), dim3(Cfg::NT), Cfg::LDS,
                      s, a);
   return hipGetLastError();
 }
@@ -1188,6 +1190,12 @@ hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s, float* ckpt) {
   if (p.BH == 0) return hipSuccess;
+  if (ckpt) {
+    // the boundary-state instance: states instead of output rows
+    if (p.dk == 128) return launch_scan<128, 32, 4, 2, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
+    if (p.dk == 64) return launch_scan<64, 16, 4, 4, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
+    return hipErrorInvalidValue;
+  }
   // Wider d_v slices share each operator load among more columns; narrower
   // ones are used when that leaves too few workgroups to fill the chip.
   if (p.dk == 128 && p.BH * (p.dv / 64) >= 256)

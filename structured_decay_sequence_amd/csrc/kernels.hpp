@@ -44,8 +44,8 @@ hipError_t general_summaries(const Problem& p, const void* workspace, const void
 
 // bf16 MFMA path: bf16 storage, C = 64, r_kv = 1, r_ab in {0, 1, 2}, d_k in {64, 128},
 // d_v a multiple of 64.  The workspace holds the fragment-ordered chunk operators.
-// fast_scan: out may be null (no output rows); ckpt, if given, receives the
-// state entering every chunk [BH, N, dk, dv] in fp32.
+// fast_scan: with ckpt given, the state entering every chunk [BH, N, dk, dv]
+// goes there in fp32 and no output rows are written (out is ignored).
 bool fast_supported(const Problem& p);
 size_t fast_workspace_bytes(const Problem& p);
 hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const float* ld,
