@@ -29,6 +29,26 @@ HIPCC_FLAGS = [
 ]
 
 
+# Sources of the bf16 MFMA kernels: none of their kernels may use scratch
+# memory (a register spill there costs time and HBM writes, and has crept in
+# unnoticed before), so the build fails if one does.
+SCRATCH_FREE = ("fast.hip", "loglinear.hip", "backward_chunk.hip")
+_RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(remarks: str):
+    """(function, bytes per lane) of every function the compiler's resource
+    remarks report with scratch memory."""
+    import re
+
+    out = []
+    for block in remarks.split("Function Name: ")[1:]:
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", block)
+        if m and int(m.group(1)) > 0:
+            out.append((block.split()[0], int(m.group(1))))
+    return out
+
+
 def sources():
     return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
@@ -53,7 +73,8 @@ def build(verbose: bool = False, extra=None, jobs: int = 0) -> str:
     inc = ["-I", os.path.join(ROOT, "include")]
     srcs = sources()
     objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
-    cmds = [[hipcc, *flags, *inc, "-c", "-o", o, s] for s, o in zip(srcs, objs)]
+    cmds = [[hipcc, *flags, *inc, "-c", "-o", o, s] + ([_RESOURCE_REMARK] if os.path.basename(s) in SCRATCH_FREE else [])
+            for s, o in zip(srcs, objs)]
     if verbose:
         for c in cmds:
             print(" ".join(c), flush=True)
@@ -63,6 +84,12 @@ def build(verbose: bool = False, extra=None, jobs: int = 0) -> str:
     for (rc, errs), s in zip(results, srcs):
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {os.path.basename(s)} ({rc}):\n{errs}")
+        if os.path.basename(s) in SCRATCH_FREE:
+            bad = scratch_users(errs)
+            if bad:
+                raise RuntimeError(f"{os.path.basename(s)}: kernels using scratch memory (bytes per lane): {bad}")
+            errs = "\n".join(l for l in errs.splitlines() if "kernel-resource-usage" not in l
+                             and not l.lstrip().startswith(("|", "^")) and "remark" not in l)
         if verbose and errs.strip():
             print(errs, file=sys.stderr)
     tmp = LIB + ".tmp"
