@@ -25,10 +25,10 @@
 // S_in and dS_end come from the chunk-boundary scans.
 //
 // Kernels, each over all chunks: prep (G and the scaled operands, row-major
-// bf16), tri (the blocks of L and the inverses of its unit diagonal blocks),
-// grouped products (the two right-hand sides, then the five gradients:
-// out = A W0 + sum_i s_i mask_i(A B_i^T) C_i), solve (Y forward, X backward
-// substitution, one wave per 16 value columns), decay.  A product group stages
+// bf16), grouped products (the two right-hand sides, then the five gradients:
+// out = A W0 + sum_i s_i mask_i(A B_i^T) C_i), solve (the blocks of L and the
+// inverses of its unit diagonal blocks in LDS, then Y by forward and X by
+// backward substitution, one wave per 16 value columns), decay.  A product group stages
 // its chunk's B-side operands in LDS row-major, straight from where they live
 // (the prep's arrays, the V and dO rows of the sequence, the fp32 boundary
 // states); operands needed transposed are read with the transposing LDS read.
@@ -96,10 +96,9 @@ struct BcBufs {
   float* gam;                // [dk] e^{G} at the chunk's last token
   __bf16 *qt, *kt;           // [C][dk]
   __bf16 *at, *bt;           // [NA][dk]
-  __bf16 *lb, *lbT;          // L blocks below the diagonal, 16x16 row-major tiles, and their transposes
-  float *dinv, *dinvT;       // inverses of the unit diagonal blocks, and their transposes
   float *ry, *rx;            // right-hand sides in tile order [NA/16][dv/16][64 lanes][4]
   __bf16 *y, *x;             // [NA][dv]
+  float *gq, *gk;            // [C][dk] the decay gradient's terms from the dQ / dK product groups
 };
 
 size_t bc_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -107,9 +106,8 @@ size_t bc_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Lays the buffers out in ws (nullptr: only count).  Returns the bytes used.
 size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
   const size_t J = static_cast<size_t>(p.BH * p.N);
-  const size_t NA = static_cast<size_t>(kCC) * p.r_ab, NB = NA / 16;
+  const size_t NA = static_cast<size_t>(kCC) * p.r_ab;
   const size_t cdk = static_cast<size_t>(kCC) * p.dk, adk = NA * p.dk, ndv = NA * p.dv;
-  const size_t lt = (NB > 0 ? NB * (NB - 1) / 2 : 0) * 256;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* r = ws ? ws + off : nullptr;
@@ -123,14 +121,12 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
   t.kt = reinterpret_cast<__bf16*>(take(J * cdk * 2));
   t.at = reinterpret_cast<__bf16*>(take(J * adk * 2));
   t.bt = reinterpret_cast<__bf16*>(take(J * adk * 2));
-  t.lb = reinterpret_cast<__bf16*>(take(J * lt * 2));
-  t.lbT = reinterpret_cast<__bf16*>(take(J * lt * 2));
-  t.dinv = reinterpret_cast<float*>(take(J * NB * 256 * 4));
-  t.dinvT = reinterpret_cast<float*>(take(J * NB * 256 * 4));
   t.ry = reinterpret_cast<float*>(take(J * ndv * 4));
   t.rx = reinterpret_cast<float*>(take(J * ndv * 4));
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.x = reinterpret_cast<__bf16*>(take(J * ndv * 2));
+  t.gq = reinterpret_cast<float*>(take(J * cdk * 4));
+  t.gk = reinterpret_cast<float*>(take(J * cdk * 4));
   if (b) *b = t;
   return off;
 }
@@ -240,71 +236,6 @@ __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// tri: blocks (i, j <= i) of L = M_<(Bt At^T) (rank rows; tokens row / r_ab),
-// formed in both orientations so that each tile is stored with 8-byte writes;
-// the diagonal blocks in fp32, then the inverses of I + L_ii by forward
-// substitution (one thread per column).
-struct BcTriArgs {
-  Problem p;
-  BcBufs w;
-};
-
-template <int DK, int RAB>
-__global__ __launch_bounds__(256) void bwc_tri_kernel(BcTriArgs a) {
-  constexpr int NA = kCC * RAB, NB = NA / 16, NT = NB * (NB + 1) / 2, NTI = NB * (NB - 1) / 2;
-  __shared__ float dg[NB][256];
-  const int64_t job = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
-  const __bf16* bt = a.w.bt + job * NA * DK;
-  const __bf16* at = a.w.at + job * NA * DK;
-  for (int idx = wave; idx < NT; idx += 4) {
-    int i = 0, jj = idx;
-    while (jj > i) {
-      jj -= i + 1;
-      ++i;
-    }
-    cf4 P = cz4(), Q = cz4();
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const cb8 bf = *reinterpret_cast<const cb8*>(bt + (16 * i + lr) * DK + 32 * ks + 8 * lg);
-      const cb8 af = *reinterpret_cast<const cb8*>(at + (16 * jj + lr) * DK + 32 * ks + 8 * lg);
-      P = mfma_b(bf, af, P);   // lane: L[16 i + 4 lg + e][16 jj + lr]
-      Q = mfma_b(af, bf, Q);   // lane: L[16 i + lr][16 jj + 4 lg + e]
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!((16 * i + 4 * lg + e) / RAB > (16 * jj + lr) / RAB)) P[e] = 0.f;
-      if (!((16 * i + lr) / RAB > (16 * jj + 4 * lg + e) / RAB)) Q[e] = 0.f;
-    }
-    if (jj < i) {
-      const int blk = i * (i - 1) / 2 + jj;
-      *reinterpret_cast<cb4*>(a.w.lb + (job * NTI + blk) * 256 + lr * 16 + 4 * lg) = to_b4(Q);
-      *reinterpret_cast<cb4*>(a.w.lbT + (job * NTI + blk) * 256 + lr * 16 + 4 * lg) = to_b4(P);
-    } else {
-      *reinterpret_cast<cf4*>(&dg[i][lr * 16 + 4 * lg]) = Q;
-    }
-  }
-  __syncthreads();
-  if (tid < NB * 16) {
-    const int blk = tid / 16, c = tid % 16;
-    float x[16];
-    float* Di = a.w.dinv + (job * NB + blk) * 256;
-    float* DiT = a.w.dinvT + (job * NB + blk) * 256;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = (r == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) v -= dg[blk][r * 16 + m] * x[m];
-      x[r] = v;
-      Di[r * 16 + c] = v;
-      DiT[c * 16 + r] = v;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Grouped products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i over one chunk.
 // A group is one or two kinds whose products read the same B-side operands
 // (W0, B1, C1, B2, C2): one workgroup per chunk stages them in LDS once, then
@@ -365,6 +296,7 @@ struct BcGroupArgs {
   BcSrc W0, B1, C1, B2, C2;     // the shared B-side operands
   BcBufs w;
   float *outa, *outb;           // right-hand sides (tile order) or gradients
+  const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
 };
 
 template <int MASK>
@@ -544,6 +476,50 @@ struct BcStg {
   }
 };
 
+// The decay gradient's terms of a dK or dQ product group, per (token, four
+// channels), from the products still in LDS (ep) and the raw inputs:
+//   dK group: -k dk - sum_r A dA         = -e^{-G_t} (k dKt  - sum_r A_t,r dAt_t,r)
+//   dQ group:  q dq + sum_r B_{t+1} dB_{t+1} = e^{G_t} (q dQt - sum_r B_t+1,r dBt_t+1,r)
+// (dAt, dBt as the products hold them, before their sign; dB_{t+1} is scaled
+// by e^{G_t}, and only inside the chunk).
+template <int KA_, int DK, int DV, int RAB, int NT>
+__device__ __forceinline__ void bc_decay_terms(const Problem& p, int64_t job, const float* ep, const BcBufs& w,
+                                               const __bf16* xr, const __bf16* rr, int tid) {
+  using K = BcKindCfg<KA_, DK, DV, RAB>;
+  constexpr bool KG = KA_ == kDk;   // else the dQ group
+  constexpr int LE = K::NOUT + 4, C4 = DK / 4;
+  const float* epb = ep + (K::M / 16) * 16 * LE;   // the rank-row kind's rows
+  const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
+  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+  const int64_t tok0 = bh * p.T + t0;
+  const float* gc = w.gc + job * kCC * DK;
+  float* dst = (KG ? w.gk : w.gq) + job * kCC * DK;
+#pragma unroll 2
+  for (int it = tid; it < kCC * C4; it += NT) {
+    const int t = it / C4, c = (it - t * C4) * 4;
+    if (t >= n) continue;
+    const cf4 g = *reinterpret_cast<const cf4*>(gc + t * DK + c);
+    const cf4 pa = *reinterpret_cast<const cf4*>(ep + t * LE + c);
+    const cb4 xv = *reinterpret_cast<const cb4*>(xr + (tok0 + t) * DK + c);
+    cf4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (float)xv[u] * pa[u];
+    const int tr = KG ? t : t + 1;   // token of the rank rows
+    if (RAB > 0 && tr < n) {
+#pragma unroll
+      for (int r = 0; r < (RAB > 0 ? RAB : 1); ++r) {
+        const cf4 pb = *reinterpret_cast<const cf4*>(epb + (tr * RAB + r) * LE + c);
+        const cb4 rv = *reinterpret_cast<const cb4*>(rr + ((tok0 + tr) * RAB + r) * DK + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] -= (float)rv[u] * pb[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] *= KG ? -expf(-g[u]) : expf(g[u]);
+    *reinterpret_cast<cf4*>(dst + t * DK + c) = v;
+  }
+}
+
 template <int KA_, int KB_>
 struct BcGroupWaves {
   template <int DK, int DV, int RAB>
@@ -629,38 +605,108 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     __syncthreads();
     bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.w, a.outa, tid);
     if constexpr (KB_ >= 0) bc_out<KB_, DK, DV, RAB, 64 * NW>(p, job, ep + WA * 16 * LE, a.w, a.outb, tid);
+    if constexpr (KA_ == kDk || KA_ == kDq) bc_decay_terms<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.w, a.xr, a.rr, tid);
   }
 }
 
 // ---------------------------------------------------------------------------
-// solve: one wave per (chunk, Y or X, 16 value columns).  Y: forward
-// substitution Y_i = D_i (R_i - sum_{j<i} L_ij Y_j); X: backward substitution
-// X_i = D_i^T (R_i - sum_{j>i} L_ji^T X_j).  The products pair two 16-row
-// blocks into one 16x16x32 MFMA (a lone block padded with zeros), with the
-// solved blocks fed back from registers as the B operand; the diagonal
-// inverses apply in fp32.
+// tri + solve: one workgroup per chunk, one wave per (Y or X, 16 value columns).
+//  * The blocks (i, j <= i) of L = M_<(Bt At^T) (rank rows; tokens row / r_ab)
+//    are formed into LDS: below the diagonal as 16x16 bf16 tiles in both
+//    orientations (each from its own product, so every tile is written with
+//    8-byte stores); the diagonal blocks in fp32, then the inverses of
+//    I + L_ii by forward substitution (one thread per column).
+//  * Y: forward substitution Y_i = D_i (R_i - sum_{j<i} L_ij Y_j); X: backward
+//    substitution X_i = D_i^T (R_i - sum_{j>i} L_ji^T X_j).  The products pair
+//    two 16-row blocks into one 16x16x32 MFMA (a lone block padded with
+//    zeros), the solved blocks fed back from registers as the B operand; the
+//    diagonal inverses apply in fp32.
+// The right-hand sides' loads are issued first, so they overlap the L phase.
 struct BcSolveArgs {
   Problem p;
   BcBufs w;
 };
 
 template <int DK, int DV, int RAB>
-__global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
-  constexpr int NA = kCC * RAB, NB = NA / 16, NTI = NB * (NB - 1) / 2, NCT = DV / 16;
-  const Problem& p = a.p;
+struct BcSolveCfg {
+  static constexpr int NA = kCC * RAB, NB = NA / 16, NT = NB * (NB + 1) / 2, NTI = NB * (NB - 1) / 2;
+  static constexpr int NCT = DV / 16, NW = 2 * NCT;
+  // LDS (bytes): L tiles and their transposes (bf16), the diagonal blocks, the
+  // inverses and their transposes (fp32)
+  static constexpr int OL = 0, OLT = OL + NTI * 512, ODG = OLT + NTI * 512, ODI = ODG + NB * 1024,
+                       ODT = ODI + NB * 1024, LDS = ODT + NB * 1024;
+};
+
+template <int DK, int DV, int RAB>
+__global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_kernel(BcSolveArgs a) {
+  using Cf = BcSolveCfg<DK, DV, RAB>;
+  constexpr int NA = Cf::NA, NB = Cf::NB, NT = Cf::NT, NCT = Cf::NCT, NW = Cf::NW;
+  __shared__ __align__(16) unsigned char sm[Cf::LDS];
+  __bf16* Lb = reinterpret_cast<__bf16*>(sm + Cf::OL);
+  __bf16* LbT = reinterpret_cast<__bf16*>(sm + Cf::OLT);
+  float* dg = reinterpret_cast<float*>(sm + Cf::ODG);
+  float* Di = reinterpret_cast<float*>(sm + Cf::ODI);
+  float* DiT = reinterpret_cast<float*>(sm + Cf::ODT);
+  const int64_t job = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const int64_t job = gw / (2 * NCT);
-  if (job >= p.BH * p.N) return;   // whole waves; no barrier in this kernel
-  const int rem = static_cast<int>(gw % (2 * NCT));
-  const bool isx = rem >= NCT;
-  const int ct = rem % NCT;
   const BcBufs& w = a.w;
+  const bool isx = wave >= NCT;
+  const int ct = wave % NCT;
+  // this wave's right-hand side tiles, loaded first
   const float* R = (isx ? w.rx : w.ry) + job * NA * DV;
-  const __bf16* Lt = (isx ? w.lbT : w.lb) + job * NTI * 256;
-  const float* Dg = (isx ? w.dinvT : w.dinv) + job * NB * 256;
+  cf4 rhs[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) rhs[i] = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+  // ---- L
+  const __bf16* bt = w.bt + job * NA * DK;
+  const __bf16* at = w.at + job * NA * DK;
+  for (int idx = wave; idx < NT; idx += NW) {
+    int i = 0, jj = idx;
+    while (jj > i) {
+      jj -= i + 1;
+      ++i;
+    }
+    cf4 P = cz4(), Q = cz4();
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+      const cb8 bf = *reinterpret_cast<const cb8*>(bt + (16 * i + lr) * DK + 32 * ks + 8 * lg);
+      const cb8 af = *reinterpret_cast<const cb8*>(at + (16 * jj + lr) * DK + 32 * ks + 8 * lg);
+      P = mfma_b(bf, af, P);   // lane: L[16 i + 4 lg + e][16 jj + lr]
+      Q = mfma_b(af, bf, Q);   // lane: L[16 i + lr][16 jj + 4 lg + e]
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!((16 * i + 4 * lg + e) / RAB > (16 * jj + lr) / RAB)) P[e] = 0.f;
+      if (!((16 * i + lr) / RAB > (16 * jj + 4 * lg + e) / RAB)) Q[e] = 0.f;
+    }
+    if (jj < i) {
+      const int blk = i * (i - 1) / 2 + jj;
+      *reinterpret_cast<cb4*>(Lb + blk * 256 + lr * 16 + 4 * lg) = to_b4(Q);
+      *reinterpret_cast<cb4*>(LbT + blk * 256 + lr * 16 + 4 * lg) = to_b4(P);
+    } else {
+      *reinterpret_cast<cf4*>(dg + i * 256 + lr * 16 + 4 * lg) = Q;
+    }
+  }
+  __syncthreads();
+  if (tid < NB * 16) {
+    const int blk = tid / 16, c = tid % 16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) v -= dg[blk * 256 + r * 16 + m] * x[m];
+      x[r] = v;
+      Di[blk * 256 + r * 16 + c] = v;
+      DiT[blk * 256 + c * 16 + r] = v;
+    }
+  }
+  __syncthreads();
+  // ---- the substitutions
+  const __bf16* Lt = isx ? LbT : Lb;
+  const float* Dg = isx ? DiT : Di;
   cb4 nb[NB];   // -solution blocks in bf16, the B operand of later blocks
   auto ltile = [&](int blk) { return *reinterpret_cast<const cb4*>(Lt + blk * 256 + lr * 16 + 4 * lg); };
   auto finish = [&](int i, cf4 acc) {
@@ -677,7 +723,7 @@ __global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
   if (!isx) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      cf4 acc = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+      cf4 acc = rhs[i];
       const int base = i * (i - 1) / 2;   // tiles (i, 0 .. i-1)
 #pragma unroll
       for (int jb = 0; jb + 1 < i; jb += 2)
@@ -688,7 +734,7 @@ __global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
   } else {
 #pragma unroll
     for (int i = NB - 1; i >= 0; --i) {
-      cf4 acc = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+      cf4 acc = rhs[i];
       // tiles (L_ji)^T for j = i+1 .. NB-1, stored at index j (j - 1) / 2 + i
       int jb = i + 1;
 #pragma unroll
@@ -701,12 +747,12 @@ __global__ __launch_bounds__(256) void bwc_solve_kernel(BcSolveArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// decay: the per-(token, channel) terms in parallel, then one thread per
-// channel sums them in reverse.
+// decay: the two product groups' per-(token, channel) terms and the chunk-end
+// term rowdot(dS_end, S_end), summed in reverse over the chunk's tokens by one
+// thread per channel.
 struct BcDecayArgs {
   Problem p;
-  const __bf16 *q, *k, *A, *B;
-  const float *dq, *dK, *dA, *dB;
+  const float *gq, *gk;   // the product groups' per-(token, channel) terms
   const float *ckpt, *gend, *sfin;
   float* dld;
 };
@@ -721,53 +767,13 @@ __global__ __launch_bounds__(256) void bwc_decay_kernel(BcDecayArgs a) {
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
   const int64_t tok0 = bh * p.T + t0;
   const int tid = threadIdx.x;
-  // per (token, channel) terms: thread item (token, 8 channels), 16-byte
-  // loads; unconditional (padding tokens read the chunk's last token, and
-  // their terms are not kept) so that the unrolled loop issues them together
-  constexpr int P8 = DK / 8;
-  auto ld8b = [](const __bf16* x, float (&f)[8]) {
-    const cb8 v = *reinterpret_cast<const cb8*>(x);
+  // per (token, channel) terms: the two product groups' partials
+  for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+    const int t = idx / (DK / 4), c = (idx - t * (DK / 4)) * 4;
+    const cf4 x = *reinterpret_cast<const cf4*>(a.gq + (job * kCC + t) * DK + c);
+    const cf4 y = *reinterpret_cast<const cf4*>(a.gk + (job * kCC + t) * DK + c);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) f[u] = (float)v[u];
-  };
-  auto ld8f = [](const float* x, float (&f)[8]) {
-    const cf4 v0 = *reinterpret_cast<const cf4*>(x), v1 = *reinterpret_cast<const cf4*>(x + 4);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f[u] = v0[u];
-      f[u + 4] = v1[u];
-    }
-  };
-#pragma unroll 2
-  for (int it = 0; it < kCC * P8 / 256; ++it) {
-    const int idx = tid + 256 * it, t = idx / P8, c = (idx - t * P8) * 8;
-    const int tc = t < n ? t : n - 1;
-    const int64_t tok = tok0 + tc, tb = tok0 + (tc + 1 < n ? tc + 1 : tc);
-    const float nb = tc + 1 < n ? 1.f : 0.f;   // B of the next token, inside the chunk only
-    float x[8], y[8], g[8];
-    ld8b(a.q + tok * DK + c, x);
-    ld8f(a.dq + tok * DK + c, y);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) g[u] = x[u] * y[u];
-    ld8b(a.k + tok * DK + c, x);
-    ld8f(a.dK + tok * DK + c, y);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) g[u] -= x[u] * y[u];
-#pragma unroll
-    for (int r = 0; r < RAB; ++r) {
-      ld8b(a.A + (tok * RAB + r) * DK + c, x);
-      ld8f(a.dA + (tok * RAB + r) * DK + c, y);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) g[u] -= x[u] * y[u];
-      ld8b(a.B + (tb * RAB + r) * DK + c, x);
-      ld8f(a.dB + (tb * RAB + r) * DK + c, y);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) g[u] += nb * x[u] * y[u];
-    }
-    if (t < n) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) gsm[t][c + u] = g[u];
-    }
+    for (int u = 0; u < 4; ++u) gsm[t][c + u] = x[u] + y[u];
   }
   // the chunk-end term rowdot(dS_end, S_end): TPC threads per channel
   {
@@ -1022,7 +1028,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcF32}, GdS{gend, kSrcF32G};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
-                   float* outa, float* outb) {
+                   float* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr) {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
@@ -1033,42 +1039,39 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb});
+                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, bf(xr), bf(rr)});
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
   if constexpr (RAB > 0) {
-    hipLaunchKernelGGL((bwc_tri_kernel<DK, RAB>), dim3(jobs), dim3(256), 0, s, BcTriArgs{p, w});
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
                    w.ry, nullptr)) != hipSuccess)
       return e;
     if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, chunk(w.at), none, GdS, chunk(w.qt), Os, none, none,
                    w.rx, nullptr)) != hipSuccess)
       return e;
-    const int64_t sw = J * 2 * (DV / 16);
-    hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(static_cast<unsigned>((sw + 3) / 4)), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(jobs), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
                        BcSolveArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
-                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA)) != hipSuccess)
+                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A)) != hipSuccess)
       return e;
     if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, Os, chunk(w.x), Sin, Vs,
-                   chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB)) != hipSuccess)
+                   chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB, q, B)) != hipSuccess)
       return e;
   } else {
     if ((e = group(std::integral_constant<int, kDk>{}, KN{}, Vs, none, GdS, Os, chunk(w.qt), none, none, dK,
-                   nullptr)) != hipSuccess)
+                   nullptr, k, nullptr)) != hipSuccess)
       return e;
     if ((e = group(std::integral_constant<int, kDq>{}, KN{}, Os, none, Sin, Vs, chunk(w.kt), none, none, dq,
-                   nullptr)) != hipSuccess)
+                   nullptr, q, nullptr)) != hipSuccess)
       return e;
   }
   if ((e = group(std::integral_constant<int, kDv>{}, KN{}, chunk(w.kt), none, GdS, chunk(w.qt), Os, chunk(w.bt),
                  chunk(w.x), dV, nullptr)) != hipSuccess)
     return e;
   hipLaunchKernelGGL((bwc_decay_kernel<DK, DV, RAB>), dim3(jobs), dim3(256), 0, s,
-                     BcDecayArgs{p, bf(q), bf(k), bf(A), bf(B), dq, dK, dA, dB, ckpt, gend, sfin, dld});
+                     BcDecayArgs{p, w.gq, w.gk, ckpt, gend, sfin, dld});
   return hipGetLastError();
 }
 
