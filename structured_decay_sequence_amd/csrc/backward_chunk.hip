@@ -92,7 +92,7 @@ __device__ __forceinline__ cb4 ltr4(const __bf16* X, int ld, int r0, int c0, int
 
 // Per-chunk buffers of the chunked backward.
 struct BcBufs {
-  float* gc;                 // [C][dk] cumulative log-decay
+  float* gc;                 // [C][dk] cumulative log-decay, base 2
   float* gam;                // [dk] e^{G} at the chunk's last token
   __bf16 *qt, *kt;           // [C][dk]
   __bf16 *at, *bt;           // [NA][dk]
@@ -145,6 +145,7 @@ struct BcPrepArgs {
 template <int DK, int RAB>
 __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
   constexpr int NP = DK / 8, NG = 256 / NP, TPG = kCC / NG;
+  constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float tot[NG][DK];
   const Problem& p = a.p;
   const int64_t job = blockIdx.x, bh = job / p.N, j = job % p.N, t0 = j * kCC;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) l[c] = 0.f;
     } else if (p.scalar) {
-      const float s = a.ld[tok];
+      const float s = a.ld[tok] * kLog2e;
 #pragma unroll
       for (int c = 0; c < 8; ++c) l[c] = s;
     } else {
@@ -171,8 +172,8 @@ __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
       const cf4 x1 = *reinterpret_cast<const cf4*>(a.ld + tok * DK + c0 + 4);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        l[c] = x0[c];
-        l[c + 4] = x1[c];
+        l[c] = x0[c] * kLog2e;
+        l[c + 4] = x1[c] * kLog2e;
       }
     }
 #pragma unroll
@@ -201,9 +202,9 @@ __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
     for (int c = 0; c < 8; ++c) {
       g[c] = G[u][c] + off[c];
       const float gp = u == 0 ? off[c] : G[u - 1][c] + off[c];   // G_{t-1}, 0 before the first token
-      eg[c] = expf(g[c]);
-      ng[c] = expf(-g[c]);
-      egp[c] = expf(gp);
+      eg[c] = __builtin_amdgcn_exp2f(g[c]);
+      ng[c] = __builtin_amdgcn_exp2f(-g[c]);
+      egp[c] = __builtin_amdgcn_exp2f(gp);
     }
     float* gcr = w.gc + (job * kCC + t) * DK + c0;
     *reinterpret_cast<cf4*>(gcr) = cf4{g[0], g[1], g[2], g[3]};
@@ -389,34 +390,18 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
 // NOUT + 4 floats) to memory, four columns per thread: scaled back from the
 // decay-scaled operands (e^{+-G} per token and channel) and signed.
 template <int KIND, int DK, int DV, int RAB, int NT>
-__device__ __forceinline__ void bc_out(const Problem& p, int64_t job, const float* ep, const BcBufs& w, float* out,
-                                       int tid) {
+__device__ __forceinline__ void bc_out(const Problem& p, int64_t job, const float* ep, float* out, int tid) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
+  static_assert(KIND == kDv, "the other gradients leave through bc_epi");
   constexpr int C4 = K::NOUT / 4, LE = K::NOUT + 4, ITEMS = K::M * C4;
   const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
   const int64_t tok0 = bh * p.T + t0;
-  const float* gc = w.gc + job * kCC * DK;
 #pragma unroll 4
   for (int it = tid; it < ITEMS; it += NT) {
-    const int row = it / C4, c = (it - row * C4) * 4;
-    const int t = row / K::RA;
+    const int t = it / C4, c = (it - t * C4) * 4;
     if (t >= n) continue;
-    cf4 v = *reinterpret_cast<const cf4*>(ep + row * LE + c);
-    if constexpr (KIND == kDq || KIND == kDk || KIND == kDa || KIND == kDb) {
-      const int tg = KIND == kDb ? (t > 0 ? t - 1 : 0) : t;
-      const cf4 g = *reinterpret_cast<const cf4*>(gc + tg * DK + c);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float f;
-        if constexpr (KIND == kDq) f = expf(g[u]);
-        else if constexpr (KIND == kDb) f = t > 0 ? expf(g[u]) : 1.f;
-        else f = expf(-g[u]);
-        v[u] *= K::SIGN * f;
-      }
-    }
-    // row-major rows of the token's rank rows: dq [T][dk], dK [T][1][dk], dV [T][1][dv], dA/dB [T][r][dk]
-    *reinterpret_cast<cf4*>(out + (tok0 * K::RA + row) * K::NOUT + c) = v;
+    *reinterpret_cast<cf4*>(out + (tok0 + t) * K::NOUT + c) = *reinterpret_cast<const cf4*>(ep + t * LE + c);
   }
 }
 
@@ -476,49 +461,96 @@ struct BcStg {
   }
 };
 
-// The decay gradient's terms of a dK or dQ product group, per (token, four
-// channels), from the products still in LDS (ep) and the raw inputs:
-//   dK group: -k dk - sum_r A dA         = -e^{-G_t} (k dKt  - sum_r A_t,r dAt_t,r)
-//   dQ group:  q dq + sum_r B_{t+1} dB_{t+1} = e^{G_t} (q dQt - sum_r B_t+1,r dBt_t+1,r)
-// (dAt, dBt as the products hold them, before their sign; dB_{t+1} is scaled
-// by e^{G_t}, and only inside the chunk).
-template <int KA_, int DK, int DV, int RAB, int NT>
-__device__ __forceinline__ void bc_decay_terms(const Problem& p, int64_t job, const float* ep, const BcBufs& w,
-                                               const __bf16* xr, const __bf16* rr, int tid) {
-  using K = BcKindCfg<KA_, DK, DV, RAB>;
-  constexpr bool KG = KA_ == kDk;   // else the dQ group
-  constexpr int LE = K::NOUT + 4, C4 = DK / 4;
-  const float* epb = ep + (K::M / 16) * 16 * LE;   // the rank-row kind's rows
-  const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
-  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
-  const int64_t tok0 = bh * p.T + t0;
-  const float* gc = w.gc + job * kCC * DK;
-  float* dst = (KG ? w.gk : w.gq) + job * kCC * DK;
-#pragma unroll 2
-  for (int it = tid; it < kCC * C4; it += NT) {
-    const int t = it / C4, c = (it - t * C4) * 4;
-    if (t >= n) continue;
-    const cf4 g = *reinterpret_cast<const cf4*>(gc + t * DK + c);
-    const cf4 pa = *reinterpret_cast<const cf4*>(ep + t * LE + c);
-    const cb4 xv = *reinterpret_cast<const cb4*>(xr + (tok0 + t) * DK + c);
-    cf4 v;
+// Epilogue of the (dK, dA) and (dQ, dB) groups (or dK, dQ alone at rank 0):
+// the products, still in LDS (ep: the first kind's kCC rows, then the rank
+// rows), become the raw operands' gradients, and the decay gradient's
+// per-(token, channel) terms are formed beside them.  An item is (token t,
+// four channels); one exp2 of the token's cumulative log-decay serves all of
+// its outputs (P = the products before their sign):
+//   dK group: f = 2^{-G_t}: dK_t = f Pk_t, dA_{t,r} = -f Pa_{t,r},
+//             term_t = -f (k_t Pk_t - sum_r A_{t,r} Pa_{t,r})
+//   dQ group: f = 2^{G_t}:  dq_t = f Pq_t, dB_{t+1,r} = -f Pb_{t+1,r} (inside
+//             the chunk; dB_{0,r} = -Pb_{0,r}),
+//             term_t = f (q_t Pq_t - sum_r B_{t+1,r} Pb_{t+1,r}).
+// The global loads (G, raw k or q, raw A or B) are issued by load() before
+// the products go through LDS, so their latency overlaps that copy.
+template <bool KG, int DK, int RAB, int NT>
+struct BcEpi {
+  static constexpr int C4 = DK / 4, LE = DK + 4, RA = RAB > 0 ? RAB : 1;
+  static constexpr int ITEMS = kCC * C4, IT = (ITEMS + NT - 1) / NT;
+  cf4 g[IT];
+  cb4 xv[IT], rv[IT][RA];
+  int n;
+  int64_t tok0;
+  __device__ __forceinline__ void load(const Problem& p, int64_t job, const BcBufs& w, const __bf16* xr,
+                                       const __bf16* rr, int tid) {
+    const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
+    n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
+    tok0 = bh * p.T + t0;
+    const float* gc = w.gc + job * kCC * DK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = (float)xv[u] * pa[u];
-    const int tr = KG ? t : t + 1;   // token of the rank rows
-    if (RAB > 0 && tr < n) {
+    for (int k = 0; k < IT; ++k) {
+      const int i0 = tid + k * NT, it = i0 < ITEMS ? i0 : ITEMS - 1;
+      const int t = it / C4, c = (it - t * C4) * 4;
+      const int tt = t < n ? t : n - 1;   // padding tokens read a live row, not kept
+      g[k] = *reinterpret_cast<const cf4*>(gc + t * DK + c);
+      xv[k] = *reinterpret_cast<const cb4*>(xr + (tok0 + tt) * DK + c);
+      if constexpr (RAB > 0) {
+        const int tr = KG ? tt : (tt + 1 < n ? tt + 1 : tt);
 #pragma unroll
-      for (int r = 0; r < (RAB > 0 ? RAB : 1); ++r) {
-        const cf4 pb = *reinterpret_cast<const cf4*>(epb + (tr * RAB + r) * LE + c);
-        const cb4 rv = *reinterpret_cast<const cb4*>(rr + ((tok0 + tr) * RAB + r) * DK + c);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] -= (float)rv[u] * pb[u];
+        for (int r = 0; r < RAB; ++r) rv[k][r] = *reinterpret_cast<const cb4*>(rr + ((tok0 + tr) * RAB + r) * DK + c);
       }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] *= KG ? -expf(-g[u]) : expf(g[u]);
-    *reinterpret_cast<cf4*>(dst + t * DK + c) = v;
   }
-}
+  __device__ __forceinline__ void finish(int64_t job, const float* ep, const BcBufs& w, float* outa, float* outb,
+                                         int tid) {
+    const float* epb = ep + kCC * LE;
+    float* dst = (KG ? w.gk : w.gq) + job * kCC * DK;
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int it = tid + k * NT;
+      const int t = it / C4, c = (it - t * C4) * 4;
+      if (it >= ITEMS || t >= n) continue;
+      cf4 f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) f[u] = __builtin_amdgcn_exp2f(KG ? -g[k][u] : g[k][u]);
+      const cf4 pa = *reinterpret_cast<const cf4*>(ep + t * LE + c);
+      cf4 o, v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o[u] = pa[u] * f[u];
+        v[u] = (float)xv[k][u] * pa[u];
+      }
+      *reinterpret_cast<cf4*>(outa + (tok0 + t) * DK + c) = o;
+      if constexpr (RAB > 0) {
+        const int tr = KG ? t : t + 1;   // token of the rank rows
+        if (tr < n) {
+#pragma unroll
+          for (int r = 0; r < RAB; ++r) {
+            const cf4 pb = *reinterpret_cast<const cf4*>(epb + (tr * RAB + r) * LE + c);
+            cf4 ob;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              v[u] -= (float)rv[k][r][u] * pb[u];
+              ob[u] = -pb[u] * f[u];
+            }
+            *reinterpret_cast<cf4*>(outb + ((tok0 + tr) * RAB + r) * DK + c) = ob;
+          }
+        }
+        if (!KG && t == 0) {
+#pragma unroll
+          for (int r = 0; r < RAB; ++r) {
+            const cf4 pb = *reinterpret_cast<const cf4*>(epb + r * LE + c);
+            *reinterpret_cast<cf4*>(outb + (tok0 * RAB + r) * DK + c) = cf4{-pb[0], -pb[1], -pb[2], -pb[3]};
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] *= KG ? -f[u] : f[u];
+      *reinterpret_cast<cf4*>(dst + t * DK + c) = v;
+    }
+  }
+};
 
 template <int KA_, int KB_>
 struct BcGroupWaves {
@@ -593,7 +625,10 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     // The gradients leave through LDS as whole rows: every wave's 16 x NOUT
     // block into the (now free) staging space, then 16-byte stores.
     constexpr int LE = K::NOUT + 4;
+    constexpr bool GRAD = KA_ == kDk || KA_ == kDq;   // the fused epilogue (else dV)
     float* ep = reinterpret_cast<float*>(smem_);
+    BcEpi<KA_ == kDk, DK, RAB, 64 * NW> epi;
+    if constexpr (GRAD) epi.load(p, job, a.w, a.xr, a.rr, tid);
     __syncthreads();   // every wave is done with the staged operands
     if (live) {
       const int lr = lane & 15, lg = lane >> 4;
@@ -603,9 +638,13 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
         for (int e = 0; e < 4; ++e) ep[(wave * 16 + 4 * lg + e) * LE + 16 * ot + lr] = acc[ot][e];
     }
     __syncthreads();
-    bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.w, a.outa, tid);
-    if constexpr (KB_ >= 0) bc_out<KB_, DK, DV, RAB, 64 * NW>(p, job, ep + WA * 16 * LE, a.w, a.outb, tid);
-    if constexpr (KA_ == kDk || KA_ == kDq) bc_decay_terms<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.w, a.xr, a.rr, tid);
+    if constexpr (GRAD) {
+      static_assert(K::M == kCC && LE == DK + 4, "fused epilogue: token rows, then rank rows, of width d_k");
+      epi.finish(job, ep, a.w, a.outa, a.outb, tid);
+    } else {
+      static_assert(KB_ < 0, "dV runs alone");
+      bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.outa, tid);
+    }
   }
 }
 
