@@ -758,7 +758,8 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
 //    two 16-row blocks into one 16x16x32 MFMA (a lone block padded with
 //    zeros), the solved blocks fed back from registers as the B operand; the
 //    diagonal inverses apply in fp32.
-// The right-hand sides' loads are issued first, so they overlap the L phase.
+// The right-hand sides' loads are issued first, so they overlap the L phase,
+// whose operands (the chunk's B~ and A~ rows) are staged in LDS.
 struct BcSolveArgs {
   Problem p;
   BcBufs w;
@@ -768,10 +769,12 @@ template <int DK, int DV, int RAB>
 struct BcSolveCfg {
   static constexpr int NA = kCC * RAB, NB = NA / 16, NT = NB * (NB + 1) / 2, NTI = NB * (NB - 1) / 2;
   static constexpr int NCT = DV / 16, NW = 2 * NCT;
+  static constexpr int LDR = DK + 16;   // staged B~ / A~ row (bf16; conflict-free 16-byte fragment reads)
   // LDS (bytes): L tiles and their transposes (bf16), the diagonal blocks, the
-  // inverses and their transposes (fp32)
+  // inverses and their transposes (fp32), the chunk's B~ and A~ rows
   static constexpr int OL = 0, OLT = OL + NTI * 512, ODG = OLT + NTI * 512, ODI = ODG + NB * 1024,
-                       ODT = ODI + NB * 1024, LDS = ODT + NB * 1024;
+                       ODT = ODI + NB * 1024, OBS = ODT + NB * 1024, OAS = OBS + NA * LDR * 2,
+                       LDS = OAS + NA * LDR * 2;
 };
 
 template <int DK, int DV, int RAB>
@@ -796,9 +799,18 @@ __global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_
   cf4 rhs[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) rhs[i] = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+  // the chunk's B~ and A~ rows into LDS: every load issued before any write
+  __bf16* bt = reinterpret_cast<__bf16*>(sm + Cf::OBS);
+  __bf16* at = reinterpret_cast<__bf16*>(sm + Cf::OAS);
+  {
+    BcStg<kSrcChunk, NA, DK, 64 * NW> sb, sa;
+    sb.load(w.bt, nullptr, job, kCC, 0, tid);
+    sa.load(w.at, nullptr, job, kCC, 0, tid);
+    sb.store(bt, Cf::LDR, tid);
+    sa.store(at, Cf::LDR, tid);
+  }
+  __syncthreads();
   // ---- L
-  const __bf16* bt = w.bt + job * NA * DK;
-  const __bf16* at = w.at + job * NA * DK;
   for (int idx = wave; idx < NT; idx += NW) {
     int i = 0, jj = idx;
     while (jj > i) {
@@ -808,8 +820,8 @@ __global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_
     cf4 P = cz4(), Q = cz4();
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
-      const cb8 bf = *reinterpret_cast<const cb8*>(bt + (16 * i + lr) * DK + 32 * ks + 8 * lg);
-      const cb8 af = *reinterpret_cast<const cb8*>(at + (16 * jj + lr) * DK + 32 * ks + 8 * lg);
+      const cb8 bf = *reinterpret_cast<const cb8*>(bt + (16 * i + lr) * Cf::LDR + 32 * ks + 8 * lg);
+      const cb8 af = *reinterpret_cast<const cb8*>(at + (16 * jj + lr) * Cf::LDR + 32 * ks + 8 * lg);
       P = mfma_b(bf, af, P);   // lane: L[16 i + 4 lg + e][16 jj + lr]
       Q = mfma_b(af, bf, Q);   // lane: L[16 i + lr][16 jj + 4 lg + e]
     }
