@@ -591,25 +591,26 @@ int64_t bw_walk_groups(const Problem& p) {
 }
 
 // Workspace: the chunk operators (and what their prepare needs), the states
-// entering the chunks, the cotangents leaving them, then the walk buffers.
-// Workspace: chunk operators, the boundary states and cotangents, then either
-// the token walks' buffers or (chunked route) the final state and the chunked
-// kernels' buffers.
+// entering the chunks, the cotangents leaving them, then either the token
+// walks' buffers or (chunked route) the chunked kernels' buffers.
 struct BwLayout {
-  size_t ops, ckpt, gend, bufs, sfin, chunk, total;
+  size_t ops, ckpt, gend, bufs, chunk, total;
 };
 BwLayout bw_layout(const Problem& p) {
   BwLayout l{};
-  const size_t states = static_cast<size_t>(p.BH * p.N) * p.dk * p.dv * sizeof(float);
+  const size_t state = static_cast<size_t>(p.dk) * p.dv;
   l.ops = 0;
-  l.ckpt = bw_align(backward_chunked(p) ? fast_workspace_bytes(p) : f32_operators_bytes(p));
-  l.gend = l.ckpt + bw_align(states);
-  l.bufs = l.gend + bw_align(states);
   if (backward_chunked(p)) {
-    l.sfin = l.bufs;
-    l.chunk = l.sfin + bw_align(static_cast<size_t>(p.BH) * p.dk * p.dv * sizeof(float));
+    // bf16 boundary states (N + 1 per head) and cotangents (N per head)
+    l.ckpt = bw_align(fast_workspace_bytes(p));
+    l.gend = l.ckpt + bw_align(static_cast<size_t>(p.BH * (p.N + 1)) * state * 2);
+    l.chunk = l.gend + bw_align(static_cast<size_t>(p.BH * p.N) * state * 2);
     l.total = l.chunk + backward_chunked_bytes(p);
   } else {
+    const size_t states = static_cast<size_t>(p.BH * p.N) * state * sizeof(float);
+    l.ckpt = bw_align(f32_operators_bytes(p));
+    l.gend = l.ckpt + bw_align(states);
+    l.bufs = l.gend + bw_align(states);
     const size_t st = static_cast<size_t>(kRB) * kCB * kBwThreads;   // floats per stored walk state
     l.total = l.bufs + static_cast<size_t>(bw_walk_groups(p)) * (p.C + 1) * st * sizeof(float);
   }
@@ -670,22 +671,21 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
   if (!backward_supported(p)) return hipErrorInvalidValue;
   const BwLayout l = bw_layout(p);
   char* ws = static_cast<char*>(workspace);
-  float* ckpt = reinterpret_cast<float*>(ws + l.ckpt);
-  float* gend = reinterpret_cast<float*>(ws + l.gend);
   if (backward_chunked(p)) {
     // Both boundary scans on bf16 MFMAs over the bf16 MFMA prepare's
-    // operators: the states entering the chunks (the forward scan), then the
-    // cotangents leaving them.
-    float* sfin = reinterpret_cast<float*>(ws + l.sfin);
+    // operators: the states entering the chunks and the final state (the
+    // forward scan), then the cotangents leaving the chunks; both in bf16.
     hipError_t e = fast_prepare(p, q, k, ld, A, B, ws + l.ops, s);
     if (e != hipSuccess) return e;
-    e = fast_scan(p, ws + l.ops, v, nullptr, sfin, S0, s, ckpt);
+    e = fast_scan(p, ws + l.ops, v, nullptr, nullptr, S0, s, ws + l.ckpt);
     if (e != hipSuccess) return e;
-    e = launch_backward_rscan(p, ws + l.ops, dout, dfinal, gend, dS0, s);
+    e = launch_backward_rscan(p, ws + l.ops, dout, dfinal, ws + l.gend, dS0, s);
     if (e != hipSuccess) return e;
-    return launch_backward_chunked(p, q, k, v, ld, A, B, dout, ckpt, gend, sfin, dq, dK, dV, dld, dA, dB,
+    return launch_backward_chunked(p, q, k, v, ld, A, B, dout, ws + l.ckpt, ws + l.gend, dq, dK, dV, dld, dA, dB,
                                    ws + l.chunk, s);
   }
+  float* ckpt = reinterpret_cast<float*>(ws + l.ckpt);
+  float* gend = reinterpret_cast<float*>(ws + l.gend);
   const float* M = nullptr;
   hipError_t e = f32_operators(p, q, k, ld, A, B, ws + l.ops, &M, s);
   if (e != hipSuccess) return e;

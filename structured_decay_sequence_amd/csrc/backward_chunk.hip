@@ -247,8 +247,9 @@ enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
 // Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
 // solve; the sequence's own rows t0 .. t0 + C - 1 (bf16 [T][cols], zero past
-// the sequence); a per-chunk fp32 boundary array; the same scaled by Gamma per row.
-enum BcSrcKind { kSrcChunk = 0, kSrcSeq = 1, kSrcF32 = 2, kSrcF32G = 3 };
+// the sequence); the bf16 boundary states (N + 1 per head: the caller names
+// the slot); the bf16 boundary cotangents, scaled by Gamma per row.
+enum BcSrcKind { kSrcChunk = 0, kSrcSeq = 1, kSrcState = 2, kSrcCotG = 3 };
 struct BcSrc {
   const void* ptr;
   int kind;
@@ -271,7 +272,7 @@ struct BcKindCfg {
   // with the transposing LDS read
   static constexpr bool W0T = KIND == kDq || KIND == kDk || KIND == kDa || KIND == kDb;
   // where the shared operands live (see BcSrcKind)
-  static constexpr int SW0 = (KIND == kRhsY || KIND == kDq || KIND == kDb) ? kSrcF32 : kSrcF32G;
+  static constexpr int SW0 = (KIND == kRhsY || KIND == kDq || KIND == kDb) ? kSrcState : kSrcCotG;
   static constexpr int SB1 = (KIND == kDq || KIND == kDb || KIND == kDk || KIND == kDa) ? kSrcSeq : kSrcChunk;
   static constexpr int SC1 = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? kSrcSeq : kSrcChunk;
 };
@@ -299,7 +300,7 @@ struct BcGroupArgs {
   BcBufs w;
   float *outa, *outb;           // right-hand sides (tile order) or gradients
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
-  const float *ckpt, *sfin;     // dK group: the states leaving the chunks (the chunk-end term)
+  const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
   float* dld;                   // dQ group: the log-decay gradient
 };
 
@@ -408,32 +409,29 @@ __device__ __forceinline__ void bc_out(const Problem& p, int64_t job, const floa
   }
 }
 
-// One operand's staging: ROWS x COLS from source kind SRC, in pieces of eight
-// elements, IT per thread (NT threads).
+// One operand's staging: ROWS x COLS bf16 from source kind SRC, in pieces of
+// eight elements, IT per thread (NT threads).  slot: the chunk's index in a
+// per-chunk source (for the boundary states, the caller's slot).
 template <int SRC, int ROWS, int COLS, int NT>
 struct BcStg {
   static constexpr int P = ROWS * COLS / 8, IT = (P + NT - 1) / NT, PR = COLS / 8;
-  static constexpr bool F32 = SRC == kSrcF32 || SRC == kSrcF32G;
-  cf4 x0[IT], x1[F32 ? IT : 1];
-  float gs[SRC == kSrcF32G ? IT : 1];
+  cb8 x[IT];
+  float gs[SRC == kSrcCotG ? IT : 1];
   int n_ = 0;
-  __device__ __forceinline__ void load(const void* ptr, const float* gam, int64_t job, int n, int64_t tok0, int tid) {
+  __device__ __forceinline__ void load(const void* ptr, const float* gam, int64_t slot, int n, int64_t tok0, int tid) {
     n_ = n;
+    const __bf16* src = static_cast<const __bf16*>(ptr);
 #pragma unroll
     for (int k = 0; k < IT; ++k) {
       const int i0 = tid + k * NT, i = i0 < P ? i0 : P - 1;   // the last piece again, not stored
       const int r = i / PR, c8 = (i - r * PR) * 8;
-      if constexpr (F32) {
-        const float* f = static_cast<const float*>(ptr) + (job * ROWS + r) * COLS + c8;
-        x0[k] = *reinterpret_cast<const cf4*>(f);
-        x1[k] = *reinterpret_cast<const cf4*>(f + 4);
-        if constexpr (SRC == kSrcF32G) gs[k] = gam[r];
-      } else if constexpr (SRC == kSrcSeq) {
+      if constexpr (SRC == kSrcSeq) {
         // rows past the sequence read its last row and are zeroed at the store
         const int rr = r < n ? r : n - 1;
-        x0[k] = *reinterpret_cast<const cf4*>(static_cast<const __bf16*>(ptr) + (tok0 + rr) * COLS + c8);
+        x[k] = *reinterpret_cast<const cb8*>(src + (tok0 + rr) * COLS + c8);
       } else {
-        x0[k] = *reinterpret_cast<const cf4*>(static_cast<const __bf16*>(ptr) + (job * ROWS + r) * COLS + c8);
+        x[k] = *reinterpret_cast<const cb8*>(src + (slot * ROWS + r) * COLS + c8);
+        if constexpr (SRC == kSrcCotG) gs[k] = gam[r];
       }
     }
   }
@@ -443,17 +441,12 @@ struct BcStg {
       const int i = tid + k * NT;
       if (i < P) {
         const int r = i / PR, c8 = (i - r * PR) * 8;
-        cb8 v;
-        if constexpr (F32) {
-          const float g = SRC == kSrcF32G ? gs[k] : 1.f;
+        cb8 v = x[k];
+        if constexpr (SRC == kSrcCotG) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            v[u] = (__bf16)(g * x0[k][u]);
-            v[u + 4] = (__bf16)(g * x1[k][u]);
-          }
-        } else {
-          v = __builtin_bit_cast(cb8, x0[k]);
-          if (SRC == kSrcSeq && r >= n_) {
+          for (int u = 0; u < 8; ++u) v[u] = (__bf16)(gs[k] * (float)x[k][u]);
+        } else if constexpr (SRC == kSrcSeq) {
+          if (r >= n_) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = (__bf16)0.f;
           }
@@ -660,13 +653,12 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   BcStg<K::SC1, kCC, K::NOUT, 64 * NW> s2;
   BcStg<kSrcChunk, (K::TERM2 ? K::NA : 16), K::KA, 64 * NW> s3;
   BcStg<kSrcChunk, (K::TERM2 ? K::NA : 16), K::NOUT, 64 * NW> s4;
-  s0.load(a.W0.ptr, a.w.gam + job * DK, job, n, tok0, tid);
+  // the boundary states have N + 1 slots per head: the state entering chunk
+  // jc is slot jc, the one leaving it slot jc + 1
+  s0.load(a.W0.ptr, a.w.gam + job * DK, K::SW0 == kSrcState ? job + bh : job, n, tok0, tid);
   // dK group: the state leaving the chunk, for the chunk-end term of the decay gradient
-  BcStg<kSrcF32, L::W0R, L::W0C, 64 * NW> se;
-  if constexpr (KA_ == kDk) {
-    const bool last = jc + 1 == p.N;
-    se.load(last ? a.sfin : a.ckpt, nullptr, last ? bh : job + 1, n, tok0, tid);
-  }
+  BcStg<kSrcState, L::W0R, L::W0C, 64 * NW> se;
+  if constexpr (KA_ == kDk) se.load(a.ckpt, nullptr, job + bh + 1, n, tok0, tid);
   s1.load(a.B1.ptr, nullptr, job, n, tok0, tid);
   s2.load(a.C1.ptr, nullptr, job, n, tok0, tid);
   if constexpr (K::TERM2) {
@@ -684,14 +676,14 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     // rowdot(dS_end, S_end) per state channel: the raw dS_end pieces staged
     // as W0 (before their Gamma scaling) against S_end, summed over the
     // PR threads of a row
-    static_assert(L::W0R == DK && L::W0C == DV && K::SW0 == kSrcF32G, "dK group: W0 is dS_end [d_k][d_v]");
+    static_assert(L::W0R == DK && L::W0C == DV && K::SW0 == kSrcCotG, "dK group: W0 is dS_end [d_k][d_v]");
     constexpr int PR = DV / 8, P = DK * DV / 8;
 #pragma unroll
     for (int k = 0; k < decltype(s0)::IT; ++k) {
       const int i = tid + k * 64 * NW;
       float d = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) d += s0.x0[k][u] * se.x0[k][u] + s0.x1[k][u] * se.x1[k][u];
+      for (int u = 0; u < 8; ++u) d += (float)s0.x[k][u] * (float)se.x[k][u];
 #pragma unroll
       for (int sh = 1; sh < PR; sh *= 2) d += __shfl_xor(d, sh, 64);
       if (i < P && i % PR == 0) a.w.ends[job * DK + i / PR] = d;
@@ -930,7 +922,7 @@ struct RsArgs {
   const __bf16* M;
   const __bf16* dout;
   const float* dfinal;
-  float* gend;   // [BH, N, dk, dv]: the cotangent of the state leaving each chunk
+  __bf16* gend;  // [BH, N, dk, dv]: the cotangent of the state leaving each chunk, bf16 (as the scan's products read it)
   float* dS0;    // [BH, dk, dv]
 };
 
@@ -956,7 +948,7 @@ __global__ __launch_bounds__(256) void bw_rscan_kernel(RsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Mbh = a.M + static_cast<size_t>(bh) * N * Cf::MSZ;
-  float* gbh = a.gend + static_cast<size_t>(bh) * N * DK * dv;
+  __bf16* gbh = a.gend + static_cast<size_t>(bh) * N * DK * dv;
 
   cb8 fr[FPW];
   cb8 dpc[2];
@@ -1021,9 +1013,9 @@ __global__ __launch_bounds__(256) void bw_rscan_kernel(RsArgs a) {
   // the cotangent leaving the last chunk: dfinal (or zero)
   for (int it = tid; it < DK * BV; it += 256) {
     const int i = it / BV, c = it % BV;
-    const float g = a.dfinal ? a.dfinal[(bh * DK + i) * dv + c0 + c] : 0.f;
+    const __bf16 g = (__bf16)(a.dfinal ? a.dfinal[(bh * DK + i) * dv + c0 + c] : 0.f);
     gbh[(static_cast<size_t>(N - 1) * DK + i) * dv + c0 + c] = g;
-    Xb[c * LDX + rs_kperm(i)] = (__bf16)g;
+    Xb[c * LDX + rs_kperm(i)] = g;
   }
   load_ops(N - 1);
   put_ops(Tb);
@@ -1059,17 +1051,26 @@ __global__ __launch_bounds__(256) void bw_rscan_kernel(RsArgs a) {
         for (int ct = 0; ct < CTN; ++ct) acc[rr][ct] = mfma_b(af, bx[ct], acc[rr][ct]);
       }
     }
-    // lane holds rows 16 kt + 4 lg + e (state channels), column 16 ct + lr
-    float* dst = j > 0 ? gbh + static_cast<size_t>(j - 1) * DK * dv : a.dS0 + static_cast<size_t>(bh) * DK * dv;
+    // lane holds rows 16 kt + 4 lg + e (state channels), column 16 ct + lr;
+    // the cotangents leaving chunks in bf16 (as the next product reads them),
+    // dS0 in fp32
+    __bf16* dst = gbh + static_cast<size_t>(j > 0 ? j - 1 : 0) * DK * dv;
+    float* d0 = a.dS0 + static_cast<size_t>(bh) * DK * dv;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
       const int kt = wave + 4 * rr;
 #pragma unroll
       for (int ct = 0; ct < CTN; ++ct) {
         const int c = 16 * ct + lr;
+        const cb4 h = to_b4(acc[rr][ct]);
+        if (j > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(16 * kt + 4 * lg + e) * dv + c0 + c] = acc[rr][ct][e];
-        *reinterpret_cast<cb4*>(Xn + c * LDX + rs_kperm(16 * kt + 4 * lg)) = to_b4(acc[rr][ct]);
+          for (int e = 0; e < 4; ++e) dst[(16 * kt + 4 * lg + e) * dv + c0 + c] = h[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d0[(16 * kt + 4 * lg + e) * dv + c0 + c] = acc[rr][ct][e];
+        }
+        *reinterpret_cast<cb4*>(Xn + c * LDX + rs_kperm(16 * kt + 4 * lg)) = h;
       }
     }
     put_ops(Tn);
@@ -1079,7 +1080,7 @@ __global__ __launch_bounds__(256) void bw_rscan_kernel(RsArgs a) {
 }
 
 template <int DK, int BV>
-hipError_t launch_rscan_t(const Problem& p, const void* M, const void* dout, const float* dfinal, float* gend,
+hipError_t launch_rscan_t(const Problem& p, const void* M, const void* dout, const float* dfinal, void* gend,
                           float* dS0, hipStream_t s) {
   using Cf = RsCfg<DK, BV>;
   const void* fn = reinterpret_cast<const void*>(bw_rscan_kernel<DK, BV>);
@@ -1087,15 +1088,15 @@ hipError_t launch_rscan_t(const Problem& p, const void* M, const void* dout, con
   if (e != hipSuccess) return e;
   const int64_t groups = (p.BH + 7) / 8;
   hipLaunchKernelGGL((bw_rscan_kernel<DK, BV>), dim3(static_cast<unsigned>(groups * 8 * (p.dv / BV))), dim3(256),
-                     Cf::LDS, s, RsArgs{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(dout), dfinal, gend, dS0});
+                     Cf::LDS, s, RsArgs{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(dout), dfinal, static_cast<__bf16*>(gend), dS0});
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int RAB>
 hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const void* k, const void* v,
-                       const float* ld, const void* A, const void* B, const void* dout, const float* ckpt,
-                       const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld, float* dA,
+                       const float* ld, const void* A, const void* B, const void* dout, const void* ckpt,
+                       const void* gend, float* dq, float* dK, float* dV, float* dld, float* dA,
                        float* dB, hipStream_t s) {
   const int64_t J = p.BH * p.N;
   const unsigned jobs = static_cast<unsigned>(J);
@@ -1106,7 +1107,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   if (e != hipSuccess) return e;
   const BcSrc none{nullptr, kSrcChunk};
   auto chunk = [](const void* x) { return BcSrc{x, kSrcChunk}; };
-  const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcF32}, GdS{gend, kSrcF32G};
+  const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcState}, GdS{gend, kSrcCotG};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
                    float* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr) -> hipError_t {
@@ -1122,7 +1123,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, bf(xr), bf(rr), ckpt, sfin, dld});
+                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, bf(xr), bf(rr), bf(ckpt), dld});
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
@@ -1165,7 +1166,7 @@ bool backward_chunked(const Problem& p) {
 
 size_t backward_chunked_bytes(const Problem& p) { return bc_layout(p, nullptr, nullptr); }
 
-hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, float* gend,
+hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, void* gend,
                                  float* dS0, hipStream_t s) {
   if (p.BH * p.N == 0) return hipSuccess;
   if (!backward_chunked(p)) return hipErrorInvalidValue;
@@ -1179,8 +1180,8 @@ hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* do
 }
 
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
-                                   const void* A, const void* B, const void* dout, const float* ckpt,
-                                   const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld,
+                                   const void* A, const void* B, const void* dout, const void* ckpt,
+                                   const void* gend, float* dq, float* dK, float* dV, float* dld,
                                    float* dA, float* dB, void* ws, hipStream_t s) {
   if (p.BH * p.N == 0) return hipSuccess;
   if (!backward_chunked(p)) return hipErrorInvalidValue;
@@ -1188,7 +1189,7 @@ hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* 
   bc_layout(p, static_cast<char*>(ws), &w);
 #define LATTN_BC(DK_, DV_, RAB_)                                                                                  \
   if (p.dk == DK_ && p.dv == DV_ && p.r_ab == RAB_)                                                              \
-    return launch_bc_t<DK_, DV_, RAB_>(p, w, q, k, v, ld, A, B, dout, ckpt, gend, sfin, dq, dK, dV, dld, dA, dB, s);
+    return launch_bc_t<DK_, DV_, RAB_>(p, w, q, k, v, ld, A, B, dout, ckpt, gend, dq, dK, dV, dld, dA, dB, s);
   LATTN_BC(128, 128, 2) LATTN_BC(128, 128, 1) LATTN_BC(128, 128, 0)
   LATTN_BC(64, 64, 2) LATTN_BC(64, 64, 1) LATTN_BC(64, 64, 0)
   LATTN_BC(128, 64, 2) LATTN_BC(128, 64, 1) LATTN_BC(128, 64, 0)

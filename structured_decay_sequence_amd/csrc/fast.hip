@@ -769,7 +769,7 @@ struct FastScanArgs {
   __bf16* out;         // output rows (the forward instance)
   float* Sfin;
   const float* S0;
-  float* ckpt;         // [BH, N, dk, dv]: the state entering every chunk, fp32 (the boundary instance)
+  __bf16* ckpt;        // [BH, N + 1, dk, dv]: the state entering every chunk, then the final state (the boundary instance)
 };
 
 // CK: the boundary-state instance, which stores the state entering every
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     const int i = it / BV, c = it % BV;
     const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
     X0[c * LDX + kperm(i)] = (__bf16)s;
-    if (CK) a.ckpt[(static_cast<size_t>(bh * N) * DK + i) * dv + c0 + c] = s;
+    if (CK) a.ckpt[(static_cast<size_t>(bh * (N + 1)) * DK + i) * dv + c0 + c] = (__bf16)s;
   }
   put_v(X0, vb[0], 0);
   // Ring invariant from here on: at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
@@ -925,9 +925,10 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
         }
       }
     }
-    if (CK && jj + 1 < N) {
-      // the state entering chunk jj + 1: this product's state rows, in fp32
-      float* ck = a.ckpt + static_cast<size_t>(bh * N + jj + 1) * DK * dv;
+    if (CK && jj < N) {
+      // the state entering chunk jj + 1 (the final state after the last
+      // chunk): this product's state rows, rounded as the next product reads them
+      __bf16* ck = a.ckpt + static_cast<size_t>(bh * (N + 1) + jj + 1) * DK * dv;
 #pragma unroll
       for (int q = 0; q < MPW; ++q) {
         const int mt = wave * MPW + q;
@@ -935,8 +936,9 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
 #pragma unroll
           for (int nt = 0; nt < NTN; ++nt) {
             const int i0 = mt * 16 + 4 * lg, c = nt * 16 + lr;
+            const bf16x4 h = to_bf16x4(acc[q][nt]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ck[(i0 + e) * dv + c0 + c] = acc[q][nt][e];
+            for (int e = 0; e < 4; ++e) ck[(i0 + e) * dv + c0 + c] = h[e];
           }
         }
       }
@@ -1135,10 +1137,10 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
 
 template <int DK, int BV, int NWV, int PD, bool CK = false>
 hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out, float* Sfin,
-                       const float* S0, float* ckpt, hipStream_t s) {
+                       const float* S0, void* ckpt, hipStream_t s) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
   FastScanArgs a{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(v),
-                 static_cast<__bf16*>(out), Sfin, S0, ckpt};
+                 static_cast<__bf16*>(out), Sfin, S0, static_cast<__bf16*>(ckpt)};
   const int nvt = p.dv / BV;
   const int64_t groups = (p.BH + 7) / 8;
   const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD, CK>);
@@ -1188,7 +1190,7 @@ hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const
 }
 
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
-                     const float* S0, hipStream_t s, float* ckpt) {
+                     const float* S0, hipStream_t s, void* ckpt) {
   if (p.BH == 0) return hipSuccess;
   if (ckpt) {
     // the boundary-state instance: states instead of output rows

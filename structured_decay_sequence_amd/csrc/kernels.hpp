@@ -44,14 +44,15 @@ hipError_t general_summaries(const Problem& p, const void* workspace, const void
 
 // bf16 MFMA path: bf16 storage, C = 64, r_kv = 1, r_ab in {0, 1, 2}, d_k in {64, 128},
 // d_v a multiple of 64.  The workspace holds the fragment-ordered chunk operators.
-// fast_scan: with ckpt given, the state entering every chunk [BH, N, dk, dv]
-// goes there in fp32 and no output rows are written (out is ignored).
+// fast_scan: with ckpt given, the state entering every chunk and the final
+// state, [BH, N + 1, dk, dv], go there in bf16 (the values the scan's own
+// products read) and no output rows are written (out is ignored).
 bool fast_supported(const Problem& p);
 size_t fast_workspace_bytes(const Problem& p);
 hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const float* ld,
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
-                     const float* S0, hipStream_t s, float* ckpt = nullptr);
+                     const float* S0, hipStream_t s, void* ckpt = nullptr);
 // Gating-chunk summaries for the query-conditioned composition, from the bf16
 // prepare's operators of the 64-token problem p: per gating chunk of G
 // consecutive chunks (G <= 4), Acal^T [dk][dk] and B^T [dv][dk] in bf16, the
@@ -104,20 +105,21 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
                             hipStream_t s);
 
 // Chunked backward on bf16 MFMAs (bf16 storage, C = 64, r_kv = 1, r_ab <= 2,
-// d_k, d_v in {64, 128}), from the chunk-boundary states ckpt, cotangents gend
-// and the final state sfin; writes every gradient but dS0 (which the reverse
-// boundary scan gives).  ws: backward_chunked_bytes(p) bytes.
+// d_k, d_v in {64, 128}), from the chunk-boundary states ckpt (bf16 [BH, N + 1,
+// dk, dv], fast_scan's boundary instance) and cotangents gend (bf16 [BH, N, dk,
+// dv]); writes every gradient but dS0 (which the reverse boundary scan gives).
+// ws: backward_chunked_bytes(p) bytes.
 bool backward_chunked(const Problem& p);
 size_t backward_chunked_bytes(const Problem& p);
 // The cotangent boundary scan of that route on bf16 MFMAs, over the bf16 MFMA
-// prepare's operators M: gend[j] (the cotangent leaving chunk j) for every
-// chunk, and dS0.
-hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, float* gend,
+// prepare's operators M: gend[j] (the cotangent leaving chunk j, bf16) for
+// every chunk, and dS0 (fp32).
+hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, void* gend,
                                  float* dS0, hipStream_t s);
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
-                                   const void* A, const void* B, const void* dout, const float* ckpt,
-                                   const float* gend, const float* sfin, float* dq, float* dK, float* dV, float* dld,
-                                   float* dA, float* dB, void* ws, hipStream_t s);
+                                   const void* A, const void* B, const void* dout, const void* ckpt,
+                                   const void* gend, float* dq, float* dK, float* dV, float* dld, float* dA,
+                                   float* dB, void* ws, hipStream_t s);
 
 // Backward pass, token-serial with chunk checkpoints: d_k, d_v <= 128,
 // r_ab <= 4, r_kv <= 2; gradients in fp32.
