@@ -675,7 +675,8 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
     // Both boundary scans on bf16 MFMAs over the bf16 MFMA prepare's
     // operators: the states entering the chunks and the final state (the
     // forward scan), then the cotangents leaving the chunks; both in bf16.
-    hipError_t e = fast_prepare(p, q, k, ld, A, B, ws + l.ops, s);
+    // the prepare also leaves the decay-scaled operands for the chunked kernels
+    hipError_t e = fast_prepare_bw(p, q, k, ld, A, B, ws + l.ops, backward_chunked_prep_out(p, ws + l.chunk), s);
     if (e != hipSuccess) return e;
     e = fast_scan(p, ws + l.ops, v, nullptr, nullptr, S0, s, ws + l.ckpt);
     if (e != hipSuccess) return e;

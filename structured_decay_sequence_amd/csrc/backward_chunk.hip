@@ -133,18 +133,20 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: G and the scaled operands.  Thread (token group tg, 8-channel piece
-// pc) owns TPG consecutive tokens of 8 channels: a prefix over its tokens,
-// then over the token groups through LDS, then 16-byte loads and stores.
-struct BcPrepArgs {
+// G: the chunk-local cumulative log-decay in base 2 (the epilogues' decay
+// factors) and e^{G} at the chunk's last token (Gamma, which scales the
+// boundary cotangents).  Thread (token group tg, 8-channel piece pc) owns TPG
+// consecutive tokens of 8 channels: a prefix over its tokens, then over the
+// token groups through LDS.  (The decay-scaled operands come from the
+// prepare kernel, which forms them anyway.)
+struct BcGArgs {
   Problem p;
-  const __bf16 *q, *k, *A, *B;
   const float* ld;
   BcBufs w;
 };
 
-template <int DK, int RAB>
-__global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
+template <int DK>
+__global__ __launch_bounds__(256) void bwc_g_kernel(BcGArgs a) {
   constexpr int NP = DK / 8, NG = 256 / NP, TPG = kCC / NG;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float tot[NG][DK];
@@ -196,43 +198,16 @@ __global__ __launch_bounds__(256) void bwc_prep_kernel(BcPrepArgs a) {
 #pragma unroll
   for (int u = 0; u < TPG; ++u) {
     const int t = tg * TPG + u;
-    const bool ok = t < n;
-    const int64_t tok = tok0 + (ok ? t : 0);
-    float g[8], eg[8], ng[8], egp[8];
+    float g[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      g[c] = G[u][c] + off[c];
-      const float gp = u == 0 ? off[c] : G[u - 1][c] + off[c];   // G_{t-1}, 0 before the first token
-      eg[c] = __builtin_amdgcn_exp2f(g[c]);
-      ng[c] = __builtin_amdgcn_exp2f(-g[c]);
-      egp[c] = __builtin_amdgcn_exp2f(gp);
-    }
+    for (int c = 0; c < 8; ++c) g[c] = G[u][c] + off[c];
     float* gcr = w.gc + (job * kCC + t) * DK + c0;
     *reinterpret_cast<cf4*>(gcr) = cf4{g[0], g[1], g[2], g[3]};
     *reinterpret_cast<cf4*>(gcr + 4) = cf4{g[4], g[5], g[6], g[7]};
     if (t == kCC - 1) {
       // padding tokens add nothing: this is G at the chunk's last token
 #pragma unroll
-      for (int c = 0; c < 8; ++c) w.gam[job * DK + c0 + c] = eg[c];
-    }
-    auto scaled = [&](const __bf16* src, const float (&f)[8], __bf16* dst) {
-      cb8 o;
-      if (ok) {
-        const cb8 x = *reinterpret_cast<const cb8*>(src);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = (__bf16)((float)x[c] * f[c]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = (__bf16)0.f;
-      }
-      *reinterpret_cast<cb8*>(dst) = o;
-    };
-    scaled(a.q + tok * DK + c0, eg, w.qt + (job * kCC + t) * DK + c0);
-    scaled(a.k + tok * DK + c0, ng, w.kt + (job * kCC + t) * DK + c0);
-#pragma unroll
-    for (int r = 0; r < RAB; ++r) {
-      scaled(a.A + (tok * RAB + r) * DK + c0, ng, w.at + ((job * kCC + t) * RAB + r) * DK + c0);
-      scaled(a.B + (tok * RAB + r) * DK + c0, egp, w.bt + ((job * kCC + t) * RAB + r) * DK + c0);
+      for (int c = 0; c < 8; ++c) w.gam[job * DK + c0 + c] = __builtin_amdgcn_exp2f(g[c]);
     }
   }
 }
@@ -1101,8 +1076,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const int64_t J = p.BH * p.N;
   const unsigned jobs = static_cast<unsigned>(J);
   auto bf = [](const void* x) { return static_cast<const __bf16*>(x); };
-  hipLaunchKernelGGL((bwc_prep_kernel<DK, RAB>), dim3(jobs), dim3(256), 0, s,
-                     BcPrepArgs{p, bf(q), bf(k), bf(A), bf(B), ld, w});
+  hipLaunchKernelGGL((bwc_g_kernel<DK>), dim3(jobs), dim3(256), 0, s, BcGArgs{p, ld, w});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const BcSrc none{nullptr, kSrcChunk};
@@ -1165,6 +1139,12 @@ bool backward_chunked(const Problem& p) {
 }
 
 size_t backward_chunked_bytes(const Problem& p) { return bc_layout(p, nullptr, nullptr); }
+
+PrepBwOut backward_chunked_prep_out(const Problem& p, void* ws) {
+  BcBufs w;
+  bc_layout(p, static_cast<char*>(ws), &w);
+  return PrepBwOut{w.qt, w.kt, w.at, w.bt};
+}
 
 hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, void* gend,
                                  float* dS0, hipStream_t s) {

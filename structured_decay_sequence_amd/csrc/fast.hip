@@ -124,8 +124,10 @@ __device__ __forceinline__ bf16x4 xtr4(const __bf16* X, int r0, int c0, int lane
 //    them, then invert.
 //  * solve and operator: wave w < KT owns the 16-column input tile w.
 // Operand source of the prepare kernel: the decay operands A, B given
-// (generic), or formed on the fly from a family's raw parameters.
-enum PrepMode { kGeneric = 0, kHdla = 1, kGdn = 2 };
+// (generic), or formed on the fly from a family's raw parameters.  kGenericBw:
+// generic, and the decay-scaled operands also go to memory for the chunked
+// backward.
+enum PrepMode { kGeneric = 0, kHdla = 1, kGdn = 2, kGenericBw = 3 };
 
 template <int DK, int RAB, bool SCAL, int MODE>
 struct PrepCfg {
@@ -163,7 +165,8 @@ struct PrepCfg {
   static constexpr int R_EG = DK * 4;
   static constexpr int DIB = 260;                // floats per inverse block (padded)
   static constexpr int R_DI = NB * DIB * 4;
-  static constexpr int R_BT = MODE == kGeneric ? 0 : kC * 4;   // beta per token
+  static constexpr bool GEN = MODE == kGeneric || MODE == kGenericBw;   // A, B given
+  static constexpr int R_BT = GEN ? 0 : kC * 4;   // beta per token
   // d_k = 64 runs two resident workgroups per compute unit, so one chunk's
   // VALU scaling overlaps the other's MFMA phases.  To fit two in LDS it keeps
   // a compact layout: the diagonal blocks are inverted in place, and M_A is
@@ -183,7 +186,7 @@ struct PrepCfg {
   static_assert(!COMPACT || R_MA <= R_LP + R_LD + NA * XRow<DK>::LD * 2,
                 "compact layout: M_A fits the region of L and B~");
   static_assert(!COMPACT || DIB == LDB, "compact layout: inverses overwrite the diagonal blocks");
-  static_assert(MODE == kGeneric || (MODE == kHdla && RAB == 2 && !SCAL) || (MODE == kGdn && RAB == 1 && SCAL),
+  static_assert(GEN || (MODE == kHdla && RAB == 2 && !SCAL) || (MODE == kGdn && RAB == 1 && SCAL),
                 "fused modes: HDLA is rank 2 per channel, Gated DeltaNet rank 1 scalar");
   static_assert(NO == NW && KT <= NW, "wave roles: one wave per channel piece");
   static_assert(!OVERLAP || (NB % 4 == 0 && NWORK > 0), "overlapped Gram phase: four diagonal blocks per inverting wave");
@@ -198,6 +201,8 @@ struct FastPrepArgs {
   const __bf16* B;
   const float* beta;   // fused modes: per-token beta [BH, T]
   __bf16* M;   // fragment-ordered chunk operators
+  // kGenericBw: per chunk-head, Q~, K~ [C][dk] and A~, B~ [C r_ab][dk] (bf16)
+  __bf16 *qt, *kt, *at, *bt;
 };
 
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& raw, const float (&f)[8]) {
@@ -268,7 +273,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
     int64_t tok;
     int c0;
     load_tok(jb, ln, tok, c0);
-    if (MODE == kGeneric) {
+    if (Cfg::GEN) {
 #pragma unroll
       for (int r = 0; r < RAB; ++r) {
         av[r] = *reinterpret_cast<const bf16x8*>(a.A + (tok * RAB + r) * DK + c0);
@@ -359,13 +364,29 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
 #pragma unroll
         for (int c = 0; c < 8; ++c) eGC[pc * 8 + c] = __builtin_amdgcn_exp2f(g2[SCAL ? 0 : c]);
       }
-      *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(NA + t, pc)) = scale8(qv, fp);
-      *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(NA + t, pc)) = scale8(kv, fn);
-      if (MODE == kGeneric) {
+      const bf16x8 sq = scale8(qv, fp), sk = scale8(kv, fn);
+      *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(NA + t, pc)) = sq;
+      *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(NA + t, pc)) = sk;
+      if constexpr (MODE == kGenericBw) {
+        // the chunked backward's copies: row t of the chunk, channels pc*8 ..
+        // (chunk bases wave-uniform, lane offsets 32-bit)
+        const size_t cb = static_cast<size_t>(job) * (kC * DK);
+        const int lo = t * DK + pc * 8;
+        *reinterpret_cast<bf16x8*>(a.qt + cb + lo) = sq;
+        *reinterpret_cast<bf16x8*>(a.kt + cb + lo) = sk;
+      }
+      if (Cfg::GEN) {
 #pragma unroll
         for (int r = 0; r < RAB; ++r) {
-          *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(RAB * t + r, pc)) = scale8(av[r], fn);
-          *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(RAB * t + r, pc)) = scale8(bv[r], fx);
+          const bf16x8 sa = scale8(av[r], fn), sb = scale8(bv[r], fx);
+          *reinterpret_cast<bf16x8*>(Xr + xoff<DK>(RAB * t + r, pc)) = sa;
+          *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(RAB * t + r, pc)) = sb;
+          if constexpr (MODE == kGenericBw) {
+            const size_t cb = static_cast<size_t>(job) * (kC * RAB * DK);
+            const int lo = (t * RAB + r) * DK + pc * 8;
+            *reinterpret_cast<bf16x8*>(a.at + cb + lo) = sa;
+            *reinterpret_cast<bf16x8*>(a.bt + cb + lo) = sb;
+          }
         }
       } else {
         // Decay operands from the raw parameters.  With lambda = exp(l) and
@@ -652,7 +673,7 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       //      acc = sum_s WX[s][k] Bmat[m][s],  Bmat = [A~^T ; M_A].
       // Fused modes: the value columns (chunk tokens) carry beta of their token.
       f32x4 vsc = f32x4{1.f, 1.f, 1.f, 1.f};
-      if (MODE != kGeneric && kt >= DK / 16) vsc = *reinterpret_cast<const f32x4*>(betas + (kt - DK / 16) * 16 + 4 * lg);
+      if (!Cfg::GEN && kt >= DK / 16) vsc = *reinterpret_cast<const f32x4*>(betas + (kt - DK / 16) * 16 + 4 * lg);
       auto store = [&](int mt, const f32x4& v) {
         const f32x4 w = f32x4{v[0] * vsc[0], v[1] * vsc[1], v[2] * vsc[2], v[3] * vsc[3]};
         *reinterpret_cast<bf16x4*>(Mout + ((mt * (KT / 2) + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4) = to_bf16x4(w);
@@ -1103,10 +1124,19 @@ __global__ __launch_bounds__(GateCfg<DK>::NT) void fast_gate_kernel(FastGateArgs
 
 template <int DK, int RAB, bool SCAL, int MODE>
 hipError_t launch_prep(const Problem& p, const void* q, const void* k, const float* ld,
-                       const void* A, const void* B, const float* beta, void* M, hipStream_t s) {
+                       const void* A, const void* B, const float* beta, void* M, hipStream_t s,
+                       const PrepBwOut* bw = nullptr) {
   using Cfg = PrepCfg<DK, RAB, SCAL, MODE>;
   FastPrepArgs a{p, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ld,
-                 static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), beta, static_cast<__bf16*>(M)};
+                 static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), beta, static_cast<__bf16*>(M),
+                 nullptr, nullptr, nullptr, nullptr};
+  if (MODE == kGenericBw) {
+    if (!bw) return hipErrorInvalidValue;
+    a.qt = static_cast<__bf16*>(bw->qt);
+    a.kt = static_cast<__bf16*>(bw->kt);
+    a.at = static_cast<__bf16*>(bw->at);
+    a.bt = static_cast<__bf16*>(bw->bt);
+  }
   const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB, SCAL, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
   if (e != hipSuccess) return e;
@@ -1161,6 +1191,19 @@ bool fast_supported(const Problem& p) {
 size_t fast_workspace_bytes(const Problem& p) {
   const size_t tiles = static_cast<size_t>((p.dk + kC) / 16) * ((p.dk + kNK) / 16);
   return static_cast<size_t>(p.BH * p.N) * tiles * 512;
+}
+
+hipError_t fast_prepare_bw(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
+                           const void* B, void* workspace, const PrepBwOut& out, hipStream_t s) {
+  if (p.BH * p.N == 0) return hipSuccess;
+  if (!fast_supported(p)) return hipErrorInvalidValue;
+#define LATTN_PBW(DK_, RAB_)                                                                                      \
+  if (p.dk == DK_ && p.r_ab == RAB_)                                                                             \
+    return p.scalar ? launch_prep<DK_, RAB_, true, kGenericBw>(p, q, k, ld, A, B, nullptr, workspace, s, &out)   \
+                    : launch_prep<DK_, RAB_, false, kGenericBw>(p, q, k, ld, A, B, nullptr, workspace, s, &out);
+  LATTN_PBW(128, 2) LATTN_PBW(128, 1) LATTN_PBW(128, 0) LATTN_PBW(64, 2) LATTN_PBW(64, 1) LATTN_PBW(64, 0)
+#undef LATTN_PBW
+  return hipErrorInvalidValue;
 }
 
 hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const float* ld,

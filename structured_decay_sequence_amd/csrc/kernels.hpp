@@ -53,6 +53,15 @@ hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const fl
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s, void* ckpt = nullptr);
+// fast_prepare, which also writes the decay-scaled operands it forms, per
+// chunk-head: Q~ = q e^{G_t}, K~ = k e^{-G_t} [C][dk], A~ = A e^{-G_t},
+// B~ = B e^{G_{t-1}} [C r_ab][dk] (bf16, zero on padding tokens; the chunked
+// backward's inputs).
+struct PrepBwOut {
+  void *qt, *kt, *at, *bt;
+};
+hipError_t fast_prepare_bw(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
+                           const void* B, void* workspace, const PrepBwOut& out, hipStream_t s);
 // Gating-chunk summaries for the query-conditioned composition, from the bf16
 // prepare's operators of the 64-token problem p: per gating chunk of G
 // consecutive chunks (G <= 4), Acal^T [dk][dk] and B^T [dv][dk] in bf16, the
@@ -111,6 +120,8 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
 // ws: backward_chunked_bytes(p) bytes.
 bool backward_chunked(const Problem& p);
 size_t backward_chunked_bytes(const Problem& p);
+// Where, inside ws, fast_prepare_bw is to put the scaled operands.
+PrepBwOut backward_chunked_prep_out(const Problem& p, void* ws);
 // The cotangent boundary scan of that route on bf16 MFMAs, over the bf16 MFMA
 // prepare's operators M: gend[j] (the cotangent leaving chunk j, bf16) for
 // every chunk, and dS0 (fp32).
