@@ -96,7 +96,7 @@ struct BcBufs {
   float* gam;                // [dk] e^{G} at the chunk's last token
   __bf16 *qt, *kt;           // [C][dk]
   __bf16 *at, *bt;           // [NA][dk]
-  float *ry, *rx;            // right-hand sides in tile order [NA/16][dv/16][64 lanes][4]
+  __bf16 *ry, *rx;           // right-hand sides in tile order [NA/16][dv/16][64 lanes][4], bf16
   __bf16 *y, *x;             // [NA][dv]
   float* gk;                 // [C][dk] the decay gradient's terms of the dK group
   float* ends;               // [dk] rowdot(dS_end, S_end), from the dK group's staging
@@ -122,8 +122,8 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
   t.kt = reinterpret_cast<__bf16*>(take(J * cdk * 2));
   t.at = reinterpret_cast<__bf16*>(take(J * adk * 2));
   t.bt = reinterpret_cast<__bf16*>(take(J * adk * 2));
-  t.ry = reinterpret_cast<float*>(take(J * ndv * 4));
-  t.rx = reinterpret_cast<float*>(take(J * ndv * 4));
+  t.ry = reinterpret_cast<__bf16*>(take(J * ndv * 2));
+  t.rx = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.x = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.gk = reinterpret_cast<float*>(take(J * cdk * 4));
@@ -273,7 +273,8 @@ struct BcGroupArgs {
   BcSrc Aa, Ab;                 // A rows of the two kinds (Ab unused for one kind)
   BcSrc W0, B1, C1, B2, C2;     // the shared B-side operands
   BcBufs w;
-  float *outa, *outb;           // right-hand sides (tile order) or gradients
+  void* outa;                   // right-hand side (bf16, tile order) or the first kind's gradient (fp32)
+  float* outb;                  // the second kind's gradient
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
   float* dld;                   // dQ group: the log-decay gradient
@@ -678,9 +679,11 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     }
   }
   if constexpr (RHS) {
+    // bf16, rounded as the solve's own products round the solved blocks
+    __bf16* rout = static_cast<__bf16*>(a.outa);
 #pragma unroll
     for (int ot = 0; ot < OT; ++ot)
-      *reinterpret_cast<cf4*>(a.outa + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
+      *reinterpret_cast<cb4*>(rout + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = to_b4(acc[ot]);
   } else {
     // The gradients leave through LDS as whole rows: every wave's 16 x NOUT
     // block into the (now free) staging space, then 16-byte stores.
@@ -701,14 +704,14 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     if constexpr (GRAD) {
       static_assert(K::M == kCC && LE == DK + 4, "fused epilogue: token rows, then rank rows, of width d_k");
       float* terms = ep + NW * 16 * LE;   // dQ group: beyond the products
-      epi.finish(job, ep, a.w, a.outa, a.outb, terms, tid);
+      epi.finish(job, ep, a.w, static_cast<float*>(a.outa), a.outb, terms, tid);
       if constexpr (KA_ == kDq) {
         __syncthreads();
         epi.reverse(p, job, a.w, terms, a.dld, tid);
       }
     } else {
       static_assert(KB_ < 0, "dV runs alone");
-      bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, a.outa, tid);
+      bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, static_cast<float*>(a.outa), tid);
     }
   }
 }
@@ -762,10 +765,10 @@ __global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_
   const bool isx = wave >= NCT;
   const int ct = wave % NCT;
   // this wave's right-hand side tiles, loaded first
-  const float* R = (isx ? w.rx : w.ry) + job * NA * DV;
-  cf4 rhs[NB];
+  const __bf16* R = (isx ? w.rx : w.ry) + job * NA * DV;
+  cb4 rhb[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) rhs[i] = *reinterpret_cast<const cf4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+  for (int i = 0; i < NB; ++i) rhb[i] = *reinterpret_cast<const cb4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
   // the chunk's B~ and A~ rows into LDS: every load issued before any write
   __bf16* bt = reinterpret_cast<__bf16*>(sm + Cf::OBS);
   __bf16* at = reinterpret_cast<__bf16*>(sm + Cf::OAS);
@@ -839,7 +842,7 @@ __global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_
   if (!isx) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      cf4 acc = rhs[i];
+      cf4 acc = cf4{(float)rhb[i][0], (float)rhb[i][1], (float)rhb[i][2], (float)rhb[i][3]};
       const int base = i * (i - 1) / 2;   // tiles (i, 0 .. i-1)
 #pragma unroll
       for (int jb = 0; jb + 1 < i; jb += 2)
@@ -850,7 +853,7 @@ __global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_
   } else {
 #pragma unroll
     for (int i = NB - 1; i >= 0; --i) {
-      cf4 acc = rhs[i];
+      cf4 acc = cf4{(float)rhb[i][0], (float)rhb[i][1], (float)rhb[i][2], (float)rhb[i][3]};
       // tiles (L_ji)^T for j = i+1 .. NB-1, stored at index j (j - 1) / 2 + i
       int jb = i + 1;
 #pragma unroll
@@ -1084,7 +1087,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcState}, GdS{gend, kSrcCotG};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
-                   float* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr) -> hipError_t {
+                   void* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr) -> hipError_t {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
