@@ -99,6 +99,7 @@ struct BcBufs {
   __bf16 *ry, *rx;           // right-hand sides in tile order [NA/16][dv/16][64 lanes][4], bf16
   __bf16 *y, *x;             // [NA][dv]
   float* gk;                 // [C][dk] the decay gradient's terms of the dK group
+  float* dv1;                // dV's first two terms, fp32 in tile order [C/16][dv/16][64 lanes][4] (r_ab > 0)
   float* ends;               // [dk] rowdot(dS_end, S_end), from the dK group's staging
 };
 
@@ -127,6 +128,7 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.x = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.gk = reinterpret_cast<float*>(take(J * cdk * 4));
+  t.dv1 = reinterpret_cast<float*>(take(p.r_ab > 0 ? J * kCC * p.dv * 4 : 0));
   t.ends = reinterpret_cast<float*>(take(J * p.dk * 4));
   if (b) *b = t;
   return off;
@@ -217,8 +219,10 @@ __global__ __launch_bounds__(256) void bwc_g_kernel(BcGArgs a) {
 // A group is one or two kinds whose products read the same B-side operands
 // (W0, B1, C1, B2, C2): one workgroup per chunk stages them in LDS once, then
 // each wave forms 16 rows of one kind's output, its A rows read from memory.
-// The pairs: (dK, dA) and (dQ, dB).
-enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 };
+// The pairs: (dK, dA), (dQ, dB), and at r_ab > 0 (the adjoint right-hand side,
+// dV's first two terms), since those read the same operands; dV's last term
+// (dV2, which needs the adjoint solve's X) then runs on its own.
+enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6, kDv1 = 7, kDv2 = 8 };
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
 // Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
 // solve; the sequence's own rows t0 .. t0 + C - 1 (bf16 [T][cols], zero past
@@ -236,10 +240,14 @@ struct BcKindCfg {
   static constexpr bool ROWS_A = KIND == kRhsY || KIND == kRhsX || KIND == kDa || KIND == kDb;
   static constexpr int M = ROWS_A ? NA : kCC;                                  // rows of A
   static constexpr int RA = ROWS_A ? RAB : 1;                                  // rows per token of A
-  static constexpr int KA = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? DK : DV;
-  static constexpr int NOUT = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? DV : DK;
+  // value-column outputs (A rows over d_k)
+  static constexpr bool VOUT = KIND == kRhsY || KIND == kRhsX || KIND == kDv || KIND == kDv1 || KIND == kDv2;
+  static constexpr int KA = VOUT ? DK : DV;
+  static constexpr int NOUT = VOUT ? DV : DK;
   static constexpr int MSK1 = (KIND == kRhsY || KIND == kDb) ? kLT : (KIND == kDq ? kLE : kGE);
-  static constexpr bool TERM2 = KIND >= kDq && RAB > 0;
+  // dV2 has only the second score term, on top of dV1's partial (INIT)
+  static constexpr bool HASW0 = KIND != kDv2, T1 = KIND != kDv2, INIT = KIND == kDv2;
+  static constexpr bool TERM2 = ((KIND >= kDq && KIND <= kDb) && RAB > 0) || KIND == kDv2;
   static constexpr int MSK2 = KIND == kDq ? kLE : (KIND == kDb ? kLT : kGT);
   static constexpr float SIGN = (KIND == kDa || KIND == kDb) ? -1.f : 1.f;
   // W0 as it lives in memory: its transpose (S_in or Gamma dS_end for dQ, dK,
@@ -249,7 +257,7 @@ struct BcKindCfg {
   // where the shared operands live (see BcSrcKind)
   static constexpr int SW0 = (KIND == kRhsY || KIND == kDq || KIND == kDb) ? kSrcState : kSrcCotG;
   static constexpr int SB1 = (KIND == kDq || KIND == kDb || KIND == kDk || KIND == kDa) ? kSrcSeq : kSrcChunk;
-  static constexpr int SC1 = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? kSrcSeq : kSrcChunk;
+  static constexpr int SC1 = (KIND == kRhsY || KIND == kRhsX || KIND == kDv || KIND == kDv1) ? kSrcSeq : kSrcChunk;
 };
 
 // LDS layout of a kind's staged operands (bf16 elements).  Rows read by
@@ -260,10 +268,10 @@ template <int KIND, int DK, int DV, int RAB>
 struct BcStage {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
   static constexpr int NA = K::NA, KA = K::KA, NOUT = K::NOUT;
-  static constexpr int W0R = K::W0T ? NOUT : KA, W0C = K::W0T ? KA : NOUT;
+  static constexpr int W0R = K::HASW0 ? (K::W0T ? NOUT : KA) : 0, W0C = K::W0T ? KA : NOUT;
   static constexpr int LW0 = W0C + (K::W0T ? 8 : 16), LB = KA + 8, LC = NOUT + 16;
-  static constexpr int OW = 0, OB1 = OW + W0R * LW0, OC1 = OB1 + kCC * LB;
-  static constexpr int OB2 = OC1 + kCC * LC, OC2 = OB2 + (K::TERM2 ? NA * LB : 0);
+  static constexpr int OW = 0, OB1 = OW + W0R * LW0, OC1 = OB1 + (K::T1 ? kCC * LB : 0);
+  static constexpr int OB2 = OC1 + (K::T1 ? kCC * LC : 0), OC2 = OB2 + (K::TERM2 ? NA * LB : 0);
   static constexpr int TOTAL = OC2 + (K::TERM2 ? NA * LC : 0);
 };
 
@@ -274,7 +282,8 @@ struct BcGroupArgs {
   BcSrc W0, B1, C1, B2, C2;     // the shared B-side operands
   BcBufs w;
   void* outa;                   // right-hand side (bf16, tile order) or the first kind's gradient (fp32)
-  float* outb;                  // the second kind's gradient
+  float* outb;                  // the second kind's gradient (dV1: its partial, fp32 tile order)
+  const float* init;            // dV2: dV1's partial, the accumulators' start
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
   float* dld;                   // dQ group: the log-decay gradient
@@ -314,7 +323,8 @@ __device__ __forceinline__ void bc_afrag(const Problem& p, int64_t job, int rb, 
 template <int KIND, int DK, int DV, int RAB>
 __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
                                         const cb8 (&af)[BcKindCfg<KIND, DK, DV, RAB>::KA / 32], const __bf16* lds,
-                                        cf4 (&acc)[BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane) {
+                                        cf4 (&acc)[BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane,
+                                        const float* init = nullptr) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
   using L = BcStage<KIND, DK, DV, RAB>;
   constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
@@ -322,15 +332,21 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
   const int r0 = 16 * rb;
 #pragma unroll
   for (int ot = 0; ot < OT; ++ot) {
-    acc[ot] = cz4();
+    if constexpr (K::INIT)
+      acc[ot] = *reinterpret_cast<const cf4*>(init + (((job * (K::M / 16) + rb) * OT + ot) * 64 + lane) * 4);
+    else
+      acc[ot] = cz4();
+    if constexpr (K::HASW0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      cb8 bw;
-      if constexpr (K::W0T)
-        bw = rowfrag(lds + L::OW + (16 * ot + lr) * L::LW0, ks, lane);
-      else
-        bw = cat8(ltr4(lds + L::OW, L::LW0, 32 * ks, 16 * ot, lane), ltr4(lds + L::OW, L::LW0, 32 * ks + 16, 16 * ot, lane));
-      acc[ot] = mfma_b(af[ks], bw, acc[ot]);
+      for (int ks = 0; ks < KS; ++ks) {
+        cb8 bw;
+        if constexpr (K::W0T)
+          bw = rowfrag(lds + L::OW + (16 * ot + lr) * L::LW0, ks, lane);
+        else
+          bw = cat8(ltr4(lds + L::OW, L::LW0, 32 * ks, 16 * ot, lane),
+                    ltr4(lds + L::OW, L::LW0, 32 * ks + 16, 16 * ot, lane));
+        acc[ot] = mfma_b(af[ks], bw, acc[ot]);
+      }
     }
   }
   const int ta0 = r0 / K::RA, ta1 = (r0 + 15) / K::RA, trow = (r0 + lr) / K::RA;
@@ -360,7 +376,8 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
     }
   };
   using I1 = std::integral_constant<int, 1>;
-  term(L::OB1, L::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
+  if constexpr (K::T1)
+    term(L::OB1, L::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
   if constexpr (K::TERM2)
     term(L::OB2, L::OC2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
          std::integral_constant<int, K::MSK2>{}, -1.f);
@@ -372,7 +389,7 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
 template <int KIND, int DK, int DV, int RAB, int NT>
 __device__ __forceinline__ void bc_out(const Problem& p, int64_t job, const float* ep, float* out, int tid) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
-  static_assert(KIND == kDv, "the other gradients leave through bc_epi");
+  static_assert(KIND == kDv || KIND == kDv2, "the other gradients leave through bc_epi");
   constexpr int C4 = K::NOUT / 4, LE = K::NOUT + 4, ITEMS = K::M * C4;
   const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
@@ -605,6 +622,10 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   using L = BcStage<KA_, DK, DV, RAB>;
   constexpr int WA = K::M / 16, KS = K::KA / 32, OT = K::NOUT / 16;
   constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX;
+  using LB_ = BcStage<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>;
+  static_assert(LB_::OW == L::OW && LB_::OB1 == L::OB1 && LB_::OC1 == L::OC1 && LB_::OB2 == L::OB2 &&
+                    LB_::OC2 == L::OC2 && LB_::LW0 == L::LW0 && LB_::LB == L::LB && LB_::LC == L::LC,
+                "the two kinds of a group read one staging layout");
   extern __shared__ __align__(16) unsigned char smem_[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem_);
   const Problem& p = a.p;
@@ -631,19 +652,23 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   BcStg<kSrcChunk, (K::TERM2 ? K::NA : 16), K::NOUT, 64 * NW> s4;
   // the boundary states have N + 1 slots per head: the state entering chunk
   // jc is slot jc, the one leaving it slot jc + 1
-  s0.load(a.W0.ptr, a.w.gam + job * DK, K::SW0 == kSrcState ? job + bh : job, n, tok0, tid);
+  if constexpr (K::HASW0) s0.load(a.W0.ptr, a.w.gam + job * DK, K::SW0 == kSrcState ? job + bh : job, n, tok0, tid);
   // dK group: the state leaving the chunk, for the chunk-end term of the decay gradient
   BcStg<kSrcState, L::W0R, L::W0C, 64 * NW> se;
   if constexpr (KA_ == kDk) se.load(a.ckpt, nullptr, job + bh + 1, n, tok0, tid);
-  s1.load(a.B1.ptr, nullptr, job, n, tok0, tid);
-  s2.load(a.C1.ptr, nullptr, job, n, tok0, tid);
+  if constexpr (K::T1) {
+    s1.load(a.B1.ptr, nullptr, job, n, tok0, tid);
+    s2.load(a.C1.ptr, nullptr, job, n, tok0, tid);
+  }
   if constexpr (K::TERM2) {
     s3.load(a.B2.ptr, nullptr, job, n, tok0, tid);
     s4.load(a.C2.ptr, nullptr, job, n, tok0, tid);
   }
-  s0.store(lds + L::OW, L::LW0, tid);
-  s1.store(lds + L::OB1, L::LB, tid);
-  s2.store(lds + L::OC1, L::LC, tid);
+  if constexpr (K::HASW0) s0.store(lds + L::OW, L::LW0, tid);
+  if constexpr (K::T1) {
+    s1.store(lds + L::OB1, L::LB, tid);
+    s2.store(lds + L::OC1, L::LC, tid);
+  }
   if constexpr (K::TERM2) {
     s3.store(lds + L::OB2, L::LB, tid);
     s4.store(lds + L::OC2, L::LC, tid);
@@ -673,17 +698,26 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   const bool live = RHS || 16 * rb / ra < n;
   if (live) {
     if (isa) {
-      bc_prod<KA_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane);
+      bc_prod<KA_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane, a.init);
     } else if constexpr (KB_ >= 0) {
-      bc_prod<KB_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane);
+      bc_prod<KB_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane, a.init);
     }
   }
   if constexpr (RHS) {
-    // bf16, rounded as the solve's own products round the solved blocks
-    __bf16* rout = static_cast<__bf16*>(a.outa);
+    if (isa) {
+      // bf16, rounded as the solve's own products round the solved blocks
+      __bf16* rout = static_cast<__bf16*>(a.outa);
 #pragma unroll
-    for (int ot = 0; ot < OT; ++ot)
-      *reinterpret_cast<cb4*>(rout + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = to_b4(acc[ot]);
+      for (int ot = 0; ot < OT; ++ot)
+        *reinterpret_cast<cb4*>(rout + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = to_b4(acc[ot]);
+    } else if constexpr (KB_ >= 0) {
+      // dV1's partial, fp32 in tile order (dV2 starts its accumulators from it)
+      static_assert(KB_ == kDv1 && BcKindCfg<KB_, DK, DV, RAB>::NOUT == K::NOUT, "the adjoint group's second kind is dV1");
+      constexpr int MB = BcKindCfg<KB_, DK, DV, RAB>::M;
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot)
+        *reinterpret_cast<cf4*>(a.outb + (((job * (MB / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
+    }
   } else {
     // The gradients leave through LDS as whole rows: every wave's 16 x NOUT
     // block into the (now free) staging space, then 16-byte stores.
@@ -1087,7 +1121,8 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcState}, GdS{gend, kSrcCotG};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
-                   void* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr) -> hipError_t {
+                   void* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr,
+                   const float* init = nullptr) -> hipError_t {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
@@ -1100,7 +1135,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, bf(xr), bf(rr), bf(ckpt), dld});
+                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, init, bf(xr), bf(rr), bf(ckpt), dld});
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
@@ -1108,8 +1143,9 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
                    w.ry, nullptr)) != hipSuccess)
       return e;
-    if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, chunk(w.at), none, GdS, chunk(w.qt), Os, none, none,
-                   w.rx, nullptr)) != hipSuccess)
+    // the adjoint right-hand side and dV's first two terms read the same operands
+    if ((e = group(std::integral_constant<int, kRhsX>{}, std::integral_constant<int, kDv1>{}, chunk(w.at), chunk(w.kt),
+                   GdS, chunk(w.qt), Os, none, none, w.rx, w.dv1)) != hipSuccess)
       return e;
     hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(jobs), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
                        BcSolveArgs{p, w});
@@ -1128,9 +1164,16 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
                    nullptr, q, nullptr)) != hipSuccess)
       return e;
   }
-  if ((e = group(std::integral_constant<int, kDv>{}, KN{}, chunk(w.kt), none, GdS, chunk(w.qt), Os, chunk(w.bt),
-                 chunk(w.x), dV, nullptr)) != hipSuccess)
-    return e;
+  if constexpr (RAB > 0) {
+    // dV's last term, -M_>(K~ B~^T) X, on top of the first two
+    if ((e = group(std::integral_constant<int, kDv2>{}, KN{}, chunk(w.kt), none, none, none, none, chunk(w.bt),
+                   chunk(w.x), dV, nullptr, nullptr, nullptr, w.dv1)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = group(std::integral_constant<int, kDv>{}, KN{}, chunk(w.kt), none, GdS, chunk(w.qt), Os, none, none, dV,
+                   nullptr)) != hipSuccess)
+      return e;
+  }
   return hipSuccess;
 }
 
