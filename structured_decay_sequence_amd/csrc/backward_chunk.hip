@@ -299,43 +299,53 @@ __device__ __forceinline__ bool bc_empty(int ta0, int ta1, int tb0, int tb1) {
   return MASK == kLE ? tb0 > ta1 : (MASK == kLT ? tb0 >= ta1 : (MASK == kGE ? tb1 < ta0 : tb1 <= ta0));
 }
 
-// The A fragments of 16 rows (block rb) of kind KIND for chunk job.
-template <int KIND, int DK, int DV, int RAB>
-__device__ __forceinline__ void bc_afrag(const Problem& p, int64_t job, int rb, const BcSrc& As,
-                                         cb8 (&af)[BcKindCfg<KIND, DK, DV, RAB>::KA / 32], int lane) {
+// The A fragments of R consecutive 16-row blocks (rb0 ..) of kind KIND for chunk job.
+template <int KIND, int DK, int DV, int RAB, int R>
+__device__ __forceinline__ void bc_afrag(const Problem& p, int64_t job, int rb0, const BcSrc& As,
+                                         cb8 (&af)[R][BcKindCfg<KIND, DK, DV, RAB>::KA / 32], int lane) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
-  const int lr = lane & 15, r0 = 16 * rb;
+  const int lr = lane & 15;
   const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
-  const __bf16* arow;
-  if (As.kind == kSrcSeq) {
-    const int r = r0 + lr < n ? r0 + lr : n - 1;   // a padding row's output is not written
-    arow = static_cast<const __bf16*>(As.ptr) + (bh * p.T + t0 + r) * K::KA;
-  } else {
-    arow = static_cast<const __bf16*>(As.ptr) + (job * K::M + r0 + lr) * K::KA;
-  }
 #pragma unroll
-  for (int ks = 0; ks < K::KA / 32; ++ks) af[ks] = rowfrag(arow, ks, lane);
+  for (int r = 0; r < R; ++r) {
+    const int row = 16 * (rb0 + r) + lr;
+    const __bf16* arow;
+    if (As.kind == kSrcSeq) {
+      const int rr = row < n ? row : n - 1;   // a padding row's output is not written
+      arow = static_cast<const __bf16*>(As.ptr) + (bh * p.T + t0 + rr) * K::KA;
+    } else {
+      arow = static_cast<const __bf16*>(As.ptr) + (job * K::M + row) * K::KA;
+    }
+#pragma unroll
+    for (int ks = 0; ks < K::KA / 32; ++ks) af[r][ks] = rowfrag(arow, ks, lane);
+  }
 }
 
-// 16 rows (block rb) of kind KIND's product for chunk job, B side in LDS:
-// acc (accumulator layout: lane holds rows 4 lg + e, column 16 ot + lr).
-template <int KIND, int DK, int DV, int RAB>
-__device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
-                                        const cb8 (&af)[BcKindCfg<KIND, DK, DV, RAB>::KA / 32], const __bf16* lds,
-                                        cf4 (&acc)[BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane,
+// R consecutive 16-row blocks (rb0 ..) of kind KIND's product for chunk job,
+// B side in LDS: acc[r] (accumulator layout: lane holds rows 4 lg + e of
+// block rb0 + r, column 16 ot + lr).  Every B-side fragment read from LDS
+// serves the R blocks, so waves of two blocks halve those reads.
+template <int KIND, int DK, int DV, int RAB, int R>
+__device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
+                                        const cb8 (&af)[R][BcKindCfg<KIND, DK, DV, RAB>::KA / 32], const __bf16* lds,
+                                        cf4 (&acc)[R][BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane,
                                         const float* init = nullptr) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
   using L = BcStage<KIND, DK, DV, RAB>;
   constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
   const int lr = lane & 15, lg = lane >> 4;
-  const int r0 = 16 * rb;
+  const int r0 = 16 * rb0;
 #pragma unroll
   for (int ot = 0; ot < OT; ++ot) {
-    if constexpr (K::INIT)
-      acc[ot] = *reinterpret_cast<const cf4*>(init + (((job * (K::M / 16) + rb) * OT + ot) * 64 + lane) * 4);
-    else
-      acc[ot] = cz4();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if constexpr (K::INIT)
+        acc[r][ot] =
+            *reinterpret_cast<const cf4*>(init + (((job * (K::M / 16) + rb0 + r) * OT + ot) * 64 + lane) * 4);
+      else
+        acc[r][ot] = cz4();
+    }
     if constexpr (K::HASW0) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -345,34 +355,49 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb,
         else
           bw = cat8(ltr4(lds + L::OW, L::LW0, 32 * ks, 16 * ot, lane),
                     ltr4(lds + L::OW, L::LW0, 32 * ks + 16, 16 * ot, lane));
-        acc[ot] = mfma_b(af[ks], bw, acc[ot]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][ot] = mfma_b(af[r][ks], bw, acc[r][ot]);
       }
     }
   }
-  const int ta0 = r0 / K::RA, ta1 = (r0 + 15) / K::RA, trow = (r0 + lr) / K::RA;
+  // token range of the R blocks' rows, and each lane's row token per block
+  const int ta0 = r0 / K::RA, ta1 = (r0 + 16 * R - 1) / K::RA;
+  int trow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) trow[r] = (r0 + 16 * r + lr) / K::RA;
   // one score term: NB columns (RB rows of B per token), mask, sign
   auto term = [&](int oB, int oC, auto nb_, auto rb_, auto mask_, float sg) {
     constexpr int NBc = decltype(nb_)::value, RB = decltype(rb_)::value, MASK = decltype(mask_)::value;
 #pragma unroll 1
     for (int c0 = 0; c0 < NBc; c0 += 32) {
       if (bc_empty<MASK>(ta0, ta1, c0 / RB, (c0 + 31) / RB)) continue;
-      cf4 s2[2];
+      cf4 s2[R][2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        s2[h] = cz4();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s2[h] = mfma_b(rowfrag(lds + oB + (c0 + 16 * h + lr) * L::LB, ks, lane), af[ks], s2[h]);
-        // lane: score(row r0 + lr, column c0 + 16 h + 4 lg + e)
+        for (int r = 0; r < R; ++r) s2[r][h] = cz4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s2[h][e] = bc_keep<MASK>(trow, (c0 + 16 * h + 4 * lg + e) / RB) ? sg * s2[h][e] : 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          const cb8 bfr = rowfrag(lds + oB + (c0 + 16 * h + lr) * L::LB, ks, lane);
+#pragma unroll
+          for (int r = 0; r < R; ++r) s2[r][h] = mfma_b(bfr, af[r][ks], s2[r][h]);
+        }
+        // lane: score(row r0 + 16 r + lr, column c0 + 16 h + 4 lg + e)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s2[r][h][e] = bc_keep<MASK>(trow[r], (c0 + 16 * h + 4 * lg + e) / RB) ? sg * s2[r][h][e] : 0.f;
       }
-      const cb8 sf = cat8(to_b4(s2[0]), to_b4(s2[1]));
+      cb8 sf[R];
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot)
-        acc[ot] = mfma_b(sf, cat8(ltr4(lds + oC, L::LC, c0, 16 * ot, lane), ltr4(lds + oC, L::LC, c0 + 16, 16 * ot, lane)),
-                         acc[ot]);
+      for (int r = 0; r < R; ++r) sf[r] = cat8(to_b4(s2[r][0]), to_b4(s2[r][1]));
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) {
+        const cb8 cf = cat8(ltr4(lds + oC, L::LC, c0, 16 * ot, lane), ltr4(lds + oC, L::LC, c0 + 16, 16 * ot, lane));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][ot] = mfma_b(sf[r], cf, acc[r][ot]);
+      }
     }
   };
   using I1 = std::integral_constant<int, 1>;
@@ -610,9 +635,19 @@ struct BcEpi {
 
 template <int KA_, int KB_>
 struct BcGroupWaves {
+  // 16-row blocks per wave of the second kind: the rank-row gradients (dA,
+  // dB) take two, so that with the first kind's one per wave every SIMD holds
+  // three blocks, and their B-side reads serve two blocks.
+  static constexpr int RB = (KB_ == kDa || KB_ == kDb) ? 2 : 1;
   template <int DK, int DV, int RAB>
   static constexpr int count() {
-    return BcKindCfg<KA_, DK, DV, RAB>::M / 16 + (KB_ >= 0 ? BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::M / 16 : 0);
+    return BcKindCfg<KA_, DK, DV, RAB>::M / 16 +
+           (KB_ >= 0 ? BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::M / (16 * RB) : 0);
+  }
+  // output rows of the group (both kinds)
+  template <int DK, int DV, int RAB>
+  static constexpr int rows() {
+    return BcKindCfg<KA_, DK, DV, RAB>::M + (KB_ >= 0 ? BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::M : 0);
   }
 };
 
@@ -635,13 +670,16 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool isa = wave < WA;
-  const int rb = isa ? wave : wave - WA;
+  constexpr int RB = BcGroupWaves<KA_, KB_>::RB;
+  constexpr int KB2 = KB_ >= 0 ? KB_ : KA_;
+  // first 16-row block of this wave within its kind
+  const int rb = isa ? wave : (wave - WA) * RB;
   // this wave's A rows first, so that their loads overlap the staging's
-  cb8 af[KS];
+  cb8 af[RB][KS];
   if (isa) {
-    bc_afrag<KA_, DK, DV, RAB>(p, job, rb, a.Aa, af, lane);
+    bc_afrag<KA_, DK, DV, RAB, 1>(p, job, rb, a.Aa, reinterpret_cast<cb8(&)[1][KS]>(af), lane);
   } else if constexpr (KB_ >= 0) {
-    bc_afrag<KB_, DK, DV, RAB>(p, job, rb, a.Ab, af, lane);
+    bc_afrag<KB_, DK, DV, RAB, RB>(p, job, rb, a.Ab, af, lane);
   }
   // Staging: every load of every operand is issued before any LDS write, so
   // their latencies overlap.
@@ -691,16 +729,17 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     }
   }
   __syncthreads();
-  cf4 acc[OT];
+  cf4 acc[RB][OT];
   // rows of padding tokens only: no gradient to write (the right-hand sides
   // are formed for them too, as zeros, since the solves read every row)
-  const int ra = isa ? K::RA : BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::RA;
+  const int ra = isa ? K::RA : BcKindCfg<KB2, DK, DV, RAB>::RA;
   const bool live = RHS || 16 * rb / ra < n;
   if (live) {
     if (isa) {
-      bc_prod<KA_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane, a.init);
+      bc_prod<KA_, DK, DV, RAB, 1>(p, job, rb, reinterpret_cast<const cb8(&)[1][KS]>(af), lds,
+                                   reinterpret_cast<cf4(&)[1][OT]>(acc), lane, a.init);
     } else if constexpr (KB_ >= 0) {
-      bc_prod<KB_, DK, DV, RAB>(p, job, rb, af, lds, acc, lane, a.init);
+      bc_prod<KB_, DK, DV, RAB, RB>(p, job, rb, af, lds, acc, lane, a.init);
     }
   }
   if constexpr (RHS) {
@@ -709,18 +748,20 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
       __bf16* rout = static_cast<__bf16*>(a.outa);
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot)
-        *reinterpret_cast<cb4*>(rout + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = to_b4(acc[ot]);
+        *reinterpret_cast<cb4*>(rout + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = to_b4(acc[0][ot]);
     } else if constexpr (KB_ >= 0) {
       // dV1's partial, fp32 in tile order (dV2 starts its accumulators from it)
-      static_assert(KB_ == kDv1 && BcKindCfg<KB_, DK, DV, RAB>::NOUT == K::NOUT, "the adjoint group's second kind is dV1");
+      static_assert(KB_ == kDv1 && RB == 1 && BcKindCfg<KB_, DK, DV, RAB>::NOUT == K::NOUT,
+                    "the adjoint group's second kind is dV1");
       constexpr int MB = BcKindCfg<KB_, DK, DV, RAB>::M;
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot)
-        *reinterpret_cast<cf4*>(a.outb + (((job * (MB / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[ot];
+        *reinterpret_cast<cf4*>(a.outb + (((job * (MB / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[0][ot];
     }
   } else {
-    // The gradients leave through LDS as whole rows: every wave's 16 x NOUT
-    // block into the (now free) staging space, then 16-byte stores.
+    // The gradients leave through LDS as whole rows: every wave's 16-row
+    // blocks of NOUT columns into the (now free) staging space (the first
+    // kind's rows, then the second's), then 16-byte stores.
     constexpr int LE = K::NOUT + 4;
     constexpr bool GRAD = KA_ == kDk || KA_ == kDq;   // the fused epilogue (else dV)
     float* ep = reinterpret_cast<float*>(smem_);
@@ -730,14 +771,19 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     if (live) {
       const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot)
+      for (int r = 0; r < RB; ++r) {
+        if (isa && r > 0) break;
+        const int blk = isa ? rb : WA + rb + r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ep[(wave * 16 + 4 * lg + e) * LE + 16 * ot + lr] = acc[ot][e];
+        for (int ot = 0; ot < OT; ++ot)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ep[(blk * 16 + 4 * lg + e) * LE + 16 * ot + lr] = acc[r][ot][e];
+      }
     }
     __syncthreads();
     if constexpr (GRAD) {
       static_assert(K::M == kCC && LE == DK + 4, "fused epilogue: token rows, then rank rows, of width d_k");
-      float* terms = ep + NW * 16 * LE;   // dQ group: beyond the products
+      float* terms = ep + BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>() * LE;   // dQ group: beyond the products
       epi.finish(job, ep, a.w, static_cast<float*>(a.outa), a.outb, terms, tid);
       if constexpr (KA_ == kDq) {
         __syncthreads();
@@ -1129,7 +1175,8 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     const void* fn = reinterpret_cast<const void*>(bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>);
     const size_t stage_b = static_cast<size_t>(L::TOTAL) * 2;
     // the products' copy, and the dQ group's decay-gradient terms beyond it
-    const size_t ep_b = static_cast<size_t>(NW) * 16 * (L::NOUT + 4) * sizeof(float) +
+    const size_t ep_b = static_cast<size_t>(BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>()) * (L::NOUT + 4) *
+                            sizeof(float) +
                         (KA_ == kDq ? BcEpi<false, DK, RAB, 64 * NW>::EXTRA : 0);
     const size_t lds = stage_b > ep_b ? stage_b : ep_b;
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
