@@ -282,7 +282,7 @@ struct BcGroupArgs {
   BcSrc W0, B1, C1, B2, C2;     // the shared B-side operands
   BcBufs w;
   void* outa;                   // right-hand side (bf16, tile order) or the first kind's gradient (fp32)
-  float* outb;                  // the second kind's gradient (dV1: its partial, fp32 tile order)
+  void* outb;                   // the second kind's gradient, or the adjoint right-hand side (bf16, tile order)
   const float* init;            // dV2: dV1's partial, the accumulators' start
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
@@ -636,9 +636,10 @@ struct BcEpi {
 template <int KA_, int KB_>
 struct BcGroupWaves {
   // 16-row blocks per wave of the second kind: the rank-row gradients (dA,
-  // dB) take two, so that with the first kind's one per wave every SIMD holds
+  // dB, and the adjoint right-hand side beside dV1) take two, so that with
+  // the first kind's one per wave every SIMD holds
   // three blocks, and their B-side reads serve two blocks.
-  static constexpr int RB = (KB_ == kDa || KB_ == kDb) ? 2 : 1;
+  static constexpr int RB = (KB_ == kDa || KB_ == kDb || KB_ == kRhsX) ? 2 : 1;
   template <int DK, int DV, int RAB>
   static constexpr int count() {
     return BcKindCfg<KA_, DK, DV, RAB>::M / 16 +
@@ -656,7 +657,9 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   using K = BcKindCfg<KA_, DK, DV, RAB>;
   using L = BcStage<KA_, DK, DV, RAB>;
   constexpr int WA = K::M / 16, KS = K::KA / 32, OT = K::NOUT / 16;
-  constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX;
+  // groups whose outputs leave in tile order: the right-hand sides (bf16)
+  // and dV1's partial (fp32)
+  constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX || KA_ == kDv1;
   using LB_ = BcStage<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>;
   static_assert(LB_::OW == L::OW && LB_::OB1 == L::OB1 && LB_::OC1 == L::OC1 && LB_::OB2 == L::OB2 &&
                     LB_::OC2 == L::OC2 && LB_::LW0 == L::LW0 && LB_::LB == L::LB && LB_::LC == L::LC,
@@ -743,20 +746,27 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     }
   }
   if constexpr (RHS) {
+    // block blk of kind KIND in tile order: a right-hand side in bf16 (rounded
+    // as the solve's own products round the solved blocks), dV1's partial in
+    // fp32 (dV2 starts its accumulators from it)
+    auto tiles = [&](auto kind_, void* dst, int blk, const cf4(&t)[OT]) {
+      constexpr int KD = decltype(kind_)::value;
+      using KC = BcKindCfg<KD, DK, DV, RAB>;
+      static_assert(KC::NOUT == K::NOUT, "tile outputs of one width");
+#pragma unroll
+      for (int ot = 0; ot < OT; ++ot) {
+        const int64_t o = (((job * (KC::M / 16) + blk) * OT + ot) * 64 + lane) * 4;
+        if constexpr (KD == kDv1)
+          *reinterpret_cast<cf4*>(static_cast<float*>(dst) + o) = t[ot];
+        else
+          *reinterpret_cast<cb4*>(static_cast<__bf16*>(dst) + o) = to_b4(t[ot]);
+      }
+    };
     if (isa) {
-      // bf16, rounded as the solve's own products round the solved blocks
-      __bf16* rout = static_cast<__bf16*>(a.outa);
-#pragma unroll
-      for (int ot = 0; ot < OT; ++ot)
-        *reinterpret_cast<cb4*>(rout + (((job * (K::NA / 16) + rb) * OT + ot) * 64 + lane) * 4) = to_b4(acc[0][ot]);
+      tiles(std::integral_constant<int, KA_>{}, a.outa, rb, acc[0]);
     } else if constexpr (KB_ >= 0) {
-      // dV1's partial, fp32 in tile order (dV2 starts its accumulators from it)
-      static_assert(KB_ == kDv1 && RB == 1 && BcKindCfg<KB_, DK, DV, RAB>::NOUT == K::NOUT,
-                    "the adjoint group's second kind is dV1");
-      constexpr int MB = BcKindCfg<KB_, DK, DV, RAB>::M;
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot)
-        *reinterpret_cast<cf4*>(a.outb + (((job * (MB / 16) + rb) * OT + ot) * 64 + lane) * 4) = acc[0][ot];
+      for (int r = 0; r < RB; ++r) tiles(std::integral_constant<int, KB_>{}, a.outb, rb + r, acc[r]);
     }
   } else {
     // The gradients leave through LDS as whole rows: every wave's 16-row
@@ -784,7 +794,7 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     if constexpr (GRAD) {
       static_assert(K::M == kCC && LE == DK + 4, "fused epilogue: token rows, then rank rows, of width d_k");
       float* terms = ep + BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>() * LE;   // dQ group: beyond the products
-      epi.finish(job, ep, a.w, static_cast<float*>(a.outa), a.outb, terms, tid);
+      epi.finish(job, ep, a.w, static_cast<float*>(a.outa), static_cast<float*>(a.outb), terms, tid);
       if constexpr (KA_ == kDq) {
         __syncthreads();
         epi.reverse(p, job, a.w, terms, a.dld, tid);
@@ -1167,7 +1177,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcState}, GdS{gend, kSrcCotG};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
-                   void* outa, float* outb, const void* xr = nullptr, const void* rr = nullptr,
+                   void* outa, void* outb, const void* xr = nullptr, const void* rr = nullptr,
                    const float* init = nullptr) -> hipError_t {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
@@ -1190,9 +1200,9 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
                    w.ry, nullptr)) != hipSuccess)
       return e;
-    // the adjoint right-hand side and dV's first two terms read the same operands
-    if ((e = group(std::integral_constant<int, kRhsX>{}, std::integral_constant<int, kDv1>{}, chunk(w.at), chunk(w.kt),
-                   GdS, chunk(w.qt), Os, none, none, w.rx, w.dv1)) != hipSuccess)
+    // dV's first two terms and the adjoint right-hand side read the same operands
+    if ((e = group(std::integral_constant<int, kDv1>{}, std::integral_constant<int, kRhsX>{}, chunk(w.kt), chunk(w.at),
+                   GdS, chunk(w.qt), Os, none, none, w.dv1, w.rx)) != hipSuccess)
       return e;
     hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(jobs), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
                        BcSolveArgs{p, w});
