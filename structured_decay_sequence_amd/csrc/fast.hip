@@ -770,6 +770,11 @@ struct ScanCfg {
   static constexpr int LDO = BV + 8;       // padded row of the output stage
   static constexpr int OBUF = kC * LDO;
   static constexpr int LDS = 2 * (XBUF + OBUF) * 2;
+  // the boundary-state instance stages the DK state rows instead of the output rows
+  static constexpr int SBUF = DK * LDO;
+  static constexpr int LDS_CK = 2 * (XBUF + SBUF) * 2;
+  static constexpr int SITEMS = DK * (BV / 8);       // 16-byte state pieces
+  static constexpr int SIT = (SITEMS + NT - 1) / NT;
   static constexpr int MSZ = MT * KT * 256;          // operator elements per chunk
   static constexpr int VT = 2;                       // tokens per V piece
   static constexpr int VITEMS = (kC / VT) * (BV / 8); // VT tokens x 8 columns each
@@ -799,7 +804,7 @@ template <int DK, int BV, int NWV, int PD, bool CK>
 __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
   constexpr int KP = Cfg::KP, MPW = Cfg::MPW, NTN = Cfg::NTN, LDX = Cfg::LDX, NT = Cfg::NT;
-  constexpr int XBUF = Cfg::XBUF, LDO = Cfg::LDO, OBUF = Cfg::OBUF, MSZ = Cfg::MSZ;
+  constexpr int XBUF = Cfg::XBUF, LDO = Cfg::LDO, OBUF = CK ? Cfg::SBUF : Cfg::OBUF, MSZ = Cfg::MSZ;
   constexpr int VITEMS = Cfg::VITEMS, OITEMS = Cfg::OITEMS, OIT = Cfg::OIT;
   static_assert(Cfg::VIT == 1, "one V piece per thread");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -872,9 +877,20 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
       }
     }
   };
-  // Output rows of chunk jj from a staging buffer to HBM (none past the end).
+  // Output rows of chunk jj from a staging buffer to HBM (none past the end);
+  // the boundary-state instance: the state leaving chunk jj (slot jj + 1).
   auto flush_out = [&](const __bf16* O, int64_t jj) {
-    if (CK) return;
+    if constexpr (CK) {
+      if (jj >= N) return;
+      __bf16* ck = a.ckpt + static_cast<size_t>(bh * (N + 1) + jj + 1) * DK * dv + c0;
+#pragma unroll
+      for (int q = 0; q < Cfg::SIT; ++q) {
+        const int it = tid + q * NT;
+        const int i = it / (BV / 8), cg = it % (BV / 8);
+        if (it < Cfg::SITEMS) *reinterpret_cast<bf16x8*>(ck + (i * dv + cg * 8)) = lds8(O + i * LDO + cg * 8);
+      }
+      return;
+    }
     const int n = chunk_len(jj);
     __bf16* oj = obh + static_cast<size_t>(jj) * kC * dv;
 #pragma unroll
@@ -938,29 +954,18 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
       for (int nt = 0; nt < NTN; ++nt) {
         const int c = nt * 16 + lr;
         if (mt < DK / 16) {
-          *reinterpret_cast<bf16x4*>(Xn + c * LDX + kperm(mt * 16 + 4 * lg)) = to_bf16x4(acc[q][nt]);
-        } else {
+          const bf16x4 h = to_bf16x4(acc[q][nt]);
+          *reinterpret_cast<bf16x4*>(Xn + c * LDX + kperm(mt * 16 + 4 * lg)) = h;
+          if (CK) {
+            // the state rows, rounded as the next product reads them, staged
+            // row-major for the 16-byte stores one chunk later
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Oc[(mt * 16 + 4 * lg + e) * LDO + c] = h[e];
+          }
+        } else if (!CK) {
           const int t = (mt - DK / 16) * 16 + 4 * lg;
 #pragma unroll
           for (int e = 0; e < 4; ++e) Oc[(t + e) * LDO + c] = (__bf16)acc[q][nt][e];
-        }
-      }
-    }
-    if (CK && jj < N) {
-      // the state entering chunk jj + 1 (the final state after the last
-      // chunk): this product's state rows, rounded as the next product reads them
-      __bf16* ck = a.ckpt + static_cast<size_t>(bh * (N + 1) + jj + 1) * DK * dv;
-#pragma unroll
-      for (int q = 0; q < MPW; ++q) {
-        const int mt = wave * MPW + q;
-        if (mt < DK / 16) {
-#pragma unroll
-          for (int nt = 0; nt < NTN; ++nt) {
-            const int i0 = mt * 16 + 4 * lg, c = nt * 16 + lr;
-            const bf16x4 h = to_bf16x4(acc[q][nt]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ck[(i0 + e) * dv + c0 + c] = h[e];
-          }
         }
       }
     }
@@ -1174,10 +1179,10 @@ hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out
   const int nvt = p.dv / BV;
   const int64_t groups = (p.BH + 7) / 8;
   const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD, CK>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  constexpr int lds = CK ? Cfg::LDS_CK : Cfg::LDS;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD, CK>), dim3(groups * 8 * nvt), dim3(Cfg::NT), Cfg::LDS,
-                     s, a);
+  hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD, CK>), dim3(groups * 8 * nvt), dim3(Cfg::NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1237,6 +1242,8 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
   if (p.BH == 0) return hipSuccess;
   if (ckpt) {
     // the boundary-state instance: states instead of output rows
+    if (p.dk == 128 && p.BH * (p.dv / 64) >= 256)
+      return launch_scan<128, 64, 12, 2, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
     if (p.dk == 128) return launch_scan<128, 32, 4, 2, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
     if (p.dk == 64) return launch_scan<64, 16, 4, 4, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
     return hipErrorInvalidValue;
