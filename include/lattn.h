@@ -245,9 +245,15 @@ int lattn_loglinear_levels(int64_t seqlen);
  * with respect to every input, by the chain rule of the recurrence (the HDLA
  * note, "Key design 3", trains through it; the pages give no backward
  * formulas).  The state entering and the cotangent leaving every chunk come
- * from two chunk-level scans over the forward's chunk operators; each chunk's
- * tokens are then walked in reverse, all chunks in parallel.  As for
- * lattn_chunk_fwd, every chunk's cumulative -log-decay must stay within
+ * from two chunk-level scans over the forward's chunk operators; then every
+ * chunk's gradients are formed independently, all chunks in parallel:
+ *  - bf16 storage, chunk 64, r_kv = 1, r_ab <= 2, d_k and d_v in {64, 128}:
+ *    matrix products through the forward's decay-scaled WY factors (a forward
+ *    and an adjoint unit-lower solve per chunk) on bf16 MFMAs with fp32
+ *    accumulation; operands and the chunk-boundary states and cotangents are
+ *    rounded to bf16 as in the bf16 forward;
+ *  - every other shape: each chunk's tokens walked in reverse in fp32.
+ * As for lattn_chunk_fwd, every chunk's cumulative -log-decay must stay within
  * LATTN_MAX_CHUNK_LOG_DECAY (lattn_check_decay_range).
  * Inputs as lattn_chunk_fwd (initial_state NULL = zero), plus
  *   dout [B,H,T,d_v] in dims->dtype;  dfinal [B,H,d_k,d_v] fp32 or NULL (zero).
