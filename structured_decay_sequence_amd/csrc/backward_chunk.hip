@@ -24,14 +24,19 @@
 //                    + rowdot(dS_end, S_end) on the chunk's last token.
 // S_in and dS_end come from the chunk-boundary scans.
 //
-// Kernels, each over all chunks: prep (G and the scaled operands, row-major
-// bf16), grouped products (the two right-hand sides, then the five gradients:
-// out = A W0 + sum_i s_i mask_i(A B_i^T) C_i), solve (the blocks of L and the
-// inverses of its unit diagonal blocks in LDS, then Y by forward and X by
-// backward substitution, one wave per 16 value columns), decay.  A product group stages
-// its chunk's B-side operands in LDS row-major, straight from where they live
-// (the prep's arrays, the V and dO rows of the sequence, the fp32 boundary
-// states); operands needed transposed are read with the transposing LDS read.
+// Kernels, each over all chunks, in order (the scaled operands come from the
+// forward's prepare kernel, which forms them anyway): G (base 2) and Gamma;
+// the grouped products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i of the
+// forward right-hand side, and of dV's first two terms with the adjoint
+// right-hand side; the solve (the blocks of L and the inverses of its unit
+// diagonal blocks in LDS, then Y by forward and X by backward substitution,
+// one wave per 16 value columns); the grouped products of dK with dA, of dQ
+// with dB, and of dV's last term.  A product group
+// stages its chunk's B-side operands in LDS row-major, straight from where
+// they live (the prepare's arrays, the V and dO rows of the sequence, the
+// bf16 boundary states and cotangents); operands needed transposed are read
+// with the transposing LDS read.  The gradient groups' epilogues also form
+// the log-decay gradient.
 // Every contraction uses one K order: K values 32 ks + 16 h + 4 g + e sit at
 // element 4 h + e of lane group g, so that a score tile pair in accumulator
 // layout is directly the A operand of the product that follows.
