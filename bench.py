@@ -386,6 +386,22 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1)
     flops = backward_flops(spec)
+    # The training pair: the forward that keeps the chunk operators and the
+    # decay-scaled operands, and the backward that reads them instead of
+    # running the prepare again (same inputs, same cotangents).
+    def timed(fn, reps=2):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        a.record(stream)
+        for _ in range(reps):
+            r = fn()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / reps, r
+    fwd_ms, (_, _, saved) = timed(lambda: lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=spec.chunk))
+    bwd_ms, _ = timed(lambda: lattn.chunk_bwd_saved(q, K, V, ld, A, B, dout, saved, chunk=spec.chunk, dfinal=dfin))
+    del saved
     return {
         "entry": "lattn_chunk_bwd",
         "kind": "chunked backward on bf16 MFMAs: boundary scans, forward and adjoint UT solves, gradient products",
@@ -395,6 +411,13 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
         "gflop": round(flops / 1e9, 2),
         "mfma_frac_bf16": round(flops / (ms / 1e3) / (PEAK["bf16_mfma_TFs"] * 1e12), 4),
         "ratio_to_forward": None,
+        "training_pair": {
+            "entries": "lattn_chunk_fwd_train + lattn_chunk_bwd_saved",
+            "fwd_train_ms": round(fwd_ms, 3),
+            "bwd_saved_ms": round(bwd_ms, 3),
+            "step_ms": round(fwd_ms + bwd_ms, 3),
+            "fwd_plus_bwd_ms": None,
+        },
     }
 
 
@@ -720,6 +743,9 @@ def main():
         print("[bench] backward leg", file=sys.stderr, flush=True)
         result["backward"] = backward_leg(spec, raw, inputs, torch, lattn, dev)
         result["backward"]["ratio_to_forward"] = round(result["backward"]["ms_per_step"] / result["ms_per_step"], 2)
+        # the same step through the plain calls: lattn_chunk_fwd, then lattn_chunk_bwd
+        result["backward"]["training_pair"]["fwd_plus_bwd_ms"] = round(
+            result["ms_per_step"] + result["backward"]["ms_per_step"], 3)
     if spec.name == workloads.HEADLINE and not args.no_loglinear:
         print("[bench] log-linear lift leg", file=sys.stderr, flush=True)
         result["loglinear"] = loglinear_leg(torch, lattn, dev, max(1, args.steps // 4), min(args.warmup, 2))

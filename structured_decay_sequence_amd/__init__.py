@@ -21,6 +21,7 @@ __all__ = [
     "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
     "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
     "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd", "loglinear_fwd", "loglinear_levels", "chunk_bwd",
+    "chunk_fwd_train", "chunk_bwd_saved", "train_saved_size",
 ]
 
 
@@ -289,15 +290,9 @@ def loglinear_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: 
     return out
 
 
-def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
-              A: Optional[torch.Tensor], B: Optional[torch.Tensor], dout: torch.Tensor, chunk: int = 64,
-              dfinal: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
-    """Backward pass of chunk_fwd (lattn_chunk_bwd): gradients of
-    sum <dout, out> + <dfinal, final_state>.  Inputs as chunk_fwd plus dout
-    [B,H,T,dv] (dtype of q) and dfinal [B,H,dk,dv] fp32 or None.  Returns fp32
-    tensors dq, dk, dv, dlog_decay, dA, dB (None when A is None), dinitial_state,
-    each shaped like its input (k, v with the rank axis)."""
+def _bwd_inputs(q, k, v, log_decay, A, B, dout, dfinal, initial_state):
+    """Checks chunk_bwd's inputs; returns (k, v with the rank axis, r_ab, r_kv,
+    the fp32 gradient tensors)."""
     Bb, H, T, dk = q.shape
     dt = q.dtype
     lead = (Bb, H)
@@ -324,8 +319,22 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torc
              dA=None if A is None else torch.empty(tuple(A.shape), **f32),
              dB=None if A is None else torch.empty(tuple(A.shape), **f32),
              dinitial_state=torch.empty((Bb, H, dk, dv), **f32))
+    return k, v, r_ab, r_kv, g
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+              A: Optional[torch.Tensor], B: Optional[torch.Tensor], dout: torch.Tensor, chunk: int = 64,
+              dfinal: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Backward pass of chunk_fwd (lattn_chunk_bwd): gradients of
+    sum <dout, out> + <dfinal, final_state>.  Inputs as chunk_fwd plus dout
+    [B,H,T,dv] (dtype of q) and dfinal [B,H,dk,dv] fp32 or None.  Returns fp32
+    tensors dq, dk, dv, dlog_decay, dA, dB (None when A is None), dinitial_state,
+    each shaped like its input (k, v with the rank axis)."""
+    k, v, r_ab, r_kv, g = _bwd_inputs(q, k, v, log_decay, A, B, dout, dfinal, initial_state)
+    Bb, H, T, dk = q.shape
     lib = _lib.load()
-    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+    dims = make_dims(Bb, H, T, dk, v.shape[-1], _dtype_code(q), log_decay.dim() == 3)
     if workspace is None:
         workspace = _workspace(q.device, int(lib.lattn_chunk_bwd_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk)))
     rc = lib.lattn_chunk_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A), _ptr(B), r_ab,
@@ -334,6 +343,78 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torc
                              _ptr(g["dinitial_state"]), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                              _stream(q.device))
     _lib.check(rc, "lattn_chunk_bwd")
+    return g
+
+
+def train_saved_size(batch, heads, seqlen, d_k, d_v, r_ab, r_kv, chunk=64, dtype=torch.bfloat16,
+                     scalar_decay=False) -> int:
+    """Bytes of the buffer chunk_fwd_train keeps for chunk_bwd_saved (0 where the
+    shape is off the training pair's route: then use chunk_fwd and chunk_bwd)."""
+    code = LATTN_BF16 if dtype == torch.bfloat16 else LATTN_FP32
+    dims = make_dims(batch, heads, seqlen, d_k, d_v, code, scalar_decay)
+    return int(_lib.load().lattn_chunk_fwd_train_saved_size(ctypes.byref(dims), r_ab, r_kv, chunk))
+
+
+def chunk_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+                    A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None, chunk: int = 64,
+                    initial_state: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The training forward (lattn_chunk_fwd_train): chunk_fwd's results, plus
+    the uint8 buffer `saved` that chunk_bwd_saved reads instead of forming the
+    chunk operators and the decay-scaled operands again.  Returns (out,
+    final_state, saved)."""
+    Bb, H, T, dk = q.shape
+    dt = q.dtype
+    lead = (Bb, H)
+    k = _ranked(k, lead, T, dk)
+    v = _ranked(v, lead, T, None)
+    r_kv, dv = k.shape[-2], v.shape[-1]
+    _need(q, dt, (Bb, H, T, dk), "q")
+    _need(k, dt, (Bb, H, T, r_kv, dk), "k")
+    _need(v, dt, (Bb, H, T, r_kv, dv), "v")
+    scalar = log_decay.dim() == 3
+    _need(log_decay, torch.float32, (Bb, H, T) if scalar else (Bb, H, T, dk), "log_decay")
+    r_ab = 0
+    if A is not None:
+        r_ab = A.shape[-2]
+        _need(A, dt, (Bb, H, T, r_ab, dk), "A")
+        _need(B, dt, (Bb, H, T, r_ab, dk), "B")
+    if initial_state is not None:
+        _need(initial_state, torch.float32, (Bb, H, dk, dv), "initial_state")
+    out = torch.empty((Bb, H, T, dv), dtype=dt, device=q.device)
+    final_state = torch.empty((Bb, H, dk, dv), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), scalar)
+    if saved is None:
+        saved = _workspace(q.device, int(lib.lattn_chunk_fwd_train_saved_size(ctypes.byref(dims), r_ab, r_kv,
+                                                                               chunk)))
+    rc = lib.lattn_chunk_fwd_train(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A), _ptr(B),
+                                   r_ab, r_kv, chunk, _ptr(out), _ptr(final_state), _ptr(initial_state), _ptr(saved),
+                                   0 if saved is None else saved.numel(), _stream(q.device))
+    _lib.check(rc, "lattn_chunk_fwd_train")
+    return out, final_state, saved
+
+
+def chunk_bwd_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
+                    A: Optional[torch.Tensor], B: Optional[torch.Tensor], dout: torch.Tensor, saved: torch.Tensor,
+                    chunk: int = 64, dfinal: Optional[torch.Tensor] = None,
+                    initial_state: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """The training backward (lattn_chunk_bwd_saved): chunk_bwd's gradients,
+    reading what chunk_fwd_train left in `saved` for the same inputs."""
+    k, v, r_ab, r_kv, g = _bwd_inputs(q, k, v, log_decay, A, B, dout, dfinal, initial_state)
+    Bb, H, T, dk = q.shape
+    lib = _lib.load()
+    dims = make_dims(Bb, H, T, dk, v.shape[-1], _dtype_code(q), log_decay.dim() == 3)
+    if workspace is None:
+        workspace = _workspace(q.device, int(lib.lattn_chunk_bwd_saved_workspace_size(ctypes.byref(dims), r_ab, r_kv,
+                                                                                        chunk)))
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A), _ptr(B),
+                                   r_ab, r_kv, chunk, _ptr(dout), _ptr(dfinal), _ptr(initial_state), _ptr(saved),
+                                   0 if saved is None else saved.numel(), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                   _ptr(g["dlog_decay"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dinitial_state"]),
+                                   _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q.device))
+    _lib.check(rc, "lattn_chunk_bwd_saved")
     return g
 
 

@@ -245,6 +245,41 @@ int check_hla_chunk(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
   return LATTN_OK;
 }
 
+// The pointer checks both backward entry points share.
+int check_bwd_args(const lattn_dims* dims, const void* q, const void* k, const void* v, const float* log_decay,
+                   const void* A, const void* B, int r_ab, int r_kv, int chunk, const void* dout,
+                   const float* dfinal, const float* initial_state, const float* dq, const float* dk,
+                   const float* dv, const float* dlog_decay, const float* dA, const float* dB,
+                   const float* dinitial_state) {
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", need));
+  LATTN_TRY(check_ptr(dout, "dout", need));
+  LATTN_TRY(check_ptr(dfinal, "dfinal", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  LATTN_TRY(check_ptr(dq, "dq", need));
+  LATTN_TRY(check_ptr(dk, "dk", need));
+  LATTN_TRY(check_ptr(dv, "dv", need));
+  LATTN_TRY(check_ptr(dlog_decay, "dlog_decay", need));
+  LATTN_TRY(check_ptr(dinitial_state, "dinitial_state", true));
+  if (r_ab == 0) {
+    if (dA != nullptr || dB != nullptr) return fail(LATTN_EINVAL, "dA and dB must be NULL when r_ab == 0");
+  } else {
+    LATTN_TRY(check_ptr(dA, "dA", need));
+    LATTN_TRY(check_ptr(dB, "dB", need));
+  }
+  return LATTN_OK;
+}
+
+// The training pair's route: the chunked backward's shapes.
+int check_train_route(const lattn::Problem& p, const char* who) {
+  if (!lattn::backward_chunked(p))
+    return fail(LATTN_EUNSUPPORTED, "%s needs bf16 storage, chunk 64, r_kv 1, r_ab <= 2 and d_k, d_v in {64, 128} "
+                "(got d_k %d, d_v %d, r_ab %d, r_kv %d, chunk %d); use lattn_chunk_fwd and lattn_chunk_bwd", who,
+                p.dk, p.dv, p.r_ab, p.r_kv, p.C);
+  return LATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,23 +425,9 @@ int lattn_chunk_bwd(const lattn_dims* dims, const void* q, const void* k, const 
                     const void* dout, const float* dfinal, const float* initial_state, float* dq, float* dk,
                     float* dv, float* dlog_decay, float* dA, float* dB, float* dinitial_state, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  LATTN_TRY(check_bwd_args(dims, q, k, v, log_decay, A, B, r_ab, r_kv, chunk, dout, dfinal, initial_state, dq, dk,
+                           dv, dlog_decay, dA, dB, dinitial_state));
   const bool need = dims->seqlen > 0;
-  LATTN_TRY(check_ptr(q, "q", need));
-  LATTN_TRY(check_ptr(dout, "dout", need));
-  LATTN_TRY(check_ptr(dfinal, "dfinal", false));
-  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
-  LATTN_TRY(check_ptr(dq, "dq", need));
-  LATTN_TRY(check_ptr(dk, "dk", need));
-  LATTN_TRY(check_ptr(dv, "dv", need));
-  LATTN_TRY(check_ptr(dlog_decay, "dlog_decay", need));
-  LATTN_TRY(check_ptr(dinitial_state, "dinitial_state", true));
-  if (r_ab == 0) {
-    if (dA != nullptr || dB != nullptr) return fail(LATTN_EINVAL, "dA and dB must be NULL when r_ab == 0");
-  } else {
-    LATTN_TRY(check_ptr(dA, "dA", need));
-    LATTN_TRY(check_ptr(dB, "dB", need));
-  }
   const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
   if (!lattn::backward_supported(p))
     return fail(LATTN_EUNSUPPORTED, "lattn_chunk_bwd needs d_k, d_v <= 128, r_ab <= 4, r_kv <= 2 "
@@ -419,6 +440,69 @@ int lattn_chunk_bwd(const lattn_dims* dims, const void* q, const void* k, const 
   LATTN_TRY(hip_status(lattn::launch_backward(p, q, k, v, log_decay, A, B, dout, dfinal, initial_state, dq, dk, dv,
                                               dlog_decay, dA, dB, dinitial_state, workspace, stream),
                        "backward launch"));
+  return ok();
+}
+
+size_t lattn_chunk_fwd_train_saved_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return 0;
+  return lattn::backward_saved_bytes(make_problem(dims, r_ab, r_kv, chunk));
+}
+
+size_t lattn_chunk_bwd_saved_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {
+  if (check_dims(dims) != LATTN_OK || check_ranks(r_ab, r_kv) != LATTN_OK ||
+      check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
+    return 0;
+  return lattn::backward_saved_workspace_bytes(make_problem(dims, r_ab, r_kv, chunk));
+}
+
+int lattn_chunk_fwd_train(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                          const float* log_decay, const void* A, const void* B, int r_ab, int r_kv, int chunk,
+                          void* out, float* final_state, const float* initial_state, void* saved,
+                          size_t saved_bytes, hipStream_t stream) {
+  LATTN_TRY(check_operands(dims, k, v, log_decay, A, B, r_ab, r_kv, chunk));
+  const bool need = dims->seqlen > 0;
+  LATTN_TRY(check_ptr(q, "q", need));
+  LATTN_TRY(check_ptr(out, "out", need));
+  LATTN_TRY(check_ptr(final_state, "final_state", false));
+  LATTN_TRY(check_ptr(initial_state, "initial_state", false));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  LATTN_TRY(check_train_route(p, "lattn_chunk_fwd_train"));
+  if (p.T == 0) return hip_status(lattn::launch_copy_state(p, initial_state, final_state, stream), "copy state");
+  const size_t need_b = lattn::backward_saved_bytes(p);
+  if (saved == nullptr || saved_bytes < need_b)
+    return fail(LATTN_EWORKSPACE, "saved has %zu bytes, %zu needed", saved_bytes, need_b);
+  LATTN_TRY(check_ptr(saved, "saved", true));
+  LATTN_TRY(hip_status(lattn::launch_forward_train(p, q, k, v, log_decay, A, B, out, final_state, initial_state,
+                                                   saved, stream),
+                       "training forward launch"));
+  return ok();
+}
+
+int lattn_chunk_bwd_saved(const lattn_dims* dims, const void* q, const void* k, const void* v,
+                          const float* log_decay, const void* A, const void* B, int r_ab, int r_kv, int chunk,
+                          const void* dout, const float* dfinal, const float* initial_state, const void* saved,
+                          size_t saved_bytes, float* dq, float* dk, float* dv, float* dlog_decay, float* dA,
+                          float* dB, float* dinitial_state, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  LATTN_TRY(check_bwd_args(dims, q, k, v, log_decay, A, B, r_ab, r_kv, chunk, dout, dfinal, initial_state, dq, dk,
+                           dv, dlog_decay, dA, dB, dinitial_state));
+  const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
+  LATTN_TRY(check_train_route(p, "lattn_chunk_bwd_saved"));
+  if (p.T == 0) return hip_status(lattn::launch_copy_state(p, dfinal, dinitial_state, stream), "copy state");
+  const size_t need_b = lattn::backward_saved_bytes(p);
+  if (saved == nullptr || saved_bytes < need_b)
+    return fail(LATTN_EWORKSPACE, "saved has %zu bytes, %zu needed", saved_bytes, need_b);
+  LATTN_TRY(check_ptr(saved, "saved", true));
+  const size_t ws = lattn::backward_saved_workspace_bytes(p);
+  if (workspace == nullptr || workspace_bytes < ws)
+    return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
+  LATTN_TRY(check_ptr(workspace, "workspace", true));
+  LATTN_TRY(hip_status(lattn::launch_backward_saved(p, q, k, v, log_decay, A, B, dout, dfinal, initial_state, saved,
+                                                    dq, dk, dv, dlog_decay, dA, dB, dinitial_state, workspace,
+                                                    stream),
+                       "saved-state backward launch"));
   return ok();
 }
 

@@ -110,11 +110,32 @@ struct BcBufs {
 
 size_t bc_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Lays the buffers out in ws (nullptr: only count).  Returns the bytes used.
-size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
+// The decay-scaled operands Q~, K~, A~, B~ laid out from base (nullptr: only
+// count).  Returns the bytes used.
+size_t bc_ops_layout(const Problem& p, char* base, PrepBwOut* o) {
+  const size_t J = static_cast<size_t>(p.BH * p.N);
+  const size_t cdk = static_cast<size_t>(kCC) * p.dk, adk = static_cast<size_t>(kCC) * p.r_ab * p.dk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = base ? base + off : nullptr;
+    off += bc_align(bytes);
+    return r;
+  };
+  PrepBwOut t{};
+  t.qt = take(J * cdk * 2);
+  t.kt = take(J * cdk * 2);
+  t.at = take(J * adk * 2);
+  t.bt = take(J * adk * 2);
+  if (o) *o = t;
+  return off;
+}
+
+// Lays the buffers out in ws (nullptr: only count); with ops given, the
+// scaled operands live there instead of in ws.  Returns the bytes used.
+size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = nullptr) {
   const size_t J = static_cast<size_t>(p.BH * p.N);
   const size_t NA = static_cast<size_t>(kCC) * p.r_ab;
-  const size_t cdk = static_cast<size_t>(kCC) * p.dk, adk = NA * p.dk, ndv = NA * p.dv;
+  const size_t cdk = static_cast<size_t>(kCC) * p.dk, ndv = NA * p.dv;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* r = ws ? ws + off : nullptr;
@@ -124,10 +145,16 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b) {
   BcBufs t{};
   t.gc = reinterpret_cast<float*>(take(J * cdk * 4));
   t.gam = reinterpret_cast<float*>(take(J * p.dk * 4));
-  t.qt = reinterpret_cast<__bf16*>(take(J * cdk * 2));
-  t.kt = reinterpret_cast<__bf16*>(take(J * cdk * 2));
-  t.at = reinterpret_cast<__bf16*>(take(J * adk * 2));
-  t.bt = reinterpret_cast<__bf16*>(take(J * adk * 2));
+  PrepBwOut o{};
+  if (ops) {
+    o = *ops;
+  } else {
+    off += bc_ops_layout(p, ws ? ws + off : nullptr, &o);
+  }
+  t.qt = static_cast<__bf16*>(o.qt);
+  t.kt = static_cast<__bf16*>(o.kt);
+  t.at = static_cast<__bf16*>(o.at);
+  t.bt = static_cast<__bf16*>(o.bt);
   t.ry = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.rx = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
@@ -1246,12 +1273,23 @@ bool backward_chunked(const Problem& p) {
          (p.dv == 64 || p.dv == 128);
 }
 
-size_t backward_chunked_bytes(const Problem& p) { return bc_layout(p, nullptr, nullptr); }
+size_t backward_chunked_bytes(const Problem& p, bool own_ops) {
+  const PrepBwOut none{};
+  return bc_layout(p, nullptr, nullptr, own_ops ? nullptr : &none);
+}
 
 PrepBwOut backward_chunked_prep_out(const Problem& p, void* ws) {
   BcBufs w;
   bc_layout(p, static_cast<char*>(ws), &w);
   return PrepBwOut{w.qt, w.kt, w.at, w.bt};
+}
+
+size_t backward_chunked_ops_bytes(const Problem& p) { return bc_ops_layout(p, nullptr, nullptr); }
+
+PrepBwOut backward_chunked_ops_at(const Problem& p, void* base) {
+  PrepBwOut o{};
+  bc_ops_layout(p, static_cast<char*>(base), &o);
+  return o;
 }
 
 hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* dout, const float* dfinal, void* gend,
@@ -1270,11 +1308,11 @@ hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* do
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                                    const void* A, const void* B, const void* dout, const void* ckpt,
                                    const void* gend, float* dq, float* dK, float* dV, float* dld,
-                                   float* dA, float* dB, void* ws, hipStream_t s) {
+                                   float* dA, float* dB, void* ws, hipStream_t s, const PrepBwOut* ops) {
   if (p.BH * p.N == 0) return hipSuccess;
   if (!backward_chunked(p)) return hipErrorInvalidValue;
   BcBufs w;
-  bc_layout(p, static_cast<char*>(ws), &w);
+  bc_layout(p, static_cast<char*>(ws), &w, ops);
 #define LATTN_BC(DK_, DV_, RAB_)                                                                                  \
   if (p.dk == DK_ && p.dv == DV_ && p.r_ab == RAB_)                                                              \
     return launch_bc_t<DK_, DV_, RAB_>(p, w, q, k, v, ld, A, B, dout, ckpt, gend, dq, dK, dV, dld, dA, dB, s);

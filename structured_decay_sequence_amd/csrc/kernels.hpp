@@ -117,11 +117,16 @@ hipError_t launch_loglinear(const Problem& p, const void* q, const void* k, cons
 // d_k, d_v in {64, 128}), from the chunk-boundary states ckpt (bf16 [BH, N + 1,
 // dk, dv], fast_scan's boundary instance) and cotangents gend (bf16 [BH, N, dk,
 // dv]); writes every gradient but dS0 (which the reverse boundary scan gives).
-// ws: backward_chunked_bytes(p) bytes.
+// ws: backward_chunked_bytes(p, ops == nullptr) bytes (own_ops false: without
+// the scaled operands, which then come from elsewhere).
 bool backward_chunked(const Problem& p);
-size_t backward_chunked_bytes(const Problem& p);
+size_t backward_chunked_bytes(const Problem& p, bool own_ops = true);
 // Where, inside ws, fast_prepare_bw is to put the scaled operands.
 PrepBwOut backward_chunked_prep_out(const Problem& p, void* ws);
+// The scaled operands on their own, laid out from base: their bytes, and where
+// each goes.
+size_t backward_chunked_ops_bytes(const Problem& p);
+PrepBwOut backward_chunked_ops_at(const Problem& p, void* base);
 // The cotangent boundary scan of that route on bf16 MFMAs, over the bf16 MFMA
 // prepare's operators M: gend[j] (the cotangent leaving chunk j, bf16) for
 // every chunk, and dS0 (fp32).
@@ -130,7 +135,7 @@ hipError_t launch_backward_rscan(const Problem& p, const void* M, const void* do
 hipError_t launch_backward_chunked(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                                    const void* A, const void* B, const void* dout, const void* ckpt,
                                    const void* gend, float* dq, float* dK, float* dV, float* dld, float* dA,
-                                   float* dB, void* ws, hipStream_t s);
+                                   float* dB, void* ws, hipStream_t s, const PrepBwOut* ops = nullptr);
 
 // Backward pass, token-serial with chunk checkpoints: d_k, d_v <= 128,
 // r_ab <= 4, r_kv <= 2; gradients in fp32.
@@ -140,6 +145,20 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            const void* A, const void* B, const void* dout, const float* dfinal, const float* S0,
                            float* dq, float* dK, float* dV, float* dld, float* dA, float* dB, float* dS0,
                            void* workspace, hipStream_t s);
+// The training pair on the chunked route (backward_chunked(p)): a forward that
+// also keeps, in a caller-owned buffer of backward_saved_bytes(p) bytes, the
+// chunk operators and the decay-scaled operands its prepare forms; and a
+// backward that reads them there instead of forming them again (workspace:
+// backward_saved_workspace_bytes(p)).  Both sizes are 0 off that route.
+size_t backward_saved_bytes(const Problem& p);
+size_t backward_saved_workspace_bytes(const Problem& p);
+hipError_t launch_forward_train(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
+                                const void* A, const void* B, void* out, float* Sfin, const float* S0, void* saved,
+                                hipStream_t s);
+hipError_t launch_backward_saved(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
+                                 const void* A, const void* B, const void* dout, const float* dfinal,
+                                 const float* S0, const void* saved, float* dq, float* dK, float* dV, float* dld,
+                                 float* dA, float* dB, float* dS0, void* workspace, hipStream_t s);
 
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,
                        const float* ld, const void* A, const void* B, float* state, void* out,

@@ -152,3 +152,56 @@ def test_hla_and_loglinear_validation_before_launch():
     assert rc == _lib.LATTN_EUNSUPPORTED
     assert lib.lattn_hla_fwd_workspace_size(ctypes.byref(d), 2, 1, 64) > 0
     assert lib.lattn_loglinear_fwd_workspace_size(ctypes.byref(d), 2, 1, 64) > 0
+
+
+def test_training_pair_sizes_follow_the_chunked_route():
+    """lattn_chunk_fwd_train's saved buffer and lattn_chunk_bwd_saved's workspace
+    exist only on the chunked backward's route (bf16, chunk 64, r_kv 1,
+    r_ab <= 2, d_k and d_v in {64, 128}); the saved-state backward needs less
+    workspace than lattn_chunk_bwd, which forms the saved operands itself."""
+    lib = _lib.load()
+    on = _dims(seqlen=256)
+    saved = lib.lattn_chunk_fwd_train_saved_size(ctypes.byref(on), 2, 1, 64)
+    ws = lib.lattn_chunk_bwd_saved_workspace_size(ctypes.byref(on), 2, 1, 64)
+    assert saved > 0 and ws > 0
+    # the saved buffer holds at least the chunk operators the forward needs
+    assert saved > lib.lattn_chunk_fwd_workspace_size(ctypes.byref(on), 2, 1, 64)
+    assert ws < lib.lattn_chunk_bwd_workspace_size(ctypes.byref(on), 2, 1, 64)
+    longer = _dims(seqlen=512)
+    assert lib.lattn_chunk_fwd_train_saved_size(ctypes.byref(longer), 2, 1, 64) > saved
+    for dims, r_ab, r_kv, chunk in [(_dims(dtype=_lib.LATTN_FP32), 2, 1, 64), (on, 2, 1, 32), (on, 2, 2, 64),
+                                    (on, 3, 1, 64), (_dims(d_k=32, d_v=32), 2, 1, 64)]:
+        assert lib.lattn_chunk_fwd_train_saved_size(ctypes.byref(dims), r_ab, r_kv, chunk) == 0
+        assert lib.lattn_chunk_bwd_saved_workspace_size(ctypes.byref(dims), r_ab, r_kv, chunk) == 0
+
+
+def test_training_pair_validation_before_launch():
+    """Off-route shapes and short buffers are rejected on the host, before any
+    device work (the pointers are never dereferenced)."""
+    lib = _lib.load()
+    f = FAKE
+    fp32 = _dims(dtype=_lib.LATTN_FP32)
+    rc = lib.lattn_chunk_fwd_train(ctypes.byref(fp32), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, 1 << 30, None)
+    assert rc == _lib.LATTN_EUNSUPPORTED
+    assert b"lattn_chunk_fwd_train" in lib.lattn_last_error()
+    on = _dims()
+    need = lib.lattn_chunk_fwd_train_saved_size(ctypes.byref(on), 2, 1, 64)
+    rc = lib.lattn_chunk_fwd_train(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need - 1, None)
+    assert rc == _lib.LATTN_EWORKSPACE
+    rc = lib.lattn_chunk_fwd_train(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, None, None, need, None)
+    assert rc == _lib.LATTN_EWORKSPACE
+    ws = lib.lattn_chunk_bwd_saved_workspace_size(ctypes.byref(on), 2, 1, 64)
+    grads = [f] * 7
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need - 1, *grads,
+                                   f, ws, None)
+    assert rc == _lib.LATTN_EWORKSPACE
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need, *grads,
+                                   f, ws - 1, None)
+    assert rc == _lib.LATTN_EWORKSPACE
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(fp32), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need, *grads,
+                                   f, ws, None)
+    assert rc == _lib.LATTN_EUNSUPPORTED
+    # r_ab == 0 takes no dA, dB
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, None, None, 0, 1, 64, f, None, None, f, need,
+                                   f, f, f, f, f, f, f, f, ws, None)
+    assert rc == _lib.LATTN_EINVAL

@@ -1,0 +1,109 @@
+"""GPU checks of the training pair (lattn_chunk_fwd_train, lattn_chunk_bwd_saved)
+through the C ABI: the training forward's results equal lattn_chunk_fwd's and
+the saved-state backward's gradients equal lattn_chunk_bwd's, bit for bit
+(the same kernels on the same operands), and both meet the oracle's gate.
+
+Gate against the oracle: max|gpu - ref| / max|ref| <= 2e-2 (bf16 storage, fp32
+arithmetic and fp32 gradients).
+"""
+import numpy as np
+import pytest
+
+from oracle import backward as bwd_oracle
+import oracle
+import workloads
+from tests.helpers import TOL, dev, host, rel_err
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+lattn = pytest.importorskip("structured_decay_sequence_amd")
+
+BF = torch.bfloat16
+PAIRS = [("dq", "dq"), ("dk", "dK"), ("dv", "dV"), ("dlog_decay", "dlog_decay"), ("dA", "dA"), ("dB", "dB"),
+         ("dinitial_state", "dS0")]
+
+# B, H, T, dk, dv, r_ab, decay, state terms: every instance of the chunked
+# route's kernels (d_k, d_v in {64, 128}, r_ab 0..2), ragged tails, one chunk
+CASES = [
+    (1, 2, 150, 64, 64, 2, "channel", True),
+    (1, 1, 200, 128, 128, 2, "channel", True),
+    (2, 1, 100, 64, 128, 0, "channel", False),
+    (1, 1, 130, 128, 64, 1, "scalar", True),
+    (2, 3, 700, 64, 64, 1, "scalar", True),
+    (1, 1, 64, 128, 128, 2, "scalar", False),
+    (1, 1, 1, 64, 64, 2, "channel", True),
+]
+
+
+def _inputs(case):
+    Bb, H, T, dk, dv, r_ab, decay, state = case
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, r_ab, 1, "bf16", decay, seed=T + 3 * dk)
+    rng = np.random.default_rng(T + 1)
+    dout = workloads.round_bf16(rng.standard_normal((Bb, H, T, dv)).astype(np.float32))
+    S0 = (rng.standard_normal((Bb, H, dk, dv)) * 0.1).astype(np.float32) if state else None
+    dfin = rng.standard_normal((Bb, H, dk, dv)).astype(np.float32) if state else None
+    return raw, dout, S0, dfin
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}-{}s{}".format(*c))
+def test_training_pair_matches_the_plain_calls(case):
+    print(f"training pair case {case}", flush=True)
+    raw, dout, S0, dfin = _inputs(case)
+    q, K, V = dev(raw["q"], BF), dev(raw["K"], BF), dev(raw["V"], BF)
+    ld, A, B = dev(raw["log_decay"]), dev(raw["A"], BF), dev(raw["B"], BF)
+    S0d, dfd, dod = dev(S0), dev(dfin), dev(dout, BF)
+    out, fin = lattn.chunk_fwd(q, K, V, ld, A, B, chunk=64, initial_state=S0d)
+    out_t, fin_t, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=64, initial_state=S0d)
+    g = lattn.chunk_bwd(q, K, V, ld, A, B, dod, chunk=64, dfinal=dfd, initial_state=S0d)
+    g_s = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dod, saved, chunk=64, dfinal=dfd, initial_state=S0d)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_t)
+    assert torch.equal(fin, fin_t)
+    for n in g:
+        if g[n] is None:
+            assert g_s[n] is None, n
+        else:
+            assert torch.equal(g[n], g_s[n]), n
+    ref = bwd_oracle.backward(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"], dout, dfin, S0)
+    for gn, rn in PAIRS:
+        if ref[rn] is None:
+            continue
+        e = rel_err(host(g_s[gn]), ref[rn])
+        print(f"{gn} {e:.2e}", flush=True)
+        assert e <= TOL["bf16"], gn
+    ref_out, ref_S = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"],
+                                    initial_state=S0)
+    assert rel_err(host(out_t), ref_out) <= TOL["bf16"]
+    assert rel_err(host(fin_t), ref_S) <= TOL["bf16"]
+
+
+def test_saved_buffer_survives_other_calls():
+    """The saved buffer is the caller's: other library calls in between (which
+    use their own workspaces) leave the saved-state backward's result unchanged."""
+    raw, dout, S0, dfin = _inputs((1, 2, 300, 64, 64, 2, "channel", True))
+    q, K, V = dev(raw["q"], BF), dev(raw["K"], BF), dev(raw["V"], BF)
+    ld, A, B = dev(raw["log_decay"]), dev(raw["A"], BF), dev(raw["B"], BF)
+    _, _, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=64, initial_state=dev(S0))
+    first = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dev(dout, BF), saved, chunk=64, dfinal=dev(dfin),
+                                  initial_state=dev(S0))
+    # unrelated work on other inputs
+    other = workloads.generic_raw(1, 2, 300, 64, 64, 2, 1, "bf16", "channel", seed=99)
+    lattn.chunk_fwd(dev(other["q"], BF), dev(other["K"], BF), dev(other["V"], BF), dev(other["log_decay"]),
+                    dev(other["A"], BF), dev(other["B"], BF), chunk=64)
+    lattn.chunk_bwd(dev(other["q"], BF), dev(other["K"], BF), dev(other["V"], BF), dev(other["log_decay"]),
+                    dev(other["A"], BF), dev(other["B"], BF), dev(dout, BF), chunk=64)
+    second = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dev(dout, BF), saved, chunk=64, dfinal=dev(dfin),
+                                   initial_state=dev(S0))
+    torch.cuda.synchronize()
+    for n in first:
+        if first[n] is not None:
+            assert torch.equal(first[n], second[n]), n
+
+
+def test_training_pair_rejects_off_route_shapes():
+    raw = workloads.generic_raw(1, 1, 64, 64, 64, 2, 1, "fp32", "channel", seed=0)
+    with pytest.raises(lattn.LattnError):
+        lattn.chunk_fwd_train(dev(raw["q"]), dev(raw["K"]), dev(raw["V"]), dev(raw["log_decay"]), dev(raw["A"]),
+                              dev(raw["B"]), chunk=64)
+    assert lattn.train_saved_size(1, 1, 64, 64, 64, 2, 1, 64, dtype=torch.float32) == 0
