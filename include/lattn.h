@@ -277,9 +277,10 @@ size_t lattn_chunk_bwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv
  * lattn_chunk_fwd_train / lattn_chunk_bwd_saved -- the training pair: the
  * forward of lattn_chunk_fwd, which also keeps in `saved` what the chunked
  * backward would otherwise form again from the inputs (the chunk operators
- * M_j and the decay-scaled operands q e^{G}, k e^{-G}, A e^{-G}, B e^{G_{t-1}}
- * of every chunk; the HDLA note, "Key design 3", trains through the chunk-wise
- * form), and the backward of lattn_chunk_bwd reading them there.
+ * M_j, the decay-scaled operands q e^{G}, k e^{-G}, A e^{-G}, B e^{G_{t-1}} and
+ * the state entering every chunk; the HDLA note, "Key design 3", trains
+ * through the chunk-wise form), and the backward of lattn_chunk_bwd reading
+ * them there.
  * Only on the chunked backward's route: bf16 storage, chunk 64, r_kv = 1,
  * r_ab <= 2, d_k and d_v in {64, 128} (LATTN_EUNSUPPORTED elsewhere; there
  * lattn_chunk_fwd_train_saved_size returns 0, and a caller uses
@@ -289,8 +290,9 @@ size_t lattn_chunk_bwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv
  *   saved: caller-owned device memory of lattn_chunk_fwd_train_saved_size()
  *   bytes, fully written; no other workspace is needed.
  * lattn_chunk_bwd_saved: arguments and results as lattn_chunk_bwd (equal to
- *   its results), plus saved as the forward with the same inputs left it
- *   (read only; the caller keeps it unchanged in between), and
+ *   its results), but no initial_state (the saved states carry it), plus
+ *   saved as the forward with the same inputs left it (read only; the caller
+ *   keeps it unchanged in between), and
  *   lattn_chunk_bwd_saved_workspace_size() bytes of caller-owned workspace.
  * The buffer's content is this library's private layout; it is valid for
  * the one set of inputs (q, k, log_decay, A, B and the shapes) it was made
@@ -302,8 +304,7 @@ int lattn_chunk_fwd_train(const lattn_dims* dims, const void* q, const void* k, 
                           size_t saved_bytes, hipStream_t stream);
 int lattn_chunk_bwd_saved(const lattn_dims* dims, const void* q, const void* k, const void* v,
                           const float* log_decay, const void* A, const void* B, int r_ab, int r_kv, int chunk,
-                          const void* dout, const float* dfinal, const float* initial_state, const void* saved,
-                          size_t saved_bytes, float* dq, float* dk, float* dv, float* dlog_decay, float* dA,
+                          const void* dout, const float* dfinal, const void* saved, size_t saved_bytes, float* dq, float* dk, float* dv, float* dlog_decay, float* dA,
                           float* dB, float* dinitial_state, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 /* Bytes of `saved` and of the saved-state backward's workspace (0 off the

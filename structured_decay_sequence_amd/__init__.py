@@ -398,11 +398,11 @@ def chunk_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay
 def chunk_bwd_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay: torch.Tensor,
                     A: Optional[torch.Tensor], B: Optional[torch.Tensor], dout: torch.Tensor, saved: torch.Tensor,
                     chunk: int = 64, dfinal: Optional[torch.Tensor] = None,
-                    initial_state: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None) -> Dict[str, Optional[torch.Tensor]]:
     """The training backward (lattn_chunk_bwd_saved): chunk_bwd's gradients,
-    reading what chunk_fwd_train left in `saved` for the same inputs."""
-    k, v, r_ab, r_kv, g = _bwd_inputs(q, k, v, log_decay, A, B, dout, dfinal, initial_state)
+    reading what chunk_fwd_train left in `saved` for the same inputs (the
+    initial state among them)."""
+    k, v, r_ab, r_kv, g = _bwd_inputs(q, k, v, log_decay, A, B, dout, dfinal, None)
     Bb, H, T, dk = q.shape
     lib = _lib.load()
     dims = make_dims(Bb, H, T, dk, v.shape[-1], _dtype_code(q), log_decay.dim() == 3)
@@ -410,7 +410,7 @@ def chunk_bwd_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_decay
         workspace = _workspace(q.device, int(lib.lattn_chunk_bwd_saved_workspace_size(ctypes.byref(dims), r_ab, r_kv,
                                                                                         chunk)))
     rc = lib.lattn_chunk_bwd_saved(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(A), _ptr(B),
-                                   r_ab, r_kv, chunk, _ptr(dout), _ptr(dfinal), _ptr(initial_state), _ptr(saved),
+                                   r_ab, r_kv, chunk, _ptr(dout), _ptr(dfinal), _ptr(saved),
                                    0 if saved is None else saved.numel(), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
                                    _ptr(g["dlog_decay"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dinitial_state"]),
                                    _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(q.device))

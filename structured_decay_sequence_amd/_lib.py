@@ -56,8 +56,8 @@ SIGNATURES = {
     "lattn_chunk_bwd_workspace_size": (_SZ, [_D, _I, _I, _I]),
     "lattn_chunk_fwd_train": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "lattn_chunk_fwd_train_saved_size": (_SZ, [_D, _I, _I, _I]),
-    "lattn_chunk_bwd_saved": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P,
-                                    _P, _P, _P, _SZ, _P]),
+    "lattn_chunk_bwd_saved": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _SZ, _P]),
     "lattn_chunk_bwd_saved_workspace_size": (_SZ, [_D, _I, _I, _I]),
     "lattn_step": (_I, [_D, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "lattn_hdla_params": (_I, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),

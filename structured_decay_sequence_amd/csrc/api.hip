@@ -482,12 +482,11 @@ int lattn_chunk_fwd_train(const lattn_dims* dims, const void* q, const void* k, 
 
 int lattn_chunk_bwd_saved(const lattn_dims* dims, const void* q, const void* k, const void* v,
                           const float* log_decay, const void* A, const void* B, int r_ab, int r_kv, int chunk,
-                          const void* dout, const float* dfinal, const float* initial_state, const void* saved,
-                          size_t saved_bytes, float* dq, float* dk, float* dv, float* dlog_decay, float* dA,
+                          const void* dout, const float* dfinal, const void* saved, size_t saved_bytes, float* dq, float* dk, float* dv, float* dlog_decay, float* dA,
                           float* dB, float* dinitial_state, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-  LATTN_TRY(check_bwd_args(dims, q, k, v, log_decay, A, B, r_ab, r_kv, chunk, dout, dfinal, initial_state, dq, dk,
-                           dv, dlog_decay, dA, dB, dinitial_state));
+  LATTN_TRY(check_bwd_args(dims, q, k, v, log_decay, A, B, r_ab, r_kv, chunk, dout, dfinal, nullptr, dq, dk, dv,
+                           dlog_decay, dA, dB, dinitial_state));
   const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
   LATTN_TRY(check_train_route(p, "lattn_chunk_bwd_saved"));
   if (p.T == 0) return hip_status(lattn::launch_copy_state(p, dfinal, dinitial_state, stream), "copy state");
@@ -499,7 +498,7 @@ int lattn_chunk_bwd_saved(const lattn_dims* dims, const void* q, const void* k, 
   if (workspace == nullptr || workspace_bytes < ws)
     return fail(LATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, ws);
   LATTN_TRY(check_ptr(workspace, "workspace", true));
-  LATTN_TRY(hip_status(lattn::launch_backward_saved(p, q, k, v, log_decay, A, B, dout, dfinal, initial_state, saved,
+  LATTN_TRY(hip_status(lattn::launch_backward_saved(p, q, k, v, log_decay, A, B, dout, dfinal, saved,
                                                     dq, dk, dv, dlog_decay, dA, dB, dinitial_state, workspace,
                                                     stream),
                        "saved-state backward launch"));

@@ -617,20 +617,21 @@ BwLayout bw_layout(const Problem& p) {
   return l;
 }
 
-// The training pair's saved buffer: the chunk operators, then the scaled
-// operands; the saved-state backward's workspace: boundary states and
-// cotangents, then the chunked kernels' buffers without the scaled operands.
+// The training pair's saved buffer: the chunk operators, the boundary states
+// (bf16, N + 1 per head), then the scaled operands; the saved-state backward's
+// workspace: the boundary cotangents, then the chunked kernels' buffers
+// without the scaled operands.
 struct SavedLayout {
-  size_t ops, scaled, total, ckpt, gend, chunk, ws_total;
+  size_t ckpt, scaled, total, chunk, ws_total;
 };
 SavedLayout saved_layout(const Problem& p) {
   SavedLayout l{};
   if (!backward_chunked(p)) return l;
   const size_t state = static_cast<size_t>(p.dk) * p.dv;
-  l.scaled = bw_align(fast_workspace_bytes(p));
+  l.ckpt = bw_align(fast_workspace_bytes(p));
+  l.scaled = l.ckpt + bw_align(static_cast<size_t>(p.BH * (p.N + 1)) * state * 2);
   l.total = l.scaled + backward_chunked_ops_bytes(p);
-  l.gend = bw_align(static_cast<size_t>(p.BH * (p.N + 1)) * state * 2);
-  l.chunk = l.gend + bw_align(static_cast<size_t>(p.BH * p.N) * state * 2);
+  l.chunk = bw_align(static_cast<size_t>(p.BH * p.N) * state * 2);
   l.ws_total = l.chunk + backward_chunked_bytes(p, false);
   return l;
 }
@@ -648,15 +649,16 @@ hipError_t launch_forward_train(const Problem& p, const void* q, const void* k, 
   const SavedLayout l = saved_layout(p);
   char* sv = static_cast<char*>(saved);
   // the backward instance of the prepare: the same operators, and the scaled
-  // operands kept beside them
+  // operands kept beside them; the scan's instance that also keeps the state
+  // entering every chunk
   hipError_t e = fast_prepare_bw(p, q, k, ld, A, B, sv, backward_chunked_ops_at(p, sv + l.scaled), s);
   if (e != hipSuccess) return e;
-  return fast_scan(p, sv, v, out, Sfin, S0, s);
+  return fast_scan(p, sv, v, out, Sfin, S0, s, sv + l.ckpt);
 }
 
 hipError_t launch_backward_saved(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                                  const void* A, const void* B, const void* dout, const float* dfinal,
-                                 const float* S0, const void* saved, float* dq, float* dK, float* dV, float* dld,
+                                 const void* saved, float* dq, float* dK, float* dV, float* dld,
                                  float* dA, float* dB, float* dS0, void* workspace, hipStream_t s) {
   if (p.BH == 0) return hipSuccess;
   if (!backward_chunked(p)) return hipErrorInvalidValue;
@@ -664,12 +666,11 @@ hipError_t launch_backward_saved(const Problem& p, const void* q, const void* k,
   char* ws = static_cast<char*>(workspace);
   const char* sv = static_cast<const char*>(saved);
   const PrepBwOut ops = backward_chunked_ops_at(p, const_cast<char*>(sv) + l.scaled);
-  hipError_t e = fast_scan(p, sv, v, nullptr, nullptr, S0, s, ws + l.ckpt);
+  // the cotangents leaving the chunks first, into the front of the workspace
+  hipError_t e = launch_backward_rscan(p, sv, dout, dfinal, ws, dS0, s);
   if (e != hipSuccess) return e;
-  e = launch_backward_rscan(p, sv, dout, dfinal, ws + l.gend, dS0, s);
-  if (e != hipSuccess) return e;
-  return launch_backward_chunked(p, q, k, v, ld, A, B, dout, ws + l.ckpt, ws + l.gend, dq, dK, dV, dld, dA, dB,
-                                 ws + l.chunk, s, &ops);
+  return launch_backward_chunked(p, q, k, v, ld, A, B, dout, sv + l.ckpt, ws, dq, dK, dV, dld, dA, dB, ws + l.chunk,
+                                 s, &ops);
 }
 
 namespace {

@@ -798,13 +798,15 @@ struct FastScanArgs {
   __bf16* ckpt;        // [BH, N + 1, dk, dv]: the state entering every chunk, then the final state (the boundary instance)
 };
 
-// CK: the boundary-state instance, which stores the state entering every
-// chunk instead of the output rows (the backward's forward scan).
-template <int DK, int BV, int NWV, int PD, bool CK>
+// CK: what the scan stores.  kScanOut: the output rows (and the final state);
+// kScanStates: the state entering every chunk instead of the output rows (the
+// backward's boundary scan); kScanBoth: both (the training forward).
+enum ScanStore { kScanOut = 0, kScanStates = 1, kScanBoth = 2 };
+template <int DK, int BV, int NWV, int PD, int CK>
 __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
   constexpr int KP = Cfg::KP, MPW = Cfg::MPW, NTN = Cfg::NTN, LDX = Cfg::LDX, NT = Cfg::NT;
-  constexpr int XBUF = Cfg::XBUF, LDO = Cfg::LDO, OBUF = CK ? Cfg::SBUF : Cfg::OBUF, MSZ = Cfg::MSZ;
+  constexpr int XBUF = Cfg::XBUF, LDO = Cfg::LDO, OBUF = CK == kScanStates ? Cfg::SBUF : Cfg::OBUF, MSZ = Cfg::MSZ;
   constexpr int VITEMS = Cfg::VITEMS, OITEMS = Cfg::OITEMS, OIT = Cfg::OIT;
   static_assert(Cfg::VIT == 1, "one V piece per thread");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -880,7 +882,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   // Output rows of chunk jj from a staging buffer to HBM (none past the end);
   // the boundary-state instance: the state leaving chunk jj (slot jj + 1).
   auto flush_out = [&](const __bf16* O, int64_t jj) {
-    if constexpr (CK) {
+    if constexpr (CK == kScanStates) {
       if (jj >= N) return;
       __bf16* ck = a.ckpt + static_cast<size_t>(bh * (N + 1) + jj + 1) * DK * dv + c0;
 #pragma unroll
@@ -909,7 +911,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     const int i = it / BV, c = it % BV;
     const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
     X0[c * LDX + kperm(i)] = (__bf16)s;
-    if (CK) a.ckpt[(static_cast<size_t>(bh * (N + 1)) * DK + i) * dv + c0 + c] = (__bf16)s;
+    if (CK == kScanStates) a.ckpt[(static_cast<size_t>(bh * (N + 1)) * DK + i) * dv + c0 + c] = (__bf16)s;
   }
   put_v(X0, vb[0], 0);
   // Ring invariant from here on: at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
@@ -956,16 +958,33 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
         if (mt < DK / 16) {
           const bf16x4 h = to_bf16x4(acc[q][nt]);
           *reinterpret_cast<bf16x4*>(Xn + c * LDX + kperm(mt * 16 + 4 * lg)) = h;
-          if (CK) {
+          if (CK == kScanStates) {
             // the state rows, rounded as the next product reads them, staged
             // row-major for the 16-byte stores one chunk later
 #pragma unroll
             for (int e = 0; e < 4; ++e) Oc[(mt * 16 + 4 * lg + e) * LDO + c] = h[e];
           }
-        } else if (!CK) {
+        } else if (CK != kScanStates) {
           const int t = (mt - DK / 16) * 16 + 4 * lg;
 #pragma unroll
           for (int e = 0; e < 4; ++e) Oc[(t + e) * LDO + c] = (__bf16)acc[q][nt][e];
+        }
+      }
+    }
+    if (CK == kScanBoth && jj == N - 1) {
+      // the state leaving the last chunk (slot N), rounded as the next
+      // product would read it
+      __bf16* ck = a.ckpt + static_cast<size_t>(bh * (N + 1) + N) * DK * dv + c0;
+#pragma unroll
+      for (int q = 0; q < MPW; ++q) {
+        const int mt = wave * MPW + q;
+        if (mt < DK / 16) {
+#pragma unroll
+          for (int nt = 0; nt < NTN; ++nt) {
+            const bf16x4 h = to_bf16x4(acc[q][nt]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ck[(mt * 16 + 4 * lg + e) * dv + nt * 16 + lr] = h[e];
+          }
         }
       }
     }
@@ -986,6 +1005,26 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     const int un = (u + 1) % 2;
     put_v(Xn, vb[un], jj + 1);
     load_v(vb[un], jj + 3);
+    if constexpr (CK == kScanBoth) {
+      // the state entering chunk jj (slot jj), from the operand buffer this
+      // step's product read (rewritten only after the barrier below): a
+      // thread gathers 8 columns of one row, consecutive threads take
+      // consecutive rows, so the 2-byte LDS reads of a wave hit distinct banks
+      if (jj < N) {
+        __bf16* ck = a.ckpt + static_cast<size_t>(bh * (N + 1) + jj) * DK * dv + c0;
+#pragma unroll
+        for (int q = 0; q < Cfg::SIT; ++q) {
+          const int it = tid + q * NT;
+          const int i = it % DK, cg = it / DK;
+          if (it < Cfg::SITEMS) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = Xc[(cg * 8 + e) * LDX + kperm(i)];
+            *reinterpret_cast<bf16x8*>(ck + (i * dv + cg * 8)) = w;
+          }
+        }
+      }
+    }
     lds_barrier();
   };
 
@@ -1170,7 +1209,7 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
                   : launch_prep<DK, RAB, false, kGeneric>(p, q, k, ld, A, B, nullptr, M, s);
 }
 
-template <int DK, int BV, int NWV, int PD, bool CK = false>
+template <int DK, int BV, int NWV, int PD, int CK = kScanOut>
 hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out, float* Sfin,
                        const float* S0, void* ckpt, hipStream_t s) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
@@ -1179,7 +1218,7 @@ hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out
   const int nvt = p.dv / BV;
   const int64_t groups = (p.BH + 7) / 8;
   const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD, CK>);
-  constexpr int lds = CK ? Cfg::LDS_CK : Cfg::LDS;
+  constexpr int lds = CK == kScanStates ? Cfg::LDS_CK : Cfg::LDS;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD, CK>), dim3(groups * 8 * nvt), dim3(Cfg::NT), lds, s, a);
@@ -1240,12 +1279,20 @@ hipError_t fast_prepare_fused(const Problem& p, int family, const void* q, const
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,
                      const float* S0, hipStream_t s, void* ckpt) {
   if (p.BH == 0) return hipSuccess;
-  if (ckpt) {
+  if (ckpt && !out) {
     // the boundary-state instance: states instead of output rows
     if (p.dk == 128 && p.BH * (p.dv / 64) >= 256)
-      return launch_scan<128, 64, 12, 2, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
-    if (p.dk == 128) return launch_scan<128, 32, 4, 2, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
-    if (p.dk == 64) return launch_scan<64, 16, 4, 4, true>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
+      return launch_scan<128, 64, 12, 2, kScanStates>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
+    if (p.dk == 128) return launch_scan<128, 32, 4, 2, kScanStates>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
+    if (p.dk == 64) return launch_scan<64, 16, 4, 4, kScanStates>(p, workspace, v, nullptr, Sfin, S0, ckpt, s);
+    return hipErrorInvalidValue;
+  }
+  if (ckpt) {
+    // output rows and the boundary states
+    if (p.dk == 128 && p.BH * (p.dv / 64) >= 256)
+      return launch_scan<128, 64, 12, 2, kScanBoth>(p, workspace, v, out, Sfin, S0, ckpt, s);
+    if (p.dk == 128) return launch_scan<128, 32, 4, 2, kScanBoth>(p, workspace, v, out, Sfin, S0, ckpt, s);
+    if (p.dk == 64) return launch_scan<64, 16, 4, 4, kScanBoth>(p, workspace, v, out, Sfin, S0, ckpt, s);
     return hipErrorInvalidValue;
   }
   // Wider d_v slices share each operator load among more columns; narrower

@@ -147,9 +147,10 @@ hipError_t launch_backward(const Problem& p, const void* q, const void* k, const
                            void* workspace, hipStream_t s);
 // The training pair on the chunked route (backward_chunked(p)): a forward that
 // also keeps, in a caller-owned buffer of backward_saved_bytes(p) bytes, the
-// chunk operators and the decay-scaled operands its prepare forms; and a
-// backward that reads them there instead of forming them again (workspace:
-// backward_saved_workspace_bytes(p)).  Both sizes are 0 off that route.
+// chunk operators and the decay-scaled operands its prepare forms and the
+// state entering every chunk; and a backward that reads them there instead of
+// forming them again (workspace: backward_saved_workspace_bytes(p)).  Both
+// sizes are 0 off that route.
 size_t backward_saved_bytes(const Problem& p);
 size_t backward_saved_workspace_bytes(const Problem& p);
 hipError_t launch_forward_train(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
@@ -157,7 +158,7 @@ hipError_t launch_forward_train(const Problem& p, const void* q, const void* k, 
                                 hipStream_t s);
 hipError_t launch_backward_saved(const Problem& p, const void* q, const void* k, const void* v, const float* ld,
                                  const void* A, const void* B, const void* dout, const float* dfinal,
-                                 const float* S0, const void* saved, float* dq, float* dK, float* dV, float* dld,
+                                 const void* saved, float* dq, float* dK, float* dV, float* dld,
                                  float* dA, float* dB, float* dS0, void* workspace, hipStream_t s);
 
 hipError_t launch_step(const Problem& p, const void* q, const void* k, const void* v,

@@ -192,16 +192,16 @@ def test_training_pair_validation_before_launch():
     assert rc == _lib.LATTN_EWORKSPACE
     ws = lib.lattn_chunk_bwd_saved_workspace_size(ctypes.byref(on), 2, 1, 64)
     grads = [f] * 7
-    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need - 1, *grads,
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, f, need - 1, *grads,
                                    f, ws, None)
     assert rc == _lib.LATTN_EWORKSPACE
-    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need, *grads,
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, f, f, 2, 1, 64, f, None, f, need, *grads,
                                    f, ws - 1, None)
     assert rc == _lib.LATTN_EWORKSPACE
-    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(fp32), f, f, f, f, f, f, 2, 1, 64, f, None, None, f, need, *grads,
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(fp32), f, f, f, f, f, f, 2, 1, 64, f, None, f, need, *grads,
                                    f, ws, None)
     assert rc == _lib.LATTN_EUNSUPPORTED
     # r_ab == 0 takes no dA, dB
-    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, None, None, 0, 1, 64, f, None, None, f, need,
+    rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, None, None, 0, 1, 64, f, None, f, need,
                                    f, f, f, f, f, f, f, f, ws, None)
     assert rc == _lib.LATTN_EINVAL

@@ -56,7 +56,7 @@ def test_training_pair_matches_the_plain_calls(case):
     out, fin = lattn.chunk_fwd(q, K, V, ld, A, B, chunk=64, initial_state=S0d)
     out_t, fin_t, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=64, initial_state=S0d)
     g = lattn.chunk_bwd(q, K, V, ld, A, B, dod, chunk=64, dfinal=dfd, initial_state=S0d)
-    g_s = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dod, saved, chunk=64, dfinal=dfd, initial_state=S0d)
+    g_s = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dod, saved, chunk=64, dfinal=dfd)
     torch.cuda.synchronize()
     assert torch.equal(out, out_t)
     assert torch.equal(fin, fin_t)
@@ -85,16 +85,14 @@ def test_saved_buffer_survives_other_calls():
     q, K, V = dev(raw["q"], BF), dev(raw["K"], BF), dev(raw["V"], BF)
     ld, A, B = dev(raw["log_decay"]), dev(raw["A"], BF), dev(raw["B"], BF)
     _, _, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=64, initial_state=dev(S0))
-    first = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dev(dout, BF), saved, chunk=64, dfinal=dev(dfin),
-                                  initial_state=dev(S0))
+    first = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dev(dout, BF), saved, chunk=64, dfinal=dev(dfin))
     # unrelated work on other inputs
     other = workloads.generic_raw(1, 2, 300, 64, 64, 2, 1, "bf16", "channel", seed=99)
     lattn.chunk_fwd(dev(other["q"], BF), dev(other["K"], BF), dev(other["V"], BF), dev(other["log_decay"]),
                     dev(other["A"], BF), dev(other["B"], BF), chunk=64)
     lattn.chunk_bwd(dev(other["q"], BF), dev(other["K"], BF), dev(other["V"], BF), dev(other["log_decay"]),
                     dev(other["A"], BF), dev(other["B"], BF), dev(dout, BF), chunk=64)
-    second = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dev(dout, BF), saved, chunk=64, dfinal=dev(dfin),
-                                   initial_state=dev(S0))
+    second = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dev(dout, BF), saved, chunk=64, dfinal=dev(dfin))
     torch.cuda.synchronize()
     for n in first:
         if first[n] is not None:
