@@ -101,6 +101,8 @@ struct BcBufs {
   float* gam;                // [dk] e^{G} at the chunk's last token
   __bf16 *qt, *kt;           // [C][dk]
   __bf16 *at, *bt;           // [NA][dk]
+  __bf16* lt;                // [NB (NB - 1) / 2][16][16] L below the diagonal blocks (bf16 tiles)
+  float* di;                 // [NB][16][16] the inverses of the diagonal blocks I + L_ii (fp32)
   __bf16 *ry, *rx;           // right-hand sides in tile order [NA/16][dv/16][64 lanes][4], bf16
   __bf16 *y, *x;             // [NA][dv]
   float* gk;                 // [C][dk] the decay gradient's terms of the dK group
@@ -121,11 +123,14 @@ size_t bc_ops_layout(const Problem& p, char* base, PrepBwOut* o) {
     off += bc_align(bytes);
     return r;
   };
+  const size_t nb = static_cast<size_t>(kCC) * p.r_ab / 16;
   PrepBwOut t{};
   t.qt = take(J * cdk * 2);
   t.kt = take(J * cdk * 2);
   t.at = take(J * adk * 2);
   t.bt = take(J * adk * 2);
+  t.lt = take(J * (nb * (nb > 0 ? nb - 1 : 0) / 2) * 256 * 2);
+  t.di = take(J * nb * 256 * 4);
   if (o) *o = t;
   return off;
 }
@@ -155,6 +160,8 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
   t.kt = static_cast<__bf16*>(o.kt);
   t.at = static_cast<__bf16*>(o.at);
   t.bt = static_cast<__bf16*>(o.bt);
+  t.lt = static_cast<__bf16*>(o.lt);
+  t.di = static_cast<float*>(o.di);
   t.ry = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.rx = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
@@ -839,19 +846,17 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// tri + solve: one workgroup per chunk, one wave per (Y or X, 16 value columns).
-//  * The blocks (i, j <= i) of L = M_<(Bt At^T) (rank rows; tokens row / r_ab)
-//    are formed into LDS: below the diagonal as 16x16 bf16 tiles in both
-//    orientations (each from its own product, so every tile is written with
-//    8-byte stores); the diagonal blocks in fp32, then the inverses of
-//    I + L_ii by forward substitution (one thread per column).
+// Solve: two workgroups per chunk (Y and X), one wave per 16 value columns.
+//  * The blocks of L = M_<(Bt At^T) (rank rows; tokens row / r_ab) come from
+//    the prepare, which formed them for the forward's own solve: the 16x16
+//    bf16 tiles below the diagonal and the fp32 inverses D_i of the diagonal
+//    blocks I + L_ii.  They are staged in LDS with their transposes.
 //  * Y: forward substitution Y_i = D_i (R_i - sum_{j<i} L_ij Y_j); X: backward
 //    substitution X_i = D_i^T (R_i - sum_{j>i} L_ji^T X_j).  The products pair
 //    two 16-row blocks into one 16x16x32 MFMA (a lone block padded with
 //    zeros), the solved blocks fed back from registers as the B operand; the
 //    diagonal inverses apply in fp32.
-// The right-hand sides' loads are issued first, so they overlap the L phase,
-// whose operands (the chunk's B~ and A~ rows) are staged in LDS.
+// The right-hand sides' loads are issued first, so they overlap the staging.
 struct BcSolveArgs {
   Problem p;
   BcBufs w;
@@ -860,13 +865,13 @@ struct BcSolveArgs {
 template <int DK, int DV, int RAB>
 struct BcSolveCfg {
   static constexpr int NA = kCC * RAB, NB = NA / 16, NT = NB * (NB + 1) / 2, NTI = NB * (NB - 1) / 2;
-  static constexpr int NCT = DV / 16, NW = 2 * NCT;
-  static constexpr int LDR = DK + 16;   // staged B~ / A~ row (bf16; conflict-free 16-byte fragment reads)
-  // LDS (bytes): L tiles and their transposes (bf16), the diagonal blocks, the
-  // inverses and their transposes (fp32), the chunk's B~ and A~ rows
-  static constexpr int OL = 0, OLT = OL + NTI * 512, ODG = OLT + NTI * 512, ODI = ODG + NB * 1024,
-                       ODT = ODI + NB * 1024, OBS = ODT + NB * 1024, OAS = OBS + NA * LDR * 2,
-                       LDS = OAS + NA * LDR * 2;
+  static constexpr int NCT = DV / 16, NW = NCT;
+  // LDS (bytes): L tiles and their transposes (bf16), the diagonal blocks'
+  // inverses and their transposes (fp32)
+  static constexpr int OL = 0, OLT = OL + NTI * 512, ODI = OLT + NTI * 512, ODT = ODI + NB * 1024,
+                       LDS = ODT + NB * 1024;
+  // 16-byte pieces of the tiles and the inverses, and per thread
+  static constexpr int NLP = NTI * 32, NDP = NB * 64, NIT = (NLP + NDP + 64 * NW - 1) / (64 * NW);
 };
 
 template <int DK, int DV, int RAB>
@@ -876,75 +881,57 @@ __global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_
   __shared__ __align__(16) unsigned char sm[Cf::LDS];
   __bf16* Lb = reinterpret_cast<__bf16*>(sm + Cf::OL);
   __bf16* LbT = reinterpret_cast<__bf16*>(sm + Cf::OLT);
-  float* dg = reinterpret_cast<float*>(sm + Cf::ODG);
   float* Di = reinterpret_cast<float*>(sm + Cf::ODI);
   float* DiT = reinterpret_cast<float*>(sm + Cf::ODT);
-  const int64_t job = blockIdx.x;
+  // Blocks b and b + 8 land on one XCD (dispatch is round-robin over 8): a
+  // chunk's Y and X workgroups take such a pair, so the blocks of L they both
+  // read meet in one L2.
+  const int64_t b = blockIdx.x;
+  const int64_t job = (b >> 4) * 8 + (b & 7);
+  if (job >= a.p.BH * a.p.N) return;
+  const bool isx = (b >> 3) & 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const BcBufs& w = a.w;
-  const bool isx = wave >= NCT;
-  const int ct = wave % NCT;
+  const int ct = wave;
   // this wave's right-hand side tiles, loaded first
   const __bf16* R = (isx ? w.rx : w.ry) + job * NA * DV;
   cb4 rhb[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) rhb[i] = *reinterpret_cast<const cb4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
-  // the chunk's B~ and A~ rows into LDS: every load issued before any write
-  __bf16* bt = reinterpret_cast<__bf16*>(sm + Cf::OBS);
-  __bf16* at = reinterpret_cast<__bf16*>(sm + Cf::OAS);
+  // L's tiles below the diagonal and the diagonal blocks' inverses as the
+  // prepare formed them (the same blocks its forward solve used): every load
+  // issued before any write, then the transposes the adjoint solve reads
   {
-    BcStg<kSrcChunk, NA, DK, 64 * NW> sb, sa;
-    sb.load(w.bt, nullptr, job, kCC, 0, tid);
-    sa.load(w.at, nullptr, job, kCC, 0, tid);
-    sb.store(bt, Cf::LDR, tid);
-    sa.store(at, Cf::LDR, tid);
-  }
-  __syncthreads();
-  // ---- L
-  for (int idx = wave; idx < NT; idx += NW) {
-    int i = 0, jj = idx;
-    while (jj > i) {
-      jj -= i + 1;
-      ++i;
-    }
-    cf4 P = cz4(), Q = cz4();
+    const cb8* gl = reinterpret_cast<const cb8*>(w.lt + job * Cf::NTI * 256);
+    const cb8* gd = reinterpret_cast<const cb8*>(w.di + job * NB * 256);
+    cb8 pc[Cf::NIT];
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-      const cb8 bf = *reinterpret_cast<const cb8*>(bt + (16 * i + lr) * Cf::LDR + 32 * ks + 8 * lg);
-      const cb8 af = *reinterpret_cast<const cb8*>(at + (16 * jj + lr) * Cf::LDR + 32 * ks + 8 * lg);
-      P = mfma_b(bf, af, P);   // lane: L[16 i + 4 lg + e][16 jj + lr]
-      Q = mfma_b(af, bf, Q);   // lane: L[16 i + lr][16 jj + 4 lg + e]
+    for (int q = 0; q < Cf::NIT; ++q) {
+      const int it = tid + q * 64 * NW;
+      if (it < Cf::NLP) pc[q] = gl[it];
+      else if (it < Cf::NLP + Cf::NDP) pc[q] = gd[it - Cf::NLP];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!((16 * i + 4 * lg + e) / RAB > (16 * jj + lr) / RAB)) P[e] = 0.f;
-      if (!((16 * i + lr) / RAB > (16 * jj + 4 * lg + e) / RAB)) Q[e] = 0.f;
-    }
-    if (jj < i) {
-      const int blk = i * (i - 1) / 2 + jj;
-      *reinterpret_cast<cb4*>(Lb + blk * 256 + lr * 16 + 4 * lg) = to_b4(Q);
-      *reinterpret_cast<cb4*>(LbT + blk * 256 + lr * 16 + 4 * lg) = to_b4(P);
-    } else {
-      *reinterpret_cast<cf4*>(dg + i * 256 + lr * 16 + 4 * lg) = Q;
+    for (int q = 0; q < Cf::NIT; ++q) {
+      const int it = tid + q * 64 * NW;
+      if (it < Cf::NLP) *reinterpret_cast<cb8*>(Lb + it * 8) = pc[q];
+      else if (it < Cf::NLP + Cf::NDP) *reinterpret_cast<cb8*>(Di + (it - Cf::NLP) * 4) = pc[q];
     }
   }
   __syncthreads();
-  if (tid < NB * 16) {
-    const int blk = tid / 16, c = tid % 16;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = (r == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) v -= dg[blk * 256 + r * 16 + m] * x[m];
-      x[r] = v;
-      Di[blk * 256 + r * 16 + c] = v;
-      DiT[blk * 256 + c * 16 + r] = v;
+  if (isx) {
+    for (int idx = tid; idx < Cf::NTI * 256; idx += 64 * NW) {
+      const int b0 = idx & ~255, r = (idx >> 4) & 15, c = idx & 15;
+      LbT[idx] = Lb[b0 + c * 16 + r];
     }
+    for (int idx = tid; idx < NB * 256; idx += 64 * NW) {
+      const int b0 = idx & ~255, r = (idx >> 4) & 15, c = idx & 15;
+      DiT[idx] = Di[b0 + c * 16 + r];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // ---- the substitutions
   const __bf16* Lt = isx ? LbT : Lb;
   const float* Dg = isx ? DiT : Di;
@@ -1236,7 +1223,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     if ((e = group(std::integral_constant<int, kDv1>{}, std::integral_constant<int, kRhsX>{}, chunk(w.kt), chunk(w.at),
                    GdS, chunk(w.qt), Os, none, none, w.dv1, w.rx)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3(jobs), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
+    hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3((jobs + 7) / 8 * 16), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
                        BcSolveArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
@@ -1281,7 +1268,7 @@ size_t backward_chunked_bytes(const Problem& p, bool own_ops) {
 PrepBwOut backward_chunked_prep_out(const Problem& p, void* ws) {
   BcBufs w;
   bc_layout(p, static_cast<char*>(ws), &w);
-  return PrepBwOut{w.qt, w.kt, w.at, w.bt};
+  return PrepBwOut{w.qt, w.kt, w.at, w.bt, w.lt, w.di};
 }
 
 size_t backward_chunked_ops_bytes(const Problem& p) { return bc_ops_layout(p, nullptr, nullptr); }

@@ -201,8 +201,12 @@ struct FastPrepArgs {
   const __bf16* B;
   const float* beta;   // fused modes: per-token beta [BH, T]
   __bf16* M;   // fragment-ordered chunk operators
-  // kGenericBw: per chunk-head, Q~, K~ [C][dk] and A~, B~ [C r_ab][dk] (bf16)
-  __bf16 *qt, *kt, *at, *bt;
+  // kGenericBw: per chunk-head, Q~, K~ [C][dk] and A~, B~ [C r_ab][dk] (bf16),
+  // L's 16x16 tiles below the diagonal blocks (bf16, row-major tiles, tile
+  // (i, j) at i (i - 1) / 2 + j) and the inverses of its unit lower-triangular
+  // diagonal blocks (fp32, row-major)
+  __bf16 *qt, *kt, *at, *bt, *lt;
+  float* di;
 };
 
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& raw, const float (&f)[8]) {
@@ -632,6 +636,29 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       invert_blocks();
       if (wave >= DK / 16 && wave < KT) x_products();
       lds_barrier();
+    }
+
+    if constexpr (MODE == kGenericBw && RAB > 0) {
+      // The chunked backward's copies of L's tiles below the diagonal and of
+      // the diagonal blocks' inverses, all complete after the barrier above
+      // (and kept until the solve has read them).  The waves that own no
+      // solve column copy them where there are such waves.
+      constexpr int NTI = NB * (NB - 1) / 2, W0 = NW > KT ? KT : 0, NCP = (NW - W0) * 64;
+      constexpr int NLP = NTI * 32, NDI = NB * 64;   // 16-byte pieces
+      if (wave >= W0) {
+        __bf16* lto = a.lt + static_cast<size_t>(job) * (NTI * 256);
+        float* dio = a.di + static_cast<size_t>(job) * (NB * 256);
+#pragma unroll 1
+        for (int it = tid - W0 * 64; it < NLP + NDI; it += NCP) {
+          if (it < NLP) {
+            *reinterpret_cast<bf16x8*>(lto + it * 8) = *reinterpret_cast<const bf16x8*>(Lpk + it * 8);
+          } else {
+            const int d = it - NLP, blk = d / 64, r = d % 64;
+            *reinterpret_cast<f32x4*>(dio + blk * 256 + r * 4) =
+                *reinterpret_cast<const f32x4*>(Dinv + blk * Cfg::DIB + r * 4);
+          }
+        }
+      }
     }
 
     // ---- P4: blocked forward substitution on wave kt's columns:
@@ -1180,6 +1207,8 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
     a.kt = static_cast<__bf16*>(bw->kt);
     a.at = static_cast<__bf16*>(bw->at);
     a.bt = static_cast<__bf16*>(bw->bt);
+    a.lt = static_cast<__bf16*>(bw->lt);
+    a.di = static_cast<float*>(bw->di);
   }
   const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB, SCAL, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);

@@ -55,10 +55,14 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
                      const float* S0, hipStream_t s, void* ckpt = nullptr);
 // fast_prepare, which also writes the decay-scaled operands it forms, per
 // chunk-head: Q~ = q e^{G_t}, K~ = k e^{-G_t} [C][dk], A~ = A e^{-G_t},
-// B~ = B e^{G_{t-1}} [C r_ab][dk] (bf16, zero on padding tokens; the chunked
+// B~ = B e^{G_{t-1}} [C r_ab][dk] (bf16, zero on padding tokens), and
+// (r_ab > 0) the blocks of L = B~ A~^T (rows and columns token-major,
+// rank-minor; entries with token(row) > token(col)): its 16x16 tiles below
+// the diagonal blocks, bf16 row-major, tile (i, j) at i (i - 1) / 2 + j, and
+// the inverses of I + L_ii, fp32 row-major [C r_ab / 16][16][16] (the chunked
 // backward's inputs).
 struct PrepBwOut {
-  void *qt, *kt, *at, *bt;
+  void *qt, *kt, *at, *bt, *lt, *di;
 };
 hipError_t fast_prepare_bw(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
                            const void* B, void* workspace, const PrepBwOut& out, hipStream_t s);
