@@ -131,6 +131,8 @@ size_t bc_ops_layout(const Problem& p, char* base, PrepBwOut* o) {
   t.bt = take(J * adk * 2);
   t.lt = take(J * (nb * (nb > 0 ? nb - 1 : 0) / 2) * 256 * 2);
   t.di = take(J * nb * 256 * 4);
+  t.gc = take(J * cdk * 4);
+  t.gam = take(J * p.dk * 4);
   if (o) *o = t;
   return off;
 }
@@ -148,8 +150,6 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
     return r;
   };
   BcBufs t{};
-  t.gc = reinterpret_cast<float*>(take(J * cdk * 4));
-  t.gam = reinterpret_cast<float*>(take(J * p.dk * 4));
   PrepBwOut o{};
   if (ops) {
     o = *ops;
@@ -162,6 +162,8 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
   t.bt = static_cast<__bf16*>(o.bt);
   t.lt = static_cast<__bf16*>(o.lt);
   t.di = static_cast<float*>(o.di);
+  t.gc = static_cast<float*>(o.gc);
+  t.gam = static_cast<float*>(o.gam);
   t.ry = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.rx = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
@@ -171,86 +173,6 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
   t.ends = reinterpret_cast<float*>(take(J * p.dk * 4));
   if (b) *b = t;
   return off;
-}
-
-// ---------------------------------------------------------------------------
-// G: the chunk-local cumulative log-decay in base 2 (the epilogues' decay
-// factors) and e^{G} at the chunk's last token (Gamma, which scales the
-// boundary cotangents).  Thread (token group tg, 8-channel piece pc) owns TPG
-// consecutive tokens of 8 channels: a prefix over its tokens, then over the
-// token groups through LDS.  (The decay-scaled operands come from the
-// prepare kernel, which forms them anyway.)
-struct BcGArgs {
-  Problem p;
-  const float* ld;
-  BcBufs w;
-};
-
-template <int DK>
-__global__ __launch_bounds__(256) void bwc_g_kernel(BcGArgs a) {
-  constexpr int NP = DK / 8, NG = 256 / NP, TPG = kCC / NG;
-  constexpr float kLog2e = 1.4426950408889634f;
-  __shared__ float tot[NG][DK];
-  const Problem& p = a.p;
-  const int64_t job = blockIdx.x, bh = job / p.N, j = job % p.N, t0 = j * kCC;
-  const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
-  const int64_t tok0 = bh * p.T + t0;
-  const int tid = threadIdx.x, pc = tid % NP, tg = tid / NP, c0 = 8 * pc;
-  float G[TPG][8], run[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) run[c] = 0.f;
-#pragma unroll
-  for (int u = 0; u < TPG; ++u) {
-    const int t = tg * TPG + u;
-    const int64_t tok = tok0 + (t < n ? t : 0);
-    float l[8];
-    if (t >= n) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) l[c] = 0.f;
-    } else if (p.scalar) {
-      const float s = a.ld[tok] * kLog2e;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) l[c] = s;
-    } else {
-      const cf4 x0 = *reinterpret_cast<const cf4*>(a.ld + tok * DK + c0);
-      const cf4 x1 = *reinterpret_cast<const cf4*>(a.ld + tok * DK + c0 + 4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        l[c] = x0[c] * kLog2e;
-        l[c + 4] = x1[c] * kLog2e;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      run[c] += l[c];
-      G[u][c] = run[c];
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) tot[tg][c0 + c] = run[c];
-  __syncthreads();
-  float off[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) off[c] = 0.f;
-  for (int g2 = 0; g2 < tg; ++g2)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) off[c] += tot[g2][c0 + c];
-  const BcBufs& w = a.w;
-#pragma unroll
-  for (int u = 0; u < TPG; ++u) {
-    const int t = tg * TPG + u;
-    float g[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) g[c] = G[u][c] + off[c];
-    float* gcr = w.gc + (job * kCC + t) * DK + c0;
-    *reinterpret_cast<cf4*>(gcr) = cf4{g[0], g[1], g[2], g[3]};
-    *reinterpret_cast<cf4*>(gcr + 4) = cf4{g[4], g[5], g[6], g[7]};
-    if (t == kCC - 1) {
-      // padding tokens add nothing: this is G at the chunk's last token
-#pragma unroll
-      for (int c = 0; c < 8; ++c) w.gam[job * DK + c0 + c] = __builtin_amdgcn_exp2f(g[c]);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1188,7 +1110,6 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   const int64_t J = p.BH * p.N;
   const unsigned jobs = static_cast<unsigned>(J);
   auto bf = [](const void* x) { return static_cast<const __bf16*>(x); };
-  hipLaunchKernelGGL((bwc_g_kernel<DK>), dim3(jobs), dim3(256), 0, s, BcGArgs{p, ld, w});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const BcSrc none{nullptr, kSrcChunk};
@@ -1268,7 +1189,7 @@ size_t backward_chunked_bytes(const Problem& p, bool own_ops) {
 PrepBwOut backward_chunked_prep_out(const Problem& p, void* ws) {
   BcBufs w;
   bc_layout(p, static_cast<char*>(ws), &w);
-  return PrepBwOut{w.qt, w.kt, w.at, w.bt, w.lt, w.di};
+  return PrepBwOut{w.qt, w.kt, w.at, w.bt, w.lt, w.di, w.gc, w.gam};
 }
 
 size_t backward_chunked_ops_bytes(const Problem& p) { return bc_ops_layout(p, nullptr, nullptr); }

@@ -205,8 +205,11 @@ struct FastPrepArgs {
   // L's 16x16 tiles below the diagonal blocks (bf16, row-major tiles, tile
   // (i, j) at i (i - 1) / 2 + j) and the inverses of its unit lower-triangular
   // diagonal blocks (fp32, row-major)
+  // and the chunk-local cumulative log-decay G in base 2, [C][dk] (fp32;
+  // padding tokens repeat the last token's), with e^{G} at the chunk's last
+  // token [dk]
   __bf16 *qt, *kt, *at, *bt, *lt;
-  float* di;
+  float *di, *gc, *gam;
 };
 
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& raw, const float (&f)[8]) {
@@ -356,6 +359,15 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
       float g2[NL];
 #pragma unroll
       for (int c = 0; c < NL; ++c) g2[c] = part[c] + x[c];
+      if constexpr (MODE == kGenericBw) {
+        // the chunked backward's copy of G (its epilogues' decay factors;
+        // chunk bases wave-uniform, lane offsets 32-bit)
+        float* gco = a.gc + static_cast<size_t>(job) * (kC * DK);
+        const int lo = t * DK + pc * 8;
+        *reinterpret_cast<f32x4*>(gco + lo) = f32x4{g2[0], g2[SCAL ? 0 : 1], g2[SCAL ? 0 : 2], g2[SCAL ? 0 : 3]};
+        *reinterpret_cast<f32x4*>(gco + lo + 4) =
+            f32x4{g2[SCAL ? 0 : 4], g2[SCAL ? 0 : 5], g2[SCAL ? 0 : 6], g2[SCAL ? 0 : 7]};
+      }
       float fp[8], fn[8], fx[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -365,8 +377,18 @@ __global__ __launch_bounds__((PrepCfg<DK, RAB, SCAL, MODE>::NT)) void fast_prepa
         fx[c] = pad ? 0.f : __builtin_amdgcn_exp2f(g2[cc] - l2[cc]);
       }
       if (t == kC - 1) {
+        float e8[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) eGC[pc * 8 + c] = __builtin_amdgcn_exp2f(g2[SCAL ? 0 : c]);
+        for (int c = 0; c < 8; ++c) {
+          e8[c] = __builtin_amdgcn_exp2f(g2[SCAL ? 0 : c]);
+          eGC[pc * 8 + c] = e8[c];
+        }
+        if constexpr (MODE == kGenericBw) {
+          // and of e^{G} at the chunk's last token
+          float* gmo = a.gam + static_cast<size_t>(job) * DK + pc * 8;
+          *reinterpret_cast<f32x4*>(gmo) = f32x4{e8[0], e8[1], e8[2], e8[3]};
+          *reinterpret_cast<f32x4*>(gmo + 4) = f32x4{e8[4], e8[5], e8[6], e8[7]};
+        }
       }
       const bf16x8 sq = scale8(qv, fp), sk = scale8(kv, fn);
       *reinterpret_cast<bf16x8*>(Xl + xoff<DK>(NA + t, pc)) = sq;
@@ -1209,6 +1231,8 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
     a.bt = static_cast<__bf16*>(bw->bt);
     a.lt = static_cast<__bf16*>(bw->lt);
     a.di = static_cast<float*>(bw->di);
+    a.gc = static_cast<float*>(bw->gc);
+    a.gam = static_cast<float*>(bw->gam);
   }
   const void* fn = reinterpret_cast<const void*>(fast_prepare_kernel<DK, RAB, SCAL, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);

@@ -59,10 +59,12 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
 // (r_ab > 0) the blocks of L = B~ A~^T (rows and columns token-major,
 // rank-minor; entries with token(row) > token(col)): its 16x16 tiles below
 // the diagonal blocks, bf16 row-major, tile (i, j) at i (i - 1) / 2 + j, and
-// the inverses of I + L_ii, fp32 row-major [C r_ab / 16][16][16] (the chunked
-// backward's inputs).
+// the inverses of I + L_ii, fp32 row-major [C r_ab / 16][16][16]; the
+// chunk-local cumulative log-decay G in base 2, fp32 [C][dk] (padding tokens
+// repeat the last token's), and e^{G} at the chunk's last token [dk] (the
+// chunked backward's inputs).
 struct PrepBwOut {
-  void *qt, *kt, *at, *bt, *lt, *di;
+  void *qt, *kt, *at, *bt, *lt, *di, *gc, *gam;
 };
 hipError_t fast_prepare_bw(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
                            const void* B, void* workspace, const PrepBwOut& out, hipStream_t s);
