@@ -893,14 +893,19 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   };
   // Loads are unconditional (chunk and token indices are clamped), so no
   // control flow separates a prefetch from the work it overlaps.
+  // The boundary-state instance needs only the operator's state rows: a
+  // wave skips its output row tiles (a wave-uniform test).
+  auto live = [&](int q) { return CK != kScanStates || wave * MPW + q < DK / 16; };
   auto load_m = [&](bf16x8 (&dst)[MPW][KP], int64_t jj) {
     jj = jj < N ? jj : N - 1;
     const __bf16* Mj = Mbh + static_cast<size_t>(jj) * MSZ;
 #pragma unroll
     for (int q = 0; q < MPW; ++q)
+      if (live(q)) {
 #pragma unroll
-      for (int kp = 0; kp < KP; ++kp)
-        dst[q][kp] = *reinterpret_cast<const bf16x8*>(Mj + moff + (q * KP + kp) * 512);
+        for (int kp = 0; kp < KP; ++kp)
+          dst[q][kp] = *reinterpret_cast<const bf16x8*>(Mj + moff + (q * KP + kp) * 512);
+      }
   };
   auto load_v = [&](bf16x8 (&dst)[VT], int64_t jj) {
     jj = jj < N ? jj : N - 1;
@@ -984,18 +989,20 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     // issued as soon as this chunk's MFMAs have read it, spreading the loads
     // over the product instead of bunching them after it.
     const __bf16* Mnext = Mbh + static_cast<size_t>(jj + PD < N ? jj + PD : N - 1) * MSZ;
+    // (a wave whose first row tile is an output tile has no live tile)
 #pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
+    for (int kp = 0; kp < (live(0) ? KP : 0); ++kp) {
       bf16x8 bv[NTN];
 #pragma unroll
       for (int nt = 0; nt < NTN; ++nt) bv[nt] = lds8(Xc + (nt * 16 + lr) * LDX + kp * 32 + 8 * lg);
 #pragma unroll
       for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-        for (int q = 0; q < MPW; ++q) acc[q][nt] = mfma32(mf[u][q][kp], bv[nt], acc[q][nt]);
+        for (int q = 0; q < MPW; ++q)
+          if (live(q)) acc[q][nt] = mfma32(mf[u][q][kp], bv[nt], acc[q][nt]);
 #pragma unroll
       for (int q = 0; q < MPW; ++q)
-        mf[u][q][kp] = *reinterpret_cast<const bf16x8*>(Mnext + moff + (q * KP + kp) * 512);
+        if (live(q)) mf[u][q][kp] = *reinterpret_cast<const bf16x8*>(Mnext + moff + (q * KP + kp) * 512);
     }
     if (jj > 0) flush_out(O0 + ((u + 1) & 1) * OBUF, jj - 1);
 #pragma unroll
