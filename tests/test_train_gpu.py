@@ -105,3 +105,35 @@ def test_training_pair_rejects_off_route_shapes():
         lattn.chunk_fwd_train(dev(raw["q"]), dev(raw["K"]), dev(raw["V"]), dev(raw["log_decay"]), dev(raw["A"]),
                               dev(raw["B"]), chunk=64)
     assert lattn.train_saved_size(1, 1, 64, 64, 64, 2, 1, 64, dtype=torch.float32) == 0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["hdla_bf16", "gdn_bf16", "hdla_long_bf16"])
+def test_training_pair_full_size_equals_the_plain_calls(name):
+    """Every bf16 workload at full size, in the launch configuration the bench
+    times: the training pair's outputs and gradients equal lattn_chunk_fwd's and
+    lattn_chunk_bwd's on every (batch, head), bit for bit (the oracle checks of
+    those calls carry over)."""
+    import bench
+    spec = workloads.CONFIGS[name]
+    print(f"training pair full size {name}", flush=True)
+    dev0 = torch.device("cuda:0")
+    draw = workloads.device_raw(spec, torch, dev0, seed=3)
+    q, K, V, ld, A, B = bench.generic_inputs(spec, draw, lattn)
+    g = torch.Generator(device=dev0)
+    g.manual_seed(4)
+    dout = torch.randn((spec.B, spec.H, spec.T, spec.dv), device=dev0, generator=g).to(q.dtype)
+    dfin = torch.randn((spec.B, spec.H, spec.dk, spec.dv), device=dev0, generator=g)
+    out, fin = lattn.chunk_fwd(q, K, V, ld, A, B, chunk=spec.chunk)
+    out_t, fin_t, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=spec.chunk)
+    assert torch.equal(out, out_t) and torch.equal(fin, fin_t)
+    del out, fin, out_t, fin_t
+    gr = lattn.chunk_bwd(q, K, V, ld, A, B, dout, chunk=spec.chunk, dfinal=dfin)
+    gs = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dout, saved, chunk=spec.chunk, dfinal=dfin)
+    torch.cuda.synchronize()
+    for n in gr:
+        if gr[n] is None:
+            assert gs[n] is None, n
+        else:
+            assert torch.isfinite(gr[n]).all(), n
+            assert torch.equal(gr[n], gs[n]), n
