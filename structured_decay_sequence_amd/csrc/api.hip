@@ -173,7 +173,7 @@ FusedPlan fused_plan(const lattn_dims* d, int family, int chunk) {
   f.p = make_problem(d, r_ab, 1, chunk);
   f.fast = lattn::fast_supported(f.p);
   if (f.fast) {
-    f.total = lattn::fast_workspace_bytes(f.p);
+    f.total = lattn::fast_forward_bytes(f.p);
     return f;
   }
   const size_t e = f.p.bf16 ? 2 : 4;
@@ -339,7 +339,7 @@ size_t lattn_chunk_fwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv
       check_chunk(chunk, r_ab, r_kv) != LATTN_OK)
     return 0;
   const lattn::Problem p = make_problem(dims, r_ab, r_kv, chunk);
-  return lattn::fast_supported(p) ? lattn::fast_workspace_bytes(p) : lattn::general_plan(p).total_bytes;
+  return lattn::fast_supported(p) ? lattn::fast_forward_bytes(p) : lattn::general_plan(p).total_bytes;
 }
 
 size_t lattn_chunk_summaries_workspace_size(const lattn_dims* dims, int r_ab, int r_kv, int chunk) {

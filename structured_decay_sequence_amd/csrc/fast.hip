@@ -845,13 +845,20 @@ struct FastScanArgs {
   float* Sfin;
   const float* S0;
   __bf16* ckpt;        // [BH, N + 1, dk, dv]: the state entering every chunk, then the final state (the boundary instance)
+  // The instance split in two sequence segments at chunk js: segment 1 runs
+  // from a zero state beside its transport (the product of its chunks'
+  // state transitions, from I); its outputs and final state are then
+  // corrected with the state leaving segment 0 (see fast_scan).
+  int64_t js;
+  __bf16* U;           // [BH, N - js, C, dk]: segment 1's query rows times its transport so far
+  float *Smid, *Sp, *Tf;   // state leaving segment 0, segment 1's zero-start final state [BH, dk, dv]; its transport [BH, dk, dk]
 };
 
 // CK: what the scan stores.  kScanOut: the output rows (and the final state);
 // kScanStates: the state entering every chunk instead of the output rows (the
 // backward's boundary scan); kScanBoth: both (the training forward).
 enum ScanStore { kScanOut = 0, kScanStates = 1, kScanBoth = 2 };
-template <int DK, int BV, int NWV, int PD, int CK>
+template <int DK, int BV, int NWV, int PD, int CK, bool SG = false>
 __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
   constexpr int KP = Cfg::KP, MPW = Cfg::MPW, NTN = Cfg::NTN, LDX = Cfg::LDX, NT = Cfg::NT;
@@ -864,13 +871,28 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   const Problem& p = a.p;
   const int dv = p.dv;
   const int nvt = dv / BV;
+  // Workgroups per head: the d_v slices; split in segments, segment 0's
+  // slices, then segment 1's slices and its transport's d_k slices.
+  static_assert(!SG || CK == kScanOut, "segments: the output instance only");
+  const int R = SG ? 2 * nvt + DK / BV : nvt;
   // Blocks of one (batch, head) land on one XCD (dispatch is round-robin over 8).
   const int b = blockIdx.x;
-  const int grp = b / (8 * nvt), rem = b % (8 * nvt);
-  const int vt = rem / 8;
+  const int grp = b / (8 * R), rem = b % (8 * R);
+  const int role = rem / 8;
   const int64_t bh = static_cast<int64_t>(grp) * 8 + rem % 8;
   const int64_t N = p.N;
   if (bh >= p.BH || N == 0) return;
+  // this workgroup's chunks [j0, j1), its slice, and (split) its segment and role
+  int64_t j0 = 0, j1 = N;
+  int seg = 0, vt = role;
+  bool tr = false;   // a transport slice: columns of I, no V
+  if constexpr (SG) {
+    seg = role >= nvt ? 1 : 0;
+    tr = role >= 2 * nvt;
+    vt = role - (seg ? (tr ? 2 * nvt : nvt) : 0);
+    j0 = seg ? a.js : 0;
+    j1 = seg ? N : a.js;
+  }
   const int c0 = vt * BV;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -883,13 +905,32 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   const int vitem = tid < VITEMS ? tid : VITEMS - 1;
   const int vs = vitem / (BV / 8), vc = vitem % (BV / 8);
   const __bf16* vbh = a.v + static_cast<size_t>(bh) * p.T * dv + c0;
+  // output rows: out [BH, T, dv], or (transport) U [BH, N - js, C, dk]; the
+  // final state's destination and row stride
   __bf16* obh = a.out + static_cast<size_t>(bh) * p.T * dv + c0;
+  int ost = dv, sst = dv;
+  int64_t jb = 0;
+  float* sfin = a.Sfin;
+  if constexpr (SG) {
+    if (tr) {
+      vbh = a.v + static_cast<size_t>(bh) * p.T * dv;
+      obh = a.U + static_cast<size_t>(bh) * (N - j0) * kC * DK + c0;
+      ost = sst = DK;
+      jb = j0;
+    }
+    sfin = seg == 0 ? a.Smid : (a.Sfin ? (tr ? a.Tf : a.Sp) : nullptr);
+  }
 
   bf16x8 mf[PD][MPW][KP];
   bf16x8 vb[2][VT];   // V ring: two chunks ahead is enough for its few KB
   auto chunk_len = [&](int64_t jj) {
     const int64_t r = p.T - jj * kC;
     return static_cast<int>(r < kC ? r : kC);   // <= 0 past the last chunk
+  };
+  // tokens this workgroup stores for chunk jj (none outside its chunks)
+  auto store_len = [&](int64_t jj) {
+    if constexpr (SG) return jj < j1 ? chunk_len(jj) : 0;
+    return chunk_len(jj);
   };
   // Loads are unconditional (chunk and token indices are clamped), so no
   // control flow separates a prefetch from the work it overlaps.
@@ -921,7 +962,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   // the chunk's end are zero.
   typedef __attribute__((__vector_size__(VT * sizeof(__bf16)))) __bf16 bf16xVT;
   auto put_v = [&](__bf16* X, const bf16x8 (&src)[VT], int64_t jj) {
-    const int n = chunk_len(jj);
+    const int n = SG && tr ? 0 : chunk_len(jj);
     if (tid < VITEMS) {
       const int pos = kperm(DK + VT * vs);
 #pragma unroll
@@ -947,29 +988,34 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
       }
       return;
     }
-    const int n = chunk_len(jj);
-    __bf16* oj = obh + static_cast<size_t>(jj) * kC * dv;
+    const int n = store_len(jj);
+    // (the unsplit instances keep their own expressions: the boundary-state
+    // output instance sits at the VGPR limit of its 12 waves)
+    __bf16* oj = SG ? obh + static_cast<size_t>(jj - jb) * kC * ost : obh + static_cast<size_t>(jj) * kC * dv;
+    const int os = SG ? ost : dv;
 #pragma unroll
     for (int q = 0; q < OIT; ++q) {
       const int it = tid + q * NT;
       const int t = it / (BV / 8), cg = it % (BV / 8);
-      if (it < OITEMS && t < n) *reinterpret_cast<bf16x8*>(oj + (t * dv + cg * 8)) = lds8(O + t * LDO + cg * 8);
+      if (it < OITEMS && t < n) *reinterpret_cast<bf16x8*>(oj + (t * os + cg * 8)) = lds8(O + t * LDO + cg * 8);
     }
   };
 
 #pragma unroll
-  for (int u = 0; u < PD; ++u) load_m(mf[u], u);
-  load_v(vb[0], 0);
-  load_v(vb[1], 1);
+  for (int u = 0; u < PD; ++u) load_m(mf[u], j0 + u);
+  load_v(vb[0], j0);
+  load_v(vb[1], j0 + 1);
   for (int it = tid; it < DK * BV; it += NT) {
     const int i = it / BV, c = it % BV;
-    const float s = a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f;
+    // the state entering chunk j0: the initial state, or (segment 1) zero
+    // beside the transport's identity columns
+    const float s = SG && seg ? (tr && i == c0 + c ? 1.f : 0.f) : (a.S0 ? a.S0[(bh * DK + i) * dv + c0 + c] : 0.f);
     X0[c * LDX + kperm(i)] = (__bf16)s;
     if (CK == kScanStates) a.ckpt[(static_cast<size_t>(bh * (N + 1)) * DK + i) * dv + c0 + c] = (__bf16)s;
   }
-  put_v(X0, vb[0], 0);
-  // Ring invariant from here on: at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
-  load_v(vb[0], 2);
+  put_v(X0, vb[0], j0);
+  // Ring invariant from here on (j0 is even): at chunk jj, vb[(jj + 1) % 2] holds V_{jj+1}.
+  load_v(vb[0], j0 + 2);
   lds_barrier();
 
   // One chunk: product from X buffer u&1; state and V_{jj+1} into the other,
@@ -1004,7 +1050,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
       for (int q = 0; q < MPW; ++q)
         if (live(q)) mf[u][q][kp] = *reinterpret_cast<const bf16x8*>(Mnext + moff + (q * KP + kp) * 512);
     }
-    if (jj > 0) flush_out(O0 + ((u + 1) & 1) * OBUF, jj - 1);
+    if (jj > (SG ? j0 : 0)) flush_out(O0 + ((u + 1) & 1) * OBUF, jj - 1);
 #pragma unroll
     for (int q = 0; q < MPW; ++q) {
       const int mt = wave * MPW + q;
@@ -1044,7 +1090,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
         }
       }
     }
-    if (jj == N - 1 && a.Sfin) {
+    if (SG ? (jj == j1 - 1 && sfin) : (jj == N - 1 && a.Sfin)) {
 #pragma unroll
       for (int q = 0; q < MPW; ++q) {
         const int mt = wave * MPW + q;
@@ -1053,7 +1099,7 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
           for (int nt = 0; nt < NTN; ++nt) {
             const int i0 = mt * 16 + 4 * lg, c = nt * 16 + lr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a.Sfin[(bh * DK + i0 + e) * dv + c0 + c] = acc[q][nt][e];
+            for (int e = 0; e < 4; ++e) (SG ? sfin : a.Sfin)[(bh * DK + i0 + e) * (SG ? sst : dv) + c0 + c] = acc[q][nt][e];
           }
         }
       }
@@ -1084,12 +1130,16 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
     lds_barrier();
   };
 
-  for (int64_t j = 0; j < N; j += PD) {
+  for (int64_t j = SG ? j0 : 0; j < (SG ? j1 : N); j += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) step(u, j + u);
   }
   // The last chunk's outputs, unless a step past the end already sent them.
-  if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
+  if constexpr (SG) {
+    if ((j1 - j0) % PD == 0) flush_out(O0 + ((j1 - 1 - j0) & 1) * OBUF, j1 - 1);
+  } else {
+    if (N % PD == 0) flush_out(O0 + ((N - 1) & 1) * OBUF, N - 1);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1269,6 +1319,110 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
                   : launch_prep<DK, RAB, false, kGeneric>(p, q, k, ld, A, B, nullptr, M, s);
 }
 
+// ---------------------------------------------------------------------------
+// The split scan's correction, from the state leaving segment 0 (Smid): every
+// output row of segment 1 gains U_j Smid (bf16 MFMAs with fp32 accumulation,
+// the sum rounded once), and the final state is Sp + Tf Smid (fp32).  One
+// four-wave workgroup per kSegFixG consecutive chunks of segment 1 (wave w:
+// the chunk's 16-token row block w), staging Smid once; with a final state,
+// first one workgroup per head for it (its serial sums then overlap the
+// chunks' workgroups instead of trailing them).
+constexpr int kSegFixG = 8;
+struct SegFixArgs {
+  Problem p;
+  int64_t js;
+  const __bf16* U;
+  const float *Smid, *Sp, *Tf;
+  __bf16* out;
+  float* Sfin;
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void fast_segfix_kernel(SegFixArgs a) {
+  const Problem& p = a.p;
+  const int dv = p.dv;
+  const int64_t N1 = p.N - a.js, NG = (N1 + kSegFixG - 1) / kSegFixG, nf = a.Sfin ? p.BH : 0;
+  const int64_t b = static_cast<int64_t>(blockIdx.x) - nf;
+  const int tid = threadIdx.x;
+  if (b < 0) {
+    // the final state of head bh (a fixed-order fp32 sum)
+    const int64_t bh = b + nf;
+    const float* Sm = a.Smid + bh * DK * dv;
+    const float* Tf = a.Tf + bh * DK * DK;
+    for (int it = tid; it < DK * dv; it += 256) {
+      const int i = it / dv, c = it % dv;
+      float s = a.Sp[bh * DK * dv + it];
+      for (int k = 0; k < DK; ++k) s += Tf[i * DK + k] * Sm[k * dv + c];
+      a.Sfin[bh * DK * dv + it] = s;
+    }
+    return;
+  }
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int LDT = DK + 8;   // Smid^T row (bf16): value column c, K = d_k contiguous
+  __bf16* St = reinterpret_cast<__bf16*>(smem);
+  float* ob = reinterpret_cast<float*>(smem + static_cast<size_t>(dv) * LDT * 2);   // [C][dv + 4]
+  const int LDO = dv + 4;
+  const int64_t bh = b / NG, g0 = (b % NG) * kSegFixG;
+  const float* Sm = a.Smid + bh * DK * dv;
+  for (int it = tid; it < DK * dv; it += 256) {
+    const int i = it / dv, c = it % dv;
+    St[c * LDT + i] = (__bf16)Sm[it];
+  }
+  const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int64_t g1 = g0 + kSegFixG < N1 ? g0 + kSegFixG : N1;
+  // The next chunk's U rows and output rows are loaded while this chunk's
+  // are formed and stored.  A thread's output pieces: items tid + 256 q of
+  // the chunk's (token, 8 columns) pieces (d_v <= 128: at most 4).
+  constexpr int OQ = kC * 128 / 8 / 256;
+  bf16x8 af[DK / 32], ov[OQ];
+  auto load = [&](int64_t jl) {
+    // A operand: row 16 w + lr of U_j (padding rows hold whatever the scan
+    // left there; a product row depends on its own A row only, and is not
+    // stored)
+    const __bf16* Ur = a.U + ((bh * N1 + jl) * kC + 16 * w + lr) * DK + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(Ur + 32 * ks);
+    const int64_t j = a.js + jl;
+    const int n = static_cast<int>(p.T - j * kC < kC ? p.T - j * kC : kC);
+    const __bf16* oj = a.out + (bh * p.T + j * kC) * dv;
+#pragma unroll
+    for (int q = 0; q < OQ; ++q) {
+      const int it = tid + 256 * q, t = it / (dv / 8), c8 = (it % (dv / 8)) * 8;
+      if (t < n) ov[q] = *reinterpret_cast<const bf16x8*>(oj + t * dv + c8);
+    }
+  };
+  load(g0);
+  for (int64_t jl = g0; jl < g1; ++jl) {
+    const int64_t j = a.js + jl;
+    const int n = static_cast<int>(p.T - j * kC < kC ? p.T - j * kC : kC);
+    __syncthreads();   // Smid^T staged; the previous chunk's rows are out of ob
+    for (int ct = 0; ct < dv / 16; ++ct) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks)
+        acc = mfma32(af[ks], lds8(St + (16 * ct + lr) * LDT + 32 * ks + 8 * lg), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[(16 * w + 4 * lg + e) * LDO + 16 * ct + lr] = acc[e];
+    }
+    bf16x8 oc[OQ];
+#pragma unroll
+    for (int q = 0; q < OQ; ++q) oc[q] = ov[q];
+    if (jl + 1 < g1) load(jl + 1);
+    __syncthreads();
+    __bf16* oj = a.out + (bh * p.T + j * kC) * dv;
+#pragma unroll
+    for (int q = 0; q < OQ; ++q) {
+      const int it = tid + 256 * q, t = it / (dv / 8), c8 = (it % (dv / 8)) * 8;
+      if (t < n) {
+        bf16x8 o = oc[q];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (__bf16)((float)o[e] + ob[t * LDO + c8 + e]);
+        *reinterpret_cast<bf16x8*>(oj + t * dv + c8) = o;
+      }
+    }
+  }
+}
+
 template <int DK, int BV, int NWV, int PD, int CK = kScanOut>
 hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out, float* Sfin,
                        const float* S0, void* ckpt, hipStream_t s) {
@@ -1285,11 +1439,74 @@ hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out
   return hipGetLastError();
 }
 
+// Workspace of the split scan after the chunk operators: U, Smid, Sp, Tf.
+struct SegLayout {
+  int64_t js;
+  size_t u, smid, sp, tf, total;
+};
+size_t seg_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+SegLayout seg_layout(const Problem& p) {
+  SegLayout l{};
+  // segment 1 starts at an even chunk (the scan's ring of two), near the middle
+  l.js = ((p.N + 1) / 2 + 1) & ~static_cast<int64_t>(1);
+  const size_t st = static_cast<size_t>(p.BH) * p.dk * p.dv * 4;
+  l.u = 0;
+  l.smid = seg_align(static_cast<size_t>(p.BH) * (p.N - l.js) * kC * p.dk * 2);
+  l.sp = l.smid + seg_align(st);
+  l.tf = l.sp + seg_align(st);
+  l.total = l.tf + seg_align(static_cast<size_t>(p.BH) * p.dk * p.dk * 4);
+  return l;
+}
+
+template <int DK, int BV, int NWV, int PD>
+hipError_t launch_scan_seg(const Problem& p, const void* M, const void* v, void* out, float* Sfin, const float* S0,
+                           char* scratch, hipStream_t s) {
+  using Cfg = ScanCfg<DK, BV, NWV, PD>;
+  const SegLayout l = seg_layout(p);
+  FastScanArgs a{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(v), static_cast<__bf16*>(out), Sfin, S0,
+                 nullptr};
+  a.js = l.js;
+  a.U = reinterpret_cast<__bf16*>(scratch + l.u);
+  a.Smid = reinterpret_cast<float*>(scratch + l.smid);
+  a.Sp = reinterpret_cast<float*>(scratch + l.sp);
+  a.Tf = reinterpret_cast<float*>(scratch + l.tf);
+  const int R = 2 * (p.dv / BV) + DK / BV;
+  const int64_t groups = (p.BH + 7) / 8;
+  const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD, kScanOut, true>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD, kScanOut, true>), dim3(groups * 8 * R), dim3(Cfg::NT),
+                     Cfg::LDS, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  SegFixArgs f{p, l.js, a.U, a.Smid, a.Sp, a.Tf, static_cast<__bf16*>(out), Sfin};
+  const int64_t blocks = p.BH * ((p.N - l.js + kSegFixG - 1) / kSegFixG) + (Sfin ? p.BH : 0);
+  const size_t lds = static_cast<size_t>(p.dv) * (DK + 8) * 2 + static_cast<size_t>(kC) * (p.dv + 4) * 4;
+  hipLaunchKernelGGL(fast_segfix_kernel<DK>, dim3(blocks), dim3(256), lds, s, f);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool fast_supported(const Problem& p) {
   return p.bf16 && p.C == kC && p.r_kv == 1 && (p.r_ab >= 0 && p.r_ab <= 2) &&
          (p.dk == 64 || p.dk == 128) && (p.dv % 64 == 0);
+}
+
+// The forward scan splits the sequence in two (fast_scan) where at d_k = 64
+// its 16-column d_v slices leave the chip's 256 compute units short of work:
+// the split scan takes 64-column slices (every slice reads the whole chunk
+// operator, so wide slices keep that traffic down), and its workgroups, one
+// per compute unit, must all be resident (d_v <= 128).
+int fast_scan_segments(const Problem& p) {
+  constexpr int64_t kCUs = 256;
+  if (!fast_supported(p) || p.dk != 64 || p.dv > 128 || p.N < 64) return 1;
+  const int64_t one = p.BH * (p.dv / 16), two = p.BH * (2 * (p.dv / 64) + 1);
+  return one < kCUs && two <= kCUs ? 2 : 1;
+}
+
+size_t fast_forward_bytes(const Problem& p) {
+  const size_t ops = fast_workspace_bytes(p);
+  return fast_scan_segments(p) == 2 ? seg_align(ops) + seg_layout(p).total : ops;
 }
 
 size_t fast_workspace_bytes(const Problem& p) {
@@ -1355,6 +1572,13 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
     if (p.dk == 64) return launch_scan<64, 16, 4, 4, kScanBoth>(p, workspace, v, out, Sfin, S0, ckpt, s);
     return hipErrorInvalidValue;
   }
+  // Split in two sequence segments (d_k = 64, few heads): the scratch after
+  // the chunk operators, as fast_forward_bytes counts it.
+  if (fast_scan_segments(p) == 2)
+    return launch_scan_seg<64, 64, 8, 2>(p, workspace, v, out, Sfin, S0,
+                                         static_cast<char*>(const_cast<void*>(workspace)) +
+                                             seg_align(fast_workspace_bytes(p)),
+                                         s);
   // Wider d_v slices share each operator load among more columns; narrower
   // ones are used when that leaves too few workgroups to fill the chip.
   if (p.dk == 128 && p.BH * (p.dv / 64) >= 256)

@@ -48,7 +48,13 @@ hipError_t general_summaries(const Problem& p, const void* workspace, const void
 // state, [BH, N + 1, dk, dv], go there in bf16 (the values the scan's own
 // products read) and no output rows are written (out is ignored).
 bool fast_supported(const Problem& p);
+// fast_workspace_bytes: the chunk operators.  fast_forward_bytes: the
+// forward's workspace, the operators and (where fast_scan_segments(p) is 2:
+// d_k = 64 with few heads) the split scan's scratch after them, which
+// fast_scan then takes from its workspace argument (output instance only).
 size_t fast_workspace_bytes(const Problem& p);
+size_t fast_forward_bytes(const Problem& p);
+int fast_scan_segments(const Problem& p);
 hipError_t fast_prepare(const Problem& p, const void* q, const void* k, const float* ld,
                         const void* A, const void* B, void* workspace, hipStream_t s);
 hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, void* out, float* Sfin,

@@ -205,3 +205,17 @@ def test_training_pair_validation_before_launch():
     rc = lib.lattn_chunk_bwd_saved(ctypes.byref(on), f, f, f, f, None, None, 0, 1, 64, f, None, f, need,
                                    f, f, f, f, f, f, f, f, ws, None)
     assert rc == _lib.LATTN_EINVAL
+
+
+def test_split_scan_workspace():
+    """The forward's workspace holds the chunk operators, plus the split scan's
+    scratch where the scan splits the sequence (d_k = 64, few heads, at least 64
+    chunks): the long-context HDLA shape splits, the headline shape does not."""
+    lib = _lib.load()
+    ops = lambda B, H, T, dk, dv: B * H * -(-T // 64) * ((dk + 64) // 16) ** 2 * 512
+    head = _dims(batch=8, heads=16, seqlen=4096, d_k=128, d_v=128)
+    assert lib.lattn_chunk_fwd_workspace_size(ctypes.byref(head), 2, 1, 64) == ops(8, 16, 4096, 128, 128)
+    long = _dims(batch=1, heads=48, seqlen=32768, d_k=64, d_v=64)
+    assert lib.lattn_chunk_fwd_workspace_size(ctypes.byref(long), 2, 1, 64) > ops(1, 48, 32768, 64, 64)
+    short = _dims(batch=1, heads=48, seqlen=4000, d_k=64, d_v=64)   # 63 chunks: not split
+    assert lib.lattn_chunk_fwd_workspace_size(ctypes.byref(short), 2, 1, 64) == ops(1, 48, 4000, 64, 64)

@@ -40,6 +40,8 @@ FUSED_CASES = [
     ("gdn", 2, 2, 130, 64, 64, "bf16", 64, False),
     ("gdn", 1, 2, 100, 128, 128, "fp32", 32, True),
     ("gdn", 1, 1, 1, 128, 128, "bf16", 64, False),       # a single token
+    ("hdla", 1, 2, 4200, 64, 64, "bf16", 64, True),      # the scan split in two segments
+    ("gdn", 1, 1, 4100, 64, 128, "bf16", 64, False),     # the same, d_v 128
 ]
 
 

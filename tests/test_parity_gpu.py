@@ -82,6 +82,46 @@ FAST_CASES = [
 ]
 
 
+# d_k = 64 with at least 64 chunks and few (batch, head) rows: the scan splits
+# the sequence in two segments, the second corrected with the state leaving
+# the first (odd chunk counts, ragged tails, an exact multiple, d_v 64 and 128,
+# ranks 0-2, both decay modes).
+SPLIT_CASES = [
+    # B, H, T, dk, dv, r_ab, decay, final state returned
+    (1, 2, 4133, 64, 64, 2, "channel", True),
+    (1, 1, 4096, 64, 128, 0, "channel", True),
+    (2, 1, 5000, 64, 64, 1, "scalar", True),
+    (1, 3, 8192, 64, 64, 2, "channel", False),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}{}fin{}".format(*c))
+def test_split_scan_parity(case):
+    Bb, H, T, dk, dv, r_ab, decay, fin = case
+    print(f"split scan case {case}", flush=True)
+    raw = workloads.generic_raw(Bb, H, T, dk, dv, r_ab, 1, "bf16", decay, seed=T + dv)
+    S0 = (np.random.default_rng(8).standard_normal((Bb, H, dk, dv)) * 0.1).astype(np.float32)
+    td = torch.bfloat16
+    out, S = lattn.chunk_fwd(dev(raw["q"], td), dev(raw["K"], td), dev(raw["V"], td), dev(raw["log_decay"]),
+                             dev(raw["A"], td), dev(raw["B"], td), chunk=64, initial_state=dev(S0),
+                             return_final_state=fin)
+    torch.cuda.synchronize()
+    ref_out, ref_S = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"],
+                                    initial_state=S0)
+    e_o = rel_err(host(out), ref_out)
+    # the second segment alone (the corrected rows)
+    half = T // 2
+    e_h = rel_err(host(out)[:, :, half:], ref_out[:, :, half:])
+    print(f"out {e_o:.2e} second half {e_h:.2e}", flush=True)
+    assert e_o <= TOL["bf16"] and e_h <= TOL["bf16"]
+    if fin:
+        e_s = rel_err(host(S), ref_S)
+        print(f"state {e_s:.2e}", flush=True)
+        assert e_s <= TOL["bf16"]
+    else:
+        assert S is None
+
+
 @pytest.mark.parametrize("case", FAST_CASES, ids=lambda c: "B{}H{}T{}dk{}dv{}r{}{}".format(*c))
 def test_mfma_path_parity(case):
     Bb, H, T, dk, dv, r_ab, decay = case
