@@ -845,13 +845,17 @@ struct FastScanArgs {
   float* Sfin;
   const float* S0;
   __bf16* ckpt;        // [BH, N + 1, dk, dv]: the state entering every chunk, then the final state (the boundary instance)
-  // The instance split in two sequence segments at chunk js: segment 1 runs
-  // from a zero state beside its transport (the product of its chunks'
-  // state transitions, from I); its outputs and final state are then
-  // corrected with the state leaving segment 0 (see fast_scan).
-  int64_t js;
-  __bf16* U;           // [BH, N - js, C, dk]: segment 1's query rows times its transport so far
-  float *Smid, *Sp, *Tf;   // state leaving segment 0, segment 1's zero-start final state [BH, dk, dv]; its transport [BH, dk, dk]
+  // The instance split in nseg sequence segments of L chunks (the last one
+  // shorter): every segment after the first runs from a zero state beside its
+  // transport (the product of its chunks' state transitions, from I); its
+  // outputs and final state are then corrected with the state entering it
+  // (see fast_scan).
+  int64_t L;
+  int nseg;
+  __bf16* U;     // [BH, N - L, C, dk]: the later segments' query rows times their transport so far
+  float* Smid;   // [BH, dk, dv]: the state leaving segment 0
+  float* Sp;     // [nseg - 1][BH, dk, dv]: segment s's zero-start final state (slot s - 1)
+  float* Tf;     // [nseg - 1][BH, dk, dk]: segment s's transport (slot s - 1)
 };
 
 // CK: what the scan stores.  kScanOut: the output rows (and the final state);
@@ -872,9 +876,9 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   const int dv = p.dv;
   const int nvt = dv / BV;
   // Workgroups per head: the d_v slices; split in segments, segment 0's
-  // slices, then segment 1's slices and its transport's d_k slices.
+  // slices, then each later segment's slices and its transport's d_k slices.
   static_assert(!SG || CK == kScanOut, "segments: the output instance only");
-  const int R = SG ? 2 * nvt + DK / BV : nvt;
+  const int R = SG ? nvt + (a.nseg - 1) * (nvt + DK / BV) : nvt;
   // Blocks of one (batch, head) land on one XCD (dispatch is round-robin over 8).
   const int b = blockIdx.x;
   const int grp = b / (8 * R), rem = b % (8 * R);
@@ -887,11 +891,14 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   int seg = 0, vt = role;
   bool tr = false;   // a transport slice: columns of I, no V
   if constexpr (SG) {
-    seg = role >= nvt ? 1 : 0;
-    tr = role >= 2 * nvt;
-    vt = role - (seg ? (tr ? 2 * nvt : nvt) : 0);
-    j0 = seg ? a.js : 0;
-    j1 = seg ? N : a.js;
+    if (role >= nvt) {
+      const int r = role - nvt, per = nvt + DK / BV;
+      seg = 1 + r / per;
+      tr = r % per >= nvt;
+      vt = r % per - (tr ? nvt : 0);
+    }
+    j0 = seg * a.L;
+    j1 = seg == a.nseg - 1 ? N : j0 + a.L;
   }
   const int c0 = vt * BV;
   const int tid = threadIdx.x;
@@ -914,11 +921,16 @@ __global__ __launch_bounds__(64 * NWV) void fast_scan_kernel(FastScanArgs a) {
   if constexpr (SG) {
     if (tr) {
       vbh = a.v + static_cast<size_t>(bh) * p.T * dv;
-      obh = a.U + static_cast<size_t>(bh) * (N - j0) * kC * DK + c0;
+      obh = a.U + static_cast<size_t>(bh) * (N - a.L) * kC * DK + c0;
       ost = sst = DK;
-      jb = j0;
+      jb = a.L;
     }
-    sfin = seg == 0 ? a.Smid : (a.Sfin ? (tr ? a.Tf : a.Sp) : nullptr);
+    // the last segment's final state matters only for the returned one
+    const bool keep = seg < a.nseg - 1 || a.Sfin;
+    sfin = seg == 0 ? a.Smid
+                    : (!keep ? nullptr
+                             : (tr ? a.Tf + static_cast<size_t>(seg - 1) * p.BH * DK * DK
+                                   : a.Sp + static_cast<size_t>(seg - 1) * p.BH * DK * dv));
   }
 
   bf16x8 mf[PD][MPW][KP];
@@ -1320,54 +1332,108 @@ hipError_t launch_prep(const Problem& p, const void* q, const void* k, const flo
 }
 
 // ---------------------------------------------------------------------------
-// The split scan's correction, from the state leaving segment 0 (Smid): every
-// output row of segment 1 gains U_j Smid (bf16 MFMAs with fp32 accumulation,
-// the sum rounded once), and the final state is Sp + Tf Smid (fp32).  One
-// four-wave workgroup per kSegFixG consecutive chunks of segment 1 (wave w:
-// the chunk's 16-token row block w), staging Smid once; with a final state,
-// first one workgroup per head for it (its serial sums then overlap the
-// chunks' workgroups instead of trailing them).
+// The split scan's correction.  The state entering segment s >= 1 is
+//   S_1 = Smid,  S_{s+1} = Sp_s + Tf_s S_s
+// (fp32, a fixed-order sum; fast_segchain_kernel forms S_s for s >= 2, one
+// workgroup per head).  Every output row of segment s then gains U_j S_s
+// (bf16 MFMAs with fp32 accumulation, the sum rounded once), and the final
+// state is Sp_last + Tf_last S_last (fp32).  fast_segfix_kernel: one
+// four-wave workgroup per kSegFixG consecutive chunks after segment 0 (wave
+// w: the chunk's 16-token row block w), staging S_s once per segment it
+// meets; with a final state, first one workgroup per head for it (its serial
+// sums then overlap the chunks' workgroups instead of trailing them).
 constexpr int kSegFixG = 8;
 struct SegFixArgs {
   Problem p;
-  int64_t js;
+  int64_t L;
+  int nseg;
   const __bf16* U;
   const float *Smid, *Sp, *Tf;
+  float* Sst;   // [nseg - 2][BH, dk, dv]: the state entering segment s >= 2 (slot s - 2)
   __bf16* out;
   float* Sfin;
 };
+
+// the state entering segment s >= 1 of head bh
+template <int DK>
+__device__ __forceinline__ const float* seg_start(const SegFixArgs& a, int s, int64_t bh) {
+  const size_t st = static_cast<size_t>(DK) * a.p.dv;
+  return s == 1 ? a.Smid + bh * st : a.Sst + (static_cast<size_t>(s - 2) * a.p.BH + bh) * st;
+}
+
+// out = Sp + Tf S over [DK][dv] (fp32, a fixed-order sum over k), 256 threads
+template <int DK>
+__device__ void seg_step(const float* Sp, const float* Tf, const float* S, float* out, int dv, int tid) {
+  for (int it = tid; it < DK * dv; it += 256) {
+    const int i = it / dv, c = it % dv;
+    float s = Sp[it];
+    for (int k = 0; k < DK; ++k) s += Tf[i * DK + k] * S[k * dv + c];
+    out[it] = s;
+  }
+}
+
+// Each step of the chain: Tf_s and S_s staged in LDS, a thread forming 4 x 4
+// blocks of S_{s+1} (d_v <= 128; the sum over k in a fixed order).
+template <int DK>
+__global__ __launch_bounds__(256) void fast_segchain_kernel(SegFixArgs a) {
+  __shared__ __align__(16) float Ts[DK * DK];
+  __shared__ __align__(16) float Ss[DK * 128];
+  const int64_t bh = blockIdx.x;
+  const int dv = a.p.dv, tid = threadIdx.x;
+  const size_t st = static_cast<size_t>(DK) * dv, tt = static_cast<size_t>(DK) * DK;
+  const int nb = dv / 4;   // 4-column blocks of a row block
+  for (int s = 1; s + 1 < a.nseg; ++s) {
+    const size_t slot = static_cast<size_t>(s - 1) * a.p.BH + bh;
+    const float* S = seg_start<DK>(a, s, bh);
+    for (int it = tid; it < DK * DK; it += 256) Ts[it] = a.Tf[slot * tt + it];
+    for (int it = tid; it < DK * dv; it += 256) Ss[it] = S[it];
+    __syncthreads();
+    for (int blk = tid; blk < (DK / 4) * nb; blk += 256) {
+      const int i0 = (blk / nb) * 4, cb = (blk % nb) * 4;
+      float acc[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = a.Sp[slot * st + (i0 + r) * dv + cb + c];
+      for (int k = 0; k < DK; ++k) {
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(Ss + k * dv + cb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = Ts[(i0 + r) * DK + k];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[r][c] += t * sv[c];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a.Sst[slot * st + (i0 + r) * dv + cb + c] = acc[r][c];
+    }
+    __syncthreads();   // the next step stages this one's rows (other threads')
+  }
+}
 
 template <int DK>
 __global__ __launch_bounds__(256) void fast_segfix_kernel(SegFixArgs a) {
   const Problem& p = a.p;
   const int dv = p.dv;
-  const int64_t N1 = p.N - a.js, NG = (N1 + kSegFixG - 1) / kSegFixG, nf = a.Sfin ? p.BH : 0;
+  const int64_t N1 = p.N - a.L, NG = (N1 + kSegFixG - 1) / kSegFixG, nf = a.Sfin ? p.BH : 0;
   const int64_t b = static_cast<int64_t>(blockIdx.x) - nf;
   const int tid = threadIdx.x;
   if (b < 0) {
-    // the final state of head bh (a fixed-order fp32 sum)
     const int64_t bh = b + nf;
-    const float* Sm = a.Smid + bh * DK * dv;
-    const float* Tf = a.Tf + bh * DK * DK;
-    for (int it = tid; it < DK * dv; it += 256) {
-      const int i = it / dv, c = it % dv;
-      float s = a.Sp[bh * DK * dv + it];
-      for (int k = 0; k < DK; ++k) s += Tf[i * DK + k] * Sm[k * dv + c];
-      a.Sfin[bh * DK * dv + it] = s;
-    }
+    const int last = a.nseg - 1;
+    const size_t slot = static_cast<size_t>(last - 1) * p.BH + bh;
+    seg_step<DK>(a.Sp + slot * DK * dv, a.Tf + slot * DK * DK, seg_start<DK>(a, last, bh), a.Sfin + bh * DK * dv,
+                 dv, tid);
     return;
   }
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int LDT = DK + 8;   // Smid^T row (bf16): value column c, K = d_k contiguous
+  constexpr int LDT = DK + 8;   // S_s^T row (bf16): value column c, K = d_k contiguous
   __bf16* St = reinterpret_cast<__bf16*>(smem);
   float* ob = reinterpret_cast<float*>(smem + static_cast<size_t>(dv) * LDT * 2);   // [C][dv + 4]
   const int LDO = dv + 4;
   const int64_t bh = b / NG, g0 = (b % NG) * kSegFixG;
-  const float* Sm = a.Smid + bh * DK * dv;
-  for (int it = tid; it < DK * dv; it += 256) {
-    const int i = it / dv, c = it % dv;
-    St[c * LDT + i] = (__bf16)Sm[it];
-  }
   const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int64_t g1 = g0 + kSegFixG < N1 ? g0 + kSegFixG : N1;
   // The next chunk's U rows and output rows are loaded while this chunk's
@@ -1382,7 +1448,7 @@ __global__ __launch_bounds__(256) void fast_segfix_kernel(SegFixArgs a) {
     const __bf16* Ur = a.U + ((bh * N1 + jl) * kC + 16 * w + lr) * DK + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(Ur + 32 * ks);
-    const int64_t j = a.js + jl;
+    const int64_t j = a.L + jl;
     const int n = static_cast<int>(p.T - j * kC < kC ? p.T - j * kC : kC);
     const __bf16* oj = a.out + (bh * p.T + j * kC) * dv;
 #pragma unroll
@@ -1392,10 +1458,21 @@ __global__ __launch_bounds__(256) void fast_segfix_kernel(SegFixArgs a) {
     }
   };
   load(g0);
+  int cur = 0;   // the segment whose entering state St holds
   for (int64_t jl = g0; jl < g1; ++jl) {
-    const int64_t j = a.js + jl;
+    const int64_t j = a.L + jl;
     const int n = static_cast<int>(p.T - j * kC < kC ? p.T - j * kC : kC);
-    __syncthreads();   // Smid^T staged; the previous chunk's rows are out of ob
+    const int sg = static_cast<int>(j / a.L);
+    if (sg != cur) {
+      __syncthreads();   // every wave is done with the previous segment's state
+      const float* Ss = seg_start<DK>(a, sg, bh);
+      for (int it = tid; it < DK * dv; it += 256) {
+        const int i = it / dv, c = it % dv;
+        St[c * LDT + i] = (__bf16)Ss[it];
+      }
+      cur = sg;
+    }
+    __syncthreads();   // St staged; the previous chunk's rows are out of ob
     for (int ct = 0; ct < dv / 16; ++ct) {
       f32x4 acc = zero4();
 #pragma unroll
@@ -1439,38 +1516,42 @@ hipError_t launch_scan(const Problem& p, const void* M, const void* v, void* out
   return hipGetLastError();
 }
 
-// Workspace of the split scan after the chunk operators: U, Smid, Sp, Tf.
+// Workspace of the split scan after the chunk operators: U, Smid, Sp, Tf, Sst.
 struct SegLayout {
-  int64_t js;
-  size_t u, smid, sp, tf, total;
+  int64_t L;
+  int nseg;
+  size_t u, smid, sp, tf, sst, total;
 };
 size_t seg_align(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-SegLayout seg_layout(const Problem& p) {
+SegLayout seg_layout(const Problem& p, int nseg) {
   SegLayout l{};
-  // segment 1 starts at an even chunk (the scan's ring of two), near the middle
-  l.js = ((p.N + 1) / 2 + 1) & ~static_cast<int64_t>(1);
+  l.nseg = nseg;
+  // segments of L chunks, L even (the scan's ring of two), the last one shorter
+  l.L = ((p.N + nseg - 1) / nseg + 1) & ~static_cast<int64_t>(1);
   const size_t st = static_cast<size_t>(p.BH) * p.dk * p.dv * 4;
   l.u = 0;
-  l.smid = seg_align(static_cast<size_t>(p.BH) * (p.N - l.js) * kC * p.dk * 2);
+  l.smid = seg_align(static_cast<size_t>(p.BH) * (p.N - l.L) * kC * p.dk * 2);
   l.sp = l.smid + seg_align(st);
-  l.tf = l.sp + seg_align(st);
-  l.total = l.tf + seg_align(static_cast<size_t>(p.BH) * p.dk * p.dk * 4);
+  l.tf = l.sp + seg_align((nseg - 1) * st);
+  l.sst = l.tf + seg_align(static_cast<size_t>(nseg - 1) * p.BH * p.dk * p.dk * 4);
+  l.total = l.sst + seg_align((nseg > 2 ? nseg - 2 : 0) * st);
   return l;
 }
 
 template <int DK, int BV, int NWV, int PD>
-hipError_t launch_scan_seg(const Problem& p, const void* M, const void* v, void* out, float* Sfin, const float* S0,
-                           char* scratch, hipStream_t s) {
+hipError_t launch_scan_seg(const Problem& p, int nseg, const void* M, const void* v, void* out, float* Sfin,
+                           const float* S0, char* scratch, hipStream_t s) {
   using Cfg = ScanCfg<DK, BV, NWV, PD>;
-  const SegLayout l = seg_layout(p);
+  const SegLayout l = seg_layout(p, nseg);
   FastScanArgs a{p, static_cast<const __bf16*>(M), static_cast<const __bf16*>(v), static_cast<__bf16*>(out), Sfin, S0,
                  nullptr};
-  a.js = l.js;
+  a.L = l.L;
+  a.nseg = nseg;
   a.U = reinterpret_cast<__bf16*>(scratch + l.u);
   a.Smid = reinterpret_cast<float*>(scratch + l.smid);
   a.Sp = reinterpret_cast<float*>(scratch + l.sp);
   a.Tf = reinterpret_cast<float*>(scratch + l.tf);
-  const int R = 2 * (p.dv / BV) + DK / BV;
+  const int nvt = p.dv / BV, R = nvt + (nseg - 1) * (nvt + DK / BV);
   const int64_t groups = (p.BH + 7) / 8;
   const void* fn = reinterpret_cast<const void*>(fast_scan_kernel<DK, BV, NWV, PD, kScanOut, true>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
@@ -1478,8 +1559,13 @@ hipError_t launch_scan_seg(const Problem& p, const void* M, const void* v, void*
   hipLaunchKernelGGL((fast_scan_kernel<DK, BV, NWV, PD, kScanOut, true>), dim3(groups * 8 * R), dim3(Cfg::NT),
                      Cfg::LDS, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  SegFixArgs f{p, l.js, a.U, a.Smid, a.Sp, a.Tf, static_cast<__bf16*>(out), Sfin};
-  const int64_t blocks = p.BH * ((p.N - l.js + kSegFixG - 1) / kSegFixG) + (Sfin ? p.BH : 0);
+  SegFixArgs f{p, l.L, nseg, a.U, a.Smid, a.Sp, a.Tf, reinterpret_cast<float*>(scratch + l.sst),
+               static_cast<__bf16*>(out), Sfin};
+  if (nseg > 2) {
+    hipLaunchKernelGGL(fast_segchain_kernel<DK>, dim3(static_cast<unsigned>(p.BH)), dim3(256), 0, s, f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t blocks = p.BH * ((p.N - l.L + kSegFixG - 1) / kSegFixG) + (Sfin ? p.BH : 0);
   const size_t lds = static_cast<size_t>(p.dv) * (DK + 8) * 2 + static_cast<size_t>(kC) * (p.dv + 4) * 4;
   hipLaunchKernelGGL(fast_segfix_kernel<DK>, dim3(blocks), dim3(256), lds, s, f);
   return hipGetLastError();
@@ -1492,21 +1578,25 @@ bool fast_supported(const Problem& p) {
          (p.dk == 64 || p.dk == 128) && (p.dv % 64 == 0);
 }
 
-// The forward scan splits the sequence in two (fast_scan) where at d_k = 64
-// its 16-column d_v slices leave the chip's 256 compute units short of work:
-// the split scan takes 64-column slices (every slice reads the whole chunk
-// operator, so wide slices keep that traffic down), and its workgroups, one
-// per compute unit, must all be resident (d_v <= 128).
+// The forward scan splits the sequence in segments (fast_scan) where at
+// d_k = 64 its 16-column d_v slices leave the chip's 256 compute units short
+// of work: the split scan takes 64-column slices (every slice reads the whole
+// chunk operator, so wide slices keep that traffic down), and its workgroups,
+// one per compute unit, must all be resident (d_v <= 128).  As many segments
+// as that allows, up to three, each of at least 32 chunks.
 int fast_scan_segments(const Problem& p) {
   constexpr int64_t kCUs = 256;
-  if (!fast_supported(p) || p.dk != 64 || p.dv > 128 || p.N < 64) return 1;
-  const int64_t one = p.BH * (p.dv / 16), two = p.BH * (2 * (p.dv / 64) + 1);
-  return one < kCUs && two <= kCUs ? 2 : 1;
+  if (!fast_supported(p) || p.dk != 64 || p.dv > 128 || p.BH * (p.dv / 16) >= kCUs) return 1;
+  const int64_t nvt = p.dv / 64;
+  for (int n = 3; n >= 2; --n)
+    if (p.BH * (nvt + (n - 1) * (nvt + 1)) <= kCUs && p.N >= 32 * n) return n;
+  return 1;
 }
 
 size_t fast_forward_bytes(const Problem& p) {
   const size_t ops = fast_workspace_bytes(p);
-  return fast_scan_segments(p) == 2 ? seg_align(ops) + seg_layout(p).total : ops;
+  const int n = fast_scan_segments(p);
+  return n > 1 ? seg_align(ops) + seg_layout(p, n).total : ops;
 }
 
 size_t fast_workspace_bytes(const Problem& p) {
@@ -1572,10 +1662,10 @@ hipError_t fast_scan(const Problem& p, const void* workspace, const void* v, voi
     if (p.dk == 64) return launch_scan<64, 16, 4, 4, kScanBoth>(p, workspace, v, out, Sfin, S0, ckpt, s);
     return hipErrorInvalidValue;
   }
-  // Split in two sequence segments (d_k = 64, few heads): the scratch after
-  // the chunk operators, as fast_forward_bytes counts it.
-  if (fast_scan_segments(p) == 2)
-    return launch_scan_seg<64, 64, 8, 2>(p, workspace, v, out, Sfin, S0,
+  // Split in sequence segments (d_k = 64, few heads): the scratch after the
+  // chunk operators, as fast_forward_bytes counts it.
+  if (const int nseg = fast_scan_segments(p); nseg > 1)
+    return launch_scan_seg<64, 64, 8, 2>(p, nseg, workspace, v, out, Sfin, S0,
                                          static_cast<char*>(const_cast<void*>(workspace)) +
                                              seg_align(fast_workspace_bytes(p)),
                                          s);

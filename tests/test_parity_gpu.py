@@ -82,16 +82,19 @@ FAST_CASES = [
 ]
 
 
-# d_k = 64 with at least 64 chunks and few (batch, head) rows: the scan splits
-# the sequence in two segments, the second corrected with the state leaving
-# the first (odd chunk counts, ragged tails, an exact multiple, d_v 64 and 128,
-# ranks 0-2, both decay modes).
+# d_k = 64 with few (batch, head) rows: the scan splits the sequence in two
+# (from 64 chunks) or three (from 96 chunks) segments, each later one
+# corrected with the state entering it (odd chunk counts, ragged tails, exact
+# multiples, d_v 64 and 128, ranks 0-2, both decay modes, with and without
+# the final state).
 SPLIT_CASES = [
     # B, H, T, dk, dv, r_ab, decay, final state returned
     (1, 2, 4133, 64, 64, 2, "channel", True),
     (1, 1, 4096, 64, 128, 0, "channel", True),
     (2, 1, 5000, 64, 64, 1, "scalar", True),
     (1, 3, 8192, 64, 64, 2, "channel", False),
+    (1, 2, 6500, 64, 64, 2, "channel", True),
+    (1, 1, 7000, 64, 128, 1, "scalar", True),
 ]
 
 
@@ -109,10 +112,10 @@ def test_split_scan_parity(case):
     ref_out, ref_S = oracle.generic(raw["q"], raw["K"], raw["V"], raw["log_decay"], raw["A"], raw["B"],
                                     initial_state=S0)
     e_o = rel_err(host(out), ref_out)
-    # the second segment alone (the corrected rows)
-    half = T // 2
-    e_h = rel_err(host(out)[:, :, half:], ref_out[:, :, half:])
-    print(f"out {e_o:.2e} second half {e_h:.2e}", flush=True)
+    # the last third alone (corrected rows in every split)
+    tail = T - T // 3
+    e_h = rel_err(host(out)[:, :, tail:], ref_out[:, :, tail:])
+    print(f"out {e_o:.2e} last third {e_h:.2e}", flush=True)
     assert e_o <= TOL["bf16"] and e_h <= TOL["bf16"]
     if fin:
         e_s = rel_err(host(S), ref_S)
