@@ -286,7 +286,9 @@ size_t lattn_chunk_bwd_workspace_size(const lattn_dims* dims, int r_ab, int r_kv
  * lattn_chunk_fwd_train_saved_size returns 0, and a caller uses
  * lattn_chunk_fwd and lattn_chunk_bwd).
  * lattn_chunk_fwd_train: arguments and results as lattn_chunk_fwd (out and
- *   final_state computed by the same kernels, so equal to its results), plus
+ *   final_state computed by the same kernels, so equal to its results, except
+ *   at the shapes where lattn_chunk_fwd splits its state scan into sequence
+ *   segments, d_k = 64 with few heads, which rounds differently), plus
  *   saved: caller-owned device memory of lattn_chunk_fwd_train_saved_size()
  *   bytes, fully written; no other workspace is needed.
  * lattn_chunk_bwd_saved: arguments and results as lattn_chunk_bwd (equal to

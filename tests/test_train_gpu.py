@@ -111,9 +111,12 @@ def test_training_pair_rejects_off_route_shapes():
 @pytest.mark.parametrize("name", ["hdla_bf16", "gdn_bf16", "hdla_long_bf16"])
 def test_training_pair_full_size_equals_the_plain_calls(name):
     """Every bf16 workload at full size, in the launch configuration the bench
-    times: the training pair's outputs and gradients equal lattn_chunk_fwd's and
-    lattn_chunk_bwd's on every (batch, head), bit for bit (the oracle checks of
-    those calls carry over)."""
+    times: the training pair's gradients equal lattn_chunk_bwd's on every
+    (batch, head), bit for bit (the oracle checks of that call carry over), and
+    its outputs equal lattn_chunk_fwd's, bit for bit where that call runs the
+    scan unsplit; where it splits the scan into sequence segments (d_k = 64,
+    few heads: the long-context workload) the two round differently and must
+    agree within the bf16 gate."""
     import bench
     spec = workloads.CONFIGS[name]
     print(f"training pair full size {name}", flush=True)
@@ -126,7 +129,17 @@ def test_training_pair_full_size_equals_the_plain_calls(name):
     dfin = torch.randn((spec.B, spec.H, spec.dk, spec.dv), device=dev0, generator=g)
     out, fin = lattn.chunk_fwd(q, K, V, ld, A, B, chunk=spec.chunk)
     out_t, fin_t, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=spec.chunk)
-    assert torch.equal(out, out_t) and torch.equal(fin, fin_t)
+    # the forward's workspace beyond the chunk operators: the split scan's
+    ops = spec.B * spec.H * -(-spec.T // spec.chunk) * ((spec.dk + spec.chunk) // 16) ** 2 * 512
+    split = lattn.workspace_size(spec.B, spec.H, spec.T, spec.dk, spec.dv, spec.r_ab, 1, spec.chunk) > ops
+    print(f"forward scan split: {split}", flush=True)
+    if split:
+        rel = lambda x, y: float((x.float() - y.float()).abs().max() / y.float().abs().max())
+        e_o, e_s = rel(out_t, out), rel(fin_t, fin)
+        print(f"training forward against the split forward: out {e_o:.2e} state {e_s:.2e}", flush=True)
+        assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+    else:
+        assert torch.equal(out, out_t) and torch.equal(fin, fin_t)
     del out, fin, out_t, fin_t
     gr = lattn.chunk_bwd(q, K, V, ld, A, B, dout, chunk=spec.chunk, dfinal=dfin)
     gs = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dout, saved, chunk=spec.chunk, dfinal=dfin)
