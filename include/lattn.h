@@ -150,7 +150,13 @@ int lattn_chunk_fwd_check(const lattn_dims* dims, const void* q, const void* k, 
  *   carrying the d_k x d_v state: per chunk one product gives the next state
  *   and the chunk's outputs (HDLA note, "Overall framework": serial chunk-state
  *   checkpoints, then chunk outputs).  Reads v and the workspace written by
- *   lattn_chunk_prepare with the same dims, ranks and chunk.
+ *   lattn_chunk_prepare with the same dims, ranks and chunk.  On the bf16 path
+ *   at d_k = 64 with few heads it splits each sequence into up to three
+ *   segments walked side by side: each later segment from a zero state beside
+ *   the product of its chunks' transitions (the composition of the chunks'
+ *   affine maps, HLA note, "Affine maps and closure under composition"), then
+ *   its outputs and final state corrected with the state entering it; that
+ *   part of the workspace is scratch for the call.
  */
 int lattn_chunk_prepare(const lattn_dims* dims, const void* q, const void* k,
                         const float* log_decay, const void* A, const void* B, int r_ab, int r_kv,
