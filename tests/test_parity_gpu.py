@@ -267,6 +267,16 @@ def test_determinism_bitwise():
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
 
 
+def test_split_scan_determinism_bitwise():
+    """The scan split in three segments (its correction and chained entering
+    states included) gives bitwise equal results on a second call."""
+    raw = workloads.generic_raw(1, 2, 6500, 64, 64, 2, 1, "bf16", "channel", seed=11)
+    S0 = (np.random.default_rng(12).standard_normal((1, 2, 64, 64)) * 0.1).astype(np.float32)
+    o1, s1 = _gpu_generic(raw, "bf16", 64, S0)
+    o2, s2 = _gpu_generic(raw, "bf16", 64, S0)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
 @pytest.mark.parametrize("dtype,r_ab,r_kv,T", [("fp32", 2, 1, 150), ("fp32", 3, 2, 70), ("bf16", 1, 1, 130)])
 def test_chunk_summaries(dtype, r_ab, r_kv, T):
     raw = workloads.generic_raw(1, 2, T, 64, 32, r_ab, r_kv, dtype, "channel", seed=8)
