@@ -364,44 +364,41 @@ def backward_flops(spec):
 
 def backward_leg(spec, raw, inputs, torch, lattn, dev):
     """lattn_chunk_bwd on the benchmark workload (same inputs as the forward,
-    seeded output cotangents and a final-state cotangent), one timed call after
-    one warm-up, HIP events on its stream.  At this shape it is the chunked
-    backward on bf16 MFMAs: the chunk operators, the boundary scans (states
-    forward, cotangents in reverse), then per chunk the forward and adjoint UT
-    solves and the gradient products; flops are their dense-size count
-    (backward_flops), priced against the bf16 MFMA peak."""
+    seeded output cotangents and a final-state cotangent), through a TrainPlan
+    (gradients, workspace and the saved buffer allocated once, as the forward's
+    ChunkPlan does): one warm-up call, then the mean of three timed calls, HIP
+    events on the stream.  At this shape it is the chunked backward on bf16
+    MFMAs: the chunk operators, the boundary scans (states forward, cotangents
+    in reverse), then per chunk the forward and adjoint UT solves and the
+    gradient products; flops are their dense-size count (backward_flops),
+    priced against the bf16 MFMA peak.  The training pair is timed the same way
+    on the same plan."""
     q, K, V, ld, A, B = inputs
     td = q.dtype
     rng = np.random.default_rng(1)
     dout = torch.from_numpy(rng.standard_normal((spec.B, spec.H, spec.T, spec.dv), dtype=np.float32)).to(td).to(dev)
     dfin = torch.from_numpy(rng.standard_normal((spec.B, spec.H, spec.dk, spec.dv), dtype=np.float32)).to(dev)
-    run = lambda: lattn.chunk_bwd(q, K, V, ld, A, B, dout, chunk=spec.chunk, dfinal=dfin)
-    run()
+    plan = lattn.TrainPlan(q, K, V, ld, A, B, dout, chunk=spec.chunk, dfinal=dfin)
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    e0.record(stream)
-    run()
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1)
-    flops = backward_flops(spec)
-    # The training pair: the forward that keeps the chunk operators and the
-    # decay-scaled operands, and the backward that reads them instead of
-    # running the prepare again (same inputs, same cotangents).
-    def timed(fn, reps=2):
+
+    def timed(fn, reps=3):
         fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize(dev)
         a.record(stream)
         for _ in range(reps):
-            r = fn()
+            fn()
         b.record(stream)
         torch.cuda.synchronize(dev)
-        return a.elapsed_time(b) / reps, r
-    fwd_ms, (_, _, saved) = timed(lambda: lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=spec.chunk))
-    bwd_ms, _ = timed(lambda: lattn.chunk_bwd_saved(q, K, V, ld, A, B, dout, saved, chunk=spec.chunk, dfinal=dfin))
-    del saved
+        return a.elapsed_time(b) / reps
+    ms = timed(plan.backward)
+    flops = backward_flops(spec)
+    # The training pair: the forward that keeps the chunk operators, the
+    # decay-scaled operands and the boundary states, and the backward that
+    # reads them instead of forming them again (same inputs, same cotangents).
+    fwd_ms = timed(plan.forward_train)
+    bwd_ms = timed(plan.backward_saved)
+    del plan
     return {
         "entry": "lattn_chunk_bwd",
         "kind": "chunked backward on bf16 MFMAs: boundary scans, forward and adjoint UT solves, gradient products",

@@ -21,7 +21,7 @@ __all__ = [
     "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
     "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
     "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd", "loglinear_fwd", "loglinear_levels", "chunk_bwd",
-    "chunk_fwd_train", "chunk_bwd_saved", "train_saved_size",
+    "chunk_fwd_train", "chunk_bwd_saved", "train_saved_size", "TrainPlan",
 ]
 
 
@@ -558,6 +558,67 @@ class ChunkPlan:
                                       self.ws_bytes, _stream(self.device))
         _lib.check(rc, "lattn_chunk_fwd")
         return self.out, self.final_state
+
+
+class TrainPlan:
+    """Pre-marshalled arguments of the backward and of the training pair on one
+    set of inputs and cotangents, for repeated calls with no per-call Python
+    work (outputs, gradients, workspaces and the saved buffer allocated once).
+
+    ``backward()`` is ``chunk_bwd``; ``forward_train()`` then
+    ``backward_saved()`` is ``chunk_fwd_train`` then ``chunk_bwd_saved`` (on
+    the shapes the training pair takes: ``self.saved`` is None elsewhere).
+    """
+
+    def __init__(self, q, k, v, log_decay, A, B, dout, chunk=64, dfinal=None, initial_state=None):
+        Bb, H, T, dk = q.shape
+        k, v, self.r_ab, self.r_kv, self.grads = _bwd_inputs(q, k, v, log_decay, A, B, dout, dfinal, initial_state)
+        dv = v.shape[-1]
+        self.chunk = chunk
+        self.dims = make_dims(Bb, H, T, dk, dv, _dtype_code(q), log_decay.dim() == 3)
+        self.lib = _lib.load()
+        d = ctypes.byref(self.dims)
+        size = lambda fn: int(getattr(self.lib, fn)(d, self.r_ab, self.r_kv, chunk))
+        self.ws_bytes = size("lattn_chunk_bwd_workspace_size")
+        self.saved_bytes = size("lattn_chunk_fwd_train_saved_size")
+        self.sws_bytes = size("lattn_chunk_bwd_saved_workspace_size")
+        self.workspace = _workspace(q.device, self.ws_bytes)
+        self.saved = _workspace(q.device, self.saved_bytes)
+        self.saved_workspace = _workspace(q.device, self.sws_bytes)
+        self.out = torch.empty((Bb, H, T, dv), dtype=q.dtype, device=q.device)
+        self.final_state = torch.empty((Bb, H, dk, dv), dtype=torch.float32, device=q.device)
+        self._keep = (q, k, v, log_decay, A, B, dout, dfinal, initial_state)
+        g = self.grads
+        self.p = dict(q=_ptr(q), k=_ptr(k), v=_ptr(v), ld=_ptr(log_decay), A=_ptr(A), B=_ptr(B), do=_ptr(dout),
+                      df=_ptr(dfinal), S0=_ptr(initial_state), ws=_ptr(self.workspace), sv=_ptr(self.saved),
+                      sws=_ptr(self.saved_workspace), out=_ptr(self.out), Sf=_ptr(self.final_state),
+                      g=[_ptr(g[n]) for n in ("dq", "dk", "dv", "dlog_decay", "dA", "dB", "dinitial_state")])
+        self.device = q.device
+
+    def backward(self):
+        p = self.p
+        rc = self.lib.lattn_chunk_bwd(ctypes.byref(self.dims), p["q"], p["k"], p["v"], p["ld"], p["A"], p["B"],
+                                      self.r_ab, self.r_kv, self.chunk, p["do"], p["df"], p["S0"], *p["g"],
+                                      p["ws"], self.ws_bytes, _stream(self.device))
+        _lib.check(rc, "lattn_chunk_bwd")
+        return self.grads
+
+    def forward_train(self):
+        p = self.p
+        rc = self.lib.lattn_chunk_fwd_train(ctypes.byref(self.dims), p["q"], p["k"], p["v"], p["ld"], p["A"],
+                                            p["B"], self.r_ab, self.r_kv, self.chunk, p["out"], p["Sf"], p["S0"],
+                                            p["sv"], self.saved_bytes, _stream(self.device))
+        _lib.check(rc, "lattn_chunk_fwd_train")
+        return self.out, self.final_state
+
+    def backward_saved(self):
+        p = self.p
+        rc = self.lib.lattn_chunk_bwd_saved(ctypes.byref(self.dims), p["q"], p["k"], p["v"], p["ld"], p["A"],
+                                            p["B"], self.r_ab, self.r_kv, self.chunk, p["do"], p["df"], p["sv"],
+                                            self.saved_bytes, *p["g"], p["sws"], self.sws_bytes,
+                                            _stream(self.device))
+        _lib.check(rc, "lattn_chunk_bwd_saved")
+        return self.grads
 
 
 class FamilyPlan:

@@ -150,3 +150,27 @@ def test_training_pair_full_size_equals_the_plain_calls(name):
         else:
             assert torch.isfinite(gr[n]).all(), n
             assert torch.equal(gr[n], gs[n]), n
+
+
+def test_train_plan_matches_the_calls():
+    """TrainPlan (pre-marshalled, as the bench times it) gives the results of
+    chunk_bwd, chunk_fwd_train and chunk_bwd_saved, bit for bit."""
+    raw, dout, S0, dfin = _inputs((1, 2, 150, 64, 64, 2, "channel", True))
+    q, K, V = dev(raw["q"], BF), dev(raw["K"], BF), dev(raw["V"], BF)
+    ld, A, B = dev(raw["log_decay"]), dev(raw["A"], BF), dev(raw["B"], BF)
+    S0d, dfd, dod = dev(S0), dev(dfin), dev(dout, BF)
+    plan = lattn.TrainPlan(q, K, V, ld, A, B, dod, chunk=64, dfinal=dfd, initial_state=S0d)
+    g_plan = {n: (None if t is None else t.clone()) for n, t in plan.backward().items()}
+    out_p, fin_p = (t.clone() for t in plan.forward_train())
+    gs_plan = plan.backward_saved()
+    g = lattn.chunk_bwd(q, K, V, ld, A, B, dod, chunk=64, dfinal=dfd, initial_state=S0d)
+    out_t, fin_t, saved = lattn.chunk_fwd_train(q, K, V, ld, A, B, chunk=64, initial_state=S0d)
+    gs = lattn.chunk_bwd_saved(q, K, V, ld, A, B, dod, saved, chunk=64, dfinal=dfd)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_t) and torch.equal(fin_p, fin_t)
+    for n in g:
+        if g[n] is None:
+            assert g_plan[n] is None and gs_plan[n] is None, n
+        else:
+            assert torch.equal(g_plan[n], g[n]), n
+            assert torch.equal(gs_plan[n], gs[n]), n
