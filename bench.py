@@ -65,8 +65,8 @@ def canonical_work(spec):
 
 def kernel_work(spec, kernels):
     """Per-launch algorithmic work of each kernel of the two-stage decomposition,
-    on the survey's per-token-head byte count split by which kernel reads or
-    writes each tensor:
+    on the canonical per-token-head byte count (the inputs read once, the
+    outputs written once) split by which kernel reads or writes each tensor:
 
     prepare: reads q, K, A, B and the log-decay;
     scan:    reads V, writes out and the final state.
@@ -563,7 +563,7 @@ def time_forward(plan, torch, dev, steps, warmup):
 
 def roofline(spec, kernels, kernel_ms):
     """The dominant kernel against the roofline that bounds it: its share of the
-    survey's algorithmic bytes (or of the flops its decomposition performs)
+    canonical algorithmic bytes (or of the flops its decomposition performs)
     divided by its event-timed duration, against the published peak."""
     kw = kernel_work(spec, kernels)
     dom = max(kernel_ms, key=kernel_ms.get)
