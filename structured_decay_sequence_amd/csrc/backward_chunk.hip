@@ -244,6 +244,7 @@ struct BcGroupArgs {
   BcBufs w;
   void* outa;                   // right-hand side (bf16, tile order) or the first kind's gradient (fp32)
   void* outb;                   // the second kind's gradient, or the adjoint right-hand side (bf16, tile order)
+  void* outc;                   // the (dK, dA) group: dV, from its fused last term on top of dV1's partial
   const float* init;            // dV2: dV1's partial, the accumulators' start
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
@@ -286,8 +287,10 @@ __device__ __forceinline__ void bc_afrag(const Problem& p, int64_t job, int rb0,
 // R consecutive 16-row blocks (rb0 ..) of kind KIND's product for chunk job,
 // B side in LDS: acc[r] (accumulator layout: lane holds rows 4 lg + e of
 // block rb0 + r, column 16 ot + lr).  Every B-side fragment read from LDS
-// serves the R blocks, so waves of two blocks halve those reads.
-template <int KIND, int DK, int DV, int RAB, int R>
+// serves the R blocks, so waves of two blocks halve those reads.  T2:
+// where another kind's staging holds the second term's operands (offsets
+// and row strides of B2, C2), or -1 for the kind's own layout.
+template <int KIND, int DK, int DV, int RAB, int R, int OB2X = -1, int LB2X = -1, int OC2X = -1, int LC2X = -1>
 __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
                                         const cb8 (&af)[R][BcKindCfg<KIND, DK, DV, RAB>::KA / 32], const __bf16* lds,
                                         cf4 (&acc)[R][BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane,
@@ -327,8 +330,9 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
 #pragma unroll
   for (int r = 0; r < R; ++r) trow[r] = (r0 + 16 * r + lr) / K::RA;
   // one score term: NB columns (RB rows of B per token), mask, sign
-  auto term = [&](int oB, int oC, auto nb_, auto rb_, auto mask_, float sg) {
+  auto term = [&](int oB, int oC, auto nb_, auto rb_, auto mask_, float sg, auto lb_, auto lc_) {
     constexpr int NBc = decltype(nb_)::value, RB = decltype(rb_)::value, MASK = decltype(mask_)::value;
+    constexpr int LBt = decltype(lb_)::value, LCt = decltype(lc_)::value;
 #pragma unroll 1
     for (int c0 = 0; c0 < NBc; c0 += 32) {
       if (bc_empty<MASK>(ta0, ta1, c0 / RB, (c0 + 31) / RB)) continue;
@@ -339,7 +343,7 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
         for (int r = 0; r < R; ++r) s2[r][h] = cz4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const cb8 bfr = rowfrag(lds + oB + (c0 + 16 * h + lr) * L::LB, ks, lane);
+          const cb8 bfr = rowfrag(lds + oB + (c0 + 16 * h + lr) * LBt, ks, lane);
 #pragma unroll
           for (int r = 0; r < R; ++r) s2[r][h] = mfma_b(bfr, af[r][ks], s2[r][h]);
         }
@@ -355,18 +359,23 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
       for (int r = 0; r < R; ++r) sf[r] = cat8(to_b4(s2[r][0]), to_b4(s2[r][1]));
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot) {
-        const cb8 cf = cat8(ltr4(lds + oC, L::LC, c0, 16 * ot, lane), ltr4(lds + oC, L::LC, c0 + 16, 16 * ot, lane));
+        const cb8 cf = cat8(ltr4(lds + oC, LCt, c0, 16 * ot, lane), ltr4(lds + oC, LCt, c0 + 16, 16 * ot, lane));
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r][ot] = mfma_b(sf[r], cf, acc[r][ot]);
       }
     }
   };
   using I1 = std::integral_constant<int, 1>;
+  using LB = std::integral_constant<int, L::LB>;
+  using LC = std::integral_constant<int, L::LC>;
   if constexpr (K::T1)
-    term(L::OB1, L::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f);
+    term(L::OB1, L::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f, LB{},
+         LC{});
   if constexpr (K::TERM2)
-    term(L::OB2, L::OC2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
-         std::integral_constant<int, K::MSK2>{}, -1.f);
+    term(OB2X < 0 ? L::OB2 : OB2X, OC2X < 0 ? L::OC2 : OC2X, std::integral_constant<int, NA>{},
+         std::integral_constant<int, (RAB > 0 ? RAB : 1)>{}, std::integral_constant<int, K::MSK2>{}, -1.f,
+         std::integral_constant<int, (LB2X < 0 ? L::LB : LB2X)>{},
+         std::integral_constant<int, (LC2X < 0 ? L::LC : LC2X)>{});
 }
 
 // A gradient kind's rows from the LDS copy of the products (ep: M rows of
@@ -601,10 +610,17 @@ struct BcGroupWaves {
   // the first kind's one per wave every SIMD holds
   // three blocks, and their B-side reads serve two blocks.
   static constexpr int RB = (KB_ == kDa || KB_ == kDb || KB_ == kRhsX) ? 2 : 1;
+  // The (dK, dA) group also forms dV's last term, -M_>(K~ B~^T) X, whose
+  // operands B~ and X it stages anyway (its own C2 and B2): one wave per
+  // 16-token block (WC of them).
+  template <int RAB>
+  static constexpr bool fuse_dv2() { return KA_ == kDk && RAB > 0; }
+  template <int RAB>
+  static constexpr int wc() { return fuse_dv2<RAB>() ? kCC / 16 : 0; }
   template <int DK, int DV, int RAB>
   static constexpr int count() {
     return BcKindCfg<KA_, DK, DV, RAB>::M / 16 +
-           (KB_ >= 0 ? BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::M / (16 * RB) : 0);
+           (KB_ >= 0 ? BcKindCfg<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>::M / (16 * RB) : 0) + wc<RAB>();
   }
   // output rows of the group (both kinds)
   template <int DK, int DV, int RAB>
@@ -636,12 +652,21 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   const bool isa = wave < WA;
   constexpr int RB = BcGroupWaves<KA_, KB_>::RB;
   constexpr int KB2 = KB_ >= 0 ? KB_ : KA_;
+  // the fused dV2 waves come last
+  constexpr bool FDV2 = BcGroupWaves<KA_, KB_>::template fuse_dv2<RAB>();
+  constexpr int WC = BcGroupWaves<KA_, KB_>::template wc<RAB>();
+  using KC = BcKindCfg<kDv2, DK, DV, RAB>;
+  constexpr int KSC = KC::KA / 32, OTC = KC::NOUT / 16;
+  const bool isc = FDV2 && wave >= NW - WC;
   // first 16-row block of this wave within its kind
-  const int rb = isa ? wave : (wave - WA) * RB;
+  const int rb = isa ? wave : (isc ? wave - (NW - WC) : (wave - WA) * RB);
   // this wave's A rows first, so that their loads overlap the staging's
   cb8 af[RB][KS];
+  cb8 afc[1][KSC];
   if (isa) {
     bc_afrag<KA_, DK, DV, RAB, 1>(p, job, rb, a.Aa, reinterpret_cast<cb8(&)[1][KS]>(af), lane);
+  } else if (isc) {
+    if constexpr (FDV2) bc_afrag<kDv2, DK, DV, RAB, 1>(p, job, rb, BcSrc{a.w.kt, kSrcChunk}, afc, lane);
   } else if constexpr (KB_ >= 0) {
     bc_afrag<KB_, DK, DV, RAB, RB>(p, job, rb, a.Ab, af, lane);
   }
@@ -694,14 +719,19 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   }
   __syncthreads();
   cf4 acc[RB][OT];
+  cf4 accc[1][OTC];
   // rows of padding tokens only: no gradient to write (the right-hand sides
   // are formed for them too, as zeros, since the solves read every row)
-  const int ra = isa ? K::RA : BcKindCfg<KB2, DK, DV, RAB>::RA;
-  const bool live = RHS || 16 * rb / ra < n;
+  const int ra = isa || isc ? 1 : BcKindCfg<KB2, DK, DV, RAB>::RA;
+  const bool live = RHS || 16 * rb / (isa ? K::RA : ra) < n;
   if (live) {
     if (isa) {
       bc_prod<KA_, DK, DV, RAB, 1>(p, job, rb, reinterpret_cast<const cb8(&)[1][KS]>(af), lds,
                                    reinterpret_cast<cf4(&)[1][OT]>(acc), lane, a.init);
+    } else if (isc) {
+      // dV2 on top of dV1's partial: B~ is this group's C2, X its B2
+      if constexpr (FDV2)
+        bc_prod<kDv2, DK, DV, RAB, 1, L::OC2, L::LC, L::OB2, L::LB>(p, job, rb, afc, lds, accc, lane, a.w.dv1);
     } else if constexpr (KB_ >= 0) {
       bc_prod<KB_, DK, DV, RAB, RB>(p, job, rb, af, lds, acc, lane, a.init);
     }
@@ -739,19 +769,31 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     BcEpi<KA_ == kDk, DK, RAB, 64 * NW> epi;
     if constexpr (GRAD) epi.load(p, job, a.w, a.xr, a.rr, tid);
     __syncthreads();   // every wave is done with the staged operands
+    // the fused dV2 rows (d_v + 4 floats each) after both kinds' rows
+    float* epc = ep + BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>() * LE;
     if (live) {
       const int lr = lane & 15, lg = lane >> 4;
+      if (isc) {
+        if constexpr (FDV2) {
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (isa && r > 0) break;
-        const int blk = isa ? rb : WA + rb + r;
+          for (int ot = 0; ot < OTC; ++ot)
 #pragma unroll
-        for (int ot = 0; ot < OT; ++ot)
+            for (int e = 0; e < 4; ++e) epc[(rb * 16 + 4 * lg + e) * (DV + 4) + 16 * ot + lr] = accc[0][ot][e];
+        }
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ep[(blk * 16 + 4 * lg + e) * LE + 16 * ot + lr] = acc[r][ot][e];
+        for (int r = 0; r < RB; ++r) {
+          if (isa && r > 0) break;
+          const int blk = isa ? rb : WA + rb + r;
+#pragma unroll
+          for (int ot = 0; ot < OT; ++ot)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ep[(blk * 16 + 4 * lg + e) * LE + 16 * ot + lr] = acc[r][ot][e];
+        }
       }
     }
     __syncthreads();
+    if constexpr (FDV2) bc_out<kDv2, DK, DV, RAB, 64 * NW>(p, job, epc, static_cast<float*>(a.outc), tid);
     if constexpr (GRAD) {
       static_assert(K::M == kCC && LE == DK + 4, "fused epilogue: token rows, then rank rows, of width d_k");
       float* terms = ep + BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>() * LE;   // dQ group: beyond the products
@@ -1118,7 +1160,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
                    void* outa, void* outb, const void* xr = nullptr, const void* rr = nullptr,
-                   const float* init = nullptr) -> hipError_t {
+                   const float* init = nullptr, void* outc = nullptr) -> hipError_t {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
@@ -1127,12 +1169,14 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     // the products' copy, and the dQ group's decay-gradient terms beyond it
     const size_t ep_b = static_cast<size_t>(BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>()) * (L::NOUT + 4) *
                             sizeof(float) +
-                        (KA_ == kDq ? BcEpi<false, DK, RAB, 64 * NW>::EXTRA : 0);
+                        (KA_ == kDq ? BcEpi<false, DK, RAB, 64 * NW>::EXTRA : 0) +
+                        static_cast<size_t>(BcGroupWaves<KA_, KB_>::template wc<RAB>()) * 16 * (DV + 4) * sizeof(float);
     const size_t lds = stage_b > ep_b ? stage_b : ep_b;
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, init, bf(xr), bf(rr), bf(ckpt), dld});
+                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, outc, init, bf(xr), bf(rr), bf(ckpt),
+                                   dld});
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
@@ -1147,8 +1191,9 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3((jobs + 7) / 8 * 16), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
                        BcSolveArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // (with dV's last term, -M_>(K~ B~^T) X, on top of the first two)
     if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
-                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A)) != hipSuccess)
+                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A, nullptr, dV)) != hipSuccess)
       return e;
     if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, Os, chunk(w.x), Sin, Vs,
                    chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB, q, B)) != hipSuccess)
@@ -1161,12 +1206,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
                    nullptr, q, nullptr)) != hipSuccess)
       return e;
   }
-  if constexpr (RAB > 0) {
-    // dV's last term, -M_>(K~ B~^T) X, on top of the first two
-    if ((e = group(std::integral_constant<int, kDv2>{}, KN{}, chunk(w.kt), none, none, none, none, chunk(w.bt),
-                   chunk(w.x), dV, nullptr, nullptr, nullptr, w.dv1)) != hipSuccess)
-      return e;
-  } else {
+  if constexpr (RAB == 0) {
     if ((e = group(std::integral_constant<int, kDv>{}, KN{}, chunk(w.kt), none, GdS, chunk(w.qt), Os, none, none, dV,
                    nullptr)) != hipSuccess)
       return e;
