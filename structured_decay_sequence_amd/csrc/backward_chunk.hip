@@ -24,14 +24,15 @@
 //                    + rowdot(dS_end, S_end) on the chunk's last token.
 // S_in and dS_end come from the chunk-boundary scans.
 //
-// Kernels, each over all chunks, in order (the scaled operands come from the
-// forward's prepare kernel, which forms them anyway): G (base 2) and Gamma;
-// the grouped products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i of the
-// forward right-hand side, and of dV's first two terms with the adjoint
-// right-hand side; the solve (the blocks of L and the inverses of its unit
-// diagonal blocks in LDS, then Y by forward and X by backward substitution,
-// one wave per 16 value columns); the grouped products of dK with dA, of dQ
-// with dB, and of dV's last term.  A product group
+// Kernels, each over all chunks, in order (the scaled operands, G (base 2),
+// Gamma, the blocks of L and the inverses of its unit diagonal blocks come
+// from the forward's prepare kernel, which forms them anyway): the grouped
+// products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i of the forward
+// right-hand side, and of dV's first two terms with the adjoint right-hand
+// side; the solve (Y by forward and X by backward substitution, one
+// workgroup each per chunk, one wave per 16 value columns); the grouped
+// products of dK with dA (and dV's last term, whose operands that group
+// stages anyway), and of dQ with dB.  A product group
 // stages its chunk's B-side operands in LDS row-major, straight from where
 // they live (the prepare's arrays, the V and dO rows of the sequence, the
 // bf16 boundary states and cotangents); operands needed transposed are read
@@ -182,7 +183,8 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
 // each wave forms 16 rows of one kind's output, its A rows read from memory.
 // The pairs: (dK, dA), (dQ, dB), and at r_ab > 0 (the adjoint right-hand side,
 // dV's first two terms), since those read the same operands; dV's last term
-// (dV2, which needs the adjoint solve's X) then runs on its own.
+// (dV2, which needs the adjoint solve's X) runs as a third role of the (dK,
+// dA) group, whose staged B2 and C2 are its X and B~.
 enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6, kDv1 = 7, kDv2 = 8 };
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
 // Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
