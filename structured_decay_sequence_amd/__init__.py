@@ -21,7 +21,7 @@ __all__ = [
     "chunk_fwd", "chunk_summaries", "step", "hdla_params", "gdn_params", "decay_range",
     "check_decay_range", "workspace_size", "make_dims", "LattnError", "version", "ChunkPlan",
     "hdla_chunk_fwd", "gdn_chunk_fwd", "FamilyPlan", "hla_fwd", "loglinear_fwd", "loglinear_levels", "chunk_bwd",
-    "chunk_fwd_train", "chunk_bwd_saved", "train_saved_size", "TrainPlan",
+    "chunk_fwd_train", "chunk_bwd_saved", "train_saved_size", "TrainPlan", "chunk_attention",
 ]
 
 
@@ -650,3 +650,53 @@ class FamilyPlan:
         rc = self.fn(ctypes.byref(self.dims), *self.args, _stream(self.device))
         _lib.check(rc, f"lattn_{self.name}_chunk_fwd")
         return self.out, self.final_state
+
+
+class _ChunkAttention(torch.autograd.Function):
+    """chunk_fwd as an autograd function: the forward keeps what the backward
+    needs (the training pair's saved buffer on its shapes, else the inputs),
+    the backward returns the gradients of every tensor input in its dtype."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, log_decay, A, B, initial_state, chunk):
+        Bb, H, T, dk = q.shape
+        r_ab = 0 if A is None else A.shape[-2]
+        r_kv = 1 if k.dim() == 4 else k.shape[-2]
+        saved = None
+        if train_saved_size(Bb, H, T, dk, v.shape[-1], r_ab, r_kv, chunk, q.dtype, log_decay.dim() == 3) > 0:
+            out, final_state, saved = chunk_fwd_train(q, k, v, log_decay, A, B, chunk=chunk,
+                                                      initial_state=initial_state)
+        else:
+            out, final_state = chunk_fwd(q, k, v, log_decay, A, B, chunk=chunk, initial_state=initial_state)
+        ctx.chunk = chunk
+        ctx.has_ab = A is not None
+        ctx.has_s0 = initial_state is not None
+        ctx.k_dim = k.dim()
+        ctx.v_dim = v.dim()
+        ctx.save_for_backward(q, k, v, log_decay, A, B, initial_state, saved)
+        return out, final_state
+
+    @staticmethod
+    def backward(ctx, dout, dfinal):
+        q, k, v, log_decay, A, B, initial_state, saved = ctx.saved_tensors
+        dout = (torch.zeros_like(q[..., :1]).expand(*q.shape[:-1], v.shape[-1]) if dout is None else dout)
+        dout = dout.to(q.dtype).contiguous()
+        dfinal = None if dfinal is None else dfinal.float().contiguous()
+        if saved is not None:
+            g = chunk_bwd_saved(q, k, v, log_decay, A, B, dout, saved, chunk=ctx.chunk, dfinal=dfinal)
+        else:
+            g = chunk_bwd(q, k, v, log_decay, A, B, dout, chunk=ctx.chunk, dfinal=dfinal,
+                          initial_state=initial_state)
+        cast = lambda t, like: None if t is None else t.reshape(like.shape).to(like.dtype)
+        return (cast(g["dq"], q), cast(g["dk"], k), cast(g["dv"], v), cast(g["dlog_decay"], log_decay),
+                cast(g["dA"], A) if ctx.has_ab else None, cast(g["dB"], B) if ctx.has_ab else None,
+                g["dinitial_state"] if ctx.has_s0 else None, None)
+
+
+def chunk_attention(q, k, v, log_decay, A=None, B=None, chunk: int = 64, initial_state=None):
+    """chunk_fwd with gradients through torch.autograd: returns (out,
+    final_state); out.backward(...) runs lattn_chunk_bwd_saved on the training
+    pair's shapes (bf16, chunk 64, r_kv 1, r_ab <= 2, d_k and d_v in {64, 128}),
+    lattn_chunk_bwd elsewhere.  Gradients come back in each input's dtype
+    (the library forms them in fp32)."""
+    return _ChunkAttention.apply(q, k, v, log_decay, A, B, initial_state, chunk)

@@ -174,3 +174,30 @@ def test_train_plan_matches_the_calls():
         else:
             assert torch.equal(g_plan[n], g[n]), n
             assert torch.equal(gs_plan[n], gs[n]), n
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_chunk_attention_autograd(dtype):
+    """chunk_attention through torch.autograd: its gradients are those of
+    lattn_chunk_bwd (through the training pair on the bf16 route, the plain
+    calls on the fp32 one) cast to the inputs' dtypes, for a loss on both the
+    outputs and the final state."""
+    td = BF if dtype == "bf16" else torch.float32
+    raw = workloads.generic_raw(1, 2, 150, 64, 64, 2, 1, dtype, "channel", seed=21)
+    rng = np.random.default_rng(22)
+    S0 = (rng.standard_normal((1, 2, 64, 64)) * 0.1).astype(np.float32)
+    wo = rng.standard_normal((1, 2, 150, 64)).astype(np.float32)
+    wf = rng.standard_normal((1, 2, 64, 64)).astype(np.float32)
+    leaf = lambda x, t=None: dev(x, t).requires_grad_(True)
+    q, K, V = leaf(raw["q"], td), leaf(raw["K"], td), leaf(raw["V"], td)
+    ld, A, B, s0 = leaf(raw["log_decay"]), leaf(raw["A"], td), leaf(raw["B"], td), leaf(S0)
+    out, fin = lattn.chunk_attention(q, K, V, ld, A, B, chunk=64, initial_state=s0)
+    loss = (out.float() * dev(wo)).sum() + (fin * dev(wf)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = lattn.chunk_bwd(q.detach(), K.detach(), V.detach(), ld.detach(), A.detach(), B.detach(),
+                          dev(wo, td), chunk=64, dfinal=dev(wf), initial_state=s0.detach())
+    torch.cuda.synchronize()
+    for t, n in ((q, "dq"), (K, "dk"), (V, "dv"), (ld, "dlog_decay"), (A, "dA"), (B, "dB"), (s0, "dinitial_state")):
+        assert t.grad is not None and t.grad.dtype == t.dtype and t.grad.shape == t.shape, n
+        assert torch.equal(t.grad, ref[n].reshape(t.shape).to(t.dtype)), n
