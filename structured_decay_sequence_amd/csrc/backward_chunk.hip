@@ -107,7 +107,6 @@ struct BcBufs {
   __bf16 *ry, *rx;           // right-hand sides in tile order [NA/16][dv/16][64 lanes][4], bf16
   __bf16 *y, *x;             // [NA][dv]
   float* gk;                 // [C][dk] the decay gradient's terms of the dK group
-  float* dv1;                // dV's first two terms, fp32 in tile order [C/16][dv/16][64 lanes][4] (r_ab > 0)
   float* ends;               // [dk] rowdot(dS_end, S_end), from the dK group's staging
 };
 
@@ -170,7 +169,6 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.x = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.gk = reinterpret_cast<float*>(take(J * cdk * 4));
-  t.dv1 = reinterpret_cast<float*>(take(p.r_ab > 0 ? J * kCC * p.dv * 4 : 0));
   t.ends = reinterpret_cast<float*>(take(J * p.dk * 4));
   if (b) *b = t;
   return off;
@@ -181,11 +179,11 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
 // A group is one or two kinds whose products read the same B-side operands
 // (W0, B1, C1, B2, C2): one workgroup per chunk stages them in LDS once, then
 // each wave forms 16 rows of one kind's output, its A rows read from memory.
-// The pairs: (dK, dA), (dQ, dB), and at r_ab > 0 (the adjoint right-hand side,
-// dV's first two terms), since those read the same operands; dV's last term
-// (dV2, which needs the adjoint solve's X) runs as a third role of the (dK,
-// dA) group, whose staged B2 and C2 are its X and B~.
-enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6, kDv1 = 7, kDv2 = 8 };
+// The pairs: (dK, dA) and (dQ, dB), since those read the same operands; at
+// r_ab > 0 dV (which needs the adjoint solve's X) runs as a third role of
+// the (dK, dA) group, whose staging holds all of its operands (BcDvInDk),
+// and the right-hand sides of the two solves run alone.
+enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 };
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
 // Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
 // solve; the sequence's own rows t0 .. t0 + C - 1 (bf16 [T][cols], zero past
@@ -204,13 +202,12 @@ struct BcKindCfg {
   static constexpr int M = ROWS_A ? NA : kCC;                                  // rows of A
   static constexpr int RA = ROWS_A ? RAB : 1;                                  // rows per token of A
   // value-column outputs (A rows over d_k)
-  static constexpr bool VOUT = KIND == kRhsY || KIND == kRhsX || KIND == kDv || KIND == kDv1 || KIND == kDv2;
+  static constexpr bool VOUT = KIND == kRhsY || KIND == kRhsX || KIND == kDv;
   static constexpr int KA = VOUT ? DK : DV;
   static constexpr int NOUT = VOUT ? DV : DK;
   static constexpr int MSK1 = (KIND == kRhsY || KIND == kDb) ? kLT : (KIND == kDq ? kLE : kGE);
-  // dV2 has only the second score term, on top of dV1's partial (INIT)
-  static constexpr bool HASW0 = KIND != kDv2, T1 = KIND != kDv2, INIT = KIND == kDv2;
-  static constexpr bool TERM2 = ((KIND >= kDq && KIND <= kDb) && RAB > 0) || KIND == kDv2;
+  static constexpr bool HASW0 = true, T1 = true;
+  static constexpr bool TERM2 = (KIND >= kDq && KIND <= kDb) && RAB > 0;
   static constexpr int MSK2 = KIND == kDq ? kLE : (KIND == kDb ? kLT : kGT);
   static constexpr float SIGN = (KIND == kDa || KIND == kDb) ? -1.f : 1.f;
   // W0 as it lives in memory: its transpose (S_in or Gamma dS_end for dQ, dK,
@@ -220,7 +217,7 @@ struct BcKindCfg {
   // where the shared operands live (see BcSrcKind)
   static constexpr int SW0 = (KIND == kRhsY || KIND == kDq || KIND == kDb) ? kSrcState : kSrcCotG;
   static constexpr int SB1 = (KIND == kDq || KIND == kDb || KIND == kDk || KIND == kDa) ? kSrcSeq : kSrcChunk;
-  static constexpr int SC1 = (KIND == kRhsY || KIND == kRhsX || KIND == kDv || KIND == kDv1) ? kSrcSeq : kSrcChunk;
+  static constexpr int SC1 = (KIND == kRhsY || KIND == kRhsX || KIND == kDv) ? kSrcSeq : kSrcChunk;
 };
 
 // LDS layout of a kind's staged operands (bf16 elements).  Rows read by
@@ -239,6 +236,26 @@ struct BcStage {
 };
 
 
+// Where a kind's product reads its B-side operands in LDS (offsets and row
+// strides, bf16 elements): by default its own staging layout; a kind that
+// runs inside another kind's group reads that group's staging instead.
+template <int KIND, int DK, int DV, int RAB>
+struct BcOwnPlace {
+  using L = BcStage<KIND, DK, DV, RAB>;
+  static constexpr int OW = L::OW, LW0 = L::LW0, OB1 = L::OB1, LB1 = L::LB, OC1 = L::OC1, LC1 = L::LC,
+                       OB2 = L::OB2, LB2 = L::LB, OC2 = L::OC2, LC2 = L::LC;
+};
+// dV (K~ Gamma dS_end + M_>=(K~ Q~^T) dO - M_>(K~ B~^T) X) inside the (dK, dA)
+// group, whose staging holds the same operands in other roles: Gamma dS_end
+// rows as its W0 (read transposed here), Q~ as its C1, dO as its B1, B~ as
+// its C2 and X as its B2.
+template <int DK, int DV, int RAB>
+struct BcDvInDk {
+  using L = BcStage<kDk, DK, DV, RAB>;
+  static constexpr int OW = L::OW, LW0 = L::LW0, OB1 = L::OC1, LB1 = L::LC, OC1 = L::OB1, LC1 = L::LB,
+                       OB2 = L::OC2, LB2 = L::LC, OC2 = L::OB2, LC2 = L::LB;
+};
+
 struct BcGroupArgs {
   Problem p;
   BcSrc Aa, Ab;                 // A rows of the two kinds (Ab unused for one kind)
@@ -247,7 +264,6 @@ struct BcGroupArgs {
   void* outa;                   // right-hand side (bf16, tile order) or the first kind's gradient (fp32)
   void* outb;                   // the second kind's gradient, or the adjoint right-hand side (bf16, tile order)
   void* outc;                   // the (dK, dA) group: dV, from its fused last term on top of dV1's partial
-  const float* init;            // dV2: dV1's partial, the accumulators' start
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
   float* dld;                   // dQ group: the log-decay gradient
@@ -289,38 +305,29 @@ __device__ __forceinline__ void bc_afrag(const Problem& p, int64_t job, int rb0,
 // R consecutive 16-row blocks (rb0 ..) of kind KIND's product for chunk job,
 // B side in LDS: acc[r] (accumulator layout: lane holds rows 4 lg + e of
 // block rb0 + r, column 16 ot + lr).  Every B-side fragment read from LDS
-// serves the R blocks, so waves of two blocks halve those reads.  T2:
-// where another kind's staging holds the second term's operands (offsets
-// and row strides of B2, C2), or -1 for the kind's own layout.
-template <int KIND, int DK, int DV, int RAB, int R, int OB2X = -1, int LB2X = -1, int OC2X = -1, int LC2X = -1>
+// serves the R blocks, so waves of two blocks halve those reads.  PL: where
+// the operands sit in LDS (BcOwnPlace, or another group's staging).
+template <int KIND, int DK, int DV, int RAB, int R, class PL = BcOwnPlace<KIND, DK, DV, RAB>>
 __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
                                         const cb8 (&af)[R][BcKindCfg<KIND, DK, DV, RAB>::KA / 32], const __bf16* lds,
-                                        cf4 (&acc)[R][BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane,
-                                        const float* init = nullptr) {
+                                        cf4 (&acc)[R][BcKindCfg<KIND, DK, DV, RAB>::NOUT / 16], int lane) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
-  using L = BcStage<KIND, DK, DV, RAB>;
   constexpr int KS = K::KA / 32, OT = K::NOUT / 16, NA = K::NA;
   const int lr = lane & 15, lg = lane >> 4;
   const int r0 = 16 * rb0;
 #pragma unroll
   for (int ot = 0; ot < OT; ++ot) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if constexpr (K::INIT)
-        acc[r][ot] =
-            *reinterpret_cast<const cf4*>(init + (((job * (K::M / 16) + rb0 + r) * OT + ot) * 64 + lane) * 4);
-      else
-        acc[r][ot] = cz4();
-    }
+    for (int r = 0; r < R; ++r) acc[r][ot] = cz4();
     if constexpr (K::HASW0) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         cb8 bw;
         if constexpr (K::W0T)
-          bw = rowfrag(lds + L::OW + (16 * ot + lr) * L::LW0, ks, lane);
+          bw = rowfrag(lds + PL::OW + (16 * ot + lr) * PL::LW0, ks, lane);
         else
-          bw = cat8(ltr4(lds + L::OW, L::LW0, 32 * ks, 16 * ot, lane),
-                    ltr4(lds + L::OW, L::LW0, 32 * ks + 16, 16 * ot, lane));
+          bw = cat8(ltr4(lds + PL::OW, PL::LW0, 32 * ks, 16 * ot, lane),
+                    ltr4(lds + PL::OW, PL::LW0, 32 * ks + 16, 16 * ot, lane));
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r][ot] = mfma_b(af[r][ks], bw, acc[r][ot]);
       }
@@ -368,16 +375,13 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
     }
   };
   using I1 = std::integral_constant<int, 1>;
-  using LB = std::integral_constant<int, L::LB>;
-  using LC = std::integral_constant<int, L::LC>;
   if constexpr (K::T1)
-    term(L::OB1, L::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f, LB{},
-         LC{});
+    term(PL::OB1, PL::OC1, std::integral_constant<int, kCC>{}, I1{}, std::integral_constant<int, K::MSK1>{}, 1.f,
+         std::integral_constant<int, PL::LB1>{}, std::integral_constant<int, PL::LC1>{});
   if constexpr (K::TERM2)
-    term(OB2X < 0 ? L::OB2 : OB2X, OC2X < 0 ? L::OC2 : OC2X, std::integral_constant<int, NA>{},
-         std::integral_constant<int, (RAB > 0 ? RAB : 1)>{}, std::integral_constant<int, K::MSK2>{}, -1.f,
-         std::integral_constant<int, (LB2X < 0 ? L::LB : LB2X)>{},
-         std::integral_constant<int, (LC2X < 0 ? L::LC : LC2X)>{});
+    term(PL::OB2, PL::OC2, std::integral_constant<int, NA>{}, std::integral_constant<int, (RAB > 0 ? RAB : 1)>{},
+         std::integral_constant<int, K::MSK2>{}, -1.f, std::integral_constant<int, PL::LB2>{},
+         std::integral_constant<int, PL::LC2>{});
 }
 
 // A gradient kind's rows from the LDS copy of the products (ep: M rows of
@@ -386,7 +390,7 @@ __device__ __forceinline__ void bc_prod(const Problem& p, int64_t job, int rb0,
 template <int KIND, int DK, int DV, int RAB, int NT>
 __device__ __forceinline__ void bc_out(const Problem& p, int64_t job, const float* ep, float* out, int tid) {
   using K = BcKindCfg<KIND, DK, DV, RAB>;
-  static_assert(KIND == kDv || KIND == kDv2, "the other gradients leave through bc_epi");
+  static_assert(KIND == kDv, "the other gradients leave through bc_epi");
   constexpr int C4 = K::NOUT / 4, LE = K::NOUT + 4, ITEMS = K::M * C4;
   const int64_t bh = job / p.N, t0 = (job % p.N) * kCC;
   const int n = static_cast<int>(p.T - t0 < kCC ? p.T - t0 : kCC);
@@ -612,13 +616,12 @@ struct BcGroupWaves {
   // the first kind's one per wave every SIMD holds
   // three blocks, and their B-side reads serve two blocks.
   static constexpr int RB = (KB_ == kDa || KB_ == kDb || KB_ == kRhsX) ? 2 : 1;
-  // The (dK, dA) group also forms dV's last term, -M_>(K~ B~^T) X, whose
-  // operands B~ and X it stages anyway (its own C2 and B2): one wave per
-  // 16-token block (WC of them).
+  // At r_ab > 0 the (dK, dA) group also forms dV, whose operands it stages
+  // anyway (BcDvInDk): one wave per 16-token block (WC of them).
   template <int RAB>
-  static constexpr bool fuse_dv2() { return KA_ == kDk && RAB > 0; }
+  static constexpr bool fuse_dv() { return KA_ == kDk && RAB > 0; }
   template <int RAB>
-  static constexpr int wc() { return fuse_dv2<RAB>() ? kCC / 16 : 0; }
+  static constexpr int wc() { return fuse_dv<RAB>() ? kCC / 16 : 0; }
   template <int DK, int DV, int RAB>
   static constexpr int count() {
     return BcKindCfg<KA_, DK, DV, RAB>::M / 16 +
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   constexpr int WA = K::M / 16, KS = K::KA / 32, OT = K::NOUT / 16;
   // groups whose outputs leave in tile order: the right-hand sides (bf16)
   // and dV1's partial (fp32)
-  constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX || KA_ == kDv1;
+  constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX;
   using LB_ = BcStage<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>;
   static_assert(LB_::OW == L::OW && LB_::OB1 == L::OB1 && LB_::OC1 == L::OC1 && LB_::OB2 == L::OB2 &&
                     LB_::OC2 == L::OC2 && LB_::LW0 == L::LW0 && LB_::LB == L::LB && LB_::LC == L::LC,
@@ -654,12 +657,12 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   const bool isa = wave < WA;
   constexpr int RB = BcGroupWaves<KA_, KB_>::RB;
   constexpr int KB2 = KB_ >= 0 ? KB_ : KA_;
-  // the fused dV2 waves come last
-  constexpr bool FDV2 = BcGroupWaves<KA_, KB_>::template fuse_dv2<RAB>();
+  // the fused dV waves come last
+  constexpr bool FDV = BcGroupWaves<KA_, KB_>::template fuse_dv<RAB>();
   constexpr int WC = BcGroupWaves<KA_, KB_>::template wc<RAB>();
-  using KC = BcKindCfg<kDv2, DK, DV, RAB>;
+  using KC = BcKindCfg<kDv, DK, DV, RAB>;
   constexpr int KSC = KC::KA / 32, OTC = KC::NOUT / 16;
-  const bool isc = FDV2 && wave >= NW - WC;
+  const bool isc = FDV && wave >= NW - WC;
   // first 16-row block of this wave within its kind
   const int rb = isa ? wave : (isc ? wave - (NW - WC) : (wave - WA) * RB);
   // this wave's A rows first, so that their loads overlap the staging's
@@ -668,7 +671,7 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   if (isa) {
     bc_afrag<KA_, DK, DV, RAB, 1>(p, job, rb, a.Aa, reinterpret_cast<cb8(&)[1][KS]>(af), lane);
   } else if (isc) {
-    if constexpr (FDV2) bc_afrag<kDv2, DK, DV, RAB, 1>(p, job, rb, BcSrc{a.w.kt, kSrcChunk}, afc, lane);
+    if constexpr (FDV) bc_afrag<kDv, DK, DV, RAB, 1>(p, job, rb, BcSrc{a.w.kt, kSrcChunk}, afc, lane);
   } else if constexpr (KB_ >= 0) {
     bc_afrag<KB_, DK, DV, RAB, RB>(p, job, rb, a.Ab, af, lane);
   }
@@ -729,30 +732,25 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   if (live) {
     if (isa) {
       bc_prod<KA_, DK, DV, RAB, 1>(p, job, rb, reinterpret_cast<const cb8(&)[1][KS]>(af), lds,
-                                   reinterpret_cast<cf4(&)[1][OT]>(acc), lane, a.init);
+                                   reinterpret_cast<cf4(&)[1][OT]>(acc), lane);
     } else if (isc) {
-      // dV2 on top of dV1's partial: B~ is this group's C2, X its B2
-      if constexpr (FDV2)
-        bc_prod<kDv2, DK, DV, RAB, 1, L::OC2, L::LC, L::OB2, L::LB>(p, job, rb, afc, lds, accc, lane, a.w.dv1);
+      // dV from this group's staged operands (BcDvInDk)
+      if constexpr (FDV) bc_prod<kDv, DK, DV, RAB, 1, BcDvInDk<DK, DV, RAB>>(p, job, rb, afc, lds, accc, lane);
     } else if constexpr (KB_ >= 0) {
-      bc_prod<KB_, DK, DV, RAB, RB>(p, job, rb, af, lds, acc, lane, a.init);
+      bc_prod<KB_, DK, DV, RAB, RB>(p, job, rb, af, lds, acc, lane);
     }
   }
   if constexpr (RHS) {
     // block blk of kind KIND in tile order: a right-hand side in bf16 (rounded
-    // as the solve's own products round the solved blocks), dV1's partial in
-    // fp32 (dV2 starts its accumulators from it)
+    // as the solve's own products round the solved blocks)
     auto tiles = [&](auto kind_, void* dst, int blk, const cf4(&t)[OT]) {
       constexpr int KD = decltype(kind_)::value;
-      using KC = BcKindCfg<KD, DK, DV, RAB>;
-      static_assert(KC::NOUT == K::NOUT, "tile outputs of one width");
+      using KT = BcKindCfg<KD, DK, DV, RAB>;
+      static_assert(KT::NOUT == K::NOUT, "tile outputs of one width");
 #pragma unroll
       for (int ot = 0; ot < OT; ++ot) {
-        const int64_t o = (((job * (KC::M / 16) + blk) * OT + ot) * 64 + lane) * 4;
-        if constexpr (KD == kDv1)
-          *reinterpret_cast<cf4*>(static_cast<float*>(dst) + o) = t[ot];
-        else
-          *reinterpret_cast<cb4*>(static_cast<__bf16*>(dst) + o) = to_b4(t[ot]);
+        const int64_t o = (((job * (KT::M / 16) + blk) * OT + ot) * 64 + lane) * 4;
+        *reinterpret_cast<cb4*>(static_cast<__bf16*>(dst) + o) = to_b4(t[ot]);
       }
     };
     if (isa) {
@@ -771,12 +769,12 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     BcEpi<KA_ == kDk, DK, RAB, 64 * NW> epi;
     if constexpr (GRAD) epi.load(p, job, a.w, a.xr, a.rr, tid);
     __syncthreads();   // every wave is done with the staged operands
-    // the fused dV2 rows (d_v + 4 floats each) after both kinds' rows
+    // the fused dV rows (d_v + 4 floats each) after both kinds' rows
     float* epc = ep + BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>() * LE;
     if (live) {
       const int lr = lane & 15, lg = lane >> 4;
       if (isc) {
-        if constexpr (FDV2) {
+        if constexpr (FDV) {
 #pragma unroll
           for (int ot = 0; ot < OTC; ++ot)
 #pragma unroll
@@ -795,7 +793,7 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (FDV2) bc_out<kDv2, DK, DV, RAB, 64 * NW>(p, job, epc, static_cast<float*>(a.outc), tid);
+    if constexpr (FDV) bc_out<kDv, DK, DV, RAB, 64 * NW>(p, job, epc, static_cast<float*>(a.outc), tid);
     if constexpr (GRAD) {
       static_assert(K::M == kCC && LE == DK + 4, "fused epilogue: token rows, then rank rows, of width d_k");
       float* terms = ep + BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>() * LE;   // dQ group: beyond the products
@@ -1162,7 +1160,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
   auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
                    void* outa, void* outb, const void* xr = nullptr, const void* rr = nullptr,
-                   const float* init = nullptr, void* outc = nullptr) -> hipError_t {
+                   void* outc = nullptr) -> hipError_t {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
@@ -1177,8 +1175,7 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, outc, init, bf(xr), bf(rr), bf(ckpt),
-                                   dld});
+                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, outc, bf(xr), bf(rr), bf(ckpt), dld});
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
@@ -1186,16 +1183,15 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
     if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
                    w.ry, nullptr)) != hipSuccess)
       return e;
-    // dV's first two terms and the adjoint right-hand side read the same operands
-    if ((e = group(std::integral_constant<int, kDv1>{}, std::integral_constant<int, kRhsX>{}, chunk(w.kt), chunk(w.at),
-                   GdS, chunk(w.qt), Os, none, none, w.dv1, w.rx)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, chunk(w.at), none, GdS, chunk(w.qt), Os, none, none,
+                   w.rx, nullptr)) != hipSuccess)
       return e;
     hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3((jobs + 7) / 8 * 16), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
                        BcSolveArgs{p, w});
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // (with dV's last term, -M_>(K~ B~^T) X, on top of the first two)
+    // (with dV, whose operands this group stages)
     if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
-                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A, nullptr, dV)) != hipSuccess)
+                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A, dV)) != hipSuccess)
       return e;
     if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, Os, chunk(w.x), Sin, Vs,
                    chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB, q, B)) != hipSuccess)
