@@ -28,11 +28,10 @@
 // Gamma, the blocks of L and the inverses of its unit diagonal blocks come
 // from the forward's prepare kernel, which forms them anyway): the grouped
 // products out = A W0 + sum_i s_i mask_i(A B_i^T) C_i of the forward
-// right-hand side, and of dV's first two terms with the adjoint right-hand
-// side; the solve (Y by forward and X by backward substitution, one
-// workgroup each per chunk, one wave per 16 value columns); the grouped
-// products of dK with dA (and dV's last term, whose operands that group
-// stages anyway), and of dQ with dB.  A product group
+// right-hand side and of the adjoint one, each group going on to its solve
+// (Y by forward and X by backward substitution, one wave per 16 value
+// columns); the grouped products of dK with dA (and dV, whose operands that
+// group stages anyway), and of dQ with dB.  A product group
 // stages its chunk's B-side operands in LDS row-major, straight from where
 // they live (the prepare's arrays, the V and dO rows of the sequence, the
 // bf16 boundary states and cotangents); operands needed transposed are read
@@ -104,7 +103,6 @@ struct BcBufs {
   __bf16 *at, *bt;           // [NA][dk]
   __bf16* lt;                // [NB (NB - 1) / 2][16][16] L below the diagonal blocks (bf16 tiles)
   float* di;                 // [NB][16][16] the inverses of the diagonal blocks I + L_ii (fp32)
-  __bf16 *ry, *rx;           // right-hand sides in tile order [NA/16][dv/16][64 lanes][4], bf16
   __bf16 *y, *x;             // [NA][dv]
   float* gk;                 // [C][dk] the decay gradient's terms of the dK group
   float* ends;               // [dk] rowdot(dS_end, S_end), from the dK group's staging
@@ -164,8 +162,6 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
   t.di = static_cast<float*>(o.di);
   t.gc = static_cast<float*>(o.gc);
   t.gam = static_cast<float*>(o.gam);
-  t.ry = reinterpret_cast<__bf16*>(take(J * ndv * 2));
-  t.rx = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.y = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.x = reinterpret_cast<__bf16*>(take(J * ndv * 2));
   t.gk = reinterpret_cast<float*>(take(J * cdk * 4));
@@ -261,8 +257,8 @@ struct BcGroupArgs {
   BcSrc Aa, Ab;                 // A rows of the two kinds (Ab unused for one kind)
   BcSrc W0, B1, C1, B2, C2;     // the shared B-side operands
   BcBufs w;
-  void* outa;                   // right-hand side (bf16, tile order) or the first kind's gradient (fp32)
-  void* outb;                   // the second kind's gradient, or the adjoint right-hand side (bf16, tile order)
+  void* outa;                   // the solved rank rows Y or X (bf16, [NA][d_v]), or the first kind's gradient (fp32)
+  void* outb;                   // the second kind's gradient
   void* outc;                   // the (dK, dA) group: dV, from its fused last term on top of dV1's partial
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
@@ -609,13 +605,141 @@ struct BcEpi {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Solve, inside the right-hand side's own group.  Once the products are done
+// the group's waves put the right-hand side's tiles (bf16, rounded as the
+// substitution's own products round the solved blocks), the blocks of L and
+// the inverses of its diagonal blocks in the LDS the staging used, then each
+// wave solves 16 columns of values.
+//  * The blocks of L = M_<(Bt At^T) (rank rows; tokens row / r_ab) come from
+//    the prepare, which formed them for the forward's own solve: the 16x16
+//    bf16 tiles below the diagonal and the fp32 inverses D_i of the diagonal
+//    blocks I + L_ii.  Their loads are issued after the staging's, and held
+//    in registers through the products; the X group stores them transposed.
+//  * Y: forward substitution Y_i = D_i (R_i - sum_{j<i} L_ij Y_j); X: backward
+//    substitution X_i = D_i^T (R_i - sum_{j>i} L_ji^T X_j).  The products pair
+//    two 16-row blocks into one 16x16x32 MFMA (a lone block padded with
+//    zeros), the solved blocks fed back from registers as the B operand; the
+//    diagonal inverses apply in fp32.
+template <int DK, int DV, int RAB>
+struct BcSolveCfg {
+  static constexpr int NA = kCC * RAB, NB = NA / 16, NTI = NB * (NB > 0 ? NB - 1 : 0) / 2;
+  static constexpr int NCT = DV / 16;
+  // LDS (bytes): L's tiles (bf16), the diagonal blocks' inverses (fp32), the
+  // right-hand side in tile order [NB][NCT][64 lanes][4] (bf16)
+  static constexpr int OL = 0, ODI = OL + NTI * 512, ORH = ODI + NB * 1024, LDS = ORH + NA * DV * 2;
+  // 16-byte pieces of the tiles and of the inverses
+  static constexpr int NLP = NTI * 32, NDP = NB * 64;
+};
+
+template <int DK, int DV, int RAB, int NT>
+struct BcSolveStg {
+  using Cf = BcSolveCfg<DK, DV, RAB>;
+  static constexpr int NIT = (Cf::NLP + Cf::NDP + NT - 1) / NT > 0 ? (Cf::NLP + Cf::NDP + NT - 1) / NT : 1;
+  cb8 pc[NIT];
+  __device__ __forceinline__ void load(const BcBufs& w, int64_t job, int tid) {
+    const cb8* gl = reinterpret_cast<const cb8*>(w.lt + job * Cf::NTI * 256);
+    const cb8* gd = reinterpret_cast<const cb8*>(w.di + job * Cf::NB * 256);
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+      const int it = tid + q * NT;
+      if (it < Cf::NLP) pc[q] = gl[it];
+      else if (it < Cf::NLP + Cf::NDP) pc[q] = gd[it - Cf::NLP];
+    }
+  }
+  // the pieces as loaded (Y), or every tile transposed (X)
+  template <bool TR>
+  __device__ __forceinline__ void store(unsigned char* sm, int tid) const {
+    __bf16* Lb = reinterpret_cast<__bf16*>(sm + Cf::OL);
+    float* Di = reinterpret_cast<float*>(sm + Cf::ODI);
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+      const int it = tid + q * NT;
+      if (it < Cf::NLP) {
+        if constexpr (TR) {
+          // tile it / 32, row (it % 32) / 2, columns 8 (it % 2) .. + 7
+          const int b0 = (it >> 5) * 256, r = (it >> 1) & 15, c0 = (it & 1) * 8;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) Lb[b0 + (c0 + u) * 16 + r] = pc[q][u];
+        } else {
+          *reinterpret_cast<cb8*>(Lb + it * 8) = pc[q];
+        }
+      } else if (it < Cf::NLP + Cf::NDP) {
+        const int i2 = it - Cf::NLP;
+        if constexpr (TR) {
+          // block i2 / 64, row (i2 % 64) / 4, columns 4 (i2 % 4) .. + 3
+          const cf4 f = __builtin_bit_cast(cf4, pc[q]);
+          const int b0 = (i2 >> 6) * 256, r = (i2 >> 2) & 15, c0 = (i2 & 3) * 4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Di[b0 + (c0 + u) * 16 + r] = f[u];
+        } else {
+          *reinterpret_cast<cb8*>(Di + i2 * 4) = pc[q];
+        }
+      }
+    }
+  }
+};
+
+// The substitution over the LDS above: wave wv solves the value column tiles
+// wv, wv + NW, .. and writes them to out ([NA][d_v], bf16).
+template <int DK, int DV, int RAB, bool ISX, int NW>
+__device__ __forceinline__ void bc_substitute(const unsigned char* sm, __bf16* out, int wave, int lane) {
+  using Cf = BcSolveCfg<DK, DV, RAB>;
+  constexpr int NB = Cf::NB, NCT = Cf::NCT;
+  const __bf16* Lt = reinterpret_cast<const __bf16*>(sm + Cf::OL);
+  const float* Dg = reinterpret_cast<const float*>(sm + Cf::ODI);
+  const __bf16* R = reinterpret_cast<const __bf16*>(sm + Cf::ORH);
+  const int lr = lane & 15, lg = lane >> 4;
+  auto ltile = [&](int blk) { return *reinterpret_cast<const cb4*>(Lt + blk * 256 + lr * 16 + 4 * lg); };
+  for (int ct = wave; ct < NCT; ct += NW) {
+    cb4 nb[NB];   // -solution blocks in bf16, the B operand of later blocks
+    auto rhs = [&](int i) {
+      const cb4 r = *reinterpret_cast<const cb4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
+      return cf4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+    };
+    auto finish = [&](int i, cf4 acc) {
+      const cf4 dF = *reinterpret_cast<const cf4*>(Dg + i * 256 + lr * 16 + 4 * lg);
+      cf4 o = cz4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dF[e], acc[e], o, 0, 0, 0);
+      nb[i] = to_b4(cf4{-o[0], -o[1], -o[2], -o[3]});
+      // lane holds rows 16 i + 4 lg + e, column 16 ct + lr
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(16 * i + 4 * lg + e) * DV + 16 * ct + lr] = (__bf16)o[e];
+    };
+    if constexpr (!ISX) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        cf4 acc = rhs(i);
+        const int base = i * (i - 1) / 2;   // tiles (i, 0 .. i-1)
+#pragma unroll
+        for (int jb = 0; jb + 1 < i; jb += 2)
+          acc = mfma_b(cat8(ltile(base + jb), ltile(base + jb + 1)), cat8(nb[jb], nb[jb + 1]), acc);
+        if (i % 2 == 1) acc = mfma_b(cat8(ltile(base + i - 1), zb4()), cat8(nb[i - 1], zb4()), acc);
+        finish(i, acc);
+      }
+    } else {
+#pragma unroll
+      for (int i = NB - 1; i >= 0; --i) {
+        cf4 acc = rhs(i);
+        // tiles (L_ji)^T for j = i+1 .. NB-1, stored at index j (j - 1) / 2 + i
+        int jb = i + 1;
+#pragma unroll
+        for (; jb + 1 < NB; jb += 2)
+          acc = mfma_b(cat8(ltile(jb * (jb - 1) / 2 + i), ltile((jb + 1) * jb / 2 + i)), cat8(nb[jb], nb[jb + 1]), acc);
+        if (jb < NB) acc = mfma_b(cat8(ltile(jb * (jb - 1) / 2 + i), zb4()), cat8(nb[jb], zb4()), acc);
+        finish(i, acc);
+      }
+    }
+  }
+}
+
 template <int KA_, int KB_>
 struct BcGroupWaves {
   // 16-row blocks per wave of the second kind: the rank-row gradients (dA,
-  // dB, and the adjoint right-hand side beside dV1) take two, so that with
-  // the first kind's one per wave every SIMD holds
-  // three blocks, and their B-side reads serve two blocks.
-  static constexpr int RB = (KB_ == kDa || KB_ == kDb || KB_ == kRhsX) ? 2 : 1;
+  // dB) take two, so that with the first kind's one per wave every SIMD
+  // holds three blocks, and their B-side reads serve two blocks.
+  static constexpr int RB = (KB_ == kDa || KB_ == kDb) ? 2 : 1;
   // At r_ab > 0 the (dK, dA) group also forms dV, whose operands it stages
   // anyway (BcDvInDk): one wave per 16-token block (WC of them).
   template <int RAB>
@@ -639,9 +763,9 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   using K = BcKindCfg<KA_, DK, DV, RAB>;
   using L = BcStage<KA_, DK, DV, RAB>;
   constexpr int WA = K::M / 16, KS = K::KA / 32, OT = K::NOUT / 16;
-  // groups whose outputs leave in tile order: the right-hand sides (bf16)
-  // and dV1's partial (fp32)
+  // the right-hand side groups, which go on to solve (bc_substitute)
   constexpr bool RHS = KA_ == kRhsY || KA_ == kRhsX;
+  static_assert(!RHS || KB_ < 0, "a right-hand side group holds one kind");
   using LB_ = BcStage<(KB_ >= 0 ? KB_ : KA_), DK, DV, RAB>;
   static_assert(LB_::OW == L::OW && LB_::OB1 == L::OB1 && LB_::OC1 == L::OC1 && LB_::OB2 == L::OB2 &&
                     LB_::OC2 == L::OC2 && LB_::LW0 == L::LW0 && LB_::LB == L::LB && LB_::LC == L::LC,
@@ -696,6 +820,9 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     s3.load(a.B2.ptr, nullptr, job, n, tok0, tid);
     s4.load(a.C2.ptr, nullptr, job, n, tok0, tid);
   }
+  // the solve's blocks of L and diagonal inverses, held through the products
+  BcSolveStg<DK, DV, RAB, 64 * NW> ss;
+  if constexpr (RHS) ss.load(a.w, job, tid);
   if constexpr (K::HASW0) s0.store(lds + L::OW, L::LW0, tid);
   if constexpr (K::T1) {
     s1.store(lds + L::OB1, L::LB, tid);
@@ -741,24 +868,17 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     }
   }
   if constexpr (RHS) {
-    // block blk of kind KIND in tile order: a right-hand side in bf16 (rounded
-    // as the solve's own products round the solved blocks)
-    auto tiles = [&](auto kind_, void* dst, int blk, const cf4(&t)[OT]) {
-      constexpr int KD = decltype(kind_)::value;
-      using KT = BcKindCfg<KD, DK, DV, RAB>;
-      static_assert(KT::NOUT == K::NOUT, "tile outputs of one width");
+    // the right-hand side's tiles, L's blocks and the diagonal inverses into
+    // the staging space, then the substitution, one value column tile a wave
+    using SC = BcSolveCfg<DK, DV, RAB>;
+    static_assert(K::M == SC::NA && K::NOUT == DV && OT == SC::NCT && NW == SC::NB, "solve tiling");
+    __syncthreads();   // every wave is done with the staged operands
+    __bf16* rt = reinterpret_cast<__bf16*>(smem_ + SC::ORH);
 #pragma unroll
-      for (int ot = 0; ot < OT; ++ot) {
-        const int64_t o = (((job * (KT::M / 16) + blk) * OT + ot) * 64 + lane) * 4;
-        *reinterpret_cast<cb4*>(static_cast<__bf16*>(dst) + o) = to_b4(t[ot]);
-      }
-    };
-    if (isa) {
-      tiles(std::integral_constant<int, KA_>{}, a.outa, rb, acc[0]);
-    } else if constexpr (KB_ >= 0) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) tiles(std::integral_constant<int, KB_>{}, a.outb, rb + r, acc[r]);
-    }
+    for (int ot = 0; ot < OT; ++ot) *reinterpret_cast<cb4*>(rt + ((rb * OT + ot) * 64 + lane) * 4) = to_b4(acc[0][ot]);
+    ss.template store<KA_ == kRhsX>(smem_, tid);
+    __syncthreads();
+    bc_substitute<DK, DV, RAB, KA_ == kRhsX, NW>(smem_, static_cast<__bf16*>(a.outa) + job * SC::NA * DV, wave, lane);
   } else {
     // The gradients leave through LDS as whole rows: every wave's 16-row
     // blocks of NOUT columns into the (now free) staging space (the first
@@ -805,135 +925,6 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
     } else {
       static_assert(KB_ < 0, "dV runs alone");
       bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, static_cast<float*>(a.outa), tid);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Solve: two workgroups per chunk (Y and X), one wave per 16 value columns.
-//  * The blocks of L = M_<(Bt At^T) (rank rows; tokens row / r_ab) come from
-//    the prepare, which formed them for the forward's own solve: the 16x16
-//    bf16 tiles below the diagonal and the fp32 inverses D_i of the diagonal
-//    blocks I + L_ii.  They are staged in LDS with their transposes.
-//  * Y: forward substitution Y_i = D_i (R_i - sum_{j<i} L_ij Y_j); X: backward
-//    substitution X_i = D_i^T (R_i - sum_{j>i} L_ji^T X_j).  The products pair
-//    two 16-row blocks into one 16x16x32 MFMA (a lone block padded with
-//    zeros), the solved blocks fed back from registers as the B operand; the
-//    diagonal inverses apply in fp32.
-// The right-hand sides' loads are issued first, so they overlap the staging.
-struct BcSolveArgs {
-  Problem p;
-  BcBufs w;
-};
-
-template <int DK, int DV, int RAB>
-struct BcSolveCfg {
-  static constexpr int NA = kCC * RAB, NB = NA / 16, NT = NB * (NB + 1) / 2, NTI = NB * (NB - 1) / 2;
-  static constexpr int NCT = DV / 16, NW = NCT;
-  // LDS (bytes): L tiles and their transposes (bf16), the diagonal blocks'
-  // inverses and their transposes (fp32)
-  static constexpr int OL = 0, OLT = OL + NTI * 512, ODI = OLT + NTI * 512, ODT = ODI + NB * 1024,
-                       LDS = ODT + NB * 1024;
-  // 16-byte pieces of the tiles and the inverses, and per thread
-  static constexpr int NLP = NTI * 32, NDP = NB * 64, NIT = (NLP + NDP + 64 * NW - 1) / (64 * NW);
-};
-
-template <int DK, int DV, int RAB>
-__global__ __launch_bounds__((64 * BcSolveCfg<DK, DV, RAB>::NW)) void bwc_solve_kernel(BcSolveArgs a) {
-  using Cf = BcSolveCfg<DK, DV, RAB>;
-  constexpr int NA = Cf::NA, NB = Cf::NB, NT = Cf::NT, NCT = Cf::NCT, NW = Cf::NW;
-  __shared__ __align__(16) unsigned char sm[Cf::LDS];
-  __bf16* Lb = reinterpret_cast<__bf16*>(sm + Cf::OL);
-  __bf16* LbT = reinterpret_cast<__bf16*>(sm + Cf::OLT);
-  float* Di = reinterpret_cast<float*>(sm + Cf::ODI);
-  float* DiT = reinterpret_cast<float*>(sm + Cf::ODT);
-  // Blocks b and b + 8 land on one XCD (dispatch is round-robin over 8): a
-  // chunk's Y and X workgroups take such a pair, so the blocks of L they both
-  // read meet in one L2.
-  const int64_t b = blockIdx.x;
-  const int64_t job = (b >> 4) * 8 + (b & 7);
-  if (job >= a.p.BH * a.p.N) return;
-  const bool isx = (b >> 3) & 1;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
-  const BcBufs& w = a.w;
-  const int ct = wave;
-  // this wave's right-hand side tiles, loaded first
-  const __bf16* R = (isx ? w.rx : w.ry) + job * NA * DV;
-  cb4 rhb[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) rhb[i] = *reinterpret_cast<const cb4*>(R + ((i * NCT + ct) * 64 + lane) * 4);
-  // L's tiles below the diagonal and the diagonal blocks' inverses as the
-  // prepare formed them (the same blocks its forward solve used): every load
-  // issued before any write, then the transposes the adjoint solve reads
-  {
-    const cb8* gl = reinterpret_cast<const cb8*>(w.lt + job * Cf::NTI * 256);
-    const cb8* gd = reinterpret_cast<const cb8*>(w.di + job * NB * 256);
-    cb8 pc[Cf::NIT];
-#pragma unroll
-    for (int q = 0; q < Cf::NIT; ++q) {
-      const int it = tid + q * 64 * NW;
-      if (it < Cf::NLP) pc[q] = gl[it];
-      else if (it < Cf::NLP + Cf::NDP) pc[q] = gd[it - Cf::NLP];
-    }
-#pragma unroll
-    for (int q = 0; q < Cf::NIT; ++q) {
-      const int it = tid + q * 64 * NW;
-      if (it < Cf::NLP) *reinterpret_cast<cb8*>(Lb + it * 8) = pc[q];
-      else if (it < Cf::NLP + Cf::NDP) *reinterpret_cast<cb8*>(Di + (it - Cf::NLP) * 4) = pc[q];
-    }
-  }
-  __syncthreads();
-  if (isx) {
-    for (int idx = tid; idx < Cf::NTI * 256; idx += 64 * NW) {
-      const int b0 = idx & ~255, r = (idx >> 4) & 15, c = idx & 15;
-      LbT[idx] = Lb[b0 + c * 16 + r];
-    }
-    for (int idx = tid; idx < NB * 256; idx += 64 * NW) {
-      const int b0 = idx & ~255, r = (idx >> 4) & 15, c = idx & 15;
-      DiT[idx] = Di[b0 + c * 16 + r];
-    }
-    __syncthreads();
-  }
-  // ---- the substitutions
-  const __bf16* Lt = isx ? LbT : Lb;
-  const float* Dg = isx ? DiT : Di;
-  cb4 nb[NB];   // -solution blocks in bf16, the B operand of later blocks
-  auto ltile = [&](int blk) { return *reinterpret_cast<const cb4*>(Lt + blk * 256 + lr * 16 + 4 * lg); };
-  auto finish = [&](int i, cf4 acc) {
-    const cf4 dF = *reinterpret_cast<const cf4*>(Dg + i * 256 + lr * 16 + 4 * lg);
-    cf4 o = cz4();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dF[e], acc[e], o, 0, 0, 0);
-    nb[i] = to_b4(cf4{-o[0], -o[1], -o[2], -o[3]});
-    // lane holds rows 16 i + 4 lg + e, column 16 ct + lr
-    __bf16* out = (isx ? w.x : w.y) + job * NA * DV;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[(16 * i + 4 * lg + e) * DV + 16 * ct + lr] = (__bf16)o[e];
-  };
-  if (!isx) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      cf4 acc = cf4{(float)rhb[i][0], (float)rhb[i][1], (float)rhb[i][2], (float)rhb[i][3]};
-      const int base = i * (i - 1) / 2;   // tiles (i, 0 .. i-1)
-#pragma unroll
-      for (int jb = 0; jb + 1 < i; jb += 2)
-        acc = mfma_b(cat8(ltile(base + jb), ltile(base + jb + 1)), cat8(nb[jb], nb[jb + 1]), acc);
-      if (i % 2 == 1) acc = mfma_b(cat8(ltile(base + i - 1), zb4()), cat8(nb[i - 1], zb4()), acc);
-      finish(i, acc);
-    }
-  } else {
-#pragma unroll
-    for (int i = NB - 1; i >= 0; --i) {
-      cf4 acc = cf4{(float)rhb[i][0], (float)rhb[i][1], (float)rhb[i][2], (float)rhb[i][3]};
-      // tiles (L_ji)^T for j = i+1 .. NB-1, stored at index j (j - 1) / 2 + i
-      int jb = i + 1;
-#pragma unroll
-      for (; jb + 1 < NB; jb += 2)
-        acc = mfma_b(cat8(ltile(jb * (jb - 1) / 2 + i), ltile((jb + 1) * jb / 2 + i)), cat8(nb[jb], nb[jb + 1]), acc);
-      if (jb < NB) acc = mfma_b(cat8(ltile(jb * (jb - 1) / 2 + i), zb4()), cat8(nb[jb], zb4()), acc);
-      finish(i, acc);
     }
   }
 }
@@ -1171,7 +1162,9 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
                             sizeof(float) +
                         (KA_ == kDq ? BcEpi<false, DK, RAB, 64 * NW>::EXTRA : 0) +
                         static_cast<size_t>(BcGroupWaves<KA_, KB_>::template wc<RAB>()) * 16 * (DV + 4) * sizeof(float);
-    const size_t lds = stage_b > ep_b ? stage_b : ep_b;
+    const size_t solve_b = KA_ == kRhsY || KA_ == kRhsX ? static_cast<size_t>(BcSolveCfg<DK, DV, RAB>::LDS) : 0;
+    size_t lds = stage_b > ep_b ? stage_b : ep_b;
+    if (solve_b > lds) lds = solve_b;
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
@@ -1180,15 +1173,13 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   };
   using KN = std::integral_constant<int, -1>;
   if constexpr (RAB > 0) {
+    // the forward and the adjoint rank rows: right-hand side, then solve
     if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
-                   w.ry, nullptr)) != hipSuccess)
+                   w.y, nullptr)) != hipSuccess)
       return e;
     if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, chunk(w.at), none, GdS, chunk(w.qt), Os, none, none,
-                   w.rx, nullptr)) != hipSuccess)
+                   w.x, nullptr)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((bwc_solve_kernel<DK, DV, RAB>), dim3((jobs + 7) / 8 * 16), dim3(64 * BcSolveCfg<DK, DV, RAB>::NW), 0, s,
-                       BcSolveArgs{p, w});
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // (with dV, whose operands this group stages)
     if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
                    chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A, dV)) != hipSuccess)
