@@ -362,6 +362,21 @@ def backward_flops(spec):
     return 2.0 * n_chunks * (prep + scans + tri + rhs + solve + grads)
 
 
+def backward_bytes(spec):
+    """Algorithmic bytes of lattn_chunk_bwd: the forward's inputs, the output
+    cotangents and the final-state cotangent read once; the gradients (fp32:
+    q, k, v, the log-decay, A, B and the initial state) written once.  What
+    the kernels hand each other (boundary states and cotangents, the scaled
+    operands, the solved rank rows) is not counted."""
+    e = 2 if spec.dtype == "bf16" else 4
+    dk, dv = spec.dk, spec.dv
+    dec = 1 if spec.scalar_decay else dk
+    rd = e * (dk + spec.r_kv * dk + spec.r_kv * dv + 2 * spec.r_ab * dk + dv) + 4 * dec
+    wr = 4 * (dk + spec.r_kv * dk + spec.r_kv * dv + 2 * spec.r_ab * dk + dec)
+    BH = spec.B * spec.H
+    return float((rd + wr) * BH * spec.T + 2 * 4 * BH * dk * dv)
+
+
 def backward_leg(spec, raw, inputs, torch, lattn, dev):
     """lattn_chunk_bwd on the benchmark workload (same inputs as the forward,
     seeded output cotangents and a final-state cotangent), through a TrainPlan
@@ -393,6 +408,7 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
         return a.elapsed_time(b) / reps
     ms = timed(plan.backward)
     flops = backward_flops(spec)
+    nbytes = backward_bytes(spec)
     # The training pair: the forward that keeps the chunk operators, the
     # decay-scaled operands and the boundary states, and the backward that
     # reads them instead of forming them again (same inputs, same cotangents).
@@ -407,6 +423,8 @@ def backward_leg(spec, raw, inputs, torch, lattn, dev):
         "unit": "tokens/s",
         "gflop": round(flops / 1e9, 2),
         "mfma_frac_bf16": round(flops / (ms / 1e3) / (PEAK["bf16_mfma_TFs"] * 1e12), 4),
+        "algorithmic_gb": round(nbytes / 1e9, 4),
+        "hbm_frac_algorithmic": round(nbytes / (ms / 1e3) / (PEAK["hbm_GBs"] * 1e9), 4),
         "ratio_to_forward": None,
         "training_pair": {
             "entries": "lattn_chunk_fwd_train + lattn_chunk_bwd_saved",

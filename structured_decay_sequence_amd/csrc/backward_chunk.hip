@@ -178,7 +178,8 @@ size_t bc_layout(const Problem& p, char* ws, BcBufs* b, const PrepBwOut* ops = n
 // The pairs: (dK, dA) and (dQ, dB), since those read the same operands; at
 // r_ab > 0 dV (which needs the adjoint solve's X) runs as a third role of
 // the (dK, dA) group, whose staging holds all of its operands (BcDvInDk),
-// and the right-hand sides of the two solves run alone.
+// and the right-hand sides of the two solves run alone, each group going on
+// to its solve.
 enum BcKind { kRhsY = 0, kRhsX = 1, kDq = 2, kDk = 3, kDv = 4, kDa = 5, kDb = 6 };
 enum BcMask { kLE = 0, kLT = 1, kGE = 2, kGT = 3 };   // keep key token s rel query token t
 // Where a chunk's operand lives: a per-chunk bf16 array of the prep or the
@@ -259,7 +260,7 @@ struct BcGroupArgs {
   BcBufs w;
   void* outa;                   // the solved rank rows Y or X (bf16, [NA][d_v]), or the first kind's gradient (fp32)
   void* outb;                   // the second kind's gradient
-  void* outc;                   // the (dK, dA) group: dV, from its fused last term on top of dV1's partial
+  void* outc;                   // the (dK, dA) group: dV (fp32), formed by its third role
   const __bf16 *xr, *rr;        // dK / dQ groups: raw k or q, and raw A or B (the decay gradient's terms)
   const __bf16* ckpt;           // dK group: the boundary states (the state leaving the chunk, for the chunk-end term)
   float* dld;                   // dQ group: the log-decay gradient
