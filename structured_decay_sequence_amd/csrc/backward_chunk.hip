@@ -760,7 +760,7 @@ struct BcGroupWaves {
 };
 
 template <int KA_, int KB_, int DK, int DV, int RAB, int NW>
-__global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
+__device__ __forceinline__ void bwc_group_body(const BcGroupArgs& a, const int64_t job) {
   using K = BcKindCfg<KA_, DK, DV, RAB>;
   using L = BcStage<KA_, DK, DV, RAB>;
   constexpr int WA = K::M / 16, KS = K::KA / 32, OT = K::NOUT / 16;
@@ -774,7 +774,7 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
   extern __shared__ __align__(16) unsigned char smem_[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem_);
   const Problem& p = a.p;
-  const int64_t job = blockIdx.x, bh = job / p.N, jc = job % p.N;
+  const int64_t bh = job / p.N, jc = job % p.N;
   const int n = static_cast<int>(p.T - jc * kCC < kCC ? p.T - jc * kCC : kCC);
   const int64_t tok0 = bh * p.T + jc * kCC;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -928,6 +928,24 @@ __global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
       bc_out<KA_, DK, DV, RAB, 64 * NW>(p, job, ep, static_cast<float*>(a.outa), tid);
     }
   }
+}
+
+template <int KA_, int KB_, int DK, int DV, int RAB, int NW>
+__global__ __launch_bounds__(64 * NW) void bwc_group_kernel(BcGroupArgs a) {
+  bwc_group_body<KA_, KB_, DK, DV, RAB, NW>(a, blockIdx.x);
+}
+
+// The two right-hand side groups (each with its solve) in one launch: blocks
+// b and b + 8, which dispatch places on one XCD, take the Y and the X group
+// of one chunk, so that the blocks of L they both read meet in one L2.
+template <int DK, int DV, int RAB, int NW>
+__global__ __launch_bounds__(64 * NW) void bwc_rhs_pair_kernel(BcGroupArgs ay, BcGroupArgs ax) {
+  const int64_t b = blockIdx.x, job = (b >> 4) * 8 + (b & 7);
+  if (job >= ay.p.BH * ay.p.N) return;
+  if ((b >> 3) & 1)
+    bwc_group_body<kRhsX, -1, DK, DV, RAB, NW>(ax, job);
+  else
+    bwc_group_body<kRhsY, -1, DK, DV, RAB, NW>(ay, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -1150,13 +1168,11 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
   auto chunk = [](const void* x) { return BcSrc{x, kSrcChunk}; };
   const BcSrc Vs{v, kSrcSeq}, Os{dout, kSrcSeq}, Sin{ckpt, kSrcState}, GdS{gend, kSrcCotG};
   // one group launch: kinds KA_ (and KB_, sharing the B-side operands)
-  auto group = [&](auto ka_, auto kb_, BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2,
-                   void* outa, void* outb, const void* xr = nullptr, const void* rr = nullptr,
-                   void* outc = nullptr) -> hipError_t {
+  // the LDS of a group of kinds KA_ (and KB_, sharing the B-side operands)
+  auto group_lds = [&](auto ka_, auto kb_) -> size_t {
     constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
     constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
     using L = BcStage<KA_, DK, DV, RAB>;
-    const void* fn = reinterpret_cast<const void*>(bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>);
     const size_t stage_b = static_cast<size_t>(L::TOTAL) * 2;
     // the products' copy, and the dQ group's decay-gradient terms beyond it
     const size_t ep_b = static_cast<size_t>(BcGroupWaves<KA_, KB_>::template rows<DK, DV, RAB>()) * (L::NOUT + 4) *
@@ -1165,40 +1181,60 @@ hipError_t launch_bc_t(const Problem& p, const BcBufs& w, const void* q, const v
                         static_cast<size_t>(BcGroupWaves<KA_, KB_>::template wc<RAB>()) * 16 * (DV + 4) * sizeof(float);
     const size_t solve_b = KA_ == kRhsY || KA_ == kRhsX ? static_cast<size_t>(BcSolveCfg<DK, DV, RAB>::LDS) : 0;
     size_t lds = stage_b > ep_b ? stage_b : ep_b;
-    if (solve_b > lds) lds = solve_b;
+    return solve_b > lds ? solve_b : lds;
+  };
+  auto args = [&](BcSrc Aa, BcSrc Ab, BcSrc W0, BcSrc B1, BcSrc C1, BcSrc B2, BcSrc C2, void* outa, void* outb,
+                  const void* xr = nullptr, const void* rr = nullptr, void* outc = nullptr) {
+    return BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, outc, bf(xr), bf(rr), bf(ckpt), dld};
+  };
+  // one group launch: kinds KA_ (and KB_), one workgroup per chunk
+  auto group = [&](auto ka_, auto kb_, const BcGroupArgs& ga) -> hipError_t {
+    constexpr int KA_ = decltype(ka_)::value, KB_ = decltype(kb_)::value;
+    constexpr int NW = BcGroupWaves<KA_, KB_>::template count<DK, DV, RAB>();
+    const void* fn = reinterpret_cast<const void*>(bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>);
+    const size_t lds = group_lds(ka_, kb_);
     hipError_t e2 = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s,
-                       BcGroupArgs{p, Aa, Ab, W0, B1, C1, B2, C2, w, outa, outb, outc, bf(xr), bf(rr), bf(ckpt), dld});
+    hipLaunchKernelGGL((bwc_group_kernel<KA_, KB_, DK, DV, RAB, NW>), dim3(jobs), dim3(64 * NW), lds, s, ga);
     return hipGetLastError();
   };
   using KN = std::integral_constant<int, -1>;
   if constexpr (RAB > 0) {
-    // the forward and the adjoint rank rows: right-hand side, then solve
-    if ((e = group(std::integral_constant<int, kRhsY>{}, KN{}, chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none,
-                   w.y, nullptr)) != hipSuccess)
-      return e;
-    if ((e = group(std::integral_constant<int, kRhsX>{}, KN{}, chunk(w.at), none, GdS, chunk(w.qt), Os, none, none,
-                   w.x, nullptr)) != hipSuccess)
-      return e;
+    // the forward and the adjoint rank rows: right-hand side, then solve,
+    // the two groups of a chunk side by side
+    {
+      using KY = std::integral_constant<int, kRhsY>;
+      using KX = std::integral_constant<int, kRhsX>;
+      constexpr int NW = BcGroupWaves<kRhsY, -1>::template count<DK, DV, RAB>();
+      static_assert(NW == BcGroupWaves<kRhsX, -1>::template count<DK, DV, RAB>(), "one block size for both");
+      const size_t ly = group_lds(KY{}, KN{}), lx = group_lds(KX{}, KN{}), lds = ly > lx ? ly : lx;
+      const void* fn = reinterpret_cast<const void*>(bwc_rhs_pair_kernel<DK, DV, RAB, NW>);
+      if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)
+        return e;
+      hipLaunchKernelGGL((bwc_rhs_pair_kernel<DK, DV, RAB, NW>), dim3((jobs + 7) / 8 * 16), dim3(64 * NW), lds, s,
+                         args(chunk(w.bt), none, Sin, chunk(w.kt), Vs, none, none, w.y, nullptr),
+                         args(chunk(w.at), none, GdS, chunk(w.qt), Os, none, none, w.x, nullptr));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // (with dV, whose operands this group stages)
-    if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{}, Vs, chunk(w.y), GdS, Os,
-                   chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A, dV)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDk>{}, std::integral_constant<int, kDa>{},
+                   args(Vs, chunk(w.y), GdS, Os, chunk(w.qt), chunk(w.x), chunk(w.bt), dK, dA, k, A, dV))) !=
+        hipSuccess)
       return e;
-    if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{}, Os, chunk(w.x), Sin, Vs,
-                   chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB, q, B)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDq>{}, std::integral_constant<int, kDb>{},
+                   args(Os, chunk(w.x), Sin, Vs, chunk(w.kt), chunk(w.y), chunk(w.at), dq, dB, q, B))) != hipSuccess)
       return e;
   } else {
-    if ((e = group(std::integral_constant<int, kDk>{}, KN{}, Vs, none, GdS, Os, chunk(w.qt), none, none, dK,
-                   nullptr, k, nullptr)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDk>{}, KN{},
+                   args(Vs, none, GdS, Os, chunk(w.qt), none, none, dK, nullptr, k, nullptr))) != hipSuccess)
       return e;
-    if ((e = group(std::integral_constant<int, kDq>{}, KN{}, Os, none, Sin, Vs, chunk(w.kt), none, none, dq,
-                   nullptr, q, nullptr)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDq>{}, KN{},
+                   args(Os, none, Sin, Vs, chunk(w.kt), none, none, dq, nullptr, q, nullptr))) != hipSuccess)
       return e;
   }
   if constexpr (RAB == 0) {
-    if ((e = group(std::integral_constant<int, kDv>{}, KN{}, chunk(w.kt), none, GdS, chunk(w.qt), Os, none, none, dV,
-                   nullptr)) != hipSuccess)
+    if ((e = group(std::integral_constant<int, kDv>{}, KN{},
+                   args(chunk(w.kt), none, GdS, chunk(w.qt), Os, none, none, dV, nullptr))) != hipSuccess)
       return e;
   }
   return hipSuccess;
