@@ -245,12 +245,16 @@ __global__ __launch_bounds__(64 * NWV) void hla_compose_kernel(HlaArgs a) {
 }
 
 // The same composition on the bf16 path, on bf16 MFMAs (16x16x32, fp32
-// accumulate).  Each wave keeps one column tile of O (c_v = w % (d_v/16)) and
-// of R (c_k = w % (d_k/16)) and the row tiles w / n_c + (NWV / n_c) u, so the
-// B operands of a history chunk (Acal_j^T and B_j^T column tiles, bf16 in
-// memory) are loaded once per wave.  R is carried in fp32 by the wave that
-// owns each tile; its bf16 copy in LDS (rows padded to d_k + 16) is the A
-// operand of the next chunk's products.
+// accumulate).  The query rows are independent (each carries its own gates),
+// so a workgroup takes 64 rows of a gating chunk: a gating chunk of L tokens
+// spreads over L / 64 workgroups.  Each
+// wave keeps one column tile of O (c_v = w % (d_v/16)) and of R
+// (c_k = w % (d_k/16)) and the row tiles w / n_c + (NWV / n_c) u, so the B
+// operands of a history chunk (Acal_j^T and B_j^T column tiles, bf16 in
+// memory) are loaded once per wave, one history chunk ahead together with its
+// gates, while the current chunk's products run.  R is carried in fp32 by the
+// wave that owns each tile; its bf16 copy in LDS (rows padded to d_k + 16) is
+// the A operand of the next chunk's products.
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 hbf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 hbf16x4;
 
@@ -265,129 +269,148 @@ struct HlaBf16Args {
   void* out;
 };
 
-template <int NWV, int DK, int DV>
-__global__ __launch_bounds__(64 * NWV) void hla_compose_bf16_kernel(HlaBf16Args a) {
+constexpr int kHcRows = 64;   // query rows per workgroup (one gate per lane)
+constexpr int kHcWaves = 8;
+
+// A barrier that orders LDS only: the next history chunk's global loads stay
+// in flight across it.
+__device__ __forceinline__ void hc_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * kHcWaves) void hla_compose_bf16_kernel(HlaBf16Args a) {
+  constexpr int NWV = kHcWaves, CR = kHcRows;
   constexpr int LDR = DK + 16;                 // bf16 per row of the A-operand copy of R
   constexpr int KB = DK / 32;                  // 32-deep K steps
   constexpr int NCV = DV / 16, NCK = DK / 16;  // column tiles of O and of R
+  constexpr int NRT = CR / 16;                 // row tiles
   static_assert(NWV % NCV == 0 && NWV % NCK == 0, "whole column tiles per wave");
+  constexpr int SV = NWV / NCV, SK = NWV / NCK;   // row-tile strides
+  static_assert(NRT % SV == 0 && NRT % SK == 0, "whole row tiles per wave");
+  constexpr int TV = NRT / SV, TK = NRT / SK;     // row tiles per wave, of O and of R
   extern __shared__ __align__(16) unsigned char smem[];
   const Problem& p = a.p;
   const int C = p.C;
   const int N = static_cast<int>(p.N);
-  const int c = N - 1 - static_cast<int>(blockIdx.x / p.BH);   // longest walks first
-  const int64_t bh = blockIdx.x % p.BH;
+  const int RS = C / CR;                       // row blocks per gating chunk
+  const int64_t per = p.BH * RS;
+  const int c = N - 1 - static_cast<int>(blockIdx.x / per);   // longest walks first
+  const int64_t rem = blockIdx.x % per;
+  const int64_t bh = rem / RS;
+  const int r0 = static_cast<int>(rem % RS) * CR;             // first query row of the block
   const int64_t job = bh * N + c;
   const int64_t t0 = static_cast<int64_t>(c) * C;
-  const int n = static_cast<int>(p.T - t0 < C ? p.T - t0 : C);
+  const int64_t left = p.T - t0 - r0;
+  if (left <= 0) return;                       // rows past the sequence (the whole workgroup)
+  const int n = static_cast<int>(left < CR ? left : CR);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int nrt = C / 16;
   __bf16* Rb = reinterpret_cast<__bf16*>(smem);
-  float* gs = reinterpret_cast<float*>(smem + static_cast<size_t>(C) * LDR * 2);
   const int cv = wave % NCV, ck = wave % NCK;
   const int rv0 = wave / NCV, rk0 = wave / NCK;
-  constexpr int SV = NWV / NCV, SK = NWV / NCK;   // row-tile strides
-  const int nov = (nrt - rv0 + SV - 1) / SV, nok = (nrt - rk0 + SK - 1) / SK;   // tiles this wave owns
-  const float* Qc = a.QB + static_cast<size_t>(job) * C * DK;
-  const float* Oc = a.OI + static_cast<size_t>(job) * C * DV;
-  f32x4 O[kHlaTiles], Rf[kHlaTiles];
+  const float* Qc = a.QB + (static_cast<size_t>(job) * C + r0) * DK;
+  const float* Oc = a.OI + (static_cast<size_t>(job) * C + r0) * DV;
+  f32x4 O[TV], Rf[TK];
 #pragma unroll
-  for (int u = 0; u < kHlaTiles; ++u) {
-    O[u] = zero4();
-    Rf[u] = zero4();
-    if (u < nov) {
-      const int rt = rv0 + SV * u;
+  for (int u = 0; u < TV; ++u) {
+    const int rt = rv0 + SV * u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = rt * 16 + 4 * lg + e;
-        O[u][e] = t < n ? Oc[static_cast<size_t>(t) * DV + cv * 16 + lr] : 0.f;
-      }
-    }
-    if (u < nok) {
-      const int rt = rk0 + SK * u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = rt * 16 + 4 * lg + e;
-        const float r = t < n ? Qc[static_cast<size_t>(t) * DK + ck * 16 + lr] : 0.f;
-        Rf[u][e] = r;
-        Rb[t * LDR + ck * 16 + lr] = (__bf16)r;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int t = rt * 16 + 4 * lg + e;
+      O[u][e] = t < n ? Oc[static_cast<size_t>(t) * DV + cv * 16 + lr] : 0.f;
     }
   }
-  const float* gb = a.gates + static_cast<size_t>(bh * p.T + t0) * N;
-  const float theta = a.theta;
-  __syncthreads();
-  for (int j = c - 1; j >= 0; --j) {
-    int act = 0;
-    for (int t = tid; t < C; t += 64 * NWV) {
-      const float w = t < n ? gb[static_cast<size_t>(t) * N + j] : 0.f;
-      // Only a gate below the threshold counts as 0; a NaN gate is applied
-      // (and propagates), so it keeps the chunk active.
-      act |= !(w < theta);
-      gs[t] = w < theta ? 0.f : w;
+#pragma unroll
+  for (int u = 0; u < TK; ++u) {
+    const int rt = rk0 + SK * u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = rt * 16 + 4 * lg + e;
+      const float r = t < n ? Qc[static_cast<size_t>(t) * DK + ck * 16 + lr] : 0.f;
+      Rf[u][e] = r;
+      Rb[t * LDR + ck * 16 + lr] = (__bf16)r;
     }
-    if (!__syncthreads_or(act)) continue;
-    const __bf16* BTj = a.BT + (static_cast<size_t>(bh) * N + j) * DV * DK + static_cast<size_t>(cv * 16 + lr) * DK;
-    const __bf16* ATj = a.AT + (static_cast<size_t>(bh) * N + j) * DK * DK + static_cast<size_t>(ck * 16 + lr) * DK;
+  }
+  const float* gb = a.gates + static_cast<size_t>(bh * p.T + t0 + r0) * N;
+  const float theta = a.theta;
+  // this wave's B-operand rows of history chunk j, and the gate of row
+  // `lane` (every wave loads all 64, so each decides alone whether the chunk
+  // is active, and all decide alike)
+  const size_t bts = static_cast<size_t>(DV) * DK, ats = static_cast<size_t>(DK) * DK;
+  const __bf16* BTb = a.BT + static_cast<size_t>(bh) * N * bts + static_cast<size_t>(cv * 16 + lr) * DK + 8 * lg;
+  const __bf16* ATb = a.AT + static_cast<size_t>(bh) * N * ats + static_cast<size_t>(ck * 16 + lr) * DK + 8 * lg;
+  hbf16x8 nv[KB], nk[KB];
+  float ng = 0.f;
+  auto fetch = [&](int j) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      nv[kb] = *reinterpret_cast<const hbf16x8*>(BTb + j * bts + kb * 32);
+      nk[kb] = *reinterpret_cast<const hbf16x8*>(ATb + j * ats + kb * 32);
+    }
+    ng = lane < n ? gb[static_cast<size_t>(lane) * N + j] : 0.f;
+  };
+  if (c > 0) fetch(c - 1);
+  hc_lds_barrier();
+  for (int j = c - 1; j >= 0; --j) {
     hbf16x8 bfv[KB], bfk[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      bfv[kb] = *reinterpret_cast<const hbf16x8*>(BTj + kb * 32 + 8 * lg);
-      bfk[kb] = *reinterpret_cast<const hbf16x8*>(ATj + kb * 32 + 8 * lg);
+      bfv[kb] = nv[kb];
+      bfk[kb] = nk[kb];
     }
+    const float w = ng;
+    if (j > 0) fetch(j - 1);
+    // Only a gate below the threshold counts as 0; a NaN gate is applied (and
+    // propagates), so it keeps the chunk active.
+    if (__ballot(lane < n && !(w < theta)) == 0) continue;
+    const float g = w < theta ? 0.f : w;   // rows past the sequence hold 0
     // O += diag(g) R B_j
 #pragma unroll
-    for (int u = 0; u < kHlaTiles; ++u) {
-      if (u < nov) {
-        const int rt = rv0 + SV * u;
-        const __bf16* arow = Rb + (rt * 16 + lr) * LDR + 8 * lg;
-        f32x4 acc = zero4();
+    for (int u = 0; u < TV; ++u) {
+      const int rt = rv0 + SV * u;
+      const __bf16* arow = Rb + (rt * 16 + lr) * LDR + 8 * lg;
+      f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const hbf16x8*>(arow + kb * 32), bfv[kb], acc,
-                                                        0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const hbf16x8*>(arow + kb * 32), bfv[kb], acc,
+                                                      0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[u][e] += gs[rt * 16 + 4 * lg + e] * acc[e];
-      }
+      for (int e = 0; e < 4; ++e) O[u][e] += __shfl(g, rt * 16 + 4 * lg + e, 64) * acc[e];
     }
     // R <- R + diag(g) (R Acal_j - R), in fp32 by the owning wave
 #pragma unroll
-    for (int u = 0; u < kHlaTiles; ++u) {
-      if (u < nok) {
-        const int rt = rk0 + SK * u;
-        const __bf16* arow = Rb + (rt * 16 + lr) * LDR + 8 * lg;
-        f32x4 acc = zero4();
+    for (int u = 0; u < TK; ++u) {
+      const int rt = rk0 + SK * u;
+      const __bf16* arow = Rb + (rt * 16 + lr) * LDR + 8 * lg;
+      f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const hbf16x8*>(arow + kb * 32), bfk[kb], acc,
-                                                        0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const hbf16x8*>(arow + kb * 32), bfk[kb], acc,
+                                                      0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Rf[u][e] += gs[rt * 16 + 4 * lg + e] * (acc[e] - Rf[u][e]);
-      }
+      for (int e = 0; e < 4; ++e) Rf[u][e] += __shfl(g, rt * 16 + 4 * lg + e, 64) * (acc[e] - Rf[u][e]);
     }
-    __syncthreads();   // every product has read the bf16 copy of R
+    hc_lds_barrier();   // every product has read the bf16 copy of R
 #pragma unroll
-    for (int u = 0; u < kHlaTiles; ++u) {
-      if (u < nok) {
-        const int rt = rk0 + SK * u;
+    for (int u = 0; u < TK; ++u) {
+      const int rt = rk0 + SK * u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Rb[(rt * 16 + 4 * lg + e) * LDR + ck * 16 + lr] = (__bf16)Rf[u][e];
-      }
+      for (int e = 0; e < 4; ++e) Rb[(rt * 16 + 4 * lg + e) * LDR + ck * 16 + lr] = (__bf16)Rf[u][e];
     }
-    __syncthreads();
+    hc_lds_barrier();
   }
   __bf16* op = static_cast<__bf16*>(a.out);
 #pragma unroll
-  for (int u = 0; u < kHlaTiles; ++u) {
-    if (u < nov) {
-      const int rt = rv0 + SV * u;
+  for (int u = 0; u < TV; ++u) {
+    const int rt = rv0 + SV * u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = rt * 16 + 4 * lg + e;
-        if (t < n) op[static_cast<size_t>(bh * p.T + t0 + t) * DV + cv * 16 + lr] = (__bf16)O[u][e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int t = rt * 16 + 4 * lg + e;
+      if (t < n) op[static_cast<size_t>(bh * p.T + t0 + r0 + t) * DV + cv * 16 + lr] = (__bf16)O[u][e];
     }
   }
 }
@@ -426,31 +449,27 @@ HlaPlan hla_plan(const Problem& p) {
   return h;
 }
 
-template <int NWV, int DK, int DV>
+template <int DK, int DV>
 hipError_t launch_compose_bf16_t(const Problem& p, const HlaBf16Args& ca, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(p.C) * (DK + 16) * 2 + static_cast<size_t>(p.C) * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(hla_compose_bf16_kernel<NWV, DK, DV>);
+  const size_t lds = static_cast<size_t>(kHcRows) * (DK + 16) * 2;
+  const void* fn = reinterpret_cast<const void*>(hla_compose_bf16_kernel<DK, DV>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((hla_compose_bf16_kernel<NWV, DK, DV>), dim3(static_cast<unsigned>(p.BH * p.N)), dim3(64 * NWV),
-                     lds, s, ca);
+  const int64_t blocks = p.BH * p.N * (p.C / kHcRows);
+  hipLaunchKernelGGL((hla_compose_bf16_kernel<DK, DV>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kHcWaves), lds,
+                     s, ca);
   return hipGetLastError();
-}
-
-template <int NWV>
-hipError_t launch_compose_bf16_w(const Problem& p, const HlaBf16Args& ca, hipStream_t s) {
-  if (p.dk == 128 && p.dv == 128) return launch_compose_bf16_t<NWV, 128, 128>(p, ca, s);
-  if (p.dk == 128 && p.dv == 64) return launch_compose_bf16_t<NWV, 128, 64>(p, ca, s);
-  if (p.dk == 64 && p.dv == 128) return launch_compose_bf16_t<NWV, 64, 128>(p, ca, s);
-  if (p.dk == 64 && p.dv == 64) return launch_compose_bf16_t<NWV, 64, 64>(p, ca, s);
-  return hipErrorInvalidValue;
 }
 
 hipError_t launch_compose_bf16(const Problem& p, const float* QB, const __bf16* AT, const __bf16* BT, const float* OI,
                                const float* gates, float theta, void* out, hipStream_t s) {
   HlaBf16Args ca{p, QB, AT, BT, OI, gates, theta, out};
-  // enough waves that each owns at most kHlaTiles row tiles of O and of R
-  return p.C > 128 ? launch_compose_bf16_w<16>(p, ca, s) : launch_compose_bf16_w<8>(p, ca, s);
+  if (p.C % kHcRows != 0) return hipErrorInvalidValue;   // gating chunks of whole row blocks
+  if (p.dk == 128 && p.dv == 128) return launch_compose_bf16_t<128, 128>(p, ca, s);
+  if (p.dk == 128 && p.dv == 64) return launch_compose_bf16_t<128, 64>(p, ca, s);
+  if (p.dk == 64 && p.dv == 128) return launch_compose_bf16_t<64, 128>(p, ca, s);
+  if (p.dk == 64 && p.dv == 64) return launch_compose_bf16_t<64, 64>(p, ca, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_hla(const Problem& p, const void* q, const void* k, const float* ld, const void* A,
