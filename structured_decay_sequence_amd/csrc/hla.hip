@@ -296,11 +296,15 @@ __global__ __launch_bounds__(64 * kHcWaves) void hla_compose_bf16_kernel(HlaBf16
   const int C = p.C;
   const int N = static_cast<int>(p.N);
   const int RS = C / CR;                       // row blocks per gating chunk
-  const int64_t per = p.BH * RS;
+  // Blocks go round-robin over the 8 XCDs, so block b takes a head with
+  // bh % 8 == b % 8: each XCD's L2 then holds the history operands of its
+  // own heads only, which every query chunk and row block of those heads reads.
+  const int64_t per = (p.BH + 7) / 8 * 8 * RS;
   const int c = N - 1 - static_cast<int>(blockIdx.x / per);   // longest walks first
-  const int64_t rem = blockIdx.x % per;
-  const int64_t bh = rem / RS;
-  const int r0 = static_cast<int>(rem % RS) * CR;             // first query row of the block
+  const int64_t rem = blockIdx.x % per, grp = rem / 8;
+  const int64_t bh = (grp / RS) * 8 + rem % 8;
+  if (bh >= p.BH) return;                      // past the last head (the whole workgroup)
+  const int r0 = static_cast<int>(grp % RS) * CR;             // first query row of the block
   const int64_t job = bh * N + c;
   const int64_t t0 = static_cast<int64_t>(c) * C;
   const int64_t left = p.T - t0 - r0;
@@ -455,7 +459,7 @@ hipError_t launch_compose_bf16_t(const Problem& p, const HlaBf16Args& ca, hipStr
   const void* fn = reinterpret_cast<const void*>(hla_compose_bf16_kernel<DK, DV>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  const int64_t blocks = p.BH * p.N * (p.C / kHcRows);
+  const int64_t blocks = (p.BH + 7) / 8 * 8 * p.N * (p.C / kHcRows);
   hipLaunchKernelGGL((hla_compose_bf16_kernel<DK, DV>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kHcWaves), lds,
                      s, ca);
   return hipGetLastError();
