@@ -318,15 +318,28 @@ __global__ __launch_bounds__(64 * kHcWaves) void hla_compose_bf16_kernel(HlaBf16
   const int rv0 = wave / NCV, rk0 = wave / NCK;
   const float* Qc = a.QB + (static_cast<size_t>(job) * C + r0) * DK;
   const float* Oc = a.OI + (static_cast<size_t>(job) * C + r0) * DV;
+  // Every row of the block lies inside the gating chunk's QB and OI rows, so
+  // the loads go out unconditionally, all before the first use; rows past
+  // the sequence are zeroed after.
   f32x4 O[TV], Rf[TK];
 #pragma unroll
   for (int u = 0; u < TV; ++u) {
     const int rt = rv0 + SV * u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = rt * 16 + 4 * lg + e;
-      O[u][e] = t < n ? Oc[static_cast<size_t>(t) * DV + cv * 16 + lr] : 0.f;
-    }
+    for (int e = 0; e < 4; ++e) O[u][e] = Oc[static_cast<size_t>(rt * 16 + 4 * lg + e) * DV + cv * 16 + lr];
+  }
+#pragma unroll
+  for (int u = 0; u < TK; ++u) {
+    const int rt = rk0 + SK * u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Rf[u][e] = Qc[static_cast<size_t>(rt * 16 + 4 * lg + e) * DK + ck * 16 + lr];
+  }
+#pragma unroll
+  for (int u = 0; u < TV; ++u) {
+    const int rt = rv0 + SV * u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (rt * 16 + 4 * lg + e >= n) O[u][e] = 0.f;
   }
 #pragma unroll
   for (int u = 0; u < TK; ++u) {
@@ -334,9 +347,8 @@ __global__ __launch_bounds__(64 * kHcWaves) void hla_compose_bf16_kernel(HlaBf16
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = rt * 16 + 4 * lg + e;
-      const float r = t < n ? Qc[static_cast<size_t>(t) * DK + ck * 16 + lr] : 0.f;
-      Rf[u][e] = r;
-      Rb[t * LDR + ck * 16 + lr] = (__bf16)r;
+      if (t >= n) Rf[u][e] = 0.f;
+      Rb[t * LDR + ck * 16 + lr] = (__bf16)Rf[u][e];
     }
   }
   const float* gb = a.gates + static_cast<size_t>(bh * p.T + t0 + r0) * N;
